@@ -1,0 +1,194 @@
+"""Seeded synthetic inputs for the precision-tracking memory scans.
+
+This module only draws random inputs with the shapes and distributions of the
+workloads; it holds none of the recurrences' arithmetic.  Both the HIP path and
+the CPU oracle read what it produces, so it imports neither of them.
+
+Recipe (every workload):
+
+* one PCG64 stream per (seed, b, h) head, so that any head can be regenerated
+  alone; the per-head draw order is fixed (listed per workload below);
+* draws are float32 standard normals, the activation is applied in float32,
+  and values that the workload stores in bf16 are then rounded from float32 to
+  bf16 with round-to-nearest-even;
+* A (forget rate per head) comes from its own stream keyed (seed, 0xA).
+
+Diagonal-precision workloads, per head, in this order:
+  q ~ N(0,1) [T,d_k]; k ~ N(0,1) [T,d_k] then L2-normalised per token;
+  v ~ N(0,1) [T,d_v]; beta = sigmoid(N(0,1)) [T,d_v]; d = softplus(N(0,1)) [T].
+Isotropic workload, per head, in this order:
+  a = exp(-softplus(N(0,1))) [T]; p = softplus(N(0,1)) [T];
+  Lambda = softplus(N(0,1)) [T]; then q, k (normalised), v as above.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+from concurrent.futures import ThreadPoolExecutor
+import os
+
+import numpy as np
+
+__all__ = [
+    "DiagSpec", "IsoSpec", "WORKLOADS", "workload",
+    "diag_head", "diag_inputs", "iso_head", "iso_inputs",
+    "f32_to_bf16_bits",
+]
+
+
+def _rng(*key: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence(list(key))))
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (round to nearest, ties to even); raw uint16 bits."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    bias = ((u >> np.uint64(16)) & np.uint64(1)) + np.uint64(0x7FFF)
+    return ((u + bias) >> np.uint64(16)).astype(np.uint16)
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (np.float32(1.0) / (np.float32(1.0) + np.exp(-x))).astype(np.float32)
+
+
+def _softplus(x: np.ndarray) -> np.ndarray:
+    return np.logaddexp(np.float32(0.0), x).astype(np.float32)
+
+
+@dataclass(frozen=True)
+class DiagSpec:
+    """A diagonal-precision workload: shapes, storage dtype and seed."""
+    name: str
+    B: int
+    H: int
+    T: int
+    d_k: int
+    d_v: int
+    dtype: str            # "f32" or "bf16": storage type of q, k, v, beta, d
+    seed: int
+    A_uniform: bool = True  # A_h ~ U(0.5, 2) per head; False -> A = 1
+    I_prior: float = 1.0
+    prefix: int = 0       # decode workloads: tokens that build the state first
+
+    def with_(self, **kw) -> "DiagSpec":
+        return replace(self, **kw)
+
+
+@dataclass(frozen=True)
+class IsoSpec:
+    """An isotropic (scalar precision per head) workload."""
+    name: str
+    B: int
+    H: int
+    T: int
+    d_k: int
+    d_v: int
+    seed: int
+    lambda0: float = 1.0
+
+    def with_(self, **kw) -> "IsoSpec":
+        return replace(self, **kw)
+
+
+WORKLOADS = {
+    s.name: s for s in [
+        DiagSpec("diag_b1h2t64d16_f32", 1, 2, 64, 16, 16, "f32", 1000, A_uniform=False),
+        DiagSpec("diag_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
+        DiagSpec("diag_b2h16t16384d128_bf16", 2, 16, 16384, 128, 128, "bf16", 1002),
+        IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
+        # one decode token after a 512-token prefix that builds the state
+        DiagSpec("decode_b256h16d128_bf16", 256, 16, 1, 128, 128, "bf16", 1004, prefix=512),
+    ]
+}
+
+
+def workload(name: str):
+    return WORKLOADS[name]
+
+
+def _A(spec: DiagSpec) -> np.ndarray:
+    if not spec.A_uniform:
+        return np.ones(spec.H, dtype=np.float32)
+    return _rng(spec.seed, 0xA).uniform(0.5, 2.0, size=spec.H).astype(np.float32)
+
+
+def diag_head(spec: DiagSpec, b: int, h: int) -> dict:
+    """Float32 draws for one head over prefix + T tokens (before any bf16 rounding)."""
+    T = spec.prefix + spec.T
+    g = _rng(spec.seed, b, h)
+    q = g.standard_normal((T, spec.d_k), dtype=np.float32)
+    k = g.standard_normal((T, spec.d_k), dtype=np.float32)
+    k = (k / np.linalg.norm(k, axis=1, keepdims=True)).astype(np.float32)
+    v = g.standard_normal((T, spec.d_v), dtype=np.float32)
+    beta = _sigmoid(g.standard_normal((T, spec.d_v), dtype=np.float32))
+    d = _softplus(g.standard_normal(T, dtype=np.float32))
+    return {"q": q, "k": k, "v": v, "beta": beta, "d": d}
+
+
+def _store(x: np.ndarray, dtype: str) -> np.ndarray:
+    return f32_to_bf16_bits(x) if dtype == "bf16" else np.ascontiguousarray(x, np.float32)
+
+
+def _threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def diag_inputs(spec: DiagSpec) -> dict:
+    """Whole-workload arrays [B,H,prefix+T,.] in storage dtype (bf16 as uint16 bits).
+
+    Returns q, k, v, beta, d, A (float32 [H]), I_prior and the spec.
+    """
+    Tt = spec.prefix + spec.T
+    shapes = {"q": (Tt, spec.d_k), "k": (Tt, spec.d_k), "v": (Tt, spec.d_v),
+              "beta": (Tt, spec.d_v), "d": (Tt,)}
+    npdt = np.uint16 if spec.dtype == "bf16" else np.float32
+    out = {n: np.empty((spec.B, spec.H) + s, dtype=npdt) for n, s in shapes.items()}
+
+    def one(bh):
+        b, h = divmod(bh, spec.H)
+        x = diag_head(spec, b, h)
+        for n in shapes:
+            out[n][b, h] = _store(x[n], spec.dtype)
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(spec.B * spec.H)))
+    out["A"] = _A(spec)
+    out["I_prior"] = float(spec.I_prior)
+    out["spec"] = spec
+    return out
+
+
+def iso_head(spec: IsoSpec, b: int, h: int) -> dict:
+    g = _rng(spec.seed, b, h)
+    T = spec.T
+    a = np.exp(-_softplus(g.standard_normal(T, dtype=np.float32))).astype(np.float32)
+    p = _softplus(g.standard_normal(T, dtype=np.float32))
+    lam = _softplus(g.standard_normal(T, dtype=np.float32))
+    q = g.standard_normal((T, spec.d_k), dtype=np.float32)
+    k = g.standard_normal((T, spec.d_k), dtype=np.float32)
+    k = (k / np.linalg.norm(k, axis=1, keepdims=True)).astype(np.float32)
+    v = g.standard_normal((T, spec.d_v), dtype=np.float32)
+    return {"a": a, "p": p, "Lambda": lam, "q": q, "k": k, "v": v}
+
+
+def iso_inputs(spec: IsoSpec, with_mean: bool = True) -> dict:
+    """Whole-workload float32 arrays: a, p, Lambda [B,H,T]; q, k [B,H,T,d_k]; v [B,H,T,d_v]."""
+    names = ["a", "p", "Lambda"] + (["q", "k", "v"] if with_mean else [])
+    shp = {"a": (spec.T,), "p": (spec.T,), "Lambda": (spec.T,),
+           "q": (spec.T, spec.d_k), "k": (spec.T, spec.d_k), "v": (spec.T, spec.d_v)}
+    out = {n: np.empty((spec.B, spec.H) + shp[n], dtype=np.float32) for n in names}
+
+    def one(bh):
+        b, h = divmod(bh, spec.H)
+        x = iso_head(spec, b, h)
+        for n in names:
+            out[n][b, h] = x[n]
+
+    with ThreadPoolExecutor(_threads()) as ex:
+        list(ex.map(one, range(spec.B * spec.H)))
+    out["lambda0"] = np.full((spec.B, spec.H), spec.lambda0, dtype=np.float32)
+    out["spec"] = spec
+    return out

@@ -1,0 +1,200 @@
+"""CPU oracle for the precision-tracking memory scans -- TEST INFRASTRUCTURE.
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may
+import this package.  It is independent of the HIP library: it shares no code
+with it and never reads anything the library produced.
+
+The arithmetic lives in ``kdn_oracle.c`` (plain sequential fp64, one head per
+call).  This module only loads it, decodes stored inputs to float64, and runs
+independent heads on a thread pool (heads never interact, so this changes no
+arithmetic).  It also enumerates the chunk/segment plan of the diagonal scan
+from its definition, for the bit-exact bookkeeping checks.
+
+Parity status: every function here is pinned by the ``-m "not gpu"`` tests
+(closed forms, special cases, brute force); see tests/test_oracle_pins.py.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import time
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kdn_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_CFLAGS = ["-O2", "-fPIC", "-shared", "-std=c99", "-fno-fast-math", "-ffp-contract=off"]
+
+_lib = None
+
+
+def build(src: str = _SRC, out: str = _LIB, extra_flags=()) -> str:
+    """Compile the oracle with gcc into a shared library; returns its path."""
+    cmd = ["gcc", *_CFLAGS, *extra_flags, "-o", out, src, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def load(path: str = _LIB):
+    """Load (building first if absent) a compiled oracle library."""
+    global _lib
+    if path == _LIB and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(out=path)
+    lib = ctypes.CDLL(path)
+    D = ctypes.POINTER(ctypes.c_double)
+    L = ctypes.c_long
+    lib.oracle_diag_head.argtypes = [L, L, L, D, D, D, D, D, ctypes.c_double, ctypes.c_double,
+                                     D, D, D, D, D, D]
+    lib.oracle_diag_head.restype = ctypes.c_int
+    lib.oracle_iso_head.argtypes = [L, D, D, D, ctypes.c_double, L, L, D, D, D, D, D, D, D, D]
+    lib.oracle_iso_head.restype = ctypes.c_int
+    if path == _LIB:
+        _lib = lib
+    return lib
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    return x.ctypes.data_as(ctypes.POINTER(ctypes.c_double))
+
+
+def decode(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Stored input -> float64.  bf16 is raw uint16 bits: the top half of a float32."""
+    if dtype == "bf16":
+        b = np.asarray(x)
+        return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _threads(threads):
+    if threads:
+        return threads
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def diag_head(q, k, v, beta, d, A, I_prior, I0=None, mu0=None, lib=None):
+    """One head of the diagonal-precision recurrence; float64 arrays in, dict out."""
+    lib = lib or load()
+    q, k, v, beta, d = (np.ascontiguousarray(x, np.float64) for x in (q, k, v, beta, d))
+    T, dk = q.shape
+    dv = v.shape[1]
+    o = np.empty((T, dv))
+    s = np.empty((T, dv))
+    I_T = np.empty((dk, dv))
+    mu_T = np.empty((dk, dv))
+    I0 = None if I0 is None else np.ascontiguousarray(I0, np.float64)
+    mu0 = None if mu0 is None else np.ascontiguousarray(mu0, np.float64)
+    rc = lib.oracle_diag_head(T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
+                              float(A), float(I_prior), _ptr(I0), _ptr(mu0),
+                              _ptr(o), _ptr(s), _ptr(I_T), _ptr(mu_T))
+    if rc != 0:
+        raise MemoryError("oracle_diag_head failed")
+    return {"o": o, "s": s, "I_T": I_T, "mu_T": mu_T}
+
+
+def diag_scan(inp: dict, heads=None, threads=None, t_range=None, I0=None, mu0=None, lib=None):
+    """Run the diagonal recurrence over heads of a synthetic-input dict.
+
+    inp: q, k, v, beta, d [B,H,T,.] in storage dtype (spec.dtype), A [H], I_prior.
+    heads: iterable of (b, h); default all.  t_range: (t0, t1) slice of tokens.
+    I0, mu0: optional [B,H,dk,dv] starting state.
+    Returns {(b,h): {"o","s","I_T","mu_T"}} in float64.
+    """
+    spec = inp["spec"]
+    B, H = inp["q"].shape[:2]
+    heads = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    t0, t1 = t_range if t_range is not None else (0, inp["q"].shape[2])
+    lib = lib or load()
+
+    def one(bh):
+        b, h = bh
+        args = [decode(inp[n][b, h, t0:t1], spec.dtype) for n in ("q", "k", "v", "beta", "d")]
+        return bh, diag_head(*args, A=float(inp["A"][h]), I_prior=inp["I_prior"],
+                             I0=None if I0 is None else I0[b, h],
+                             mu0=None if mu0 is None else mu0[b, h], lib=lib)
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        return dict(ex.map(one, heads))
+
+
+def iso_head(a, p, Lam, lambda0, q=None, k=None, v=None, mu0=None, lib=None):
+    """One head of the isotropic (scalar precision) filter; float64 in, dict out."""
+    lib = lib or load()
+    a, p, Lam = (np.ascontiguousarray(x, np.float64) for x in (a, p, Lam))
+    T = a.shape[0]
+    lam = np.empty(T)
+    if q is None:
+        rc = lib.oracle_iso_head(T, _ptr(a), _ptr(p), _ptr(Lam), float(lambda0), 0, 0,
+                                 None, None, None, None, _ptr(lam), None, None, None)
+        if rc != 0:
+            raise MemoryError("oracle_iso_head failed")
+        return {"lambda": lam}
+    q, k, v = (np.ascontiguousarray(x, np.float64) for x in (q, k, v))
+    dk, dv = q.shape[1], v.shape[1]
+    o = np.empty((T, dv))
+    s = np.empty((T, dv))
+    mu_T = np.empty((dk, dv))
+    mu0 = None if mu0 is None else np.ascontiguousarray(mu0, np.float64)
+    rc = lib.oracle_iso_head(T, _ptr(a), _ptr(p), _ptr(Lam), float(lambda0), dk, dv,
+                             _ptr(q), _ptr(k), _ptr(v), _ptr(mu0), _ptr(lam),
+                             _ptr(o), _ptr(s), _ptr(mu_T))
+    if rc != 0:
+        raise MemoryError("oracle_iso_head failed")
+    return {"lambda": lam, "o": o, "s": s, "mu_T": mu_T}
+
+
+def iso_scan(inp: dict, heads=None, threads=None, with_mean=True, lib=None):
+    """Run the isotropic filter over heads of a synthetic-input dict (float32 arrays)."""
+    B, H = inp["a"].shape[:2]
+    heads = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    lib = lib or load()
+
+    def one(bh):
+        b, h = bh
+        f = lambda n: np.asarray(inp[n][b, h], np.float32).astype(np.float64)
+        mean = (f("q"), f("k"), f("v")) if with_mean else (None, None, None)
+        return bh, iso_head(f("a"), f("p"), f("Lambda"), float(inp["lambda0"][b, h]),
+                            *mean, lib=lib)
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        return dict(ex.map(one, heads))
+
+
+def plan(T: int, chunk: int, segments: int):
+    """Chunk and segment bounds of a T-token scan, enumerated from the definition.
+
+    Tokens are cut into n_chunks = ceil(T / chunk) chunks, the last one ragged.
+    Segment s owns chunks [floor(s*n/S), floor((s+1)*n/S)), i.e. tokens from
+    chunk*that up to min(chunk*next, T).  Returns (chunk_starts, chunk_lens,
+    segment_token_bounds) as Python int lists.
+    """
+    n = -(-T // chunk)
+    starts = [c * chunk for c in range(n)]
+    lens = [min(chunk, T - c * chunk) for c in range(n)]
+    bounds = [min((s * n // segments) * chunk, T) for s in range(segments + 1)]
+    return starts, lens, bounds
+
+
+def element_offset(b: int, h: int, t: int, x: int, H: int, T: int, D: int) -> int:
+    """Element index of [b, h, t, x] in a contiguous [B, H, T, D] tensor (Python int)."""
+    return ((b * H + h) * T + t) * D + x
+
+
+class Timer:
+    """Steady-clock wall time of a block (used by the CPU-baseline leg)."""
+
+    def __enter__(self):
+        self.t0 = time.perf_counter()
+        return self
+
+    def __exit__(self, *exc):
+        self.seconds = time.perf_counter() - self.t0

@@ -1,0 +1,297 @@
+"""Pins of the CPU oracle: facts fixed by the pages and by mathematics.
+
+Each pin takes a loaded oracle library, so the same checks also run against
+deliberately broken copies of the oracle (tests/test_oracle_mutants.py).  None
+of them retypes the oracle's own update lines: they use closed forms, special
+cases, an independently coded textbook filter, Mobius-matrix products and
+structural identities.
+
+Sources (page title and section):
+  Palimpsa = "Learning to Remember, Learn, and Forget in Attention-Based
+             Models", Metodologia 1-2 (forget gate, I_t and mu_t updates) and
+             4 (Mamba2 as the limit where I_t stays at I_prior).
+  KLA      = "Riassunto Tecnico: Kalman Linear Attention (KLA)", Metodologia
+             1 (OU prior, observation precision, query read-out), 2 (precision
+             as a Mobius map, affine information mean), 3 (gates from
+             precision ratios).
+  KDN      = "Kalman Delta Networks" abstract (scalar-precision isotropic
+             variant, Mobius uncertainty recurrences, constant-memory decoding).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+
+RTOL = 1e-11  # fp64 sequential vs. closed form: tiny inputs, well conditioned
+
+
+def _close(x, y, rtol=RTOL, atol=0.0, what=""):
+    x = np.asarray(x, np.float64)
+    y = np.asarray(y, np.float64)
+    scale = np.maximum(np.abs(y), np.max(np.abs(y)) * 1e-3 + 1e-300)
+    err = np.max(np.abs(x - y) / scale) if x.size else 0.0
+    assert np.all(np.abs(x - y) <= rtol * scale + atol), f"{what}: max rel err {err:.3e}"
+
+
+def diag_case(seed=7, T=9, dk=3, dv=5, A=0.7, I_prior=1.3, with_state=True):
+    g = np.random.default_rng(seed)
+    k = g.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    c = dict(
+        q=g.standard_normal((T, dk)), k=k, v=g.standard_normal((T, dv)),
+        beta=1.0 / (1.0 + np.exp(-g.standard_normal((T, dv)))),
+        d=np.log1p(np.exp(g.standard_normal(T))), A=A, I_prior=I_prior,
+    )
+    if with_state:
+        c["I0"] = 0.5 + g.random((dk, dv)) * 2.0
+        c["mu0"] = g.standard_normal((dk, dv))
+    return c
+
+
+def _run_diag(lib, c, **over):
+    c = {**c, **over}
+    return oracle.diag_head(c["q"], c["k"], c["v"], c["beta"], c["d"], c["A"], c["I_prior"],
+                            I0=c.get("I0"), mu0=c.get("mu0"), lib=lib)
+
+
+# ---------------------------------------------------------------------------
+# Diagonal-precision path
+# ---------------------------------------------------------------------------
+
+def pin_diag_closed_form(lib):
+    """P-1.  Multiplying the Palimpsa mean update by I_t gives the affine
+    information-form recurrence eta_t = alpha_t eta_{t-1} + (beta_t v_t) (outer) k_t,
+    and I_t - I_prior decays by the same alpha.  Unrolled, with
+    G(s,t) = prod_{r=s+1..t} alpha_r:
+      I_t   = I_prior + G(0,t)(I_0 - I_prior) + sum_s G(s,t) beta_s (outer) k_s^2
+      eta_t = G(0,t) I_0 mu_0 + sum_s G(s,t) (beta_s v_s) (outer) k_s
+      mu_t  = eta_t / I_t,  o_t = mu_t^T q_t.
+    Checked at every prefix length so every o_t is covered."""
+    for c in (diag_case(), diag_case(seed=11, T=6, dk=4, dv=2, A=1.9, I_prior=0.4)):
+        T = c["q"].shape[0]
+        alpha = np.exp(-c["A"] * c["d"])
+        res = _run_diag(lib, c)
+        for t in range(1, T + 1):
+            G = lambda s: np.prod(alpha[s:t])  # tokens are 1-based: G(s,t) = alpha_{s+1..t}
+            I = c["I_prior"] + G(0) * (c["I0"] - c["I_prior"])
+            eta = G(0) * c["I0"] * c["mu0"]
+            for s in range(1, t + 1):
+                ks, bs, vs = c["k"][s - 1], c["beta"][s - 1], c["v"][s - 1]
+                I = I + G(s) * np.outer(ks ** 2, bs)
+                eta = eta + G(s) * np.outer(ks, bs * vs)
+            mu = eta / I
+            _close(res["o"][t - 1], mu.T @ c["q"][t - 1], what=f"o_{t}")
+            if t == T:
+                _close(res["I_T"], I, what="I_T")
+                _close(res["mu_T"], mu, what="mu_T")
+        # the error scale bounds the read-out
+        assert np.all(res["s"] >= np.abs(res["o"]) * (1 - 1e-15))
+
+
+def pin_diag_no_write(lib):
+    """P-2.  beta = 0 and I_0 = I_prior: the precision stays at the prior and
+    the mean only decays, mu_t = (prod alpha) mu_0."""
+    c = diag_case(seed=3, with_state=True)
+    c["beta"] = np.zeros_like(c["beta"])
+    c["I0"] = np.full_like(c["I0"], c["I_prior"])
+    res = _run_diag(lib, c)
+    _close(res["I_T"], np.full_like(c["I0"], c["I_prior"]), rtol=1e-14, what="I_T")
+    decay = np.prod(np.exp(-c["A"] * c["d"]))
+    _close(res["mu_T"], decay * c["mu0"], rtol=1e-13, what="mu_T")
+    _close(res["o"][-1], (decay * c["mu0"]).T @ c["q"][-1], rtol=1e-12, what="o_T")
+
+
+def pin_diag_positive(lib):
+    """P-3.  With beta >= 0 the precision never drops below min(I_0, I_prior)
+    (induction on the Palimpsa I_t update); it also never decreases below the
+    prior once it starts above it."""
+    for seed in range(4):
+        c = diag_case(seed=100 + seed, T=12)
+        c["I0"] = c["I0"] * 0.1
+        lo = min(np.min(c["I0"]), c["I_prior"])
+        for t in range(1, 13):
+            res = _run_diag(lib, c, q=c["q"][:t], k=c["k"][:t], v=c["v"][:t],
+                            beta=c["beta"][:t], d=c["d"][:t])
+            assert np.all(res["I_T"] >= lo * (1 - 1e-15)), "precision fell below its floor"
+
+
+def pin_diag_mamba2_limit(lib):
+    """P-4.  Palimpsa Metodologia 4: when the importance stays at I_prior the
+    model is Mamba2.  With I_prior much larger than beta k^2 the oracle must
+    approach the scalar-decay gated linear-attention recurrence
+    S_t = alpha_t S_{t-1} + k_t (beta_t v_t)^T,  o_t = S_t^T q_t / I_prior,
+    with relative gap of order max(beta k^2) / I_prior."""
+    c = diag_case(seed=5, T=10, dk=4, dv=3, with_state=False)
+    big = 1e9
+    res = _run_diag(lib, c, I_prior=big)
+    alpha = np.exp(-c["A"] * c["d"])
+    S = np.zeros((4, 3))
+    for t in range(10):
+        S = alpha[t] * S + np.outer(c["k"][t], c["beta"][t] * c["v"][t])
+        _close(res["o"][t] * big, S.T @ c["q"][t], rtol=1e-7, what=f"GLA o_{t}")
+
+
+def pin_diag_special_gates(lib):
+    """P-5.  d = 0 (alpha = 1, nothing forgotten): the mean is the running
+    precision-weighted average (I_0 mu_0 + sum beta v (outer) k) / (I_0 + sum beta (outer) k^2).
+    d huge (alpha = 0, everything forgotten): memoryless,
+    mu_t = (beta v (outer) k) / (I_prior + beta (outer) k^2)."""
+    c = diag_case(seed=9)
+    res = _run_diag(lib, c, d=np.zeros_like(c["d"]))
+    num = c["I0"] * c["mu0"] + sum(np.outer(c["k"][t], c["beta"][t] * c["v"][t]) for t in range(9))
+    den = c["I0"] + sum(np.outer(c["k"][t] ** 2, c["beta"][t]) for t in range(9))
+    _close(res["I_T"], den, what="I_T (alpha=1)")
+    _close(res["mu_T"], num / den, what="mu_T (alpha=1)")
+
+    res = _run_diag(lib, c, d=np.full_like(c["d"], 1e4))
+    kT, bT, vT = c["k"][-1], c["beta"][-1], c["v"][-1]
+    den = c["I_prior"] + np.outer(kT ** 2, bT)
+    _close(res["I_T"], den, what="I_T (alpha=0)")
+    _close(res["mu_T"], np.outer(kT, bT * vT) / den, what="mu_T (alpha=0)")
+
+
+def pin_diag_chaining(lib):
+    """P-6.  Constant-memory decoding (KDN abstract): the state is all that
+    carries over, so scan(T1) then scan(T2) from its final state equals
+    scan(T1 + T2), token for token."""
+    c = diag_case(seed=21, T=11)
+    full = _run_diag(lib, c)
+    cut = 4
+    first = _run_diag(lib, c, **{n: c[n][:cut] for n in ("q", "k", "v", "beta", "d")})
+    second = _run_diag(lib, c, I0=first["I_T"], mu0=first["mu_T"],
+                       **{n: c[n][cut:] for n in ("q", "k", "v", "beta", "d")})
+    np.testing.assert_array_equal(np.vstack([first["o"], second["o"]]), full["o"])
+    np.testing.assert_array_equal(second["I_T"], full["I_T"])
+    np.testing.assert_array_equal(second["mu_T"], full["mu_T"])
+
+
+DIAG_PINS = [pin_diag_closed_form, pin_diag_no_write, pin_diag_positive,
+             pin_diag_mamba2_limit, pin_diag_special_gates, pin_diag_chaining]
+
+
+# ---------------------------------------------------------------------------
+# Isotropic (scalar precision) path
+# ---------------------------------------------------------------------------
+
+def iso_case(seed=13, T=10, dk=3, dv=4):
+    g = np.random.default_rng(seed)
+    sp = lambda x: np.log1p(np.exp(x))
+    k = g.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    return dict(a=np.exp(-sp(g.standard_normal(T))), p=sp(g.standard_normal(T)),
+                Lam=sp(g.standard_normal(T)), lambda0=1.0 + g.random(),
+                q=g.standard_normal((T, dk)), k=k, v=g.standard_normal((T, dv)),
+                mu0=g.standard_normal((dk, dv)))
+
+
+def mobius_matrix(a, p, Lam):
+    """Predict (variance a^2/l + p) then add Lam, as a 2x2 fractional-linear map
+    l -> ((1 + Lam p) l + Lam a^2) / (p l + a^2)   (KLA Metodologia 2)."""
+    return np.array([[1.0 + Lam * p, Lam * a * a], [p, a * a]])
+
+
+def _apply(M, lam0):
+    return (M[0, 0] * lam0 + M[0, 1]) / (M[1, 0] * lam0 + M[1, 1])
+
+
+def _compose(Ms, rng):
+    """Product M_n ... M_1 in a random bracketing (later factors on the left)."""
+    items = list(Ms)
+    while len(items) > 1:
+        i = int(rng.integers(0, len(items) - 1))
+        items[i:i + 2] = [items[i + 1] @ items[i]]
+    return items[0]
+
+
+def pin_iso_mobius(lib):
+    """P-7.  Mobius maps compose associatively (KLA Metodologia 2): lambda_t
+    from the oracle's predict/update equals the composed matrix product applied
+    to lambda_0, in any bracketing.  det M_t = a_t^2 > 0 and every entry is
+    positive, so lambda_t > 0."""
+    c = iso_case(T=40)
+    res = oracle.iso_head(c["a"], c["p"], c["Lam"], c["lambda0"], lib=lib)
+    rng = np.random.default_rng(0)
+    Ms = [mobius_matrix(c["a"][t], c["p"][t], c["Lam"][t]) for t in range(40)]
+    for t in range(1, 41):
+        P = _compose(Ms[:t], rng)
+        P = P / np.max(P)  # projective scale does not change the map
+        _close(res["lambda"][t - 1], _apply(P, c["lambda0"]), rtol=1e-12, what=f"lambda_{t}")
+        assert abs(np.linalg.det(Ms[t - 1]) - c["a"][t - 1] ** 2) < 1e-12
+    assert np.all(res["lambda"] > 0)
+
+
+def pin_iso_scalar_kalman(lib):
+    """P-8.  d_k = d_v = 1 with k = q = 1: the oracle is a scalar Kalman filter
+    observing y_t = v_t with noise variance 1/Lambda_t.  Compare with the
+    covariance-form textbook filter:
+      P- = a^2 P + p;  K = P- / (P- + 1/Lambda);  m = a m + K (y - a m);
+      P = (1 - K) P-;  then lambda_t = 1/P and o_t = m."""
+    c = iso_case(seed=17, T=25, dk=1, dv=1)
+    ones = np.ones((25, 1))
+    res = oracle.iso_head(c["a"], c["p"], c["Lam"], c["lambda0"], q=ones, k=ones,
+                          v=c["v"], mu0=np.array([[0.3]]), lib=lib)
+    P, m = 1.0 / c["lambda0"], 0.3
+    for t in range(25):
+        a, p, L, y = c["a"][t], c["p"][t], c["Lam"][t], c["v"][t, 0]
+        Pm = a * a * P + p
+        K = Pm / (Pm + 1.0 / L)
+        m = a * m + K * (y - a * m)
+        P = (1.0 - K) * Pm
+        _close(res["lambda"][t], 1.0 / P, rtol=1e-12, what=f"lambda_{t}")
+        _close(res["o"][t, 0], m, rtol=1e-12, what=f"m_{t}")
+
+
+def pin_iso_fixed_point(lib):
+    """P-9.  Constant (a, p, Lambda): lambda_t converges to the positive root of
+    p l^2 + (a^2 - 1 - Lambda p) l - Lambda a^2 = 0 (steady-state scalar
+    Riccati).  p = 0 reduces to the affine l_t = l_{t-1} / a^2 + Lambda, and
+    a = 1, p = 0 to l_t = l_0 + t Lambda."""
+    for a, p, L in [(0.8, 0.3, 1.2), (0.95, 2.0, 0.05), (0.3, 0.01, 3.0)]:
+        T = 400
+        res = oracle.iso_head(np.full(T, a), np.full(T, p), np.full(T, L), 1.0, lib=lib)
+        b = a * a - 1.0 - L * p
+        star = (-b + np.sqrt(b * b + 4 * p * L * a * a)) / (2 * p)
+        _close(res["lambda"][-1], star, rtol=1e-12, what="fixed point")
+    T = 12
+    res = oracle.iso_head(np.full(T, 0.9), np.zeros(T), np.full(T, 0.5), 2.0, lib=lib)
+    lam, ref = 2.0, []
+    for _ in range(T):
+        lam = lam / 0.81 + 0.5
+        ref.append(lam)
+    _close(res["lambda"], ref, rtol=1e-13, what="p=0 affine")
+    res = oracle.iso_head(np.ones(T), np.zeros(T), np.full(T, 0.25), 2.0, lib=lib)
+    _close(res["lambda"], 2.0 + 0.25 * np.arange(1, T + 1), rtol=1e-14, what="a=1,p=0")
+
+
+def pin_iso_mean_closed_form(lib):
+    """P-10.  KLA Metodologia 2-3: with the precisions known, the mean is the
+    affine recurrence mu_t = F_t mu_{t-1} + G_t k_t v_t^T, forget gate
+    F_t = a_t lambda^-_t / lambda_t, write gate G_t = Lambda_t / lambda_t,
+    where lambda^-_t = lambda_{t-1} / (a_t^2 + p_t lambda_{t-1}).  Unrolled:
+    mu_t = (prod F) mu_0 + sum_s (prod_{r>s} F_r) G_s k_s v_s^T.  The
+    precisions here come from Mobius products, not from the oracle."""
+    c = iso_case(seed=29, T=9, dk=3, dv=4)
+    T = 9
+    res = oracle.iso_head(c["a"], c["p"], c["Lam"], c["lambda0"], q=c["q"], k=c["k"],
+                          v=c["v"], mu0=c["mu0"], lib=lib)
+    lam = [c["lambda0"]]
+    P = np.eye(2)
+    for t in range(T):
+        P = mobius_matrix(c["a"][t], c["p"][t], c["Lam"][t]) @ P
+        lam.append(_apply(P, c["lambda0"]))
+    lam_pred = [lam[t] / (c["a"][t] ** 2 + c["p"][t] * lam[t]) for t in range(T)]
+    F = np.array([c["a"][t] * lam_pred[t] / lam[t + 1] for t in range(T)])
+    G = np.array([c["Lam"][t] / lam[t + 1] for t in range(T)])
+    assert np.all((F > 0) & (F < c["a"])) and np.all((G > 0) & (G <= 1))
+    for t in range(1, T + 1):
+        mu = np.prod(F[:t]) * c["mu0"]
+        for s in range(1, t + 1):
+            mu = mu + np.prod(F[s:t]) * G[s - 1] * np.outer(c["k"][s - 1], c["v"][s - 1])
+        _close(res["o"][t - 1], mu.T @ c["q"][t - 1], rtol=1e-12, what=f"o_{t}")
+        if t == T:
+            _close(res["mu_T"], mu, rtol=1e-12, what="mu_T")
+
+
+ISO_PINS = [pin_iso_mobius, pin_iso_scalar_kalman, pin_iso_fixed_point, pin_iso_mean_closed_form]
+ALL_PINS = DIAG_PINS + ISO_PINS

@@ -1,0 +1,44 @@
+"""The pins catch plausible mistakes: each mutant is a copy of the oracle with
+one planted error (a dropped term, a wrong sign, a wrong operand or index),
+built on the CPU; at least one pin must fail on every mutant."""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins as pins
+
+MUTANTS = {
+    "prior_term_dropped": ("(1.0 - alpha) * I_prior", "0.0 * I_prior"),
+    "prior_sign": ("(1.0 - alpha) * I_prior", "(1.0 + alpha) * I_prior"),
+    "key_not_squared": ("bt[i] * kt[j] * kt[j]", "bt[i] * kt[j]"),
+    "mean_not_decayed": ("alpha * (I_old / I_new) * mu[e]", "(I_old / I_new) * mu[e]"),
+    "mean_ratio_inverted": ("alpha * (I_old / I_new) * mu[e]", "alpha * (I_new / I_old) * mu[e]"),
+    "write_uses_query": ("bt[i] * vt[i] * kt[j]", "bt[i] * vt[i] * qt[j]"),
+    "write_drops_beta": ("bt[i] * vt[i] * kt[j]", "vt[i] * kt[j]"),
+    "forget_ignores_A": ("exp(-A * d[t])", "exp(-d[t])"),
+    "readout_transposed": ("qt[j] * mu[j * dv + i];\n                acc", "qt[j] * mu[(i * dk + j) % n];\n                acc"),
+    "iso_decay_not_squared": ("a[t] * a[t] / lambda + p[t]", "a[t] / lambda + p[t]"),
+    "iso_noise_dropped": ("a[t] * a[t] / lambda + p[t]", "a[t] * a[t] / lambda"),
+    "iso_mean_not_decayed": ("mean_pred = a[t] * mu[e]", "mean_pred = mu[e]"),
+    "iso_write_uses_query": ("Lam[t] * kt[j] * vt[i]", "Lam[t] * qt[j] * vt[i]"),
+    "iso_obs_precision_squared": ("lambda_pred + Lam[t];", "lambda_pred + Lam[t] * Lam[t];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    before, after = MUTANTS[name]
+    src = open(oracle._SRC).read()
+    assert src.count(before) >= 1, f"mutation site for {name} not found"
+    mutated = src.replace(before, after, 1)
+    path = tmp_path / "mutant.c"
+    path.write_text(mutated)
+    lib = oracle.load(oracle.build(src=str(path), out=str(tmp_path / f"lib_{name}.so")))
+    failures = 0
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, FloatingPointError, ValueError):
+            failures += 1
+    assert failures > 0, f"no pin caught mutant {name}"
