@@ -1,0 +1,60 @@
+// kdn_internal.h -- helpers shared by the libkdnscan translation units.
+// gfx950 (CDNA4) only: wave64, 64 KiB-per-workgroup static LDS limit lifted
+// to 160 KiB per CU, fp32 VALU without packed math.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/kdnscan.h"
+
+namespace kdn {
+
+constexpr int kWave = 64;
+constexpr int kNumCU = 256;  // MI355X compute units (8 XCDs x 32)
+
+// bf16 -> fp32 is exact: the bf16 bits are the top half of the float.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_at(const uint16_t* p, int64_t i) {
+    return __uint_as_float(static_cast<uint32_t>(p[i]) << 16);
+}
+
+// Raw hardware reciprocal (v_rcp_f32, about 1 ulp).
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// exp(x) through the hardware base-2 exponential.
+__device__ __forceinline__ float fast_exp(float x) {
+    return __builtin_amdgcn_exp2f(x * 1.4426950408889634f);
+}
+
+// Load one 16-byte vector of elements from global memory.
+__device__ __forceinline__ uint4 ld16(const void* p) {
+    return *reinterpret_cast<const uint4*>(p);
+}
+
+// Widen a 16-byte vector (8 bf16 or 4 f32) into floats; returns the count.
+template <bool BF16>
+__device__ __forceinline__ void widen(const uint4& u, float* out) {
+    if constexpr (BF16) {
+        out[0] = bf16_lo(u.x); out[1] = bf16_hi(u.x);
+        out[2] = bf16_lo(u.y); out[3] = bf16_hi(u.y);
+        out[4] = bf16_lo(u.z); out[5] = bf16_hi(u.z);
+        out[6] = bf16_lo(u.w); out[7] = bf16_hi(u.w);
+    } else {
+        out[0] = __uint_as_float(u.x); out[1] = __uint_as_float(u.y);
+        out[2] = __uint_as_float(u.z); out[3] = __uint_as_float(u.w);
+    }
+}
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool head_size_ok(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128; }
+
+inline int launch_status() {
+    return hipGetLastError() == hipSuccess ? KDN_OK : KDN_EHIP;
+}
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace kdn

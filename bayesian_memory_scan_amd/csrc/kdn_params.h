@@ -1,0 +1,68 @@
+// kdn_params.h -- kernel parameter blocks and launcher entry points shared
+// between the C-ABI layer and the kernel translation units.
+#pragma once
+
+#include "kdn_internal.h"
+
+namespace kdn {
+
+// Segmented scan over a d_k x d_v state per head: the diagonal-precision scan,
+// or the gated mean of the isotropic filter (F, G set, beta/d unused).
+struct DiagParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;   // diagonal: beta [BH,T,dv]
+    const void* d;      // diagonal: d [BH,T]
+    const float* F;     // isotropic: forget gate F_t [BH,T]
+    const float* G;     // isotropic: write gate G_t [BH,T]
+    const float* A;
+    const float* I0;
+    const float* mu0;
+    float* o;
+    float* I_T;
+    float* mu_T;
+    float* comp;   // [BH][S][2][dk][dv]: segment composites, then carry-in states
+    float* gdec;   // [BH][S]: decay product of each segment
+    int64_t H;
+    int64_t T;
+    int64_t dv;
+    float I_prior;
+    int32_t S;
+    int32_t nchunks;
+};
+
+struct DecodeParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const void* d;
+    const float* A;
+    float* I;
+    float* mu;
+    float* o;
+    int64_t H;
+    float I_prior;
+};
+
+struct MobParams {
+    const float* a;
+    const float* p;
+    const float* Lam;
+    const float* lambda0;
+    float* lambda_out;
+    float* F;        // [BH,T] forget gates (NULL: precision path only)
+    float* G;        // [BH,T] write gates
+    float* blk;      // [BH][nblk][4] block composites
+    int64_t T;
+    int32_t nblk;
+};
+
+int diag_chunk();
+int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, bool iso, hipStream_t st);
+int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
+int mob_block();
+int mobius_launch(const MobParams& p, int64_t BH, hipStream_t st);
+
+}  // namespace kdn

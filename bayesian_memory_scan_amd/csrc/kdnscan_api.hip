@@ -1,0 +1,250 @@
+// kdnscan_api.hip -- the C ABI: argument validation, planning, workspace
+// layout and kernel dispatch.  Validation completes before any HIP call.
+#include "kdn_params.h"
+
+#include <atomic>
+#include <cmath>
+
+namespace {
+
+using namespace kdn;
+
+std::atomic<int32_t> g_segments_override{0};
+
+constexpr int64_t kMaxGrid = 2147483647;  // hardware limit on grid.x
+constexpr int32_t kMaxSegments = 64;
+
+struct Plan {
+    int32_t chunk;
+    int32_t nchunks;
+    int32_t S;
+};
+
+// Chunking and segment count of a (possibly isotropic) segmented scan.
+Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
+    Plan pl;
+    pl.chunk = diag_chunk();
+    pl.nchunks = static_cast<int32_t>((T + pl.chunk - 1) / pl.chunk);
+    const int64_t ci = dv < 64 ? dv : 64;
+    const int64_t units = BH * (dv / ci);
+    int64_t S = 1;
+    const int32_t ov = g_segments_override.load();
+    if (ov > 0) {
+        S = ov;
+    } else if (units > 0 && units < kNumCU && pl.nchunks >= 16) {
+        S = (kNumCU + units - 1) / units;
+        if (S > pl.nchunks / 8) S = pl.nchunks / 8;
+    }
+    if (S > kMaxSegments) S = kMaxSegments;
+    if (S > pl.nchunks) S = pl.nchunks;
+    if (S < 1) S = 1;
+    pl.S = static_cast<int32_t>(S);
+    return pl;
+}
+
+size_t scan_workspace_bytes(int64_t BH, int64_t dk, int64_t dv, const Plan& pl) {
+    if (pl.S <= 1) return 0;
+    const size_t comp = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * dk * dv, 256);
+    const size_t gdec = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S, 256);
+    return comp + gdec;
+}
+
+bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
+
+bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+bool ok_opt(const void* p) { return p == nullptr || aligned16(p); }
+
+// Workspace protocol; returns KDN_OK to proceed, 1 for "query answered".
+int workspace_check(void* workspace, size_t* workspace_bytes, size_t need) {
+    if (workspace == nullptr && workspace_bytes != nullptr) {
+        *workspace_bytes = need;
+        return 1;
+    }
+    if (need == 0) return KDN_OK;
+    if (workspace == nullptr || workspace_bytes == nullptr || *workspace_bytes < need) {
+        if (workspace_bytes) *workspace_bytes = need;
+        return KDN_EWORKSPACE;
+    }
+    if (!aligned16(workspace)) return KDN_EINVAL;
+    return KDN_OK;
+}
+
+// Guard against int64 overflow of element counts: B*H*T*D must stay < 2^62.
+bool sizes_fit(int64_t B, int64_t H, int64_t T, int64_t D) {
+    const double n = static_cast<double>(B) * static_cast<double>(H) * static_cast<double>(T > 0 ? T : 1) *
+                     static_cast<double>(D);
+    return n < 4.0e18;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kdn_status_string(int status) {
+    switch (status) {
+        case KDN_OK: return "ok";
+        case KDN_EINVAL: return "invalid argument (size, NULL pointer, alignment or I_prior)";
+        case KDN_EUNSUPPORTED: return "unsupported configuration (d_k and d_v must be 16, 32, 64 or 128)";
+        case KDN_EWORKSPACE: return "workspace missing or too small";
+        case KDN_EHIP: return "HIP launch failed";
+        default: return "unknown status";
+    }
+}
+
+int32_t kdn_set_diag_segments(int32_t segments) {
+    return g_segments_override.exchange(segments > 0 ? segments : 0);
+}
+
+int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                  int32_t* chunk, int32_t* segments, int64_t* seg_bounds, int32_t max_segments) {
+    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
+    const Plan pl = plan_scan(B * H, T, d_v);
+    if (chunk) *chunk = pl.chunk;
+    if (segments) *segments = pl.S;
+    if (seg_bounds) {
+        if (max_segments < pl.S) return KDN_EINVAL;
+        for (int32_t s = 0; s <= pl.S; ++s) {
+            const int64_t c = static_cast<int64_t>(s) * pl.nchunks / pl.S;
+            const int64_t t = c * pl.chunk;
+            seg_bounds[s] = t < T ? t : T;
+        }
+    }
+    return KDN_OK;
+}
+
+int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                      kdn_dtype in_dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* beta, const void* d,
+                      const float* A, float I_prior,
+                      const float* I0, const float* mu0,
+                      float* o, float* I_T, float* mu_T,
+                      void* workspace, size_t* workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    if (!finite_positive(I_prior)) return KDN_EINVAL;
+    if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
+    const int64_t BH = B * H;
+    if (BH > 0 && !ok_ptr(A)) return KDN_EINVAL;
+    if (BH > 0 && T > 0) {
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(d) || !ok_ptr(o))
+            return KDN_EINVAL;
+    }
+    if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
+
+    const Plan pl = plan_scan(BH, T, d_v);
+    const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
+    if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
+    const size_t need = scan_workspace_bytes(BH, d_k, d_v, pl);
+    const int wc = workspace_check(workspace, workspace_bytes, need);
+    if (wc == 1) return KDN_OK;
+    if (wc != KDN_OK) return wc;
+    if (BH == 0) return KDN_OK;
+
+    DiagParams p{};
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
+    p.A = A; p.I0 = I0; p.mu0 = mu0;
+    p.o = o; p.I_T = I_T; p.mu_T = mu_T;
+    if (pl.S > 1) {
+        char* ws = static_cast<char*>(workspace);
+        p.comp = reinterpret_cast<float*>(ws);
+        p.gdec = reinterpret_cast<float*>(ws + align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * d_k * d_v, 256));
+    }
+    p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
+    p.S = pl.S; p.nchunks = pl.nchunks;
+    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, false, static_cast<hipStream_t>(stream));
+}
+
+int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
+                              const float* a, const float* p, const float* Lambda,
+                              const float* lambda0, float* lambda_out,
+                              int64_t d_k, int64_t d_v,
+                              const float* q, const float* k, const float* v,
+                              const float* mu0, float* o, float* mu_T,
+                              void* workspace, size_t* workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    const bool mean = !(d_k == 0 && d_v == 0);
+    if (mean && (!head_size_ok(d_k) || !head_size_ok(d_v))) return KDN_EUNSUPPORTED;
+    if (!sizes_fit(B, H, T, mean ? (d_k > d_v ? d_k : d_v) : 1)) return KDN_EINVAL;
+    const int64_t BH = B * H;
+    if (BH > 0 && T > 0) {
+        if (!ok_ptr(a) || !ok_ptr(p) || !ok_ptr(Lambda)) return KDN_EINVAL;
+        if (mean && (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(o))) return KDN_EINVAL;
+    }
+    if (!ok_opt(lambda0) || !ok_opt(lambda_out) || !ok_opt(mu0) || !ok_opt(mu_T)) return KDN_EINVAL;
+
+    const int64_t blk = mob_block();
+    const int64_t nblk = (T + blk - 1) / blk;
+    if (BH * nblk > kMaxGrid) return KDN_EINVAL;
+    const size_t b_blk = align_up(sizeof(float) * static_cast<size_t>(BH) * nblk * 4, 256);
+    size_t need = (BH > 0 && T > 0) ? b_blk : 0;
+    Plan pl{};
+    size_t b_gate = 0;
+    if (mean) {
+        pl = plan_scan(BH, T, d_v);
+        const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
+        if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
+        b_gate = align_up(sizeof(float) * static_cast<size_t>(BH) * T, 256);
+        need += 2 * b_gate + scan_workspace_bytes(BH, d_k, d_v, pl);
+    }
+    const int wc = workspace_check(workspace, workspace_bytes, need);
+    if (wc == 1) return KDN_OK;
+    if (wc != KDN_OK) return wc;
+    if (BH == 0) return KDN_OK;
+
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    MobParams mp{};
+    mp.a = a; mp.p = p; mp.Lam = Lambda; mp.lambda0 = lambda0; mp.lambda_out = lambda_out;
+    mp.T = T; mp.nblk = static_cast<int32_t>(nblk);
+    if (T > 0) {
+        mp.blk = reinterpret_cast<float*>(ws);
+        ws += b_blk;
+    }
+    if (mean && T > 0) {
+        mp.F = reinterpret_cast<float*>(ws);
+        mp.G = reinterpret_cast<float*>(ws + b_gate);
+        ws += 2 * b_gate;
+    }
+    int rc = mobius_launch(mp, BH, st);
+    if (rc != KDN_OK || !mean) return rc;
+
+    DiagParams dp{};
+    dp.q = q; dp.k = k; dp.v = v;
+    dp.F = mp.F; dp.G = mp.G;
+    dp.mu0 = mu0; dp.o = o; dp.mu_T = mu_T;
+    if (pl.S > 1) {
+        dp.comp = reinterpret_cast<float*>(ws);
+        dp.gdec = reinterpret_cast<float*>(ws + align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * d_k * d_v, 256));
+    }
+    dp.H = H; dp.T = T; dp.dv = d_v; dp.I_prior = 1.0f;
+    dp.S = pl.S; dp.nchunks = pl.nchunks;
+    return diag_scan_launch(dp, B, d_k, false, true, st);
+}
+
+int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in_dtype,
+                    const void* q, const void* k, const void* v,
+                    const void* beta, const void* d,
+                    const float* A, float I_prior,
+                    float* I, float* mu, float* o, void* stream) {
+    if (B < 0 || H < 0) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    if (!finite_positive(I_prior)) return KDN_EINVAL;
+    if (!sizes_fit(B, H, 1, d_k * d_v)) return KDN_EINVAL;
+    const int64_t BH = B * H;
+    if (BH > kMaxGrid) return KDN_EINVAL;
+    if (BH == 0) return KDN_OK;
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(d) || !ok_ptr(A) ||
+        !ok_ptr(I) || !ok_ptr(mu) || !ok_ptr(o))
+        return KDN_EINVAL;
+    DecodeParams p{};
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d; p.A = A;
+    p.I = I; p.mu = mu; p.o = o; p.H = H; p.I_prior = I_prior;
+    return decode_launch(p, B, d_k, d_v, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+#!/usr/bin/env python3
+"""Benchmark of the diagonal-precision scan forward on one MI355X.
+
+Default workload: B=8, H=16, T=2048, d_k=d_v=128, bf16 inputs, fp32 state
+and output (a 760M-class layer shape).  A step is one kdn_diag_scan_fwd call
+over that batch, inputs already resident in HBM.  Prints one JSON line with
+tokens/s (tokens = B*T positions, all heads), the roofline of the dominant
+kernel (timed live with HIP events on the launch stream) and the fp64 CPU
+oracle timed on a bounded sample of the same workload.
+
+Other workloads (--workload) print the same fields for the decode step and
+the isotropic scan; they are not the headline line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
+# fp32 VALU ceiling without packed math: 256 CU x 4 SIMD x 16 lanes x 2 flop x 2.4 GHz
+PEAK_FP32_VALU_TFLOPS = 78.6
+DIAG_FLOPS_PER_ENTRY_STEP = 11   # I update 4, eta update 3, reciprocal+multiply 2, read-out 2
+ISO_FLOPS_PER_ENTRY_STEP = 5     # mean update 3, read-out 2
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="diag_b8h16t2048d128_bf16")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="target CPU time of the oracle sample")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    return ap.parse_args()
+
+
+def _traffic(kernel_file: str, profile_json: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None if the
+    kernel source changed since they were taken."""
+    path = os.path.join(ROOT, "profiles", profile_json)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "bayesian_memory_scan_amd", "csrc", kernel_file), "rb").read()
+    if rec.get("source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def _up(x, torch, dev):
+    import numpy as np
+    x = np.ascontiguousarray(x)
+    return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
+
+
+def _time_steps(torch, step, steps, warmup):
+    """Warmup, then `steps` timed steps; wall clock plus per-step HIP events on
+    the current stream (the stream every launch goes to)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        e0.record()
+        step()
+        e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return wall, sum(per) / len(per), min(per)
+
+
+def _cpu_threads():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_baseline_diag(inp, spec, target_s):
+    """fp64 oracle on whole heads of the same workload; tokens/s scaled to all H heads."""
+    import oracle
+    threads = _cpu_threads()
+    heads_all = [(b, h) for b in range(spec.B) for h in range(spec.H)]
+    # calibrate on one head, then size the sample to about target_s of wall time
+    with oracle.Timer() as t1:
+        oracle.diag_scan(inp, heads=heads_all[:1], threads=1)
+    n = max(1, min(len(heads_all), int(target_s / max(t1.seconds, 1e-3) * threads)))
+    heads = heads_all[:n]
+    with oracle.Timer() as t:
+        oracle.diag_scan(inp, heads=heads, threads=threads)
+    T = spec.prefix + spec.T
+    tokens = n * T / spec.H
+    return {"value": tokens / t.seconds, "unit": "tokens/s", "cores": min(threads, n),
+            "kind": "oracle",
+            "sample": f"{n} of {len(heads_all)} heads x {T} tokens, fp64 sequential oracle, "
+                      f"{t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
+
+
+def cpu_baseline_iso(inp, spec, target_s):
+    import oracle
+    threads = _cpu_threads()
+    heads_all = [(b, h) for b in range(spec.B) for h in range(spec.H)]
+    with oracle.Timer() as t1:
+        oracle.iso_scan(inp, heads=heads_all[:1], threads=1)
+    n = max(1, min(len(heads_all), int(target_s / max(t1.seconds, 1e-3) * threads)))
+    with oracle.Timer() as t:
+        oracle.iso_scan(inp, heads=heads_all[:n], threads=threads)
+    return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
+            "cores": min(threads, n), "kind": "oracle",
+            "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle, "
+                      f"{t.seconds:.1f} s wall"}
+
+
+def main():
+    a = _args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {a.gpus}); the scans shard over "
+              "(batch, head) with no communication, so there is no multi-GPU step to time.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bayesian_memory_scan_amd import kdnscan as kdn
+    from bayesian_memory_scan_amd import synth
+
+    dev = torch.device("cuda:0")
+    spec = synth.workload(a.workload)
+    out = {"metric": "tokens/s per MI355X, diag-precision scan fwd; % of HBM/FP32 roofline",
+           "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
+
+    if a.workload.startswith("diag_"):
+        inp = synth.diag_inputs(spec)
+        x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "d", "A")}
+        o = torch.empty((spec.B, spec.H, spec.T, spec.d_v), dtype=torch.float32, device=dev)
+        st = torch.empty((2, spec.B, spec.H, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
+        _, S, _ = kdn.kdn_diag_plan(spec.B, spec.H, spec.T, spec.d_k, spec.d_v)
+
+        def step():
+            kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], x["A"],
+                                  spec.I_prior, o=o, I_T=st[0], mu_T=st[1])
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tokens = spec.B * spec.T
+        flops = DIAG_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        out.update({
+            "value": tokens / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "T": spec.T,
+                       "d_k": spec.d_k, "d_v": spec.d_v, "inputs": spec.dtype, "state": "fp32",
+                       "segments": S, "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),
+                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min,
+                         "kernels_per_step": 1 if S == 1 else 3},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+    elif a.workload.startswith("decode_"):
+        inp = synth.diag_inputs(spec)
+        P = spec.prefix
+        x = {n: _up(inp[n][:, :, :P], torch, dev) for n in ("q", "k", "v", "beta", "d")}
+        A = _up(inp["A"], torch, dev)
+        _, I, mu = kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], A,
+                                         spec.I_prior)
+        del x
+        y = {n: _up(inp[n][:, :, P], torch, dev) for n in ("q", "k", "v", "beta", "d")}
+        o = torch.empty((spec.B, spec.H, spec.d_v), dtype=torch.float32, device=dev)
+
+        def step():
+            kdn.kdn_decode_step(y["q"], y["k"], y["v"], y["beta"], y["d"], A, spec.I_prior,
+                                I, mu, o=o)
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        BH = spec.B * spec.H
+        nbytes = BH * (4 * 4 * spec.d_k * spec.d_v + 2 * (2 * spec.d_k + 2 * spec.d_v + 1)
+                       + 4 * spec.d_v)
+        achieved = nbytes / (ev_ms * 1e-3) / 1e9
+        out.update({
+            "metric": "tokens/s per MI355X, diag-precision decode step; % of HBM roofline",
+            "value": spec.B / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "d_k": spec.d_k,
+                       "d_v": spec.d_v, "state": "fp32, in place", "prefix": P},
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                         "traffic": _traffic("decode.hip", f"traffic_{spec.name}.json"),
+                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_diag(inp, spec.with_(B=8), a.cpu_seconds)
+    elif a.workload.startswith("iso_"):
+        inp = synth.iso_inputs(spec)
+        x = {n: _up(inp[n], torch, dev) for n in ("a", "p", "Lambda", "q", "k", "v", "lambda0")}
+
+        def step():
+            kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"], x["q"],
+                                          x["k"], x["v"])
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        flops = ISO_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        out.update({
+            "metric": "tokens/s per MI355X, isotropic Mobius scan + gated mean scan",
+            "value": spec.B * spec.T / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "T": spec.T,
+                       "d_k": spec.d_k, "d_v": spec.d_v, "inputs": "fp32"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": None, "launch_ms_avg": ev_ms, "launch_ms_min": ev_min,
+                         "note": "whole step (all kernels) timed by events"},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_iso(inp, spec, a.cpu_seconds)
+    else:
+        raise SystemExit(f"unknown workload {a.workload}")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

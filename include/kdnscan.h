@@ -1,0 +1,160 @@
+/*
+ * kdnscan.h -- C ABI of libkdnscan: precision-tracking associative-memory
+ * scans on AMD Instinct MI355X (gfx950).
+ *
+ * Sources of the operations (page title, section):
+ *   [Palimpsa] "Learning to Remember, Learn, and Forget in Attention-Based
+ *              Models" (technical summary), Metodologia 1: forget gate
+ *              alpha_t = exp(-A d_t); Metodologia 2: the diagonal precision
+ *              ("importance") update of I_t and the precision-weighted mean
+ *              update of mu_t.
+ *   [KLA]      "Riassunto Tecnico: Kalman Linear Attention (KLA)",
+ *              Metodologia 1: OU decay and process noise, observation
+ *              precision, read-out of the posterior mean by the query;
+ *              Metodologia 2: the precision update is a Mobius
+ *              (fractional-linear) map, composed by an associative prefix
+ *              scan, and the mean update is affine once precisions are known;
+ *              Metodologia 3: forget and write gates from precision ratios.
+ *   [KDN]      "Kalman Delta Networks" abstract: Diagonal and Isotropic KDN,
+ *              Mobius uncertainty recurrences, constant-memory decoding.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are contiguous, row-major, and live in device memory
+ *     (hipMalloc'd or torch CUDA tensors); the caller owns every buffer.
+ *     Scalars and workspace_bytes are host values.
+ *   - The memory state of one head is a d_k x d_v matrix: entry [j][i]
+ *     couples key channel j with value channel i.  Read-out:
+ *     o_t[i] = sum_j q_t[j] mu_t[j][i], taken after token t's update.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t passed as void*;
+ *     NULL = the default stream) and return without synchronising.  The
+ *     library never allocates device memory.
+ *   - Arguments are validated before any HIP call; a rejected call touches
+ *     no memory.  Return values: KDN_OK or a negative KDN_E* code (see
+ *     kdn_status_string).  Values inside tensors are not checked: they are
+ *     preconditions (A > 0, d >= 0, beta >= 0, I0 > 0, a > 0, p >= 0,
+ *     Lambda >= 0, lambda0 > 0).  Under them every precision stays > 0.
+ *   - Supported head sizes: d_k, d_v in {16, 32, 64, 128}; other values
+ *     return KDN_EUNSUPPORTED.  Every pointer must be 16-byte aligned.
+ *
+ * Workspace protocol (entry points that take one)
+ *   - workspace == NULL and workspace_bytes != NULL: write the number of
+ *     bytes needed to *workspace_bytes and return KDN_OK without launching.
+ *   - otherwise the call runs; if it needs workspace and workspace is NULL
+ *     or *workspace_bytes is smaller than needed, it returns KDN_EWORKSPACE
+ *     (writing the needed size when workspace_bytes != NULL).
+ */
+#ifndef KDNSCAN_H
+#define KDNSCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDN_F32 = 0, KDN_BF16 = 1 } kdn_dtype;
+
+enum {
+    KDN_OK = 0,
+    KDN_EINVAL = -1,        /* bad size, NULL required pointer, misalignment, I_prior <= 0 */
+    KDN_EUNSUPPORTED = -2,  /* valid but not implemented (head size outside the list) */
+    KDN_EWORKSPACE = -3,    /* workspace missing or too small */
+    KDN_EHIP = -4           /* a HIP launch failed */
+};
+
+/*
+ * Diagonal-precision scan, forward [Palimpsa Metodologia 1-2; KLA Metodologia 1].
+ * For every head (b, h) and token t = 0..T-1, with every entry [j][i]:
+ *   alpha_t = exp(-A[h] d_t)
+ *   I_t  = alpha_t I_{t-1} + (1 - alpha_t) I_prior + beta_t[i] k_t[j]^2
+ *   mu_t = alpha_t (I_{t-1} / I_t) mu_{t-1} + beta_t[i] v_t[i] k_t[j] / I_t
+ *   o_t[i] = sum_j q_t[j] mu_t[j][i]
+ * Inputs (in_dtype: KDN_F32 = float, KDN_BF16 = bfloat16):
+ *   q, k [B,H,T,d_k];  v, beta [B,H,T,d_v];  d [B,H,T].
+ *   A [H] float (forget rate per head);  I_prior > 0 (scalar prior precision).
+ *   I0, mu0 [B,H,d_k,d_v] float: starting state; NULL -> I_prior and 0.
+ * Outputs (float): o [B,H,T,d_v]; I_T, mu_T [B,H,d_k,d_v] final state, or
+ *   NULL to skip.  I_T may alias I0 and mu_T may alias mu0 (continuation);
+ *   no other aliasing between inputs and outputs is allowed.
+ * Long sequences are split into segments whose composites are carried in
+ * order; the workspace holds them (the query returns 0 when not needed).
+ */
+int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                      kdn_dtype in_dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* beta, const void* d,
+                      const float* A, float I_prior,
+                      const float* I0, const float* mu0,
+                      float* o, float* I_T, float* mu_T,
+                      void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Isotropic scalar-precision filter [KDN abstract, Isotropic KDN;
+ * KLA Metodologia 1-3].  Per head, per token:
+ *   lambda_t = M_t(lambda_{t-1}),  M_t = [[1 + Lambda_t p_t, Lambda_t a_t^2],
+ *                                         [p_t,              a_t^2          ]]
+ *   acting as l -> (m11 l + m12) / (m21 l + m22): predict (the mean decays
+ *   by a_t, process noise p_t) then add observation precision Lambda_t.
+ *   The maps are composed by an associative prefix scan.  Then the gates
+ *   lambda^-_t = lambda_{t-1} / (a_t^2 + p_t lambda_{t-1}),
+ *   F_t = a_t lambda^-_t / lambda_t,  G_t = Lambda_t / lambda_t
+ *   drive the affine mean scan mu_t = F_t mu_{t-1} + G_t k_t v_t^T with
+ *   read-out o_t[i] = sum_j q_t[j] mu_t[j][i].
+ * Inputs (float): a, p, Lambda [B,H,T]; lambda0 [B,H] or NULL (-> 1).
+ *   d_k == 0 && d_v == 0 runs the precision path only (q, k, v, mu0, o,
+ *   mu_T ignored).  Otherwise q, k [B,H,T,d_k], v [B,H,T,d_v]; mu0
+ *   [B,H,d_k,d_v] or NULL (-> 0).
+ * Outputs (float): lambda_out [B,H,T] or NULL; o [B,H,T,d_v] (required for
+ *   the mean path); mu_T [B,H,d_k,d_v] or NULL.
+ * Workspace: per-block Mobius composites, the gates and per-chunk mean
+ *   composites.
+ */
+int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
+                              const float* a, const float* p, const float* Lambda,
+                              const float* lambda0, float* lambda_out,
+                              int64_t d_k, int64_t d_v,
+                              const float* q, const float* k, const float* v,
+                              const float* mu0, float* o, float* mu_T,
+                              void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * One-token decode of the diagonal recurrence [Palimpsa Metodologia 1-2;
+ * constant-memory decoding, KDN abstract].  The same update as
+ * kdn_diag_scan_fwd for a single token, applied in place:
+ *   q, k [B,H,d_k]; v, beta [B,H,d_v]; d [B,H] (in_dtype);  A [H] float;
+ *   I, mu [B,H,d_k,d_v] float, read and overwritten with the new state;
+ *   o [B,H,d_v] float.
+ */
+int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in_dtype,
+                    const void* q, const void* k, const void* v,
+                    const void* beta, const void* d,
+                    const float* A, float I_prior,
+                    float* I, float* mu, float* o, void* stream);
+
+/*
+ * Plan of a diagonal scan (host only, no HIP call): the token chunk length
+ * staged per step, the number of sequence segments and their token bounds
+ * seg_bounds[0..S] (seg_bounds may be NULL; it must hold S+1 entries when
+ * given, S <= max_segments).  Segment s owns whole chunks
+ * [floor(s n / S), floor((s+1) n / S)) of the n = ceil(T / chunk) chunks.
+ */
+int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                  int32_t* chunk, int32_t* segments,
+                  int64_t* seg_bounds, int32_t max_segments);
+
+/*
+ * Process-wide override of the number of sequence segments used by
+ * kdn_diag_scan_fwd (0 restores the automatic choice).  For tests and
+ * tuning; not thread-safe against concurrent calls.  Returns the previous
+ * value.
+ */
+int32_t kdn_set_diag_segments(int32_t segments);
+
+/* Human-readable text of a status code; never NULL. */
+const char* kdn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDNSCAN_H */

@@ -1,0 +1,133 @@
+"""The C ABI on the CPU: symbols, argument validation, workspace protocol and
+the chunk/segment plan (bit-exact against the oracle's enumeration).  Every
+call here returns before any HIP call, so no GPU is needed."""
+import ctypes
+import subprocess
+
+import pytest
+
+import oracle
+
+kdn = pytest.importorskip("bayesian_memory_scan_amd.kdnscan")
+lib = kdn.lib
+
+FAKE = 0x10000  # a 16-byte aligned address that is never dereferenced
+MIS = FAKE + 4
+
+
+def test_exports_every_header_symbol():
+    names = kdn.header_functions()
+    assert {"kdn_diag_scan_fwd", "kdn_mobius_precision_scan", "kdn_decode_step",
+            "kdn_status_string"} <= set(names)
+    out = subprocess.run(["nm", "-D", "--defined-only", kdn.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for n in names:
+        assert n in exported, f"{n} declared in kdnscan.h but not exported"
+        assert hasattr(lib, n)
+
+
+def test_status_strings():
+    for code in (0, -1, -2, -3, -4, 7):
+        assert isinstance(kdn.kdn_status_string(code), str) and kdn.kdn_status_string(code)
+
+
+def _diag(B=1, H=1, T=8, dk=16, dv=16, dt=kdn.KDN_F32, q=FAKE, k=FAKE, v=FAKE, beta=FAKE, d=FAKE,
+          A=FAKE, I_prior=1.0, I0=None, mu0=None, o=FAKE, I_T=None, mu_T=None, ws=None,
+          nbytes=None):
+    nb = None if nbytes is None else ctypes.byref(nbytes)
+    return lib.kdn_diag_scan_fwd(B, H, T, dk, dv, dt, q, k, v, beta, d, A, I_prior, I0, mu0,
+                                 o, I_T, mu_T, ws, nb, None)
+
+
+def test_diag_validation():
+    n = ctypes.c_size_t(0)
+    q = dict(nbytes=n)  # query mode: validation then return, never a launch
+    assert _diag(**q) == kdn.KDN_OK
+    assert _diag(B=-1, **q) == kdn.KDN_EINVAL
+    assert _diag(T=-5, **q) == kdn.KDN_EINVAL
+    assert _diag(dk=24, **q) == kdn.KDN_EUNSUPPORTED
+    assert _diag(dv=256, **q) == kdn.KDN_EUNSUPPORTED
+    assert _diag(dt=7, **q) == kdn.KDN_EINVAL
+    assert _diag(I_prior=0.0, **q) == kdn.KDN_EINVAL
+    assert _diag(I_prior=float("nan"), **q) == kdn.KDN_EINVAL
+    assert _diag(I_prior=-1.0, **q) == kdn.KDN_EINVAL
+    for name in ("q", "k", "v", "beta", "d", "A", "o"):
+        assert _diag(**{name: None}, **q) == kdn.KDN_EINVAL, name
+        assert _diag(**{name: MIS}, **q) == kdn.KDN_EINVAL, name
+    for name in ("I0", "mu0", "I_T", "mu_T"):
+        assert _diag(**{name: MIS}, **q) == kdn.KDN_EINVAL, name
+    # empty batches need no input pointers
+    assert _diag(B=0, q=None, k=None, v=None, beta=None, d=None, A=None, o=None, **q) == kdn.KDN_OK
+    assert _diag(T=0, q=None, k=None, v=None, beta=None, d=None, o=None, **q) == kdn.KDN_OK
+
+
+def test_diag_workspace_protocol():
+    n = ctypes.c_size_t(12345)
+    assert _diag(B=8, H=16, T=2048, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
+    assert n.value == 0  # one segment: no workspace
+    n = ctypes.c_size_t(0)
+    assert _diag(B=2, H=16, T=16384, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
+    chunk, S, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
+    expect_comp = 4 * 2 * 16 * S * 2 * 128 * 128
+    assert n.value >= expect_comp and n.value % 256 == 0
+    need = n.value
+    # running with too little (or no) workspace is refused before any launch
+    small = ctypes.c_size_t(need - 1)
+    assert _diag(B=2, H=16, T=16384, dk=128, dv=128, ws=FAKE, nbytes=small) == kdn.KDN_EWORKSPACE
+    assert small.value == need
+    assert _diag(B=2, H=16, T=16384, dk=128, dv=128, ws=None, nbytes=None) == kdn.KDN_EWORKSPACE
+
+
+def test_mobius_validation_and_workspace():
+    n = ctypes.c_size_t(0)
+    nb = ctypes.byref(n)
+    call = lambda B=1, H=1, T=8, dk=0, dv=0, a=FAKE, p=FAKE, L=FAKE, q=FAKE, o=FAKE: \
+        lib.kdn_mobius_precision_scan(B, H, T, a, p, L, None, FAKE, dk, dv, q, q, q, None, o,
+                                      None, None, nb, None)
+    assert call() == kdn.KDN_OK and n.value > 0          # precision path: block composites
+    prec = n.value
+    assert call(dk=64, dv=64) == kdn.KDN_OK and n.value > prec  # + gates (+ segment carry)
+    assert call(dk=48, dv=64) == kdn.KDN_EUNSUPPORTED
+    assert call(B=-1) == kdn.KDN_EINVAL
+    assert call(a=None) == kdn.KDN_EINVAL
+    assert call(L=MIS) == kdn.KDN_EINVAL
+    assert call(dk=64, dv=64, q=None) == kdn.KDN_EINVAL
+    assert call(dk=64, dv=64, o=None) == kdn.KDN_EINVAL
+    assert call(T=0, a=None, p=None, L=None) == kdn.KDN_OK and n.value == 0
+
+
+def test_decode_validation():
+    call = lambda B=1, H=1, dk=16, dv=16, dt=kdn.KDN_BF16, I_prior=1.0, I=FAKE, q=FAKE: \
+        lib.kdn_decode_step(B, H, dk, dv, dt, q, FAKE, FAKE, FAKE, FAKE, FAKE, I_prior, I, FAKE,
+                            FAKE, None)
+    assert call(B=-1) == kdn.KDN_EINVAL
+    assert call(dk=8) == kdn.KDN_EUNSUPPORTED
+    assert call(I_prior=0.0) == kdn.KDN_EINVAL
+    assert call(I=None) == kdn.KDN_EINVAL
+    assert call(q=MIS) == kdn.KDN_EINVAL
+    assert call(dt=3) == kdn.KDN_EINVAL
+    assert call(B=0, I=None, q=None) == kdn.KDN_OK
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 64, 100, 2048, 16383, 16384, 65536])
+@pytest.mark.parametrize("S", [0, 1, 2, 3, 4, 7])
+def test_plan_matches_oracle_enumeration(T, S):
+    """P-11: the library's chunk and segment bounds equal the oracle's
+    enumeration from the definition, bit for bit."""
+    prev = kdn.kdn_set_diag_segments(S)
+    try:
+        chunk, segs, bounds = kdn.kdn_diag_plan(2, 16, T, 128, 128)
+    finally:
+        kdn.kdn_set_diag_segments(prev)
+    _, _, ref = oracle.plan(T, chunk, segs)
+    assert bounds == ref
+    if S:
+        assert segs == min(S, -(-T // chunk))
+
+
+def test_plan_auto_segments_fill_the_chip():
+    _, S1, _ = kdn.kdn_diag_plan(8, 16, 2048, 128, 128)
+    _, S2, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
+    _, S3, _ = kdn.kdn_diag_plan(1, 2, 64, 16, 16)
+    assert S1 == 1 and S2 == 4 and S3 == 1
