@@ -51,8 +51,15 @@ __device__ __forceinline__ void widen(const uint4& u, float* out) {
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool head_size_ok(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128; }
 
+// Records the error of the last failed launch (per thread) for
+// kdn_last_hip_error().
+void note_hip_error(hipError_t e);
+
 inline int launch_status() {
-    return hipGetLastError() == hipSuccess ? KDN_OK : KDN_EHIP;
+    const hipError_t e = hipGetLastError();
+    if (e == hipSuccess) return KDN_OK;
+    note_hip_error(e);
+    return KDN_EHIP;
 }
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

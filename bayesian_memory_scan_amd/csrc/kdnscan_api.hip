@@ -5,6 +5,13 @@
 #include <atomic>
 #include <cmath>
 
+namespace kdn {
+namespace {
+thread_local hipError_t g_last_error = hipSuccess;
+}
+void note_hip_error(hipError_t e) { g_last_error = e; }
+}  // namespace kdn
+
 namespace {
 
 using namespace kdn;
@@ -91,6 +98,10 @@ const char* kdn_status_string(int status) {
     }
 }
 
+const char* kdn_last_hip_error(void) {
+    return hipGetErrorString(g_last_error);
+}
+
 int32_t kdn_set_diag_segments(int32_t segments) {
     return g_segments_override.exchange(segments > 0 ? segments : 0);
 }
@@ -155,6 +166,7 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     }
     p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.S = pl.S; p.nchunks = pl.nchunks;
+    (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, false, static_cast<hipStream_t>(stream));
 }
 
@@ -209,6 +221,7 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
         mp.G = reinterpret_cast<float*>(ws + b_gate);
         ws += 2 * b_gate;
     }
+    (void)hipGetLastError();  // launch status below must reflect this call only
     int rc = mobius_launch(mp, BH, st);
     if (rc != KDN_OK || !mean) return rc;
 
@@ -244,6 +257,7 @@ int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in
     DecodeParams p{};
     p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d; p.A = A;
     p.I = I; p.mu = mu; p.o = o; p.H = H; p.I_prior = I_prior;
+    (void)hipGetLastError();  // launch status below must reflect this call only
     return decode_launch(p, B, d_k, d_v, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
 }
 

@@ -17,7 +17,8 @@ __all__ = [
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
     "KDN_F32", "KDN_BF16", "KdnError",
     "kdn_diag_scan_fwd", "kdn_mobius_precision_scan", "kdn_decode_step",
-    "kdn_diag_plan", "kdn_set_diag_segments", "kdn_status_string", "header_functions",
+    "kdn_diag_plan", "kdn_set_diag_segments", "kdn_status_string", "kdn_last_hip_error",
+    "header_functions",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -31,6 +32,14 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(
         f"{LIB_PATH} is missing: build it first (python -c 'import __graft_entry__ as g; g.build()' "
         "or python -m bayesian_memory_scan_amd._build). There is no CPU fallback.")
+
+# torch ships its own HIP runtime (same SONAME as the system one).  Load torch
+# first so that libkdnscan binds to that single runtime instance: streams and
+# device pointers from torch are then valid in the library.
+try:
+    import torch as _torch_mod  # noqa: F401
+except ImportError:  # pragma: no cover - CPU-only validation use
+    _torch_mod = None
 
 lib = ctypes.CDLL(LIB_PATH)
 
@@ -58,11 +67,14 @@ lib.kdn_set_diag_segments.argtypes = [_i32]
 lib.kdn_set_diag_segments.restype = _i32
 lib.kdn_status_string.argtypes = [ctypes.c_int]
 lib.kdn_status_string.restype = ctypes.c_char_p
+lib.kdn_last_hip_error.argtypes = []
+lib.kdn_last_hip_error.restype = ctypes.c_char_p
 
 
 class KdnError(RuntimeError):
     def __init__(self, fn: str, code: int):
-        super().__init__(f"{fn} failed: {code} ({kdn_status_string(code)})")
+        extra = f"; HIP: {lib.kdn_last_hip_error().decode()}" if code == KDN_EHIP else ""
+        super().__init__(f"{fn} failed: {code} ({kdn_status_string(code)}){extra}")
         self.code = code
 
 
@@ -70,6 +82,10 @@ def header_functions(path: str = HEADER) -> list[str]:
     """Names of the functions include/kdnscan.h declares."""
     text = open(path).read()
     return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kdn_\w+)\s*\(", text, re.M)))
+
+
+def kdn_last_hip_error() -> str:
+    return lib.kdn_last_hip_error().decode()
 
 
 def kdn_status_string(code: int) -> str:
@@ -141,6 +157,12 @@ def _workspace(fn, args, device):
     return ws, need
 
 
+def _nbytes(ws, need):
+    """Size argument of a run call: NULL when no workspace is passed (a NULL
+    workspace with a non-NULL size pointer would be a size query)."""
+    return None if ws is None else ctypes.byref(need)
+
+
 def _in_dtype(t):
     torch = _torch()
     if t.dtype == torch.float32:
@@ -185,7 +207,7 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
                 ws, nbytes, st)
 
     ws, need = _workspace(lib.kdn_diag_scan_fwd, args, dev)
-    rc = lib.kdn_diag_scan_fwd(*args(_ptr(ws), ctypes.byref(need)))
+    rc = lib.kdn_diag_scan_fwd(*args(_ptr(ws), _nbytes(ws, need)))
     if rc != KDN_OK:
         raise KdnError("kdn_diag_scan_fwd", rc)
     return o, I_T, mu_T
@@ -220,7 +242,7 @@ def kdn_mobius_precision_scan(a, p, Lam, lambda0=None, q=None, k=None, v=None, m
                 _ptr(q), _ptr(k), _ptr(v), _ptr(mu0), _ptr(o), _ptr(mu_T), ws, nbytes, st)
 
     ws, need = _workspace(lib.kdn_mobius_precision_scan, args, dev)
-    rc = lib.kdn_mobius_precision_scan(*args(_ptr(ws), ctypes.byref(need)))
+    rc = lib.kdn_mobius_precision_scan(*args(_ptr(ws), _nbytes(ws, need)))
     if rc != KDN_OK:
         raise KdnError("kdn_mobius_precision_scan", rc)
     return lam, o, mu_T

@@ -154,6 +154,10 @@ int32_t kdn_set_diag_segments(int32_t segments);
 /* Human-readable text of a status code; never NULL. */
 const char* kdn_status_string(int status);
 
+/* Text of the HIP error behind the calling thread's last KDN_EHIP (or "no
+ * error"); never NULL.  Diagnostic only. */
+const char* kdn_last_hip_error(void);
+
 #ifdef __cplusplus
 }
 #endif
