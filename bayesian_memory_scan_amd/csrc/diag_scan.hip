@@ -50,6 +50,44 @@ __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int s
     t1 = c1 * C < p.T ? c1 * C : p.T;
 }
 
+// v_fmac_f32 with its first multiplicand broadcast from lane N of each row of
+// 16 lanes (DPP row_newbcast): acc += bcast_N(src) * other.  The per-lane
+// key-side values (k, k^2, q of 16 rows) live one per lane, so a single VGPR
+// feeds 16 entries without LDS traffic.
+template <int N>
+__device__ __forceinline__ void fmac_bcast(float& acc, float src, float other) {
+    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
+        : "+v"(acc)
+        : "v"(src), "v"(other), "n"(N));
+}
+
+template <int N, int JP>
+struct Unroll {
+    template <typename F>
+    __device__ __forceinline__ static void run(F&& f) {
+        f(std::integral_constant<int, N>{});
+        Unroll<N + 1, JP>::run(f);
+    }
+};
+template <int JP>
+struct Unroll<JP, JP> {
+    template <typename F>
+    __device__ __forceinline__ static void run(F&&) {}
+};
+
+__device__ __forceinline__ float uniform(float x) {
+    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
+}
+
+// Scaled frame.  Between renormalisations the kernel keeps I~ = s_t I_t and
+// eta~ = s_t eta_t, where s_t = prod(1/alpha) since the frame's start token.
+// Per token and entry that turns both updates into accumulations:
+//   I~  += beta_i s_t k_j^2 + (1 - alpha_t) I_prior s_t,   eta~ += beta_i v_i s_t k_j,
+// and mu = eta~ / I~ needs no scale at all.  A frame starts at every chunk's
+// first token and wherever s would pass e^kFrameLog; at a start the state is
+// multiplied by rho_t = alpha_t / s_{t-1} and s restarts at 1.
+constexpr float kFrameLog = 30.0f;
+
 template <int DK, int CI, int W, int C, bool BF16, int MODE>
 __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     constexpr bool COMPOSITE = (MODE & 1) != 0;
@@ -63,23 +101,29 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     constexpr int VB = C * CI / VW;      // vectors of beta (and v) per chunk
     constexpr int NVK = (VK + NTH - 1) / NTH;
     constexpr int NVB = (VB + NTH - 1) / NTH;
-    static_assert(NTH % CI == 0 && DK % P == 0 && JP % 4 == 0, "tile shape");
-    static_assert(C <= NTH, "one thread per token for the gates");
+    static_assert(NTH % CI == 0 && DK % P == 0, "tile shape");
+    static_assert(JP == 4 || JP == 8 || JP == 16, "key rows per lane: one DPP row");
+    static_assert(CI >= 16, "a DPP row must stay inside one row group");
+    static_assert(C == 16, "per-token scalars are scanned across 16 lanes");
     static_assert(!(ISO_M && BF16), "isotropic inputs are fp32");
 
-    __shared__ float s_k[2][C][DK];
-    __shared__ float s_k2[2][ISO_M ? 1 : C][DK];
-    __shared__ float s_q[2][COMPOSITE ? 1 : C][DK];
-    __shared__ float s_b[2][ISO_M ? 1 : C][CI];
-    __shared__ float s_v[2][C][CI];
-    __shared__ float s_a[2][C];
-    __shared__ float s_c[2][C];
-    __shared__ float s_o[2][COMPOSITE ? 1 : C][P][CI];
+    struct Stage {
+        float k[C][DK];
+        float k2[ISO_M ? 1 : C][DK];
+        float q[COMPOSITE ? 1 : C][DK];
+        float2 bv[C][CI];   // (beta_i, v_i), or (v_i, -) in the isotropic modes
+        float4 sc[C];       // per token: rho, dP (or 1/s), s, G s (isotropic)
+    };
+    __shared__ Stage stg[2];
+    __shared__ float opart[2][COMPOSITE ? 1 : C][P][CI];
+    __shared__ float s_final[2];  // s of the segment's last token; sum of -log(alpha)
 
     const int tid = threadIdx.x;
+    const int lane = tid % kWave;
     const int col = tid % CI;
     const int rg = tid / CI;
     const int j0 = rg * JP;
+    const int jl = j0 + (lane & (JP - 1));   // the key row this lane holds for broadcasts
     const int ntile = static_cast<int>(p.dv / CI);
     const int nseg = COMPOSITE ? p.S - 1 : p.S;
     int64_t wg = blockIdx.x;
@@ -103,10 +147,10 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     const float* Fh = ISO_M ? p.F + bh * p.T : nullptr;
     const float* Gh = ISO_M ? p.G + bh * p.T : nullptr;
 
-    // ---- state, JP key rows per lane: I (J in DIAG_COMP; unused in ISO) and eta
-    //      (the information mean in DIAG, the mean itself in ISO) ----
+    // ---- state, JP key rows per lane, in the scaled frame with s = 1 at the
+    //      segment start: I~ (J~ in DIAG_COMP, unused in ISO) and eta~ (the
+    //      information mean in DIAG, the mean itself in ISO) ----
     float I[JP], eta[JP];
-    float gprod = 1.0f;
     if constexpr (COMPOSITE) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) { I[r] = 0.0f; eta[r] = 0.0f; }
@@ -139,6 +183,8 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     // ---- chunk staging: global -> registers -> LDS (fp32) ----
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
     float rd = 0.0f, rg2 = 0.0f;
+    float s_prev = 1.0f;   // wave 0, lanes < 16: s of the previous staged token
+    float lsum = 0.0f;     // wave 0, lanes < 16: sum of -log(alpha) so far
 
     auto fetch = [&](int64_t t0, int L) {
 #pragma unroll
@@ -172,7 +218,8 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         }
     };
 
-    auto commit = [&](int nb, int L) {
+    auto commit = [&](int nb, int L, bool last) {
+        Stage& S = stg[nb];
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
             const int vi = tid + n * NTH;
@@ -183,13 +230,13 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                 widen<BF16>(rk[n], f);
 #pragma unroll
                 for (int e = 0; e < VW; ++e) {
-                    s_k[nb][row][c0 + e] = f[e];
-                    if constexpr (!ISO_M) s_k2[nb][row][c0 + e] = f[e] * f[e];
+                    S.k[row][c0 + e] = f[e];
+                    if constexpr (!ISO_M) S.k2[row][c0 + e] = f[e] * f[e];
                 }
                 if constexpr (!COMPOSITE) {
                     widen<BF16>(rq[n], f);
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) s_q[nb][row][c0 + e] = f[e];
+                    for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
                 }
             }
         }
@@ -199,25 +246,76 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             const int row = vi / (CI / VW);
             const int c0 = (vi % (CI / VW)) * VW;
             if (vi < VB && row < L) {
-                float f[VW];
-                if constexpr (!ISO_M) {
-                    widen<BF16>(rb[n], f);
+                float fv[VW];
+                widen<BF16>(rv[n], fv);
+                if constexpr (ISO_M) {
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) s_b[nb][row][c0 + e] = f[e];
+                    for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fv[e], 0.0f);
+                } else {
+                    float fb[VW];
+                    widen<BF16>(rb[n], fb);
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fv[e]);
                 }
-                widen<BF16>(rv[n], f);
-#pragma unroll
-                for (int e = 0; e < VW; ++e) s_v[nb][row][c0 + e] = f[e];
             }
         }
-        if (tid < L) {
+        // Per-token scalars: lanes 0..15 of wave 0, one token each.
+        if (tid < C) {
+            const bool valid = tid < L;
+            float alpha, grow, ell;  // alpha_t, 1/alpha_t, -log(alpha_t)
             if constexpr (ISO_M) {
-                s_a[nb][tid] = rd;    // F_t
-                s_c[nb][tid] = rg2;   // G_t
+                alpha = valid ? rd : 1.0f;
+                grow = 1.0f / alpha;
+                ell = valid ? -__logf(alpha) : 0.0f;
             } else {
-                const float alpha = fast_exp(-A * rd);
-                s_a[nb][tid] = alpha;
-                s_c[nb][tid] = (1.0f - alpha) * I_prior;
+                ell = valid ? A * rd : 0.0f;
+                alpha = fast_exp(-ell);
+                grow = fast_exp(ell);
+            }
+            // frame boundaries from the running log-growth after the first token
+            float c = tid == 0 ? 0.0f : ell;
+#pragma unroll
+            for (int o = 1; o < C; o <<= 1) {
+                const float u = __shfl_up(c, o, C);
+                if (tid >= o) c += u;
+            }
+            const int fr = static_cast<int>(c * (1.0f / kFrameLog));
+            const int fr_prev = __shfl_up(fr, 1, C);
+            const bool start = tid == 0 || fr != fr_prev;
+            // s_t: product of 1/alpha since the frame start (segmented scan)
+            float sv = start ? 1.0f : grow;
+            bool sf = start;
+#pragma unroll
+            for (int o = 1; o < C; o <<= 1) {
+                const float pv = __shfl_up(sv, o, C);
+                const bool pf = __shfl_up(static_cast<int>(sf), o, C) != 0;
+                if (tid >= o) {
+                    if (!sf) sv *= pv;
+                    sf = sf || pf;
+                }
+            }
+            float sp = __shfl_up(sv, 1, C);
+            if (tid == 0) sp = s_prev;
+            const float rho = start ? alpha / sp : 1.0f;
+            float4 rec;
+            rec.x = rho;
+            rec.z = sv;
+            if constexpr (ISO_M) {
+                rec.y = 1.0f / sv;
+                rec.w = rg2 * sv;                          // G_t s_t
+            } else {
+                rec.y = (1.0f - alpha) * I_prior * sv;     // dP_t
+                rec.w = 0.0f;
+            }
+            if (valid) S.sc[tid] = rec;
+            s_prev = __shfl(sv, L - 1, C);
+            float tot = ell;
+#pragma unroll
+            for (int o = 1; o < C; o <<= 1) tot += __shfl_xor(tot, o, C);
+            lsum += tot;
+            if (last && tid == 0) {
+                s_final[0] = s_prev;
+                s_final[1] = lsum;
             }
         }
     };
@@ -230,7 +328,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 
     if (nch > 0) {
         fetch(t_begin, chunk_len(0));
-        commit(0, chunk_len(0));
+        commit(0, chunk_len(0), nch == 1);
     }
     __syncthreads();
     if (nch > 1) fetch(t_begin + C, chunk_len(1));
@@ -239,56 +337,68 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         const int b = static_cast<int>(c & 1);
         const int L = chunk_len(c);
         const int64_t t0 = t_begin + c * C;
+        const Stage& S = stg[b];
 
         for (int tt = 0; tt < L; ++tt) {
-            const float a = s_a[b][tt];
-            const float cc = s_c[b][tt];
-            float bi = 0.0f, bvi;
+            const float4 sc = S.sc[tt];
+            const uint32_t rho_bits = __builtin_amdgcn_readfirstlane(__float_as_uint(sc.x));
+            if (rho_bits != 0x3f800000u) {
+                const float rho = __uint_as_float(rho_bits);
+#pragma unroll
+                for (int r = 0; r < JP; ++r) {
+                    if constexpr (!ISO_M) I[r] *= rho;
+                    eta[r] *= rho;
+                }
+            }
+            const float2 bvv = S.bv[tt][col];
+            const float vk = S.k[tt][jl];
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (ISO_M) {
-                bvi = cc * s_v[b][tt][col];          // G_t v_t[i]
-            } else {
-                bi = s_b[b][tt][col];
-                bvi = bi * s_v[b][tt][col];          // beta_t[i] v_t[i]
-            }
-            float acc = 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < JP; jj += 4) {
-                const float4 kk = *reinterpret_cast<const float4*>(&s_k[b][tt][j0 + jj]);
-                const float kv[4] = {kk.x, kk.y, kk.z, kk.w};
-                float k2v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-                if constexpr (!ISO_M) {
-                    const float4 k2 = *reinterpret_cast<const float4*>(&s_k2[b][tt][j0 + jj]);
-                    k2v[0] = k2.x; k2v[1] = k2.y; k2v[2] = k2.z; k2v[3] = k2.w;
-                }
-                float qv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                const float gvs = bvv.x * sc.w;          // G_t v_i s_t
+                Unroll<0, JP>::run([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
+                    fmac_bcast<r>(eta[r], vk, gvs);
+                });
                 if constexpr (!COMPOSITE) {
-                    const float4 qq = *reinterpret_cast<const float4*>(&s_q[b][tt][j0 + jj]);
-                    qv[0] = qq.x; qv[1] = qq.y; qv[2] = qq.z; qv[3] = qq.w;
+                    const float vq = S.q[tt][jl];
+                    Unroll<0, JP>::run([&](auto rr) {
+                        constexpr int r = decltype(rr)::value;
+                        fmac_bcast<r>(acc[r & 3], vq, eta[r]);
+                    });
+                    opart[b][tt][rg][col] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * sc.y;
                 }
+            } else {
+                const float bs = bvv.x * sc.z;           // beta_i s_t
+                const float bvs = bs * bvv.y;            // beta_i v_i s_t
+                const float vk2 = S.k2[tt][jl];
+                Unroll<0, JP>::run([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
+                    fmac_bcast<r>(I[r], vk2, bs);
+                });
+                if constexpr (!COMPOSITE) {
+                    const float dP = uniform(sc.y);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if constexpr (MODE == DIAG) {
-                        const float w = __builtin_fmaf(bi, k2v[e], cc);
-                        I[jj + e] = __builtin_fmaf(a, I[jj + e], w);
-                        eta[jj + e] = __builtin_fmaf(a, eta[jj + e], bvi * kv[e]);
-                        const float m = eta[jj + e] * fast_rcp(I[jj + e]);
-                        acc = __builtin_fmaf(qv[e], m, acc);
-                    } else if constexpr (MODE == DIAG_COMP) {
-                        I[jj + e] = __builtin_fmaf(a, I[jj + e], bi * k2v[e]);
-                        eta[jj + e] = __builtin_fmaf(a, eta[jj + e], bvi * kv[e]);
-                    } else if constexpr (MODE == ISO) {
-                        eta[jj + e] = __builtin_fmaf(a, eta[jj + e], bvi * kv[e]);
-                        acc = __builtin_fmaf(qv[e], eta[jj + e], acc);
-                    } else {
-                        eta[jj + e] = __builtin_fmaf(a, eta[jj + e], bvi * kv[e]);
-                    }
+                    for (int r = 0; r < JP; ++r) I[r] += dP;
+                }
+                Unroll<0, JP>::run([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
+                    fmac_bcast<r>(eta[r], vk, bvs);
+                });
+                if constexpr (!COMPOSITE) {
+                    const float vq = S.q[tt][jl];
+                    float m[JP];
+#pragma unroll
+                    for (int r = 0; r < JP; ++r) m[r] = eta[r] * fast_rcp(I[r]);
+                    Unroll<0, JP>::run([&](auto rr) {
+                        constexpr int r = decltype(rr)::value;
+                        fmac_bcast<r>(acc[r & 3], vq, m[r]);
+                    });
+                    opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
                 }
             }
-            if constexpr (COMPOSITE) gprod *= a;
-            else s_o[b][tt][rg][col] = acc;
         }
 
-        if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
+        if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1), c + 2 == nch);
         __syncthreads();
         if constexpr (!COMPOSITE) {
             for (int e = tid; e < L * CI; e += NTH) {
@@ -296,30 +406,32 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                 const int cc = e % CI;
                 float sum = 0.0f;
 #pragma unroll
-                for (int g = 0; g < P; ++g) sum += s_o[b][tt][g][cc];
+                for (int g = 0; g < P; ++g) sum += opart[b][tt][g][cc];
                 p.o[(bh * p.T + t0 + tt) * p.dv + tile * CI + cc] = sum;
             }
         }
         if (c + 2 < nch) fetch(t0 + 2 * C, chunk_len(c + 2));
     }
 
+    // back from the scaled frame: true state = scaled state / s_last
+    const float s_last = nch > 0 ? s_final[0] : 1.0f;
     if constexpr (COMPOSITE) {
         float* cj = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i;
-            cj[off] = I[r];
-            cj[static_cast<int64_t>(DK) * p.dv + off] = eta[r];
+            cj[off] = I[r] / s_last;
+            cj[static_cast<int64_t>(DK) * p.dv + off] = eta[r] / s_last;
         }
-        if (tid == 0 && tile == 0) p.gdec[bh * p.S + seg] = gprod;
+        if (tid == 0 && tile == 0) p.gdec[bh * p.S + seg] = nch > 0 ? __expf(-s_final[1]) : 1.0f;
     } else if (seg == p.S - 1) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = (bh * DK + j0 + r) * p.dv + i;
             if constexpr (ISO_M) {
-                if (p.mu_T) p.mu_T[off] = eta[r];
+                if (p.mu_T) p.mu_T[off] = eta[r] / s_last;
             } else {
-                if (p.I_T) p.I_T[off] = I[r];
+                if (p.I_T) p.I_T[off] = I[r] / s_last;
                 if (p.mu_T) p.mu_T[off] = eta[r] / I[r];
             }
         }
