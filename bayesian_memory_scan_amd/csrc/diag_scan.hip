@@ -75,6 +75,18 @@ struct Unroll<JP, JP> {
     __device__ __forceinline__ static void run(F&&) {}
 };
 
+// Workgroups are dealt to the 8 XCDs round-robin by blockIdx.  Renumber them
+// so that consecutive logical ids run on one XCD: the column tiles of a head
+// (adjacent ids) then share that XCD's L2 and read q, k from HBM once.
+__device__ __forceinline__ int64_t xcd_local_id() {
+    constexpr uint32_t kXcd = 8;
+    const uint32_t n = gridDim.x;
+    const uint32_t b = blockIdx.x;
+    const uint32_t full = n / kXcd * kXcd;
+    if (b >= full) return b;
+    return static_cast<int64_t>(b % kXcd) * (full / kXcd) + b / kXcd;
+}
+
 __device__ __forceinline__ float uniform(float x) {
     return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
@@ -126,7 +138,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     const int jl = j0 + (lane & (JP - 1));   // the key row this lane holds for broadcasts
     const int ntile = static_cast<int>(p.dv / CI);
     const int nseg = COMPOSITE ? p.S - 1 : p.S;
-    int64_t wg = blockIdx.x;
+    int64_t wg = xcd_local_id();
     const int tile = static_cast<int>(wg % ntile);
     wg /= ntile;
     const int seg = static_cast<int>(wg % nseg);

@@ -135,7 +135,7 @@ def main():
     from bayesian_memory_scan_amd import synth
 
     dev = torch.device("cuda:0")
-    spec = synth.workload(a.workload)
+    spec = synth.workload(a.workload) if a.workload in synth.WORKLOADS else None
     out = {"metric": "tokens/s per MI355X, diag-precision scan fwd; % of HBM/FP32 roofline",
            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic"}
@@ -226,6 +226,24 @@ def main():
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_iso(inp, spec, a.cpu_seconds)
+    elif a.workload == "copy_1gib":
+        # plain device-to-device copy of 1 GiB: the reference for HBM counters
+        # (read 1 GiB + write 1 GiB per step) and for attainable copy bandwidth
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+
+        def step():
+            dst.copy_(src)
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        gbs = 2 * 4 * n / (ev_ms * 1e-3) / 1e9
+        out.update({"metric": "copy GB/s (read + write)", "value": gbs, "unit": "GB/s",
+                    "ms_per_step": wall / a.steps * 1e3,
+                    "config": {"workload": "copy_1gib", "bytes_read": 4 * n, "bytes_written": 4 * n},
+                    "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+                                 "launch_ms_avg": ev_ms, "launch_ms_min": ev_min}})
     else:
         raise SystemExit(f"unknown workload {a.workload}")
 
