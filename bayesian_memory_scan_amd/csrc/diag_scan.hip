@@ -35,11 +35,9 @@
 namespace kdn {
 
 
-// Kernel modes.  DIAG: diagonal precision (I, eta) with read-out.  ISO: the
-// gated affine mean of the isotropic filter, mu_t = F_t mu_{t-1} + G_t k v^T
-// (KLA Metodologia 2-3), with read-out.  The _COMP variants compute segment
-// composites from a zero state, without read-out.
-enum Mode { DIAG = 0, DIAG_COMP = 1, ISO = 2, ISO_COMP = 3 };
+// Kernel modes.  DIAG: diagonal precision (I, eta) with read-out.  DIAG_COMP:
+// segment composites from a zero state, without read-out.
+enum Mode { DIAG = 0, DIAG_COMP = 1 };
 
 // Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S).
 __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
@@ -99,11 +97,11 @@ __device__ __forceinline__ float uniform(float x) {
 // first token and wherever s would pass e^kFrameLog; at a start the state is
 // multiplied by rho_t = alpha_t / s_{t-1} and s restarts at 1.
 constexpr float kFrameLog = 30.0f;
+constexpr int kDiagChunkTokens = 16;
 
 template <int DK, int CI, int W, int C, bool BF16, int MODE>
 __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
-    constexpr bool COMPOSITE = (MODE & 1) != 0;
-    constexpr bool ISO_M = MODE >= ISO;
+    constexpr bool COMPOSITE = MODE == DIAG_COMP;
     using E = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int NTH = W * kWave;
     constexpr int P = NTH / CI;          // row groups per workgroup
@@ -117,18 +115,16 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     static_assert(JP == 4 || JP == 8 || JP == 16, "key rows per lane: one DPP row");
     static_assert(CI >= 16, "a DPP row must stay inside one row group");
     static_assert(C == 16, "per-token scalars are scanned across 16 lanes");
-    static_assert(!(ISO_M && BF16), "isotropic inputs are fp32");
 
     struct Stage {
         float k[C][DK];
-        float k2[ISO_M ? 1 : C][DK];
+        float k2[C][DK];
         float q[COMPOSITE ? 1 : C][DK];
-        float2 bv[C][CI];   // (beta_i, v_i), or (v_i, -) in the isotropic modes
-        float4 sc[C];       // per token: rho, dP (or 1/s), s, G s (isotropic)
+        float2 bv[C][CI];   // (beta_i, v_i)
+        float4 sc[C];       // per token: rho, dP, s, -
     };
     __shared__ Stage stg[2];
     __shared__ float opart[2][COMPOSITE ? 1 : C][P][CI];
-    __shared__ float s_final[2];  // s of the segment's last token; sum of -log(alpha)
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -149,19 +145,14 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     int64_t t_begin, t_end;
     segment_tokens(p, C, seg, t_begin, t_end);
 
-    const float A = ISO_M ? 0.0f : p.A[h];
     const float I_prior = p.I_prior;
     const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
     const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
     const E* vh = static_cast<const E*>(p.v) + bh * p.T * p.dv + tile * CI;
-    const E* bth = ISO_M ? nullptr : static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI;
-    const E* dh = ISO_M ? nullptr : static_cast<const E*>(p.d) + bh * p.T;
-    const float* Fh = ISO_M ? p.F + bh * p.T : nullptr;
-    const float* Gh = ISO_M ? p.G + bh * p.T : nullptr;
+    const E* bth = static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI;
 
     // ---- state, JP key rows per lane, in the scaled frame with s = 1 at the
-    //      segment start: I~ (J~ in DIAG_COMP, unused in ISO) and eta~ (the
-    //      information mean in DIAG, the mean itself in ISO) ----
+    //      segment start: I~ (J~ in DIAG_COMP) and the information mean eta~ ----
     float I[JP], eta[JP];
     if constexpr (COMPOSITE) {
 #pragma unroll
@@ -172,21 +163,16 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             for (int r = 0; r < JP; ++r) {
                 const int64_t off = (bh * DK + j0 + r) * p.dv + i;
                 const float m0 = p.mu0 ? p.mu0[off] : 0.0f;
-                if constexpr (ISO_M) {
-                    I[r] = 1.0f;
-                    eta[r] = m0;
-                } else {
-                    const float I0 = p.I0 ? p.I0[off] : I_prior;
-                    I[r] = I0;
-                    eta[r] = I0 * m0;
-                }
+                const float I0 = p.I0 ? p.I0[off] : I_prior;
+                I[r] = I0;
+                eta[r] = I0 * m0;
             }
         } else {
             const float* cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
 #pragma unroll
             for (int r = 0; r < JP; ++r) {
                 const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i;
-                I[r] = ISO_M ? 1.0f : I_prior + cin[off];
+                I[r] = I_prior + cin[off];
                 eta[r] = cin[static_cast<int64_t>(DK) * p.dv + off];
             }
         }
@@ -194,9 +180,10 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 
     // ---- chunk staging: global -> registers -> LDS (fp32) ----
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
-    float rd = 0.0f, rg2 = 0.0f;
-    float s_prev = 1.0f;   // wave 0, lanes < 16: s of the previous staged token
-    float lsum = 0.0f;     // wave 0, lanes < 16: sum of -log(alpha) so far
+    float4 rsc = make_float4(1.0f, 0.0f, 1.0f, 0.0f);
+    float s_prev = 1.0f;   // scale of the last token of the previous chunk (uniform)
+    float lsum = 0.0f;     // composites: sum of -log(alpha) over the segment (uniform)
+    const float4* sch = p.scal + bh * p.T;
 
     auto fetch = [&](int64_t t0, int L) {
 #pragma unroll
@@ -214,23 +201,14 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             const int cv = vi % (CI / VW);
             if (vi < VB && row < L) {
                 const int64_t off = (t0 + row) * p.dv + cv * VW;
-                if constexpr (!ISO_M) rb[n] = ld16(bth + off);
+                rb[n] = ld16(bth + off);
                 rv[n] = ld16(vh + off);
             }
         }
-        if (tid < L) {
-            if constexpr (ISO_M) {
-                rd = Fh[t0 + tid];
-                rg2 = Gh[t0 + tid];
-            } else if constexpr (BF16) {
-                rd = bf16_at(reinterpret_cast<const uint16_t*>(dh), t0 + tid);
-            } else {
-                rd = reinterpret_cast<const float*>(dh)[t0 + tid];
-            }
-        }
+        if (tid < L) rsc = sch[t0 + tid];
     };
 
-    auto commit = [&](int nb, int L, bool last) {
+    auto commit = [&](int nb, int L) {
         Stage& S = stg[nb];
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
@@ -243,7 +221,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 #pragma unroll
                 for (int e = 0; e < VW; ++e) {
                     S.k[row][c0 + e] = f[e];
-                    if constexpr (!ISO_M) S.k2[row][c0 + e] = f[e] * f[e];
+                    S.k2[row][c0 + e] = f[e] * f[e];
                 }
                 if constexpr (!COMPOSITE) {
                     widen<BF16>(rq[n], f);
@@ -258,78 +236,14 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             const int row = vi / (CI / VW);
             const int c0 = (vi % (CI / VW)) * VW;
             if (vi < VB && row < L) {
-                float fv[VW];
+                float fv[VW], fb[VW];
                 widen<BF16>(rv[n], fv);
-                if constexpr (ISO_M) {
+                widen<BF16>(rb[n], fb);
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fv[e], 0.0f);
-                } else {
-                    float fb[VW];
-                    widen<BF16>(rb[n], fb);
-#pragma unroll
-                    for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fv[e]);
-                }
+                for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fv[e]);
             }
         }
-        // Per-token scalars: lanes 0..15 of wave 0, one token each.
-        if (tid < C) {
-            const bool valid = tid < L;
-            float alpha, grow, ell;  // alpha_t, 1/alpha_t, -log(alpha_t)
-            if constexpr (ISO_M) {
-                alpha = valid ? rd : 1.0f;
-                grow = 1.0f / alpha;
-                ell = valid ? -__logf(alpha) : 0.0f;
-            } else {
-                ell = valid ? A * rd : 0.0f;
-                alpha = fast_exp(-ell);
-                grow = fast_exp(ell);
-            }
-            // frame boundaries from the running log-growth after the first token
-            float c = tid == 0 ? 0.0f : ell;
-#pragma unroll
-            for (int o = 1; o < C; o <<= 1) {
-                const float u = __shfl_up(c, o, C);
-                if (tid >= o) c += u;
-            }
-            const int fr = static_cast<int>(c * (1.0f / kFrameLog));
-            const int fr_prev = __shfl_up(fr, 1, C);
-            const bool start = tid == 0 || fr != fr_prev;
-            // s_t: product of 1/alpha since the frame start (segmented scan)
-            float sv = start ? 1.0f : grow;
-            bool sf = start;
-#pragma unroll
-            for (int o = 1; o < C; o <<= 1) {
-                const float pv = __shfl_up(sv, o, C);
-                const bool pf = __shfl_up(static_cast<int>(sf), o, C) != 0;
-                if (tid >= o) {
-                    if (!sf) sv *= pv;
-                    sf = sf || pf;
-                }
-            }
-            float sp = __shfl_up(sv, 1, C);
-            if (tid == 0) sp = s_prev;
-            const float rho = start ? alpha / sp : 1.0f;
-            float4 rec;
-            rec.x = rho;
-            rec.z = sv;
-            if constexpr (ISO_M) {
-                rec.y = 1.0f / sv;
-                rec.w = rg2 * sv;                          // G_t s_t
-            } else {
-                rec.y = (1.0f - alpha) * I_prior * sv;     // dP_t
-                rec.w = 0.0f;
-            }
-            if (valid) S.sc[tid] = rec;
-            s_prev = __shfl(sv, L - 1, C);
-            float tot = ell;
-#pragma unroll
-            for (int o = 1; o < C; o <<= 1) tot += __shfl_xor(tot, o, C);
-            lsum += tot;
-            if (last && tid == 0) {
-                s_final[0] = s_prev;
-                s_final[1] = lsum;
-            }
-        }
+        if (tid < L) S.sc[tid] = rsc;
     };
 
     const int64_t nch = (t_end - t_begin + C - 1) / C;
@@ -340,7 +254,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 
     if (nch > 0) {
         fetch(t_begin, chunk_len(0));
-        commit(0, chunk_len(0), nch == 1);
+        commit(0, chunk_len(0));
     }
     __syncthreads();
     if (nch > 1) fetch(t_begin + C, chunk_len(1));
@@ -350,36 +264,25 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         const int L = chunk_len(c);
         const int64_t t0 = t_begin + c * C;
         const Stage& S = stg[b];
+        const float inv_sp = 1.0f / s_prev;   // a chunk's first token restarts the frame
 
         for (int tt = 0; tt < L; ++tt) {
             const float4 sc = S.sc[tt];
-            const uint32_t rho_bits = __builtin_amdgcn_readfirstlane(__float_as_uint(sc.x));
+            const float rho_t = sc.x * (tt == 0 ? inv_sp : 1.0f);
+            const uint32_t rho_bits = __builtin_amdgcn_readfirstlane(__float_as_uint(rho_t));
+            if constexpr (COMPOSITE) lsum += sc.w;
             if (rho_bits != 0x3f800000u) {
                 const float rho = __uint_as_float(rho_bits);
 #pragma unroll
                 for (int r = 0; r < JP; ++r) {
-                    if constexpr (!ISO_M) I[r] *= rho;
+                    I[r] *= rho;
                     eta[r] *= rho;
                 }
             }
             const float2 bvv = S.bv[tt][col];
             const float vk = S.k[tt][jl];
             float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (ISO_M) {
-                const float gvs = bvv.x * sc.w;          // G_t v_i s_t
-                Unroll<0, JP>::run([&](auto rr) {
-                    constexpr int r = decltype(rr)::value;
-                    fmac_bcast<r>(eta[r], vk, gvs);
-                });
-                if constexpr (!COMPOSITE) {
-                    const float vq = S.q[tt][jl];
-                    Unroll<0, JP>::run([&](auto rr) {
-                        constexpr int r = decltype(rr)::value;
-                        fmac_bcast<r>(acc[r & 3], vq, eta[r]);
-                    });
-                    opart[b][tt][rg][col] = ((acc[0] + acc[1]) + (acc[2] + acc[3])) * sc.y;
-                }
-            } else {
+            {
                 const float bs = bvv.x * sc.z;           // beta_i s_t
                 const float bvs = bs * bvv.y;            // beta_i v_i s_t
                 const float vk2 = S.k2[tt][jl];
@@ -410,7 +313,8 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             }
         }
 
-        if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1), c + 2 == nch);
+        s_prev = S.sc[L - 1].z;
+        if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
         __syncthreads();
         if constexpr (!COMPOSITE) {
             for (int e = tid; e < L * CI; e += NTH) {
@@ -426,7 +330,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     }
 
     // back from the scaled frame: true state = scaled state / s_last
-    const float s_last = nch > 0 ? s_final[0] : 1.0f;
+    const float s_last = s_prev;
     if constexpr (COMPOSITE) {
         float* cj = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
 #pragma unroll
@@ -435,18 +339,58 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             cj[off] = I[r] / s_last;
             cj[static_cast<int64_t>(DK) * p.dv + off] = eta[r] / s_last;
         }
-        if (tid == 0 && tile == 0) p.gdec[bh * p.S + seg] = nch > 0 ? __expf(-s_final[1]) : 1.0f;
+        if (tid == 0 && tile == 0) p.gdec[bh * p.S + seg] = __expf(-lsum);
     } else if (seg == p.S - 1) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = (bh * DK + j0 + r) * p.dv + i;
-            if constexpr (ISO_M) {
-                if (p.mu_T) p.mu_T[off] = eta[r] / s_last;
-            } else {
-                if (p.I_T) p.I_T[off] = I[r] / s_last;
-                if (p.mu_T) p.mu_T[off] = eta[r] / I[r];
-            }
+            if (p.I_T) p.I_T[off] = I[r] / s_last;
+            if (p.mu_T) p.mu_T[off] = eta[r] / I[r];
         }
+    }
+}
+
+// Per-token scalars of the scaled frame, one thread per 16-token chunk of a
+// head, walking its tokens in order: alpha = exp(-A d), the frame cuts (a
+// frame starts at the chunk's first token and wherever the log-growth since
+// that token crosses a multiple of kFrameLog), s = product of 1/alpha since
+// the frame start, rho = alpha / s_{t-1} at a start (for the chunk's first
+// token only alpha: the main pass divides by the previous chunk's last s),
+// dP = (1 - alpha) I_prior s.  Output (rho, dP, s, A d) per token.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units, int32_t nch) {
+    constexpr int C = kDiagChunkTokens;
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (u >= n_units) return;
+    const int64_t bh = u / nch;
+    const int64_t t0 = (u % nch) * C;
+    const int L = p.T - t0 < C ? static_cast<int>(p.T - t0) : C;
+    const float A = p.A[bh % p.H];
+    float cum = 0.0f, s = 1.0f;
+    int fr_prev = 0;
+    float4* out = p.scal + bh * p.T + t0;
+    for (int k = 0; k < L; ++k) {
+        const int64_t t = bh * p.T + t0 + k;
+        const float d = BF16 ? bf16_at(static_cast<const uint16_t*>(p.d), t) : static_cast<const float*>(p.d)[t];
+        const float ell = A * d;
+        const float alpha = fast_exp(-ell);
+        float rho;
+        if (k == 0) {
+            rho = alpha;
+            s = 1.0f;
+        } else {
+            cum += ell;
+            const int fr = static_cast<int>(cum * (1.0f / kFrameLog));
+            if (fr != fr_prev) {
+                rho = alpha / s;
+                s = 1.0f;
+            } else {
+                rho = 1.0f;
+                s *= fast_exp(ell);
+            }
+            fr_prev = fr;
+        }
+        out[k] = make_float4(rho, (1.0f - alpha) * p.I_prior * s, s, ell);
     }
 }
 
@@ -498,7 +442,7 @@ __global__ __launch_bounds__(256) void k_diag_copy_state(DiagParams p, int64_t n
 // Host side
 // ---------------------------------------------------------------------------
 
-constexpr int kDiagChunk = 16;
+constexpr int kDiagChunk = kDiagChunkTokens;
 
 // Workgroup width for a (DK, CI) tile: enough waves that each lane keeps
 // 16 key rows when the tile is large, never fewer than one wave.
@@ -538,36 +482,54 @@ static int launch_mode(const DiagParams& p, int64_t dk, int CI, int64_t grid, hi
 
 int diag_chunk() { return kDiagChunk; }
 
-// Enqueue a whole segmented scan (diagonal precision, or the isotropic gated
-// mean when iso is set).  Arguments were validated by the caller; comp/gdec
-// point into a workspace of the size the planner reported when S > 1.
-int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, bool iso, hipStream_t st) {
+int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st) {
+    const int32_t nch = static_cast<int32_t>((p.T + kDiagChunk - 1) / kDiagChunk);
+    const int64_t n = B * p.H * nch;
+    if (n == 0) return KDN_OK;
+    const dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+    if (bf16) hipLaunchKernelGGL(k_diag_prep<true>, grid, dim3(256), 0, st, p, n, nch);
+    else hipLaunchKernelGGL(k_diag_prep<false>, grid, dim3(256), 0, st, p, n, nch);
+    return launch_status();
+}
+
+// Ordered carry over segments: composites -> starting state of every segment.
+int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st) {
+    const int64_t n = B * p.H * dk * p.dv;
+    if (n == 0) return KDN_OK;
+    hipLaunchKernelGGL(k_diag_carry, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
+                       p, dk, n, iso ? 1 : 0);
+    return launch_status();
+}
+
+// T == 0: write the starting state as the final state (iso: mean only).
+int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st) {
+    const int64_t n = B * p.H * dk * p.dv;
+    if (n == 0) return KDN_OK;
+    hipLaunchKernelGGL(k_diag_copy_state, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
+                       p, n, iso ? 1 : 0);
+    return launch_status();
+}
+
+// Enqueue the whole diagonal scan.  Arguments were validated by the caller;
+// comp/gdec point into a workspace of the size the planner reported when S > 1.
+int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, hipStream_t st) {
     const int64_t BH = B * p.H;
     if (BH == 0) return KDN_OK;
-    if (p.T == 0) {
-        const int64_t n = BH * dk * p.dv;
-        hipLaunchKernelGGL(k_diag_copy_state, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
-                           p, n, iso ? 1 : 0);
-        return launch_status();
-    }
+    if (p.T == 0) return copy_state_launch(p, B, dk, false, st);
     const int CI = p.dv < 64 ? static_cast<int>(p.dv) : 64;
     const int64_t ntile = p.dv / CI;
-    int rc = KDN_OK;
+    int rc = diag_prep_launch(p, B, bf16, st);
+    if (rc != KDN_OK) return rc;
     if (p.S > 1) {
         const int64_t g1 = BH * (p.S - 1) * ntile;
-        if (iso) rc = launch_mode<false, ISO_COMP>(p, dk, CI, g1, st);
-        else rc = bf16 ? launch_mode<true, DIAG_COMP>(p, dk, CI, g1, st)
-                       : launch_mode<false, DIAG_COMP>(p, dk, CI, g1, st);
+        rc = bf16 ? launch_mode<true, DIAG_COMP>(p, dk, CI, g1, st)
+                  : launch_mode<false, DIAG_COMP>(p, dk, CI, g1, st);
         if (rc != KDN_OK) return rc;
         if ((rc = launch_status()) != KDN_OK) return rc;
-        const int64_t n = BH * dk * p.dv;
-        hipLaunchKernelGGL(k_diag_carry, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
-                           p, dk, n, iso ? 1 : 0);
-        if ((rc = launch_status()) != KDN_OK) return rc;
+        if ((rc = diag_carry_launch(p, B, dk, false, st)) != KDN_OK) return rc;
     }
     const int64_t g2 = BH * p.S * ntile;
-    if (iso) rc = launch_mode<false, ISO>(p, dk, CI, g2, st);
-    else rc = bf16 ? launch_mode<true, DIAG>(p, dk, CI, g2, st) : launch_mode<false, DIAG>(p, dk, CI, g2, st);
+    rc = bf16 ? launch_mode<true, DIAG>(p, dk, CI, g2, st) : launch_mode<false, DIAG>(p, dk, CI, g2, st);
     if (rc != KDN_OK) return rc;
     return launch_status();
 }

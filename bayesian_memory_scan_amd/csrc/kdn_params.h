@@ -22,6 +22,7 @@ struct DiagParams {
     float* o;
     float* I_T;
     float* mu_T;
+    float4* scal;  // [BH][T] per-token scalars of the diagonal scan (rho, dP, s, -log alpha)
     float* comp;   // [BH][S][2][dk][dv]: segment composites, then carry-in states
     float* gdec;   // [BH][S]: decay product of each segment
     int64_t H;
@@ -60,9 +61,14 @@ struct MobParams {
 };
 
 int diag_chunk();
-int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, bool iso, hipStream_t st);
+int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st);
+int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, hipStream_t st);
+int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
+int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int mob_block();
 int mobius_launch(const MobParams& p, int64_t BH, hipStream_t st);
+int iso_chunk();
+int iso_mean_launch(const DiagParams& p, int64_t B, int64_t dk, hipStream_t st);
 
 }  // namespace kdn

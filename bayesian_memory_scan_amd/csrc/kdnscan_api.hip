@@ -49,6 +49,27 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
     return pl;
 }
 
+// Segments of the isotropic mean scan: about two workgroups per CU, at least
+// four 16-token chunks per segment.
+Plan plan_iso(int64_t BH, int64_t T) {
+    Plan pl;
+    pl.chunk = iso_chunk();
+    pl.nchunks = static_cast<int32_t>((T + pl.chunk - 1) / pl.chunk);
+    int64_t S = 1;
+    const int32_t ov = g_segments_override.load();
+    if (ov > 0) {
+        S = ov;
+    } else if (BH > 0) {
+        S = (2 * kNumCU + BH - 1) / BH;
+        if (S > pl.nchunks / 4) S = pl.nchunks / 4;
+    }
+    if (S > kMaxSegments) S = kMaxSegments;
+    if (S > pl.nchunks) S = pl.nchunks;
+    if (S < 1) S = 1;
+    pl.S = static_cast<int32_t>(S);
+    return pl;
+}
+
 size_t scan_workspace_bytes(int64_t BH, int64_t dk, int64_t dv, const Plan& pl) {
     if (pl.S <= 1) return 0;
     const size_t comp = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * dk * dv, 256);
@@ -149,7 +170,8 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const Plan pl = plan_scan(BH, T, d_v);
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
     if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
-    const size_t need = scan_workspace_bytes(BH, d_k, d_v, pl);
+    const size_t b_scal = align_up(16 * static_cast<size_t>(BH) * T, 256);   // per-token scalars
+    const size_t need = b_scal + scan_workspace_bytes(BH, d_k, d_v, pl);
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
     if (wc != KDN_OK) return wc;
@@ -159,15 +181,16 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
     p.A = A; p.I0 = I0; p.mu0 = mu0;
     p.o = o; p.I_T = I_T; p.mu_T = mu_T;
+    p.scal = reinterpret_cast<float4*>(workspace);
     if (pl.S > 1) {
-        char* ws = static_cast<char*>(workspace);
+        char* ws = static_cast<char*>(workspace) + b_scal;
         p.comp = reinterpret_cast<float*>(ws);
         p.gdec = reinterpret_cast<float*>(ws + align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * d_k * d_v, 256));
     }
     p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.S = pl.S; p.nchunks = pl.nchunks;
     (void)hipGetLastError();  // launch status below must reflect this call only
-    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, false, static_cast<hipStream_t>(stream));
+    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
 }
 
 int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
@@ -196,9 +219,8 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
     Plan pl{};
     size_t b_gate = 0;
     if (mean) {
-        pl = plan_scan(BH, T, d_v);
-        const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
-        if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
+        pl = plan_iso(BH, T);
+        if (BH * pl.S > kMaxGrid) return KDN_EINVAL;
         b_gate = align_up(sizeof(float) * static_cast<size_t>(BH) * T, 256);
         need += 2 * b_gate + scan_workspace_bytes(BH, d_k, d_v, pl);
     }
@@ -235,7 +257,7 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
     }
     dp.H = H; dp.T = T; dp.dv = d_v; dp.I_prior = 1.0f;
     dp.S = pl.S; dp.nchunks = pl.nchunks;
-    return diag_scan_launch(dp, B, d_k, false, true, st);
+    return iso_mean_launch(dp, B, d_k, st);
 }
 
 int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in_dtype,

@@ -65,12 +65,12 @@ def test_diag_validation():
 def test_diag_workspace_protocol():
     n = ctypes.c_size_t(12345)
     assert _diag(B=8, H=16, T=2048, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
-    assert n.value == 0  # one segment: no workspace
+    assert n.value == 16 * 8 * 16 * 2048  # one segment: per-token scalars only
     n = ctypes.c_size_t(0)
     assert _diag(B=2, H=16, T=16384, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
     chunk, S, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
-    expect_comp = 4 * 2 * 16 * S * 2 * 128 * 128
-    assert n.value >= expect_comp and n.value % 256 == 0
+    expect = 16 * 2 * 16 * 16384 + 4 * 2 * 16 * S * 2 * 128 * 128
+    assert n.value >= expect and n.value % 256 == 0
     need = n.value
     # running with too little (or no) workspace is refused before any launch
     small = ctypes.c_size_t(need - 1)
