@@ -85,6 +85,13 @@ __device__ __forceinline__ int64_t xcd_local_id() {
     return static_cast<int64_t>(b % kXcd) * (full / kXcd) + b / kXcd;
 }
 
+// Value of lane N of this lane's row of 16 (DPP row_newbcast), as a plain
+// operand; the compiler folds it into the consuming v_mul_f32.
+template <int N>
+__device__ __forceinline__ float bcast(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, true));
+}
+
 __device__ __forceinline__ float uniform(float x) {
     return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
@@ -266,8 +273,21 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         const Stage& S = stg[b];
         const float inv_sp = 1.0f / s_prev;   // a chunk's first token restarts the frame
 
+        // Software-pipelined over tokens: the next token's LDS operands are
+        // loaded while the current one computes.
+        float4 sc = S.sc[0];
+        float2 bvv = S.bv[0][col];
+        float vk = S.k[0][jl], vk2 = S.k2[0][jl];
+        float vq = 0.0f;
+        if constexpr (!COMPOSITE) vq = S.q[0][jl];
         for (int tt = 0; tt < L; ++tt) {
-            const float4 sc = S.sc[tt];
+            const int tn = tt + 1 < L ? tt + 1 : tt;
+            const float4 sc_n = S.sc[tn];
+            const float2 bvv_n = S.bv[tn][col];
+            const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl];
+            float vq_n = 0.0f;
+            if constexpr (!COMPOSITE) vq_n = S.q[tn][jl];
+
             const float rho_t = sc.x * (tt == 0 ? inv_sp : 1.0f);
             const uint32_t rho_bits = __builtin_amdgcn_readfirstlane(__float_as_uint(rho_t));
             if constexpr (COMPOSITE) lsum += sc.w;
@@ -279,38 +299,42 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                     eta[r] *= rho;
                 }
             }
-            const float2 bvv = S.bv[tt][col];
-            const float vk = S.k[tt][jl];
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            {
-                const float bs = bvv.x * sc.z;           // beta_i s_t
-                const float bvs = bs * bvv.y;            // beta_i v_i s_t
-                const float vk2 = S.k2[tt][jl];
-                Unroll<0, JP>::run([&](auto rr) {
-                    constexpr int r = decltype(rr)::value;
-                    fmac_bcast<r>(I[r], vk2, bs);
-                });
-                if constexpr (!COMPOSITE) {
-                    const float dP = uniform(sc.y);
+            const float bs = bvv.x * sc.z;           // beta_i s_t
+            const float bvs = bs * bvv.y;            // beta_i v_i s_t
+            Unroll<0, JP>::run([&](auto rr) {
+                constexpr int r = decltype(rr)::value;
+                fmac_bcast<r>(I[r], vk2, bs);
+            });
+            if constexpr (!COMPOSITE) {
+                const float dP = uniform(sc.y);
 #pragma unroll
-                    for (int r = 0; r < JP; ++r) I[r] += dP;
-                }
-                Unroll<0, JP>::run([&](auto rr) {
-                    constexpr int r = decltype(rr)::value;
-                    fmac_bcast<r>(eta[r], vk, bvs);
-                });
-                if constexpr (!COMPOSITE) {
-                    const float vq = S.q[tt][jl];
-                    float m[JP];
-#pragma unroll
-                    for (int r = 0; r < JP; ++r) m[r] = eta[r] * fast_rcp(I[r]);
-                    Unroll<0, JP>::run([&](auto rr) {
-                        constexpr int r = decltype(rr)::value;
-                        fmac_bcast<r>(acc[r & 3], vq, m[r]);
-                    });
-                    opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                }
+                for (int r = 0; r < JP; ++r) I[r] += dP;
             }
+            Unroll<0, JP>::run([&](auto rr) {
+                constexpr int r = decltype(rr)::value;
+                fmac_bcast<r>(eta[r], vk, bvs);
+            });
+            if constexpr (!COMPOSITE) {
+                float m[JP];
+#pragma unroll
+                for (int r = 0; r < JP; ++r) m[r] = eta[r] * fast_rcp(I[r]);
+                // four read-out accumulators, each started by a broadcast multiply
+                float acc[4];
+                Unroll<0, 4>::run([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
+                    acc[r] = bcast<r>(vq) * m[r];
+                });
+                Unroll<4, JP>::run([&](auto rr) {
+                    constexpr int r = decltype(rr)::value;
+                    fmac_bcast<r>(acc[r & 3], vq, m[r]);
+                });
+                opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            }
+            sc = sc_n;
+            bvv = bvv_n;
+            vk = vk_n;
+            vk2 = vk2_n;
+            vq = vq_n;
         }
 
         s_prev = S.sc[L - 1].z;
