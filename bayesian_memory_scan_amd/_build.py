@@ -16,7 +16,7 @@ LIB = os.path.join(HERE, "libkdnscan.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["kdnscan_api.hip", "diag_scan.hip", "decode.hip", "mobius_scan.hip", "iso_scan.hip"]
+SOURCES = ["kdnscan_api.hip", "diag_scan.hip", "decode.hip", "mobius_scan.hip", "iso_scan.hip", "diag_comp.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

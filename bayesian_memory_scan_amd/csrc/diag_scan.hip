@@ -16,18 +16,17 @@
 // Work decomposition (one GPU):
 //   * a workgroup owns one head (b,h), one tile of CI value columns and one
 //     sequence segment; lane <-> value column i, and each lane keeps JP key
-//     rows j of (I, eta) in VGPRs for the whole segment;
+//     rows j of (I, eta) in VGPRs for the whole segment, in a scaled frame
+//     (below) so both updates are plain accumulations;
 //   * tokens are staged C at a time into LDS (double-buffered, converted to
 //     fp32, k^2 precomputed) while the next chunk's global loads are in
-//     flight; per-token partial read-outs from the P row groups are summed
-//     through LDS once per chunk;
-//   * long sequences are cut into S segments: a composite pass computes, from
-//     a zero state, each segment's decay product and (J, eta) contribution
-//     (J = I - I_prior obeys J_t = alpha_t J_{t-1} + beta k^2); a carry pass
-//     combines them in order, (G2, X2) o (G1, X1) = (G2 G1, G2 X1 + X2), into
-//     every segment's starting state; the main pass then runs all segments
-//     in parallel.  The association is the one that makes the precision and
-//     information-mean updates scannable (KLA Metodologia 2).
+//     flight; the per-token frame scalars come from a small prep kernel; the
+//     key-side values of a lane's rows reach the fmacs as DPP row broadcasts;
+//     per-token partial read-outs of the P row groups are summed through LDS
+//     once per chunk;
+//   * long sequences are cut into S segments whose starting states come from
+//     segment composites computed on the matrix cores and carried in order
+//     (diag_comp.hip); all segments then run in parallel.
 #include "kdn_params.h"
 
 #include <type_traits>
@@ -35,9 +34,6 @@
 namespace kdn {
 
 
-// Kernel modes.  DIAG: diagonal precision (I, eta) with read-out.  DIAG_COMP:
-// segment composites from a zero state, without read-out.
-enum Mode { DIAG = 0, DIAG_COMP = 1 };
 
 // Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S).
 __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
@@ -106,9 +102,8 @@ __device__ __forceinline__ float uniform(float x) {
 constexpr float kFrameLog = 30.0f;
 constexpr int kDiagChunkTokens = 16;
 
-template <int DK, int CI, int W, int C, bool BF16, int MODE>
+template <int DK, int CI, int W, int C, bool BF16>
 __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
-    constexpr bool COMPOSITE = MODE == DIAG_COMP;
     using E = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int NTH = W * kWave;
     constexpr int P = NTH / CI;          // row groups per workgroup
@@ -126,12 +121,12 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     struct Stage {
         float k[C][DK];
         float k2[C][DK];
-        float q[COMPOSITE ? 1 : C][DK];
+        float q[C][DK];
         float2 bv[C][CI];   // (beta_i, v_i)
         float4 sc[C];       // per token: rho, dP, s, -
     };
     __shared__ Stage stg[2];
-    __shared__ float opart[2][COMPOSITE ? 1 : C][P][CI];
+    __shared__ float opart[2][C][P][CI];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -140,13 +135,11 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     const int j0 = rg * JP;
     const int jl = j0 + (lane & (JP - 1));   // the key row this lane holds for broadcasts
     const int ntile = static_cast<int>(p.dv / CI);
-    const int nseg = COMPOSITE ? p.S - 1 : p.S;
     int64_t wg = xcd_local_id();
     const int tile = static_cast<int>(wg % ntile);
     wg /= ntile;
-    const int seg = static_cast<int>(wg % nseg);
-    const int64_t bh = wg / nseg;
-    const int h = static_cast<int>(bh % p.H);
+    const int seg = static_cast<int>(wg % p.S);
+    const int64_t bh = wg / p.S;
     const int i = tile * CI + col;
 
     int64_t t_begin, t_end;
@@ -159,29 +152,24 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     const E* bth = static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI;
 
     // ---- state, JP key rows per lane, in the scaled frame with s = 1 at the
-    //      segment start: I~ (J~ in DIAG_COMP) and the information mean eta~ ----
+    //      segment start: I~ and the information mean eta~ ----
     float I[JP], eta[JP];
-    if constexpr (COMPOSITE) {
+    if (p.S == 1) {
 #pragma unroll
-        for (int r = 0; r < JP; ++r) { I[r] = 0.0f; eta[r] = 0.0f; }
+        for (int r = 0; r < JP; ++r) {
+            const int64_t off = (bh * DK + j0 + r) * p.dv + i;
+            const float m0 = p.mu0 ? p.mu0[off] : 0.0f;
+            const float I0 = p.I0 ? p.I0[off] : I_prior;
+            I[r] = I0;
+            eta[r] = I0 * m0;
+        }
     } else {
-        if (p.S == 1) {
+        const float* cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
 #pragma unroll
-            for (int r = 0; r < JP; ++r) {
-                const int64_t off = (bh * DK + j0 + r) * p.dv + i;
-                const float m0 = p.mu0 ? p.mu0[off] : 0.0f;
-                const float I0 = p.I0 ? p.I0[off] : I_prior;
-                I[r] = I0;
-                eta[r] = I0 * m0;
-            }
-        } else {
-            const float* cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
-#pragma unroll
-            for (int r = 0; r < JP; ++r) {
-                const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i;
-                I[r] = I_prior + cin[off];
-                eta[r] = cin[static_cast<int64_t>(DK) * p.dv + off];
-            }
+        for (int r = 0; r < JP; ++r) {
+            const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i;
+            I[r] = I_prior + cin[off];
+            eta[r] = cin[static_cast<int64_t>(DK) * p.dv + off];
         }
     }
 
@@ -189,7 +177,6 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
     float4 rsc = make_float4(1.0f, 0.0f, 1.0f, 0.0f);
     float s_prev = 1.0f;   // scale of the last token of the previous chunk (uniform)
-    float lsum = 0.0f;     // composites: sum of -log(alpha) over the segment (uniform)
     const float4* sch = p.scal + bh * p.T;
 
     auto fetch = [&](int64_t t0, int L) {
@@ -198,7 +185,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             const int vi = tid + n * NTH;
             if (vi < VK && vi * VW < L * DK) {
                 rk[n] = ld16(kh + t0 * DK + static_cast<int64_t>(vi) * VW);
-                if constexpr (!COMPOSITE) rq[n] = ld16(qh + t0 * DK + static_cast<int64_t>(vi) * VW);
+                rq[n] = ld16(qh + t0 * DK + static_cast<int64_t>(vi) * VW);
             }
         }
 #pragma unroll
@@ -230,11 +217,9 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                     S.k[row][c0 + e] = f[e];
                     S.k2[row][c0 + e] = f[e] * f[e];
                 }
-                if constexpr (!COMPOSITE) {
-                    widen<BF16>(rq[n], f);
+                widen<BF16>(rq[n], f);
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
-                }
+                for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
             }
         }
 #pragma unroll
@@ -279,18 +264,17 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         float2 bvv = S.bv[0][col];
         float vk = S.k[0][jl], vk2 = S.k2[0][jl];
         float vq = 0.0f;
-        if constexpr (!COMPOSITE) vq = S.q[0][jl];
+        vq = S.q[0][jl];
         for (int tt = 0; tt < L; ++tt) {
             const int tn = tt + 1 < L ? tt + 1 : tt;
             const float4 sc_n = S.sc[tn];
             const float2 bvv_n = S.bv[tn][col];
             const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl];
             float vq_n = 0.0f;
-            if constexpr (!COMPOSITE) vq_n = S.q[tn][jl];
+            vq_n = S.q[tn][jl];
 
             const float rho_t = sc.x * (tt == 0 ? inv_sp : 1.0f);
             const uint32_t rho_bits = __builtin_amdgcn_readfirstlane(__float_as_uint(rho_t));
-            if constexpr (COMPOSITE) lsum += sc.w;
             if (rho_bits != 0x3f800000u) {
                 const float rho = __uint_as_float(rho_bits);
 #pragma unroll
@@ -305,31 +289,27 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                 constexpr int r = decltype(rr)::value;
                 fmac_bcast<r>(I[r], vk2, bs);
             });
-            if constexpr (!COMPOSITE) {
-                const float dP = uniform(sc.y);
+            const float dP = uniform(sc.y);
 #pragma unroll
-                for (int r = 0; r < JP; ++r) I[r] += dP;
-            }
+            for (int r = 0; r < JP; ++r) I[r] += dP;
             Unroll<0, JP>::run([&](auto rr) {
                 constexpr int r = decltype(rr)::value;
                 fmac_bcast<r>(eta[r], vk, bvs);
             });
-            if constexpr (!COMPOSITE) {
-                float m[JP];
+            float m[JP];
 #pragma unroll
-                for (int r = 0; r < JP; ++r) m[r] = eta[r] * fast_rcp(I[r]);
-                // four read-out accumulators, each started by a broadcast multiply
-                float acc[4];
-                Unroll<0, 4>::run([&](auto rr) {
-                    constexpr int r = decltype(rr)::value;
-                    acc[r] = bcast<r>(vq) * m[r];
-                });
-                Unroll<4, JP>::run([&](auto rr) {
-                    constexpr int r = decltype(rr)::value;
-                    fmac_bcast<r>(acc[r & 3], vq, m[r]);
-                });
-                opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            }
+            for (int r = 0; r < JP; ++r) m[r] = eta[r] * fast_rcp(I[r]);
+            // four read-out accumulators, each started by a broadcast multiply
+            float acc[4];
+            Unroll<0, 4>::run([&](auto rr) {
+                constexpr int r = decltype(rr)::value;
+                acc[r] = bcast<r>(vq) * m[r];
+            });
+            Unroll<4, JP>::run([&](auto rr) {
+                constexpr int r = decltype(rr)::value;
+                fmac_bcast<r>(acc[r & 3], vq, m[r]);
+            });
+            opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             sc = sc_n;
             bvv = bvv_n;
             vk = vk_n;
@@ -340,31 +320,20 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         s_prev = S.sc[L - 1].z;
         if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
         __syncthreads();
-        if constexpr (!COMPOSITE) {
-            for (int e = tid; e < L * CI; e += NTH) {
-                const int tt = e / CI;
-                const int cc = e % CI;
-                float sum = 0.0f;
+        for (int e = tid; e < L * CI; e += NTH) {
+            const int tt = e / CI;
+            const int cc = e % CI;
+            float sum = 0.0f;
 #pragma unroll
-                for (int g = 0; g < P; ++g) sum += opart[b][tt][g][cc];
-                p.o[(bh * p.T + t0 + tt) * p.dv + tile * CI + cc] = sum;
-            }
+            for (int g = 0; g < P; ++g) sum += opart[b][tt][g][cc];
+            p.o[(bh * p.T + t0 + tt) * p.dv + tile * CI + cc] = sum;
         }
         if (c + 2 < nch) fetch(t0 + 2 * C, chunk_len(c + 2));
     }
 
     // back from the scaled frame: true state = scaled state / s_last
     const float s_last = s_prev;
-    if constexpr (COMPOSITE) {
-        float* cj = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
-#pragma unroll
-        for (int r = 0; r < JP; ++r) {
-            const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i;
-            cj[off] = I[r] / s_last;
-            cj[static_cast<int64_t>(DK) * p.dv + off] = eta[r] / s_last;
-        }
-        if (tid == 0 && tile == 0) p.gdec[bh * p.S + seg] = __expf(-lsum);
-    } else if (seg == p.S - 1) {
+    if (seg == p.S - 1) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = (bh * DK + j0 + r) * p.dv + i;
@@ -475,31 +444,31 @@ constexpr int diag_waves(int DK, int CI) {
     return w < 1 ? 1 : w;
 }
 
-template <int DK, int CI, bool BF16, int MODE>
+template <int DK, int CI, bool BF16>
 static void launch_one(const DiagParams& p, int64_t grid, hipStream_t st) {
     constexpr int W = diag_waves(DK, CI);
-    hipLaunchKernelGGL((k_diag<DK, CI, W, kDiagChunk, BF16, MODE>), dim3(static_cast<uint32_t>(grid)),
+    hipLaunchKernelGGL((k_diag<DK, CI, W, kDiagChunk, BF16>), dim3(static_cast<uint32_t>(grid)),
                        dim3(W * kWave), 0, st, p);
 }
 
-template <int DK, bool BF16, int MODE>
+template <int DK, bool BF16>
 static int launch_dk(const DiagParams& p, int CI, int64_t grid, hipStream_t st) {
     switch (CI) {
-        case 16: launch_one<DK, 16, BF16, MODE>(p, grid, st); break;
-        case 32: launch_one<DK, 32, BF16, MODE>(p, grid, st); break;
-        case 64: launch_one<DK, 64, BF16, MODE>(p, grid, st); break;
+        case 16: launch_one<DK, 16, BF16>(p, grid, st); break;
+        case 32: launch_one<DK, 32, BF16>(p, grid, st); break;
+        case 64: launch_one<DK, 64, BF16>(p, grid, st); break;
         default: return KDN_EUNSUPPORTED;
     }
     return KDN_OK;
 }
 
-template <bool BF16, int MODE>
-static int launch_mode(const DiagParams& p, int64_t dk, int CI, int64_t grid, hipStream_t st) {
+template <bool BF16>
+static int launch_main(const DiagParams& p, int64_t dk, int CI, int64_t grid, hipStream_t st) {
     switch (dk) {
-        case 16: return launch_dk<16, BF16, MODE>(p, CI, grid, st);
-        case 32: return launch_dk<32, BF16, MODE>(p, CI, grid, st);
-        case 64: return launch_dk<64, BF16, MODE>(p, CI, grid, st);
-        case 128: return launch_dk<128, BF16, MODE>(p, CI, grid, st);
+        case 16: return launch_dk<16, BF16>(p, CI, grid, st);
+        case 32: return launch_dk<32, BF16>(p, CI, grid, st);
+        case 64: return launch_dk<64, BF16>(p, CI, grid, st);
+        case 128: return launch_dk<128, BF16>(p, CI, grid, st);
         default: return KDN_EUNSUPPORTED;
     }
 }
@@ -536,7 +505,7 @@ int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipS
 
 // Enqueue the whole diagonal scan.  Arguments were validated by the caller;
 // comp/gdec point into a workspace of the size the planner reported when S > 1.
-int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, hipStream_t st) {
+int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
     const int64_t BH = B * p.H;
     if (BH == 0) return KDN_OK;
     if (p.T == 0) return copy_state_launch(p, B, dk, false, st);
@@ -544,16 +513,9 @@ int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, hipS
     const int64_t ntile = p.dv / CI;
     int rc = diag_prep_launch(p, B, bf16, st);
     if (rc != KDN_OK) return rc;
-    if (p.S > 1) {
-        const int64_t g1 = BH * (p.S - 1) * ntile;
-        rc = bf16 ? launch_mode<true, DIAG_COMP>(p, dk, CI, g1, st)
-                  : launch_mode<false, DIAG_COMP>(p, dk, CI, g1, st);
-        if (rc != KDN_OK) return rc;
-        if ((rc = launch_status()) != KDN_OK) return rc;
-        if ((rc = diag_carry_launch(p, B, dk, false, st)) != KDN_OK) return rc;
-    }
+    if (p.S > 1 && (rc = diag_comp_launch(p, B, dk, bf16, R, st)) != KDN_OK) return rc;
     const int64_t g2 = BH * p.S * ntile;
-    rc = bf16 ? launch_mode<true, DIAG>(p, dk, CI, g2, st) : launch_mode<false, DIAG>(p, dk, CI, g2, st);
+    rc = bf16 ? launch_main<true>(p, dk, CI, g2, st) : launch_main<false>(p, dk, CI, g2, st);
     if (rc != KDN_OK) return rc;
     return launch_status();
 }

@@ -24,7 +24,9 @@ struct DiagParams {
     float* mu_T;
     float4* scal;  // [BH][T] per-token scalars of the diagonal scan (rho, dP, s, -log alpha)
     float* comp;   // [BH][S][2][dk][dv]: segment composites, then carry-in states
-    float* gdec;   // [BH][S]: decay product of each segment
+    float* gdec;   // [BH][S]: decay product of each segment (isotropic scan)
+    float* sub;    // [BH][S-1][R][2][dk][dv]: sub-segment composites (diagonal scan)
+    float* gsub;   // [BH][S-1][R]: decay product of each sub-segment
     int64_t H;
     int64_t T;
     int64_t dv;
@@ -62,9 +64,10 @@ struct MobParams {
 
 int diag_chunk();
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st);
-int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, hipStream_t st);
+int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
+int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int mob_block();
 int mobius_launch(const MobParams& p, int64_t BH, hipStream_t st);

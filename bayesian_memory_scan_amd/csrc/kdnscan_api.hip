@@ -25,6 +25,7 @@ struct Plan {
     int32_t chunk;
     int32_t nchunks;
     int32_t S;
+    int32_t R;   // sub-segments per segment for the composite pass (diagonal scan)
 };
 
 // Chunking and segment count of a (possibly isotropic) segmented scan.
@@ -46,6 +47,15 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
     if (S > pl.nchunks) S = pl.nchunks;
     if (S < 1) S = 1;
     pl.S = static_cast<int32_t>(S);
+    // composites: about two workgroups per CU, at least 4 chunks per sub-segment
+    int64_t R = 1;
+    if (pl.S > 1 && BH > 0) {
+        R = (2 * kNumCU + BH * (pl.S - 1) - 1) / (BH * (pl.S - 1));
+        const int64_t per_seg = pl.nchunks / pl.S;
+        if (R > per_seg / 4) R = per_seg / 4;
+        if (R < 1) R = 1;
+    }
+    pl.R = static_cast<int32_t>(R);
     return pl;
 }
 
@@ -75,6 +85,23 @@ size_t scan_workspace_bytes(int64_t BH, int64_t dk, int64_t dv, const Plan& pl) 
     const size_t comp = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * dk * dv, 256);
     const size_t gdec = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S, 256);
     return comp + gdec;
+}
+
+// Diagonal scan: carry-in states + sub-segment composites and decays.
+struct DiagWs {
+    size_t scal, comp, sub, gsub, total;
+};
+DiagWs diag_workspace(int64_t BH, int64_t T, int64_t dk, int64_t dv, const Plan& pl) {
+    DiagWs w{};
+    w.scal = align_up(16 * static_cast<size_t>(BH) * T, 256);
+    if (pl.S > 1) {
+        const size_t nsub = static_cast<size_t>(BH) * (pl.S - 1) * pl.R;
+        w.comp = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * dk * dv, 256);
+        w.sub = align_up(sizeof(float) * nsub * 2 * dk * dv, 256);
+        w.gsub = align_up(sizeof(float) * nsub, 256);
+    }
+    w.total = w.scal + w.comp + w.sub + w.gsub;
+    return w;
 }
 
 bool finite_positive(float x) { return std::isfinite(x) && x > 0.0f; }
@@ -170,8 +197,8 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const Plan pl = plan_scan(BH, T, d_v);
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
     if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
-    const size_t b_scal = align_up(16 * static_cast<size_t>(BH) * T, 256);   // per-token scalars
-    const size_t need = b_scal + scan_workspace_bytes(BH, d_k, d_v, pl);
+    const DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
+    const size_t need = dw.total;
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
     if (wc != KDN_OK) return wc;
@@ -181,16 +208,17 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
     p.A = A; p.I0 = I0; p.mu0 = mu0;
     p.o = o; p.I_T = I_T; p.mu_T = mu_T;
-    p.scal = reinterpret_cast<float4*>(workspace);
+    char* ws = static_cast<char*>(workspace);
+    p.scal = reinterpret_cast<float4*>(ws);
     if (pl.S > 1) {
-        char* ws = static_cast<char*>(workspace) + b_scal;
-        p.comp = reinterpret_cast<float*>(ws);
-        p.gdec = reinterpret_cast<float*>(ws + align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * d_k * d_v, 256));
+        p.comp = reinterpret_cast<float*>(ws + dw.scal);
+        p.sub = reinterpret_cast<float*>(ws + dw.scal + dw.comp);
+        p.gsub = reinterpret_cast<float*>(ws + dw.scal + dw.comp + dw.sub);
     }
     p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.S = pl.S; p.nchunks = pl.nchunks;
     (void)hipGetLastError();  // launch status below must reflect this call only
-    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
 }
 
 int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
