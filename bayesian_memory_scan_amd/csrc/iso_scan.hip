@@ -34,16 +34,15 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_iso(DiagParams p) {
     constexpr int C = kIsoChunk;
     constexpr int W = DV / 16;                 // waves: one per 16 value columns
     constexpr int NTH = W * kWave;
-    constexpr int KR = DK + 16;                // k row stride for (w k)^T V A-operands: conflict-free
-    constexpr int QR = DK + 2;                 // q, k row stride for Q K^T and Q mu operands: conflict-free
+    constexpr int QR = DK + 2;                 // q, k row stride: conflict-free Q K^T / Q mu reads,
+                                               // at most 2-way for the (w k)^T V reads
     constexpr int VR = DV + 16;                // row stride of v
     constexpr int KSTEPS = DK / 4;             // MFMA k-steps over d_k
     constexpr int MT = DK / 16;                // row tiles of mu
 
     struct Stage {
         float qr[COMPOSITE ? 1 : C][QR];       // q row-major [t][j]
-        float kq[COMPOSITE ? 1 : C][QR];       // k row-major [s][j] (second copy, other stride)
-        float kr[C][KR];                       // k row-major [s][j]
+        float kq[C][QR];                       // k row-major [s][j]
         float vr[C][VR];                       // v row-major [s][i]
         float4 sc[C];                          // b2_t, e^{b_t}, G_t, w_t
         float decay;                           // e^{b_last}
@@ -141,13 +140,11 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_iso(DiagParams p) {
             if (e < QV) {
                 const int t = 4 * e / DK;
                 const int j = 4 * e % DK;
-                const float kv[4] = {rk[n].x, rk[n].y, rk[n].z, rk[n].w};
-                *reinterpret_cast<float4*>(&S.kr[t][j]) = rk[n];
+                *reinterpret_cast<float2*>(&S.kq[t][j]) = make_float2(rk[n].x, rk[n].y);
+                *reinterpret_cast<float2*>(&S.kq[t][j + 2]) = make_float2(rk[n].z, rk[n].w);
                 if constexpr (!COMPOSITE) {
                     *reinterpret_cast<float2*>(&S.qr[t][j]) = make_float2(rq[n].x, rq[n].y);
                     *reinterpret_cast<float2*>(&S.qr[t][j + 2]) = make_float2(rq[n].z, rq[n].w);
-                    *reinterpret_cast<float2*>(&S.kq[t][j]) = make_float2(kv[0], kv[1]);
-                    *reinterpret_cast<float2*>(&S.kq[t][j + 2]) = make_float2(kv[2], kv[3]);
                 }
             }
         }
@@ -245,7 +242,7 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_iso(DiagParams p) {
                 macc[m] *= decay;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    macc[m] = mfma4(S.kr[4 * kk + g][16 * m + c] * wk[kk], bv[kk], macc[m]);
+                    macc[m] = mfma4(S.kq[4 * kk + g][16 * m + c] * wk[kk], bv[kk], macc[m]);
             }
             if constexpr (!COMPOSITE) store_mu_slice();
         }

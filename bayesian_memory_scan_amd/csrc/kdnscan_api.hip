@@ -59,8 +59,8 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
     return pl;
 }
 
-// Segments of the isotropic mean scan: about two workgroups per CU, at least
-// four 16-token chunks per segment.
+// Segments of the isotropic mean scan: about three workgroups per CU, at
+// least four 16-token chunks per segment.
 Plan plan_iso(int64_t BH, int64_t T) {
     Plan pl;
     pl.chunk = iso_chunk();
@@ -70,7 +70,7 @@ Plan plan_iso(int64_t BH, int64_t T) {
     if (ov > 0) {
         S = ov;
     } else if (BH > 0) {
-        S = (2 * kNumCU + BH - 1) / BH;
+        S = (3 * kNumCU + BH - 1) / BH;
         if (S > pl.nchunks / 4) S = pl.nchunks / 4;
     }
     if (S > kMaxSegments) S = kMaxSegments;

@@ -17,9 +17,9 @@
 // Two launches:
 //   k_mob_reduce: per (head, block of 4096 tokens) the block's composite;
 //   k_mob_apply:  per (head, block) the carry-in (ordered product of earlier
-//                 block composites), the in-block exclusive scan of
-//                 per-thread composites (DPP-free: __shfl_up within the wave,
-//                 LDS across the 4 waves), then each thread walks its 16
+//                 block composites, itself a wave scan), the in-block
+//                 exclusive scan of per-thread composites (__shfl_up within the
+//                 wave, LDS across the 4 waves), then each thread walks its 16
 //                 tokens sequentially from its starting precision and writes
 //                 lambda_t and the gates of KLA Metodologia 3:
 //                   lambda^-_t = lambda_{t-1} / (a_t^2 + p_t lambda_{t-1})
@@ -66,16 +66,44 @@ __device__ __forceinline__ Mob mob_shfl_up(const Mob& M, int s) {
 }
 
 
-// Composite of this thread's (up to) 16 consecutive tokens.
-__device__ __forceinline__ Mob thread_composite(const MobParams& p, int64_t bh, int64_t t0) {
+// The 16 consecutive tokens of one thread: float4 loads when the head's rows
+// are 16-byte aligned and the run is whole, else scalar loads (padding:
+// a = 1, p = 0, Lambda = 0, the identity map).
+struct Run16 {
+    float a[kMobPer], p[kMobPer], L[kMobPer];
+};
+
+__device__ __forceinline__ void load_run(const MobParams& P, int64_t bh, int64_t t0, Run16& r) {
+    const float* a = P.a + bh * P.T;
+    const float* pp = P.p + bh * P.T;
+    const float* L = P.Lam + bh * P.T;
+    if ((P.T & 3) == 0 && t0 + kMobPer <= P.T) {
+#pragma unroll
+        for (int u = 0; u < kMobPer; u += 4) {
+            const float4 x = *reinterpret_cast<const float4*>(a + t0 + u);
+            const float4 y = *reinterpret_cast<const float4*>(pp + t0 + u);
+            const float4 z = *reinterpret_cast<const float4*>(L + t0 + u);
+            r.a[u] = x.x; r.a[u + 1] = x.y; r.a[u + 2] = x.z; r.a[u + 3] = x.w;
+            r.p[u] = y.x; r.p[u + 1] = y.y; r.p[u + 2] = y.z; r.p[u + 3] = y.w;
+            r.L[u] = z.x; r.L[u + 1] = z.y; r.L[u + 2] = z.z; r.L[u + 3] = z.w;
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kMobPer; ++u) {
+            const bool in = t0 + u < P.T;
+            r.a[u] = in ? a[t0 + u] : 1.0f;
+            r.p[u] = in ? pp[t0 + u] : 0.0f;
+            r.L[u] = in ? L[t0 + u] : 0.0f;
+        }
+    }
+}
+
+// Composite of a thread's run (later maps on the left).
+__device__ __forceinline__ Mob run_composite(const Run16& r) {
     Mob P = mob_identity();
-    const float* a = p.a + bh * p.T;
-    const float* pp = p.p + bh * p.T;
-    const float* L = p.Lam + bh * p.T;
 #pragma unroll
     for (int u = 0; u < kMobPer; ++u) {
-        const int64_t t = t0 + u;
-        if (t < p.T) P = mob_after(mob_step(a[t], pp[t], L[t]), P);
+        P = mob_after(mob_step(r.a[u], r.p[u], r.L[u]), P);
         if ((u & 3) == 3) P = mob_norm(P);
     }
     return P;
@@ -106,8 +134,10 @@ __global__ __launch_bounds__(kMobThreads) void k_mob_reduce(MobParams p) {
     const int64_t bh = blockIdx.x / p.nblk;
     const int blk = static_cast<int>(blockIdx.x % p.nblk);
     const int64_t t0 = static_cast<int64_t>(blk) * kMobBlock + static_cast<int64_t>(threadIdx.x) * kMobPer;
+    Run16 run;
+    load_run(p, bh, t0, run);
     Mob excl;
-    const Mob inc = block_scan(thread_composite(p, bh, t0), &excl, s_w);
+    const Mob inc = block_scan(run_composite(run), &excl, s_w);
     if (threadIdx.x == kMobThreads - 1) {
         float* o = p.blk + (bh * p.nblk + blk) * 4;
         o[0] = inc.m11; o[1] = inc.m12; o[2] = inc.m21; o[3] = inc.m22;
@@ -121,36 +151,71 @@ __global__ __launch_bounds__(kMobThreads) void k_mob_apply(MobParams p) {
     const int blk = static_cast<int>(blockIdx.x % p.nblk);
     const int64_t t0 = static_cast<int64_t>(blk) * kMobBlock + static_cast<int64_t>(threadIdx.x) * kMobPer;
 
-    if (threadIdx.x == 0) {
+    // carry-in: ordered product of the earlier blocks' composites, a wave scan
+    // over groups of 64 blocks
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
         Mob C = mob_identity();
-        for (int b = 0; b < blk; ++b) {
-            const float* m = p.blk + (bh * p.nblk + b) * 4;
-            C = mob_norm(mob_after(Mob{m[0], m[1], m[2], m[3]}, C));
+        for (int b0 = 0; b0 < blk; b0 += kWave) {
+            Mob x = mob_identity();
+            if (b0 + lane < blk) {
+                const float* m = p.blk + (bh * p.nblk + b0 + lane) * 4;
+                x = Mob{m[0], m[1], m[2], m[3]};
+            }
+#pragma unroll
+            for (int s = 1; s < kWave; s <<= 1) {
+                const Mob y = mob_shfl_up(x, s);
+                if (lane >= s) x = mob_norm(mob_after(x, y));
+            }
+            const Mob grp = Mob{__shfl(x.m11, kWave - 1), __shfl(x.m12, kWave - 1),
+                                __shfl(x.m21, kWave - 1), __shfl(x.m22, kWave - 1)};
+            C = mob_norm(mob_after(grp, C));
         }
-        s_carry = C;
+        if (lane == 0) s_carry = C;
     }
+    Run16 run;
+    load_run(p, bh, t0, run);
     Mob excl;
-    block_scan(thread_composite(p, bh, t0), &excl, s_w);  // also orders s_carry
+    block_scan(run_composite(run), &excl, s_w);  // its barrier also publishes s_carry
     const Mob start = mob_after(excl, s_carry);
 
     const float l0 = p.lambda0 ? p.lambda0[bh] : 1.0f;
     float lam = mob_apply(start, l0);
-    const float* a = p.a + bh * p.T;
-    const float* pp = p.p + bh * p.T;
-    const float* L = p.Lam + bh * p.T;
+    float lo[kMobPer], fo[kMobPer], go[kMobPer];
 #pragma unroll
     for (int u = 0; u < kMobPer; ++u) {
-        const int64_t t = t0 + u;
-        if (t >= p.T) break;
-        const float at = a[t];
-        const float lpred = lam / __builtin_fmaf(pp[t], lam, at * at);
-        const float lnew = lpred + L[t];
-        if (p.lambda_out) p.lambda_out[bh * p.T + t] = lnew;
-        if (p.F) {
-            p.F[bh * p.T + t] = at * lpred / lnew;
-            p.G[bh * p.T + t] = L[t] / lnew;
-        }
+        const float at = run.a[u];
+        const float lpred = lam * fast_rcp(__builtin_fmaf(run.p[u], lam, at * at));
+        const float lnew = lpred + run.L[u];
+        const float inv = fast_rcp(lnew);
+        lo[u] = lnew;
+        fo[u] = at * lpred * inv;
+        go[u] = run.L[u] * inv;
         lam = lnew;
+    }
+    const bool whole = (p.T & 3) == 0 && t0 + kMobPer <= p.T;
+    float* lout = p.lambda_out ? p.lambda_out + bh * p.T : nullptr;
+    float* Fo = p.F ? p.F + bh * p.T : nullptr;
+    float* Go = p.F ? p.G + bh * p.T : nullptr;
+    if (whole) {
+#pragma unroll
+        for (int u = 0; u < kMobPer; u += 4) {
+            if (lout) *reinterpret_cast<float4*>(lout + t0 + u) = make_float4(lo[u], lo[u + 1], lo[u + 2], lo[u + 3]);
+            if (Fo) {
+                *reinterpret_cast<float4*>(Fo + t0 + u) = make_float4(fo[u], fo[u + 1], fo[u + 2], fo[u + 3]);
+                *reinterpret_cast<float4*>(Go + t0 + u) = make_float4(go[u], go[u + 1], go[u + 2], go[u + 3]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kMobPer; ++u) {
+            if (t0 + u >= p.T) break;
+            if (lout) lout[t0 + u] = lo[u];
+            if (Fo) {
+                Fo[t0 + u] = fo[u];
+                Go[t0 + u] = go[u];
+            }
+        }
     }
 }
 
