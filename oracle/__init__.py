@@ -53,6 +53,10 @@ def load(path: str = _LIB):
     lib.oracle_diag_head.restype = ctypes.c_int
     lib.oracle_iso_head.argtypes = [L, D, D, D, ctypes.c_double, L, L, D, D, D, D, D, D, D, D]
     lib.oracle_iso_head.restype = ctypes.c_int
+    PP = ctypes.POINTER(D)
+    lib.oracle_diag_head_bwd.argtypes = [L, L, L, D, D, D, D, D, ctypes.c_double, ctypes.c_double,
+                                         D, D, D, D, D, PP, PP]
+    lib.oracle_diag_head_bwd.restype = ctypes.c_int
     if path == _LIB:
         _lib = lib
     return lib
@@ -99,6 +103,67 @@ def diag_head(q, k, v, beta, d, A, I_prior, I0=None, mu0=None, lib=None):
     if rc != 0:
         raise MemoryError("oracle_diag_head failed")
     return {"o": o, "s": s, "I_T": I_T, "mu_T": mu_T}
+
+
+GRAD_NAMES = ("dq", "dk", "dv", "dbeta", "dd", "dA", "dI_prior", "dI0", "dmu0")
+
+
+def diag_head_bwd(q, k, v, beta, d, A, I_prior, dout, I0=None, mu0=None, dI_T=None,
+                  dmu_T=None, lib=None):
+    """Gradient of one head of the diagonal recurrence (float64 in).
+
+    Returns {name: array} for GRAD_NAMES (dI0 / dmu0 only when I0 / mu0 are
+    given) and {"scale_" + name: array}, the same sums taken over absolute
+    values of their terms.
+    """
+    lib = lib or load()
+    q, k, v, beta, d, dout = (np.ascontiguousarray(x, np.float64) for x in (q, k, v, beta, d, dout))
+    T, dk = q.shape
+    dv = v.shape[1]
+    shapes = {"dq": (T, dk), "dk": (T, dk), "dv": (T, dv), "dbeta": (T, dv), "dd": (T,),
+              "dA": (1,), "dI_prior": (1,), "dI0": (dk, dv), "dmu0": (dk, dv)}
+    out = {n: np.zeros(shapes[n]) for n in GRAD_NAMES}
+    sc = {n: np.zeros(shapes[n]) for n in GRAD_NAMES}
+    opt = lambda x: None if x is None else np.ascontiguousarray(x, np.float64)
+    I0, mu0, dI_T, dmu_T = opt(I0), opt(mu0), opt(dI_T), opt(dmu_T)
+    D = ctypes.POINTER(ctypes.c_double)
+    gp = (D * 9)(*[_ptr(out[n]) for n in GRAD_NAMES])
+    sp = (D * 9)(*[_ptr(sc[n]) for n in GRAD_NAMES])
+    rc = lib.oracle_diag_head_bwd(T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
+                                  float(A), float(I_prior), _ptr(I0), _ptr(mu0), _ptr(dout),
+                                  _ptr(dI_T), _ptr(dmu_T), gp, sp)
+    if rc != 0:
+        raise MemoryError("oracle_diag_head_bwd failed")
+    res = {n: out[n] for n in GRAD_NAMES if not (n == "dI0" and I0 is None)
+           and not (n == "dmu0" and mu0 is None)}
+    res.update({"scale_" + n: sc[n] for n in res})
+    res["dA"], res["dI_prior"] = float(res["dA"][0]), float(res["dI_prior"][0])
+    res["scale_dA"], res["scale_dI_prior"] = float(res["scale_dA"][0]), float(res["scale_dI_prior"][0])
+    return res
+
+
+def diag_scan_bwd(inp: dict, dout: np.ndarray, heads=None, threads=None, I0=None, mu0=None,
+                  dI_T=None, dmu_T=None, lib=None):
+    """Gradients over heads of a synthetic-input dict; dout [B,H,T,dv] float.
+
+    Returns {(b,h): diag_head_bwd(...) result}.
+    """
+    spec = inp["spec"]
+    B, H = inp["q"].shape[:2]
+    heads = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    lib = lib or load()
+    pick = lambda x, b, h: None if x is None else np.asarray(x[b, h], np.float64)
+
+    def one(bh):
+        b, h = bh
+        args = [decode(inp[n][b, h], spec.dtype) for n in ("q", "k", "v", "beta", "d")]
+        return bh, diag_head_bwd(*args, A=float(inp["A"][h]), I_prior=inp["I_prior"],
+                                 dout=np.asarray(dout[b, h], np.float64),
+                                 I0=pick(I0, b, h), mu0=pick(mu0, b, h),
+                                 dI_T=pick(dI_T, b, h), dmu_T=pick(dmu_T, b, h), lib=lib)
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        return dict(ex.map(one, heads))
 
 
 def diag_scan(inp: dict, heads=None, threads=None, t_range=None, I0=None, mu0=None, lib=None):

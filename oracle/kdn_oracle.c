@@ -161,3 +161,128 @@ int oracle_iso_head(long T, const double* a, const double* p, const double* Lam,
     free(mu);
     return 0;
 }
+
+/*
+ * Reverse-mode gradient of the diagonal-precision memory above.  The pages
+ * train these layers but print no gradient, so this is the mechanical adjoint
+ * of the printed recurrence (Palimpsa summary, Metodologia items 1-2, in its
+ * direct mu form), written entry by entry: every memory entry [j][i] follows
+ * its own scalar recurrence (the update is elementwise), so for each entry
+ * the forward values I_t, mu_t are recorded, then walked back in time.
+ *
+ * For the scalar loss
+ *   L = sum_t sum_i dout[t][i] o_t[i] + sum_e dI_T[e] I_T[e] + sum_e dmu_T[e] mu_T[e]
+ * (dI_T, dmu_T may be NULL = zero) it returns dL/d(input) in
+ *   g[0] dq [T][dk]   g[1] dk [T][dk]   g[2] dv [T][dv]   g[3] dbeta [T][dv]
+ *   g[4] dd [T]       g[5] dA [1]       g[6] dI_prior [1]
+ *   g[7] dI0 [dk][dv] g[8] dmu0 [dk][dv]
+ * With I0 == NULL the start is I_prior, whose path then feeds g[6] and g[7]
+ * is not written; with mu0 == NULL the start mean is 0 and g[8] is not
+ * written.
+ *
+ * scale (may be NULL, else 9 arrays shaped like g) receives the same
+ * quantities computed with every term replaced by its absolute value: the
+ * natural error scale of each gradient (it bounds |g|).
+ *
+ * Returns 0, or -1 if scratch memory cannot be allocated.
+ */
+int oracle_diag_head_bwd(long T, long dk, long dv,
+                         const double* q, const double* k, const double* v,
+                         const double* beta, const double* d,
+                         double A, double I_prior,
+                         const double* I0, const double* mu0,
+                         const double* dout, const double* dI_T, const double* dmu_T,
+                         double* const* g, double* const* scale)
+{
+    const long n = dk * dv;
+    double* Ih = (double*)malloc(sizeof(double) * (T + 1));   /* I before/after each token */
+    double* mh = (double*)malloc(sizeof(double) * (T + 1));   /* mu before/after each token */
+    if (!Ih || !mh) { free(Ih); free(mh); return -1; }
+
+    const long sizes[9] = {T * dk, T * dk, T * dv, T * dv, T, 1, 1, n, n};
+    for (int a = 0; a < 9; ++a) {
+        if ((a == 7 && !I0) || (a == 8 && !mu0)) continue;
+        memset(g[a], 0, sizeof(double) * sizes[a]);
+        if (scale) memset(scale[a], 0, sizeof(double) * sizes[a]);
+    }
+
+    for (long j = 0; j < dk; ++j) {
+        for (long i = 0; i < dv; ++i) {
+            const long e = j * dv + i;
+
+            /* forward, recording the entry's history */
+            Ih[0] = I0 ? I0[e] : I_prior;
+            mh[0] = mu0 ? mu0[e] : 0.0;
+            for (long t = 0; t < T; ++t) {
+                const double alpha = exp(-A * d[t]);
+                const double b = beta[t * dv + i], kk = k[t * dk + j], vv = v[t * dv + i];
+                const double I_old = Ih[t];
+                const double I_new = alpha * I_old + (1.0 - alpha) * I_prior + b * kk * kk;
+                mh[t + 1] = alpha * (I_old / I_new) * mh[t] + (1.0 / I_new) * (b * vv * kk);
+                Ih[t + 1] = I_new;
+            }
+
+            /* adjoints of the state after the last token, and their magnitudes */
+            double gI = dI_T ? dI_T[e] : 0.0, gM = dmu_T ? dmu_T[e] : 0.0;
+            double aI = fabs(gI), aM = fabs(gM);
+
+            for (long t = T - 1; t >= 0; --t) {
+                const double alpha = exp(-A * d[t]);
+                const double b = beta[t * dv + i], kk = k[t * dk + j], vv = v[t * dv + i];
+                const double qq = q[t * dk + j], go = dout[t * dv + i];
+                const double Ip = Ih[t], In = Ih[t + 1], mp = mh[t], mn = mh[t + 1];
+
+                /* read-out o_t[i] += q_t[j] mu_t[j][i] */
+                gM += qq * go;
+                aM += fabs(qq * go);
+                g[0][t * dk + j] += mn * go;
+                if (scale) scale[0][t * dk + j] += fabs(mn * go);
+
+                /* mu_t = (alpha I_{t-1} mu_{t-1} + b v k) / I_t: its I_t dependence */
+                const double gIn = gI - gM * mn / In;
+                const double aIn = aI + aM * fabs(mn) / In;
+
+                /* I_t = alpha I_{t-1} + (1 - alpha) I_prior + b k^2 and mu_t's own inputs */
+                const double g_alpha = gM * Ip * mp / In + gIn * (Ip - I_prior);
+                const double a_alpha = aM * fabs(Ip * mp) / In + aIn * fabs(Ip - I_prior);
+                g[1][t * dk + j] += gM * b * vv / In + gIn * 2.0 * b * kk;
+                g[2][t * dv + i] += gM * b * kk / In;
+                g[3][t * dv + i] += gM * vv * kk / In + gIn * kk * kk;
+                g[4][t] += g_alpha * (-A * alpha);
+                g[5][0] += g_alpha * (-d[t] * alpha);
+                g[6][0] += gIn * (1.0 - alpha);
+                if (scale) {
+                    scale[1][t * dk + j] += aM * fabs(b * vv) / In + aIn * 2.0 * fabs(b * kk);
+                    scale[2][t * dv + i] += aM * fabs(b * kk) / In;
+                    scale[3][t * dv + i] += aM * fabs(vv * kk) / In + aIn * kk * kk;
+                    scale[4][t] += a_alpha * fabs(A * alpha);
+                    scale[5][0] += a_alpha * fabs(d[t] * alpha);
+                    scale[6][0] += aIn * (1.0 - alpha);
+                }
+
+                /* carry to the state before token t */
+                const double gM_prev = gM * alpha * Ip / In;
+                const double gI_prev = gM * alpha * mp / In + gIn * alpha;
+                aI = aM * alpha * fabs(mp) / In + aIn * alpha;
+                aM = aM * alpha * Ip / In;
+                gM = gM_prev;
+                gI = gI_prev;
+            }
+
+            if (I0) {
+                g[7][e] = gI;
+                if (scale) scale[7][e] = aI;
+            } else {
+                g[6][0] += gI;
+                if (scale) scale[6][0] += aI;
+            }
+            if (mu0) {
+                g[8][e] = gM;
+                if (scale) scale[8][e] = aM;
+            }
+        }
+    }
+    free(Ih);
+    free(mh);
+    return 0;
+}

@@ -294,4 +294,114 @@ def pin_iso_mean_closed_form(lib):
 
 
 ISO_PINS = [pin_iso_mobius, pin_iso_scalar_kalman, pin_iso_fixed_point, pin_iso_mean_closed_form]
-ALL_PINS = DIAG_PINS + ISO_PINS
+
+
+# ---------------------------------------------------------------------------
+# Gradient of the diagonal path (the pages print none: it is pinned to the
+# forward oracle by central finite differences, which share no code with it)
+# ---------------------------------------------------------------------------
+def _bwd_loss_weights(c, seed=99):
+    g = np.random.default_rng(seed)
+    T, dk = c["q"].shape
+    dv = c["v"].shape[1]
+    return g.standard_normal((T, dv)), g.standard_normal((dk, dv)), g.standard_normal((dk, dv))
+
+
+def _loss(lib, c, W):
+    r = _run_diag(lib, c)
+    return float(np.sum(W[0] * r["o"]) + np.sum(W[1] * r["I_T"]) + np.sum(W[2] * r["mu_T"]))
+
+
+def _finite_difference(lib, c, W, name, idx, rel_h=1e-5):
+    x = c[name]
+    base = float(x if np.isscalar(x) else x[idx])
+    h = rel_h * max(1.0, abs(base))
+
+    def at(val):
+        if np.isscalar(x):
+            return _loss(lib, {**c, name: val}, W)
+        y = np.array(x, dtype=np.float64, copy=True)
+        y[idx] = val
+        return _loss(lib, {**c, name: y}, W)
+
+    return (at(base + h) - at(base - h)) / (2.0 * h)
+
+
+def _run_bwd(lib, c, W, with_final=True):
+    return oracle.diag_head_bwd(c["q"], c["k"], c["v"], c["beta"], c["d"], c["A"], c["I_prior"],
+                                W[0], I0=c.get("I0"), mu0=c.get("mu0"),
+                                dI_T=W[1] if with_final else None,
+                                dmu_T=W[2] if with_final else None, lib=lib)
+
+
+def _check_fd(lib, c, W, grads, names):
+    for gname, iname in names:
+        x = c[iname]
+        idxs = [()] if np.isscalar(x) else list(np.ndindex(np.shape(x)))
+        fd = np.array([_finite_difference(lib, c, W, iname, ix) for ix in idxs])
+        got = np.atleast_1d(np.asarray(grads[gname], np.float64)).reshape(-1)
+        _close(got, fd, rtol=2e-6, atol=1e-9, what=f"{gname} vs finite differences")
+
+
+def pin_bwd_finite_differences(lib):
+    """Every gradient, with a starting state and gradients into the final
+    state, equals the central finite difference of the forward oracle's loss."""
+    c = diag_case(seed=21, T=6, dk=3, dv=2, A=0.9, I_prior=0.8)
+    W = _bwd_loss_weights(c)
+    g = _run_bwd(lib, c, W)
+    _check_fd(lib, c, W, g, [("dq", "q"), ("dk", "k"), ("dv", "v"), ("dbeta", "beta"),
+                             ("dd", "d"), ("dA", "A"), ("dI_prior", "I_prior"),
+                             ("dI0", "I0"), ("dmu0", "mu0")])
+
+
+def pin_bwd_prior_start(lib):
+    """Without a starting state the memory starts at I_prior (mean 0): the
+    start's dependence on I_prior is part of dI_prior, and no state gradients
+    are returned."""
+    c = diag_case(seed=22, T=5, dk=2, dv=3, A=1.4, I_prior=1.7, with_state=False)
+    W = _bwd_loss_weights(c, seed=5)
+    g = _run_bwd(lib, c, W)
+    assert "dI0" not in g and "dmu0" not in g
+    _check_fd(lib, c, W, g, [("dI_prior", "I_prior"), ("dd", "d"), ("dk", "k"), ("dbeta", "beta")])
+
+
+def pin_bwd_readout_only(lib):
+    """Loss on the outputs alone (no final-state gradient) still matches."""
+    c = diag_case(seed=23, T=7, dk=2, dv=2, A=0.3, I_prior=2.2)
+    W = _bwd_loss_weights(c, seed=6)
+    W = (W[0], np.zeros_like(W[1]), np.zeros_like(W[2]))
+    g = _run_bwd(lib, c, W, with_final=False)
+    _check_fd(lib, c, W, g, [("dq", "q"), ("dv", "v"), ("dI0", "I0"), ("dmu0", "mu0"),
+                             ("dA", "A")])
+
+
+def pin_bwd_empty_sequence(lib):
+    """T = 0: the final state is the starting state, so its gradient passes
+    straight through and every per-token gradient is empty."""
+    c = diag_case(seed=24, T=0, dk=3, dv=2)
+    W = _bwd_loss_weights(c)
+    g = _run_bwd(lib, c, W)
+    _close(g["dI0"], W[1], what="dI0 at T=0")
+    _close(g["dmu0"], W[2], what="dmu0 at T=0")
+    assert g["dA"] == 0.0 and g["dI_prior"] == 0.0 and g["dq"].size == 0
+
+
+def pin_bwd_scale_bounds(lib):
+    """Each returned scale is the sum of the absolute values of the terms of
+    its gradient, so it bounds it; and it is not vacuous (a gradient that is a
+    single product has |g| equal to its scale)."""
+    c = diag_case(seed=25, T=8, dk=3, dv=3)
+    W = _bwd_loss_weights(c)
+    g = _run_bwd(lib, c, W)
+    for n in oracle.GRAD_NAMES:
+        assert np.all(np.abs(g[n]) <= g["scale_" + n] * (1 + 1e-12) + 1e-300), n
+    # dq_t[j] = sum_i mu_t[j,i] dout_t[i] with dv = 1 is one product
+    c1 = diag_case(seed=26, T=4, dk=2, dv=1)
+    W1 = _bwd_loss_weights(c1)
+    g1 = _run_bwd(lib, c1, W1)
+    _close(np.abs(g1["dq"]), g1["scale_dq"], what="single-term scale")
+
+
+BWD_PINS = [pin_bwd_finite_differences, pin_bwd_prior_start, pin_bwd_readout_only,
+            pin_bwd_empty_sequence, pin_bwd_scale_bounds]
+ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS

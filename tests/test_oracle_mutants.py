@@ -23,6 +23,19 @@ MUTANTS = {
     "iso_mean_not_decayed": ("mean_pred = a[t] * mu[e]", "mean_pred = mu[e]"),
     "iso_write_uses_query": ("Lam[t] * kt[j] * vt[i]", "Lam[t] * qt[j] * vt[i]"),
     "iso_obs_precision_squared": ("lambda_pred + Lam[t];", "lambda_pred + Lam[t] * Lam[t];"),
+    # gradient of the diagonal path
+    "bwd_mean_ignores_precision": ("gIn = gI - gM * mn / In;", "gIn = gI;"),
+    "bwd_key_square_factor": ("gIn * 2.0 * b * kk;", "gIn * b * kk;"),
+    "bwd_gate_sign": ("g[4][t] += g_alpha * (-A * alpha);", "g[4][t] += g_alpha * (A * alpha);"),
+    "bwd_gate_drops_prior": ("gIn * (Ip - I_prior);", "gIn * Ip;"),
+    "bwd_mean_carry_undecayed": ("gM_prev = gM * alpha * Ip / In;", "gM_prev = gM * Ip / In;"),
+    "bwd_precision_carry_drops_mean": ("gI_prev = gM * alpha * mp / In + gIn * alpha;",
+                                       "gI_prev = gIn * alpha;"),
+    "bwd_query_grad_uses_old_mean": ("g[0][t * dk + j] += mn * go;", "g[0][t * dk + j] += mp * go;"),
+    "bwd_value_grad_drops_beta": ("g[2][t * dv + i] += gM * b * kk / In;",
+                                  "g[2][t * dv + i] += gM * kk / In;"),
+    "bwd_prior_start_dropped": ("g[6][0] += gI;", "g[6][0] += 0.0 * gI;"),
+    "bwd_readout_uses_key": ("gM += qq * go;", "gM += kk * go;"),
 }
 
 
