@@ -1,0 +1,781 @@
+// diag_bwd.hip -- gradient of the diagonal-precision memory scan.
+//
+// Forward (Palimpsa, "Learning to Remember, Learn, and Forget in
+// Attention-Based Models", Metodologia 1-2; read-out as in the KLA summary,
+// Metodologia 1), per head and memory entry [j][i]:
+//   I_t = alpha_t I_{t-1} + (1 - alpha_t) I_prior + beta_t[i] k_t[j]^2
+//   eta_t = alpha_t eta_{t-1} + beta_t[i] v_t[i] k_t[j]     (eta = I mu)
+//   mu_t = eta_t / I_t,   o_t[i] = sum_j q_t[j] mu_t[j][i],   alpha_t = exp(-A d_t)
+// The pages train with these layers but print no gradient; this file runs the
+// adjoint of the information form.  With g_t = q_t[j] dout_t[i] the adjoints
+// of the state after token t obey, backwards in time,
+//   lam_eta_t = alpha_{t+1} lam_eta_{t+1} + g_t / I_t
+//   lam_I_t   = alpha_{t+1} lam_I_{t+1}  - g_t mu_t / I_t
+// and the input gradients are contractions of them:
+//   dbeta_t[i] = sum_j lam_I k_j^2 + lam_eta v_i k_j     dv_t[i] = beta_i sum_j lam_eta k_j
+//   dk_t[j]    = sum_i 2 lam_I beta_i k_j + lam_eta beta_i v_i
+//   dq_t[j]    = sum_i mu_t dout_t[i]
+//   dalpha_t   = sum_ji lam_I_t (I_{t-1} - I_prior) + lam_eta_t eta_{t-1}
+// The state is rebuilt as J = I - I_prior (J_t = alpha_t J_{t-1} + beta k^2)
+// and eta, in the scaled frame of the forward pass (J~ = s J, eta~ = s eta
+// with s = prod 1/alpha since the frame start), where both are plain
+// accumulations.  The scaled adjoints L = lam_eta / s and M = lam_I / s
+// accumulate the same way,
+//   L += g / I~,   M -= g mu / I~     (I~ = J~ + s I_prior),
+// a frame change multiplies (J~, eta~) and (L, M) by the same rho, and
+//   dalpha_t = (rho_t / alpha_t) sum_ji M_t J~_{t-1} + L_t eta~_{t-1}
+// involves no cancellation (J >= 0).
+//
+// Work decomposition (one GPU):
+//   * a checkpoint pass runs the state recurrence forward and stores the state
+//     before every 16-token chunk (unscaled);
+//   * the reverse pass walks chunks last to first.  Inside a chunk it rebuilds
+//     the states of 3 or 4 tokens at a time from the chunk's checkpoint, keeps them
+//     in registers and walks those tokens backwards;
+//   * lane <-> key row j, 16 value columns per lane (one DPP row of 16 lanes
+//     holds the 16 columns' value-side operands, which reach the fmacs as
+//     row broadcasts); a wave covers 64 rows x 16 columns and a workgroup
+//     d_k rows x min(d_v, 64) columns;
+//   * sums over i (dq, dk) are in-lane, then over the column waves through
+//     LDS once per chunk, then over column tiles in a finishing pass; sums
+//     over j (dbeta, dv) go through a 64-lane butterfly per token, then LDS.
+#include "kdn_lane.h"
+#include "kdn_params.h"
+
+namespace kdn {
+
+constexpr int kBwdChunk = 16;   // tokens per chunk: the checkpoint interval
+
+template <int DK, int DV>
+struct BwdShape {
+    static constexpr int RH = DK / 64;                 // waves along the key rows
+    static constexpr int CI = DV < 64 ? DV : 64;       // value columns per workgroup
+    static constexpr int CG = CI / 16;                 // waves along the value columns
+    static constexpr int W = RH * CG;
+    static constexpr int NTH = W * kWave;
+    static constexpr int NTILE = DV / CI;
+    static constexpr int BLK = DK * CI;                // floats of one checkpoint half
+    // token states held in registers at once: 4, or 3 where two waves share a
+    // SIMD (256 registers per lane)
+    static constexpr int HELD = W > 4 ? 3 : 4;
+    static_assert(DK == 64 || DK == 128, "key rows: one or two waves of 64");
+};
+
+template <int DK, int CI, bool REV>
+struct BwdStage {
+    float k[kBwdChunk][DK];
+    float q[REV ? kBwdChunk : 1][DK];
+    float b[kBwdChunk][CI];
+    float v[kBwdChunk][CI];
+    float g[REV ? kBwdChunk : 1][CI];      // dout
+    float4 sc[kBwdChunk + 1];              // frame scalars; [L] = next chunk's first token
+};
+
+// Global -> registers (in flight while the previous chunk computes) -> LDS.
+template <int DK, int CI, int NTH, bool BF16, bool REV>
+struct BwdLoader {
+    using E = typename std::conditional<BF16, uint16_t, float>::type;
+    static constexpr int VW = BF16 ? 8 : 4;
+    static constexpr int VK = kBwdChunk * DK / VW;
+    static constexpr int VB = kBwdChunk * CI / VW;
+    static constexpr int VG = kBwdChunk * CI / 4;
+    static constexpr int NVK = (VK + NTH - 1) / NTH;
+    static constexpr int NVB = (VB + NTH - 1) / NTH;
+    static constexpr int NVG = (VG + NTH - 1) / NTH;
+
+    uint4 rk[NVK], rq[REV ? NVK : 1], rb[NVB], rv[NVB];
+    float4 rg[REV ? NVG : 1];
+    float4 rsc;
+
+    __device__ __forceinline__ void fetch(const BwdParams& p, int64_t bh, int tile, int64_t t0,
+                                          int L, int tid) {
+        const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
+        const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
+        const E* bth = static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI;
+        const E* vh = static_cast<const E*>(p.v) + bh * p.T * p.dv + tile * CI;
+#pragma unroll
+        for (int n = 0; n < NVK; ++n) {
+            const int vi = tid + n * NTH;
+            if (vi < VK && vi * VW < L * DK) {
+                rk[n] = ld16(kh + t0 * DK + static_cast<int64_t>(vi) * VW);
+                if constexpr (REV) rq[n] = ld16(qh + t0 * DK + static_cast<int64_t>(vi) * VW);
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVB; ++n) {
+            const int vi = tid + n * NTH;
+            const int row = vi / (CI / VW);
+            const int cv = vi % (CI / VW);
+            if (vi < VB && row < L) {
+                const int64_t off = (t0 + row) * p.dv + cv * VW;
+                rb[n] = ld16(bth + off);
+                rv[n] = ld16(vh + off);
+            }
+        }
+        if constexpr (REV) {
+            const float* gh = p.dout + bh * p.T * p.dv + tile * CI;
+#pragma unroll
+            for (int n = 0; n < NVG; ++n) {
+                const int vi = tid + n * NTH;
+                const int row = vi / (CI / 4);
+                const int cv = vi % (CI / 4);
+                if (vi < VG && row < L)
+                    rg[n] = *reinterpret_cast<const float4*>(gh + (t0 + row) * p.dv + cv * 4);
+            }
+        }
+        if (tid <= L) {
+            const int64_t t = t0 + tid;
+            rsc = t < p.T ? p.scal[bh * p.T + t] : make_float4(1.0f, 0.0f, 1.0f, 0.0f);
+        }
+    }
+
+    __device__ __forceinline__ void commit(BwdStage<DK, CI, REV>& S, int L, int tid) {
+#pragma unroll
+        for (int n = 0; n < NVK; ++n) {
+            const int vi = tid + n * NTH;
+            if (vi < VK && vi * VW < L * DK) {
+                const int row = vi * VW / DK;
+                const int c0 = vi * VW % DK;
+                float f[VW];
+                widen<BF16>(rk[n], f);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) S.k[row][c0 + e] = f[e];
+                if constexpr (REV) {
+                    widen<BF16>(rq[n], f);
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
+                }
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVB; ++n) {
+            const int vi = tid + n * NTH;
+            const int row = vi / (CI / VW);
+            const int c0 = (vi % (CI / VW)) * VW;
+            if (vi < VB && row < L) {
+                float fb[VW], fv[VW];
+                widen<BF16>(rb[n], fb);
+                widen<BF16>(rv[n], fv);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) {
+                    S.b[row][c0 + e] = fb[e];
+                    S.v[row][c0 + e] = fv[e];
+                }
+            }
+        }
+        if constexpr (REV) {
+#pragma unroll
+            for (int n = 0; n < NVG; ++n) {
+                const int vi = tid + n * NTH;
+                const int row = vi / (CI / 4);
+                const int c0 = (vi % (CI / 4)) * 4;
+                if (vi < VG && row < L) *reinterpret_cast<float4*>(&S.g[row][c0]) = rg[n];
+            }
+        }
+        if (tid <= L) S.sc[tid] = rsc;
+    }
+};
+
+// One forward token on a lane's 16 entries, in place:
+//   state *= rho (frame change), J~ += beta_c s k_j^2, eta~ += beta_c v_c s k_j.
+// bs = beta_c s and bvs = beta_c v_c s are held by lane c of each DPP row.
+__device__ __forceinline__ void bwd_step_inplace(float (&I)[16], float (&E)[16], float rho,
+                                                 float bs, float bvs, float kj, float k2j) {
+    const uint32_t rb = __builtin_amdgcn_readfirstlane(__float_as_uint(rho));
+    if (rb != 0x3f800000u) {
+        const float r = __uint_as_float(rb);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            I[c] *= r;
+            E[c] *= r;
+        }
+    }
+    Unroll<0, 16>::run([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        fmac_bcast<c>(I[c], bs, k2j);
+    });
+    Unroll<0, 16>::run([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        fmac_bcast<c>(E[c], bvs, kj);
+    });
+}
+
+// The same token, reading the state before it from (Ii, Ei) and writing the
+// state after it to (Io, Eo).
+__device__ __forceinline__ void bwd_step_copy(const float (&Ii)[16], const float (&Ei)[16],
+                                              float (&Io)[16], float (&Eo)[16], float rho,
+                                              float bs, float bvs, float kj, float k2j) {
+    const uint32_t rb = __builtin_amdgcn_readfirstlane(__float_as_uint(rho));
+    if (rb != 0x3f800000u) {
+        const float r = __uint_as_float(rb);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            Io[c] = Ii[c] * r;
+            Eo[c] = Ei[c] * r;
+        }
+    } else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            Io[c] = Ii[c];
+            Eo[c] = Ei[c];
+        }
+    }
+    Unroll<0, 16>::run([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        fmac_bcast<c>(Io[c], bs, k2j);
+    });
+    Unroll<0, 16>::run([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        fmac_bcast<c>(Eo[c], bvs, kj);
+    });
+}
+
+__device__ __forceinline__ void load16(const float* src, float (&x)[16]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const float4 f = reinterpret_cast<const float4*>(src)[n];
+        x[4 * n] = f.x; x[4 * n + 1] = f.y; x[4 * n + 2] = f.z; x[4 * n + 3] = f.w;
+    }
+}
+
+__device__ __forceinline__ void store16(float* dst, const float (&x)[16]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+        reinterpret_cast<float4*>(dst)[n] = make_float4(x[4 * n], x[4 * n + 1], x[4 * n + 2], x[4 * n + 3]);
+}
+
+// Starting state of a lane's 16 entries, unscaled: I0 (or I_prior), its
+// excess J0 = I0 - I_prior, mu0 (absent: 0) and eta0 = I0 mu0.
+__device__ __forceinline__ void start_state(const BwdParams& p, int64_t off, float (&I)[16],
+                                            float (&J)[16], float (&E)[16], float (&m0)[16]) {
+    if (p.I0) load16(p.I0 + off, I);
+    else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) I[c] = p.I_prior;
+    }
+    if (p.mu0) load16(p.mu0 + off, m0);
+    else {
+#pragma unroll
+        for (int c = 0; c < 16; ++c) m0[c] = 0.0f;
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        J[c] = I[c] - p.I_prior;
+        E[c] = I[c] * m0[c];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Checkpoint pass: the state before every chunk, unscaled, in the slab layout
+// [bh][tile][chunk][I | eta][column wave][row][16] the reverse pass reads.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdParams p) {
+    using Sh = BwdShape<DK, DV>;
+    constexpr int C = kBwdChunk;
+    constexpr int CI = Sh::CI;
+    __shared__ BwdStage<DK, CI, false> stg[2];
+    BwdLoader<DK, CI, Sh::NTH, BF16, false> ld;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = tid / kWave;
+    const int rh = w / Sh::CG;
+    const int cg = w % Sh::CG;
+    const int j = rh * 64 + lane;
+    const int lc = cg * 16 + (lane & 15);      // this lane's value column in the tile (for operands)
+    const int64_t wg = xcd_local_id();
+    const int tile = static_cast<int>(wg % Sh::NTILE);
+    const int64_t bh = wg / Sh::NTILE;
+    const int64_t nch = p.nchunks;
+
+    float I[16], m0[16], J[16], E[16];
+    start_state(p, (bh * DK + j) * p.dv + tile * CI + cg * 16, I, J, E, m0);
+    float* ck = p.ckpt + (bh * Sh::NTILE + tile) * nch * 2 * Sh::BLK + (cg * DK + j) * 16;
+    store16(ck, J);
+    store16(ck + Sh::BLK, E);
+
+    auto chunk_len = [&](int64_t c) -> int {
+        const int64_t rem = p.T - c * C;
+        return static_cast<int>(rem < C ? rem : C);
+    };
+    const int64_t nrun = nch - 1;               // the last chunk's end state is not needed
+    if (nrun > 0) {
+        ld.fetch(p, bh, tile, 0, chunk_len(0), tid);
+        ld.commit(stg[0], chunk_len(0), tid);
+    }
+    __syncthreads();
+    if (nrun > 1) ld.fetch(p, bh, tile, C, chunk_len(1), tid);
+
+    for (int64_t c = 0; c < nrun; ++c) {
+        const int b = static_cast<int>(c & 1);
+        const BwdStage<DK, CI, false>& S = stg[b];
+        const int L = chunk_len(c);
+        for (int tt = 0; tt < L; ++tt) {
+            const float4 sc = S.sc[tt];
+            const float kj = S.k[tt][j];
+            const float b = S.b[tt][lc] * sc.z;
+            const float bvs = dpp_src(b * S.v[tt][lc]);
+            bwd_step_inplace(J, E, sc.x, dpp_src(b), bvs, kj, kj * kj);
+        }
+        // unscale and store the state before chunk c + 1
+        const float inv_s = 1.0f / uniform(S.sc[L - 1].z);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            J[e] *= inv_s;
+            E[e] *= inv_s;
+        }
+        float* dst = ck + (c + 1) * 2 * Sh::BLK;
+        store16(dst, J);
+        store16(dst + Sh::BLK, E);
+        if (c + 1 < nrun) ld.commit(stg[b ^ 1], chunk_len(c + 1), tid);
+        __syncthreads();
+        if (c + 2 < nrun) ld.fetch(p, bh, tile, (c + 2) * C, chunk_len(c + 2), tid);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Reverse pass.
+// ---------------------------------------------------------------------------
+template <int DK, int DV, bool BF16>
+__global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams p) {
+    using Sh = BwdShape<DK, DV>;
+    constexpr int C = kBwdChunk;
+    constexpr int CI = Sh::CI;
+    constexpr int CG = Sh::CG;
+    constexpr int RH = Sh::RH;
+    constexpr int W = Sh::W;
+    constexpr int NTH = Sh::NTH;
+    constexpr int HELD = Sh::HELD;
+    __shared__ BwdStage<DK, CI, true> stg[2];
+    __shared__ float2 dqk[C][CG][DK];          // per-wave dq and (dk / s) partial sums
+    __shared__ float pq[C][RH][CG][32];        // per-wave sums over rows: P (0..15), Q (16..31)
+    __shared__ float2 xs[C][W];                // per-wave dalpha sums (X1, X2) of token t + 1
+    __shared__ float4 xsc[C];                  // their per-token factors
+    BwdLoader<DK, CI, NTH, BF16, true> ld;
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int w = tid / kWave;
+    const int rh = w / CG;
+    const int cg = w % CG;
+    const int j = rh * 64 + lane;
+    const int lc = cg * 16 + (lane & 15);
+    const int64_t wg = xcd_local_id();
+    const int tile = static_cast<int>(wg % Sh::NTILE);
+    const int64_t bh = wg / Sh::NTILE;
+    const int64_t T = p.T;
+    const int64_t nch = p.nchunks;
+    const float I_prior = p.I_prior;
+    const int64_t ent = (bh * DK + j) * p.dv + tile * CI + cg * 16;   // this lane's 16 entries
+    // this column tile's slices of the partial-sum buffers
+    float* const part_dq = p.part_dq + tile * p.BH * T * DK;
+    float* const part_dk = p.part_dk + tile * p.BH * T * DK;
+    float* const part_da = p.part_da + tile * p.BH * T;
+    float* const part_dip = p.part_dip + tile * p.BH * T;
+
+    float L[16], M[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+        L[c] = 0.0f;
+        M[c] = 0.0f;
+    }
+
+    const float* ckb = p.ckpt + (bh * Sh::NTILE + tile) * nch * 2 * Sh::BLK + (cg * DK + j) * 16;
+
+    auto chunk_len = [&](int64_t c) -> int {
+        const int64_t rem = T - c * C;
+        return static_cast<int>(rem < C ? rem : C);
+    };
+
+    if (nch > 0) {
+        ld.fetch(p, bh, tile, (nch - 1) * C, chunk_len(nch - 1), tid);
+        ld.commit(stg[0], chunk_len(nch - 1), tid);
+    }
+    __syncthreads();
+
+    // one reverse step: token tt of the staged chunk, (J, E) its state after the token
+    auto reverse_step = [&](const BwdStage<DK, CI, true>& S, int tt, int64_t t0, int Lc,
+                            const float (&J)[16], const float (&E)[16]) __attribute__((always_inline)) {
+        const int64_t t = t0 + tt;
+        const float4 sct = S.sc[tt];
+        const float sIp = uniform(sct.z) * I_prior;     // s_t I_prior: I~ = J~ + s I_prior
+        if (t + 1 < T) {
+            // dalpha of token t+1: (L, M) still belong to it (its frame), (J, E)
+            // is the state before it
+            float x1a = 0.0f, x1b = 0.0f, x2 = 0.0f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) {
+                x1a = fmaf(M[c], J[c], x1a);
+                x1b = fmaf(L[c], E[c], x1b);
+                x2 += M[c];
+            }
+            const float tot = wave_sum2(x1a + x1b, x2);
+            if (lane == 0) xs[tt][w].x = tot;
+            if (lane == 32) xs[tt][w].y = tot;
+            const float4 scn = S.sc[tt + 1];
+            const float rho_n = uniform(tt + 1 < Lc ? scn.x : scn.x / sct.z);
+            if (tid == 0) {
+                // rho_{t+1} / alpha_{t+1}: 1 / s_t where token t+1 starts a frame
+                // (rho = alpha / s_t there), else 1 / alpha_{t+1}
+                const bool start = __float_as_uint(rho_n) != 0x3f800000u;
+                const float fac = start ? 1.0f / sct.z : fast_exp(scn.w);
+                xsc[tt] = make_float4(fac, (1.0f - fast_exp(-scn.w)) * scn.z, 0.0f, 0.0f);
+            }
+            if (__float_as_uint(rho_n) != 0x3f800000u) {
+#pragma unroll
+                for (int c = 0; c < 16; ++c) {
+                    L[c] *= rho_n;
+                    M[c] *= rho_n;
+                }
+            }
+        } else {
+            // last token: gradients arriving through the final state
+            // (lam_eta += dmu_T / I_T, lam_I += dI_T - dmu_T mu_T / I_T), scaled;
+            // one column at a time to keep register pressure down
+            const float inv_s = 1.0f / uniform(sct.z);
+            Unroll<0, 16>::run([&](auto cc) {
+                constexpr int c = decltype(cc)::value;
+                const float gm = p.dmu_T ? p.dmu_T[ent + c] : 0.0f;
+                const float gi = p.dI_T ? p.dI_T[ent + c] : 0.0f;
+                const float r = fast_rcp(J[c] + sIp);
+                const float gr = gm * r;
+                L[c] = gr;
+                M[c] = fmaf(-gr, E[c] * r, gi * inv_s);
+            });
+        }
+
+        const float kj = S.k[tt][j];
+        const float qj = S.q[tt][j];
+        const float k2j = kj * kj;
+        const float bc = dpp_src(S.b[tt][lc]);
+        const float bvc = dpp_src(S.b[tt][lc] * S.v[tt][lc]);
+        const float gc = dpp_src(S.g[tt][lc]);
+        float dq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        float dka[2] = {0.0f, 0.0f}, dkb[2] = {0.0f, 0.0f};
+        // The row sums P_c = sum_j M k_j^2 and Q_c = sum_j L k_j are folded into
+        // the 64-lane butterfly as soon as column c is done (the first two
+        // levels pair P_c with Q_c, then column c with c + 8).
+        float wlo[8], x8[8];
+        Unroll<0, 16>::run([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            const float r = fast_rcp(J[c] + sIp);
+            const float mu = E[c] * r;
+            fmac_bcast<c>(dq4[c & 3], gc, mu);              // dq_j  += dout_c mu
+            const float gr = bcast<c>(gc) * (qj * r);       // q_j dout_c / I~
+            L[c] += gr;
+            M[c] = fmaf(-gr, mu, M[c]);
+            fmac_bcast<c>(dka[c & 1], bc, M[c]);            // sum_c beta_c M
+            fmac_bcast<c>(dkb[c & 1], bvc, L[c]);           // sum_c beta_c v_c L
+            const float wc = swap32_add(M[c] * k2j, L[c] * kj);
+            if constexpr (c < 8) wlo[c] = wc;
+            else x8[c - 8] = swap16_add(wlo[c - 8], wc);
+        });
+        const float red = wave_sum32_tail(x8, lane);
+        if (!(lane & 1)) pq[tt][rh][cg][(lane >> 5) * 16 + ((lane >> 1) & 15)] = red;
+        dqk[tt][cg][j] = make_float2((dq4[0] + dq4[1]) + (dq4[2] + dq4[3]),
+                                     2.0f * kj * (dka[0] + dka[1]) + (dkb[0] + dkb[1]));
+    };
+
+    for (int64_t c = nch - 1; c >= 0; --c) {
+        const int b = static_cast<int>((nch - 1 - c) & 1);
+        const BwdStage<DK, CI, true>& S = stg[b];
+        const int Lc = chunk_len(c);
+        const int64_t t0 = c * C;
+        const float* ck = ckb + c * 2 * Sh::BLK;
+        const int nheld = (Lc + HELD - 1) / HELD;
+
+        for (int m = nheld - 1; m >= 0; --m) {
+            float sJ[HELD][16], sE[HELD][16];
+            load16(ck, sJ[0]);
+            load16(ck + Sh::BLK, sE[0]);
+            auto operands = [&](int tt, float& rho, float& bs, float& bvs,
+                                float& kj) __attribute__((always_inline)) {
+                const float4 sc = S.sc[tt];
+                rho = sc.x;
+                kj = S.k[tt][j];
+                const float b = S.b[tt][lc] * sc.z;
+                bvs = dpp_src(b * S.v[tt][lc]);
+                bs = dpp_src(b);
+            };
+            for (int tt = 0; tt < HELD * m; ++tt) {
+                float rho, bs, bvs, kj;
+                operands(tt, rho, bs, bvs, kj);
+                bwd_step_inplace(sJ[0], sE[0], rho, bs, bvs, kj, kj * kj);
+            }
+            Unroll<0, HELD>::run([&](auto uu) {
+                constexpr int u = decltype(uu)::value;
+                const int tt = HELD * m + u;
+                if (tt < Lc) {
+                    float rho, bs, bvs, kj;
+                    operands(tt, rho, bs, bvs, kj);
+                    if constexpr (u == 0)
+                        bwd_step_inplace(sJ[0], sE[0], rho, bs, bvs, kj, kj * kj);
+                    else
+                        bwd_step_copy(sJ[u - 1], sE[u - 1], sJ[u], sE[u], rho, bs, bvs, kj, kj * kj);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            Unroll<0, HELD>::run([&](auto uu) {
+                constexpr int u = HELD - 1 - decltype(uu)::value;
+                const int tt = HELD * m + u;
+                if (tt < Lc) reverse_step(S, tt, t0, Lc, sJ[u], sE[u]);
+                __builtin_amdgcn_sched_barrier(0);   // keep steps apart: bounds register pressure
+            });
+        }
+
+        __syncthreads();
+        // the previous chunk's loads fly while this chunk's outputs are written
+        if (c > 0) ld.fetch(p, bh, tile, (c - 1) * C, chunk_len(c - 1), tid);
+
+        // ---- chunk outputs ----
+        const int64_t tokbase = bh * T + t0;                      // token index into [BH,T]
+        for (int e = tid; e < Lc * CI; e += NTH) {
+            const int tt = e / CI;
+            const int ci = e % CI;
+            const int g = ci / 16;
+            const int cc = ci % 16;
+            float P = 0.0f, Q = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RH; ++r) {
+                P += pq[tt][r][g][cc];
+                Q += pq[tt][r][g][16 + cc];
+            }
+            const float s = S.sc[tt].z;
+            const float bi = S.b[tt][ci];
+            const float vi = S.v[tt][ci];
+            const int64_t o = (tokbase + tt) * p.dv + tile * CI + ci;
+            p.dbeta[o] = s * fmaf(vi, Q, P);
+            p.dv_out[o] = s * bi * Q;
+        }
+        for (int e = tid; e < Lc * DK; e += NTH) {
+            const int tt = e / DK;
+            const int jj = e % DK;
+            float sq = 0.0f, sk = 0.0f;
+#pragma unroll
+            for (int g = 0; g < CG; ++g) {
+                const float2 x = dqk[tt][g][jj];
+                sq += x.x;
+                sk += x.y;
+            }
+            const int64_t o = (tokbase + tt) * DK + jj;
+            part_dq[o] = sq;
+            part_dk[o] = sk * S.sc[tt].z;
+        }
+        for (int tt = tid; tt < Lc; tt += NTH) {
+            if (t0 + tt + 1 < T) {
+                float X1 = 0.0f, X2 = 0.0f;
+#pragma unroll
+                for (int ww = 0; ww < W; ++ww) {
+                    X1 += xs[tt][ww].x;
+                    X2 += xs[tt][ww].y;
+                }
+                const float4 f = xsc[tt];
+                part_da[tokbase + tt + 1] = f.x * X1;
+                part_dip[tokbase + tt + 1] = f.y * X2;
+            }
+        }
+        if (c > 0) ld.commit(stg[b ^ 1], chunk_len(c - 1), tid);
+        __syncthreads();
+    }
+
+    // ---- the starting state (before token 0) ----
+    float I0[16], J0[16], E0[16], m0[16];
+    start_state(p, ent, I0, J0, E0, m0);
+    __shared__ float2 xfin[W];
+    float di[16], dm[16];   // gradients of the starting state's I0 and mu0
+    if (T > 0) {
+        float x1a = 0.0f, x1b = 0.0f, x2 = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            x1a = fmaf(M[c], J0[c], x1a);
+            x1b = fmaf(L[c], E0[c], x1b);
+            x2 += M[c];
+        }
+        const float tot = wave_sum2(x1a + x1b, x2);
+        if (lane == 0) xfin[w].x = tot;
+        if (lane == 32) xfin[w].y = tot;
+        // token 0 starts a frame with s = 1 and rho = alpha_0
+        const float alpha0 = fast_exp(-uniform(p.scal[bh * T].w));
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            L[c] *= alpha0;
+            M[c] *= alpha0;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float X1 = 0.0f, X2 = 0.0f;
+            for (int ww = 0; ww < W; ++ww) {
+                X1 += xfin[ww].x;
+                X2 += xfin[ww].y;
+            }
+            part_da[bh * T] = X1;
+            part_dip[bh * T] = (1.0f - alpha0) * X2;
+        }
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            di[c] = fmaf(L[c], m0[c], M[c]);   // through I0 directly and through eta0 = I0 mu0
+            dm[c] = L[c] * I0[c];
+        }
+    } else {
+        // no token: the final state is the starting state
+        if (p.dmu_T) load16(p.dmu_T + ent, dm);
+        else {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) dm[c] = 0.0f;
+        }
+        if (p.dI_T) load16(p.dI_T + ent, di);
+        else {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) di[c] = 0.0f;
+        }
+    }
+    if (p.dI0 && p.I0) store16(p.dI0 + ent, di);
+    if (p.dmu0 && p.mu0) store16(p.dmu0 + ent, dm);
+    __syncthreads();
+    {
+        float x = 0.0f;
+        if (!p.I0) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) x += di[c];
+        }
+        const float tot = wave_sum2(x, 0.0f);
+        if (lane == 0) xfin[w].x = tot;
+        __syncthreads();
+        if (tid == 0) {
+            float X = 0.0f;
+            for (int ww = 0; ww < W; ++ww) X += xfin[ww].x;
+            p.part_dip0[tile * p.BH + bh] = X;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Finishing passes: sum the column tiles' partials (fixed order: the result
+// does not depend on timing).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_diag_bwd_rows(BwdParams p, int64_t n4) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= n4) return;
+    const int64_t stride4 = n4;   // float4s per tile slice
+    const float4* a = reinterpret_cast<const float4*>(p.part_dq);
+    const float4* b = reinterpret_cast<const float4*>(p.part_dk);
+    float4 sq = a[e], sk = b[e];
+    for (int t = 1; t < p.ntile; ++t) {
+        const float4 x = a[t * stride4 + e], y = b[t * stride4 + e];
+        sq.x += x.x; sq.y += x.y; sq.z += x.z; sq.w += x.w;
+        sk.x += y.x; sk.y += y.y; sk.z += y.z; sk.w += y.w;
+    }
+    reinterpret_cast<float4*>(p.dq)[e] = sq;
+    reinterpret_cast<float4*>(p.dk)[e] = sk;
+}
+
+// One workgroup per head (b, h): dd_t = -A alpha_t dalpha_t, and the head's
+// sums of the dA terms (-d_t alpha_t dalpha_t) and the dI_prior terms.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_diag_bwd_tokens(BwdParams p) {
+    const int64_t bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const float A = p.A[bh % p.H];
+    const int64_t n = p.BH * p.T;
+    float sa = 0.0f, si = 0.0f;
+    for (int64_t t = tid; t < p.T; t += 256) {
+        const int64_t x = bh * p.T + t;
+        float da = 0.0f, di = 0.0f;
+        for (int tl = 0; tl < p.ntile; ++tl) {
+            da += p.part_da[tl * n + x];
+            di += p.part_dip[tl * n + x];
+        }
+        const float alpha = fast_exp(-p.scal[x].w);
+        const float d = BF16 ? bf16_at(static_cast<const uint16_t*>(p.d), x) : static_cast<const float*>(p.d)[x];
+        p.dd[x] = -A * alpha * da;
+        sa = fmaf(-d * alpha, da, sa);
+        si += di;
+    }
+    __shared__ float red[2][256];
+    red[0][tid] = sa;
+    red[1][tid] = si;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) {
+            red[0][tid] += red[0][tid + h];
+            red[1][tid] += red[1][tid + h];
+        }
+        __syncthreads();
+    }
+    if (tid == 0) {
+        float i0 = 0.0f;
+        for (int tl = 0; tl < p.ntile; ++tl) i0 += p.part_dip0[tl * p.BH + bh];
+        p.part_head[2 * bh] = red[0][0];
+        p.part_head[2 * bh + 1] = red[1][0] + i0;
+    }
+}
+
+// dA[h] = sum over the batch of the heads' sums; dI_prior = sum over all.
+__global__ __launch_bounds__(256) void k_diag_bwd_heads(BwdParams p) {
+    const int tid = threadIdx.x;
+    const int64_t B = p.H > 0 ? p.BH / p.H : 0;
+    for (int64_t h = tid; h < p.H; h += 256) {
+        float s = 0.0f;
+        for (int64_t b = 0; b < B; ++b) s += p.part_head[2 * (b * p.H + h)];
+        p.dA[h] = s;
+    }
+    if (!p.dI_prior) return;
+    __shared__ float red[256];
+    float s = 0.0f;
+    for (int64_t x = tid; x < p.BH; x += 256) s += p.part_head[2 * x + 1];
+    red[tid] = s;
+    __syncthreads();
+    for (int h = 128; h > 0; h >>= 1) {
+        if (tid < h) red[tid] += red[tid + h];
+        __syncthreads();
+    }
+    if (tid == 0) p.dI_prior[0] = red[0];
+}
+
+template <int DK, int DV, bool BF16>
+static int launch_bwd_shape(const BwdParams& p, hipStream_t st) {
+    using Sh = BwdShape<DK, DV>;
+    const dim3 grid(static_cast<uint32_t>(p.BH * Sh::NTILE));
+    if (p.T > 0) hipLaunchKernelGGL((k_diag_bwd_ckpt<DK, DV, BF16>), grid, dim3(Sh::NTH), 0, st, p);
+    hipLaunchKernelGGL((k_diag_bwd<DK, DV, BF16>), grid, dim3(Sh::NTH), 0, st, p);
+    return launch_status();
+}
+
+template <int DK, bool BF16>
+static int launch_bwd_dv(const BwdParams& p, int64_t dv, hipStream_t st) {
+    switch (dv) {
+        case 16: return launch_bwd_shape<DK, 16, BF16>(p, st);
+        case 32: return launch_bwd_shape<DK, 32, BF16>(p, st);
+        case 64: return launch_bwd_shape<DK, 64, BF16>(p, st);
+        case 128: return launch_bwd_shape<DK, 128, BF16>(p, st);
+        default: return KDN_EUNSUPPORTED;
+    }
+}
+
+// Enqueue the whole gradient: frame scalars, checkpoints, reverse pass, and
+// the finishing sums.  Arguments were validated by the caller.
+int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk, bool bf16,
+                    hipStream_t st) {
+    if (p.BH > 0) {
+        if (p.T > 0) {
+            const int rc = diag_prep_launch(prep, B, bf16, st);
+            if (rc != KDN_OK) return rc;
+        }
+        int rc;
+        if (dk == 64) rc = bf16 ? launch_bwd_dv<64, true>(p, p.dv, st) : launch_bwd_dv<64, false>(p, p.dv, st);
+        else rc = bf16 ? launch_bwd_dv<128, true>(p, p.dv, st) : launch_bwd_dv<128, false>(p, p.dv, st);
+        if (rc != KDN_OK) return rc;
+        if (p.ntile > 1 && p.T > 0) {
+            const int64_t n4 = p.BH * p.T * dk / 4;
+            hipLaunchKernelGGL(k_diag_bwd_rows, dim3(static_cast<uint32_t>((n4 + 255) / 256)), dim3(256), 0,
+                               st, p, n4);
+        }
+        if (bf16) hipLaunchKernelGGL(k_diag_bwd_tokens<true>, dim3(static_cast<uint32_t>(p.BH)), dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(k_diag_bwd_tokens<false>, dim3(static_cast<uint32_t>(p.BH)), dim3(256), 0, st, p);
+    }
+    if (p.H > 0) hipLaunchKernelGGL(k_diag_bwd_heads, dim3(1), dim3(256), 0, st, p);
+    return launch_status();
+}
+
+}  // namespace kdn

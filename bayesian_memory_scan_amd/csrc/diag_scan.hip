@@ -27,13 +27,10 @@
 //   * long sequences are cut into S segments whose starting states come from
 //     segment composites computed on the matrix cores and carried in order
 //     (diag_comp.hip); all segments then run in parallel.
+#include "kdn_lane.h"
 #include "kdn_params.h"
 
-#include <type_traits>
-
 namespace kdn {
-
-
 
 // Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S).
 __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
@@ -42,54 +39,6 @@ __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int s
     const int64_t c1 = static_cast<int64_t>(seg + 1) * p.nchunks / p.S;
     t0 = c0 * C;
     t1 = c1 * C < p.T ? c1 * C : p.T;
-}
-
-// v_fmac_f32 with its first multiplicand broadcast from lane N of each row of
-// 16 lanes (DPP row_newbcast): acc += bcast_N(src) * other.  The per-lane
-// key-side values (k, k^2, q of 16 rows) live one per lane, so a single VGPR
-// feeds 16 entries without LDS traffic.
-template <int N>
-__device__ __forceinline__ void fmac_bcast(float& acc, float src, float other) {
-    asm("v_fmac_f32_dpp %0, %1, %2 row_newbcast:%3 row_mask:0xf bank_mask:0xf"
-        : "+v"(acc)
-        : "v"(src), "v"(other), "n"(N));
-}
-
-template <int N, int JP>
-struct Unroll {
-    template <typename F>
-    __device__ __forceinline__ static void run(F&& f) {
-        f(std::integral_constant<int, N>{});
-        Unroll<N + 1, JP>::run(f);
-    }
-};
-template <int JP>
-struct Unroll<JP, JP> {
-    template <typename F>
-    __device__ __forceinline__ static void run(F&&) {}
-};
-
-// Workgroups are dealt to the 8 XCDs round-robin by blockIdx.  Renumber them
-// so that consecutive logical ids run on one XCD: the column tiles of a head
-// (adjacent ids) then share that XCD's L2 and read q, k from HBM once.
-__device__ __forceinline__ int64_t xcd_local_id() {
-    constexpr uint32_t kXcd = 8;
-    const uint32_t n = gridDim.x;
-    const uint32_t b = blockIdx.x;
-    const uint32_t full = n / kXcd * kXcd;
-    if (b >= full) return b;
-    return static_cast<int64_t>(b % kXcd) * (full / kXcd) + b / kXcd;
-}
-
-// Value of lane N of this lane's row of 16 (DPP row_newbcast), as a plain
-// operand; the compiler folds it into the consuming v_mul_f32.
-template <int N>
-__device__ __forceinline__ float bcast(float x) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x150 + N, 0xf, 0xf, true));
-}
-
-__device__ __forceinline__ float uniform(float x) {
-    return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
 
 // Scaled frame.  Between renormalisations the kernel keeps I~ = s_t I_t and

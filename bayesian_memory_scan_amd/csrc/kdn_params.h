@@ -62,7 +62,48 @@ struct MobParams {
     int32_t nblk;
 };
 
+// Gradient of the diagonal-precision scan.
+struct BwdParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const void* d;
+    const float* A;
+    const float* I0;
+    const float* mu0;
+    const float* dout;    // [BH,T,dv]
+    const float* dI_T;    // [BH,dk,dv] or NULL
+    const float* dmu_T;   // [BH,dk,dv] or NULL
+    float* dv_out;        // [BH,T,dv]
+    float* dbeta;         // [BH,T,dv]
+    float* dd;            // [BH,T]
+    float* dA;            // [H]
+    float* dI_prior;      // [1] or NULL
+    float* dI0;           // [BH,dk,dv] or NULL
+    float* dmu0;          // [BH,dk,dv] or NULL
+    float* dq;            // [BH,T,dk]
+    float* dk;            // [BH,T,dk]
+    const float4* scal;   // [BH][T] frame scalars (rho, dP, s, A d) from the prep pass
+    float* ckpt;          // [BH][ntile][nch][2][dk*CI]: state before each chunk, unscaled
+    float* part_dq;       // [ntile][BH,T,dk] column-tile partial sums (== dq when ntile == 1)
+    float* part_dk;       // [ntile][BH,T,dk] (== dk when ntile == 1)
+    float* part_da;       // [ntile][BH,T]: d loss / d alpha_t per column tile
+    float* part_dip;      // [ntile][BH,T]: d loss / d I_prior through token t, per tile
+    float* part_dip0;     // [ntile][BH]: through the starting state (I0 == NULL)
+    float* part_head;     // [BH][2]: per-head sums of the dA and dI_prior terms
+    int64_t BH;
+    int64_t H;
+    int64_t T;
+    int64_t dv;
+    float I_prior;
+    int32_t nchunks;
+    int32_t ntile;
+};
+
 int diag_chunk();
+int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
+                    bool bf16, hipStream_t st);
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st);
 int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);

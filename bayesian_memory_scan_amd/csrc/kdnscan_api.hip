@@ -221,6 +221,91 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
 }
 
+int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                      kdn_dtype in_dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* beta, const void* d,
+                      const float* A, float I_prior,
+                      const float* I0, const float* mu0,
+                      const float* d_o, const float* d_I_T, const float* d_mu_T,
+                      float* dq, float* dk, float* dv, float* dbeta, float* dd,
+                      float* dA, float* dI_prior, float* dI0, float* dmu0,
+                      void* workspace, size_t* workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v) || d_k < 64) return KDN_EUNSUPPORTED;
+    if (!finite_positive(I_prior)) return KDN_EINVAL;
+    if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
+    const int64_t BH = B * H;
+    if (H > 0 && !ok_ptr(dA)) return KDN_EINVAL;
+    if (BH > 0 && !ok_ptr(A)) return KDN_EINVAL;
+    if (BH > 0 && T > 0) {
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(d) || !ok_ptr(d_o))
+            return KDN_EINVAL;
+        if (!ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dbeta) || !ok_ptr(dd))
+            return KDN_EINVAL;
+    }
+    if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(d_I_T) || !ok_opt(d_mu_T)) return KDN_EINVAL;
+    if (!ok_opt(dI_prior) || !ok_opt(dI0) || !ok_opt(dmu0)) return KDN_EINVAL;
+    if ((dI0 && !I0) || (dmu0 && !mu0)) return KDN_EINVAL;
+
+    const int64_t ci = d_v < 64 ? d_v : 64;
+    const int64_t ntile = d_v / ci;
+    const int64_t nch = (T + diag_chunk() - 1) / diag_chunk();
+    if (BH * ntile > kMaxGrid || BH > kMaxGrid) return KDN_EINVAL;
+    const size_t f = sizeof(float);
+    const size_t b_scal = align_up(16 * static_cast<size_t>(BH) * T, 256);
+    const size_t b_ckpt = align_up(f * static_cast<size_t>(BH) * nch * 2 * d_k * d_v, 256);
+    const size_t b_rows = ntile > 1 ? align_up(f * static_cast<size_t>(ntile) * BH * T * d_k, 256) : 0;
+    const size_t b_tok = align_up(f * static_cast<size_t>(ntile) * BH * T, 256);
+    const size_t b_dip0 = align_up(f * static_cast<size_t>(ntile) * BH, 256);
+    const size_t b_head = align_up(f * 2 * static_cast<size_t>(BH), 256);
+    const size_t need = b_scal + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head;
+    const int wc = workspace_check(workspace, workspace_bytes, need);
+    if (wc == 1) return KDN_OK;
+    if (wc != KDN_OK) return wc;
+    if (H == 0) return KDN_OK;
+
+    char* ws = static_cast<char*>(workspace);
+    float4* scal = nullptr;
+    BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
+    p.A = A; p.I0 = I0; p.mu0 = mu0;
+    p.dout = d_o; p.dI_T = d_I_T; p.dmu_T = d_mu_T;
+    p.dv_out = dv; p.dbeta = dbeta; p.dd = dd; p.dA = dA; p.dI_prior = dI_prior;
+    p.dI0 = dI0; p.dmu0 = dmu0; p.dq = dq; p.dk = dk;
+    if (BH > 0) {
+        scal = reinterpret_cast<float4*>(ws);
+        p.scal = scal;
+        ws += b_scal;
+        p.ckpt = reinterpret_cast<float*>(ws);
+        ws += b_ckpt;
+        if (ntile > 1) {
+            p.part_dq = reinterpret_cast<float*>(ws);
+            p.part_dk = reinterpret_cast<float*>(ws + b_rows);
+            ws += 2 * b_rows;
+        } else {
+            p.part_dq = dq;
+            p.part_dk = dk;
+        }
+        p.part_da = reinterpret_cast<float*>(ws);
+        p.part_dip = reinterpret_cast<float*>(ws + b_tok);
+        ws += 2 * b_tok;
+        p.part_dip0 = reinterpret_cast<float*>(ws);
+        ws += b_dip0;
+        p.part_head = reinterpret_cast<float*>(ws);
+    }
+    p.BH = BH; p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
+    p.nchunks = static_cast<int32_t>(nch); p.ntile = static_cast<int32_t>(ntile);
+
+    DiagParams prep{};
+    prep.d = d; prep.A = A; prep.scal = scal;
+    prep.H = H; prep.T = T; prep.dv = d_v; prep.I_prior = I_prior;
+    prep.S = 1; prep.nchunks = static_cast<int32_t>(nch);
+    (void)hipGetLastError();  // launch status below must reflect this call only
+    return diag_bwd_launch(p, prep, B, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+}
+
 int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
                               const float* a, const float* p, const float* Lambda,
                               const float* lambda0, float* lambda_out,

@@ -16,7 +16,7 @@ import re
 __all__ = [
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
     "KDN_F32", "KDN_BF16", "KdnError",
-    "kdn_diag_scan_fwd", "kdn_mobius_precision_scan", "kdn_decode_step",
+    "kdn_diag_scan_fwd", "kdn_diag_scan_bwd", "kdn_mobius_precision_scan", "kdn_decode_step",
     "kdn_diag_plan", "kdn_set_diag_segments", "kdn_status_string", "kdn_last_hip_error",
     "header_functions",
 ]
@@ -53,6 +53,12 @@ lib.kdn_diag_scan_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _szp, _vp]
 lib.kdn_diag_scan_fwd.restype = ctypes.c_int
+lib.kdn_diag_scan_bwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                  _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
+                                  _vp, _vp, _vp,
+                                  _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _szp, _vp]
+lib.kdn_diag_scan_bwd.restype = ctypes.c_int
 lib.kdn_mobius_precision_scan.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp,
                                           _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp,
                                           _vp, _szp, _vp]
@@ -211,6 +217,54 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
     if rc != KDN_OK:
         raise KdnError("kdn_diag_scan_fwd", rc)
     return o, I_T, mu_T
+
+
+def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_T=None,
+                      d_mu_T=None, want_prior=True, stream=None):
+    """Gradient of kdn_diag_scan_fwd for L = sum(d_o o) + sum(d_I_T I_T) + sum(d_mu_T mu_T).
+
+    Inputs as for the forward call plus d_o [B,H,T,d_v] and optional d_I_T,
+    d_mu_T [B,H,d_k,d_v] (all float32).  Returns a dict of float32 tensors:
+    dq, dk [B,H,T,d_k]; dv, dbeta [B,H,T,d_v]; dd [B,H,T]; dA [H];
+    dI_prior [1] (when want_prior); dI0 / dmu0 [B,H,d_k,d_v] when I0 / mu0
+    are given.
+    """
+    torch = _torch()
+    dev = q.device
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dts = (torch.float32, torch.bfloat16, torch.int16, torch.uint16)
+    for n, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d)):
+        _check(t, n, dts, dev)
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, beta, d must share one dtype")
+    f32 = (torch.float32,)
+    for n, t in (("A", A), ("d_o", d_o), ("I0", I0), ("mu0", mu0), ("d_I_T", d_I_T),
+                 ("d_mu_T", d_mu_T)):
+        _check(t, n, f32, dev)
+    new = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+    g = {"dq": new(B, H, T, dk), "dk": new(B, H, T, dk), "dv": new(B, H, T, dv),
+         "dbeta": new(B, H, T, dv), "dd": new(B, H, T), "dA": new(H)}
+    if want_prior:
+        g["dI_prior"] = new(1)
+    if I0 is not None:
+        g["dI0"] = new(B, H, dk, dv)
+    if mu0 is not None:
+        g["dmu0"] = new(B, H, dk, dv)
+    st = _stream(stream)
+    o = lambda n: _ptr(g.get(n))
+
+    def args(ws, nbytes):
+        return (B, H, T, dk, dv, _in_dtype(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
+                _ptr(A), float(I_prior), _ptr(I0), _ptr(mu0), _ptr(d_o), _ptr(d_I_T),
+                _ptr(d_mu_T), o("dq"), o("dk"), o("dv"), o("dbeta"), o("dd"), o("dA"),
+                o("dI_prior"), o("dI0"), o("dmu0"), ws, nbytes, st)
+
+    ws, need = _workspace(lib.kdn_diag_scan_bwd, args, dev)
+    rc = lib.kdn_diag_scan_bwd(*args(_ptr(ws), _nbytes(ws, need)))
+    if rc != KDN_OK:
+        raise KdnError("kdn_diag_scan_bwd", rc)
+    return g
 
 
 def kdn_mobius_precision_scan(a, p, Lam, lambda0=None, q=None, k=None, v=None, mu0=None,

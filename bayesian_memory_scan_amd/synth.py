@@ -16,6 +16,10 @@ Recipe (every workload):
 Diagonal-precision workloads, per head, in this order:
   q ~ N(0,1) [T,d_k]; k ~ N(0,1) [T,d_k] then L2-normalised per token;
   v ~ N(0,1) [T,d_v]; beta = sigmoid(N(0,1)) [T,d_v]; d = softplus(N(0,1)) [T].
+Gradient workloads reuse a diagonal workload's inputs and add, from a stream
+keyed (seed, 0xD0): d_o ~ N(0,1) [B,H,T,d_v], then d_I_T, d_mu_T ~ N(0,1)
+[B,H,d_k,d_v] (loss weights); a starting state comes from (seed, 0x50):
+I0 ~ U(0.2, 3.2), mu0 ~ N(0,1).
 Isotropic workload, per head, in this order:
   a = exp(-softplus(N(0,1))) [T]; p = softplus(N(0,1)) [T];
   Lambda = softplus(N(0,1)) [T]; then q, k (normalised), v as above.
@@ -30,7 +34,7 @@ import numpy as np
 
 __all__ = [
     "DiagSpec", "IsoSpec", "WORKLOADS", "workload",
-    "diag_head", "diag_inputs", "iso_head", "iso_inputs",
+    "diag_head", "diag_inputs", "iso_head", "iso_inputs", "grad_inputs", "state_inputs",
     "f32_to_bf16_bits",
 ]
 
@@ -94,6 +98,8 @@ WORKLOADS = {
         DiagSpec("diag_b1h2t64d16_f32", 1, 2, 64, 16, 16, "f32", 1000, A_uniform=False),
         DiagSpec("diag_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         DiagSpec("diag_b2h16t16384d128_bf16", 2, 16, 16384, 128, 128, "bf16", 1002),
+        # gradient of the headline forward workload (same inputs)
+        DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
         # one decode token after a 512-token prefix that builds the state
         DiagSpec("decode_b256h16d128_bf16", 256, 16, 1, 128, 128, "bf16", 1004, prefix=512),
@@ -159,6 +165,27 @@ def diag_inputs(spec: DiagSpec) -> dict:
     out["I_prior"] = float(spec.I_prior)
     out["spec"] = spec
     return out
+
+
+def grad_inputs(spec: DiagSpec, final_state: bool = True) -> dict:
+    """Seeded upstream gradients for a gradient test: d_o [B,H,T,d_v] and, if
+    final_state, d_I_T and d_mu_T [B,H,d_k,d_v]; all float32 standard normal
+    (loss weights, so no structure beyond scale)."""
+    g = _rng(spec.seed, 0xD0)
+    out = {"d_o": g.standard_normal((spec.B, spec.H, spec.T, spec.d_v), dtype=np.float32)}
+    if final_state:
+        out["d_I_T"] = g.standard_normal((spec.B, spec.H, spec.d_k, spec.d_v), dtype=np.float32)
+        out["d_mu_T"] = g.standard_normal((spec.B, spec.H, spec.d_k, spec.d_v), dtype=np.float32)
+    return out
+
+
+def state_inputs(spec: DiagSpec) -> dict:
+    """A seeded starting state: I0 ~ U(0.2, 3.2) (positive precisions) and
+    mu0 ~ N(0, 1), float32 [B,H,d_k,d_v]."""
+    g = _rng(spec.seed, 0x50)
+    shape = (spec.B, spec.H, spec.d_k, spec.d_v)
+    return {"I0": (0.2 + 3.0 * g.random(shape)).astype(np.float32),
+            "mu0": g.standard_normal(shape, dtype=np.float32)}
 
 
 def iso_head(spec: IsoSpec, b: int, h: int) -> dict:

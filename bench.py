@@ -31,6 +31,9 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E, GB/s
 PEAK_FP32_VALU_TFLOPS = 157.3
 DIAG_FLOPS_PER_ENTRY_STEP = 11   # I update 4, eta update 3, reciprocal+multiply 2, read-out 2
 ISO_FLOPS_PER_ENTRY_STEP = 5     # mean update 3, read-out 2
+# gradient: state recurrences 4, mu = eta / I 2, adjoint updates 4 (g = q dout, g / I, g mu / I),
+# dq 2, dk 4, dbeta / dv row sums 4, dalpha 4
+BWD_FLOPS_PER_ENTRY_STEP = 24
 
 
 def _args():
@@ -110,6 +113,22 @@ def cpu_baseline_diag(inp, spec, target_s):
                       f"{t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
 
 
+def cpu_baseline_bwd(inp, grads, spec, target_s):
+    """fp64 oracle gradient on whole heads of the same workload; tokens/s scaled to all heads."""
+    import oracle
+    threads = _cpu_threads()
+    heads_all = [(b, h) for b in range(spec.B) for h in range(spec.H)]
+    with oracle.Timer() as t1:
+        oracle.diag_scan_bwd(inp, grads["d_o"], heads=heads_all[:1], threads=1)
+    n = max(1, min(len(heads_all), int(target_s / max(t1.seconds, 1e-3) * threads)))
+    with oracle.Timer() as t:
+        oracle.diag_scan_bwd(inp, grads["d_o"], heads=heads_all[:n], threads=threads)
+    return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
+            "cores": min(threads, n), "kind": "oracle",
+            "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle "
+                      f"gradient, {t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
+
+
 def cpu_baseline_iso(inp, spec, target_s):
     import oracle
     threads = _cpu_threads()
@@ -174,6 +193,35 @@ def main():
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+    elif a.workload.startswith("bwd_"):
+        inp = synth.diag_inputs(spec)
+        grads = synth.grad_inputs(spec, final_state=False)
+        x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "d", "A")}
+        d_o = _up(grads["d_o"], torch, dev)
+
+        def step():
+            kdn.kdn_diag_scan_bwd(x["q"], x["k"], x["v"], x["beta"], x["d"], x["A"],
+                                  spec.I_prior, d_o)
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        flops = BWD_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        out.update({
+            "metric": "tokens/s per MI355X, diag-precision scan backward (gradient of all inputs)",
+            "value": spec.B * spec.T / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "T": spec.T,
+                       "d_k": spec.d_k, "d_v": spec.d_v, "inputs": spec.dtype,
+                       "gradients": "fp32, loss on o only", "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": _traffic("diag_bwd.hip", f"traffic_{spec.name}.json"),
+                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min,
+                         "note": "events bracket the whole call: frame scalars, checkpoints, "
+                                 "reverse pass and finishing sums; traffic is the reverse pass"},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_bwd(inp, grads, spec, a.cpu_seconds)
     elif a.workload.startswith("decode_"):
         inp = synth.diag_inputs(spec)
         P = spec.prefix

@@ -90,6 +90,36 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * Gradient of kdn_diag_scan_fwd (reverse mode).  The pages train with these
+ * layers [Palimpsa summary, Metodologia 3; KDN abstract, pretraining] but
+ * print no gradient: this is the exact adjoint of the recurrence above, in
+ * fp32.  For the scalar loss
+ *   L = sum d_o * o + sum d_I_T * I_T + sum d_mu_T * mu_T
+ * it writes (float, all outputs overwritten, none accumulated into):
+ *   dq, dk [B,H,T,d_k];  dv, dbeta [B,H,T,d_v];  dd [B,H,T];
+ *   dA [H] (summed over the batch);  dI_prior [1] or NULL;
+ *   dI0, dmu0 [B,H,d_k,d_v] or NULL (allowed only when I0 / mu0 are given;
+ *   with I0 == NULL the start I_prior's share goes to dI_prior).
+ * Inputs: those of the forward call (same dtype rules), plus d_o [B,H,T,d_v]
+ *   float (required), d_I_T, d_mu_T [B,H,d_k,d_v] float or NULL (= 0).
+ * Supported: d_k in {64, 128}, d_v in {16, 32, 64, 128} (else
+ *   KDN_EUNSUPPORTED).  The forward pass is recomputed from checkpoints the
+ *   call writes into its workspace (8 bytes per state entry per 16 tokens,
+ *   plus per-token partial sums); query its size as for the forward call.
+ *   Outputs must not alias inputs.  Deterministic: no atomics.
+ */
+int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                      kdn_dtype in_dtype,
+                      const void* q, const void* k, const void* v,
+                      const void* beta, const void* d,
+                      const float* A, float I_prior,
+                      const float* I0, const float* mu0,
+                      const float* d_o, const float* d_I_T, const float* d_mu_T,
+                      float* dq, float* dk, float* dv, float* dbeta, float* dd,
+                      float* dA, float* dI_prior, float* dI0, float* dmu0,
+                      void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * Isotropic scalar-precision filter [KDN abstract, Isotropic KDN;
  * KLA Metodologia 1-3].  Per head, per token:
  *   lambda_t = M_t(lambda_{t-1}),  M_t = [[1 + Lambda_t p_t, Lambda_t a_t^2],

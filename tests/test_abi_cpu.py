@@ -131,3 +131,58 @@ def test_plan_auto_segments_fill_the_chip():
     _, S2, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
     _, S3, _ = kdn.kdn_diag_plan(1, 2, 64, 16, 16)
     assert S1 == 1 and S2 == 4 and S3 == 1
+
+
+def _bwd(B=1, H=1, T=8, dk=64, dv=16, dt=kdn.KDN_F32, ptr=FAKE, A=FAKE, I_prior=1.0, I0=None,
+         mu0=None, d_o=FAKE, dI_T=None, dmu_T=None, outs=None, dA=FAKE, dIp=None, dI0=None,
+         dmu0=None, ws=None, nbytes=None):
+    o = outs if outs is not None else {}
+    g = lambda n: o.get(n, FAKE)
+    nb = None if nbytes is None else ctypes.byref(nbytes)
+    return lib.kdn_diag_scan_bwd(B, H, T, dk, dv, dt, g("q") if "q" in o else ptr, ptr, ptr, ptr,
+                                 ptr, A, I_prior, I0, mu0, d_o, dI_T, dmu_T, g("dq"), g("dk"),
+                                 g("dv"), g("dbeta"), g("dd"), dA, dIp, dI0, dmu0, ws, nb, None)
+
+
+def test_bwd_validation():
+    n = ctypes.c_size_t(0)
+    q = dict(nbytes=n)
+    assert _bwd(**q) == kdn.KDN_OK
+    assert _bwd(dk=32, **q) == kdn.KDN_EUNSUPPORTED      # the gradient needs d_k of 64 or 128
+    assert _bwd(dk=16, **q) == kdn.KDN_EUNSUPPORTED
+    assert _bwd(dv=24, **q) == kdn.KDN_EUNSUPPORTED
+    assert _bwd(dk=128, dv=128, **q) == kdn.KDN_OK
+    assert _bwd(B=-1, **q) == kdn.KDN_EINVAL
+    assert _bwd(dt=5, **q) == kdn.KDN_EINVAL
+    assert _bwd(I_prior=0.0, **q) == kdn.KDN_EINVAL
+    assert _bwd(d_o=None, **q) == kdn.KDN_EINVAL
+    assert _bwd(dA=None, **q) == kdn.KDN_EINVAL
+    assert _bwd(A=MIS, **q) == kdn.KDN_EINVAL
+    for name in ("dq", "dk", "dv", "dbeta", "dd"):
+        assert _bwd(outs={name: None}, **q) == kdn.KDN_EINVAL, name
+        assert _bwd(outs={name: MIS}, **q) == kdn.KDN_EINVAL, name
+    # state gradients need the state they differentiate
+    assert _bwd(dI0=FAKE, **q) == kdn.KDN_EINVAL
+    assert _bwd(dmu0=FAKE, **q) == kdn.KDN_EINVAL
+    assert _bwd(I0=FAKE, mu0=FAKE, dI0=FAKE, dmu0=FAKE, dIp=FAKE, **q) == kdn.KDN_OK
+    assert _bwd(I0=MIS, **q) == kdn.KDN_EINVAL
+    assert _bwd(dI_T=MIS, **q) == kdn.KDN_EINVAL
+    # an empty batch or sequence needs no token pointers
+    assert _bwd(T=0, ptr=None, d_o=None, outs={n: None for n in ("dq", "dk", "dv", "dbeta", "dd")},
+                **q) == kdn.KDN_OK
+    assert _bwd(B=0, ptr=None, A=None, d_o=None, **q) == kdn.KDN_OK
+
+
+def test_bwd_workspace():
+    n = ctypes.c_size_t(0)
+    assert _bwd(B=8, H=16, T=2048, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
+    BH, T, nch = 128, 2048, 128
+    ckpt = 4 * BH * nch * 2 * 128 * 128
+    rows = 2 * 4 * 2 * BH * T * 128        # two column tiles: dq and dk partials
+    assert n.value >= 16 * BH * T + ckpt + rows and n.value % 256 == 0
+    small = ctypes.c_size_t(n.value - 1)
+    assert _bwd(B=8, H=16, T=2048, dk=128, dv=128, ws=FAKE, nbytes=small) == kdn.KDN_EWORKSPACE
+    # one column tile: dq and dk are written directly, no row partials
+    m = ctypes.c_size_t(0)
+    assert _bwd(B=8, H=16, T=2048, dk=128, dv=64, nbytes=m) == kdn.KDN_OK
+    assert m.value < 16 * BH * T + ckpt // 2 + rows // 2
