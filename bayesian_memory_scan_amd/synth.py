@@ -20,6 +20,9 @@ Gradient workloads reuse a diagonal workload's inputs and add, from a stream
 keyed (seed, 0xD0): d_o ~ N(0,1) [B,H,T,d_v], then d_I_T, d_mu_T ~ N(0,1)
 [B,H,d_k,d_v] (loss weights); a starting state comes from (seed, 0x50):
 I0 ~ U(0.2, 3.2), mu0 ~ N(0,1).
+Process-noise diagonal workloads take a diagonal workload's q, k, v, beta and
+add, from a stream keyed (seed, 0xAB): a = exp(-softplus(N(0,1))) [B,H,T]
+(decay in (0,1)), then p = softplus(N(0,1)) [B,H,T] (process-noise variance).
 Isotropic workload, per head, in this order:
   a = exp(-softplus(N(0,1))) [T]; p = softplus(N(0,1)) [T];
   Lambda = softplus(N(0,1)) [T]; then q, k (normalised), v as above.
@@ -35,6 +38,7 @@ import numpy as np
 __all__ = [
     "DiagSpec", "IsoSpec", "WORKLOADS", "workload",
     "diag_head", "diag_inputs", "iso_head", "iso_inputs", "grad_inputs", "state_inputs",
+    "noise_inputs",
     "f32_to_bf16_bits",
 ]
 
@@ -98,6 +102,8 @@ WORKLOADS = {
         DiagSpec("diag_b1h2t64d16_f32", 1, 2, 64, 16, 16, "f32", 1000, A_uniform=False),
         DiagSpec("diag_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         DiagSpec("diag_b2h16t16384d128_bf16", 2, 16, 16384, 128, 128, "bf16", 1002),
+        # diagonal KDN with process noise, at the headline shape
+        DiagSpec("noise_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1005),
         # gradient of the headline forward workload (same inputs)
         DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
@@ -176,6 +182,17 @@ def grad_inputs(spec: DiagSpec, final_state: bool = True) -> dict:
     if final_state:
         out["d_I_T"] = g.standard_normal((spec.B, spec.H, spec.d_k, spec.d_v), dtype=np.float32)
         out["d_mu_T"] = g.standard_normal((spec.B, spec.H, spec.d_k, spec.d_v), dtype=np.float32)
+    return out
+
+
+def noise_inputs(spec: DiagSpec) -> dict:
+    """A diagonal workload's inputs plus the per-token decay a and process-noise
+    variance p, float32 [B,H,T] (the d input is not used by this filter)."""
+    out = diag_inputs(spec)
+    g = _rng(spec.seed, 0xAB)
+    shape = (spec.B, spec.H, spec.T)
+    out["a"] = np.exp(-_softplus(g.standard_normal(shape, dtype=np.float32))).astype(np.float32)
+    out["p"] = _softplus(g.standard_normal(shape, dtype=np.float32))
     return out
 
 

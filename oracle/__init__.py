@@ -53,6 +53,8 @@ def load(path: str = _LIB):
     lib.oracle_diag_head.restype = ctypes.c_int
     lib.oracle_iso_head.argtypes = [L, D, D, D, ctypes.c_double, L, L, D, D, D, D, D, D, D, D]
     lib.oracle_iso_head.restype = ctypes.c_int
+    lib.oracle_diag_noise_head.argtypes = [L, L, L, D, D, D, D, D, D, D, D, D, D, D, D]
+    lib.oracle_diag_noise_head.restype = ctypes.c_int
     PP = ctypes.POINTER(D)
     lib.oracle_diag_head_bwd.argtypes = [L, L, L, D, D, D, D, D, ctypes.c_double, ctypes.c_double,
                                          D, D, D, D, D, PP, PP]
@@ -161,6 +163,45 @@ def diag_scan_bwd(inp: dict, dout: np.ndarray, heads=None, threads=None, I0=None
                                  dout=np.asarray(dout[b, h], np.float64),
                                  I0=pick(I0, b, h), mu0=pick(mu0, b, h),
                                  dI_T=pick(dI_T, b, h), dmu_T=pick(dmu_T, b, h), lib=lib)
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        return dict(ex.map(one, heads))
+
+
+def diag_noise_head(q, k, v, beta, a, p, lam0=None, mu0=None, lib=None):
+    """One head of the diagonal KDN with process noise (float64 in)."""
+    lib = lib or load()
+    q, k, v, beta, a, p = (np.ascontiguousarray(x, np.float64) for x in (q, k, v, beta, a, p))
+    T, dk = q.shape
+    dv = v.shape[1]
+    o = np.empty((T, dv))
+    s = np.empty((T, dv))
+    lam_T = np.empty((dk, dv))
+    mu_T = np.empty((dk, dv))
+    opt = lambda x: None if x is None else np.ascontiguousarray(x, np.float64)
+    lam0, mu0 = opt(lam0), opt(mu0)
+    rc = lib.oracle_diag_noise_head(T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(a),
+                                    _ptr(p), _ptr(lam0), _ptr(mu0), _ptr(o), _ptr(s),
+                                    _ptr(lam_T), _ptr(mu_T))
+    if rc != 0:
+        raise MemoryError("oracle_diag_noise_head failed")
+    return {"o": o, "s": s, "I_T": lam_T, "mu_T": mu_T}
+
+
+def diag_noise_scan(inp: dict, heads=None, threads=None, lam0=None, mu0=None, lib=None):
+    """The process-noise diagonal filter over heads of a synthetic-input dict
+    (q, k, v, beta in storage dtype, a, p float32 [B,H,T])."""
+    spec = inp["spec"]
+    B, H = inp["q"].shape[:2]
+    heads = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    lib = lib or load()
+    pick = lambda x, b, h: None if x is None else np.asarray(x[b, h], np.float64)
+
+    def one(bh):
+        b, h = bh
+        args = [decode(inp[n][b, h], spec.dtype) for n in ("q", "k", "v", "beta")]
+        ap = [np.asarray(inp[n][b, h], np.float64) for n in ("a", "p")]
+        return bh, diag_noise_head(*args, *ap, lam0=pick(lam0, b, h), mu0=pick(mu0, b, h), lib=lib)
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         return dict(ex.map(one, heads))

@@ -286,3 +286,69 @@ int oracle_diag_head_bwd(long T, long dk, long dv,
     free(mh);
     return 0;
 }
+
+/*
+ * Diagonal KDN with process noise: every memory entry [j][i] is its own
+ * scalar Kalman filter (Kalman Delta Networks abstract, "Diagonal KDN": a
+ * diagonal Gaussian posterior whose uncertainty recurrence is a Mobius map;
+ * the predict step is the KLA summary's, Metodologia 1: the latent decays by
+ * a_t and gains process noise of variance p_t).  Per token t, with the
+ * entry's observation precision w = beta_t[i] k_t[j]^2 and write
+ * beta_t[i] v_t[i] k_t[j] (the Palimpsa write, Metodologia 2):
+ *
+ *   predict  variance 1/lambda -> a_t^2 / lambda + p_t, mean mu -> a_t mu
+ *   update   lambda_t = lambda_pred + w
+ *            mu_t = (lambda_pred a_t mu_{t-1} + beta_t[i] v_t[i] k_t[j]) / lambda_t
+ *   read     o_t[i] = sum_j q_t[j] mu_t[j][i]
+ *
+ * lam0 / mu0 may be NULL (then 1 and 0).  s (may be NULL) receives
+ * sum_j |q_t[j] mu_t[j][i]|.  lam_T, mu_T may be NULL.  Returns 0 or -1.
+ */
+int oracle_diag_noise_head(long T, long dk, long dv,
+                           const double* q, const double* k, const double* v,
+                           const double* beta, const double* a, const double* p,
+                           const double* lam0, const double* mu0,
+                           double* o, double* s, double* lam_T, double* mu_T)
+{
+    const long n = dk * dv;
+    double* lam = (double*)malloc(sizeof(double) * n);
+    double* mu = (double*)malloc(sizeof(double) * n);
+    if (!lam || !mu) { free(lam); free(mu); return -1; }
+    for (long e = 0; e < n; ++e) {
+        lam[e] = lam0 ? lam0[e] : 1.0;
+        mu[e] = mu0 ? mu0[e] : 0.0;
+    }
+
+    for (long t = 0; t < T; ++t) {
+        const double* kt = k + t * dk;
+        const double* qt = q + t * dk;
+        const double* vt = v + t * dv;
+        const double* bt = beta + t * dv;
+        for (long j = 0; j < dk; ++j) {
+            for (long i = 0; i < dv; ++i) {
+                const long e = j * dv + i;
+                const double variance_pred = a[t] * a[t] / lam[e] + p[t];
+                const double lambda_pred = 1.0 / variance_pred;
+                const double obs = bt[i] * kt[j] * kt[j];
+                const double lambda_new = lambda_pred + obs;
+                mu[e] = (lambda_pred * a[t] * mu[e] + bt[i] * vt[i] * kt[j]) / lambda_new;
+                lam[e] = lambda_new;
+            }
+        }
+        for (long i = 0; i < dv; ++i) {
+            double acc = 0.0, mag = 0.0;
+            for (long j = 0; j < dk; ++j) {
+                const double term = qt[j] * mu[j * dv + i];
+                acc += term;
+                mag += fabs(term);
+            }
+            o[t * dv + i] = acc;
+            if (s) s[t * dv + i] = mag;
+        }
+    }
+    if (lam_T) memcpy(lam_T, lam, sizeof(double) * n);
+    if (mu_T) memcpy(mu_T, mu, sizeof(double) * n);
+    free(lam);
+    free(mu);
+    return 0;
+}

@@ -402,6 +402,108 @@ def pin_bwd_scale_bounds(lib):
     _close(np.abs(g1["dq"]), g1["scale_dq"], what="single-term scale")
 
 
+# ---------------------------------------------------------------------------
+# Diagonal KDN with process noise (per-entry scalar Kalman filter)
+# ---------------------------------------------------------------------------
+def noise_case(seed=41, T=11, dk=3, dv=4):
+    g = np.random.default_rng(seed)
+    k = g.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)
+    return dict(q=g.standard_normal((T, dk)), k=k, v=g.standard_normal((T, dv)),
+                beta=1.0 / (1.0 + np.exp(-g.standard_normal((T, dv)))),
+                a=np.exp(-np.log1p(np.exp(g.standard_normal(T)))),
+                p=np.log1p(np.exp(g.standard_normal(T))),
+                lam0=0.5 + g.random((dk, dv)) * 2.0, mu0=g.standard_normal((dk, dv)))
+
+
+def _run_noise(lib, c, **over):
+    c = {**c, **over}
+    return oracle.diag_noise_head(c["q"], c["k"], c["v"], c["beta"], c["a"], c["p"],
+                                  lam0=c.get("lam0"), mu0=c.get("mu0"), lib=lib)
+
+
+def pin_noise_equals_isotropic_single_entry(lib):
+    """With one key and one value channel and k_t = +-1, the entry's
+    observation precision beta k^2 is beta and its write beta v k: exactly the
+    isotropic filter with Lambda_t = beta_t (an independent, pinned oracle)."""
+    g = np.random.default_rng(42)
+    T = 13
+    c = noise_case(seed=42, T=T, dk=1, dv=1)
+    c["k"] = np.where(g.random((T, 1)) < 0.5, -1.0, 1.0)
+    c["lam0"] = np.array([[1.7]])
+    c["mu0"] = np.array([[0.4]])
+    r = _run_noise(lib, c)
+    iso = oracle.iso_head(c["a"], c["p"], c["beta"][:, 0], 1.7, c["q"], c["k"], c["v"],
+                          mu0=c["mu0"], lib=lib)
+    _close(r["I_T"][0, 0], iso["lambda"][-1], what="precision vs isotropic")
+    _close(r["o"], iso["o"], what="read-out vs isotropic")
+    _close(r["mu_T"], iso["mu_T"], what="mean vs isotropic")
+
+
+def pin_noise_mobius(lib):
+    """Each entry's precision is the ordered product of its Mobius maps
+    [[1 + w p, w a^2], [p, a^2]] (w = beta k^2) applied to lambda_0."""
+    c = noise_case(seed=43)
+    r = _run_noise(lib, c)
+    T, dk = c["q"].shape
+    dv = c["v"].shape[1]
+    for j in range(dk):
+        for i in range(dv):
+            P = np.eye(2)
+            for t in range(T):
+                w = c["beta"][t, i] * c["k"][t, j] ** 2
+                M = np.array([[1 + w * c["p"][t], w * c["a"][t] ** 2], [c["p"][t], c["a"][t] ** 2]])
+                P = M @ P
+            lam0 = c["lam0"][j, i]
+            _close(r["I_T"][j, i], (P[0, 0] * lam0 + P[0, 1]) / (P[1, 0] * lam0 + P[1, 1]),
+                   what="precision vs Mobius product")
+
+
+def pin_noise_textbook_kalman(lib):
+    """Against a covariance-form scalar Kalman filter per entry, coded
+    independently: the entry observes z = v / k with noise variance 1/(beta k^2)."""
+    c = noise_case(seed=44, T=9, dk=2, dv=3)
+    r = _run_noise(lib, c)
+    T, dk = c["q"].shape
+    dv = c["v"].shape[1]
+    mu = np.array(c["mu0"], dtype=np.float64)
+    P = 1.0 / np.array(c["lam0"], dtype=np.float64)
+    o = np.zeros((T, dv))
+    for t in range(T):
+        for j in range(dk):
+            for i in range(dv):
+                Pp = c["a"][t] ** 2 * P[j, i] + c["p"][t]
+                m = c["a"][t] * mu[j, i]
+                kk = c["k"][t, j]
+                R = 1.0 / (c["beta"][t, i] * kk * kk)
+                K = Pp / (Pp + R)
+                mu[j, i] = m + K * (c["v"][t, i] / kk - m)
+                P[j, i] = (1.0 - K) * Pp
+        o[t] = c["q"][t] @ mu
+    _close(r["mu_T"], mu, rtol=1e-10, what="mean vs covariance-form Kalman filter")
+    _close(r["I_T"], 1.0 / P, rtol=1e-10, what="precision vs covariance-form Kalman filter")
+    _close(r["o"], o, rtol=1e-10, what="read-out vs covariance-form Kalman filter")
+
+
+def pin_noise_static_limit(lib):
+    """a = 1 and p = 0: a static latent, so the filter is batch Bayesian
+    estimation: lambda_T = lambda_0 + sum w, mu_T = (lambda_0 mu_0 + sum beta v k) / lambda_T."""
+    c = noise_case(seed=45, T=10)
+    T = c["q"].shape[0]
+    c["a"] = np.ones(T)
+    c["p"] = np.zeros(T)
+    r = _run_noise(lib, c)
+    W = np.einsum("ti,tj->ji", c["beta"], c["k"] ** 2)
+    X = np.einsum("ti,tj->ji", c["beta"] * c["v"], c["k"])
+    lam = c["lam0"] + W
+    _close(r["I_T"], lam, what="static precision")
+    _close(r["mu_T"], (c["lam0"] * c["mu0"] + X) / lam, what="static mean")
+
+
+NOISE_PINS = [pin_noise_equals_isotropic_single_entry, pin_noise_mobius, pin_noise_textbook_kalman,
+              pin_noise_static_limit]
+
+
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_prior_start, pin_bwd_readout_only,
             pin_bwd_empty_sequence, pin_bwd_scale_bounds]
-ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS
+ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS + NOISE_PINS

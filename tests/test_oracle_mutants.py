@@ -36,6 +36,12 @@ MUTANTS = {
                                   "g[2][t * dv + i] += gM * kk / In;"),
     "bwd_prior_start_dropped": ("g[6][0] += gI;", "g[6][0] += 0.0 * gI;"),
     "bwd_readout_uses_key": ("gM += qq * go;", "gM += kk * go;"),
+    # diagonal KDN with process noise
+    "noise_dropped": ("a[t] * a[t] / lam[e] + p[t];", "a[t] * a[t] / lam[e];"),
+    "noise_decay_not_squared": ("a[t] * a[t] / lam[e] + p[t];", "a[t] / lam[e] + p[t];"),
+    "noise_mean_not_decayed": ("lambda_pred * a[t] * mu[e]", "lambda_pred * mu[e]"),
+    "noise_obs_not_squared": ("const double obs = bt[i] * kt[j] * kt[j];", "const double obs = bt[i] * kt[j];"),
+    "noise_write_uses_query": ("bt[i] * vt[i] * kt[j]) / lambda_new;", "bt[i] * vt[i] * qt[j]) / lambda_new;"),
 }
 
 
