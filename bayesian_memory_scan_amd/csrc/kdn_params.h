@@ -62,6 +62,26 @@ struct MobParams {
     int32_t nblk;
 };
 
+// Diagonal KDN with process noise: per-entry scalar Kalman filter.
+struct NoiseParams {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* beta;
+    const float* a;       // [BH,T] decay
+    const float* p;       // [BH,T] process-noise variance
+    const float* lam0;    // [BH,dk,dv] or NULL (-> 1)
+    const float* mu0;     // [BH,dk,dv] or NULL (-> 0)
+    float* o;             // [BH,T,dv]
+    float* lam_T;         // [BH,dk,dv] or NULL
+    float* mu_T;          // [BH,dk,dv] or NULL
+    int64_t H;
+    int64_t T;
+    int64_t dv;
+};
+
+int noise_launch(const NoiseParams& p, int64_t B, int64_t dk, bool bf16, hipStream_t st);
+
 // Gradient of the diagonal-precision scan.
 struct BwdParams {
     const void* q;

@@ -221,6 +221,34 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
 }
 
+int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                            kdn_dtype in_dtype,
+                            const void* q, const void* k, const void* v, const void* beta,
+                            const float* a, const float* p,
+                            const float* lambda0, const float* mu0,
+                            float* o, float* lambda_T, float* mu_T, void* stream) {
+    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
+    const int64_t BH = B * H;
+    if (BH > 0 && T > 0) {
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(a) || !ok_ptr(p) ||
+            !ok_ptr(o))
+            return KDN_EINVAL;
+    }
+    if (!ok_opt(lambda0) || !ok_opt(mu0) || !ok_opt(lambda_T) || !ok_opt(mu_T)) return KDN_EINVAL;
+    const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
+    if (BH * ntile > kMaxGrid) return KDN_EINVAL;
+    if (BH == 0) return KDN_OK;
+    NoiseParams np{};
+    np.q = q; np.k = k; np.v = v; np.beta = beta; np.a = a; np.p = p;
+    np.lam0 = lambda0; np.mu0 = mu0; np.o = o; np.lam_T = lambda_T; np.mu_T = mu_T;
+    np.H = H; np.T = T; np.dv = d_v;
+    (void)hipGetLastError();  // launch status below must reflect this call only
+    return noise_launch(np, B, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+}
+
 int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       kdn_dtype in_dtype,
                       const void* q, const void* k, const void* v,

@@ -16,7 +16,8 @@ import re
 __all__ = [
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
     "KDN_F32", "KDN_BF16", "KdnError",
-    "kdn_diag_scan_fwd", "kdn_diag_scan_bwd", "kdn_mobius_precision_scan", "kdn_decode_step",
+    "kdn_diag_scan_fwd", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd",
+    "kdn_mobius_precision_scan", "kdn_decode_step",
     "kdn_diag_plan", "kdn_set_diag_segments", "kdn_status_string", "kdn_last_hip_error",
     "header_functions",
 ]
@@ -53,6 +54,9 @@ lib.kdn_diag_scan_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _szp, _vp]
 lib.kdn_diag_scan_fwd.restype = ctypes.c_int
+lib.kdn_diag_noise_scan_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
+                                        _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
+lib.kdn_diag_noise_scan_fwd.restype = ctypes.c_int
 lib.kdn_diag_scan_bwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                   _vp, _vp, _vp,
@@ -217,6 +221,38 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
     if rc != KDN_OK:
         raise KdnError("kdn_diag_scan_fwd", rc)
     return o, I_T, mu_T
+
+
+def kdn_diag_noise_scan_fwd(q, k, v, beta, a, p, lambda0=None, mu0=None, want_state=True,
+                            stream=None):
+    """Diagonal KDN with process noise on [B,H,T,.] CUDA tensors.
+
+    q, k [B,H,T,d_k]; v, beta [B,H,T,d_v] (float32 or bf16); a, p [B,H,T]
+    float32; optional lambda0, mu0 [B,H,d_k,d_v] float32.  Returns
+    (o, lambda_T, mu_T) (states None when want_state is False).
+    """
+    torch = _torch()
+    dev = q.device
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dts = (torch.float32, torch.bfloat16, torch.int16, torch.uint16)
+    for n, t in (("q", q), ("k", k), ("v", v), ("beta", beta)):
+        _check(t, n, dts, dev)
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, beta must share one dtype")
+    for n, t in (("a", a), ("p", p), ("lambda0", lambda0), ("mu0", mu0)):
+        _check(t, n, (torch.float32,), dev)
+    o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+    lam_T = mu_T = None
+    if want_state:
+        lam_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+        mu_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    rc = lib.kdn_diag_noise_scan_fwd(B, H, T, dk, dv, _in_dtype(q), _ptr(q), _ptr(k), _ptr(v),
+                                     _ptr(beta), _ptr(a), _ptr(p), _ptr(lambda0), _ptr(mu0),
+                                     _ptr(o), _ptr(lam_T), _ptr(mu_T), _stream(stream))
+    if rc != KDN_OK:
+        raise KdnError("kdn_diag_noise_scan_fwd", rc)
+    return o, lam_T, mu_T
 
 
 def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_T=None,

@@ -34,6 +34,9 @@ ISO_FLOPS_PER_ENTRY_STEP = 5     # mean update 3, read-out 2
 # gradient: state recurrences 4, mu = eta / I 2, adjoint updates 4 (g = q dout, g / I, g mu / I),
 # dq 2, dk 4, dbeta / dv row sums 4, dalpha 4
 BWD_FLOPS_PER_ENTRY_STEP = 24
+# process-noise filter: predict 6 (a^2 + p lambda 2, reciprocal, lambda r, a r, eta a r),
+# update 4, read-out 4 (reciprocal, multiply, multiply-add)
+NOISE_FLOPS_PER_ENTRY_STEP = 14
 
 
 def _args():
@@ -129,6 +132,21 @@ def cpu_baseline_bwd(inp, grads, spec, target_s):
                       f"gradient, {t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
 
 
+def cpu_baseline_noise(inp, spec, target_s):
+    import oracle
+    threads = _cpu_threads()
+    heads_all = [(b, h) for b in range(spec.B) for h in range(spec.H)]
+    with oracle.Timer() as t1:
+        oracle.diag_noise_scan(inp, heads=heads_all[:1], threads=1)
+    n = max(1, min(len(heads_all), int(target_s / max(t1.seconds, 1e-3) * threads)))
+    with oracle.Timer() as t:
+        oracle.diag_noise_scan(inp, heads=heads_all[:n], threads=threads)
+    return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
+            "cores": min(threads, n), "kind": "oracle",
+            "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle, "
+                      f"{t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
+
+
 def cpu_baseline_iso(inp, spec, target_s):
     import oracle
     threads = _cpu_threads()
@@ -193,6 +211,30 @@ def main():
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+    elif a.workload.startswith("noise_"):
+        inp = synth.noise_inputs(spec)
+        x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "a", "p")}
+
+        def step():
+            kdn.kdn_diag_noise_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["a"], x["p"])
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        flops = NOISE_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        out.update({
+            "metric": "tokens/s per MI355X, diagonal KDN with process noise, forward",
+            "value": spec.B * spec.T / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "T": spec.T,
+                       "d_k": spec.d_k, "d_v": spec.d_v, "inputs": spec.dtype, "state": "fp32",
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": _traffic("diag_noise.hip", f"traffic_{spec.name}.json"),
+                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_noise(inp, spec, a.cpu_seconds)
     elif a.workload.startswith("bwd_"):
         inp = synth.diag_inputs(spec)
         grads = synth.grad_inputs(spec, final_state=False)

@@ -90,6 +90,29 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * Diagonal KDN with process noise, forward [KDN abstract, Diagonal KDN;
+ * predict step KLA Metodologia 1; write Palimpsa Metodologia 2].  Every
+ * memory entry [j][i] of head (b, h) is a scalar Kalman filter:
+ *   predict  variance 1/lambda -> a_t^2/lambda + p_t,  mean mu -> a_t mu
+ *   update   lambda_t = lambda^- + beta_t[i] k_t[j]^2
+ *            mu_t = (lambda^- a_t mu_{t-1} + beta_t[i] v_t[i] k_t[j]) / lambda_t
+ *   read     o_t[i] = sum_j q_t[j] mu_t[j][i]
+ * i.e. lambda follows the Mobius map l -> ((1 + w p) l + w a^2) / (p l + a^2)
+ * with w = beta k^2.
+ * Inputs: q, k [B,H,T,d_k]; v, beta [B,H,T,d_v] (in_dtype); a, p [B,H,T]
+ *   float (decay, process-noise variance); lambda0, mu0 [B,H,d_k,d_v] float
+ *   or NULL (-> 1 and 0).
+ * Outputs (float): o [B,H,T,d_v]; lambda_T, mu_T [B,H,d_k,d_v] or NULL.
+ *   No workspace: each head's sequence runs in one workgroup pass.
+ */
+int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                            kdn_dtype in_dtype,
+                            const void* q, const void* k, const void* v, const void* beta,
+                            const float* a, const float* p,
+                            const float* lambda0, const float* mu0,
+                            float* o, float* lambda_T, float* mu_T, void* stream);
+
+/*
  * Gradient of kdn_diag_scan_fwd (reverse mode).  The pages train with these
  * layers [Palimpsa summary, Metodologia 3; KDN abstract, pretraining] but
  * print no gradient: this is the exact adjoint of the recurrence above, in

@@ -186,3 +186,17 @@ def test_bwd_workspace():
     m = ctypes.c_size_t(0)
     assert _bwd(B=8, H=16, T=2048, dk=128, dv=64, nbytes=m) == kdn.KDN_OK
     assert m.value < 16 * BH * T + ckpt // 2 + rows // 2
+
+
+def test_noise_validation():
+    call = lambda B=1, H=1, T=8, dk=16, dv=16, dt=kdn.KDN_BF16, q=FAKE, a=FAKE, o=FAKE, lam0=None: \
+        lib.kdn_diag_noise_scan_fwd(B, H, T, dk, dv, dt, q, FAKE, FAKE, FAKE, a, FAKE, lam0, None,
+                                    o, None, None, None)
+    assert call(B=-1) == kdn.KDN_EINVAL
+    assert call(dk=24) == kdn.KDN_EUNSUPPORTED
+    assert call(dt=9) == kdn.KDN_EINVAL
+    assert call(q=None) == kdn.KDN_EINVAL
+    assert call(a=MIS) == kdn.KDN_EINVAL
+    assert call(o=None) == kdn.KDN_EINVAL
+    assert call(lam0=MIS) == kdn.KDN_EINVAL
+    assert call(B=0, q=None, a=None, o=None) == kdn.KDN_OK
