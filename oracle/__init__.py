@@ -75,7 +75,7 @@ def decode(x: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         b = np.asarray(x)
         return (b.astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
-    return np.asarray(x, dtype=np.float32).astype(np.float64)
+    return np.asarray(x).astype(np.float64)   # float32 storage widens exactly
 
 
 def _threads(threads):
@@ -105,6 +105,19 @@ def diag_head(q, k, v, beta, d, A, I_prior, I0=None, mu0=None, lib=None):
     if rc != 0:
         raise MemoryError("oracle_diag_head failed")
     return {"o": o, "s": s, "I_T": I_T, "mu_T": mu_T}
+
+
+def gate_beta(inp: dict, b: int, h: int, t0=0, t1=None) -> np.ndarray:
+    """beta_t[i] of head (b, h) as float64 [T, dv].  A workload without beta
+    uses Palimpsa-M gating ("Learning to Remember, Learn, and Forget in
+    Attention-Based Models", Metodologia 3): the step gate d_t is also the
+    input gate, beta_t[i] = d_t for every value channel i."""
+    spec = inp["spec"]
+    t1 = inp["q"].shape[2] if t1 is None else t1
+    if inp["beta"] is not None:
+        return decode(inp["beta"][b, h, t0:t1], spec.dtype)
+    d = decode(inp["d"][b, h, t0:t1], spec.dtype)
+    return np.repeat(d[:, None], inp["v"].shape[-1], axis=1)
 
 
 GRAD_NAMES = ("dq", "dk", "dv", "dbeta", "dd", "dA", "dI_prior", "dI0", "dmu0")
@@ -158,11 +171,18 @@ def diag_scan_bwd(inp: dict, dout: np.ndarray, heads=None, threads=None, I0=None
 
     def one(bh):
         b, h = bh
-        args = [decode(inp[n][b, h], spec.dtype) for n in ("q", "k", "v", "beta", "d")]
-        return bh, diag_head_bwd(*args, A=float(inp["A"][h]), I_prior=inp["I_prior"],
-                                 dout=np.asarray(dout[b, h], np.float64),
-                                 I0=pick(I0, b, h), mu0=pick(mu0, b, h),
-                                 dI_T=pick(dI_T, b, h), dmu_T=pick(dmu_T, b, h), lib=lib)
+        args = [decode(inp[n][b, h], spec.dtype) for n in ("q", "k", "v", "d")]
+        args.insert(3, gate_beta(inp, b, h))
+        g = diag_head_bwd(*args, A=float(inp["A"][h]), I_prior=inp["I_prior"],
+                          dout=np.asarray(dout[b, h], np.float64),
+                          I0=pick(I0, b, h), mu0=pick(mu0, b, h),
+                          dI_T=pick(dI_T, b, h), dmu_T=pick(dmu_T, b, h), lib=lib)
+        if inp["beta"] is None:
+            # Palimpsa-M gating: beta_t[i] = d_t, so d_t also collects every dbeta_t[i]
+            g["dd"] = g["dd"] + g["dbeta"].sum(axis=1)
+            g["scale_dd"] = g["scale_dd"] + g["scale_dbeta"].sum(axis=1)
+            del g["dbeta"], g["scale_dbeta"]
+        return bh, g
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         return dict(ex.map(one, heads))
@@ -223,13 +243,38 @@ def diag_scan(inp: dict, heads=None, threads=None, t_range=None, I0=None, mu0=No
 
     def one(bh):
         b, h = bh
-        args = [decode(inp[n][b, h, t0:t1], spec.dtype) for n in ("q", "k", "v", "beta", "d")]
+        args = [decode(inp[n][b, h, t0:t1], spec.dtype) for n in ("q", "k", "v", "d")]
+        args.insert(3, gate_beta(inp, b, h, t0, t1))
         return bh, diag_head(*args, A=float(inp["A"][h]), I_prior=inp["I_prior"],
                              I0=None if I0 is None else I0[b, h],
                              mu0=None if mu0 is None else mu0[b, h], lib=lib)
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         return dict(ex.map(one, heads))
+
+
+def diag_scan_varlen(inp: dict, cu_seqlens, I0=None, mu0=None, threads=None, lib=None):
+    """Packed variable-length batch: inputs [1,H,total_T,.]; sequence s owns
+    packed tokens [cu[s], cu[s+1]) and starts from its own state (I0, mu0
+    [N,H,dk,dv] or the prior).  Each (sequence, head) is an independent run
+    of the diagonal recurrence.  Returns {(s, h): diag_head result}."""
+    spec = inp["spec"]
+    H = inp["q"].shape[1]
+    cu = [int(x) for x in cu_seqlens]
+    runs = [(s, h) for s in range(len(cu) - 1) for h in range(H)]
+    lib = lib or load()
+    pick = lambda x, s, h: None if x is None else np.asarray(x[s, h], np.float64)
+
+    def one(sh):
+        s, h = sh
+        t0, t1 = cu[s], cu[s + 1]
+        args = [decode(inp[n][0, h, t0:t1], spec.dtype) for n in ("q", "k", "v", "d")]
+        args.insert(3, gate_beta(inp, 0, h, t0, t1))
+        return sh, diag_head(*args, A=float(inp["A"][h]), I_prior=inp["I_prior"],
+                             I0=pick(I0, s, h), mu0=pick(mu0, s, h), lib=lib)
+
+    with ThreadPoolExecutor(_threads(threads)) as ex:
+        return dict(ex.map(one, runs))
 
 
 def iso_head(a, p, Lam, lambda0, q=None, k=None, v=None, mu0=None, lib=None):

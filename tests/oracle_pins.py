@@ -500,10 +500,86 @@ def pin_noise_static_limit(lib):
     _close(r["mu_T"], (c["lam0"] * c["mu0"] + X) / lam, what="static mean")
 
 
+# ---------------------------------------------------------------------------
+# Palimpsa-M gating (beta_t = d_t) and the packed variable-length batch
+# ---------------------------------------------------------------------------
+def _m_inputs(T=9, dk=3, dv=4, seed=51, H=2):
+    from bayesian_memory_scan_amd import synth
+    spec = synth.DiagSpec(f"m_pin_{seed}", 1, H, T, dk, dv, "f32", seed)
+    inp = synth.diag_inputs(spec)
+    inp["beta"] = None
+    return inp
+
+
+def pin_m_gating_mamba2_limit(lib):
+    """Palimpsa Metodologia 3-4: with d_t as both forget and input gate and
+    I_prior far above d k^2 the model is Mamba2's recurrence
+    S_t = exp(-A d_t) S_{t-1} + d_t k_t v_t^T, o_t = S_t^T q_t / I_prior."""
+    inp = _m_inputs()
+    inp["I_prior"] = 1e9
+    res = oracle.diag_scan(inp, lib=lib)
+    for h in range(2):
+        q, k, v, d = (inp[n][0, h].astype(np.float64) for n in ("q", "k", "v", "d"))
+        alpha = np.exp(-float(inp["A"][h]) * d)
+        S = np.zeros((q.shape[1], v.shape[1]))
+        for t in range(q.shape[0]):
+            S = alpha[t] * S + d[t] * np.outer(k[t], v[t])
+            _close(res[(0, h)]["o"][t] * 1e9, S.T @ q[t], rtol=1e-7, what=f"Mamba2 o_{t}")
+
+
+def pin_m_gating_gradient(lib):
+    """With d_t in both gates, dL/dd_t (forget path plus input path) equals the
+    central finite difference of the forward loss in d_t."""
+    inp = _m_inputs(T=6, dk=2, dv=3, seed=52, H=1)
+    W = np.random.default_rng(53).standard_normal((1, 1, 6, 3))
+    g = oracle.diag_scan_bwd(inp, W, lib=lib)[(0, 0)]
+    assert "dbeta" not in g
+
+    def loss(d):
+        x = dict(inp)
+        x["d"] = d.astype(np.float32) if d.dtype == np.float32 else d
+        return float(np.sum(W[0, 0] * oracle.diag_scan(x, lib=lib)[(0, 0)]["o"]))
+
+    d0 = inp["d"].astype(np.float64)
+    fd = []
+    for t in range(6):
+        h = 1e-5 * max(1.0, abs(d0[0, 0, t]))
+        dp, dm = d0.copy(), d0.copy()
+        dp[0, 0, t] += h
+        dm[0, 0, t] -= h
+        fd.append((loss(dp) - loss(dm)) / (2 * h))
+    _close(g["dd"], np.array(fd), rtol=2e-6, atol=1e-9, what="dd under Palimpsa-M gating")
+
+
+def pin_varlen_continuation(lib):
+    """A packed batch of two sequences, the second started from the first's
+    final state, equals one run over their concatenation; an empty sequence
+    returns its starting state."""
+    from bayesian_memory_scan_amd import synth
+    spec = synth.DiagSpec("varlen_pin", 1, 2, 20, 3, 2, "f32", 54)
+    inp = synth.diag_inputs(spec)
+    whole = oracle.diag_scan(inp, lib=lib)
+    first = oracle.diag_scan_varlen(inp, [0, 7], lib=lib)
+    I7 = np.stack([first[(0, h)]["I_T"] for h in range(2)])[None]
+    m7 = np.stack([first[(0, h)]["mu_T"] for h in range(2)])[None]
+    I0 = np.concatenate([np.ones((1, 2, 3, 2)) * 2.0, I7, np.ones((1, 2, 3, 2)) * 0.5])
+    m0 = np.concatenate([np.zeros((1, 2, 3, 2)), m7, np.full((1, 2, 3, 2), 0.3)])
+    runs = oracle.diag_scan_varlen(inp, [0, 7, 20, 20], I0=I0, mu0=m0, lib=lib)
+    for h in range(2):
+        _close(np.concatenate([first[(0, h)]["o"], runs[(1, h)]["o"]]), whole[(0, h)]["o"],
+               what="continued read-out")
+        _close(runs[(1, h)]["I_T"], whole[(0, h)]["I_T"], what="continued precision")
+        _close(runs[(2, h)]["I_T"], I0[2, h], what="empty sequence precision")
+        _close(runs[(2, h)]["mu_T"], m0[2, h], what="empty sequence mean")
+
+
+M_PINS = [pin_m_gating_mamba2_limit, pin_m_gating_gradient, pin_varlen_continuation]
+
+
 NOISE_PINS = [pin_noise_equals_isotropic_single_entry, pin_noise_mobius, pin_noise_textbook_kalman,
               pin_noise_static_limit]
 
 
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_prior_start, pin_bwd_readout_only,
             pin_bwd_empty_sequence, pin_bwd_scale_bounds]
-ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS + NOISE_PINS
+ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS + NOISE_PINS + M_PINS
