@@ -57,7 +57,8 @@ void k_decode(DecodeParams p) {
     float bcol[4], bvcol[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-        const float b = load(p.beta, bh * DV + cg * 4 + e);
+        // beta == NULL: Palimpsa-M gating, beta[i] = d
+        const float b = p.beta ? load(p.beta, bh * DV + cg * 4 + e) : load(p.d, bh);
         bcol[e] = b;
         bvcol[e] = b * load(p.v, bh * DV + cg * 4 + e);
     }

@@ -91,7 +91,9 @@ struct BwdLoader {
                                           int L, int tid) {
         const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
         const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
-        const E* bth = static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI;
+        // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
+        const E* bth = p.beta ? static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI : nullptr;
+        const E* dh = static_cast<const E*>(p.d) + bh * p.T;
         const E* vh = static_cast<const E*>(p.v) + bh * p.T * p.dv + tile * CI;
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
@@ -108,7 +110,7 @@ struct BwdLoader {
             const int cv = vi % (CI / VW);
             if (vi < VB && row < L) {
                 const int64_t off = (t0 + row) * p.dv + cv * VW;
-                rb[n] = ld16(bth + off);
+                rb[n] = bth ? ld16(bth + off) : splat16<BF16>(dh, t0 + row);
                 rv[n] = ld16(vh + off);
             }
         }
@@ -545,8 +547,25 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             const float bi = S.b[tt][ci];
             const float vi = S.v[tt][ci];
             const int64_t o = (tokbase + tt) * p.dv + tile * CI + ci;
-            p.dbeta[o] = s * fmaf(vi, Q, P);
+            if (p.dbeta) p.dbeta[o] = s * fmaf(vi, Q, P);
             p.dv_out[o] = s * bi * Q;
+        }
+        if (!p.beta) {
+            // Palimpsa-M gating: beta_t[i] = d_t, so d_t collects sum_i dbeta_t[i]
+            float* const part_db = p.part_db + tile * p.BH * T;
+            for (int tt = tid; tt < Lc; tt += NTH) {
+                float sum = 0.0f;
+                for (int ci = 0; ci < CI; ++ci) {
+                    float P = 0.0f, Q = 0.0f;
+#pragma unroll
+                    for (int r = 0; r < RH; ++r) {
+                        P += pq[tt][r][ci / 16][ci % 16];
+                        Q += pq[tt][r][ci / 16][16 + ci % 16];
+                    }
+                    sum += fmaf(S.v[tt][ci], Q, P);
+                }
+                part_db[tokbase + tt] = S.sc[tt].z * sum;
+            }
         }
         for (int e = tid; e < Lc * DK; e += NTH) {
             const int tt = e / DK;
@@ -688,7 +707,11 @@ __global__ __launch_bounds__(256) void k_diag_bwd_tokens(BwdParams p) {
         }
         const float alpha = fast_exp(-p.scal[x].w);
         const float d = BF16 ? bf16_at(static_cast<const uint16_t*>(p.d), x) : static_cast<const float*>(p.d)[x];
-        p.dd[x] = -A * alpha * da;
+        float db = 0.0f;   // Palimpsa-M gating: the input-gate share of d_t
+        if (!p.beta) {
+            for (int tl = 0; tl < p.ntile; ++tl) db += p.part_db[tl * n + x];
+        }
+        p.dd[x] = fmaf(-A * alpha, da, db);
         sa = fmaf(-d * alpha, da, sa);
         si += di;
     }

@@ -80,7 +80,9 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_diag_comp(DiagParams p, int
 
     const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
     const E* vh = static_cast<const E*>(p.v) + bh * p.T * DV;
-    const E* bth = static_cast<const E*>(p.beta) + bh * p.T * DV;
+    // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
+    const E* bth = p.beta ? static_cast<const E*>(p.beta) + bh * p.T * DV : nullptr;
+    const E* dh = static_cast<const E*>(p.d) + bh * p.T;
     const float4* sch = p.scal + bh * p.T;
 
     f32x4c J[MT], X[MT];
@@ -107,7 +109,8 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_diag_comp(DiagParams p, int
             rb[n] = make_uint4(0u, 0u, 0u, 0u);
             rv[n] = rb[n];
             if (e * VW < L * DV) {
-                rb[n] = ld16(bth + t0 * DV + static_cast<int64_t>(e) * VW);
+                rb[n] = bth ? ld16(bth + t0 * DV + static_cast<int64_t>(e) * VW)
+                            : splat16<BF16>(dh, t0 + e * VW / DV);
                 rv[n] = ld16(vh + t0 * DV + static_cast<int64_t>(e) * VW);
             }
         }

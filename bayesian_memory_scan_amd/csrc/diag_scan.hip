@@ -32,6 +32,29 @@
 
 namespace kdn {
 
+// Packed variable-length batch: tokens of sequence s, [cu[s], cu[s+1]),
+// clamped into [0, T] so that a malformed offset table cannot send a
+// workgroup out of bounds.
+__device__ __forceinline__ void sequence_tokens(const DiagParams& p, int32_t s, int64_t& t0,
+                                                int64_t& t1) {
+    int64_t a = p.cu_seqlens[s], b = p.cu_seqlens[s + 1];
+    a = a < 0 ? 0 : (a > p.T ? p.T : a);
+    b = b < a ? a : (b > p.T ? p.T : b);
+    t0 = a;
+    t1 = b;
+}
+
+// The sequence holding packed token t: the last s with cu[s] <= t.
+__device__ __forceinline__ int32_t find_sequence(const DiagParams& p, int64_t t) {
+    int32_t lo = 0, hi = p.nseq;
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) / 2;
+        if (p.cu_seqlens[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
 // Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S).
 __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
                                                int64_t& t0, int64_t& t1) {
@@ -84,21 +107,50 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     const int j0 = rg * JP;
     const int jl = j0 + (lane & (JP - 1));   // the key row this lane holds for broadcasts
     const int ntile = static_cast<int>(p.dv / CI);
-    int64_t wg = xcd_local_id();
-    const int tile = static_cast<int>(wg % ntile);
-    wg /= ntile;
-    const int seg = static_cast<int>(wg % p.S);
-    const int64_t bh = wg / p.S;
+    // Packed variable-length batch: workgroups go out in blockIdx order, so
+    // runs are numbered to follow the plan's longest-first order (the longest
+    // sequences start first, the short ones fill in behind), in groups of
+    // 8 runs x ntile tiles where a run's tiles are 8 blocks apart and so land
+    // on the same XCD (blocks are dealt to the 8 XCDs round-robin).
+    // Otherwise XCD-local ids.
+    int64_t wg;
+    int tile;
+    if (p.cu_seqlens) {
+        const int64_t b = blockIdx.x;
+        const int64_t within = b % (8 * ntile);
+        tile = static_cast<int>(within / 8);
+        wg = b / (8 * ntile) * 8 + within % 8;
+        if (wg >= static_cast<int64_t>(p.nseq) * p.H) return;   // padding of the last group
+    } else {
+        wg = xcd_local_id();
+        tile = static_cast<int>(wg % ntile);
+        wg /= ntile;
+    }
     const int i = tile * CI + col;
-
-    int64_t t_begin, t_end;
-    segment_tokens(p, C, seg, t_begin, t_end);
+    // bh: head of the token inputs; sb: slot of this run's starting/final state
+    int seg;
+    int64_t bh, sb, t_begin, t_end;
+    if (p.cu_seqlens) {
+        // one whole sequence of one head
+        bh = wg % p.H;
+        const int32_t sq = p.seq_order[wg / p.H];
+        sb = static_cast<int64_t>(sq) * p.H + bh;
+        seg = 0;
+        sequence_tokens(p, sq, t_begin, t_end);
+    } else {
+        seg = static_cast<int>(wg % p.S);
+        bh = wg / p.S;
+        sb = bh;
+        segment_tokens(p, C, seg, t_begin, t_end);
+    }
 
     const float I_prior = p.I_prior;
     const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
     const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
     const E* vh = static_cast<const E*>(p.v) + bh * p.T * p.dv + tile * CI;
-    const E* bth = static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI;
+    // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
+    const E* bth = p.beta ? static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI : nullptr;
+    const E* dh = static_cast<const E*>(p.d) + bh * p.T;
 
     // ---- state, JP key rows per lane, in the scaled frame with s = 1 at the
     //      segment start: I~ and the information mean eta~ ----
@@ -106,7 +158,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     if (p.S == 1) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
-            const int64_t off = (bh * DK + j0 + r) * p.dv + i;
+            const int64_t off = (sb * DK + j0 + r) * p.dv + i;
             const float m0 = p.mu0 ? p.mu0[off] : 0.0f;
             const float I0 = p.I0 ? p.I0[off] : I_prior;
             I[r] = I0;
@@ -144,7 +196,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             const int cv = vi % (CI / VW);
             if (vi < VB && row < L) {
                 const int64_t off = (t0 + row) * p.dv + cv * VW;
-                rb[n] = ld16(bth + off);
+                rb[n] = bth ? ld16(bth + off) : splat16<BF16>(dh, t0 + row);
                 rv[n] = ld16(vh + off);
             }
         }
@@ -285,7 +337,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     if (seg == p.S - 1) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
-            const int64_t off = (bh * DK + j0 + r) * p.dv + i;
+            const int64_t off = (sb * DK + j0 + r) * p.dv + i;
             if (p.I_T) p.I_T[off] = I[r] / s_last;
             if (p.mu_T) p.mu_T[off] = eta[r] / I[r];
         }
@@ -299,14 +351,9 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 // the frame start, rho = alpha / s_{t-1} at a start (for the chunk's first
 // token only alpha: the main pass divides by the previous chunk's last s),
 // dP = (1 - alpha) I_prior s.  Output (rho, dP, s, A d) per token.
+// One chunk's walk: tokens [t0, t0 + L) of head bh, a chunk start.
 template <bool BF16>
-__global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units, int32_t nch) {
-    constexpr int C = kDiagChunkTokens;
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (u >= n_units) return;
-    const int64_t bh = u / nch;
-    const int64_t t0 = (u % nch) * C;
-    const int L = p.T - t0 < C ? static_cast<int>(p.T - t0) : C;
+__device__ __forceinline__ void prep_chunk(const DiagParams& p, int64_t bh, int64_t t0, int L) {
     const float A = p.A[bh % p.H];
     float cum = 0.0f, s = 1.0f;
     int fr_prev = 0;
@@ -334,6 +381,32 @@ __global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units
         }
         out[k] = make_float4(rho, (1.0f - alpha) * p.I_prior * s, s, ell);
     }
+}
+
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units, int32_t nch) {
+    constexpr int C = kDiagChunkTokens;
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (u >= n_units) return;
+    const int64_t bh = u / nch;
+    const int64_t t0 = (u % nch) * C;
+    prep_chunk<BF16>(p, bh, t0, p.T - t0 < C ? static_cast<int>(p.T - t0) : C);
+}
+
+// Packed variable-length batch: chunks start at every sequence's first token.
+// One thread per (head, packed token); the threads at a chunk start walk it.
+template <bool BF16>
+__global__ __launch_bounds__(256) void k_diag_prep_varlen(DiagParams p) {
+    constexpr int C = kDiagChunkTokens;
+    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (u >= p.H * p.T) return;
+    const int64_t h = u / p.T;
+    const int64_t t = u % p.T;
+    int64_t t_begin, t_end;
+    const int32_t s = find_sequence(p, t);
+    sequence_tokens(p, s, t_begin, t_end);
+    if ((t - t_begin) % C != 0) return;
+    prep_chunk<BF16>(p, h, t, t_end - t < C ? static_cast<int>(t_end - t) : C);
 }
 
 // Carry pass: in order over segments, turn each segment's composite into the
@@ -423,6 +496,51 @@ static int launch_main(const DiagParams& p, int64_t dk, int CI, int64_t grid, hi
 }
 
 int diag_chunk() { return kDiagChunk; }
+
+// The plan of a packed batch: sequences ordered longest first (ties by
+// index), by rank counting in one workgroup.  Past kMaxPlanSort sequences
+// the quadratic count is skipped and the order is the identity.
+constexpr int32_t kMaxPlanSort = 16384;
+
+__global__ __launch_bounds__(1024) void k_varlen_plan(DiagParams p) {
+    const int32_t n = p.nseq;
+    for (int32_t s = threadIdx.x; s < n; s += 1024) {
+        int32_t rank = s;
+        if (n <= kMaxPlanSort) {
+            int64_t a0, a1;
+            sequence_tokens(p, s, a0, a1);
+            const int64_t len = a1 - a0;
+            rank = 0;
+            for (int32_t u = 0; u < n; ++u) {
+                int64_t b0, b1;
+                sequence_tokens(p, u, b0, b1);
+                const int64_t lu = b1 - b0;
+                rank += (lu > len || (lu == len && u < s)) ? 1 : 0;
+            }
+        }
+        p.seq_order[rank] = s;
+    }
+}
+
+// Packed variable-length batch (p.cu_seqlens set, p.S == 1): the plan, frame
+// scalars per sequence-aligned chunk, then one workgroup per (sequence, head,
+// tile).
+int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st) {
+    hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(1024), 0, st, p);
+    const int64_t n = p.H * p.T;
+    if (n > 0) {
+        const dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+        if (bf16) hipLaunchKernelGGL(k_diag_prep_varlen<true>, grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(k_diag_prep_varlen<false>, grid, dim3(256), 0, st, p);
+    }
+    const int CI = p.dv < 64 ? static_cast<int>(p.dv) : 64;
+    const int64_t runs = static_cast<int64_t>(p.nseq) * p.H;
+    const int64_t grid = (runs + 7) / 8 * 8 * (p.dv / CI);   // whole groups of 8 runs
+    if (grid == 0) return launch_status();
+    const int rc = bf16 ? launch_main<true>(p, dk, CI, grid, st) : launch_main<false>(p, dk, CI, grid, st);
+    if (rc != KDN_OK) return rc;
+    return launch_status();
+}
 
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st) {
     const int32_t nch = static_cast<int32_t>((p.T + kDiagChunk - 1) / kDiagChunk);

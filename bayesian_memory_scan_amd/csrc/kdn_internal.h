@@ -48,6 +48,20 @@ __device__ __forceinline__ void widen(const uint4& u, float* out) {
     }
 }
 
+// A 16-byte vector holding VW copies of element idx (bf16 bits or f32): the
+// input gate of Palimpsa-M gating, where beta_t[i] = d_t for every i.
+template <bool BF16>
+__device__ __forceinline__ uint4 splat16(const void* base, int64_t idx) {
+    if constexpr (BF16) {
+        const uint32_t b = static_cast<const uint16_t*>(base)[idx];
+        const uint32_t w = b | (b << 16);
+        return make_uint4(w, w, w, w);
+    } else {
+        const uint32_t b = __float_as_uint(static_cast<const float*>(base)[idx]);
+        return make_uint4(b, b, b, b);
+    }
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool head_size_ok(int64_t n) { return n == 16 || n == 32 || n == 64 || n == 128; }
 

@@ -33,6 +33,9 @@ struct DiagParams {
     float I_prior;
     int32_t S;
     int32_t nchunks;
+    const int64_t* cu_seqlens;   // packed variable-length batch: [nseq + 1] offsets, or NULL
+    int32_t* seq_order;          // its sequences, longest first (written by the plan pass)
+    int32_t nseq;
 };
 
 struct DecodeParams {
@@ -111,6 +114,7 @@ struct BwdParams {
     float* part_da;       // [ntile][BH,T]: d loss / d alpha_t per column tile
     float* part_dip;      // [ntile][BH,T]: d loss / d I_prior through token t, per tile
     float* part_dip0;     // [ntile][BH]: through the starting state (I0 == NULL)
+    float* part_db;       // [ntile][BH,T]: sum_i dbeta_t[i] per tile (Palimpsa-M gating only)
     float* part_head;     // [BH][2]: per-head sums of the dA and dI_prior terms
     int64_t BH;
     int64_t H;
@@ -126,6 +130,7 @@ int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64
                     bool bf16, hipStream_t st);
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st);
 int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
+int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
 int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);

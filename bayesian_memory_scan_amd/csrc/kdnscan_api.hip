@@ -189,7 +189,7 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const int64_t BH = B * H;
     if (BH > 0 && !ok_ptr(A)) return KDN_EINVAL;
     if (BH > 0 && T > 0) {
-        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(d) || !ok_ptr(o))
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(o))
             return KDN_EINVAL;
     }
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
@@ -219,6 +219,50 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     p.S = pl.S; p.nchunks = pl.nchunks;
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
+}
+
+int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                             kdn_dtype in_dtype, const int64_t* cu_seqlens,
+                             const void* q, const void* k, const void* v,
+                             const void* beta, const void* d,
+                             const float* A, float I_prior,
+                             const float* I0, const float* mu0,
+                             float* o, float* I_T, float* mu_T,
+                             void* workspace, size_t* workspace_bytes, void* stream) {
+    if (N < 0 || H < 0 || total_T < 0 || N >= 2147483647) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    if (!finite_positive(I_prior)) return KDN_EINVAL;
+    if (!sizes_fit(1, H, total_T, d_k > d_v ? d_k : d_v) || !sizes_fit(N, H, 1, d_k * d_v)) return KDN_EINVAL;
+    const bool work = N > 0 && H > 0;
+    if (work && (cu_seqlens == nullptr || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0))
+        return KDN_EINVAL;
+    if (work && !ok_ptr(A)) return KDN_EINVAL;
+    if (H > 0 && total_T > 0) {
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(o))
+            return KDN_EINVAL;
+    }
+    if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
+    const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
+    if ((N * H + 7) * ntile > kMaxGrid || H * total_T / 256 > kMaxGrid) return KDN_EINVAL;
+    const size_t b_scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
+    const size_t need = work ? b_scal + align_up(4 * static_cast<size_t>(N), 256) : 0;
+    const int wc = workspace_check(workspace, workspace_bytes, need);
+    if (wc == 1) return KDN_OK;
+    if (wc != KDN_OK) return wc;
+    if (!work) return KDN_OK;
+
+    DiagParams p{};
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
+    p.A = A; p.I0 = I0; p.mu0 = mu0;
+    p.o = o; p.I_T = I_T; p.mu_T = mu_T;
+    p.scal = reinterpret_cast<float4*>(workspace);
+    p.seq_order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + b_scal);
+    p.H = H; p.T = total_T; p.dv = d_v; p.I_prior = I_prior;
+    p.S = 1; p.nchunks = 0;
+    p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
+    (void)hipGetLastError();  // launch status below must reflect this call only
+    return diag_varlen_launch(p, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
 }
 
 int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
@@ -268,10 +312,11 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     if (H > 0 && !ok_ptr(dA)) return KDN_EINVAL;
     if (BH > 0 && !ok_ptr(A)) return KDN_EINVAL;
     if (BH > 0 && T > 0) {
-        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(d) || !ok_ptr(d_o))
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(d_o))
             return KDN_EINVAL;
-        if (!ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dbeta) || !ok_ptr(dd))
-            return KDN_EINVAL;
+        if (!ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dd)) return KDN_EINVAL;
+        // Palimpsa-M gating (beta == NULL) has no beta to differentiate
+        if (beta ? !ok_ptr(dbeta) : dbeta != nullptr) return KDN_EINVAL;
     }
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(d_I_T) || !ok_opt(d_mu_T)) return KDN_EINVAL;
     if (!ok_opt(dI_prior) || !ok_opt(dI0) || !ok_opt(dmu0)) return KDN_EINVAL;
@@ -288,7 +333,8 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const size_t b_tok = align_up(f * static_cast<size_t>(ntile) * BH * T, 256);
     const size_t b_dip0 = align_up(f * static_cast<size_t>(ntile) * BH, 256);
     const size_t b_head = align_up(f * 2 * static_cast<size_t>(BH), 256);
-    const size_t need = b_scal + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head;
+    const size_t b_db = beta ? 0 : b_tok;
+    const size_t need = b_scal + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db;
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
     if (wc != KDN_OK) return wc;
@@ -322,6 +368,8 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
         p.part_dip0 = reinterpret_cast<float*>(ws);
         ws += b_dip0;
         p.part_head = reinterpret_cast<float*>(ws);
+        ws += b_head;
+        if (!beta) p.part_db = reinterpret_cast<float*>(ws);
     }
     p.BH = BH; p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.nchunks = static_cast<int32_t>(nch); p.ntile = static_cast<int32_t>(ntile);
@@ -414,7 +462,7 @@ int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in
     const int64_t BH = B * H;
     if (BH > kMaxGrid) return KDN_EINVAL;
     if (BH == 0) return KDN_OK;
-    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_ptr(beta) || !ok_ptr(d) || !ok_ptr(A) ||
+    if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(A) ||
         !ok_ptr(I) || !ok_ptr(mu) || !ok_ptr(o))
         return KDN_EINVAL;
     DecodeParams p{};

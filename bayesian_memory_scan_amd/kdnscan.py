@@ -16,7 +16,7 @@ import re
 __all__ = [
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
     "KDN_F32", "KDN_BF16", "KdnError",
-    "kdn_diag_scan_fwd", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd",
+    "kdn_diag_scan_fwd", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd", "kdn_diag_scan_varlen_fwd",
     "kdn_mobius_precision_scan", "kdn_decode_step",
     "kdn_diag_plan", "kdn_set_diag_segments", "kdn_status_string", "kdn_last_hip_error",
     "header_functions",
@@ -54,6 +54,10 @@ lib.kdn_diag_scan_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _szp, _vp]
 lib.kdn_diag_scan_fwd.restype = ctypes.c_int
+lib.kdn_diag_scan_varlen_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _szp, _vp]
+lib.kdn_diag_scan_varlen_fwd.restype = ctypes.c_int
 lib.kdn_diag_noise_scan_fwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp]
 lib.kdn_diag_noise_scan_fwd.restype = ctypes.c_int
@@ -188,8 +192,8 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
 
     q, k [B,H,T,d_k]; v, beta [B,H,T,d_v]; d [B,H,T] (all float32, or all
     bfloat16 / raw-bf16 int16); A [H] float32; I_prior float; optional I0, mu0
-    [B,H,d_k,d_v] float32.  Returns (o, I_T, mu_T) (states None when
-    want_state is False).
+    [B,H,d_k,d_v] float32.  beta None selects Palimpsa-M gating (beta_t = d_t).
+    Returns (o, I_T, mu_T) (states None when want_state is False).
     """
     torch = _torch()
     dev = q.device
@@ -198,7 +202,7 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
     dts = (torch.float32, torch.bfloat16, torch.int16, torch.uint16)
     for n, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d)):
         _check(t, n, dts, dev)
-        if t.dtype != q.dtype:
+        if t is not None and t.dtype != q.dtype:
             raise TypeError("q, k, v, beta, d must share one dtype")
     f32 = (torch.float32,)
     _check(A, "A", f32, dev)
@@ -220,6 +224,47 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
     rc = lib.kdn_diag_scan_fwd(*args(_ptr(ws), _nbytes(ws, need)))
     if rc != KDN_OK:
         raise KdnError("kdn_diag_scan_fwd", rc)
+    return o, I_T, mu_T
+
+
+def kdn_diag_scan_varlen_fwd(q, k, v, beta, d, A, I_prior, cu_seqlens, I0=None, mu0=None,
+                             want_state=True, stream=None):
+    """Diagonal scan over a packed variable-length batch.
+
+    q, k [H,total_T,d_k]; v, beta [H,total_T,d_v]; d [H,total_T] (float32 or
+    bf16; beta None = Palimpsa-M gating); cu_seqlens int64 [N+1] on the device;
+    I0, mu0 [N,H,d_k,d_v] float32 or None.  Returns (o [H,total_T,d_v], I_T,
+    mu_T [N,H,d_k,d_v]).
+    """
+    torch = _torch()
+    dev = q.device
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dts = (torch.float32, torch.bfloat16, torch.int16, torch.uint16)
+    for n, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d)):
+        _check(t, n, dts, dev)
+        if t is not None and t.dtype != q.dtype:
+            raise TypeError("q, k, v, beta, d must share one dtype")
+    _check(cu_seqlens, "cu_seqlens", (torch.int64,), dev)
+    for n, t in (("A", A), ("I0", I0), ("mu0", mu0)):
+        _check(t, n, (torch.float32,), dev)
+    N = cu_seqlens.numel() - 1
+    o = torch.empty((H, T, dv), dtype=torch.float32, device=dev)
+    I_T = mu_T = None
+    if want_state:
+        I_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+        mu_T = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    st = _stream(stream)
+
+    def args(ws, nbytes):
+        return (N, H, T, dk, dv, _in_dtype(q), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                _ptr(beta), _ptr(d), _ptr(A), float(I_prior), _ptr(I0), _ptr(mu0), _ptr(o),
+                _ptr(I_T), _ptr(mu_T), ws, nbytes, st)
+
+    ws, need = _workspace(lib.kdn_diag_scan_varlen_fwd, args, dev)
+    rc = lib.kdn_diag_scan_varlen_fwd(*args(_ptr(ws), _nbytes(ws, need)))
+    if rc != KDN_OK:
+        raise KdnError("kdn_diag_scan_varlen_fwd", rc)
     return o, I_T, mu_T
 
 
@@ -272,7 +317,7 @@ def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_
     dts = (torch.float32, torch.bfloat16, torch.int16, torch.uint16)
     for n, t in (("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d)):
         _check(t, n, dts, dev)
-        if t.dtype != q.dtype:
+        if t is not None and t.dtype != q.dtype:
             raise TypeError("q, k, v, beta, d must share one dtype")
     f32 = (torch.float32,)
     for n, t in (("A", A), ("d_o", d_o), ("I0", I0), ("mu0", mu0), ("d_I_T", d_I_T),
@@ -280,7 +325,9 @@ def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_
         _check(t, n, f32, dev)
     new = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
     g = {"dq": new(B, H, T, dk), "dk": new(B, H, T, dk), "dv": new(B, H, T, dv),
-         "dbeta": new(B, H, T, dv), "dd": new(B, H, T), "dA": new(H)}
+         "dd": new(B, H, T), "dA": new(H)}
+    if beta is not None:   # beta None: Palimpsa-M gating, whose beta share is in dd
+        g["dbeta"] = new(B, H, T, dv)
     if want_prior:
         g["dI_prior"] = new(1)
     if I0 is not None:

@@ -23,6 +23,11 @@ I0 ~ U(0.2, 3.2), mu0 ~ N(0,1).
 Process-noise diagonal workloads take a diagonal workload's q, k, v, beta and
 add, from a stream keyed (seed, 0xAB): a = exp(-softplus(N(0,1))) [B,H,T]
 (decay in (0,1)), then p = softplus(N(0,1)) [B,H,T] (process-noise variance).
+Palimpsa-M workloads are diagonal workloads with beta removed (the step gate
+d_t doubles as the input gate).  Packed variable-length workloads draw one
+[1,H,total_T,.] diagonal workload and cut it into N sequences at N-1 distinct
+cut points drawn uniformly from [1, total_T) with a stream keyed (seed, 0x1E)
+(so lengths follow the spacing of uniform points: many short, a few long).
 Isotropic workload, per head, in this order:
   a = exp(-softplus(N(0,1))) [T]; p = softplus(N(0,1)) [T];
   Lambda = softplus(N(0,1)) [T]; then q, k (normalised), v as above.
@@ -38,7 +43,7 @@ import numpy as np
 __all__ = [
     "DiagSpec", "IsoSpec", "WORKLOADS", "workload",
     "diag_head", "diag_inputs", "iso_head", "iso_inputs", "grad_inputs", "state_inputs",
-    "noise_inputs",
+    "noise_inputs", "VarlenSpec", "varlen_inputs",
     "f32_to_bf16_bits",
 ]
 
@@ -97,6 +102,24 @@ class IsoSpec:
         return replace(self, **kw)
 
 
+@dataclass(frozen=True)
+class VarlenSpec:
+    """A packed variable-length batch of the diagonal scan."""
+    name: str
+    H: int
+    N: int                # sequences
+    total_T: int          # packed tokens per head
+    d_k: int
+    d_v: int
+    dtype: str
+    seed: int
+    m_gating: bool = False
+    I_prior: float = 1.0
+
+    def with_(self, **kw) -> "VarlenSpec":
+        return replace(self, **kw)
+
+
 WORKLOADS = {
     s.name: s for s in [
         DiagSpec("diag_b1h2t64d16_f32", 1, 2, 64, 16, 16, "f32", 1000, A_uniform=False),
@@ -104,6 +127,10 @@ WORKLOADS = {
         DiagSpec("diag_b2h16t16384d128_bf16", 2, 16, 16384, 128, 128, "bf16", 1002),
         # diagonal KDN with process noise, at the headline shape
         DiagSpec("noise_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1005),
+        # Palimpsa-M gating (beta_t = d_t) at the headline shape
+        DiagSpec("diagm_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1006),
+        # packed variable-length batch: 64 sequences, 16384 packed tokens per head
+        VarlenSpec("varlen_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1007),
         # gradient of the headline forward workload (same inputs)
         DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
@@ -193,6 +220,21 @@ def noise_inputs(spec: DiagSpec) -> dict:
     shape = (spec.B, spec.H, spec.T)
     out["a"] = np.exp(-_softplus(g.standard_normal(shape, dtype=np.float32))).astype(np.float32)
     out["p"] = _softplus(g.standard_normal(shape, dtype=np.float32))
+    return out
+
+
+def varlen_inputs(spec: VarlenSpec) -> dict:
+    """Packed inputs [1,H,total_T,.] (beta None under Palimpsa-M gating) plus
+    cu_seqlens (int64 [N+1]) of the seeded length mix."""
+    base = DiagSpec(spec.name, 1, spec.H, spec.total_T, spec.d_k, spec.d_v, spec.dtype, spec.seed,
+                    I_prior=spec.I_prior)
+    out = diag_inputs(base)
+    if spec.m_gating:
+        out["beta"] = None
+    g = _rng(spec.seed, 0x1E)
+    cuts = np.sort(g.choice(np.arange(1, spec.total_T), size=spec.N - 1, replace=False)) \
+        if spec.N > 1 else np.zeros(0, np.int64)
+    out["cu_seqlens"] = np.concatenate([[0], cuts, [spec.total_T]]).astype(np.int64)
     return out
 
 

@@ -132,6 +132,25 @@ def cpu_baseline_bwd(inp, grads, spec, target_s):
                       f"gradient, {t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
 
 
+def cpu_baseline_varlen(inp, spec, target_s):
+    """fp64 oracle over the packed batch's (sequence, head) runs; a prefix of
+    the sequences sized to about target_s, scaled by its share of tokens."""
+    import oracle
+    threads = _cpu_threads()
+    cu = [int(x) for x in inp["cu_seqlens"]]
+    with oracle.Timer() as t1:
+        oracle.diag_scan_varlen(inp, cu[:2], threads=1)
+    per_token = t1.seconds / max(1, cu[1]) / spec.H * 1.0
+    n = 1
+    while n < spec.N and (cu[n + 1] * spec.H * per_token) / threads < target_s:
+        n += 1
+    with oracle.Timer() as t:
+        oracle.diag_scan_varlen(inp, cu[:n + 1], threads=threads)
+    return {"value": cu[n] / t.seconds, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {n} of {spec.N} sequences ({cu[n]} of {spec.total_T} packed tokens) x "
+                      f"{spec.H} heads, fp64 sequential oracle, {t.seconds:.1f} s wall"}
+
+
 def cpu_baseline_noise(inp, spec, target_s):
     import oracle
     threads = _cpu_threads()
@@ -211,6 +230,64 @@ def main():
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+    elif a.workload.startswith("diagm_"):
+        # Palimpsa-M gating: the step gate d_t is also the input gate (no beta input)
+        inp = synth.diag_inputs(spec)
+        inp["beta"] = None
+        x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "d", "A")}
+        o = torch.empty((spec.B, spec.H, spec.T, spec.d_v), dtype=torch.float32, device=dev)
+        st = torch.empty((2, spec.B, spec.H, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
+
+        def step():
+            kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], None, x["d"], x["A"], spec.I_prior,
+                                  o=o, I_T=st[0], mu_T=st[1])
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        flops = DIAG_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        out.update({
+            "metric": "tokens/s per MI355X, diag-precision scan fwd under Palimpsa-M gating",
+            "value": spec.B * spec.T / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "T": spec.T,
+                       "d_k": spec.d_k, "d_v": spec.d_v, "inputs": spec.dtype,
+                       "gating": "beta_t = d_t", "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),
+                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+    elif a.workload.startswith("varlen_"):
+        inp = synth.varlen_inputs(spec)
+        x = {n: _up(inp[n][0], torch, dev) for n in ("q", "k", "v", "beta", "d")}
+        A = _up(inp["A"], torch, dev)
+        cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+
+        def step():
+            kdn.kdn_diag_scan_varlen_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], A,
+                                         spec.I_prior, cu)
+
+        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        flops = DIAG_FLOPS_PER_ENTRY_STEP * spec.H * spec.total_T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        lens = [int(b - a_) for a_, b in zip(inp["cu_seqlens"][:-1], inp["cu_seqlens"][1:])]
+        out.update({
+            "metric": "tokens/s per MI355X, diag-precision scan fwd over a packed variable-length batch",
+            "value": spec.total_T / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "sequences": spec.N, "H": spec.H,
+                       "packed_T": spec.total_T, "d_k": spec.d_k, "d_v": spec.d_v,
+                       "inputs": spec.dtype, "length_min": min(lens), "length_max": max(lens),
+                       "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),
+                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_varlen(inp, spec, a.cpu_seconds)
     elif a.workload.startswith("noise_"):
         inp = synth.noise_inputs(spec)
         x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "a", "p")}

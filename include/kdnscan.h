@@ -72,6 +72,8 @@ enum {
  *   o_t[i] = sum_j q_t[j] mu_t[j][i]
  * Inputs (in_dtype: KDN_F32 = float, KDN_BF16 = bfloat16):
  *   q, k [B,H,T,d_k];  v, beta [B,H,T,d_v];  d [B,H,T].
+ *   beta == NULL selects Palimpsa-M gating [Palimpsa Metodologia 3]: the
+ *   step gate d_t is also the input gate, beta_t[i] = d_t for every i.
  *   A [H] float (forget rate per head);  I_prior > 0 (scalar prior precision).
  *   I0, mu0 [B,H,d_k,d_v] float: starting state; NULL -> I_prior and 0.
  * Outputs (float): o [B,H,T,d_v]; I_T, mu_T [B,H,d_k,d_v] final state, or
@@ -88,6 +90,34 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       const float* I0, const float* mu0,
                       float* o, float* I_T, float* mu_T,
                       void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * Diagonal-precision scan over a packed variable-length batch: the same
+ * recurrence as kdn_diag_scan_fwd, restarted at every sequence start
+ * [Palimpsa Metodologia 1-3; Palimpsa-M gating with beta == NULL].
+ *   cu_seqlens: DEVICE int64 [N+1], cu[0] = 0 <= cu[1] <= ... <= cu[N] =
+ *     total_T; sequence s owns packed tokens [cu[s], cu[s+1]) (empty
+ *     sequences allowed).  Offsets outside [0, total_T] are clamped (the
+ *     kernels never leave the buffers), but then the results are undefined.
+ *   q, k [H,total_T,d_k]; v, beta [H,total_T,d_v]; d [H,total_T] (in_dtype;
+ *     beta may be NULL); A [H] float; I_prior > 0.
+ *   I0, mu0 [N,H,d_k,d_v] float or NULL: each sequence's starting state.
+ *   Outputs: o [H,total_T,d_v]; I_T, mu_T [N,H,d_k,d_v] or NULL.
+ *   Workspace: 16 bytes per (head, packed token) of frame scalars, plus the
+ *   plan (4 bytes per sequence).
+ * Work plan: one workgroup per (sequence, head, 64-column tile), chunks of 16
+ * tokens aligned to each sequence start, dispatched longest sequence first
+ * (the order is computed on the device from cu_seqlens; up to 16384
+ * sequences, beyond that in index order).
+ */
+int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                             kdn_dtype in_dtype, const int64_t* cu_seqlens,
+                             const void* q, const void* k, const void* v,
+                             const void* beta, const void* d,
+                             const float* A, float I_prior,
+                             const float* I0, const float* mu0,
+                             float* o, float* I_T, float* mu_T,
+                             void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
  * Diagonal KDN with process noise, forward [KDN abstract, Diagonal KDN;
@@ -123,6 +153,8 @@ int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_
  *   dA [H] (summed over the batch);  dI_prior [1] or NULL;
  *   dI0, dmu0 [B,H,d_k,d_v] or NULL (allowed only when I0 / mu0 are given;
  *   with I0 == NULL the start I_prior's share goes to dI_prior).
+ *   With beta == NULL (Palimpsa-M gating, beta_t[i] = d_t) dbeta must be
+ *   NULL and dd includes the input-gate share sum_i dL/dbeta_t[i].
  * Inputs: those of the forward call (same dtype rules), plus d_o [B,H,T,d_v]
  *   float (required), d_I_T, d_mu_T [B,H,d_k,d_v] float or NULL (= 0).
  * Supported: d_k in {64, 128}, d_v in {16, 32, 64, 128} (else
@@ -176,6 +208,7 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
  * constant-memory decoding, KDN abstract].  The same update as
  * kdn_diag_scan_fwd for a single token, applied in place:
  *   q, k [B,H,d_k]; v, beta [B,H,d_v]; d [B,H] (in_dtype);  A [H] float;
+ *   beta == NULL: Palimpsa-M gating (beta[i] = d), as for the scan;
  *   I, mu [B,H,d_k,d_v] float, read and overwritten with the new state;
  *   o [B,H,d_v] float.
  */

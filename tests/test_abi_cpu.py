@@ -52,9 +52,12 @@ def test_diag_validation():
     assert _diag(I_prior=0.0, **q) == kdn.KDN_EINVAL
     assert _diag(I_prior=float("nan"), **q) == kdn.KDN_EINVAL
     assert _diag(I_prior=-1.0, **q) == kdn.KDN_EINVAL
-    for name in ("q", "k", "v", "beta", "d", "A", "o"):
+    for name in ("q", "k", "v", "d", "A", "o"):
         assert _diag(**{name: None}, **q) == kdn.KDN_EINVAL, name
+    for name in ("q", "k", "v", "beta", "d", "A", "o"):
         assert _diag(**{name: MIS}, **q) == kdn.KDN_EINVAL, name
+    # beta may be NULL: Palimpsa-M gating (the step gate d_t is the input gate)
+    assert _diag(beta=None, **q) == kdn.KDN_OK
     for name in ("I0", "mu0", "I_T", "mu_T"):
         assert _diag(**{name: MIS}, **q) == kdn.KDN_EINVAL, name
     # empty batches need no input pointers
@@ -161,6 +164,14 @@ def test_bwd_validation():
     for name in ("dq", "dk", "dv", "dbeta", "dd"):
         assert _bwd(outs={name: None}, **q) == kdn.KDN_EINVAL, name
         assert _bwd(outs={name: MIS}, **q) == kdn.KDN_EINVAL, name
+    # Palimpsa-M gating: no beta, so no dbeta (its share goes to dd)
+    n2 = ctypes.c_size_t(0)
+    call_m = lambda dbeta: lib.kdn_diag_scan_bwd(1, 1, 8, 64, 16, kdn.KDN_F32, FAKE, FAKE, FAKE, None,
+                                                 FAKE, FAKE, 1.0, None, None, FAKE, None, None, FAKE,
+                                                 FAKE, FAKE, dbeta, FAKE, FAKE, None, None, None,
+                                                 None, ctypes.byref(n2), None)
+    assert call_m(None) == kdn.KDN_OK
+    assert call_m(FAKE) == kdn.KDN_EINVAL
     # state gradients need the state they differentiate
     assert _bwd(dI0=FAKE, **q) == kdn.KDN_EINVAL
     assert _bwd(dmu0=FAKE, **q) == kdn.KDN_EINVAL
@@ -200,3 +211,22 @@ def test_noise_validation():
     assert call(o=None) == kdn.KDN_EINVAL
     assert call(lam0=MIS) == kdn.KDN_EINVAL
     assert call(B=0, q=None, a=None, o=None) == kdn.KDN_OK
+
+
+def test_varlen_validation_and_workspace():
+    n = ctypes.c_size_t(0)
+    call = lambda N=3, H=2, T=40, dk=64, dv=64, cu=FAKE, q=FAKE, beta=FAKE, I0=None, nb=n, ws=None: \
+        lib.kdn_diag_scan_varlen_fwd(N, H, T, dk, dv, kdn.KDN_BF16, cu, q, FAKE, FAKE, beta, FAKE,
+                                     FAKE, 1.0, I0, None, FAKE, None, None, ws,
+                                     None if nb is None else ctypes.byref(nb), None)
+    assert call() == kdn.KDN_OK
+    assert n.value == 16 * 2 * 40 + 256        # frame scalars + the longest-first plan
+    assert call(N=-1) == kdn.KDN_EINVAL
+    assert call(cu=None) == kdn.KDN_EINVAL
+    assert call(cu=FAKE + 4) == kdn.KDN_EINVAL  # int64 offsets must be 8-byte aligned
+    assert call(q=None) == kdn.KDN_EINVAL
+    assert call(beta=None) == kdn.KDN_OK        # Palimpsa-M gating
+    assert call(dk=24) == kdn.KDN_EUNSUPPORTED
+    assert call(I0=MIS) == kdn.KDN_EINVAL
+    assert call(N=0, cu=None) == kdn.KDN_OK and n.value == 0
+    assert call(nb=None, ws=None) == kdn.KDN_EWORKSPACE
