@@ -55,6 +55,8 @@ def load(path: str = _LIB):
     lib.oracle_iso_head.restype = ctypes.c_int
     lib.oracle_diag_noise_head.argtypes = [L, L, L, D, D, D, D, D, D, D, D, D, D, D, D]
     lib.oracle_diag_noise_head.restype = ctypes.c_int
+    lib.oracle_kdn_exact_head.argtypes = [L, L, L, D, D, D, D, D, D, D, D, D, D, D]
+    lib.oracle_kdn_exact_head.restype = ctypes.c_int
     PP = ctypes.POINTER(D)
     lib.oracle_diag_head_bwd.argtypes = [L, L, L, D, D, D, D, D, ctypes.c_double, ctypes.c_double,
                                          D, D, D, D, D, PP, PP]
@@ -206,6 +208,26 @@ def diag_noise_head(q, k, v, beta, a, p, lam0=None, mu0=None, lib=None):
     if rc != 0:
         raise MemoryError("oracle_diag_noise_head failed")
     return {"o": o, "s": s, "I_T": lam_T, "mu_T": mu_T}
+
+
+def kdn_exact_head(q, k, v, beta, a, p, P0=None, mu0=None, lib=None):
+    """Exact (dense-covariance) Kalman filter of one head: float64 in, dict
+    out with o [T,dv], P_T [dv,dk,dk] (one covariance per value column) and
+    mu_T [dk,dv]."""
+    lib = lib or load()
+    q, k, v, beta, a, p = (np.ascontiguousarray(x, np.float64) for x in (q, k, v, beta, a, p))
+    T, dk = q.shape
+    dv = v.shape[1]
+    o = np.empty((T, dv))
+    P_T = np.empty((dv, dk, dk))
+    mu_T = np.empty((dk, dv))
+    opt = lambda x: None if x is None else np.ascontiguousarray(x, np.float64)
+    P0, mu0 = opt(P0), opt(mu0)
+    rc = lib.oracle_kdn_exact_head(T, dk, dv, _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(a),
+                                   _ptr(p), _ptr(P0), _ptr(mu0), _ptr(o), _ptr(P_T), _ptr(mu_T))
+    if rc != 0:
+        raise MemoryError("oracle_kdn_exact_head failed")
+    return {"o": o, "P_T": P_T, "mu_T": mu_T}
 
 
 def diag_noise_scan(inp: dict, heads=None, threads=None, lam0=None, mu0=None, lib=None):

@@ -288,17 +288,23 @@ int oracle_diag_head_bwd(long T, long dk, long dv,
 }
 
 /*
- * Diagonal KDN with process noise: every memory entry [j][i] is its own
- * scalar Kalman filter (Kalman Delta Networks abstract, "Diagonal KDN": a
- * diagonal Gaussian posterior whose uncertainty recurrence is a Mobius map;
- * the predict step is the KLA summary's, Metodologia 1: the latent decays by
- * a_t and gains process noise of variance p_t).  Per token t, with the
- * entry's observation precision w = beta_t[i] k_t[j]^2 and write
- * beta_t[i] v_t[i] k_t[j] (the Palimpsa write, Metodologia 2):
+ * Diagonal KDN with process noise (Kalman Delta Networks abstract, "Diagonal
+ * KDN": each one-step posterior is projected onto the diagonal Gaussian
+ * family by online mean-field variational inference, and the Kalman gain
+ * weights each residual write).  The memory column i is a latent vector
+ * s_i in R^{d_k} observed through v_t[i] = k_t^T s_i + noise of precision
+ * beta_t[i]; the state keeps one mean and one precision per entry [j][i].
+ * Per token t, for every column i:
  *
- *   predict  variance 1/lambda -> a_t^2 / lambda + p_t, mean mu -> a_t mu
- *   update   lambda_t = lambda_pred + w
- *            mu_t = (lambda_pred a_t mu_{t-1} + beta_t[i] v_t[i] k_t[j]) / lambda_t
+ *   predict  (KLA summary, Metodologia 1: decay a_t, process noise p_t)
+ *            variance_pred[j] = a_t^2 / lambda[j] + p_t,  mean_pred[j] = a_t mu[j]
+ *   update   the exact one-step posterior from this diagonal prior is
+ *            Gaussian with precision diag(1/variance_pred) + beta k k^T and mean
+ *              mean_pred + variance_pred . k (v - k^T mean_pred) / S,
+ *              S = sum_j k_j^2 variance_pred[j] + 1/beta
+ *            (the Kalman gain on the residual); its mean-field projection
+ *            keeps that mean and the diagonal of that precision:
+ *            lambda[j] = 1/variance_pred[j] + beta k_j^2
  *   read     o_t[i] = sum_j q_t[j] mu_t[j][i]
  *
  * lam0 / mu0 may be NULL (then 1 and 0).  s (may be NULL) receives
@@ -313,7 +319,12 @@ int oracle_diag_noise_head(long T, long dk, long dv,
     const long n = dk * dv;
     double* lam = (double*)malloc(sizeof(double) * n);
     double* mu = (double*)malloc(sizeof(double) * n);
-    if (!lam || !mu) { free(lam); free(mu); return -1; }
+    double* var_pred = (double*)malloc(sizeof(double) * dk);
+    double* mean_pred = (double*)malloc(sizeof(double) * dk);
+    if (!lam || !mu || !var_pred || !mean_pred) {
+        free(lam); free(mu); free(var_pred); free(mean_pred);
+        return -1;
+    }
     for (long e = 0; e < n; ++e) {
         lam[e] = lam0 ? lam0[e] : 1.0;
         mu[e] = mu0 ? mu0[e] : 0.0;
@@ -324,15 +335,21 @@ int oracle_diag_noise_head(long T, long dk, long dv,
         const double* qt = q + t * dk;
         const double* vt = v + t * dv;
         const double* bt = beta + t * dv;
-        for (long j = 0; j < dk; ++j) {
-            for (long i = 0; i < dv; ++i) {
+        for (long i = 0; i < dv; ++i) {
+            double S = 1.0 / bt[i];
+            double prediction = 0.0;
+            for (long j = 0; j < dk; ++j) {
                 const long e = j * dv + i;
-                const double variance_pred = a[t] * a[t] / lam[e] + p[t];
-                const double lambda_pred = 1.0 / variance_pred;
-                const double obs = bt[i] * kt[j] * kt[j];
-                const double lambda_new = lambda_pred + obs;
-                mu[e] = (lambda_pred * a[t] * mu[e] + bt[i] * vt[i] * kt[j]) / lambda_new;
-                lam[e] = lambda_new;
+                var_pred[j] = a[t] * a[t] / lam[e] + p[t];
+                mean_pred[j] = a[t] * mu[e];
+                S += kt[j] * kt[j] * var_pred[j];
+                prediction += kt[j] * mean_pred[j];
+            }
+            const double residual = vt[i] - prediction;
+            for (long j = 0; j < dk; ++j) {
+                const long e = j * dv + i;
+                mu[e] = mean_pred[j] + var_pred[j] * kt[j] * residual / S;
+                lam[e] = 1.0 / var_pred[j] + bt[i] * kt[j] * kt[j];
             }
         }
         for (long i = 0; i < dv; ++i) {
@@ -350,5 +367,83 @@ int oracle_diag_noise_head(long T, long dk, long dv,
     if (mu_T) memcpy(mu_T, mu, sizeof(double) * n);
     free(lam);
     free(mu);
+    free(var_pred);
+    free(mean_pred);
+    return 0;
+}
+
+/*
+ * Exact KDN: the Kalman filter the diagonal and isotropic variants
+ * approximate (Kalman Delta Networks abstract: exact tracking is a dense,
+ * state-dependent Riccati recursion).  The memory is a d_k x d_v matrix whose
+ * value column i is a latent vector s_i in R^{d_k}:
+ *   transition   s_i <- a_t s_i + noise, covariance p_t Id   (KLA Metodologia 1)
+ *   observation  v_t[i] = k_t^T s_i + noise, precision beta_t[i]
+ * Each column keeps a full covariance P_i [d_k x d_k] and mean m_i; per token,
+ * in covariance form:
+ *   P- = a^2 P + p Id,  u = P- k,  S = k^T u + 1/beta,  K = u / S
+ *   m  = a m + K (v_i - a k^T m),   P = P- - K u^T
+ *   o_t[i] = q_t^T m_i
+ * P0 [d_v][d_k][d_k] (may be NULL: Id / lambda0 with lambda0 = 1) and mu0
+ * [d_k][d_v] (NULL: 0) give the start.  o is [T][d_v]; P_T (may be NULL)
+ * receives the final covariances, mu_T (may be NULL) the means [d_k][d_v].
+ * Returns 0 or -1.
+ */
+int oracle_kdn_exact_head(long T, long dk, long dv,
+                          const double* q, const double* k, const double* v,
+                          const double* beta, const double* a, const double* p,
+                          const double* P0, const double* mu0,
+                          double* o, double* P_T, double* mu_T)
+{
+    double* P = (double*)malloc(sizeof(double) * dv * dk * dk);
+    double* m = (double*)malloc(sizeof(double) * dv * dk);
+    double* u = (double*)malloc(sizeof(double) * dk);
+    if (!P || !m || !u) { free(P); free(m); free(u); return -1; }
+    for (long i = 0; i < dv; ++i) {
+        for (long r = 0; r < dk; ++r) {
+            m[i * dk + r] = mu0 ? mu0[r * dv + i] : 0.0;
+            for (long c = 0; c < dk; ++c)
+                P[(i * dk + r) * dk + c] = P0 ? P0[(i * dk + r) * dk + c] : (r == c ? 1.0 : 0.0);
+        }
+    }
+    for (long t = 0; t < T; ++t) {
+        const double* kt = k + t * dk;
+        const double* qt = q + t * dk;
+        const double a2 = a[t] * a[t];
+        for (long i = 0; i < dv; ++i) {
+            double* Pi = P + i * dk * dk;
+            double* mi = m + i * dk;
+            /* predict */
+            for (long r = 0; r < dk; ++r) {
+                for (long c = 0; c < dk; ++c) Pi[r * dk + c] *= a2;
+                Pi[r * dk + r] += p[t];
+                mi[r] *= a[t];
+            }
+            /* update with the scalar observation v_t[i] of k_t^T s_i */
+            double S = 1.0 / beta[t * dv + i];
+            double pred = 0.0;
+            for (long r = 0; r < dk; ++r) {
+                double acc = 0.0;
+                for (long c = 0; c < dk; ++c) acc += Pi[r * dk + c] * kt[c];
+                u[r] = acc;
+                S += kt[r] * acc;
+                pred += kt[r] * mi[r];
+            }
+            const double resid = v[t * dv + i] - pred;
+            for (long r = 0; r < dk; ++r) mi[r] += u[r] / S * resid;
+            for (long r = 0; r < dk; ++r)
+                for (long c = 0; c < dk; ++c) Pi[r * dk + c] -= u[r] * u[c] / S;
+            double acc = 0.0;
+            for (long r = 0; r < dk; ++r) acc += qt[r] * mi[r];
+            o[t * dv + i] = acc;
+        }
+    }
+    if (P_T) memcpy(P_T, P, sizeof(double) * dv * dk * dk);
+    if (mu_T)
+        for (long i = 0; i < dv; ++i)
+            for (long r = 0; r < dk; ++r) mu_T[r * dv + i] = m[i * dk + r];
+    free(P);
+    free(m);
+    free(u);
     return 0;
 }

@@ -459,45 +459,36 @@ def pin_noise_mobius(lib):
                    what="precision vs Mobius product")
 
 
-def pin_noise_textbook_kalman(lib):
-    """Against a covariance-form scalar Kalman filter per entry, coded
-    independently: the entry observes z = v / k with noise variance 1/(beta k^2)."""
-    c = noise_case(seed=44, T=9, dk=2, dv=3)
-    r = _run_noise(lib, c)
+def pin_noise_mean_field_step(lib):
+    """Every step is the mean-field projection of an exact one-step posterior:
+    starting from the diagonal filter's state after t tokens (means mu, a
+    diagonal covariance diag(1/lambda) per column), one step of the exact
+    dense filter gives the diagonal filter's mean after t + 1 tokens, and the
+    diagonal of the exact posterior precision is its lambda.  The exact
+    filter is an independently coded covariance-form Riccati recursion."""
+    c = noise_case(seed=44, T=9, dk=4, dv=3)
     T, dk = c["q"].shape
     dv = c["v"].shape[1]
-    mu = np.array(c["mu0"], dtype=np.float64)
-    P = 1.0 / np.array(c["lam0"], dtype=np.float64)
-    o = np.zeros((T, dv))
     for t in range(T):
-        for j in range(dk):
-            for i in range(dv):
-                Pp = c["a"][t] ** 2 * P[j, i] + c["p"][t]
-                m = c["a"][t] * mu[j, i]
-                kk = c["k"][t, j]
-                R = 1.0 / (c["beta"][t, i] * kk * kk)
-                K = Pp / (Pp + R)
-                mu[j, i] = m + K * (c["v"][t, i] / kk - m)
-                P[j, i] = (1.0 - K) * Pp
-        o[t] = c["q"][t] @ mu
-    _close(r["mu_T"], mu, rtol=1e-10, what="mean vs covariance-form Kalman filter")
-    _close(r["I_T"], 1.0 / P, rtol=1e-10, what="precision vs covariance-form Kalman filter")
-    _close(r["o"], o, rtol=1e-10, what="read-out vs covariance-form Kalman filter")
+        before = _run_noise(lib, {**c, **{n: c[n][:t] for n in ("q", "k", "v", "beta", "a", "p")}})
+        after = _run_noise(lib, {**c, **{n: c[n][:t + 1] for n in ("q", "k", "v", "beta", "a", "p")}})
+        P0 = np.stack([np.diag(1.0 / before["I_T"][:, i]) for i in range(dv)])
+        sl = lambda n: c[n][t:t + 1]
+        ex = oracle.kdn_exact_head(sl("q"), sl("k"), sl("v"), sl("beta"), sl("a"), sl("p"), P0=P0,
+                                   mu0=before["mu_T"], lib=lib)
+        _close(after["mu_T"], ex["mu_T"], rtol=1e-10, what=f"mean-field mean, step {t}")
+        for i in range(dv):
+            _close(after["I_T"][:, i], np.diag(np.linalg.inv(ex["P_T"][i])), rtol=1e-10,
+                   what=f"mean-field precision, step {t}")
 
 
-def pin_noise_static_limit(lib):
-    """a = 1 and p = 0: a static latent, so the filter is batch Bayesian
-    estimation: lambda_T = lambda_0 + sum w, mu_T = (lambda_0 mu_0 + sum beta v k) / lambda_T."""
-    c = noise_case(seed=45, T=10)
-    T = c["q"].shape[0]
-    c["a"] = np.ones(T)
-    c["p"] = np.zeros(T)
+def pin_noise_residual_write(lib):
+    """A token whose value the current mean already predicts exactly
+    (v = k^T a mu) writes nothing: only the precision and the decay move."""
+    c = noise_case(seed=45, T=1, dk=3, dv=2)
+    c["v"] = (c["k"][0] @ (c["a"][0] * c["mu0"]))[None, :]
     r = _run_noise(lib, c)
-    W = np.einsum("ti,tj->ji", c["beta"], c["k"] ** 2)
-    X = np.einsum("ti,tj->ji", c["beta"] * c["v"], c["k"])
-    lam = c["lam0"] + W
-    _close(r["I_T"], lam, what="static precision")
-    _close(r["mu_T"], (c["lam0"] * c["mu0"] + X) / lam, what="static mean")
+    _close(r["mu_T"], c["a"][0] * c["mu0"], what="no residual, no write")
 
 
 # ---------------------------------------------------------------------------
@@ -576,10 +567,72 @@ def pin_varlen_continuation(lib):
 M_PINS = [pin_m_gating_mamba2_limit, pin_m_gating_gradient, pin_varlen_continuation]
 
 
-NOISE_PINS = [pin_noise_equals_isotropic_single_entry, pin_noise_mobius, pin_noise_textbook_kalman,
-              pin_noise_static_limit]
+# ---------------------------------------------------------------------------
+# Exact KDN (dense Riccati)
+# ---------------------------------------------------------------------------
+def pin_exact_axis_keys_equal_diagonal(lib):
+    """With keys on the coordinate axes (k_t = +-e_j) and diagonal starting
+    covariances, the covariance stays diagonal, so the exact filter and the
+    diagonal (mean-field) filter are the same filter."""
+    g = np.random.default_rng(61)
+    c = noise_case(seed=61, T=15, dk=4, dv=3)
+    T, dk = c["q"].shape
+    dv = c["v"].shape[1]
+    k = np.zeros((T, dk))
+    k[np.arange(T), g.integers(0, dk, T)] = np.where(g.random(T) < 0.5, -1.0, 1.0)
+    c["k"] = k
+    P0 = np.stack([np.diag(1.0 / c["lam0"][:, i]) for i in range(dv)])
+    ex = oracle.kdn_exact_head(c["q"], k, c["v"], c["beta"], c["a"], c["p"], P0=P0, mu0=c["mu0"], lib=lib)
+    dg = _run_noise(lib, c)
+    _close(ex["o"], dg["o"], rtol=1e-10, what="exact vs diagonal, axis keys")
+    _close(ex["mu_T"], dg["mu_T"], rtol=1e-10, what="means, axis keys")
+    for i in range(dv):
+        _close(np.diag(ex["P_T"][i]), 1.0 / dg["I_T"][:, i], rtol=1e-10, what="variances, axis keys")
+
+
+def pin_exact_static_regression(lib):
+    """a = 1, p = 0: the posterior of a static column is Bayesian linear
+    regression: precision P0^-1 + sum beta k k^T, mean by a linear solve."""
+    c = noise_case(seed=62, T=12, dk=3, dv=2)
+    T, dk = c["q"].shape
+    dv = c["v"].shape[1]
+    g = np.random.default_rng(62)
+    P0 = []
+    for i in range(dv):
+        X = g.standard_normal((dk, dk))
+        P0.append(X @ X.T + dk * np.eye(dk))
+    P0 = np.stack(P0)
+    ex = oracle.kdn_exact_head(c["q"], c["k"], c["v"], c["beta"], np.ones(T), np.zeros(T), P0=P0,
+                               mu0=c["mu0"], lib=lib)
+    for i in range(dv):
+        Lam = np.linalg.inv(P0[i]) + sum(c["beta"][t, i] * np.outer(c["k"][t], c["k"][t]) for t in range(T))
+        rhs = np.linalg.inv(P0[i]) @ c["mu0"][:, i] + sum(c["beta"][t, i] * c["v"][t, i] * c["k"][t]
+                                                           for t in range(T))
+        _close(ex["mu_T"][:, i], np.linalg.solve(Lam, rhs), rtol=1e-9, what="regression mean")
+        _close(ex["P_T"][i], np.linalg.inv(Lam), rtol=1e-9, what="regression covariance")
+
+
+def pin_exact_covariance_valid(lib):
+    """Every final covariance is symmetric positive definite, and no larger
+    than the prediction alone would give (observations only add information)."""
+    c = noise_case(seed=63, T=30, dk=5, dv=2)
+    ex = oracle.kdn_exact_head(c["q"], c["k"], c["v"], c["beta"], c["a"], c["p"], lib=lib)
+    none = oracle.kdn_exact_head(c["q"], c["k"], c["v"], np.full_like(c["beta"], 1e-300), c["a"],
+                                 c["p"], lib=lib)
+    for i in range(2):
+        P = ex["P_T"][i]
+        _close(P, P.T, rtol=1e-12, what="symmetric")
+        assert np.all(np.linalg.eigvalsh(P) > 0)
+        assert np.all(np.linalg.eigvalsh(none["P_T"][i] - P) > -1e-12)
+
+
+EXACT_PINS = [pin_exact_axis_keys_equal_diagonal, pin_exact_static_regression, pin_exact_covariance_valid]
+
+
+NOISE_PINS = [pin_noise_equals_isotropic_single_entry, pin_noise_mobius, pin_noise_mean_field_step,
+              pin_noise_residual_write]
 
 
 BWD_PINS = [pin_bwd_finite_differences, pin_bwd_prior_start, pin_bwd_readout_only,
             pin_bwd_empty_sequence, pin_bwd_scale_bounds]
-ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS + NOISE_PINS + M_PINS
+ALL_PINS = DIAG_PINS + ISO_PINS + BWD_PINS + NOISE_PINS + M_PINS + EXACT_PINS

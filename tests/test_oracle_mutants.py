@@ -37,11 +37,19 @@ MUTANTS = {
     "bwd_prior_start_dropped": ("g[6][0] += gI;", "g[6][0] += 0.0 * gI;"),
     "bwd_readout_uses_key": ("gM += qq * go;", "gM += kk * go;"),
     # diagonal KDN with process noise
-    "noise_dropped": ("a[t] * a[t] / lam[e] + p[t];", "a[t] * a[t] / lam[e];"),
-    "noise_decay_not_squared": ("a[t] * a[t] / lam[e] + p[t];", "a[t] / lam[e] + p[t];"),
-    "noise_mean_not_decayed": ("lambda_pred * a[t] * mu[e]", "lambda_pred * mu[e]"),
-    "noise_obs_not_squared": ("const double obs = bt[i] * kt[j] * kt[j];", "const double obs = bt[i] * kt[j];"),
-    "noise_write_uses_query": ("bt[i] * vt[i] * kt[j]) / lambda_new;", "bt[i] * vt[i] * qt[j]) / lambda_new;"),
+    "noise_dropped": ("var_pred[j] = a[t] * a[t] / lam[e] + p[t];", "var_pred[j] = a[t] * a[t] / lam[e];"),
+    "noise_decay_not_squared": ("var_pred[j] = a[t] * a[t] / lam[e] + p[t];", "var_pred[j] = a[t] / lam[e] + p[t];"),
+    "noise_mean_not_decayed": ("mean_pred[j] = a[t] * mu[e];", "mean_pred[j] = mu[e];"),
+    "noise_obs_not_squared": ("lam[e] = 1.0 / var_pred[j] + bt[i] * kt[j] * kt[j];", "lam[e] = 1.0 / var_pred[j] + bt[i] * kt[j];"),
+    "noise_gain_ignores_obs_noise": ("double S = 1.0 / bt[i];", "double S = 0.0;"),
+    "noise_write_not_residual": ("const double residual = vt[i] - prediction;", "const double residual = vt[i];"),
+    "noise_gain_uses_query": ("var_pred[j] * kt[j] * residual / S;", "var_pred[j] * qt[j] * residual / S;"),
+    # exact KDN
+    "exact_noise_dropped": ("Pi[r * dk + r] += p[t];", "Pi[r * dk + r] += 0.0 * p[t];"),
+    "exact_mean_not_decayed": ("mi[r] *= a[t];", "mi[r] *= 1.0;"),
+    "exact_gain_unnormalised": ("mi[r] += u[r] / S * resid;", "mi[r] += u[r] * resid;"),
+    "exact_cov_update_sign": ("Pi[r * dk + c] -= u[r] * u[c] / S;", "Pi[r * dk + c] += u[r] * u[c] / S;"),
+    "exact_obs_noise_wrong": ("double S = 1.0 / beta[t * dv + i];", "double S = beta[t * dv + i];"),
 }
 
 
