@@ -1,24 +1,28 @@
-// diag_noise.hip -- diagonal KDN with process noise, forward.
+// diag_noise.hip -- Diagonal KDN with process noise, forward.
 //
-// Every memory entry [j][i] of a head is its own scalar Kalman filter (Kalman
-// Delta Networks abstract, "Diagonal KDN"; predict step as in the KLA summary,
-// Metodologia 1: the latent decays by a_t and gains process noise p_t; write
-// as in the Palimpsa summary, Metodologia 2).  In information form, with the
-// entry's observation precision w = beta_t[i] k_t[j]^2:
-//   r_t     = 1 / (a_t^2 + p_t lambda_{t-1})          (so lambda^- = lambda r)
-//   lambda_t = lambda_{t-1} r_t + w                   (a Mobius map of lambda_{t-1})
-//   eta_t   = a_t r_t eta_{t-1} + beta_t[i] v_t[i] k_t[j]      (eta = lambda mu)
-//   o_t[i]  = sum_j q_t[j] eta_t[j][i] / lambda_t[j][i]
-// The decay a_t r_t differs per entry, so unlike the Palimpsa recurrence
-// there is no shared scale to fold away: each entry-step costs two
-// reciprocals.
+// Kalman Delta Networks abstract, "Diagonal KDN": each one-step posterior is
+// projected onto the diagonal Gaussian family by online mean-field VI, and
+// the Kalman gain weights each residual write.  Memory column i is a latent
+// s_i in R^{d_k} observed through v_t[i] = k_t^T s_i + noise (precision
+// beta_t[i]); the predict step decays by a_t and adds process noise p_t (KLA
+// summary, Metodologia 1).  Per entry the kernel keeps a variance sig = 1/lambda
+// and a mean mu.  Per token, for every column i:
+//   sp   = a^2 sig + p,   mp = a mu                        (predict, per entry)
+//   S_i  = sum_j k_j^2 sp_j + 1/beta_i,  r_i = v_i - sum_j k_j mp_j
+//   mu   = mp + sp k_j r_i / S_i                           (residual write)
+//   sig  = sp / (1 + beta_i k_j^2 sp)                      (diagonal of the
+//                                                           posterior precision)
+//   o_t[i] = sum_j q_j mu_j
+// The precision 1/sig follows the Mobius map l -> ((1 + w p) l + w a^2) / (p l + a^2),
+// w = beta k^2.
 //
 // Work decomposition as in the diagonal scan: a workgroup owns one head and
 // one tile of value columns for the whole sequence; lane <-> value column i,
 // JP key rows per lane in VGPRs; tokens staged 16 at a time through LDS
-// (double-buffered, widened to fp32); the key-side values reach the fmacs as
-// DPP row broadcasts; per-token partial read-outs of the row groups are
-// summed through LDS once per chunk.
+// (double-buffered, widened to fp32); key-side values reach the fmacs as DPP
+// row broadcasts.  The two sums over j per (token, column) are the only
+// coupling between entries: each row group's partial sums meet in a
+// double-buffered LDS slot behind one barrier per token.
 #include "kdn_lane.h"
 #include "kdn_params.h"
 
@@ -46,11 +50,12 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
         float k[C][DK];
         float k2[C][DK];
         float q[C][DK];
-        float2 bv[C][CI];   // (beta_i, beta_i v_i)
+        float2 bv[C][CI];   // (beta_i, v_i)
         float4 sc[C];       // (a^2, p, a, -)
     };
     __shared__ Stage stg[2];
     __shared__ float opart[2][C][P][CI];
+    __shared__ float2 red[2][P][CI];   // per-token partial (sum k^2 sp, sum k mp) of each row group
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -72,13 +77,12 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
     const float* ah = p.a + bh * T;
     const float* ph = p.p + bh * T;
 
-    float lam[JP], eta[JP];
+    float sig[JP], mu[JP];   // variance 1/lambda and mean of each entry
 #pragma unroll
     for (int r = 0; r < JP; ++r) {
         const int64_t off = (bh * DK + j0 + r) * p.dv + i;
-        const float l0 = p.lam0 ? p.lam0[off] : 1.0f;
-        lam[r] = l0;
-        eta[r] = l0 * (p.mu0 ? p.mu0[off] : 0.0f);
+        sig[r] = p.lam0 ? 1.0f / p.lam0[off] : 1.0f;
+        mu[r] = p.mu0 ? p.mu0[off] : 0.0f;
     }
 
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
                 widen<BF16>(rv[n], fv);
                 widen<BF16>(rb[n], fb);
 #pragma unroll
-                for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fb[e] * fv[e]);
+                for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fv[e]);
             }
         }
         if (tid < L) S.sc[tid] = make_float4(rap.x * rap.x, rap.y, rap.x, 0.0f);
@@ -171,25 +175,39 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
             const float2 bvv_n = S.bv[tn][col];
             const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl], vq_n = S.q[tn][jl];
 
-            // predict: r = 1 / (a^2 + p lambda), lambda^- = lambda r, eta -> a r eta
+            // predict, and this row group's share of the two sums over j
+            float ps[2] = {0.0f, 0.0f}, pm[2] = {0.0f, 0.0f};
+            float sp[JP];
 #pragma unroll
             for (int r = 0; r < JP; ++r) {
-                const float rr = fast_rcp(fmaf(sc.y, lam[r], sc.x));
-                lam[r] *= rr;
-                eta[r] *= sc.z * rr;
+                sp[r] = fmaf(sc.x, sig[r], sc.y);
+                mu[r] *= sc.z;
             }
-            // update: lambda += beta_i k_j^2, eta += beta_i v_i k_j
             Unroll<0, JP>::run([&](auto rr) {
                 constexpr int r = decltype(rr)::value;
-                fmac_bcast<r>(lam[r], vk2, bvv.x);
+                fmac_bcast<r>(ps[r & 1], vk2, sp[r]);   // sum_j k_j^2 sp_j
+                fmac_bcast<r>(pm[r & 1], vk, mu[r]);    // sum_j k_j mp_j
             });
+            red[tt & 1][rg][col] = make_float2(ps[0] + ps[1], pm[0] + pm[1]);
+            __syncthreads();
+            float Ssum = fast_rcp(bvv.x), pred = 0.0f;
+#pragma unroll
+            for (int g = 0; g < P; ++g) {
+                const float2 x = red[tt & 1][g][col];
+                Ssum += x.x;
+                pred += x.y;
+            }
+            // residual write with the Kalman gain, and the projected variance
+            const float gain = (bvv.y - pred) * fast_rcp(Ssum);
             Unroll<0, JP>::run([&](auto rr) {
                 constexpr int r = decltype(rr)::value;
-                fmac_bcast<r>(eta[r], vk, bvv.y);
+                fmac_bcast<r>(mu[r], vk, sp[r] * gain);
+                const float den = fmaf(bcast<r>(vk2) * bvv.x, sp[r], 1.0f);
+                sig[r] = sp[r] * fast_rcp(den);
             });
             float m[JP];
 #pragma unroll
-            for (int r = 0; r < JP; ++r) m[r] = eta[r] * fast_rcp(lam[r]);
+            for (int r = 0; r < JP; ++r) m[r] = mu[r];
             float acc[4];
             Unroll<0, 4>::run([&](auto rr) {
                 constexpr int r = decltype(rr)::value;
@@ -223,8 +241,8 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
 #pragma unroll
     for (int r = 0; r < JP; ++r) {
         const int64_t off = (bh * DK + j0 + r) * p.dv + i;
-        if (p.lam_T) p.lam_T[off] = lam[r];
-        if (p.mu_T) p.mu_T[off] = eta[r] / lam[r];
+        if (p.lam_T) p.lam_T[off] = 1.0f / sig[r];
+        if (p.mu_T) p.mu_T[off] = mu[r];
     }
 }
 

@@ -34,9 +34,10 @@ ISO_FLOPS_PER_ENTRY_STEP = 5     # mean update 3, read-out 2
 # gradient: state recurrences 4, mu = eta / I 2, adjoint updates 4 (g = q dout, g / I, g mu / I),
 # dq 2, dk 4, dbeta / dv row sums 4, dalpha 4
 BWD_FLOPS_PER_ENTRY_STEP = 24
-# process-noise filter: predict 6 (a^2 + p lambda 2, reciprocal, lambda r, a r, eta a r),
-# update 4, read-out 4 (reciprocal, multiply, multiply-add)
-NOISE_FLOPS_PER_ENTRY_STEP = 14
+# Diagonal KDN (residual write): predict 3 (a^2 sig + p, a mu), the two sums over j 4,
+# mean write 3 (sp gain, fma), projected variance 5 (beta k^2, fma, reciprocal, multiply),
+# read-out 2
+NOISE_FLOPS_PER_ENTRY_STEP = 17
 
 
 def _args():

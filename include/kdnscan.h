@@ -120,15 +120,18 @@ int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
                              void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
- * Diagonal KDN with process noise, forward [KDN abstract, Diagonal KDN;
- * predict step KLA Metodologia 1; write Palimpsa Metodologia 2].  Every
- * memory entry [j][i] of head (b, h) is a scalar Kalman filter:
- *   predict  variance 1/lambda -> a_t^2/lambda + p_t,  mean mu -> a_t mu
- *   update   lambda_t = lambda^- + beta_t[i] k_t[j]^2
- *            mu_t = (lambda^- a_t mu_{t-1} + beta_t[i] v_t[i] k_t[j]) / lambda_t
+ * Diagonal KDN with process noise, forward [KDN abstract, Diagonal KDN:
+ * one-step posteriors projected onto diagonal Gaussians by mean-field VI,
+ * residual writes weighted by the Kalman gain; predict step KLA
+ * Metodologia 1].  Memory column i of head (b, h) is a latent vector
+ * observed through v_t[i] = k_t^T s_i + noise of precision beta_t[i]; each
+ * entry [j][i] keeps a mean and a precision lambda.  Per token:
+ *   predict  variance 1/lambda -> a_t^2/lambda + p_t (= sp),  mean -> a_t mu
+ *   update   mu[j][i] += sp k_j (v_i - sum_l k_l mu[l][i]) / (sum_l k_l^2 sp_l + 1/beta_i)
+ *            lambda[j][i] = 1/sp + beta_i k_j^2
  *   read     o_t[i] = sum_j q_t[j] mu_t[j][i]
- * i.e. lambda follows the Mobius map l -> ((1 + w p) l + w a^2) / (p l + a^2)
- * with w = beta k^2.
+ * so lambda follows the Mobius map l -> ((1 + w p) l + w a^2) / (p l + a^2),
+ * w = beta k^2.
  * Inputs: q, k [B,H,T,d_k]; v, beta [B,H,T,d_v] (in_dtype); a, p [B,H,T]
  *   float (decay, process-noise variance); lambda0, mu0 [B,H,d_k,d_v] float
  *   or NULL (-> 1 and 0).
