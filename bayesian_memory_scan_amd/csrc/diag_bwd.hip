@@ -188,8 +188,8 @@ __device__ __forceinline__ void bwd_step_inplace(float (&I)[16], float (&E)[16],
         const float r = __uint_as_float(rb);
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
-            I[c] *= r;
-            E[c] *= r;
+            scale_inplace(I[c], r);
+            scale_inplace(E[c], r);
         }
     }
     Unroll<0, 16>::run([&](auto cc) {
@@ -293,7 +293,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
 
     float I[16], m0[16], J[16], E[16];
     start_state(p, (bh * DK + j) * p.dv + tile * CI + cg * 16, I, J, E, m0);
-    float* ck = p.ckpt + (bh * Sh::NTILE + tile) * nch * 2 * Sh::BLK + (cg * DK + j) * 16;
+    float* ck = p.ckpt + (bh * Sh::NTILE + tile) * (nch + 1) * 2 * Sh::BLK + (cg * DK + j) * 16;
     store16(ck, J);
     store16(ck + Sh::BLK, E);
 
@@ -301,7 +301,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
         const int64_t rem = p.T - c * C;
         return static_cast<int>(rem < C ? rem : C);
     };
-    const int64_t nrun = nch - 1;               // the last chunk's end state is not needed
+    const int64_t nrun = nch;                   // slot nch: the final state (for the last token's adjoint)
     if (nrun > 0) {
         ld.fetch(p, bh, tile, 0, chunk_len(0), tid);
         ld.commit(stg[0], chunk_len(0), tid);
@@ -383,7 +383,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         M[c] = 0.0f;
     }
 
-    const float* ckb = p.ckpt + (bh * Sh::NTILE + tile) * nch * 2 * Sh::BLK + (cg * DK + j) * 16;
+    const float* ckb = p.ckpt + (bh * Sh::NTILE + tile) * (nch + 1) * 2 * Sh::BLK + (cg * DK + j) * 16;
 
     auto chunk_len = [&](int64_t c) -> int {
         const int64_t rem = T - c * C;
@@ -393,6 +393,22 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
     if (nch > 0) {
         ld.fetch(p, bh, tile, (nch - 1) * C, chunk_len(nch - 1), tid);
         ld.commit(stg[0], chunk_len(nch - 1), tid);
+        // Gradients arriving through the final state, in the last token's
+        // frame (s = s_{T-1}): lam_eta = dmu_T / I_T and lam_I = dI_T -
+        // dmu_T mu_T / I_T, scaled by 1 / s.  The checkpoint pass stored the
+        // final state (J_T, eta_T) unscaled after the last chunk.
+        float JT[16], ET[16];
+        load16(ckb + nch * 2 * Sh::BLK, JT);
+        load16(ckb + nch * 2 * Sh::BLK + Sh::BLK, ET);
+        const float inv_s = 1.0f / uniform(p.scal[bh * T + T - 1].z);
+        Unroll<0, 16>::run([&](auto cc) {
+            constexpr int c = decltype(cc)::value;
+            const float gm = p.dmu_T ? p.dmu_T[ent + c] : 0.0f;
+            const float gi = p.dI_T ? p.dI_T[ent + c] : 0.0f;
+            const float rI = 1.0f / (JT[c] + I_prior);          // 1 / I_T
+            L[c] = gm * rI * inv_s;
+            M[c] = (gi - gm * ET[c] * rI * rI) * inv_s;
+        });
     }
     __syncthreads();
 
@@ -402,9 +418,11 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const int64_t t = t0 + tt;
         const float4 sct = S.sc[tt];
         const float sIp = uniform(sct.z) * I_prior;     // s_t I_prior: I~ = J~ + s I_prior
-        if (t + 1 < T) {
+        const bool has_next = t + 1 < T;
+        {
             // dalpha of token t+1: (L, M) still belong to it (its frame), (J, E)
-            // is the state before it
+            // is the state before it (computed for every token, written when
+            // token t+1 exists)
             float x1a = 0.0f, x1b = 0.0f, x2 = 0.0f;
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
@@ -416,8 +434,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             if (lane == 0) xs[tt][w].x = tot;
             if (lane == 32) xs[tt][w].y = tot;
             const float4 scn = S.sc[tt + 1];
-            const float rho_n = uniform(tt + 1 < Lc ? scn.x : scn.x / sct.z);
-            if (tid == 0) {
+            const float rho_n = has_next ? uniform(tt + 1 < Lc ? scn.x : scn.x / sct.z) : 1.0f;
+            if (tid == 0 && has_next) {
                 // rho_{t+1} / alpha_{t+1}: 1 / s_t where token t+1 starts a frame
                 // (rho = alpha / s_t there), else 1 / alpha_{t+1}
                 const bool start = __float_as_uint(rho_n) != 0x3f800000u;
@@ -427,24 +445,10 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             if (__float_as_uint(rho_n) != 0x3f800000u) {
 #pragma unroll
                 for (int c = 0; c < 16; ++c) {
-                    L[c] *= rho_n;
-                    M[c] *= rho_n;
+                    scale_inplace(L[c], rho_n);
+                    scale_inplace(M[c], rho_n);
                 }
             }
-        } else {
-            // last token: gradients arriving through the final state
-            // (lam_eta += dmu_T / I_T, lam_I += dI_T - dmu_T mu_T / I_T), scaled;
-            // one column at a time to keep register pressure down
-            const float inv_s = 1.0f / uniform(sct.z);
-            Unroll<0, 16>::run([&](auto cc) {
-                constexpr int c = decltype(cc)::value;
-                const float gm = p.dmu_T ? p.dmu_T[ent + c] : 0.0f;
-                const float gi = p.dI_T ? p.dI_T[ent + c] : 0.0f;
-                const float r = fast_rcp(J[c] + sIp);
-                const float gr = gm * r;
-                L[c] = gr;
-                M[c] = fmaf(-gr, E[c] * r, gi * inv_s);
-            });
         }
 
         const float kj = S.k[tt][j];
@@ -453,8 +457,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const float bc = dpp_src(S.b[tt][lc]);
         const float bvc = dpp_src(S.b[tt][lc] * S.v[tt][lc]);
         const float gc = dpp_src(S.g[tt][lc]);
-        float dq4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        float dka[2] = {0.0f, 0.0f}, dkb[2] = {0.0f, 0.0f};
+        const float ngc = dpp_src(-S.g[tt][lc]);
+        float dq4[4], dka[2], dkb[2];
         // The row sums P_c = sum_j M k_j^2 and Q_c = sum_j L k_j are folded into
         // the 64-lane butterfly as soon as column c is done (the first two
         // levels pair P_c with Q_c, then column c with c + 8).
@@ -463,12 +467,20 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             constexpr int c = decltype(cc)::value;
             const float r = fast_rcp(J[c] + sIp);
             const float mu = E[c] * r;
-            fmac_bcast<c>(dq4[c & 3], gc, mu);              // dq_j  += dout_c mu
-            const float gr = bcast<c>(gc) * (qj * r);       // q_j dout_c / I~
-            L[c] += gr;
-            M[c] = fmaf(-gr, mu, M[c]);
-            fmac_bcast<c>(dka[c & 1], bc, M[c]);            // sum_c beta_c M
-            fmac_bcast<c>(dkb[c & 1], bvc, L[c]);           // sum_c beta_c v_c L
+            const float qr = qj * r;
+            fmac_bcast<c>(L[c], gc, qr);                    // L += q_j dout_c / I~
+            fmac_bcast<c>(M[c], ngc, qr * mu);              // M -= q_j dout_c mu / I~
+            // dq_j += dout_c mu; sum_c beta_c M; sum_c beta_c v_c L (first
+            // products start the accumulators)
+            if constexpr (c < 4) dq4[c] = bcast<c>(gc) * mu;
+            else fmac_bcast<c>(dq4[c & 3], gc, mu);
+            if constexpr (c < 2) {
+                dka[c] = bcast<c>(bc) * M[c];
+                dkb[c] = bcast<c>(bvc) * L[c];
+            } else {
+                fmac_bcast<c>(dka[c & 1], bc, M[c]);
+                fmac_bcast<c>(dkb[c & 1], bvc, L[c]);
+            }
             const float wc = swap32_add(M[c] * k2j, L[c] * kj);
             if constexpr (c < 8) wlo[c] = wc;
             else x8[c - 8] = swap16_add(wlo[c - 8], wc);
@@ -522,7 +534,6 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 constexpr int u = HELD - 1 - decltype(uu)::value;
                 const int tt = HELD * m + u;
                 if (tt < Lc) reverse_step(S, tt, t0, Lc, sJ[u], sE[u]);
-                __builtin_amdgcn_sched_barrier(0);   // keep steps apart: bounds register pressure
             });
         }
 

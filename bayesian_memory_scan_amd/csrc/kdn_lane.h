@@ -29,6 +29,14 @@ __device__ __forceinline__ float dpp_src(float x) {
     return x;
 }
 
+// x *= s in place (the result stays in x's register).  Used inside uniform
+// branches on loop-carried state: a plain multiply lets the register
+// allocator pick a new register in one branch and then copy every value
+// back at the merge.
+__device__ __forceinline__ void scale_inplace(float& x, float s) {
+    asm("v_mul_f32 %0, %1, %0" : "+v"(x) : "s"(s));
+}
+
 // Compile-time loop N, N+1, ..., END-1 (register arrays need constant indices).
 template <int N, int END>
 struct Unroll {

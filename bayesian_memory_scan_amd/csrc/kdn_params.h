@@ -108,7 +108,7 @@ struct BwdParams {
     float* dq;            // [BH,T,dk]
     float* dk;            // [BH,T,dk]
     const float4* scal;   // [BH][T] frame scalars (rho, dP, s, A d) from the prep pass
-    float* ckpt;          // [BH][ntile][nch][2][dk*CI]: state before each chunk, unscaled
+    float* ckpt;          // [BH][ntile][nch+1][2][dk*CI]: state before each chunk and the final state, unscaled
     float* part_dq;       // [ntile][BH,T,dk] column-tile partial sums (== dq when ntile == 1)
     float* part_dk;       // [ntile][BH,T,dk] (== dk when ntile == 1)
     float* part_da;       // [ntile][BH,T]: d loss / d alpha_t per column tile

@@ -328,7 +328,7 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     if (BH * ntile > kMaxGrid || BH > kMaxGrid) return KDN_EINVAL;
     const size_t f = sizeof(float);
     const size_t b_scal = align_up(16 * static_cast<size_t>(BH) * T, 256);
-    const size_t b_ckpt = align_up(f * static_cast<size_t>(BH) * nch * 2 * d_k * d_v, 256);
+    const size_t b_ckpt = align_up(f * static_cast<size_t>(BH) * (nch + 1) * 2 * d_k * d_v, 256);
     const size_t b_rows = ntile > 1 ? align_up(f * static_cast<size_t>(ntile) * BH * T * d_k, 256) : 0;
     const size_t b_tok = align_up(f * static_cast<size_t>(ntile) * BH * T, 256);
     const size_t b_dip0 = align_up(f * static_cast<size_t>(ntile) * BH, 256);
