@@ -313,12 +313,20 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
         const int b = static_cast<int>(c & 1);
         const BwdStage<DK, CI, false>& S = stg[b];
         const int L = chunk_len(c);
+        // software-pipelined: the next token's LDS operands load while this one computes
+        float2 scx = make_float2(S.sc[0].x, S.sc[0].z);
+        float kj = S.k[0][j], bj = S.b[0][lc], vj = S.v[0][lc];
         for (int tt = 0; tt < L; ++tt) {
-            const float4 sc = S.sc[tt];
-            const float kj = S.k[tt][j];
-            const float b = S.b[tt][lc] * sc.z;
-            const float bvs = dpp_src(b * S.v[tt][lc]);
-            bwd_step_inplace(J, E, sc.x, dpp_src(b), bvs, kj, kj * kj);
+            const int tn = tt + 1 < L ? tt + 1 : tt;
+            const float2 scx_n = make_float2(S.sc[tn].x, S.sc[tn].z);
+            const float kj_n = S.k[tn][j], bj_n = S.b[tn][lc], vj_n = S.v[tn][lc];
+            const float b = bj * scx.y;
+            const float bvs = dpp_src(b * vj);
+            bwd_step_inplace(J, E, scx.x, dpp_src(b), bvs, kj, kj * kj);
+            scx = scx_n;
+            kj = kj_n;
+            bj = bj_n;
+            vj = vj_n;
         }
         // unscale and store the state before chunk c + 1
         const float inv_s = 1.0f / uniform(S.sc[L - 1].z);
@@ -512,10 +520,23 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 bvs = dpp_src(b * S.v[tt][lc]);
                 bs = dpp_src(b);
             };
-            for (int tt = 0; tt < HELD * m; ++tt) {
-                float rho, bs, bvs, kj;
-                operands(tt, rho, bs, bvs, kj);
-                bwd_step_inplace(sJ[0], sE[0], rho, bs, bvs, kj, kj * kj);
+            {
+                // software-pipelined like the checkpoint pass
+                const int n = HELD * m;
+                float2 scx = make_float2(S.sc[0].x, S.sc[0].z);
+                float kj = S.k[0][j], bj = S.b[0][lc], vj = S.v[0][lc];
+                for (int tt = 0; tt < n; ++tt) {
+                    const int tn = tt + 1 < n ? tt + 1 : tt;
+                    const float2 scx_n = make_float2(S.sc[tn].x, S.sc[tn].z);
+                    const float kj_n = S.k[tn][j], bj_n = S.b[tn][lc], vj_n = S.v[tn][lc];
+                    const float b = bj * scx.y;
+                    const float bvs = dpp_src(b * vj);
+                    bwd_step_inplace(sJ[0], sE[0], scx.x, dpp_src(b), bvs, kj, kj * kj);
+                    scx = scx_n;
+                    kj = kj_n;
+                    bj = bj_n;
+                    vj = vj_n;
+                }
             }
             Unroll<0, HELD>::run([&](auto uu) {
                 constexpr int u = decltype(uu)::value;
