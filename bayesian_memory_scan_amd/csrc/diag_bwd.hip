@@ -240,6 +240,15 @@ __device__ __forceinline__ void load16(const float* src, float (&x)[16]) {
     }
 }
 
+// Checkpoint slot c (0 <= c <= nch) of run r (= bh * NTILE + tile), each slot
+// 2 * BLK floats (J then eta).  Slots 0 .. nch-1 of a run are contiguous; the
+// final states (slot nch) of all runs follow after every run's slots, so the
+// per-run stride stays nch slots (a power of two for power-of-two T).
+template <int BLK>
+__device__ __forceinline__ float* ckpt_slot(float* base, int64_t r, int64_t c, int64_t nch, int64_t nruns) {
+    return c < nch ? base + (r * nch + c) * 2 * BLK : base + (nruns * nch + r) * 2 * BLK;
+}
+
 __device__ __forceinline__ void store16(float* dst, const float (&x)[16]) {
 #pragma unroll
     for (int n = 0; n < 4; ++n)
@@ -293,7 +302,10 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
 
     float I[16], m0[16], J[16], E[16];
     start_state(p, (bh * DK + j) * p.dv + tile * CI + cg * 16, I, J, E, m0);
-    float* ck = p.ckpt + (bh * Sh::NTILE + tile) * (nch + 1) * 2 * Sh::BLK + (cg * DK + j) * 16;
+    const int64_t run = bh * Sh::NTILE + tile;
+    const int64_t nruns = p.BH * Sh::NTILE;
+    const int64_t lane_off = (cg * DK + j) * 16;
+    float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, 0, nch, nruns) + lane_off;
     store16(ck, J);
     store16(ck + Sh::BLK, E);
 
@@ -335,7 +347,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
             J[e] *= inv_s;
             E[e] *= inv_s;
         }
-        float* dst = ck + (c + 1) * 2 * Sh::BLK;
+        float* dst = ckpt_slot<Sh::BLK>(p.ckpt, run, c + 1, nch, nruns) + lane_off;
         store16(dst, J);
         store16(dst + Sh::BLK, E);
         if (c + 1 < nrun) ld.commit(stg[b ^ 1], chunk_len(c + 1), tid);
@@ -391,7 +403,9 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         M[c] = 0.0f;
     }
 
-    const float* ckb = p.ckpt + (bh * Sh::NTILE + tile) * (nch + 1) * 2 * Sh::BLK + (cg * DK + j) * 16;
+    const int64_t run = bh * Sh::NTILE + tile;
+    const int64_t nruns = p.BH * Sh::NTILE;
+    const int64_t lane_off = (cg * DK + j) * 16;
 
     auto chunk_len = [&](int64_t c) -> int {
         const int64_t rem = T - c * C;
@@ -406,8 +420,9 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         // dmu_T mu_T / I_T, scaled by 1 / s.  The checkpoint pass stored the
         // final state (J_T, eta_T) unscaled after the last chunk.
         float JT[16], ET[16];
-        load16(ckb + nch * 2 * Sh::BLK, JT);
-        load16(ckb + nch * 2 * Sh::BLK + Sh::BLK, ET);
+        const float* ckT = ckpt_slot<Sh::BLK>(p.ckpt, run, nch, nch, nruns) + lane_off;
+        load16(ckT, JT);
+        load16(ckT + Sh::BLK, ET);
         const float inv_s = 1.0f / uniform(p.scal[bh * T + T - 1].z);
         Unroll<0, 16>::run([&](auto cc) {
             constexpr int c = decltype(cc)::value;
@@ -504,7 +519,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const BwdStage<DK, CI, true>& S = stg[b];
         const int Lc = chunk_len(c);
         const int64_t t0 = c * C;
-        const float* ck = ckb + c * 2 * Sh::BLK;
+        const float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, c, nch, nruns) + lane_off;
         const int nheld = (Lc + HELD - 1) / HELD;
 
         for (int m = nheld - 1; m >= 0; --m) {
