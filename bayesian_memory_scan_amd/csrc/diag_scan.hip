@@ -410,8 +410,11 @@ __global__ __launch_bounds__(256) void k_diag_prep_varlen(DiagParams p) {
 }
 
 // Carry pass: in order over segments, turn each segment's composite into the
-// state it starts from.  One thread per memory entry of every head.
+// state it starts from.  One thread per memory entry of every head.  The
+// composites of 8 segments are loaded together, so a long chain of segments
+// costs one memory round trip per 8 (the isotropic pass touches only eta).
 __global__ __launch_bounds__(256) void k_diag_carry(DiagParams p, int64_t dk, int64_t n_total, int iso) {
+    constexpr int B8 = 8;
     const int64_t n_per_head = dk * p.dv;
     const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
     if (e >= n_total) return;
@@ -429,18 +432,27 @@ __global__ __launch_bounds__(256) void k_diag_carry(DiagParams p, int64_t dk, in
     } else {
         eta = p.I_prior * m0;
     }
-    for (int s = 0; s < p.S; ++s) {
-        float* slot = p.comp + ((bh * p.S + s) * 2) * n_per_head;
-        float Js = 0.0f, es = 0.0f, G = 1.0f;
-        if (s + 1 < p.S) {
-            Js = slot[r];
-            es = slot[n_per_head + r];
-            G = p.gdec[bh * p.S + s];
+    float* const base = p.comp + bh * p.S * 2 * n_per_head + r;
+    for (int s0 = 0; s0 < p.S; s0 += B8) {
+        float Js[B8], es[B8], G[B8];
+#pragma unroll
+        for (int u = 0; u < B8; ++u) {
+            const int s = s0 + u;
+            const bool has = s + 1 < p.S;     // the last segment's composite is never read
+            Js[u] = has && !iso ? base[s * 2 * n_per_head] : 0.0f;
+            es[u] = has ? base[(s * 2 + 1) * n_per_head] : 0.0f;
+            G[u] = has ? p.gdec[bh * p.S + s] : 1.0f;
         }
-        slot[r] = J;
-        slot[n_per_head + r] = eta;
-        J = __builtin_fmaf(G, J, Js);
-        eta = __builtin_fmaf(G, eta, es);
+#pragma unroll
+        for (int u = 0; u < B8; ++u) {
+            const int s = s0 + u;
+            if (s < p.S) {
+                if (!iso) base[s * 2 * n_per_head] = J;
+                base[(s * 2 + 1) * n_per_head] = eta;
+            }
+            J = __builtin_fmaf(G[u], J, Js[u]);
+            eta = __builtin_fmaf(G[u], eta, es[u]);
+        }
     }
 }
 

@@ -13,10 +13,29 @@
 // runs on v_mfma_f32_16x16x4f32.  Lane layout (checked on the device): A[i][k]
 // in lane i + 16k, B[k][j] in lane j + 16k, D[i][j] in lane j + 16(i/4), reg i%4.
 //
-// A workgroup owns one (head, segment); wave w owns value columns
-// [16w, 16w+16) and keeps its d_k x 16 slice of mu in MFMA accumulators.  The
-// segment composite pass (COMPOSITE) runs only the state update from a zero
-// state; segments are then combined in order by the shared carry pass.
+// One wave per (head, segment, tile of NC <= 64 value columns), no barriers:
+// every operand is loaded from global memory straight into the register
+// layout its MFMA wants.  Lane (c, g) = lane c + 16 g.
+//   * mu (d_k x NC) lives in MFMA accumulators as MT x NT tiles of 16 x 16.
+//     Tiles interleave rows and columns: tile (m, n) element (i, j) is
+//     mu[MT i + m][NT j + n], so lane (c, g), register r of tile (m, n) holds
+//     mu[MT (4g + r) + m][NT c + n].  A lane's registers then cover contiguous
+//     runs of columns (vector loads and stores) and of rows.
+//   * A contraction may visit its summation index in any order, provided both
+//     operands agree.  Q mu visits d_k row j = MT (4g + r) + m at k-step
+//     (m, r), lane group g, so its B operand is the lane's own accumulator
+//     register and its A operand is the run Q[t][4 MT g .. 4 MT g + 4 MT).
+//     Q K^T visits the same order.
+//   * The wave computes S^T = K Q^T rather than S: its accumulator layout,
+//     S[t = c][s = 4g + r] in lane (c, g), register r, is the A-operand layout
+//     of (S (.) D) V with token s = 4g + kk at k-step kk, so no transpose.
+//   * (S (.) D) V and the state update visit token s = 4g + kk and share the
+//     V operand V[s][NT c + n].  The update's A operand K[s][MT c + m] is
+//     the chunk's k transposed; the main pass writes its q-side k to a
+//     per-wave LDS tile and reads it back transposed (the only LDS use).
+// The segment composite pass (COMPOSITE) runs only the state update from a
+// zero state; segments are then combined in order by the shared carry pass.
+#include "kdn_lane.h"
 #include "kdn_params.h"
 
 namespace kdn {
@@ -28,44 +47,133 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 }
 
 constexpr int kIsoChunk = 16;
+// Value columns per wave: at d_k = d_v = 64 one wave holds the head's whole
+// mu (64 registers) and two operand sets within the 256 registers of two
+// waves per SIMD, and nothing (S = Q K^T, the q and k reads) is repeated
+// across column tiles.
+constexpr int kIsoCols = 64;
 
-template <int DK, int DV, bool COMPOSITE>
-__global__ __launch_bounds__(DV / 16 * kWave) void k_iso(DiagParams p) {
+// Buffer resource over `bytes` bytes from `base` (raw, untyped, gfx9 format
+// word).  Loads past the end return 0 and stores past the end are dropped, so
+// a ragged chunk needs no branches: the wait counters stay exact and the next
+// chunk's loads stay in flight.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// N contiguous floats at byte offset `off` (16-byte aligned for N >= 4,
+// 8-byte for N == 2).
+template <int N>
+__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[N]) {
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * e, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[e + i] = __uint_as_float(u[i]);
+        }
+    } else if constexpr (N == 2) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        x[0] = __uint_as_float(u[0]);
+        x[1] = __uint_as_float(u[1]);
+    } else {
+        x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[N]) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int e = 0; e < N; e += 4) {
+            const u32x4 u = {__float_as_uint(x[e]), __float_as_uint(x[e + 1]), __float_as_uint(x[e + 2]),
+                             __float_as_uint(x[e + 3])};
+            __builtin_amdgcn_raw_buffer_store_b128(u, r, off + 4 * e, 0, 0);
+        }
+    } else if constexpr (N == 2) {
+        const u32x2 u = {__float_as_uint(x[0]), __float_as_uint(x[1])};
+        __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
+    } else {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, off, 0, 0);
+    }
+}
+
+// N contiguous floats (16-byte aligned for N >= 4, 8-byte for N == 2).
+template <int N>
+__device__ __forceinline__ void store_run(float* dst, const float (&x)[N]) {
+    if constexpr (N >= 4) {
+#pragma unroll
+        for (int e = 0; e < N; e += 4)
+            *reinterpret_cast<float4*>(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
+    } else if constexpr (N == 2) {
+        *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);
+    } else {
+        dst[0] = x[0];
+    }
+}
+
+// Inclusive prefix sum over the 16 lanes of each DPP row.
+__device__ __forceinline__ float row_prefix16(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
+    return x;
+}
+
+// One chunk's operands in lane (c, g); t0 is the chunk's first token.  The
+// query-side set (q, k in the d_k visiting order, gates) and the update-side
+// set (k transposed, v) are both loaded a whole chunk ahead.
+template <int DK>
+struct IsoQK {
+    static constexpr int MT = DK / 16;
+    float q[4 * MT];                   // Q[t0 + c][4 MT g + e]
+    float k[4 * MT];                   // K[t0 + c][4 MT g + e]
+    float F, G;                        // gates of token t0 + c
+};
+
+template <int DK, int NC, bool COMPOSITE>
+struct IsoKV {
+    static constexpr int MT = DK / 16;
+    static constexpr int NT = NC / 16;
+    float kt[COMPOSITE ? 4 : 1][MT];   // K[t0 + 4g + kk][MT c + m] (composite pass; the
+                                       // main pass transposes its q-side k through LDS)
+    float v[4][NT];                    // V[t0 + 4g + kk][tile columns NT c + n]
+    float F, G;                        // gates of token t0 + c (composite pass)
+};
+
+template <int DK, int NC, bool COMPOSITE>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(DK <= 64 ? 2 : 1)))
+void k_iso(DiagParams p) {
     constexpr int C = kIsoChunk;
-    constexpr int W = DV / 16;                 // waves: one per 16 value columns
-    constexpr int NTH = W * kWave;
-    constexpr int QR = DK + 2;                 // q, k row stride: conflict-free Q K^T / Q mu reads,
-                                               // at most 2-way for the (w k)^T V reads
-    constexpr int VR = DV + 16;                // row stride of v
-    constexpr int KSTEPS = DK / 4;             // MFMA k-steps over d_k
     constexpr int MT = DK / 16;                // row tiles of mu
+    constexpr int NT = NC / 16;                // column tiles of mu
+    using QK = IsoQK<DK>;
+    using KV = IsoKV<DK, NC, COMPOSITE>;
+    constexpr int KR = DK + 4;                 // row stride of the LDS copy of k
+    __shared__ float4 kbuf4[COMPOSITE ? 1 : C * KR / 4];
+    float* const kbuf = reinterpret_cast<float*>(kbuf4);
 
-    struct Stage {
-        float qr[COMPOSITE ? 1 : C][QR];       // q row-major [t][j]
-        float kq[C][QR];                       // k row-major [s][j]
-        float vr[C][VR];                       // v row-major [s][i]
-        float4 sc[C];                          // b2_t, e^{b_t}, G_t, w_t
-        float decay;                           // e^{b_last}
-    };
-    __shared__ Stage stg[2];
-    __shared__ float st[COMPOSITE ? 1 : W][C][C];   // per-wave S^T [s][t]
-    __shared__ float mu_s[COMPOSITE ? 1 : W][COMPOSITE ? 1 : DK][16];   // mu slice of each wave
-    __shared__ float s_logsum;
-
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave;
-    const int w = tid / kWave;
-    const int g = lane / 16;
-    const int c = lane % 16;
-    const int64_t bh = blockIdx.x / p.S;
-    const int seg = static_cast<int>(blockIdx.x % p.S) ;
+    const int lane = threadIdx.x;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int ntile = static_cast<int>(p.dv / NC);
+    const int64_t id = xcd_local_id();         // a head-segment's column tiles share an XCD
+    const int tile = static_cast<int>(id % ntile);
+    const int64_t rest = id / ntile;
+    const int seg = static_cast<int>(rest % p.S);
+    const int64_t bh = rest / p.S;
     const int nseg_run = COMPOSITE ? p.S - 1 : p.S;
-    if (seg >= nseg_run) return;               // whole workgroup exits together
+    if (seg >= nseg_run) return;
 
     const int64_t c0 = static_cast<int64_t>(seg) * p.nchunks / p.S;
     const int64_t c1 = static_cast<int64_t>(seg + 1) * p.nchunks / p.S;
     const int64_t t_begin = c0 * C;
     const int64_t t_end = c1 * C < p.T ? c1 * C : p.T;
+    const int64_t DV = p.dv;
+    const int64_t cb = static_cast<int64_t>(tile) * NC;   // first column of the tile
 
     const float* qh = static_cast<const float*>(p.q) + bh * p.T * DK;
     const float* kh = static_cast<const float*>(p.k) + bh * p.T * DK;
@@ -73,213 +181,220 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_iso(DiagParams p) {
     const float* Fh = p.F + bh * p.T;
     const float* Gh = p.G + bh * p.T;
 
-    // ---- mu slice (rows all d_k, columns 16w..16w+15) in accumulator layout:
-    //      macc[m][r] = mu[16m + 4g + r][16w + c] ----
-    f32x4 macc[MT];
+    // macc[m][n][r] = mu[MT (4g + r) + m][cb + NT c + n]
+    f32x4 macc[MT][NT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float x = 0.0f;
-            if constexpr (!COMPOSITE) {
-                const int64_t off = static_cast<int64_t>(16 * m + 4 * g + r) * DV + 16 * w + c;
-                if (p.S == 1) {
-                    if (p.mu0) x = p.mu0[bh * DK * DV + off];
-                } else {
-                    x = p.comp[((bh * p.S + seg) * 2 + 1) * DK * DV + off];
-                }
-            }
-            macc[m][r] = x;
-        }
-    }
-    auto store_mu_slice = [&]() {
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) mu_s[w][16 * m + 4 * g + r][c] = macc[m][r];
-    };
-    if constexpr (!COMPOSITE) store_mu_slice();
-
-    // ---- staging ----
-    constexpr int QV = C * DK / 4;             // float4 vectors of q (and k) per chunk
-    constexpr int VV = C * DV / 4;
-    constexpr int NQ = (QV + NTH - 1) / NTH;
-    constexpr int NV = (VV + NTH - 1) / NTH;
-    float4 rq[NQ], rk[NQ], rv[NV];
-    float rF = 1.0f, rG = 0.0f;
-    float logsum = 0.0f;   // wave 0 lanes < 16: sum of log2 F over the segment
-
-    auto fetch = [&](int64_t t0, int L) {
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int e = tid + n * NTH;
-            rk[n] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            rq[n] = rk[n];
-            if (e < QV && e * 4 < L * DK) {
-                rk[n] = *reinterpret_cast<const float4*>(kh + t0 * DK + 4 * e);
-                if constexpr (!COMPOSITE) rq[n] = *reinterpret_cast<const float4*>(qh + t0 * DK + 4 * e);
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            const int e = tid + n * NTH;
-            rv[n] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-            if (e < VV && e * 4 < L * DV) rv[n] = *reinterpret_cast<const float4*>(vh + t0 * DV + 4 * e);
-        }
-        if (tid < C) {
-            rF = tid < L ? Fh[t0 + tid] : 1.0f;
-            rG = tid < L ? Gh[t0 + tid] : 0.0f;
-        }
-    };
-
-    auto commit = [&](int nb) {
-        Stage& S = stg[nb];
-#pragma unroll
-        for (int n = 0; n < NQ; ++n) {
-            const int e = tid + n * NTH;
-            if (e < QV) {
-                const int t = 4 * e / DK;
-                const int j = 4 * e % DK;
-                *reinterpret_cast<float2*>(&S.kq[t][j]) = make_float2(rk[n].x, rk[n].y);
-                *reinterpret_cast<float2*>(&S.kq[t][j + 2]) = make_float2(rk[n].z, rk[n].w);
-                if constexpr (!COMPOSITE) {
-                    *reinterpret_cast<float2*>(&S.qr[t][j]) = make_float2(rq[n].x, rq[n].y);
-                    *reinterpret_cast<float2*>(&S.qr[t][j + 2]) = make_float2(rq[n].z, rq[n].w);
-                }
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NV; ++n) {
-            const int e = tid + n * NTH;
-            if (e < VV) *reinterpret_cast<float4*>(&S.vr[4 * e / DV][4 * e % DV]) = rv[n];
-        }
-        if (tid < C) {
-            const float l2 = __log2f(rF);           // <= 0 (F in (0, 1])
-            float b2 = l2;
-#pragma unroll
-            for (int o = 1; o < C; o <<= 1) {
-                const float u = __shfl_up(b2, o, C);
-                if (tid >= o) b2 += u;
-            }
-            const float blast = __shfl(b2, C - 1, C);
-            S.sc[tid] = make_float4(b2, exp2f(b2), rG, rG * exp2f(blast - b2));
-            if (tid == 0) S.decay = exp2f(blast);
-            logsum += blast;
-        }
-    };
-
-    const int64_t nch = (t_end - t_begin + C - 1) / C;
-    auto chunk_len = [&](int64_t cc) -> int {
-        const int64_t rem = t_end - (t_begin + cc * C);
-        return static_cast<int>(rem < C ? rem : C);
-    };
-
-    if (nch > 0) {
-        fetch(t_begin, chunk_len(0));
-        commit(0);
-    }
-    __syncthreads();
-    if (nch > 1) fetch(t_begin + C, chunk_len(1));
-
-    for (int64_t ch = 0; ch < nch; ++ch) {
-        const int b = static_cast<int>(ch & 1);
-        const int L = chunk_len(ch);
-        const int64_t t0 = t_begin + ch * C;
-        const Stage& S = stg[b];
-
-        if constexpr (!COMPOSITE) {
-            // S = Q K^T, computed by every wave (no cross-wave exchange):
-            // sacc[r] = S[t = 4g + r][s = c].  The q A-operands are kept for Q mu.
-            float qa[KSTEPS];
-            f32x4 sp[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) sp[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk) {   // four independent accumulation chains
-                qa[kk] = S.qr[c][4 * kk + g];
-                sp[kk & 3] = mfma4(qa[kk], S.kq[c][4 * kk + g], sp[kk & 3]);
-            }
-            const f32x4 sacc = (sp[0] + sp[1]) + (sp[2] + sp[3]);
-            // A operand of (S (.) D) V wants A[t = c][s = 4kk + g]: transpose
-            // the 16 x 16 tile through this wave's LDS scratch.
-            *reinterpret_cast<float4*>(&st[w][c][4 * g]) = make_float4(sacc[0], sacc[1], sacc[2], sacc[3]);
-            const float4 sct = S.sc[c];
-            float av[4];
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int s_ = 4 * kk + g;
-                const float4 scs = S.sc[s_];
-                const float sv = st[w][s_][c];
-                av[kk] = s_ <= c ? sv * exp2f(sct.x - scs.x) * scs.z : 0.0f;
-            }
-            f32x4 op[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) op[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int kk = 0; kk < KSTEPS; ++kk)
-                op[kk & 3] = mfma4(qa[kk] * sct.y, mu_s[w][4 * kk + g][c], op[kk & 3]);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) op[kk] = mfma4(av[kk], S.vr[4 * kk + g][16 * w + c], op[kk]);
-            const f32x4 oacc = (op[0] + op[1]) + (op[2] + op[3]);
+        for (int n = 0; n < NT; ++n)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int t = 4 * g + r;
-                if (t < L) p.o[(bh * p.T + t0 + t) * DV + 16 * w + c] = oacc[r];
+                float x = 0.0f;
+                if constexpr (!COMPOSITE) {
+                    const int64_t off = static_cast<int64_t>(MT * (4 * g + r) + m) * DV + cb + NT * c + n;
+                    if (p.S == 1) {
+                        if (p.mu0) x = p.mu0[bh * DK * DV + off];
+                    } else {
+                        x = p.comp[((bh * p.S + seg) * 2 + 1) * DK * DV + off];
+                    }
+                }
+                macc[m][n][r] = x;
+            }
+
+    // Operand loads of the chunk at token t0 through buffer resources that
+    // end at the chunk's last token (rows past it read as 0; F as 1).
+    auto chunk_rows = [&](int64_t t0) -> int64_t {
+        const int64_t L = t_end - t0;
+        return L < 0 ? 0 : (L < C ? L : C);
+    };
+    auto load_qk = [&](int64_t t0, QK& x) __attribute__((always_inline)) {
+        const int64_t L = chunk_rows(t0);
+        const uint32_t off = static_cast<uint32_t>((c * DK + 4 * MT * g) * 4);
+        buf_load<4 * MT>(buf_rsrc(qh + t0 * DK, L * DK * 4), off, x.q);
+        buf_load<4 * MT>(buf_rsrc(kh + t0 * DK, L * DK * 4), off, x.k);
+        float f[1], gg[1];
+        buf_load<1>(buf_rsrc(Fh + t0, L * 4), static_cast<uint32_t>(c * 4), f);
+        buf_load<1>(buf_rsrc(Gh + t0, L * 4), static_cast<uint32_t>(c * 4), gg);
+        x.F = f[0];   // 0 past the chunk's end; compute() substitutes 1 there
+        x.G = gg[0];
+    };
+    auto load_kv = [&](int64_t t0, KV& x) __attribute__((always_inline)) {
+        const int64_t L = chunk_rows(t0);
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kh + t0 * DK, L * DK * 4);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vh + t0 * DV, L * DV * 4);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int s_ = 4 * g + kk;
+            if constexpr (COMPOSITE) buf_load<MT>(rk, static_cast<uint32_t>((s_ * DK + MT * c) * 4), x.kt[kk]);
+            buf_load<NT>(rv, static_cast<uint32_t>((s_ * DV + cb + NT * c) * 4), x.v[kk]);
+        }
+        if constexpr (COMPOSITE) {
+            float f[1], gg[1];
+            buf_load<1>(buf_rsrc(Fh + t0, L * 4), static_cast<uint32_t>(c * 4), f);
+            buf_load<1>(buf_rsrc(Gh + t0, L * 4), static_cast<uint32_t>(c * 4), gg);
+            x.F = f[0];
+            x.G = gg[0];
+        }
+    };
+
+    float logsum = 0.0f;   // sum of log2 F over the segment
+    // One chunk: qk is the query-side set (unused by the composite pass), kv
+    // the update-side set; F and G come from kv in the composite pass.
+    auto compute = [&](int64_t t0, QK& qk, const KV& kv) __attribute__((always_inline)) {
+        // F past the chunk's end is 1 (no decay); the loads gave 0 there
+        const float Fc = t0 + c < t_end ? (COMPOSITE ? kv.F : qk.F) : 1.0f;
+        const float Gc = COMPOSITE ? kv.G : qk.G;
+        const float b = row_prefix16(__log2f(Fc));         // b_t of token t0 + c (<= 0)
+        const float blast = bcast<15>(b);
+        const float wt = Gc * exp2f(blast - b);            // w of token t0 + c
+        // b, G and w of token s = 4g + kk, from lane s of this row
+        float bs[4], gs[4], ws[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int src = 16 * g + 4 * g + kk;
+            bs[kk] = __shfl(b, src);
+            gs[kk] = __shfl(Gc, src);
+            ws[kk] = __shfl(wt, src);
+        }
+        if constexpr (!COMPOSITE) {
+            // k of token t0 + c to LDS: the update reads it transposed.  One
+            // wave owns kbuf and its LDS operations complete in order.
+#pragma unroll
+            for (int e = 0; e < 4 * MT; e += 4)
+                *reinterpret_cast<float4*>(&kbuf[c * KR + 4 * MT * g + e]) =
+                    make_float4(qk.k[e], qk.k[e + 1], qk.k[e + 2], qk.k[e + 3]);
+            // S^T = K Q^T: register r = S[t = c][s = 4g + r]
+            f32x4 sp[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) sp[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int e = 0; e < 4 * MT; ++e) sp[e & 1] = mfma4(qk.k[e], qk.q[e], sp[e & 1]);
+            const f32x4 sacc = sp[0] + sp[1];
+            // P[t = c][s = 4g + kk] = S e^{b_t - b_s} G_s [s <= t]
+            float pa[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                pa[kk] = 4 * g + kk <= c ? sacc[kk] * exp2f(b - bs[kk]) * gs[kk] : 0.0f;
+            // O = diag(e^b) Q mu_start + P V
+            const float eb = exp2f(b);
+#pragma unroll
+            for (int e = 0; e < 4 * MT; ++e) qk.q[e] *= eb;
+            f32x4 oacc[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) oacc[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) oacc[n] = mfma4(qk.q[MT * r + m], macc[m][n][r], oacc[n]);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) oacc[n] = mfma4(pa[kk], kv.v[kk][n], oacc[n]);
+            const __amdgpu_buffer_rsrc_t ro = buf_rsrc(p.o + (bh * p.T + t0) * DV, chunk_rows(t0) * DV * 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float row[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) row[n] = oacc[n][r];
+                buf_store<NT>(ro, static_cast<uint32_t>(((4 * g + r) * DV + cb + NT * c) * 4), row);
             }
         }
-
-        // state update: mu = e^{b_last} mu + (w (.) K)^T V
-        {
-            const float decay = S.decay;
-            float bv[4], wk[4];
+        // mu = e^{b_last} mu + (w (.) K)^T V
+        const float decay = exp2f(blast);
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float aw[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
-                bv[kk] = S.vr[4 * kk + g][16 * w + c];
-                wk[kk] = S.sc[4 * kk + g].w;
+                float ktm;
+                if constexpr (COMPOSITE) ktm = kv.kt[kk][m];
+                else ktm = kbuf[(4 * g + kk) * KR + MT * c + m];
+                aw[kk] = ws[kk] * ktm;
             }
 #pragma unroll
-            for (int m = 0; m < MT; ++m) {
-                macc[m] *= decay;
+            for (int n = 0; n < NT; ++n) {
+                macc[m][n] *= decay;
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    macc[m] = mfma4(S.kq[4 * kk + g][16 * m + c] * wk[kk], bv[kk], macc[m]);
+                for (int kk = 0; kk < 4; ++kk) macc[m][n] = mfma4(aw[kk], kv.v[kk][n], macc[m][n]);
             }
-            if constexpr (!COMPOSITE) store_mu_slice();
         }
+        logsum += blast;
+    };
 
-        if (ch + 1 < nch) commit(b ^ 1);
-        __syncthreads();
-        if (ch + 2 < nch) fetch(t0 + 2 * C, chunk_len(ch + 2));
+    // The loads are unconditional (a chunk past the segment's end reads as
+    // zeros without touching memory), so the compiler's wait counts stay
+    // exact and never wait on the chunk being prefetched.
+    const int64_t nch = (t_end - t_begin + C - 1) / C;
+    if constexpr (COMPOSITE) {
+        // two update-side sets: the next chunk's loads are in flight while one computes
+        QK none;
+        KV xa, xb;
+        load_kv(t_begin, xa);
+        for (int64_t ch = 0; ch < nch; ch += 2) {
+            const int64_t t0 = t_begin + ch * C;
+            load_kv(t0 + C, xb);
+            compute(t0, none, xa);
+            if (ch + 1 >= nch) break;
+            load_kv(t0 + 2 * C, xa);
+            compute(t0 + C, none, xb);
+        }
+    } else {
+        // two sets of everything: each chunk's operands load a whole chunk ahead
+        QK qa, qb;
+        KV ka, kb;
+        load_qk(t_begin, qa);
+        load_kv(t_begin, ka);
+        for (int64_t ch = 0; ch < nch; ch += 2) {
+            const int64_t t0 = t_begin + ch * C;
+            load_qk(t0 + C, qb);
+            load_kv(t0 + C, kb);
+            compute(t0, qa, ka);
+            if (ch + 1 >= nch) break;
+            load_qk(t0 + 2 * C, qa);
+            load_kv(t0 + 2 * C, ka);
+            compute(t0 + C, qb, kb);
+        }
     }
 
-    if (tid == 0) s_logsum = logsum;
-    __syncthreads();
     if constexpr (COMPOSITE) {
         float* slot = p.comp + ((bh * p.S + seg) * 2 + 1) * DK * DV;
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                slot[static_cast<int64_t>(16 * m + 4 * g + r) * DV + 16 * w + c] = macc[m][r];
-        if (tid == 0) p.gdec[bh * p.S + seg] = exp2f(s_logsum);
+            for (int r = 0; r < 4; ++r) {
+                float row[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) row[n] = macc[m][n][r];
+                store_run<NT>(slot + static_cast<int64_t>(MT * (4 * g + r) + m) * DV + cb + NT * c, row);
+            }
+        if (lane == 0 && tile == 0) p.gdec[bh * p.S + seg] = exp2f(logsum);
     } else if (seg == p.S - 1 && p.mu_T) {
 #pragma unroll
         for (int m = 0; m < MT; ++m)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                p.mu_T[(bh * DK + 16 * m + 4 * g + r) * DV + 16 * w + c] = macc[m][r];
+            for (int r = 0; r < 4; ++r) {
+                float row[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) row[n] = macc[m][n][r];
+                store_run<NT>(p.mu_T + (bh * DK + MT * (4 * g + r) + m) * DV + cb + NT * c, row);
+            }
     }
 }
 
 int iso_chunk() { return kIsoChunk; }
 
+// Column tiles of one head: min(d_v, kIsoCols) columns each.
+int iso_tiles(int64_t dv) { return dv > kIsoCols ? static_cast<int>(dv / kIsoCols) : 1; }
+
 template <int DK, bool COMPOSITE>
 static int iso_launch_dv(const DiagParams& p, int64_t dv, int64_t grid, hipStream_t st) {
     switch (dv) {
-        case 16: hipLaunchKernelGGL((k_iso<DK, 16, COMPOSITE>), dim3(grid), dim3(64), 0, st, p); break;
-        case 32: hipLaunchKernelGGL((k_iso<DK, 32, COMPOSITE>), dim3(grid), dim3(128), 0, st, p); break;
-        case 64: hipLaunchKernelGGL((k_iso<DK, 64, COMPOSITE>), dim3(grid), dim3(256), 0, st, p); break;
-        case 128: hipLaunchKernelGGL((k_iso<DK, 128, COMPOSITE>), dim3(grid), dim3(512), 0, st, p); break;
+        case 16: hipLaunchKernelGGL((k_iso<DK, 16, COMPOSITE>), dim3(grid), dim3(kWave), 0, st, p); break;
+        case 32: hipLaunchKernelGGL((k_iso<DK, 32, COMPOSITE>), dim3(grid), dim3(kWave), 0, st, p); break;
+        case 64:
+        case 128: hipLaunchKernelGGL((k_iso<DK, kIsoCols, COMPOSITE>), dim3(grid), dim3(kWave), 0, st, p); break;
         default: return KDN_EUNSUPPORTED;
     }
     return launch_status();
@@ -297,11 +412,12 @@ static int iso_launch(const DiagParams& p, int64_t dk, int64_t dv, int64_t grid,
 }
 
 // Enqueue the gated mean scan; F, G were written by the Mobius pass.
+// One wave per (head, segment, column tile).
 int iso_mean_launch(const DiagParams& p, int64_t B, int64_t dk, hipStream_t st) {
     const int64_t BH = B * p.H;
     if (BH == 0) return KDN_OK;
     if (p.T == 0) return copy_state_launch(p, B, dk, true, st);   // mu_T = mu0
-    const int64_t grid = BH * p.S;
+    const int64_t grid = BH * p.S * iso_tiles(p.dv);
     int rc;
     if (p.S > 1) {
         if ((rc = iso_launch<true>(p, dk, p.dv, grid, st)) != KDN_OK) return rc;

@@ -138,6 +138,7 @@ int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipS
 int mob_block();
 int mobius_launch(const MobParams& p, int64_t BH, hipStream_t st);
 int iso_chunk();
+int iso_tiles(int64_t dv);
 int iso_mean_launch(const DiagParams& p, int64_t B, int64_t dk, hipStream_t st);
 
 }  // namespace kdn

@@ -59,9 +59,9 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
     return pl;
 }
 
-// Segments of the isotropic mean scan: about three workgroups per CU, at
-// least four 16-token chunks per segment.
-Plan plan_iso(int64_t BH, int64_t T) {
+// Segments of the isotropic mean scan: about two one-wave workgroups per
+// SIMD, at least four 16-token chunks per segment.
+Plan plan_iso(int64_t BH, int64_t T, int64_t dv) {
     Plan pl;
     pl.chunk = iso_chunk();
     pl.nchunks = static_cast<int32_t>((T + pl.chunk - 1) / pl.chunk);
@@ -70,7 +70,8 @@ Plan plan_iso(int64_t BH, int64_t T) {
     if (ov > 0) {
         S = ov;
     } else if (BH > 0) {
-        S = (3 * kNumCU + BH - 1) / BH;
+        const int64_t units = BH * iso_tiles(dv);
+        S = (8 * kNumCU + units - 1) / units;
         if (S > pl.nchunks / 4) S = pl.nchunks / 4;
     }
     if (S > kMaxSegments) S = kMaxSegments;
@@ -408,8 +409,8 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
     Plan pl{};
     size_t b_gate = 0;
     if (mean) {
-        pl = plan_iso(BH, T);
-        if (BH * pl.S > kMaxGrid) return KDN_EINVAL;
+        pl = plan_iso(BH, T, d_v);
+        if (BH * pl.S * iso_tiles(d_v) > kMaxGrid) return KDN_EINVAL;
         b_gate = align_up(sizeof(float) * static_cast<size_t>(BH) * T, 256);
         need += 2 * b_gate + scan_workspace_bytes(BH, d_k, d_v, pl);
     }

@@ -220,6 +220,28 @@ def test_iso_small(kdn, shape, S):
         gu.check_state(mu_T[b, h], r["mu_T"], f"iso mu_T[{b},{h}]")
 
 
+@pytest.mark.parametrize("S", [1, 2])
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_iso_head_sizes(kdn, dk, dv, S):
+    """Every (d_k, d_v) pairing of the one-wave kernel: row and column tile
+    interleaves, 1-4 column tiles per head, ragged last chunk (T = 45)."""
+    kdn.kdn_set_diag_segments(S)
+    spec = synth.IsoSpec("iso_sizes", 1, 2, 45, dk, dv, dk * 1000 + dv)
+    inp = synth.iso_inputs(spec)
+    x = gu.upload_iso(inp)
+    print(f"iso head sizes dk={dk} dv={dv} S={S}", flush=True)
+    _, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
+                                               x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    ref = oracle.iso_scan(inp)
+    o, mu_T = o.cpu().numpy(), mu_T.cpu().numpy()
+    for b, h in _all_heads(1, 2):
+        r = ref[(b, h)]
+        gu.check_o(o[b, h], r, f"iso o[{b},{h}] dk={dk} dv={dv}")
+        gu.check_state(mu_T[b, h], r["mu_T"], f"iso mu_T[{b},{h}] dk={dk} dv={dv}")
+
+
 @pytest.mark.parametrize("T", [1, 15, 4096, 4097, 3 * 4096 + 5])
 def test_iso_precision_only(kdn, T):
     spec = synth.IsoSpec("iso_prec", 2, 2, T, 64, 64, 37)
