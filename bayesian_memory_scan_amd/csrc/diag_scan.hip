@@ -95,7 +95,6 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         float k2[C][DK];
         float q[C][DK];
         float2 bv[C][CI];   // (beta_i, v_i)
-        float4 sc[C];       // per token: rho, dP, s, -
     };
     __shared__ Stage stg[2];
     __shared__ float opart[2][C][P][CI];
@@ -176,9 +175,13 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 
     // ---- chunk staging: global -> registers -> LDS (fp32) ----
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
-    float4 rsc = make_float4(1.0f, 0.0f, 1.0f, 0.0f);
     float s_prev = 1.0f;   // scale of the last token of the previous chunk (uniform)
     const float4* sch = p.scal + bh * p.T;
+    // The per-token frame scalars (rho, dP, s, -) are read through the scalar
+    // cache: their addresses are uniform, so they land in SGPRs and feed the
+    // VALU as scalar operands with no LDS staging and no readfirstlane.
+    typedef __attribute__((address_space(4))) const float scalar_f32;
+    auto frame_scalars = [&](int64_t t0) { return (scalar_f32*)(uintptr_t)(sch + t0); };
 
     auto fetch = [&](int64_t t0, int L) {
 #pragma unroll
@@ -200,7 +203,6 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                 rv[n] = ld16(vh + off);
             }
         }
-        if (tid < L) rsc = sch[t0 + tid];
     };
 
     auto commit = [&](int nb, int L) {
@@ -236,7 +238,6 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                 for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fv[e]);
             }
         }
-        if (tid < L) S.sc[tid] = rsc;
     };
 
     const int64_t nch = (t_end - t_begin + C - 1) / C;
@@ -259,23 +260,14 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         const Stage& S = stg[b];
         const float inv_sp = 1.0f / s_prev;   // a chunk's first token restarts the frame
 
-        // Software-pipelined over tokens: the next token's LDS operands are
-        // loaded while the current one computes.
-        float4 sc = S.sc[0];
-        float2 bvv = S.bv[0][col];
-        float vk = S.k[0][jl], vk2 = S.k2[0][jl];
-        float vq = 0.0f;
-        vq = S.q[0][jl];
-        for (int tt = 0; tt < L; ++tt) {
-            const int tn = tt + 1 < L ? tt + 1 : tt;
-            const float4 sc_n = S.sc[tn];
-            const float2 bvv_n = S.bv[tn][col];
-            const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl];
-            float vq_n = 0.0f;
-            vq_n = S.q[tn][jl];
-
-            const float rho_t = sc.x * (tt == 0 ? inv_sp : 1.0f);
-            const uint32_t rho_bits = __builtin_amdgcn_readfirstlane(__float_as_uint(rho_t));
+        scalar_f32* const cs = frame_scalars(t0);
+        // One token: frame change, state update, read-out partial.  bvv, vk,
+        // vk2, vq are the token's operands from the stage.
+        auto token = [&](int tt, const float2 bvv, const float vk, const float vk2,
+                         const float vq) __attribute__((always_inline)) {
+            const float s_t = cs[4 * tt + 2];
+            const uint32_t rho_bits = tt == 0 ? __builtin_amdgcn_readfirstlane(__float_as_uint(cs[0] * inv_sp))
+                                              : __float_as_uint(cs[4 * tt]);
             if (rho_bits != 0x3f800000u) {
                 const float rho = __uint_as_float(rho_bits);
 #pragma unroll
@@ -284,13 +276,13 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                     eta[r] *= rho;
                 }
             }
-            const float bs = bvv.x * sc.z;           // beta_i s_t
+            const float bs = bvv.x * s_t;            // beta_i s_t
             const float bvs = bs * bvv.y;            // beta_i v_i s_t
             Unroll<0, JP>::run([&](auto rr) {
                 constexpr int r = decltype(rr)::value;
                 fmac_bcast<r>(I[r], vk2, bs);
             });
-            const float dP = uniform(sc.y);
+            const float dP = cs[4 * tt + 1];
 #pragma unroll
             for (int r = 0; r < JP; ++r) I[r] += dP;
             Unroll<0, JP>::run([&](auto rr) {
@@ -311,14 +303,33 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
                 fmac_bcast<r>(acc[r & 3], vq, m[r]);
             });
             opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            sc = sc_n;
-            bvv = bvv_n;
-            vk = vk_n;
-            vk2 = vk2_n;
-            vq = vq_n;
+        };
+
+        if (L == C) {
+            // a whole chunk: unrolled, so every stage offset is a constant and
+            // the compiler schedules the operand reads ahead by itself
+            Unroll<0, C>::run([&](auto u) {
+                constexpr int tt = decltype(u)::value;
+                token(tt, S.bv[tt][col], S.k[tt][jl], S.k2[tt][jl], S.q[tt][jl]);
+            });
+        } else {
+            // the ragged last chunk, software-pipelined over tokens: the next
+            // token's LDS operands are loaded while the current one computes
+            float2 bvv = S.bv[0][col];
+            float vk = S.k[0][jl], vk2 = S.k2[0][jl], vq = S.q[0][jl];
+            for (int tt = 0; tt < L; ++tt) {
+                const int tn = tt + 1 < L ? tt + 1 : tt;
+                const float2 bvv_n = S.bv[tn][col];
+                const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl], vq_n = S.q[tn][jl];
+                token(tt, bvv, vk, vk2, vq);
+                bvv = bvv_n;
+                vk = vk_n;
+                vk2 = vk2_n;
+                vq = vq_n;
+            }
         }
 
-        s_prev = S.sc[L - 1].z;
+        s_prev = cs[4 * (L - 1) + 2];
         if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
         __syncthreads();
         for (int e = tid; e < L * CI; e += NTH) {
