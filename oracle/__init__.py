@@ -325,8 +325,9 @@ def iso_head(a, p, Lam, lambda0, q=None, k=None, v=None, mu0=None, lib=None):
     return {"lambda": lam, "o": o, "s": s, "mu_T": mu_T}
 
 
-def iso_scan(inp: dict, heads=None, threads=None, with_mean=True, lib=None):
-    """Run the isotropic filter over heads of a synthetic-input dict (float32 arrays)."""
+def iso_scan(inp: dict, heads=None, threads=None, with_mean=True, mu0=None, lib=None):
+    """Run the isotropic filter over heads of a synthetic-input dict (float32
+    arrays); mu0 [B,H,d_k,d_v] is an optional starting mean (default 0)."""
     B, H = inp["a"].shape[:2]
     heads = list(heads) if heads is not None else [(b, h) for b in range(B) for h in range(H)]
     lib = lib or load()
@@ -335,8 +336,9 @@ def iso_scan(inp: dict, heads=None, threads=None, with_mean=True, lib=None):
         b, h = bh
         f = lambda n: np.asarray(inp[n][b, h], np.float32).astype(np.float64)
         mean = (f("q"), f("k"), f("v")) if with_mean else (None, None, None)
+        m0 = None if mu0 is None else np.asarray(mu0[b, h], np.float64)
         return bh, iso_head(f("a"), f("p"), f("Lambda"), float(inp["lambda0"][b, h]),
-                            *mean, lib=lib)
+                            *mean, mu0=m0, lib=lib)
 
     with ThreadPoolExecutor(_threads(threads)) as ex:
         return dict(ex.map(one, heads))

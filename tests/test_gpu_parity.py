@@ -242,6 +242,79 @@ def test_iso_head_sizes(kdn, dk, dv, S):
         gu.check_state(mu_T[b, h], r["mu_T"], f"iso mu_T[{b},{h}] dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("S", [1, 4])
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 33, 64])
+def test_iso_short_sequences(kdn, T, S):
+    """Chunks of one token, a single ragged chunk, exact chunk multiples, and
+    more segments requested than there are chunks (the plan clamps)."""
+    kdn.kdn_set_diag_segments(S)
+    spec = synth.IsoSpec("iso_short", 2, 2, T, 64, 64, 4000 + T)
+    inp = synth.iso_inputs(spec)
+    x = gu.upload_iso(inp)
+    print(f"iso short T={T} S={S}", flush=True)
+    _, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
+                                               x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    ref = oracle.iso_scan(inp)
+    o, mu_T = o.cpu().numpy(), mu_T.cpu().numpy()
+    for b, h in _all_heads(2, 2):
+        r = ref[(b, h)]
+        gu.check_o(o[b, h], r, f"iso o[{b},{h}] T={T} S={S}")
+        gu.check_state(mu_T[b, h], r["mu_T"], f"iso mu_T[{b},{h}] T={T} S={S}")
+
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_iso_initial_state(kdn, S):
+    """A nonzero starting mean (mu0) and precision (lambda0), both segmentings:
+    the starting mean reaches the first segment through the carry pass."""
+    kdn.kdn_set_diag_segments(S)
+    B, H, T, dk, dv = 2, 2, 300, 64, 128
+    spec = synth.IsoSpec("iso_state", B, H, T, dk, dv, 51)
+    inp = synth.iso_inputs(spec)
+    g = np.random.default_rng(52)
+    inp["lambda0"] = (0.2 + 3.0 * g.random((B, H))).astype(np.float32)
+    mu0 = g.standard_normal((B, H, dk, dv)).astype(np.float32)
+    x = gu.upload_iso(inp)
+    print(f"iso initial state S={S}", flush=True)
+    _, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
+                                               x["q"], x["k"], x["v"], mu0=gu.dev_tensor(mu0))
+    torch.cuda.synchronize()
+    ref = oracle.iso_scan(inp, mu0=mu0)
+    o, mu_T = o.cpu().numpy(), mu_T.cpu().numpy()
+    for b, h in _all_heads(B, H):
+        r = ref[(b, h)]
+        gu.check_o(o[b, h], r, f"iso o[{b},{h}] S={S}")
+        gu.check_state(mu_T[b, h], r["mu_T"], f"iso mu_T[{b},{h}] S={S}")
+
+
+def test_iso_chaining(kdn):
+    """scan(T1) then scan(T2) started from its last precision and final mean
+    equals one scan over T1 + T2."""
+    B, H, T, cut, dk, dv = 1, 2, 200, 77, 32, 64
+    spec = synth.IsoSpec("iso_chain", B, H, T, dk, dv, 61)
+    inp = synth.iso_inputs(spec)
+    ref = oracle.iso_scan(inp)
+    part = lambda a, b: {n: (np.ascontiguousarray(v[:, :, a:b])
+                             if isinstance(v, np.ndarray) and v.ndim >= 3 else v)
+                         for n, v in inp.items()}
+    x1 = gu.upload_iso(part(0, cut))
+    lam1, o1, mu1 = kdn.kdn_mobius_precision_scan(x1["a"], x1["p"], x1["Lambda"], x1["lambda0"],
+                                                  x1["q"], x1["k"], x1["v"])
+    x2 = gu.upload_iso(part(cut, T))
+    lam2, o2, mu2 = kdn.kdn_mobius_precision_scan(x2["a"], x2["p"], x2["Lambda"],
+                                                  lam1[:, :, -1].contiguous(), x2["q"], x2["k"],
+                                                  x2["v"], mu0=mu1)
+    torch.cuda.synchronize()
+    lam = torch.cat([lam1, lam2], dim=2).cpu().numpy()
+    o = torch.cat([o1, o2], dim=2).cpu().numpy()
+    mu2 = mu2.cpu().numpy()
+    for b, h in _all_heads(B, H):
+        r = ref[(b, h)]
+        gu.check_rel(lam[b, h], r["lambda"], f"chained lambda[{b},{h}]")
+        gu.check_o(o[b, h], r, f"chained iso o[{b},{h}]")
+        gu.check_state(mu2[b, h], r["mu_T"], f"chained iso mu_T[{b},{h}]")
+
+
 @pytest.mark.parametrize("T", [1, 15, 4096, 4097, 3 * 4096 + 5])
 def test_iso_precision_only(kdn, T):
     spec = synth.IsoSpec("iso_prec", 2, 2, T, 64, 64, 37)
