@@ -16,58 +16,88 @@
 // The precision 1/sig follows the Mobius map l -> ((1 + w p) l + w a^2) / (p l + a^2),
 // w = beta k^2.
 //
-// Work decomposition as in the diagonal scan: a workgroup owns one head and
-// one tile of value columns for the whole sequence; lane <-> value column i,
-// JP key rows per lane in VGPRs; tokens staged 16 at a time through LDS
-// (double-buffered, widened to fp32); key-side values reach the fmacs as DPP
-// row broadcasts.  The two sums over j per (token, column) are the only
-// coupling between entries: each row group's partial sums meet in a
-// double-buffered LDS slot behind one barrier per token.
+// Work decomposition: a workgroup owns one head and one tile of value
+// columns for the whole sequence.  Every wave holds all d_k rows of its
+// columns, so the two sums over j close inside the wave and need no barrier:
+//   * lane = rg * CPW + cw: RG = d_k/16 row groups of 16 rows, CPW = 64/RG
+//     columns per wave; each lane keeps 16 rows of one column in VGPRs;
+//   * the sums over a column's row groups run on permlane32/permlane16 swaps
+//     and one DPP rotate (lane bits log2(CPW)..5), two values at once;
+//   * tokens are staged 16 at a time through LDS (double-buffered, widened to
+//     fp32, k^2 precomputed); a lane reads its 16 rows of k, k^2 and q as
+//     broadcast ds_read_b128, so every fmac has plain VGPR operands;
+//   * the read-out sum lands in every lane of the column; the row group 0
+//     lanes write it to an LDS row that the workgroup stores once per chunk.
 #include "kdn_lane.h"
 #include "kdn_params.h"
 
 namespace kdn {
 
 constexpr int kNoiseChunk = 16;
+constexpr int kNoiseRows = 16;        // key rows per lane
+constexpr int kDppRowRor8 = 0x128;    // row_ror:8, lane l <-> l ^ 8 inside a row of 16
 
-template <int DK, int CI, int W, bool BF16>
+// Sum over the RG row groups of a column (lane bits above the column index).
+// Two values at once: on return every lane holds both totals.
+template <int RG>
+__device__ __forceinline__ void group_sum2(float& a, float& b) {
+    if constexpr (RG > 1) {
+        float x = swap32_add(a, b);                 // lanes 0-31: a, 32-63: b, over bit 5
+        if constexpr (RG >= 4) x = swap16_add(x, x);   // bit 4
+        if constexpr (RG >= 8) x += dpp<kDppRowRor8>(x);   // bit 3
+        const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+        a = __uint_as_float(r[0]);
+        b = __uint_as_float(r[1]);
+    }
+}
+
+template <int RG>
+__device__ __forceinline__ float group_sum1(float x) {
+    if constexpr (RG > 1) {
+        x = swap32_add(x, x);
+        if constexpr (RG >= 4) x = swap16_add(x, x);
+        if constexpr (RG >= 8) x += dpp<kDppRowRor8>(x);
+    }
+    return x;
+}
+
+template <int DK, int W, bool BF16>
 __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
     using E = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int C = kNoiseChunk;
+    constexpr int JP = kNoiseRows;
+    constexpr int RG = DK / JP;          // row groups of a column
+    constexpr int CPW = kWave / RG;      // columns per wave
+    constexpr int CI = W * CPW;          // columns per workgroup
     constexpr int NTH = W * kWave;
-    constexpr int P = NTH / CI;          // row groups per workgroup
-    constexpr int JP = DK / P;           // key rows per lane
     constexpr int VW = BF16 ? 8 : 4;
     constexpr int VK = C * DK / VW;
     constexpr int VB = C * CI / VW;
     constexpr int NVK = (VK + NTH - 1) / NTH;
     constexpr int NVB = (VB + NTH - 1) / NTH;
-    static_assert(NTH % CI == 0 && DK % P == 0, "tile shape");
-    static_assert(JP == 4 || JP == 8 || JP == 16, "key rows per lane: one DPP row");
-    static_assert(CI >= 16, "a DPP row must stay inside one row group");
+    static_assert(DK % JP == 0 && CPW * RG == kWave, "tile shape");
 
     struct Stage {
-        float k[C][DK];
-        float k2[C][DK];
-        float q[C][DK];
+        float4 k[C][DK / 4];
+        float4 k2[C][DK / 4];
+        float4 q[C][DK / 4];
         float2 bv[C][CI];   // (beta_i, v_i)
         float4 sc[C];       // (a^2, p, a, -)
     };
     __shared__ Stage stg[2];
-    __shared__ float opart[2][C][P][CI];
-    __shared__ float2 red[2][P][CI];   // per-token partial (sum k^2 sp, sum k mp) of each row group
+    __shared__ float orow[2][C][CI];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
-    const int col = tid % CI;
-    const int rg = tid / CI;
-    const int j0 = rg * JP;
-    const int jl = j0 + (lane & (JP - 1));
-    const int ntile = static_cast<int>(p.dv / CI);
+    const int w = tid / kWave;
+    const int rg = lane / CPW;
+    const int col = w * CPW + lane % CPW;     // column within the tile
+    const int ntile = static_cast<int>((p.dv + CI - 1) / CI);
     const int64_t wg = xcd_local_id();
     const int tile = static_cast<int>(wg % ntile);
     const int64_t bh = wg / ntile;
     const int i = tile * CI + col;
+    const bool live = i < p.dv;               // d_v smaller than a wave's columns
     const int64_t T = p.T;
 
     const E* qh = static_cast<const E*>(p.q) + bh * T * DK;
@@ -76,13 +106,15 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
     const E* bth = static_cast<const E*>(p.beta) + bh * T * p.dv + tile * CI;
     const float* ah = p.a + bh * T;
     const float* ph = p.p + bh * T;
+    const int ncol = p.dv - tile * CI < CI ? static_cast<int>(p.dv - tile * CI) : CI;
 
-    float sig[JP], mu[JP];   // variance 1/lambda and mean of each entry
+    // variance 1/lambda and frame-scaled mean of this lane's 16 rows of column i
+    float sig[JP], mt[JP];
 #pragma unroll
     for (int r = 0; r < JP; ++r) {
-        const int64_t off = (bh * DK + j0 + r) * p.dv + i;
-        sig[r] = p.lam0 ? 1.0f / p.lam0[off] : 1.0f;
-        mu[r] = p.mu0 ? p.mu0[off] : 0.0f;
+        const int64_t off = (bh * DK + rg * JP + r) * p.dv + i;
+        sig[r] = live && p.lam0 ? 1.0f / p.lam0[off] : 1.0f;
+        mt[r] = live && p.mu0 ? p.mu0[off] : 0.0f;
     }
 
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
@@ -102,7 +134,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
             const int vi = tid + n * NTH;
             const int row = vi / (CI / VW);
             const int cv = vi % (CI / VW);
-            if (vi < VB && row < L) {
+            if (vi < VB && row < L && cv * VW < ncol) {
                 const int64_t off = (t0 + row) * p.dv + cv * VW;
                 rb[n] = ld16(bth + off);
                 rv[n] = ld16(vh + off);
@@ -113,22 +145,23 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
 
     auto commit = [&](int nb, int L) {
         Stage& S = stg[nb];
+        float* const kf = reinterpret_cast<float*>(S.k);
+        float* const k2f = reinterpret_cast<float*>(S.k2);
+        float* const qf = reinterpret_cast<float*>(S.q);
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
             const int vi = tid + n * NTH;
             if (vi < VK && vi * VW < L * DK) {
-                const int row = vi * VW / DK;
-                const int c0 = vi * VW % DK;
                 float f[VW];
                 widen<BF16>(rk[n], f);
 #pragma unroll
                 for (int e = 0; e < VW; ++e) {
-                    S.k[row][c0 + e] = f[e];
-                    S.k2[row][c0 + e] = f[e] * f[e];
+                    kf[vi * VW + e] = f[e];
+                    k2f[vi * VW + e] = f[e] * f[e];
                 }
                 widen<BF16>(rq[n], f);
 #pragma unroll
-                for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
+                for (int e = 0; e < VW; ++e) qf[vi * VW + e] = f[e];
             }
         }
 #pragma unroll
@@ -136,7 +169,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
             const int vi = tid + n * NTH;
             const int row = vi / (CI / VW);
             const int c0 = (vi % (CI / VW)) * VW;
-            if (vi < VB && row < L) {
+            if (vi < VB && row < L && c0 < ncol) {
                 float fv[VW], fb[VW];
                 widen<BF16>(rv[n], fv);
                 widen<BF16>(rb[n], fb);
@@ -160,69 +193,66 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
     __syncthreads();
     if (nch > 1) fetch(C, chunk_len(1));
 
+    // The mean is carried in a decayed frame, mu = Am * mt with Am the product
+    // of a since the frame start, so the predict step costs one multiply per
+    // token instead of one per entry.  A frame restarts (mt *= Am, Am = 1)
+    // when Am falls below 2^-32; Am is the same in every lane.
+    float Am = 1.0f;
     for (int64_t c = 0; c < nch; ++c) {
         const int b = static_cast<int>(c & 1);
         const int L = chunk_len(c);
         const int64_t t0 = c * C;
         const Stage& S = stg[b];
 
-        float4 sc = S.sc[0];
-        float2 bvv = S.bv[0][col];
-        float vk = S.k[0][jl], vk2 = S.k2[0][jl], vq = S.q[0][jl];
-        for (int tt = 0; tt < L; ++tt) {
-            const int tn = tt + 1 < L ? tt + 1 : tt;
-            const float4 sc_n = S.sc[tn];
-            const float2 bvv_n = S.bv[tn][col];
-            const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl], vq_n = S.q[tn][jl];
-
-            // predict, and this row group's share of the two sums over j
-            float ps[2] = {0.0f, 0.0f}, pm[2] = {0.0f, 0.0f};
-            float sp[JP];
+        // One token, all in registers of this wave: predict, the two sums
+        // over j, the residual write, the projected variance, the read-out.
+        auto token = [&](int tt) __attribute__((always_inline)) {
+            const float4 sc = S.sc[tt];
+            const float2 bvv = S.bv[tt][col];
+            float kr[JP], k2r[JP], qr[JP];
+#pragma unroll
+            for (int u = 0; u < JP / 4; ++u) {
+                const float4 x = S.k[tt][rg * (JP / 4) + u];
+                const float4 y = S.k2[tt][rg * (JP / 4) + u];
+                const float4 z = S.q[tt][rg * (JP / 4) + u];
+                kr[4 * u] = x.x; kr[4 * u + 1] = x.y; kr[4 * u + 2] = x.z; kr[4 * u + 3] = x.w;
+                k2r[4 * u] = y.x; k2r[4 * u + 1] = y.y; k2r[4 * u + 2] = y.z; k2r[4 * u + 3] = y.w;
+                qr[4 * u] = z.x; qr[4 * u + 1] = z.y; qr[4 * u + 2] = z.z; qr[4 * u + 3] = z.w;
+            }
+            Am *= sc.z;
+            if (Am < 0x1p-32f) {
+#pragma unroll
+                for (int r = 0; r < JP; ++r) mt[r] *= Am;
+                Am = 1.0f;
+            }
+            float sp[JP], ps[2] = {0.0f, 0.0f}, pm[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int r = 0; r < JP; ++r) {
                 sp[r] = fmaf(sc.x, sig[r], sc.y);
-                mu[r] *= sc.z;
+                ps[r & 1] = fmaf(k2r[r], sp[r], ps[r & 1]);   // sum_j k_j^2 sp_j
+                pm[r & 1] = fmaf(kr[r], mt[r], pm[r & 1]);    // sum_j k_j mp_j / Am
             }
-            Unroll<0, JP>::run([&](auto rr) {
-                constexpr int r = decltype(rr)::value;
-                fmac_bcast<r>(ps[r & 1], vk2, sp[r]);   // sum_j k_j^2 sp_j
-                fmac_bcast<r>(pm[r & 1], vk, mu[r]);    // sum_j k_j mp_j
-            });
-            red[tt & 1][rg][col] = make_float2(ps[0] + ps[1], pm[0] + pm[1]);
-            __syncthreads();
-            float Ssum = fast_rcp(bvv.x), pred = 0.0f;
+            float Sp = ps[0] + ps[1], Pm = pm[0] + pm[1];
+            group_sum2<RG>(Sp, Pm);
+            // residual write with the Kalman gain (in the frame), and the
+            // projected variance
+            const float gain = (bvv.y - Am * Pm) * fast_rcp((Sp + fast_rcp(bvv.x)) * Am);
+            float acc[2] = {0.0f, 0.0f};
 #pragma unroll
-            for (int g = 0; g < P; ++g) {
-                const float2 x = red[tt & 1][g][col];
-                Ssum += x.x;
-                pred += x.y;
-            }
-            // residual write with the Kalman gain, and the projected variance
-            const float gain = (bvv.y - pred) * fast_rcp(Ssum);
-            Unroll<0, JP>::run([&](auto rr) {
-                constexpr int r = decltype(rr)::value;
-                fmac_bcast<r>(mu[r], vk, sp[r] * gain);
-                const float den = fmaf(bcast<r>(vk2) * bvv.x, sp[r], 1.0f);
+            for (int r = 0; r < JP; ++r) {
+                mt[r] = fmaf(kr[r], sp[r] * gain, mt[r]);
+                const float den = fmaf(k2r[r] * bvv.x, sp[r], 1.0f);
                 sig[r] = sp[r] * fast_rcp(den);
-            });
-            float m[JP];
-#pragma unroll
-            for (int r = 0; r < JP; ++r) m[r] = mu[r];
-            float acc[4];
-            Unroll<0, 4>::run([&](auto rr) {
-                constexpr int r = decltype(rr)::value;
-                acc[r] = bcast<r>(vq) * m[r];
-            });
-            Unroll<4, JP>::run([&](auto rr) {
-                constexpr int r = decltype(rr)::value;
-                fmac_bcast<r>(acc[r & 3], vq, m[r]);
-            });
-            opart[b][tt][rg][col] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            sc = sc_n;
-            bvv = bvv_n;
-            vk = vk_n;
-            vk2 = vk2_n;
-            vq = vq_n;
+                acc[r & 1] = fmaf(qr[r], mt[r], acc[r & 1]);
+            }
+            const float o_t = group_sum1<RG>(acc[0] + acc[1]);
+            if (rg == 0) orow[b][tt][col] = Am * o_t;
+        };
+
+        if (L == C) {
+            Unroll<0, C>::run([&](auto u) { token(decltype(u)::value); });
+        } else {
+            for (int tt = 0; tt < L; ++tt) token(tt);
         }
 
         if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
@@ -230,52 +260,56 @@ __global__ __launch_bounds__(W * kWave) void k_diag_noise(NoiseParams p) {
         for (int e = tid; e < L * CI; e += NTH) {
             const int tt = e / CI;
             const int cc = e % CI;
-            float sum = 0.0f;
-#pragma unroll
-            for (int g = 0; g < P; ++g) sum += opart[b][tt][g][cc];
-            p.o[(bh * T + t0 + tt) * p.dv + tile * CI + cc] = sum;
+            if (cc < ncol) p.o[(bh * T + t0 + tt) * p.dv + tile * CI + cc] = orow[b][tt][cc];
         }
         if (c + 2 < nch) fetch(t0 + 2 * C, chunk_len(c + 2));
     }
 
+    if (live) {
 #pragma unroll
-    for (int r = 0; r < JP; ++r) {
-        const int64_t off = (bh * DK + j0 + r) * p.dv + i;
-        if (p.lam_T) p.lam_T[off] = 1.0f / sig[r];
-        if (p.mu_T) p.mu_T[off] = mu[r];
+        for (int r = 0; r < JP; ++r) {
+            const int64_t off = (bh * DK + rg * JP + r) * p.dv + i;
+            if (p.lam_T) p.lam_T[off] = 1.0f / sig[r];
+            if (p.mu_T) p.mu_T[off] = Am * mt[r];
+        }
     }
 }
 
-constexpr int noise_waves(int DK, int CI) {
-    const int w = DK * CI / (kWave * 16);
-    return w < 1 ? 1 : w;
+// Waves per workgroup: 64 value columns per workgroup where d_v allows.
+constexpr int noise_waves(int DK, int64_t dv) {
+    const int cpw = kWave / (DK / kNoiseRows);
+    const int64_t cols = dv < 64 ? dv : 64;
+    const int64_t w = (cols + cpw - 1) / cpw;
+    return static_cast<int>(w < 1 ? 1 : w);
 }
 
-template <int DK, int CI, bool BF16>
-static void noise_one(const NoiseParams& p, int64_t grid, hipStream_t st) {
-    constexpr int W = noise_waves(DK, CI);
-    hipLaunchKernelGGL((k_diag_noise<DK, CI, W, BF16>), dim3(static_cast<uint32_t>(grid)),
-                       dim3(W * kWave), 0, st, p);
+template <int DK, int W, bool BF16>
+static void noise_one(const NoiseParams& p, int64_t BH, hipStream_t st) {
+    constexpr int CI = W * (kWave / (DK / kNoiseRows));
+    const int64_t grid = BH * ((p.dv + CI - 1) / CI);
+    hipLaunchKernelGGL((k_diag_noise<DK, W, BF16>), dim3(static_cast<uint32_t>(grid)), dim3(W * kWave), 0, st, p);
 }
 
+// W runs up to d_k / 16 (64 columns of d_k / 16 row groups each).
 template <int DK, bool BF16>
-static int noise_dk(const NoiseParams& p, int CI, int64_t grid, hipStream_t st) {
-    switch (CI) {
-        case 16: noise_one<DK, 16, BF16>(p, grid, st); break;
-        case 32: noise_one<DK, 32, BF16>(p, grid, st); break;
-        case 64: noise_one<DK, 64, BF16>(p, grid, st); break;
-        default: return KDN_EUNSUPPORTED;
-    }
+static int noise_dk(const NoiseParams& p, int64_t BH, hipStream_t st) {
+    constexpr int WMAX = DK / kNoiseRows;
+    const int w = noise_waves(DK, p.dv);
+    if (w == 1) noise_one<DK, 1, BF16>(p, BH, st);
+    else if (w == 2 && WMAX >= 2) noise_one<DK, (WMAX >= 2 ? 2 : 1), BF16>(p, BH, st);
+    else if (w == 4 && WMAX >= 4) noise_one<DK, (WMAX >= 4 ? 4 : 1), BF16>(p, BH, st);
+    else if (w == 8 && WMAX >= 8) noise_one<DK, (WMAX >= 8 ? 8 : 1), BF16>(p, BH, st);
+    else return KDN_EUNSUPPORTED;
     return KDN_OK;
 }
 
 template <bool BF16>
-static int noise_main(const NoiseParams& p, int64_t dk, int CI, int64_t grid, hipStream_t st) {
+static int noise_main(const NoiseParams& p, int64_t dk, int64_t BH, hipStream_t st) {
     switch (dk) {
-        case 16: return noise_dk<16, BF16>(p, CI, grid, st);
-        case 32: return noise_dk<32, BF16>(p, CI, grid, st);
-        case 64: return noise_dk<64, BF16>(p, CI, grid, st);
-        case 128: return noise_dk<128, BF16>(p, CI, grid, st);
+        case 16: return noise_dk<16, BF16>(p, BH, st);
+        case 32: return noise_dk<32, BF16>(p, BH, st);
+        case 64: return noise_dk<64, BF16>(p, BH, st);
+        case 128: return noise_dk<128, BF16>(p, BH, st);
         default: return KDN_EUNSUPPORTED;
     }
 }
@@ -296,9 +330,7 @@ int noise_launch(const NoiseParams& p, int64_t B, int64_t dk, bool bf16, hipStre
         hipLaunchKernelGGL(k_noise_copy, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st, p, n);
         return launch_status();
     }
-    const int CI = p.dv < 64 ? static_cast<int>(p.dv) : 64;
-    const int64_t grid = BH * (p.dv / CI);
-    const int rc = bf16 ? noise_main<true>(p, dk, CI, grid, st) : noise_main<false>(p, dk, CI, grid, st);
+    const int rc = bf16 ? noise_main<true>(p, dk, BH, st) : noise_main<false>(p, dk, BH, st);
     if (rc != KDN_OK) return rc;
     return launch_status();
 }
