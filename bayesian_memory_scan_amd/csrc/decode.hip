@@ -8,21 +8,25 @@
 //   mu' = (alpha I mu + beta[i] v[i] k[j]) / I'
 //   o[i] = sum_j q[j] mu'[j][i]
 // The step is a streaming read-modify-write of 2 x d_k x d_v floats per head:
-// HBM-bound.  One workgroup per head; each thread owns one float4 column group
-// and NF key rows, issues all its state loads before any arithmetic, and the
-// per-column partial read-outs are summed across row groups through LDS.
+// HBM-bound.  One workgroup (up to 512 threads) per head; each thread owns one
+// float4 column group and NF key rows, issues all its state loads before any
+// arithmetic, and the per-column partial read-outs are summed across row
+// groups through LDS.  State loads and stores are non-temporal: the state is
+// touched once per call, so it should not displace anything from the caches
+// (and a repeated call cannot be served from the last-level cache).
 #include "kdn_params.h"
 
 #include <type_traits>
 
 namespace kdn {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__((DK * DV / 4 < 256 ? DK * DV / 4 : 256))
+__global__ __launch_bounds__((DK * DV / 4 < 512 ? DK * DV / 4 : 512))
 void k_decode(DecodeParams p) {
     using E = typename std::conditional<BF16, uint16_t, float>::type;
-    constexpr int NTH = DK * DV / 4 < 256 ? DK * DV / 4 : 256;
+    constexpr int NTH = DK * DV / 4 < 512 ? DK * DV / 4 : 512;
     constexpr int CG = DV / 4;            // float4 column groups per row
     constexpr int RG = NTH / CG;          // row groups
     constexpr int NF = DK / RG;           // rows per thread
@@ -41,15 +45,15 @@ void k_decode(DecodeParams p) {
         else return static_cast<const float*>(base)[idx];
     };
 
-    float4* I4 = reinterpret_cast<float4*>(p.I + bh * DK * DV);
-    float4* M4 = reinterpret_cast<float4*>(p.mu + bh * DK * DV);
+    f32x4* I4 = reinterpret_cast<f32x4*>(p.I + bh * DK * DV);
+    f32x4* M4 = reinterpret_cast<f32x4*>(p.mu + bh * DK * DV);
 
-    float4 Iv[NF], Mv[NF];
+    f32x4 Iv[NF], Mv[NF];
 #pragma unroll
     for (int n = 0; n < NF; ++n) {
         const int j = r0 + n * RG;
-        Iv[n] = I4[j * CG + cg];
-        Mv[n] = M4[j * CG + cg];
+        Iv[n] = __builtin_nontemporal_load(&I4[j * CG + cg]);
+        Mv[n] = __builtin_nontemporal_load(&M4[j * CG + cg]);
     }
 
     const float alpha = fast_exp(-p.A[h] * load(p.d, bh));
@@ -70,18 +74,19 @@ void k_decode(DecodeParams p) {
         const float kj = load(p.k, bh * DK + j);
         const float qj = load(p.q, bh * DK + j);
         const float k2 = kj * kj;
-        float Io[4] = {Iv[n].x, Iv[n].y, Iv[n].z, Iv[n].w};
-        float Mo[4] = {Mv[n].x, Mv[n].y, Mv[n].z, Mv[n].w};
+        float Io[4] = {Iv[n][0], Iv[n][1], Iv[n][2], Iv[n][3]};
+        float Mo[4] = {Mv[n][0], Mv[n][1], Mv[n][2], Mv[n][3]};
         float In[4], Mn[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             In[e] = __builtin_fmaf(alpha, Io[e], __builtin_fmaf(bcol[e], k2, c));
             const float eta = __builtin_fmaf(alpha * Io[e], Mo[e], bvcol[e] * kj);
-            Mn[e] = eta / In[e];
+            Mn[e] = eta * fast_rcp(In[e]);
             acc[e] = __builtin_fmaf(qj, Mn[e], acc[e]);
         }
-        I4[j * CG + cg] = make_float4(In[0], In[1], In[2], In[3]);
-        M4[j * CG + cg] = make_float4(Mn[0], Mn[1], Mn[2], Mn[3]);
+        // the new state is not read again by this call: stream it past the caches
+        __builtin_nontemporal_store(f32x4{In[0], In[1], In[2], In[3]}, &I4[j * CG + cg]);
+        __builtin_nontemporal_store(f32x4{Mn[0], Mn[1], Mn[2], Mn[3]}, &M4[j * CG + cg]);
     }
 
     s_part[r0][cg] = make_float4(acc[0], acc[1], acc[2], acc[3]);
@@ -102,10 +107,10 @@ static int launch_dv(const DecodeParams& p, int64_t dv, int64_t grid, hipStream_
         hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(grid)), dim3(nth), 0, st, p);
     };
     switch (dv) {
-        case 16: go(k_decode<DK, 16, BF16>, DK * 16 / 4 < 256 ? DK * 16 / 4 : 256); break;
-        case 32: go(k_decode<DK, 32, BF16>, DK * 32 / 4 < 256 ? DK * 32 / 4 : 256); break;
-        case 64: go(k_decode<DK, 64, BF16>, DK * 64 / 4 < 256 ? DK * 64 / 4 : 256); break;
-        case 128: go(k_decode<DK, 128, BF16>, DK * 128 / 4 < 256 ? DK * 128 / 4 : 256); break;
+        case 16: go(k_decode<DK, 16, BF16>, DK * 16 / 4 < 512 ? DK * 16 / 4 : 512); break;
+        case 32: go(k_decode<DK, 32, BF16>, DK * 32 / 4 < 512 ? DK * 32 / 4 : 512); break;
+        case 64: go(k_decode<DK, 64, BF16>, DK * 64 / 4 < 512 ? DK * 64 / 4 : 512); break;
+        case 128: go(k_decode<DK, 128, BF16>, DK * 128 / 4 < 512 ? DK * 128 / 4 : 512); break;
         default: return KDN_EUNSUPPORTED;
     }
     return launch_status();
