@@ -7,16 +7,28 @@
 // affine recurrences
 //   J_t = alpha_t J_{t-1} + beta_t[i] k_t[j]^2,   eta_t = alpha_t eta_{t-1} + beta_t[i] v_t[i] k_t[j].
 // Over a stretch of tokens starting from zero they give the composite
-// (G, J, eta): G = prod alpha, and per 16-token chunk with in-chunk
-// log-decays b_t = -sum_{u<=t} A d_u and weights w_s = e^{b_last - b_s} <= 1,
-//   J   <- e^{b_last} J   + (w (.) K^2)^T B,      eta <- e^{b_last} eta + (w (.) K)^T (B (.) V),
-// two genuine contractions over the chunk's tokens: v_mfma_f32_16x16x4f32.
+// (G, J, eta): G = prod alpha and, with w_s = prod_{u > s} alpha_u the decay of
+// token s to the end of the stretch,
+//   J = (w (.) K^2)^T B,      eta = (w (.) K)^T (B (.) V),
+// two genuine contractions over the stretch's tokens, accumulated 16 tokens
+// at a time on v_mfma_f32_16x16x4f32.
 // Composites combine in order, (G2, X2) o (G1, X1) = (G2 G1, G2 X1 + X2), the
 // associativity that makes these updates scannable (KLA summary,
 // Metodologia 2).
 //
-// A workgroup owns one sub-segment of one head; wave w owns value columns
-// [16w, 16w+16) and all d_k rows, J and eta in MFMA accumulators.
+// One wave per (head, sub-segment, tile of NC <= 32 value columns), with all
+// d_k rows; no LDS and no barriers.  Every operand is loaded from global
+// memory straight into its MFMA register layout (A[i][k] in lane i + 16k,
+// B[k][j] in lane j + 16k, D[i][j] in lane j + 16(i/4), register i%4):
+//   * J and eta live in accumulators as MT x NT tiles of 16 x 16 whose rows
+//     and columns interleave: tile (m, n) element (i, j) is entry
+//     [MT i + m][NT j + n], so lane (c, g), register r holds [MT (4g + r) + m][NT c + n];
+//   * both contractions visit token s = 4g + kk at k-step kk, so lane (c, g)
+//     reads the run k_s[MT c .. MT c + MT) for its A operands and the runs
+//     beta_s, v_s [NT c .. NT c + NT) for its B operands: one vector load each;
+//   * loads go through buffer resources that end at the sub-segment's last
+//     token (rows past it read as 0), so the prefetched chunk stays in flight.
+#include "kdn_lane.h"
 #include "kdn_params.h"
 
 #include <type_traits>
@@ -28,6 +40,11 @@ typedef float f32x4c __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4c mfma4c(float a, float b, f32x4c c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+constexpr int kCompCols = 32;   // value columns per wave: 2 x MT x 2 x 4 accumulator registers
+
+// Column tiles of one head in the composite pass.
+static inline int comp_tiles(int64_t dv) { return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1; }
 
 // Token range of sub-segment r of segment s: the segment's chunks split in R.
 __device__ __forceinline__ void sub_tokens(const DiagParams& p, int C, int R, int s, int r,
@@ -41,42 +58,31 @@ __device__ __forceinline__ void sub_tokens(const DiagParams& p, int C, int R, in
     t1 = b * C < p.T ? b * C : p.T;
 }
 
-template <int DK, int DV, bool BF16>
-__global__ __launch_bounds__(DV / 16 * kWave) void k_diag_comp(DiagParams p, int32_t R) {
+template <int DK, int NC, bool BF16>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(BF16 || DK < 128 ? 2 : 1)))
+void k_diag_comp(DiagParams p, int32_t R) {
     using E = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int C = 16;
-    constexpr int W = DV / 16;
-    constexpr int NTH = W * kWave;
-    constexpr int KR = DK + 16;          // row strides: conflict-free MFMA operand reads
-    constexpr int VR = DV + 16;
     constexpr int MT = DK / 16;
-    constexpr int VW = BF16 ? 8 : 4;     // elements per 16-byte vector
-    constexpr int NKV = (C * DK / VW + NTH - 1) / NTH;
-    constexpr int NVV = (C * DV / VW + NTH - 1) / NTH;
+    constexpr int NT = NC / 16;
+    constexpr int ES = static_cast<int>(sizeof(E));
 
-    struct Stage {
-        float k[C][KR];
-        float k2[C][KR];
-        float b[C][VR];
-        float bv[C][VR];
-        float w[C];
-        float decay;
-    };
-    __shared__ Stage stg[2];
-    __shared__ float s_logsum;
-
-    const int tid = threadIdx.x;
-    const int lane = tid % kWave;
-    const int wv = tid / kWave;
-    const int g = lane / 16;
-    const int c = lane % 16;
+    const int lane = threadIdx.x;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int ntile = static_cast<int>(p.dv / NC);
     const int nsub = (p.S - 1) * R;
-    const int64_t bh = blockIdx.x / nsub;
-    const int sr = static_cast<int>(blockIdx.x % nsub);
+    const int64_t id = xcd_local_id();       // a sub-segment's column tiles share an XCD
+    const int tile = static_cast<int>(id % ntile);
+    const int64_t rest = id / ntile;
+    const int sr = static_cast<int>(rest % nsub);
+    const int64_t bh = rest / nsub;
     const int seg = sr / R;
     const int sub = sr % R;
     int64_t t_begin, t_end;
     sub_tokens(p, C, R, seg, sub, t_begin, t_end);
+    const int64_t DV = p.dv;
+    const int64_t cb = static_cast<int64_t>(tile) * NC;
 
     const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
     const E* vh = static_cast<const E*>(p.v) + bh * p.T * DV;
@@ -85,138 +91,118 @@ __global__ __launch_bounds__(DV / 16 * kWave) void k_diag_comp(DiagParams p, int
     const E* dh = static_cast<const E*>(p.d) + bh * p.T;
     const float4* sch = p.scal + bh * p.T;
 
-    f32x4c J[MT], X[MT];
+    f32x4c J[MT][NT], X[MT][NT];
 #pragma unroll
-    for (int m = 0; m < MT; ++m) {
-        J[m] = f32x4c{0.0f, 0.0f, 0.0f, 0.0f};
-        X[m] = J[m];
-    }
-
-    uint4 rk[NKV], rb[NVV], rv[NVV];
-    float rl = 0.0f;
-    float logsum = 0.0f;   // wave 0 lanes < 16: sum of b_last over chunks (log of prod alpha)
-
-    auto fetch = [&](int64_t t0, int L) {
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int n = 0; n < NKV; ++n) {
-            const int e = tid + n * NTH;
-            rk[n] = make_uint4(0u, 0u, 0u, 0u);
-            if (e * VW < L * DK) rk[n] = ld16(kh + t0 * DK + static_cast<int64_t>(e) * VW);
+        for (int n = 0; n < NT; ++n) {
+            J[m][n] = f32x4c{0.0f, 0.0f, 0.0f, 0.0f};
+            X[m][n] = J[m][n];
         }
-#pragma unroll
-        for (int n = 0; n < NVV; ++n) {
-            const int e = tid + n * NTH;
-            rb[n] = make_uint4(0u, 0u, 0u, 0u);
-            rv[n] = rb[n];
-            if (e * VW < L * DV) {
-                rb[n] = bth ? ld16(bth + t0 * DV + static_cast<int64_t>(e) * VW)
-                            : splat16<BF16>(dh, t0 + e * VW / DV);
-                rv[n] = ld16(vh + t0 * DV + static_cast<int64_t>(e) * VW);
-            }
-        }
-        if (tid < C) rl = tid < L ? sch[t0 + tid].w : 0.0f;   // A d_t (0: padding)
+
+    // one chunk's operands in lane (c, g): token s = 4g + kk for the
+    // contractions, token c for the decay scalars
+    struct Ops {
+        float k[4][MT];     // k_s[MT c + m]
+        float b[4][NT];     // beta_s[cb + NT c + n]
+        float v[4][NT];     // v_s[cb + NT c + n]
+        float ad;           // A d of token t0 + c (0 past the end)
     };
-
-    auto commit = [&](int nb) {
-        Stage& S = stg[nb];
-#pragma unroll
-        for (int n = 0; n < NKV; ++n) {
-            const int e = tid + n * NTH;
-            if (e * VW < C * DK) {
-                const int t = e * VW / DK;
-                const int j = e * VW % DK;
-                float f[VW];
-                widen<BF16>(rk[n], f);
-#pragma unroll
-                for (int u = 0; u < VW; ++u) {
-                    S.k[t][j + u] = f[u];
-                    S.k2[t][j + u] = f[u] * f[u];
-                }
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NVV; ++n) {
-            const int e = tid + n * NTH;
-            if (e * VW < C * DV) {
-                const int t = e * VW / DV;
-                const int i = e * VW % DV;
-                float fb[VW], fv[VW];
-                widen<BF16>(rb[n], fb);
-                widen<BF16>(rv[n], fv);
-#pragma unroll
-                for (int u = 0; u < VW; ++u) {
-                    S.b[t][i + u] = fb[u];
-                    S.bv[t][i + u] = fb[u] * fv[u];
-                }
-            }
-        }
-        if (tid < C) {
-            float b = -rl;
-#pragma unroll
-            for (int o = 1; o < C; o <<= 1) {
-                const float u = __shfl_up(b, o, C);
-                if (tid >= o) b += u;
-            }
-            const float blast = __shfl(b, C - 1, C);
-            S.w[tid] = fast_exp(blast - b);
-            if (tid == 0) S.decay = fast_exp(blast);
-            logsum += blast;
-        }
-    };
-
-    const int64_t nch = (t_end - t_begin + C - 1) / C;
-    auto chunk_len = [&](int64_t ch) -> int {
-        const int64_t rem = t_end - (t_begin + ch * C);
-        return static_cast<int>(rem < C ? rem : C);
-    };
-
-    if (nch > 0) {
-        fetch(t_begin, chunk_len(0));
-        commit(0);
-    }
-    __syncthreads();
-    if (nch > 1) fetch(t_begin + C, chunk_len(1));
-
-    for (int64_t ch = 0; ch < nch; ++ch) {
-        const int bsel = static_cast<int>(ch & 1);
-        const Stage& S = stg[bsel];
-        const float decay = S.decay;
-        float wk[4], bj[4], be[4];
+    auto load = [&](int64_t t0, Ops& x) __attribute__((always_inline)) {
+        const int64_t L0 = t_end - t0;
+        const int64_t L = (t0 < t_begin || L0 < 0) ? 0 : (L0 < C ? L0 : C);   // 0: nothing is read
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kh + t0 * DK, L * DK * ES);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vh + t0 * DV, L * DV * ES);
+        const __amdgpu_buffer_rsrc_t rb = bth ? buf_rsrc(bth + t0 * DV, L * DV * ES) : buf_rsrc(dh + t0, L * ES);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            wk[kk] = S.w[4 * kk + g];
-            bj[kk] = S.b[4 * kk + g][16 * wv + c];
-            be[kk] = S.bv[4 * kk + g][16 * wv + c];
-        }
+            const int s_ = 4 * g + kk;
+            buf_load_widen<E, MT>(rk, static_cast<uint32_t>((s_ * DK + MT * c) * ES), x.k[kk]);
+            buf_load_widen<E, NT>(rv, static_cast<uint32_t>((s_ * DV + cb + NT * c) * ES), x.v[kk]);
+            if (bth) {
+                buf_load_widen<E, NT>(rb, static_cast<uint32_t>((s_ * DV + cb + NT * c) * ES), x.b[kk]);
+            } else {
+                float d1[1];
+                buf_load_widen<E, 1>(rb, static_cast<uint32_t>(s_ * ES), d1);
 #pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            J[m] *= decay;
-            X[m] *= decay;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                J[m] = mfma4c(S.k2[4 * kk + g][16 * m + c] * wk[kk], bj[kk], J[m]);
-                X[m] = mfma4c(S.k[4 * kk + g][16 * m + c] * wk[kk], be[kk], X[m]);
+                for (int n = 0; n < NT; ++n) x.b[kk][n] = d1[0];
             }
         }
-        if (ch + 1 < nch) commit(bsel ^ 1);
-        __syncthreads();
-        if (ch + 2 < nch) fetch(t_begin + (ch + 2) * C, chunk_len(ch + 2));
+        float ad[1];
+        buf_load<1>(buf_rsrc(sch + t0, L * 16), static_cast<uint32_t>(c * 16 + 12), ad);
+        x.ad = ad[0];
+    };
+
+    // Chunks are visited last to first.  Every token's weight is its decay to
+    // the sub-segment's end, w_s = exp(-sum_{u > s} A d_u): no accumulator is
+    // rescaled per chunk, and the exponent is built by additions only (Rsum,
+    // the log-decay of the chunks already visited, plus the in-chunk suffix),
+    // so its rounding error stays relative to its own size.
+    float Rsum = 0.0f;
+    auto compute = [&](const Ops& x) __attribute__((always_inline)) {
+        const float P = row_prefix16(x.ad);          // in-chunk inclusive sum of A d
+        const float Tc = bcast<15>(P);                // the chunk's total
+        const float wt = fast_exp(-(Rsum + (Tc - P)));   // weight of token t0 + c
+        float ws[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ws[kk] = __shfl(wt, 16 * g + 4 * g + kk);
+        float bv[4][NT];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) bv[kk][n] = x.b[kk][n] * x.v[kk][n];
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            float wk[4], wk2[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                wk[kk] = ws[kk] * x.k[kk][m];
+                wk2[kk] = wk[kk] * x.k[kk][m];
+            }
+            // k-step outermost: 2 NT independent accumulators between two
+            // MFMAs on the same one
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int n = 0; n < NT; ++n) {
+                    J[m][n] = mfma4c(wk2[kk], x.b[kk][n], J[m][n]);
+                    X[m][n] = mfma4c(wk[kk], bv[kk][n], X[m][n]);
+                }
+        }
+        Rsum += Tc;
+    };
+
+    // two operand sets: the previous chunk loads while this one computes
+    // (a chunk before the sub-segment reads nothing)
+    const int64_t nch = (t_end - t_begin + C - 1) / C;
+    Ops xa, xb;
+    load(t_begin + (nch - 1) * C, xa);
+    for (int64_t i = 0; i < nch; i += 2) {
+        const int64_t t0 = t_begin + (nch - 1 - i) * C;
+        load(t0 - C, xb);
+        compute(xa);
+        if (i + 1 >= nch) break;
+        load(t0 - 2 * C, xa);
+        compute(xb);
     }
 
-    if (tid == 0) s_logsum = logsum;
-    __syncthreads();
-    // J[m][r] = J[16m + 4g + r][16 wv + c]
     const int64_t slot = (bh * (p.S - 1) + seg) * R + sub;
     float* out = p.sub + slot * 2 * DK * DV;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int64_t off = static_cast<int64_t>(16 * m + 4 * g + r) * DV + 16 * wv + c;
-            out[off] = J[m][r];
-            out[static_cast<int64_t>(DK) * DV + off] = X[m][r];
+            float rowJ[NT], rowX[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                rowJ[n] = J[m][n][r];
+                rowX[n] = X[m][n][r];
+            }
+            const int64_t off = static_cast<int64_t>(MT * (4 * g + r) + m) * DV + cb + NT * c;
+            store_run<NT>(out + off, rowJ);
+            store_run<NT>(out + static_cast<int64_t>(DK) * DV + off, rowX);
         }
-    if (tid == 0) p.gsub[slot] = fast_exp(s_logsum);
+    if (lane == 0 && tile == 0) p.gsub[slot] = fast_exp(-Rsum);
 }
 
 // Ordered carry: sub-segment composites -> the starting (J, eta) of every
@@ -255,10 +241,10 @@ __global__ __launch_bounds__(256) void k_diag_carry_sub(DiagParams p, int64_t dk
 template <int DK, bool BF16>
 static int comp_launch_dv(const DiagParams& p, int64_t dv, int64_t grid, int32_t R, hipStream_t st) {
     switch (dv) {
-        case 16: hipLaunchKernelGGL((k_diag_comp<DK, 16, BF16>), dim3(grid), dim3(64), 0, st, p, R); break;
-        case 32: hipLaunchKernelGGL((k_diag_comp<DK, 32, BF16>), dim3(grid), dim3(128), 0, st, p, R); break;
-        case 64: hipLaunchKernelGGL((k_diag_comp<DK, 64, BF16>), dim3(grid), dim3(256), 0, st, p, R); break;
-        case 128: hipLaunchKernelGGL((k_diag_comp<DK, 128, BF16>), dim3(grid), dim3(512), 0, st, p, R); break;
+        case 16: hipLaunchKernelGGL((k_diag_comp<DK, 16, BF16>), dim3(grid), dim3(kWave), 0, st, p, R); break;
+        case 32:
+        case 64:
+        case 128: hipLaunchKernelGGL((k_diag_comp<DK, kCompCols, BF16>), dim3(grid), dim3(kWave), 0, st, p, R); break;
         default: return KDN_EUNSUPPORTED;
     }
     return launch_status();
@@ -275,11 +261,12 @@ static int comp_launch(const DiagParams& p, int64_t dk, int64_t grid, int32_t R,
     }
 }
 
-// Composites of segments 0..S-2 in R sub-segments each, then the carry into
-// every segment's starting state (p.comp).  Needs the per-token scalars.
+// Composites of segments 0..S-2 in R sub-segments each (one wave per
+// sub-segment and column tile), then the carry into every segment's starting
+// state (p.comp).  Needs the per-token scalars.
 int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
     const int64_t BH = B * p.H;
-    const int64_t grid = BH * (p.S - 1) * R;
+    const int64_t grid = BH * (p.S - 1) * R * comp_tiles(p.dv);
     int rc = bf16 ? comp_launch<true>(p, dk, grid, R, st) : comp_launch<false>(p, dk, grid, R, st);
     if (rc != KDN_OK) return rc;
     const int64_t n = BH * dk * p.dv;

@@ -53,76 +53,6 @@ constexpr int kIsoChunk = 16;
 // across column tiles.
 constexpr int kIsoCols = 64;
 
-// Buffer resource over `bytes` bytes from `base` (raw, untyped, gfx9 format
-// word).  Loads past the end return 0 and stores past the end are dropped, so
-// a ragged chunk needs no branches: the wait counters stay exact and the next
-// chunk's loads stay in flight.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* base, int64_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), 0x00020000);
-}
-
-// N contiguous floats at byte offset `off` (16-byte aligned for N >= 4,
-// 8-byte for N == 2).
-template <int N>
-__device__ __forceinline__ void buf_load(__amdgpu_buffer_rsrc_t r, uint32_t off, float (&x)[N]) {
-    if constexpr (N >= 4) {
-#pragma unroll
-        for (int e = 0; e < N; e += 4) {
-            const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * e, 0, 0);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) x[e + i] = __uint_as_float(u[i]);
-        }
-    } else if constexpr (N == 2) {
-        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-        x[0] = __uint_as_float(u[0]);
-        x[1] = __uint_as_float(u[1]);
-    } else {
-        x[0] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-    }
-}
-
-template <int N>
-__device__ __forceinline__ void buf_store(__amdgpu_buffer_rsrc_t r, uint32_t off, const float (&x)[N]) {
-    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-    if constexpr (N >= 4) {
-#pragma unroll
-        for (int e = 0; e < N; e += 4) {
-            const u32x4 u = {__float_as_uint(x[e]), __float_as_uint(x[e + 1]), __float_as_uint(x[e + 2]),
-                             __float_as_uint(x[e + 3])};
-            __builtin_amdgcn_raw_buffer_store_b128(u, r, off + 4 * e, 0, 0);
-        }
-    } else if constexpr (N == 2) {
-        const u32x2 u = {__float_as_uint(x[0]), __float_as_uint(x[1])};
-        __builtin_amdgcn_raw_buffer_store_b64(u, r, off, 0, 0);
-    } else {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x[0]), r, off, 0, 0);
-    }
-}
-
-// N contiguous floats (16-byte aligned for N >= 4, 8-byte for N == 2).
-template <int N>
-__device__ __forceinline__ void store_run(float* dst, const float (&x)[N]) {
-    if constexpr (N >= 4) {
-#pragma unroll
-        for (int e = 0; e < N; e += 4)
-            *reinterpret_cast<float4*>(dst + e) = make_float4(x[e], x[e + 1], x[e + 2], x[e + 3]);
-    } else if constexpr (N == 2) {
-        *reinterpret_cast<float2*>(dst) = make_float2(x[0], x[1]);
-    } else {
-        dst[0] = x[0];
-    }
-}
-
-// Inclusive prefix sum over the 16 lanes of each DPP row.
-__device__ __forceinline__ float row_prefix16(float x) {
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x111, 0xf, 0xf, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x112, 0xf, 0xf, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x114, 0xf, 0xf, true));
-    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x118, 0xf, 0xf, true));
-    return x;
-}
-
 // One chunk's operands in lane (c, g); t0 is the chunk's first token.  The
 // query-side set (q, k in the d_k visiting order, gates) and the update-side
 // set (k transposed, v) are both loaded a whole chunk ahead.

@@ -47,10 +47,13 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
     if (S > pl.nchunks) S = pl.nchunks;
     if (S < 1) S = 1;
     pl.S = static_cast<int32_t>(S);
-    // composites: about two workgroups per CU, at least 4 chunks per sub-segment
+    // composites: at most eight one-wave workgroups (32 columns each) per CU,
+    // the number resident at once (two per SIMD), so that none waits for a
+    // second round; at least 4 chunks per sub-segment
     int64_t R = 1;
     if (pl.S > 1 && BH > 0) {
-        R = (2 * kNumCU + BH * (pl.S - 1) - 1) / (BH * (pl.S - 1));
+        const int64_t units = BH * (pl.S - 1) * (dv > 32 ? dv / 32 : 1);
+        R = 8 * kNumCU / units;
         const int64_t per_seg = pl.nchunks / pl.S;
         if (R > per_seg / 4) R = per_seg / 4;
         if (R < 1) R = 1;
@@ -198,6 +201,8 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const Plan pl = plan_scan(BH, T, d_v);
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
     if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
+    // composite pass: one wave per (head, sub-segment, 32-column tile)
+    if (pl.S > 1 && BH * (pl.S - 1) * pl.R * (d_v / 16) > kMaxGrid) return KDN_EINVAL;
     const DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
     const size_t need = dw.total;
     const int wc = workspace_check(workspace, workspace_bytes, need);
