@@ -255,6 +255,26 @@ __device__ __forceinline__ void store16(float* dst, const float (&x)[16]) {
         reinterpret_cast<float4*>(dst)[n] = make_float4(x[4 * n], x[4 * n + 1], x[4 * n + 2], x[4 * n + 3]);
 }
 
+// A lane's 16 entries inside one checkpoint half of BLK floats, interleaved
+// by float4: float4 n of lane l sits at (n * BLK/16 + l) * 4, so each of the
+// four vector accesses of a wave covers 1 KB of contiguous memory.
+template <int BLK>
+__device__ __forceinline__ void load16_ckpt(const float* half, int64_t l, float (&x)[16]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const float4 f = reinterpret_cast<const float4*>(half)[n * (BLK / 16) + l];
+        x[4 * n] = f.x; x[4 * n + 1] = f.y; x[4 * n + 2] = f.z; x[4 * n + 3] = f.w;
+    }
+}
+
+template <int BLK>
+__device__ __forceinline__ void store16_ckpt(float* half, int64_t l, const float (&x)[16]) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+        reinterpret_cast<float4*>(half)[n * (BLK / 16) + l] =
+            make_float4(x[4 * n], x[4 * n + 1], x[4 * n + 2], x[4 * n + 3]);
+}
+
 // Starting state of a lane's 16 entries, unscaled: I0 (or I_prior), its
 // excess J0 = I0 - I_prior, mu0 (absent: 0) and eta0 = I0 mu0.
 __device__ __forceinline__ void start_state(const BwdParams& p, int64_t off, float (&I)[16],
@@ -304,10 +324,10 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
     start_state(p, (bh * DK + j) * p.dv + tile * CI + cg * 16, I, J, E, m0);
     const int64_t run = bh * Sh::NTILE + tile;
     const int64_t nruns = p.BH * Sh::NTILE;
-    const int64_t lane_off = (cg * DK + j) * 16;
-    float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, 0, nch, nruns) + lane_off;
-    store16(ck, J);
-    store16(ck + Sh::BLK, E);
+    const int64_t lid = cg * DK + j;            // this lane's index in a checkpoint half
+    float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, 0, nch, nruns);
+    store16_ckpt<Sh::BLK>(ck, lid, J);
+    store16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, E);
 
     auto chunk_len = [&](int64_t c) -> int {
         const int64_t rem = p.T - c * C;
@@ -325,20 +345,19 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
         const int b = static_cast<int>(c & 1);
         const BwdStage<DK, CI, false>& S = stg[b];
         const int L = chunk_len(c);
-        // software-pipelined: the next token's LDS operands load while this one computes
-        float2 scx = make_float2(S.sc[0].x, S.sc[0].z);
-        float kj = S.k[0][j], bj = S.b[0][lc], vj = S.v[0][lc];
-        for (int tt = 0; tt < L; ++tt) {
-            const int tn = tt + 1 < L ? tt + 1 : tt;
-            const float2 scx_n = make_float2(S.sc[tn].x, S.sc[tn].z);
-            const float kj_n = S.k[tn][j], bj_n = S.b[tn][lc], vj_n = S.v[tn][lc];
-            const float b = bj * scx.y;
-            const float bvs = dpp_src(b * vj);
-            bwd_step_inplace(J, E, scx.x, dpp_src(b), bvs, kj, kj * kj);
-            scx = scx_n;
-            kj = kj_n;
-            bj = bj_n;
-            vj = vj_n;
+        auto token = [&](int tt) __attribute__((always_inline)) {
+            const float4 sc = S.sc[tt];
+            const float kj = S.k[tt][j];
+            const float b = S.b[tt][lc] * sc.z;
+            const float bvs = dpp_src(b * S.v[tt][lc]);
+            bwd_step_inplace(J, E, sc.x, dpp_src(b), bvs, kj, kj * kj);
+        };
+        if (L == C) {
+            // a whole chunk, unrolled: constant stage offsets, operand reads
+            // scheduled ahead by the compiler
+            Unroll<0, C>::run([&](auto u) { token(decltype(u)::value); });
+        } else {
+            for (int tt = 0; tt < L; ++tt) token(tt);
         }
         // unscale and store the state before chunk c + 1
         const float inv_s = 1.0f / uniform(S.sc[L - 1].z);
@@ -347,9 +366,9 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
             J[e] *= inv_s;
             E[e] *= inv_s;
         }
-        float* dst = ckpt_slot<Sh::BLK>(p.ckpt, run, c + 1, nch, nruns) + lane_off;
-        store16(dst, J);
-        store16(dst + Sh::BLK, E);
+        float* dst = ckpt_slot<Sh::BLK>(p.ckpt, run, c + 1, nch, nruns);
+        store16_ckpt<Sh::BLK>(dst, lid, J);
+        store16_ckpt<Sh::BLK>(dst + Sh::BLK, lid, E);
         if (c + 1 < nrun) ld.commit(stg[b ^ 1], chunk_len(c + 1), tid);
         __syncthreads();
         if (c + 2 < nrun) ld.fetch(p, bh, tile, (c + 2) * C, chunk_len(c + 2), tid);
@@ -405,7 +424,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
 
     const int64_t run = bh * Sh::NTILE + tile;
     const int64_t nruns = p.BH * Sh::NTILE;
-    const int64_t lane_off = (cg * DK + j) * 16;
+    const int64_t lid = cg * DK + j;            // this lane's index in a checkpoint half
 
     auto chunk_len = [&](int64_t c) -> int {
         const int64_t rem = T - c * C;
@@ -420,9 +439,9 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         // dmu_T mu_T / I_T, scaled by 1 / s.  The checkpoint pass stored the
         // final state (J_T, eta_T) unscaled after the last chunk.
         float JT[16], ET[16];
-        const float* ckT = ckpt_slot<Sh::BLK>(p.ckpt, run, nch, nch, nruns) + lane_off;
-        load16(ckT, JT);
-        load16(ckT + Sh::BLK, ET);
+        const float* ckT = ckpt_slot<Sh::BLK>(p.ckpt, run, nch, nch, nruns);
+        load16_ckpt<Sh::BLK>(ckT, lid, JT);
+        load16_ckpt<Sh::BLK>(ckT + Sh::BLK, lid, ET);
         const float inv_s = 1.0f / uniform(p.scal[bh * T + T - 1].z);
         Unroll<0, 16>::run([&](auto cc) {
             constexpr int c = decltype(cc)::value;
@@ -519,13 +538,13 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const BwdStage<DK, CI, true>& S = stg[b];
         const int Lc = chunk_len(c);
         const int64_t t0 = c * C;
-        const float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, c, nch, nruns) + lane_off;
+        const float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, c, nch, nruns);
         const int nheld = (Lc + HELD - 1) / HELD;
 
         for (int m = nheld - 1; m >= 0; --m) {
             float sJ[HELD][16], sE[HELD][16];
-            load16(ck, sJ[0]);
-            load16(ck + Sh::BLK, sE[0]);
+            load16_ckpt<Sh::BLK>(ck, lid, sJ[0]);
+            load16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, sE[0]);
             auto operands = [&](int tt, float& rho, float& bs, float& bvs,
                                 float& kj) __attribute__((always_inline)) {
                 const float4 sc = S.sc[tt];
