@@ -80,6 +80,20 @@ def test_diag_head_sizes(kdn, dk, dv):
     gu.compare_diag(inp, res, _all_heads(1, 2), what=f"dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_diag_composite_head_sizes(kdn, dk, dv):
+    """Two segments, so the first is a composite cut into several sub-segments:
+    every (d_k, d_v) pairing of the composite pass's one-wave tiles, with a
+    ragged final chunk (T = 601)."""
+    kdn.kdn_set_diag_segments(2)
+    dt = "bf16" if (dk + dv) % 64 == 0 else "f32"
+    inp = synth.diag_inputs(gu.diag_spec(1, 2, 601, dk, dv, dt, seed=7000 + dk + dv))
+    print(f"diag composite dk={dk} dv={dv} {dt}", flush=True)
+    res = _run_diag(kdn, gu.upload_diag(inp))
+    gu.compare_diag(inp, res, _all_heads(1, 2), what=f"composite dk={dk} dv={dv}")
+
+
 @pytest.mark.parametrize("S", [1, 4])
 def test_diag_initial_state(kdn, S):
     """Nonzero starting state (I0 != I_prior, mu0 != 0), both segmentings."""
