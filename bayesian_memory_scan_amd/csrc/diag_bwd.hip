@@ -740,19 +740,19 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
 // does not depend on timing).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_diag_bwd_rows(BwdParams p, int64_t n4) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= n4) return;
     const int64_t stride4 = n4;   // float4s per tile slice
     const float4* a = reinterpret_cast<const float4*>(p.part_dq);
     const float4* b = reinterpret_cast<const float4*>(p.part_dk);
-    float4 sq = a[e], sk = b[e];
-    for (int t = 1; t < p.ntile; ++t) {
-        const float4 x = a[t * stride4 + e], y = b[t * stride4 + e];
-        sq.x += x.x; sq.y += x.y; sq.z += x.z; sq.w += x.w;
-        sk.x += y.x; sk.y += y.y; sk.z += y.z; sk.w += y.w;
+    for (int64_t e = elem_first(); e < n4; e += elem_stride()) {
+        float4 sq = a[e], sk = b[e];
+        for (int t = 1; t < p.ntile; ++t) {
+            const float4 x = a[t * stride4 + e], y = b[t * stride4 + e];
+            sq.x += x.x; sq.y += x.y; sq.z += x.z; sq.w += x.w;
+            sk.x += y.x; sk.y += y.y; sk.z += y.z; sk.w += y.w;
+        }
+        reinterpret_cast<float4*>(p.dq)[e] = sq;
+        reinterpret_cast<float4*>(p.dk)[e] = sk;
     }
-    reinterpret_cast<float4*>(p.dq)[e] = sq;
-    reinterpret_cast<float4*>(p.dk)[e] = sk;
 }
 
 // One workgroup per head (b, h): dd_t = -A alpha_t dalpha_t, and the head's
@@ -857,7 +857,7 @@ int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64
         if (rc != KDN_OK) return rc;
         if (p.ntile > 1 && p.T > 0) {
             const int64_t n4 = p.BH * p.T * dk / 4;
-            hipLaunchKernelGGL(k_diag_bwd_rows, dim3(static_cast<uint32_t>((n4 + 255) / 256)), dim3(256), 0,
+            hipLaunchKernelGGL(k_diag_bwd_rows, dim3(elem_groups(n4)), dim3(256), 0,
                                st, p, n4);
         }
         if (bf16) hipLaunchKernelGGL(k_diag_bwd_tokens<true>, dim3(static_cast<uint32_t>(p.BH)), dim3(256), 0, st, p);

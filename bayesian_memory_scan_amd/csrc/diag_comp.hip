@@ -207,10 +207,8 @@ void k_diag_comp(DiagParams p, int32_t R) {
 
 // Ordered carry: sub-segment composites -> the starting (J, eta) of every
 // main segment.  One thread per memory entry of every head.
-__global__ __launch_bounds__(256) void k_diag_carry_sub(DiagParams p, int64_t dk, int64_t n_total, int32_t R) {
+__device__ __forceinline__ void carry_sub_entry(const DiagParams& p, int64_t dk, int64_t e, int32_t R) {
     const int64_t n_per_head = dk * p.dv;
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= n_total) return;
     const int64_t bh = e / n_per_head;
     const int64_t r = e % n_per_head;
     const int64_t off = bh * n_per_head + r;
@@ -236,6 +234,10 @@ __global__ __launch_bounds__(256) void k_diag_carry_sub(DiagParams p, int64_t dk
             eta = __builtin_fmaf(G, eta, sub[n_per_head + r]);
         }
     }
+}
+
+__global__ __launch_bounds__(256) void k_diag_carry_sub(DiagParams p, int64_t dk, int64_t n_total, int32_t R) {
+    for (int64_t e = elem_first(); e < n_total; e += elem_stride()) carry_sub_entry(p, dk, e, R);
 }
 
 template <int DK, bool BF16>
@@ -270,7 +272,7 @@ int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int3
     int rc = bf16 ? comp_launch<true>(p, dk, grid, R, st) : comp_launch<false>(p, dk, grid, R, st);
     if (rc != KDN_OK) return rc;
     const int64_t n = BH * dk * p.dv;
-    hipLaunchKernelGGL(k_diag_carry_sub, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_diag_carry_sub, dim3(elem_groups(n)), dim3(256), 0, st,
                        p, dk, n, R);
     return launch_status();
 }

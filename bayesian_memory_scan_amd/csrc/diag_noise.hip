@@ -316,10 +316,10 @@ static int noise_main(const NoiseParams& p, int64_t dk, int64_t BH, hipStream_t 
 
 // T == 0: the final state is the starting state.
 __global__ __launch_bounds__(256) void k_noise_copy(NoiseParams p, int64_t n) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= n) return;
-    if (p.lam_T) p.lam_T[e] = p.lam0 ? p.lam0[e] : 1.0f;
-    if (p.mu_T) p.mu_T[e] = p.mu0 ? p.mu0[e] : 0.0f;
+    for (int64_t e = elem_first(); e < n; e += elem_stride()) {
+        if (p.lam_T) p.lam_T[e] = p.lam0 ? p.lam0[e] : 1.0f;
+        if (p.mu_T) p.mu_T[e] = p.mu0 ? p.mu0[e] : 0.0f;
+    }
 }
 
 int noise_launch(const NoiseParams& p, int64_t B, int64_t dk, bool bf16, hipStream_t st) {
@@ -327,7 +327,7 @@ int noise_launch(const NoiseParams& p, int64_t B, int64_t dk, bool bf16, hipStre
     if (BH == 0) return KDN_OK;
     if (p.T == 0) {
         const int64_t n = BH * dk * p.dv;
-        hipLaunchKernelGGL(k_noise_copy, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st, p, n);
+        hipLaunchKernelGGL(k_noise_copy, dim3(elem_groups(n)), dim3(256), 0, st, p, n);
         return launch_status();
     }
     const int rc = bf16 ? noise_main<true>(p, dk, BH, st) : noise_main<false>(p, dk, BH, st);

@@ -397,11 +397,11 @@ __device__ __forceinline__ void prep_chunk(const DiagParams& p, int64_t bh, int6
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units, int32_t nch) {
     constexpr int C = kDiagChunkTokens;
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (u >= n_units) return;
-    const int64_t bh = u / nch;
-    const int64_t t0 = (u % nch) * C;
-    prep_chunk<BF16>(p, bh, t0, p.T - t0 < C ? static_cast<int>(p.T - t0) : C);
+    for (int64_t u = elem_first(); u < n_units; u += elem_stride()) {
+        const int64_t bh = u / nch;
+        const int64_t t0 = (u % nch) * C;
+        prep_chunk<BF16>(p, bh, t0, p.T - t0 < C ? static_cast<int>(p.T - t0) : C);
+    }
 }
 
 // Packed variable-length batch: chunks start at every sequence's first token.
@@ -409,26 +409,24 @@ __global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_diag_prep_varlen(DiagParams p) {
     constexpr int C = kDiagChunkTokens;
-    const int64_t u = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (u >= p.H * p.T) return;
-    const int64_t h = u / p.T;
-    const int64_t t = u % p.T;
-    int64_t t_begin, t_end;
-    const int32_t s = find_sequence(p, t);
-    sequence_tokens(p, s, t_begin, t_end);
-    if ((t - t_begin) % C != 0) return;
-    prep_chunk<BF16>(p, h, t, t_end - t < C ? static_cast<int>(t_end - t) : C);
+    for (int64_t u = elem_first(); u < p.H * p.T; u += elem_stride()) {
+        const int64_t h = u / p.T;
+        const int64_t t = u % p.T;
+        int64_t t_begin, t_end;
+        const int32_t s = find_sequence(p, t);
+        sequence_tokens(p, s, t_begin, t_end);
+        if ((t - t_begin) % C != 0) continue;
+        prep_chunk<BF16>(p, h, t, t_end - t < C ? static_cast<int>(t_end - t) : C);
+    }
 }
 
 // Carry pass: in order over segments, turn each segment's composite into the
 // state it starts from.  One thread per memory entry of every head.  The
 // composites of 8 segments are loaded together, so a long chain of segments
 // costs one memory round trip per 8 (the isotropic pass touches only eta).
-__global__ __launch_bounds__(256) void k_diag_carry(DiagParams p, int64_t dk, int64_t n_total, int iso) {
+__device__ __forceinline__ void carry_entry(const DiagParams& p, int64_t dk, int64_t e, int iso) {
     constexpr int B8 = 8;
     const int64_t n_per_head = dk * p.dv;
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= n_total) return;
     const int64_t bh = e / n_per_head;
     const int64_t r = e % n_per_head;
     const int64_t off = bh * n_per_head + r;
@@ -467,13 +465,17 @@ __global__ __launch_bounds__(256) void k_diag_carry(DiagParams p, int64_t dk, in
     }
 }
 
+__global__ __launch_bounds__(256) void k_diag_carry(DiagParams p, int64_t dk, int64_t n_total, int iso) {
+    for (int64_t e = elem_first(); e < n_total; e += elem_stride()) carry_entry(p, dk, e, iso);
+}
+
 // T == 0: the final state is the starting state.
 __global__ __launch_bounds__(256) void k_diag_copy_state(DiagParams p, int64_t n, int iso) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e >= n) return;
-    const float m0 = p.mu0 ? p.mu0[e] : 0.0f;
-    if (!iso && p.I_T) p.I_T[e] = p.I0 ? p.I0[e] : p.I_prior;
-    if (p.mu_T) p.mu_T[e] = m0;
+    for (int64_t e = elem_first(); e < n; e += elem_stride()) {
+        const float m0 = p.mu0 ? p.mu0[e] : 0.0f;
+        if (!iso && p.I_T) p.I_T[e] = p.I0 ? p.I0[e] : p.I_prior;
+        if (p.mu_T) p.mu_T[e] = m0;
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -552,7 +554,7 @@ int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t s
     hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(1024), 0, st, p);
     const int64_t n = p.H * p.T;
     if (n > 0) {
-        const dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+        const dim3 grid(elem_groups(n));
         if (bf16) hipLaunchKernelGGL(k_diag_prep_varlen<true>, grid, dim3(256), 0, st, p);
         else hipLaunchKernelGGL(k_diag_prep_varlen<false>, grid, dim3(256), 0, st, p);
     }
@@ -569,7 +571,7 @@ int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st) 
     const int32_t nch = static_cast<int32_t>((p.T + kDiagChunk - 1) / kDiagChunk);
     const int64_t n = B * p.H * nch;
     if (n == 0) return KDN_OK;
-    const dim3 grid(static_cast<uint32_t>((n + 255) / 256));
+    const dim3 grid(elem_groups(n));
     if (bf16) hipLaunchKernelGGL(k_diag_prep<true>, grid, dim3(256), 0, st, p, n, nch);
     else hipLaunchKernelGGL(k_diag_prep<false>, grid, dim3(256), 0, st, p, n, nch);
     return launch_status();
@@ -579,7 +581,7 @@ int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st) 
 int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st) {
     const int64_t n = B * p.H * dk * p.dv;
     if (n == 0) return KDN_OK;
-    hipLaunchKernelGGL(k_diag_carry, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_diag_carry, dim3(elem_groups(n)), dim3(256), 0, st,
                        p, dk, n, iso ? 1 : 0);
     return launch_status();
 }
@@ -588,7 +590,7 @@ int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipS
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st) {
     const int64_t n = B * p.H * dk * p.dv;
     if (n == 0) return KDN_OK;
-    hipLaunchKernelGGL(k_diag_copy_state, dim3(static_cast<uint32_t>((n + 255) / 256)), dim3(256), 0, st,
+    hipLaunchKernelGGL(k_diag_copy_state, dim3(elem_groups(n)), dim3(256), 0, st,
                        p, n, iso ? 1 : 0);
     return launch_status();
 }

@@ -14,6 +14,24 @@ namespace kdn {
 constexpr int kWave = 64;
 constexpr int kNumCU = 256;  // MI355X compute units (8 XCDs x 32)
 
+// Element-wise passes: 256-thread workgroups walking their range with a grid
+// stride, so the grid stays far below the 2^32 - 1 work-item limit of one
+// dispatch whatever the element count.
+constexpr int kElemThreads = 256;
+constexpr int64_t kElemMaxGroups = 65536;   // 16.8 M threads: 32 waves on every SIMD
+
+inline uint32_t elem_groups(int64_t n) {
+    const int64_t g = (n + kElemThreads - 1) / kElemThreads;
+    return static_cast<uint32_t>(g < kElemMaxGroups ? g : kElemMaxGroups);
+}
+
+__device__ __forceinline__ int64_t elem_first() {
+    return static_cast<int64_t>(blockIdx.x) * kElemThreads + threadIdx.x;
+}
+__device__ __forceinline__ int64_t elem_stride() {
+    return static_cast<int64_t>(gridDim.x) * kElemThreads;
+}
+
 // bf16 -> fp32 is exact: the bf16 bits are the top half of the float.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

@@ -18,7 +18,14 @@ using namespace kdn;
 
 std::atomic<int32_t> g_segments_override{0};
 
-constexpr int64_t kMaxGrid = 2147483647;  // hardware limit on grid.x
+// One dispatch covers at most 2^32 - 1 work-items (the dispatch packet's grid
+// size is 32 bits).  Per-head and per-block launches use at most 512 threads
+// per workgroup; element-wise passes walk with a grid stride and always fit.
+constexpr int64_t kMaxItems = 4294967295;
+constexpr int64_t kMaxGroupThreads = 512;
+bool grid_fits(int64_t groups, int64_t threads = kMaxGroupThreads) {
+    return groups >= 0 && groups <= kMaxItems / threads;
+}
 constexpr int32_t kMaxSegments = 64;
 
 struct Plan {
@@ -128,8 +135,10 @@ int workspace_check(void* workspace, size_t* workspace_bytes, size_t need) {
     return KDN_OK;
 }
 
-// Guard against int64 overflow of element counts: B*H*T*D must stay < 2^62.
+// Guard against overflow: B*H*T*D must stay < 2^62 (int64 element counts)
+// and T below 2^31 (chunk and block counts are int32).
 bool sizes_fit(int64_t B, int64_t H, int64_t T, int64_t D) {
+    if (T > 2147483647) return false;
     const double n = static_cast<double>(B) * static_cast<double>(H) * static_cast<double>(T > 0 ? T : 1) *
                      static_cast<double>(D);
     return n < 4.0e18;
@@ -200,9 +209,9 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
 
     const Plan pl = plan_scan(BH, T, d_v);
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
-    if (BH * pl.S * ntile > kMaxGrid) return KDN_EINVAL;
-    // composite pass: one wave per (head, sub-segment, 32-column tile)
-    if (pl.S > 1 && BH * (pl.S - 1) * pl.R * (d_v / 16) > kMaxGrid) return KDN_EINVAL;
+    if (!grid_fits(BH * pl.S * ntile)) return KDN_EINVAL;
+    // composite pass: one wave per (head, sub-segment, column tile of 16 or 32)
+    if (pl.S > 1 && !grid_fits(BH * (pl.S - 1) * pl.R * (d_v / 16), kWave)) return KDN_EINVAL;
     const DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
     const size_t need = dw.total;
     const int wc = workspace_check(workspace, workspace_bytes, need);
@@ -250,7 +259,7 @@ int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     }
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
-    if ((N * H + 7) * ntile > kMaxGrid || H * total_T / 256 > kMaxGrid) return KDN_EINVAL;
+    if (!grid_fits((N * H + 7) * ntile)) return KDN_EINVAL;
     const size_t b_scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
     const size_t need = work ? b_scal + align_up(4 * static_cast<size_t>(N), 256) : 0;
     const int wc = workspace_check(workspace, workspace_bytes, need);
@@ -289,7 +298,7 @@ int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_
     }
     if (!ok_opt(lambda0) || !ok_opt(mu0) || !ok_opt(lambda_T) || !ok_opt(mu_T)) return KDN_EINVAL;
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
-    if (BH * ntile > kMaxGrid) return KDN_EINVAL;
+    if (!grid_fits(BH * ntile)) return KDN_EINVAL;
     if (BH == 0) return KDN_OK;
     NoiseParams np{};
     np.q = q; np.k = k; np.v = v; np.beta = beta; np.a = a; np.p = p;
@@ -331,7 +340,7 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const int64_t ci = d_v < 64 ? d_v : 64;
     const int64_t ntile = d_v / ci;
     const int64_t nch = (T + diag_chunk() - 1) / diag_chunk();
-    if (BH * ntile > kMaxGrid || BH > kMaxGrid) return KDN_EINVAL;
+    if (!grid_fits(BH * ntile)) return KDN_EINVAL;
     const size_t f = sizeof(float);
     const size_t b_scal = align_up(16 * static_cast<size_t>(BH) * T, 256);
     const size_t b_ckpt = align_up(f * static_cast<size_t>(BH) * (nch + 1) * 2 * d_k * d_v, 256);
@@ -408,14 +417,14 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
 
     const int64_t blk = mob_block();
     const int64_t nblk = (T + blk - 1) / blk;
-    if (BH * nblk > kMaxGrid) return KDN_EINVAL;
+    if (!grid_fits(BH * nblk)) return KDN_EINVAL;
     const size_t b_blk = align_up(sizeof(float) * static_cast<size_t>(BH) * nblk * 4, 256);
     size_t need = (BH > 0 && T > 0) ? b_blk : 0;
     Plan pl{};
     size_t b_gate = 0;
     if (mean) {
         pl = plan_iso(BH, T, d_v);
-        if (BH * pl.S * iso_tiles(d_v) > kMaxGrid) return KDN_EINVAL;
+        if (!grid_fits(BH * pl.S * iso_tiles(d_v), kWave)) return KDN_EINVAL;
         b_gate = align_up(sizeof(float) * static_cast<size_t>(BH) * T, 256);
         need += 2 * b_gate + scan_workspace_bytes(BH, d_k, d_v, pl);
     }
@@ -466,7 +475,7 @@ int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in
     if (!finite_positive(I_prior)) return KDN_EINVAL;
     if (!sizes_fit(B, H, 1, d_k * d_v)) return KDN_EINVAL;
     const int64_t BH = B * H;
-    if (BH > kMaxGrid) return KDN_EINVAL;
+    if (!grid_fits(BH)) return KDN_EINVAL;
     if (BH == 0) return KDN_OK;
     if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(A) ||
         !ok_ptr(I) || !ok_ptr(mu) || !ok_ptr(o))

@@ -35,6 +35,11 @@
  *     Lambda >= 0, lambda0 > 0).  Under them every precision stays > 0.
  *   - Supported head sizes: d_k, d_v in {16, 32, 64, 128}; other values
  *     return KDN_EUNSUPPORTED.  Every pointer must be 16-byte aligned.
+ *   - Size limits (KDN_EINVAL beyond them): T (or total_T) < 2^31; every
+ *     element count B*H*T*d < 2^62; and one workgroup per head (or per head
+ *     and column tile, segment or 4096-token block, whichever the call
+ *     launches) must leave the grid within 2^32 - 1 work-items at 512
+ *     threads per workgroup, about 8.4 million such units.
  *
  * Workspace protocol (entry points that take one)
  *   - workspace == NULL and workspace_bytes != NULL: write the number of

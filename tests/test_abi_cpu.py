@@ -65,6 +65,26 @@ def test_diag_validation():
     assert _diag(T=0, q=None, k=None, v=None, beta=None, d=None, o=None, **q) == kdn.KDN_OK
 
 
+def test_size_limits():
+    """T below 2^31; one dispatch within 2^32 - 1 work-items (512 threads per
+    head, 64 per composite or isotropic wave)."""
+    n = ctypes.c_size_t(0)
+    assert _diag(T=2 ** 31, nbytes=n) == kdn.KDN_EINVAL
+    assert _diag(T=2 ** 31 - 1, nbytes=n) == kdn.KDN_OK
+    # 2^23 heads of one 16-column tile: 2^32 threads, one past the limit
+    assert _diag(B=2 ** 23, nbytes=n) == kdn.KDN_EINVAL
+    assert _diag(B=2 ** 23 - 1, nbytes=n) == kdn.KDN_OK
+    call = lambda B, T=8: lib.kdn_mobius_precision_scan(B, 1, T, FAKE, FAKE, FAKE, None, FAKE, 0, 0,
+                                                         None, None, None, None, None, None,
+                                                         None, ctypes.byref(n), None)
+    assert call(2 ** 23 - 1) == kdn.KDN_OK
+    assert call(2 ** 23) == kdn.KDN_EINVAL
+    assert call(1, T=2 ** 31) == kdn.KDN_EINVAL
+    dec = lambda B: lib.kdn_decode_step(B, 1, 16, 16, kdn.KDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, 1.0, FAKE, FAKE, FAKE, None)
+    assert dec(2 ** 23) == kdn.KDN_EINVAL
+
+
 def test_diag_workspace_protocol():
     n = ctypes.c_size_t(12345)
     assert _diag(B=8, H=16, T=2048, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
