@@ -46,6 +46,143 @@ namespace kdn {
 
 constexpr int kBwdChunk = 16;   // tokens per chunk: the checkpoint interval
 
+// Recompute schedule of a whole chunk.  The reverse pass needs the state after
+// each token, last token first; only the state before the chunk is stored.
+// With `slots` register-held states, the cheapest order of checkpoint loads,
+// forward steps (in place, or copied into a free slot) and reverse steps was
+// found by a shortest-path search over (tokens left, states held), counting a
+// copy step 1.6 in-place steps (its register moves); recompute_schedule.py in
+// this directory prints these tables.  Against holding `slots` consecutive
+// states rebuilt from the checkpoint each time, 3 slots need 36 steps per 16
+// tokens instead of 61, and 4 slots 30 instead of 40.
+enum : int8_t { kRecLoad = 0, kRecStep = 1, kRecRev = 2 };
+struct RecOp {
+    int8_t kind;   // kRecLoad: checkpoint -> slot dst; kRecStep: token tok from slot src into slot dst
+    int8_t src;    // (src == dst: in place); kRecRev: reverse step of token tok, its state in slot src
+    int8_t dst;
+    int8_t tok;
+};
+template <int SLOTS>
+struct RecSchedule;
+
+// 16 tokens, 3 slots: 36 steps, 13 of them copies, 3 loads (cost 43.95)
+template <>
+struct RecSchedule<3> {
+    static constexpr int N = 55;
+    static constexpr RecOp ops[N] = {
+        {0, 0, 0, -1},
+        {1, 0, 0, 0},
+        {1, 0, 0, 1},
+        {1, 0, 0, 2},
+        {1, 0, 0, 3},
+        {1, 0, 0, 4},
+        {1, 0, 0, 5},
+        {1, 0, 0, 6},
+        {1, 0, 1, 7},
+        {1, 1, 1, 8},
+        {1, 1, 1, 9},
+        {1, 1, 1, 10},
+        {1, 1, 1, 11},
+        {1, 1, 1, 12},
+        {1, 1, 2, 13},
+        {1, 2, 2, 14},
+        {1, 2, 2, 15},
+        {2, 2, 2, 15},
+        {1, 1, 2, 13},
+        {1, 2, 2, 14},
+        {2, 2, 2, 14},
+        {1, 1, 2, 13},
+        {2, 2, 2, 13},
+        {2, 1, 1, 12},
+        {1, 0, 1, 7},
+        {1, 1, 1, 8},
+        {1, 1, 1, 9},
+        {1, 1, 2, 10},
+        {1, 2, 2, 11},
+        {2, 2, 2, 11},
+        {1, 1, 2, 10},
+        {2, 2, 2, 10},
+        {2, 1, 1, 9},
+        {1, 0, 1, 7},
+        {1, 1, 2, 8},
+        {2, 2, 2, 8},
+        {2, 1, 1, 7},
+        {2, 0, 0, 6},
+        {0, 0, 0, -1},
+        {1, 0, 0, 0},
+        {1, 0, 0, 1},
+        {1, 0, 1, 2},
+        {1, 1, 1, 3},
+        {1, 1, 2, 4},
+        {1, 2, 2, 5},
+        {2, 2, 2, 5},
+        {1, 1, 2, 4},
+        {2, 2, 2, 4},
+        {2, 1, 1, 3},
+        {1, 0, 1, 2},
+        {2, 1, 1, 2},
+        {2, 0, 0, 1},
+        {0, 0, 0, -1},
+        {1, 0, 0, 0},
+        {2, 0, 0, 0}};
+};
+
+// 16 tokens, 4 slots: 30 steps, 13 of them copies, 3 loads (cost 37.95)
+template <>
+struct RecSchedule<4> {
+    static constexpr int N = 49;
+    static constexpr RecOp ops[N] = {
+        {0, 0, 0, -1},
+        {1, 0, 0, 0},
+        {1, 0, 0, 1},
+        {1, 0, 0, 2},
+        {1, 0, 0, 3},
+        {1, 0, 0, 4},
+        {1, 0, 0, 5},
+        {1, 0, 0, 6},
+        {1, 0, 1, 7},
+        {1, 1, 1, 8},
+        {1, 1, 1, 9},
+        {1, 1, 1, 10},
+        {1, 1, 2, 11},
+        {1, 2, 2, 12},
+        {1, 2, 2, 13},
+        {1, 2, 3, 14},
+        {1, 3, 3, 15},
+        {2, 3, 3, 15},
+        {1, 2, 3, 14},
+        {2, 3, 3, 14},
+        {2, 2, 2, 13},
+        {1, 1, 2, 11},
+        {1, 2, 3, 12},
+        {2, 3, 3, 12},
+        {2, 2, 2, 11},
+        {2, 1, 1, 10},
+        {1, 0, 1, 7},
+        {1, 1, 2, 8},
+        {1, 2, 3, 9},
+        {2, 3, 3, 9},
+        {2, 2, 2, 8},
+        {2, 1, 1, 7},
+        {2, 0, 0, 6},
+        {0, 0, 0, -1},
+        {1, 0, 0, 0},
+        {1, 0, 0, 1},
+        {1, 0, 1, 2},
+        {1, 1, 1, 3},
+        {1, 1, 2, 4},
+        {1, 2, 3, 5},
+        {2, 3, 3, 5},
+        {2, 2, 2, 4},
+        {2, 1, 1, 3},
+        {1, 0, 1, 2},
+        {2, 1, 1, 2},
+        {2, 0, 0, 1},
+        {0, 0, 0, -1},
+        {1, 0, 0, 0},
+        {2, 0, 0, 0}};
+};
+
 template <int DK, int DV>
 struct BwdShape {
     static constexpr int RH = DK / 64;                 // waves along the key rows
@@ -540,20 +677,49 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const int64_t t0 = c * C;
         const float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, c, nch, nruns);
         const int nheld = (Lc + HELD - 1) / HELD;
+        auto operands = [&](int tt, float& rho, float& bs, float& bvs,
+                            float& kj) __attribute__((always_inline)) {
+            const float4 sc = S.sc[tt];
+            rho = sc.x;
+            kj = S.k[tt][j];
+            const float b = S.b[tt][lc] * sc.z;
+            bvs = dpp_src(b * S.v[tt][lc]);
+            bs = dpp_src(b);
+        };
 
-        for (int m = nheld - 1; m >= 0; --m) {
+        if (Lc == C) {
+            // a whole chunk: the fixed recompute schedule, unrolled (slot
+            // indices and stage offsets are constants)
+            using RS = RecSchedule<HELD>;
+            float sJ[HELD][16], sE[HELD][16];
+            Unroll<0, RS::N>::run([&](auto ii) {
+                constexpr RecOp op = RS::ops[decltype(ii)::value];
+                if constexpr (op.kind == kRecLoad) {
+                    load16_ckpt<Sh::BLK>(ck, lid, sJ[op.dst]);
+                    load16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, sE[op.dst]);
+                } else if constexpr (op.kind == kRecStep) {
+                    float rho, bs, bvs, kj;
+                    operands(op.tok, rho, bs, bvs, kj);
+                    if constexpr (op.src == op.dst)
+                        bwd_step_inplace(sJ[op.dst], sE[op.dst], rho, bs, bvs, kj, kj * kj);
+                    else
+                        bwd_step_copy(sJ[op.src], sE[op.src], sJ[op.dst], sE[op.dst], rho, bs, bvs, kj,
+                                      kj * kj);
+                } else {
+                    reverse_step(S, op.tok, t0, Lc, sJ[op.src], sE[op.src]);
+                }
+                // keep each op's loads and temporaries within the op: hoisting
+                // across ops raises register pressure past the budget
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+
+        // the ragged last chunk: groups of HELD consecutive states, each
+        // rebuilt from the checkpoint
+        for (int m = Lc == C ? -1 : nheld - 1; m >= 0; --m) {
             float sJ[HELD][16], sE[HELD][16];
             load16_ckpt<Sh::BLK>(ck, lid, sJ[0]);
             load16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, sE[0]);
-            auto operands = [&](int tt, float& rho, float& bs, float& bvs,
-                                float& kj) __attribute__((always_inline)) {
-                const float4 sc = S.sc[tt];
-                rho = sc.x;
-                kj = S.k[tt][j];
-                const float b = S.b[tt][lc] * sc.z;
-                bvs = dpp_src(b * S.v[tt][lc]);
-                bs = dpp_src(b);
-            };
             {
                 // software-pipelined like the checkpoint pass
                 const int n = HELD * m;
