@@ -89,10 +89,15 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     static_assert(JP == 4 || JP == 8 || JP == 16, "key rows per lane: one DPP row");
     static_assert(CI >= 16, "a DPP row must stay inside one row group");
     static_assert(C == 16, "per-token scalars are scanned across 16 lanes");
+    // k^2 is staged next to k where the LDS allows it; a workgroup of fewer
+    // than 8 waves must leave room for a second one on its CU (80 KB), and
+    // then squares k per token instead (one multiply per token and lane).
+    constexpr int kLdsK2 = 2 * (3 * C * DK + 2 * C * CI) * 4 + 2 * C * P * CI * 4;
+    constexpr bool K2 = W >= 8 || kLdsK2 <= 80 * 1024;
 
     struct Stage {
         float k[C][DK];
-        float k2[C][DK];
+        float k2[K2 ? C : 1][DK];
         float q[C][DK];
         float2 bv[C][CI];   // (beta_i, v_i)
     };
@@ -218,7 +223,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 #pragma unroll
                 for (int e = 0; e < VW; ++e) {
                     S.k[row][c0 + e] = f[e];
-                    S.k2[row][c0 + e] = f[e] * f[e];
+                    if constexpr (K2) S.k2[row][c0 + e] = f[e] * f[e];
                 }
                 widen<BF16>(rq[n], f);
 #pragma unroll
@@ -310,17 +315,26 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             // the compiler schedules the operand reads ahead by itself
             Unroll<0, C>::run([&](auto u) {
                 constexpr int tt = decltype(u)::value;
-                token(tt, S.bv[tt][col], S.k[tt][jl], S.k2[tt][jl], S.q[tt][jl]);
+                const float vk = S.k[tt][jl];
+                float vk2;
+                if constexpr (K2) vk2 = S.k2[tt][jl];
+                else vk2 = dpp_src(vk * vk);
+                token(tt, S.bv[tt][col], vk, vk2, S.q[tt][jl]);
             });
         } else {
             // the ragged last chunk, software-pipelined over tokens: the next
             // token's LDS operands are loaded while the current one computes
             float2 bvv = S.bv[0][col];
-            float vk = S.k[0][jl], vk2 = S.k2[0][jl], vq = S.q[0][jl];
+            float vk = S.k[0][jl], vk2, vq = S.q[0][jl];
+            if constexpr (K2) vk2 = S.k2[0][jl];
+            else vk2 = dpp_src(vk * vk);
             for (int tt = 0; tt < L; ++tt) {
                 const int tn = tt + 1 < L ? tt + 1 : tt;
                 const float2 bvv_n = S.bv[tn][col];
-                const float vk_n = S.k[tn][jl], vk2_n = S.k2[tn][jl], vq_n = S.q[tn][jl];
+                const float vk_n = S.k[tn][jl], vq_n = S.q[tn][jl];
+                float vk2_n;
+                if constexpr (K2) vk2_n = S.k2[tn][jl];
+                else vk2_n = dpp_src(vk_n * vk_n);
                 token(tt, bvv, vk, vk2, vq);
                 bvv = bvv_n;
                 vk = vk_n;
@@ -522,6 +536,10 @@ static int launch_main(const DiagParams& p, int64_t dk, int CI, int64_t grid, hi
 
 int diag_chunk() { return kDiagChunk; }
 
+// Packed batches run 32-column tiles (two 4-wave workgroups per CU): runs of
+// mixed lengths then finish in finer pieces, which evens out the tail.
+int varlen_cols(int64_t dv) { return dv < 32 ? static_cast<int>(dv) : 32; }
+
 // The plan of a packed batch: sequences ordered longest first (ties by
 // index), by rank counting in one workgroup.  Past kMaxPlanSort sequences
 // the quadratic count is skipped and the order is the identity.
@@ -558,7 +576,7 @@ int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t s
         if (bf16) hipLaunchKernelGGL(k_diag_prep_varlen<true>, grid, dim3(256), 0, st, p);
         else hipLaunchKernelGGL(k_diag_prep_varlen<false>, grid, dim3(256), 0, st, p);
     }
-    const int CI = p.dv < 64 ? static_cast<int>(p.dv) : 64;
+    const int CI = varlen_cols(p.dv);
     const int64_t runs = static_cast<int64_t>(p.nseq) * p.H;
     const int64_t grid = (runs + 7) / 8 * 8 * (p.dv / CI);   // whole groups of 8 runs
     if (grid == 0) return launch_status();

@@ -126,6 +126,7 @@ struct BwdParams {
 };
 
 int diag_chunk();
+int varlen_cols(int64_t dv);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
                     bool bf16, hipStream_t st);
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st);

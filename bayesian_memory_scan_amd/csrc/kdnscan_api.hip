@@ -258,7 +258,7 @@ int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
             return KDN_EINVAL;
     }
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
-    const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
+    const int64_t ntile = d_v / varlen_cols(d_v);
     if (!grid_fits((N * H + 7) * ntile)) return KDN_EINVAL;
     const size_t b_scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
     const size_t need = work ? b_scal + align_up(4 * static_cast<size_t>(N), 256) : 0;
