@@ -208,6 +208,16 @@ struct BwdStage {
     float4 sc[kBwdChunk + 1];              // frame scalars; [L] = next chunk's first token
 };
 
+// One 16-byte vector of a column tile's own operands (beta, v, dout), read
+// exactly once: non-temporal, so that they do not push the chunk checkpoints
+// (read up to three times) out of L2.  k and q are shared by a head's column
+// tiles and stay cached.
+__device__ __forceinline__ uint4 ld16_once(const void* p) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    const u32x4 u = __builtin_nontemporal_load(static_cast<const u32x4*>(p));
+    return make_uint4(u[0], u[1], u[2], u[3]);
+}
+
 // Global -> registers (in flight while the previous chunk computes) -> LDS.
 template <int DK, int CI, int NTH, bool BF16, bool REV>
 struct BwdLoader {
@@ -247,8 +257,8 @@ struct BwdLoader {
             const int cv = vi % (CI / VW);
             if (vi < VB && row < L) {
                 const int64_t off = (t0 + row) * p.dv + cv * VW;
-                rb[n] = bth ? ld16(bth + off) : splat16<BF16>(dh, t0 + row);
-                rv[n] = ld16(vh + off);
+                rb[n] = bth ? ld16_once(bth + off) : splat16<BF16>(dh, t0 + row);
+                rv[n] = ld16_once(vh + off);
             }
         }
         if constexpr (REV) {
@@ -258,8 +268,11 @@ struct BwdLoader {
                 const int vi = tid + n * NTH;
                 const int row = vi / (CI / 4);
                 const int cv = vi % (CI / 4);
-                if (vi < VG && row < L)
-                    rg[n] = *reinterpret_cast<const float4*>(gh + (t0 + row) * p.dv + cv * 4);
+                if (vi < VG && row < L) {
+                    const uint4 u = ld16_once(gh + (t0 + row) * p.dv + cv * 4);
+                    rg[n] = make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z),
+                                        __uint_as_float(u.w));
+                }
             }
         }
         if (tid <= L) {
@@ -392,15 +405,26 @@ __device__ __forceinline__ void store16(float* dst, const float (&x)[16]) {
         reinterpret_cast<float4*>(dst)[n] = make_float4(x[4 * n], x[4 * n + 1], x[4 * n + 2], x[4 * n + 3]);
 }
 
-// A lane's 16 entries inside one checkpoint half of BLK floats, interleaved
-// by float4: float4 n of lane l sits at (n * BLK/16 + l) * 4, so each of the
-// four vector accesses of a wave covers 1 KB of contiguous memory.
+// A lane's 16 entries inside one checkpoint half of BLK floats are
+// interleaved by float4: float4 n of lane l sits at (n * BLK/16 + l) * 4, so
+// each of the four vector accesses of a wave covers 1 KB of contiguous memory.
+//
+// Both halves (J, then eta) of a lane's 16 entries in checkpoint slot `slot`,
+// through one buffer resource: the lane's offset is one VGPR and the float4
+// offsets are scalar, so no 64-bit addresses stay live between the loads.
 template <int BLK>
-__device__ __forceinline__ void load16_ckpt(const float* half, int64_t l, float (&x)[16]) {
+__device__ __forceinline__ void load_ckpt(const float* slot, int64_t l, float (&J)[16], float (&E)[16]) {
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(slot, 2 * BLK * 4);
+    const uint32_t vo = static_cast<uint32_t>(l) * 16;
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        const float4 f = reinterpret_cast<const float4*>(half)[n * (BLK / 16) + l];
-        x[4 * n] = f.x; x[4 * n + 1] = f.y; x[4 * n + 2] = f.z; x[4 * n + 3] = f.w;
+        const auto a = __builtin_amdgcn_raw_buffer_load_b128(r, vo, n * BLK, 0);
+        const auto b = __builtin_amdgcn_raw_buffer_load_b128(r, vo, 4 * BLK + n * BLK, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            J[4 * n + i] = __uint_as_float(a[i]);
+            E[4 * n + i] = __uint_as_float(b[i]);
+        }
     }
 }
 
@@ -577,8 +601,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         // final state (J_T, eta_T) unscaled after the last chunk.
         float JT[16], ET[16];
         const float* ckT = ckpt_slot<Sh::BLK>(p.ckpt, run, nch, nch, nruns);
-        load16_ckpt<Sh::BLK>(ckT, lid, JT);
-        load16_ckpt<Sh::BLK>(ckT + Sh::BLK, lid, ET);
+        load_ckpt<Sh::BLK>(ckT, lid, JT, ET);
         const float inv_s = 1.0f / uniform(p.scal[bh * T + T - 1].z);
         Unroll<0, 16>::run([&](auto cc) {
             constexpr int c = decltype(cc)::value;
@@ -695,8 +718,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             Unroll<0, RS::N>::run([&](auto ii) {
                 constexpr RecOp op = RS::ops[decltype(ii)::value];
                 if constexpr (op.kind == kRecLoad) {
-                    load16_ckpt<Sh::BLK>(ck, lid, sJ[op.dst]);
-                    load16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, sE[op.dst]);
+                    load_ckpt<Sh::BLK>(ck, lid, sJ[op.dst], sE[op.dst]);
                 } else if constexpr (op.kind == kRecStep) {
                     float rho, bs, bvs, kj;
                     operands(op.tok, rho, bs, bvs, kj);
@@ -718,8 +740,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         // rebuilt from the checkpoint
         for (int m = Lc == C ? -1 : nheld - 1; m >= 0; --m) {
             float sJ[HELD][16], sE[HELD][16];
-            load16_ckpt<Sh::BLK>(ck, lid, sJ[0]);
-            load16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, sE[0]);
+            load_ckpt<Sh::BLK>(ck, lid, sJ[0], sE[0]);
             {
                 // software-pipelined like the checkpoint pass
                 const int n = HELD * m;
