@@ -369,6 +369,306 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     }
 }
 
+// The same scan for 64-column tiles with a block of RB key rows x 2 value
+// columns per lane and every multiplicand in a VGPR.  A wave holds 2*RB key
+// rows: lanes 0-31 the first RB, lanes 32-63 the next RB, lane l % 32 the
+// column pair (2c, 2c+1).  At d_k = 128, RB = 4 gives 16-wave workgroups,
+// four waves per SIMD: a wave issues a VALU instruction at most every few
+// clocks, so the SIMD needs several waves to keep its VALU busy, and a
+// 64-column tile of a head is all the work one workgroup has.
+//   * Staging folds the frame scale into the key side (s_t k_t[j] and
+//     s_t k_t[j]^2) and pairs beta with beta*v, so a token's operands are
+//     four LDS vector reads per lane (three shared by half a wave), loaded
+//     while the previous token computes.
+//   * Per entry: two fmacs for the updates, the prior increment (held in a
+//     VGPR: an SGPR operand halves the issue rate), the reciprocal, the
+//     quotient and the read-out fmac; no DPP or SGPR multiplicands.
+//   * The two row blocks of a column are summed by one v_permlane32_swap;
+//     the waves' partial read-outs go through LDS once per chunk, single-
+//     buffered (with a second barrier) when 16 waves' worth would not fit
+//     next to the stage.
+template <int DK, int RB, int C, bool BF16>
+__global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p) {
+    using E = typename std::conditional<BF16, uint16_t, float>::type;
+    constexpr int CI = 64;
+    constexpr int W = DK / (2 * RB);     // waves: 2*RB key rows each
+    constexpr int NTH = W * kWave;
+    constexpr int P = W;                 // row groups of the read-out: one per wave
+    // partial read-outs double-buffered while they fit next to the stage
+    constexpr int NOB = W > 8 ? 1 : 2;
+    constexpr int VW = BF16 ? 8 : 4;
+    constexpr int VK = C * DK / VW;
+    constexpr int VB = C * CI / VW;
+    constexpr int NVK = (VK + NTH - 1) / NTH;
+    constexpr int NVB = (VB + NTH - 1) / NTH;
+    static_assert(RB == 4 || RB == 8, "key rows per lane");
+    static_assert(DK % (2 * RB) == 0 && NTH <= 1024, "tile shape");
+    static_assert(C == 16, "per-token scalars come in 16-token chunks");
+
+    struct Stage {
+        float ks[C][DK];    // s_t k_t[j]
+        float k2s[C][DK];   // s_t k_t[j]^2
+        float q[C][DK];
+        float2 bv[C][CI];   // (beta_i, beta_i v_i)
+    };
+    __shared__ Stage stg[2];
+    __shared__ float opart[NOB][C][P][CI];
+
+    const int tid = threadIdx.x;
+    const int lane = tid % kWave;
+    const int wv = tid / kWave;
+    const int half = lane / 32;          // which RB-row block of the wave's 2*RB rows
+    const int cp = lane % 32;            // column pair
+    const int j0 = wv * 2 * RB + half * RB;
+    const int ocol = 2 * cp + half;      // the column whose read-out partial this lane ends with
+    const int ntile = static_cast<int>(p.dv / CI);
+    int64_t wg = xcd_local_id();
+    const int tile = static_cast<int>(wg % ntile);
+    wg /= ntile;
+    const int i0 = tile * CI + 2 * cp;
+    const int seg = static_cast<int>(wg % p.S);
+    const int64_t bh = wg / p.S;
+    int64_t t_begin, t_end;
+    segment_tokens(p, C, seg, t_begin, t_end);
+
+    const float I_prior = p.I_prior;
+    const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
+    const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
+    const E* vh = static_cast<const E*>(p.v) + bh * p.T * p.dv + tile * CI;
+    const E* bth = p.beta ? static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI : nullptr;
+    const E* dh = static_cast<const E*>(p.d) + bh * p.T;
+
+    float I[RB][2], eta[RB][2];
+    if (p.S == 1) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t off = (bh * DK + j0 + r) * p.dv + i0;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const float m0 = p.mu0 ? p.mu0[off + c] : 0.0f;
+                const float I0 = p.I0 ? p.I0[off + c] : I_prior;
+                I[r][c] = I0;
+                eta[r][c] = I0 * m0;
+            }
+        }
+    } else {
+        const float* cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i0;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                I[r][c] = I_prior + cin[off + c];
+                eta[r][c] = cin[static_cast<int64_t>(DK) * p.dv + off + c];
+            }
+        }
+    }
+
+    uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
+    float rs[NVK];
+    float s_prev = 1.0f;
+    const float4* sch = p.scal + bh * p.T;
+    typedef __attribute__((address_space(4))) const float scalar_f32;
+    auto frame_scalars = [&](int64_t t0) { return (scalar_f32*)(uintptr_t)(sch + t0); };
+
+    auto fetch = [&](int64_t t0, int L) {
+#pragma unroll
+        for (int n = 0; n < NVK; ++n) {
+            const int vi = tid + n * NTH;
+            if (vi < VK && vi * VW < L * DK) {
+                rk[n] = ld16(kh + t0 * DK + static_cast<int64_t>(vi) * VW);
+                rq[n] = ld16(qh + t0 * DK + static_cast<int64_t>(vi) * VW);
+                rs[n] = sch[t0 + vi * VW / DK].z;
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVB; ++n) {
+            const int vi = tid + n * NTH;
+            const int row = vi / (CI / VW);
+            const int cv = vi % (CI / VW);
+            if (vi < VB && row < L) {
+                const int64_t off = (t0 + row) * p.dv + cv * VW;
+                rb[n] = bth ? ld16(bth + off) : splat16<BF16>(dh, t0 + row);
+                rv[n] = ld16(vh + off);
+            }
+        }
+    };
+
+    auto commit = [&](int nb, int L) {
+        Stage& S = stg[nb];
+#pragma unroll
+        for (int n = 0; n < NVK; ++n) {
+            const int vi = tid + n * NTH;
+            if (vi < VK && vi * VW < L * DK) {
+                const int row = vi * VW / DK;
+                const int c0 = vi * VW % DK;
+                float f[VW];
+                widen<BF16>(rk[n], f);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) {
+                    const float ks = f[e] * rs[n];
+                    S.ks[row][c0 + e] = ks;
+                    S.k2s[row][c0 + e] = ks * f[e];
+                }
+                widen<BF16>(rq[n], f);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
+            }
+        }
+#pragma unroll
+        for (int n = 0; n < NVB; ++n) {
+            const int vi = tid + n * NTH;
+            const int row = vi / (CI / VW);
+            const int c0 = (vi % (CI / VW)) * VW;
+            if (vi < VB && row < L) {
+                float fv[VW], fb[VW];
+                widen<BF16>(rv[n], fv);
+                widen<BF16>(rb[n], fb);
+#pragma unroll
+                for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fb[e] * fv[e]);
+            }
+        }
+    };
+
+    const int64_t nch = (t_end - t_begin + C - 1) / C;
+    auto chunk_len = [&](int64_t c) -> int {
+        const int64_t rem = t_end - (t_begin + c * C);
+        return static_cast<int>(rem < C ? rem : C);
+    };
+
+    if (nch > 0) {
+        fetch(t_begin, chunk_len(0));
+        commit(0, chunk_len(0));
+    }
+    __syncthreads();
+    if (nch > 1) fetch(t_begin + C, chunk_len(1));
+
+    for (int64_t c = 0; c < nch; ++c) {
+        const int b = static_cast<int>(c & 1);
+        const int L = chunk_len(c);
+        const int64_t t0 = t_begin + c * C;
+        const Stage& S = stg[b];
+        const float inv_sp = 1.0f / s_prev;
+        scalar_f32* const cs = frame_scalars(t0);
+
+        // A token's operands: RB key rows of s k, s k^2 and q (shared by
+        // half a wave) and the lane's (beta, beta v) column pair.
+        struct Ops {
+            float4 k[RB / 4], k2[RB / 4], q[RB / 4];
+            float4 bv;
+        };
+        auto load_ops = [&](int tt) __attribute__((always_inline)) {
+            Ops o;
+            const float4* kp = reinterpret_cast<const float4*>(&S.ks[tt][j0]);
+            const float4* k2p = reinterpret_cast<const float4*>(&S.k2s[tt][j0]);
+            const float4* qp = reinterpret_cast<const float4*>(&S.q[tt][j0]);
+#pragma unroll
+            for (int h = 0; h < RB / 4; ++h) {
+                o.k[h] = kp[h];
+                o.k2[h] = k2p[h];
+                o.q[h] = qp[h];
+            }
+            o.bv = *reinterpret_cast<const float4*>(&S.bv[tt][2 * cp]);
+            return o;
+        };
+        auto lane_of = [](const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; };
+        // One token from its operands and its frame scalars (rho as bits, the
+        // prior increment dP): frame change, state update, read-out partial.
+        auto token = [&](int tt, const Ops& o, uint32_t rho_bits, float dP) __attribute__((always_inline)) {
+            if (rho_bits != 0x3f800000u) {
+                const float rho = __uint_as_float(rho_bits);
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) {
+                        I[r][cc] *= rho;
+                        eta[r][cc] *= rho;
+                    }
+            }
+            const float bet[2] = {o.bv.x, o.bv.z};
+            const float bvv[2] = {o.bv.y, o.bv.w};
+            float acc[2];
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const float kk = lane_of(o.k[r / 4], r % 4);
+                const float k2 = lane_of(o.k2[r / 4], r % 4);
+                const float qq = lane_of(o.q[r / 4], r % 4);
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) {
+                    I[r][cc] = __builtin_fmaf(k2, bet[cc], I[r][cc]) + dP;
+                    eta[r][cc] = __builtin_fmaf(kk, bvv[cc], eta[r][cc]);
+                    const float m = eta[r][cc] * fast_rcp(I[r][cc]);
+                    acc[cc] = r == 0 ? qq * m : __builtin_fmaf(qq, m, acc[cc]);
+                }
+            }
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]), __float_as_uint(acc[1]), false, false);
+            opart[b % NOB][tt][wv][ocol] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        };
+        auto rho_at = [&](int tt) -> uint32_t {
+            return tt == 0 ? __builtin_amdgcn_readfirstlane(__float_as_uint(cs[0] * inv_sp))
+                           : __float_as_uint(cs[4 * tt]);
+        };
+        // the prior increment in a VGPR: an SGPR operand halves the issue
+        // rate of the adds that read it
+        auto dP_at = [&](int tt) { return vgpr_copy(cs[4 * tt + 1]); };
+
+        if (L == C) {
+            // a whole chunk, unrolled; each token's LDS operands and frame
+            // scalars are loaded while the previous token computes
+            Ops cur = load_ops(0);
+            uint32_t rho_c = rho_at(0);
+            float dP_c = dP_at(0);
+            Unroll<0, C>::run([&](auto u) {
+                constexpr int tt = decltype(u)::value;
+                Ops nxt;
+                uint32_t rho_n = 0;
+                float dP_n = 0.0f;
+                if constexpr (tt + 1 < C) {
+                    nxt = load_ops(tt + 1);
+                    rho_n = rho_at(tt + 1);
+                    dP_n = dP_at(tt + 1);
+                }
+                token(tt, cur, rho_c, dP_c);
+                if constexpr (tt + 1 < C) {
+                    cur = nxt;
+                    rho_c = rho_n;
+                    dP_c = dP_n;
+                }
+            });
+        } else {
+            for (int tt = 0; tt < L; ++tt) token(tt, load_ops(tt), rho_at(tt), dP_at(tt));
+        }
+
+        s_prev = cs[4 * (L - 1) + 2];
+        if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
+        __syncthreads();
+        for (int e = tid; e < L * CI; e += NTH) {
+            const int tt = e / CI;
+            const int cc = e % CI;
+            float sum = 0.0f;
+#pragma unroll
+            for (int g = 0; g < P; ++g) sum += opart[b % NOB][tt][g][cc];
+            p.o[(bh * p.T + t0 + tt) * p.dv + tile * CI + cc] = sum;
+        }
+        // one partial buffer: every sum is read before the next chunk writes it
+        if (NOB == 1) __syncthreads();
+        if (c + 2 < nch) fetch(t0 + 2 * C, chunk_len(c + 2));
+    }
+
+    const float s_last = s_prev;
+    if (seg == p.S - 1) {
+#pragma unroll
+        for (int r = 0; r < RB; ++r) {
+            const int64_t off = (bh * DK + j0 + r) * p.dv + i0;
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+                if (p.I_T) p.I_T[off + cc] = I[r][cc] / s_last;
+                if (p.mu_T) p.mu_T[off + cc] = eta[r][cc] / I[r][cc];
+            }
+        }
+    }
+}
+
 // Per-token scalars of the scaled frame, one thread per 16-token chunk of a
 // head, walking its tokens in order: alpha = exp(-A d), the frame cuts (a
 // frame starts at the chunk's first token and wherever the log-growth since
@@ -514,6 +814,12 @@ static void launch_one(const DiagParams& p, int64_t grid, hipStream_t st) {
 
 template <int DK, bool BF16>
 static int launch_dk(const DiagParams& p, int CI, int64_t grid, hipStream_t st) {
+    if (CI == 64 && !p.cu_seqlens) {
+        constexpr int RB = DK >= 64 ? 4 : 8;
+        hipLaunchKernelGGL((k_diag_blk<DK, RB, kDiagChunk, BF16>), dim3(static_cast<uint32_t>(grid)),
+                           dim3(DK / (2 * RB) * kWave), 0, st, p);
+        return KDN_OK;
+    }
     switch (CI) {
         case 16: launch_one<DK, 16, BF16>(p, grid, st); break;
         case 32: launch_one<DK, 32, BF16>(p, grid, st); break;

@@ -37,6 +37,15 @@ __device__ __forceinline__ void scale_inplace(float& x, float s) {
     asm("v_mul_f32 %0, %1, %0" : "+v"(x) : "s"(s));
 }
 
+// A wave-uniform value copied into a VGPR.  VALU instructions with an SGPR
+// operand issue at half the rate of all-VGPR ones on gfx950, so a scalar
+// read by many instructions is moved once.
+__device__ __forceinline__ float vgpr_copy(float s) {
+    float v;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(v) : "s"(s));
+    return v;
+}
+
 // Compile-time loop N, N+1, ..., END-1 (register arrays need constant indices).
 template <int N, int END>
 struct Unroll {
