@@ -94,6 +94,21 @@ def test_diag_composite_head_sizes(kdn, dk, dv):
     gu.compare_diag(inp, res, _all_heads(1, 2), what=f"composite dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("S", [1, 2])
+@pytest.mark.parametrize("dv", [32, 128])
+def test_diag_frame_restarts_inside_chunks(kdn, dv, S):
+    """Fast decays: A = 6 gives about 5 nats of decay per token, so the scaled
+    frame restarts two or three times inside every 16-token chunk (not only at
+    chunk starts), in the 64-column block kernel (d_v = 128) and the narrow-tile
+    kernel (d_v = 32), with a ragged last chunk and with composites (S = 2)."""
+    kdn.kdn_set_diag_segments(S)
+    inp = synth.diag_inputs(gu.diag_spec(1, 2, 203, 128, dv, "bf16", seed=8100 + dv))
+    inp["A"] = np.full_like(inp["A"], 6.0)
+    print(f"diag frame restarts dv={dv} S={S}", flush=True)
+    res = _run_diag(kdn, gu.upload_diag(inp))
+    gu.compare_diag(inp, res, _all_heads(1, 2), what=f"frame restarts dv={dv} S={S}")
+
+
 @pytest.mark.parametrize("S", [1, 4])
 def test_diag_initial_state(kdn, S):
     """Nonzero starting state (I0 != I_prior, mu0 != 0), both segmentings."""
