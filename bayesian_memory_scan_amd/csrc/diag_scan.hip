@@ -422,14 +422,38 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     const int j0 = wv * 2 * RB + half * RB;
     const int ocol = 2 * cp + half;      // the column whose read-out partial this lane ends with
     const int ntile = static_cast<int>(p.dv / CI);
-    int64_t wg = xcd_local_id();
-    const int tile = static_cast<int>(wg % ntile);
-    wg /= ntile;
+    // Packed variable-length batch: runs follow the plan's longest-first
+    // order in groups of 8 runs x ntile tiles, a run's tiles 8 blocks apart
+    // (so on one XCD), as in k_diag.  Otherwise XCD-local ids.
+    int64_t wg;
+    int tile;
+    if (p.cu_seqlens) {
+        const int64_t blk = blockIdx.x;
+        const int64_t within = blk % (8 * ntile);
+        tile = static_cast<int>(within / 8);
+        wg = blk / (8 * ntile) * 8 + within % 8;
+        if (wg >= static_cast<int64_t>(p.nseq) * p.H) return;   // padding of the last group
+    } else {
+        wg = xcd_local_id();
+        tile = static_cast<int>(wg % ntile);
+        wg /= ntile;
+    }
     const int i0 = tile * CI + 2 * cp;
-    const int seg = static_cast<int>(wg % p.S);
-    const int64_t bh = wg / p.S;
-    int64_t t_begin, t_end;
-    segment_tokens(p, C, seg, t_begin, t_end);
+    // bh: head of the token inputs; sb: slot of this run's starting/final state
+    int seg;
+    int64_t bh, sb, t_begin, t_end;
+    if (p.cu_seqlens) {
+        bh = wg % p.H;
+        const int32_t sq = p.seq_order[wg / p.H];
+        sb = static_cast<int64_t>(sq) * p.H + bh;
+        seg = 0;
+        sequence_tokens(p, sq, t_begin, t_end);
+    } else {
+        seg = static_cast<int>(wg % p.S);
+        bh = wg / p.S;
+        sb = bh;
+        segment_tokens(p, C, seg, t_begin, t_end);
+    }
 
     const float I_prior = p.I_prior;
     const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
@@ -442,7 +466,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     if (p.S == 1) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int64_t off = (bh * DK + j0 + r) * p.dv + i0;
+            const int64_t off = (sb * DK + j0 + r) * p.dv + i0;
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
                 const float m0 = p.mu0 ? p.mu0[off + c] : 0.0f;
@@ -659,7 +683,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     if (seg == p.S - 1) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
-            const int64_t off = (bh * DK + j0 + r) * p.dv + i0;
+            const int64_t off = (sb * DK + j0 + r) * p.dv + i0;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
                 if (p.I_T) p.I_T[off + cc] = I[r][cc] / s_last;
@@ -814,7 +838,7 @@ static void launch_one(const DiagParams& p, int64_t grid, hipStream_t st) {
 
 template <int DK, bool BF16>
 static int launch_dk(const DiagParams& p, int CI, int64_t grid, hipStream_t st) {
-    if (CI == 64 && !p.cu_seqlens) {
+    if (CI == 64) {
         constexpr int RB = DK >= 64 ? 4 : 8;
         hipLaunchKernelGGL((k_diag_blk<DK, RB, kDiagChunk, BF16>), dim3(static_cast<uint32_t>(grid)),
                            dim3(DK / (2 * RB) * kWave), 0, st, p);
@@ -842,9 +866,9 @@ static int launch_main(const DiagParams& p, int64_t dk, int CI, int64_t grid, hi
 
 int diag_chunk() { return kDiagChunk; }
 
-// Packed batches run 32-column tiles (two 4-wave workgroups per CU): runs of
-// mixed lengths then finish in finer pieces, which evens out the tail.
-int varlen_cols(int64_t dv) { return dv < 32 ? static_cast<int>(dv) : 32; }
+// Packed batches run the block kernel's 64-column tiles where the head is
+// that wide, else 32- or d_v-column tiles.
+int varlen_cols(int64_t dv) { return dv >= 64 ? 64 : (dv < 32 ? static_cast<int>(dv) : 32); }
 
 // The plan of a packed batch: sequences ordered longest first (ties by
 // index), by rank counting in one workgroup.  Past kMaxPlanSort sequences

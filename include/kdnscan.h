@@ -110,7 +110,8 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
  *   Outputs: o [H,total_T,d_v]; I_T, mu_T [N,H,d_k,d_v] or NULL.
  *   Workspace: 16 bytes per (head, packed token) of frame scalars, plus the
  *   plan (4 bytes per sequence).
- * Work plan: one workgroup per (sequence, head, 32-column tile), chunks of 16
+ * Work plan: one workgroup per (sequence, head, column tile: 64 columns, or
+ * 32 / d_v columns when d_v < 64), chunks of 16
  * tokens aligned to each sequence start, dispatched longest sequence first
  * (the order is computed on the device from cu_seqlens; up to 16384
  * sequences, beyond that in index order).
