@@ -25,7 +25,6 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 template <int DK, int DV, bool BF16>
 __global__ __launch_bounds__((DK * DV / 4 < 512 ? DK * DV / 4 : 512))
 void k_decode(DecodeParams p) {
-    using E = typename std::conditional<BF16, uint16_t, float>::type;
     constexpr int NTH = DK * DV / 4 < 512 ? DK * DV / 4 : 512;
     constexpr int CG = DV / 4;            // float4 column groups per row
     constexpr int RG = NTH / CG;          // row groups
@@ -48,6 +47,30 @@ void k_decode(DecodeParams p) {
     f32x4* I4 = reinterpret_cast<f32x4*>(p.I + bh * DK * DV);
     f32x4* M4 = reinterpret_cast<f32x4*>(p.mu + bh * DK * DV);
 
+    // Every small per-token input is loaded first, before the state and so
+    // before the first state store.  vmcnt counts loads and stores in issue
+    // order, and the compiler cannot move a load of k or q above a store of
+    // the state (it cannot rule out aliasing), so a load left inside the row
+    // loop would wait for the previous row's stores to complete.
+    const float dval = load(p.d, bh);
+    // beta == NULL: Palimpsa-M gating, beta[i] = d (the source is selected,
+    // not branched on, so that the loads issue back to back)
+    const void* bsrc = p.beta ? p.beta : p.d;
+    const int64_t b0 = p.beta ? bh * DV + cg * 4 : bh;
+    const int bst = p.beta ? 1 : 0;
+    float bcol[4], bvcol[4], kr[NF], qr[NF];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const float b = load(bsrc, b0 + e * bst);
+        bcol[e] = b;
+        bvcol[e] = b * load(p.v, bh * DV + cg * 4 + e);
+    }
+#pragma unroll
+    for (int n = 0; n < NF; ++n) {
+        const int j = r0 + n * RG;
+        kr[n] = load(p.k, bh * DK + j);
+        qr[n] = load(p.q, bh * DK + j);
+    }
     f32x4 Iv[NF], Mv[NF];
 #pragma unroll
     for (int n = 0; n < NF; ++n) {
@@ -56,23 +79,15 @@ void k_decode(DecodeParams p) {
         Mv[n] = __builtin_nontemporal_load(&M4[j * CG + cg]);
     }
 
-    const float alpha = fast_exp(-p.A[h] * load(p.d, bh));
+    const float alpha = fast_exp(-p.A[h] * dval);
     const float c = (1.0f - alpha) * p.I_prior;
-    float bcol[4], bvcol[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        // beta == NULL: Palimpsa-M gating, beta[i] = d
-        const float b = p.beta ? load(p.beta, bh * DV + cg * 4 + e) : load(p.d, bh);
-        bcol[e] = b;
-        bvcol[e] = b * load(p.v, bh * DV + cg * 4 + e);
-    }
 
     float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int n = 0; n < NF; ++n) {
         const int j = r0 + n * RG;
-        const float kj = load(p.k, bh * DK + j);
-        const float qj = load(p.q, bh * DK + j);
+        const float kj = kr[n];
+        const float qj = qr[n];
         const float k2 = kj * kj;
         float Io[4] = {Iv[n][0], Iv[n][1], Iv[n][2], Iv[n][3]};
         float Mo[4] = {Mv[n][0], Mv[n][1], Mv[n][2], Mv[n][3]};
