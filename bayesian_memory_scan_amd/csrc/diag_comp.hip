@@ -106,6 +106,7 @@ void k_diag_comp(DiagParams p, int32_t R) {
         float k[4][MT];     // k_s[MT c + m]
         float b[4][NT];     // beta_s[cb + NT c + n]
         float v[4][NT];     // v_s[cb + NT c + n]
+        float d[4];         // d_s (the input gate under Palimpsa-M gating)
         float ad;           // A d of token t0 + c (0 past the end)
     };
     auto load = [&](int64_t t0, Ops& x) __attribute__((always_inline)) {
@@ -113,20 +114,21 @@ void k_diag_comp(DiagParams p, int32_t R) {
         const int64_t L = (t0 < t_begin || L0 < 0) ? 0 : (L0 < C ? L0 : C);   // 0: nothing is read
         const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kh + t0 * DK, L * DK * ES);
         const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vh + t0 * DV, L * DV * ES);
-        const __amdgpu_buffer_rsrc_t rb = bth ? buf_rsrc(bth + t0 * DV, L * DV * ES) : buf_rsrc(dh + t0, L * ES);
+        // beta and d are both loaded, with no branch (compute() picks d under
+        // Palimpsa-M gating): a load behind a branch makes the compiler wait
+        // for every load in flight, the prefetched chunk's included.  Without
+        // beta its resource is empty, so those loads return 0 and read nothing.
+        const __amdgpu_buffer_rsrc_t rb = bth ? buf_rsrc(bth + t0 * DV, L * DV * ES) : buf_rsrc(dh, 0);
+        const __amdgpu_buffer_rsrc_t rd = buf_rsrc(dh + t0, L * ES);
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
             const int s_ = 4 * g + kk;
             buf_load_widen<E, MT>(rk, static_cast<uint32_t>((s_ * DK + MT * c) * ES), x.k[kk]);
             buf_load_widen<E, NT>(rv, static_cast<uint32_t>((s_ * DV + cb + NT * c) * ES), x.v[kk]);
-            if (bth) {
-                buf_load_widen<E, NT>(rb, static_cast<uint32_t>((s_ * DV + cb + NT * c) * ES), x.b[kk]);
-            } else {
-                float d1[1];
-                buf_load_widen<E, 1>(rb, static_cast<uint32_t>(s_ * ES), d1);
-#pragma unroll
-                for (int n = 0; n < NT; ++n) x.b[kk][n] = d1[0];
-            }
+            buf_load_widen<E, NT>(rb, static_cast<uint32_t>((s_ * DV + cb + NT * c) * ES), x.b[kk]);
+            float d1[1];
+            buf_load_widen<E, 1>(rd, static_cast<uint32_t>(s_ * ES), d1);
+            x.d[kk] = d1[0];
         }
         float ad[1];
         buf_load<1>(buf_rsrc(sch + t0, L * 16), static_cast<uint32_t>(c * 16 + 12), ad);
@@ -146,11 +148,15 @@ void k_diag_comp(DiagParams p, int32_t R) {
         float ws[4];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) ws[kk] = __shfl(wt, 16 * g + 4 * g + kk);
-        float bv[4][NT];
+        // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
+        float bs[4][NT], bv[4][NT];
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-            for (int n = 0; n < NT; ++n) bv[kk][n] = x.b[kk][n] * x.v[kk][n];
+            for (int n = 0; n < NT; ++n) {
+                bs[kk][n] = bth ? x.b[kk][n] : x.d[kk];
+                bv[kk][n] = bs[kk][n] * x.v[kk][n];
+            }
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
             float wk[4], wk2[4];
@@ -165,7 +171,7 @@ void k_diag_comp(DiagParams p, int32_t R) {
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int n = 0; n < NT; ++n) {
-                    J[m][n] = mfma4c(wk2[kk], x.b[kk][n], J[m][n]);
+                    J[m][n] = mfma4c(wk2[kk], bs[kk][n], J[m][n]);
                     X[m][n] = mfma4c(wk[kk], bv[kk][n], X[m][n]);
                 }
         }
