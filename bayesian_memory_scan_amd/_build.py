@@ -1,4 +1,5 @@
-"""Build libkdnscan.so (gfx950 only) in-tree with hipcc.
+"""Build libkdnscan.so (gfx950 only) in-tree with hipcc, and next to it the
+measurement-only issue-rate probe libkdnprobe.so.
 
 Every translation unit is compiled for gfx950 with packed fp32 math disabled
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``), then linked into one
@@ -14,6 +15,9 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkdnscan.so")
+# measurement-only library (issue-rate probe); not linked into libkdnscan
+PROBE_LIB = os.path.join(HERE, "libkdnprobe.so")
+PROBE_SOURCES = ["issue_rates.hip"]
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -84,15 +88,16 @@ def build(verbose: bool = False) -> str:
             raise RuntimeError(f"DPP read-after-write hazard in {src}:\n" + "\n".join(hz[:10]))
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp,
-           *objs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    with ThreadPoolExecutor(len(SOURCES) + len(PROBE_SOURCES)) as ex:
+        objs = list(ex.map(compile_one, SOURCES + PROBE_SOURCES))
+    for out, group in ((LIB, objs[:len(SOURCES)]), (PROBE_LIB, objs[len(SOURCES):])):
+        tmp = out + ".tmp"
+        cmd = [HIPCC, "--offload-arch=gfx950", "-mcode-object-version=5", "-shared", "-fPIC", "-o", tmp,
+               *group]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.run(cmd, check=True)
+        os.replace(tmp, out)
     return LIB
 
 

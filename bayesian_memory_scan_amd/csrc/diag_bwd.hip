@@ -1035,7 +1035,7 @@ int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64
                     hipStream_t st) {
     if (p.BH > 0) {
         if (p.T > 0) {
-            const int rc = diag_prep_launch(prep, B, bf16, st);
+            const int rc = diag_prep_launch(prep, B, bf16, false, st);
             if (rc != KDN_OK) return rc;
         }
         int rc;

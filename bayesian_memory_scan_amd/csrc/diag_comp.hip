@@ -44,19 +44,7 @@ __device__ __forceinline__ f32x4c mfma4c(float a, float b, f32x4c c) {
 constexpr int kCompCols = 32;   // value columns per wave: 2 x MT x 2 x 4 accumulator registers
 
 // Column tiles of one head in the composite pass.
-static inline int comp_tiles(int64_t dv) { return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1; }
-
-// Token range of sub-segment r of segment s: the segment's chunks split in R.
-__device__ __forceinline__ void sub_tokens(const DiagParams& p, int C, int R, int s, int r,
-                                           int64_t& t0, int64_t& t1) {
-    const int64_t c0 = static_cast<int64_t>(s) * p.nchunks / p.S;
-    const int64_t c1 = static_cast<int64_t>(s + 1) * p.nchunks / p.S;
-    const int64_t n = c1 - c0;
-    const int64_t a = c0 + static_cast<int64_t>(r) * n / R;
-    const int64_t b = c0 + static_cast<int64_t>(r + 1) * n / R;
-    t0 = a * C;
-    t1 = b * C < p.T ? b * C : p.T;
-}
+int comp_tiles(int64_t dv) { return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1; }
 
 template <int DK, int NC, bool BF16>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(BF16 || DK < 128 ? 2 : 1)))
@@ -81,6 +69,7 @@ void k_diag_comp(DiagParams p, int32_t R) {
     const int sub = sr % R;
     int64_t t_begin, t_end;
     sub_tokens(p, C, R, seg, sub, t_begin, t_end);
+    if (lane == 0) echo_bounds(p, blockIdx.x, 2, bh, seg, sub, t_begin, t_end, tile);
     const int64_t DV = p.dv;
     const int64_t cb = static_cast<int64_t>(tile) * NC;
 

@@ -32,38 +32,6 @@
 
 namespace kdn {
 
-// Packed variable-length batch: tokens of sequence s, [cu[s], cu[s+1]),
-// clamped into [0, T] so that a malformed offset table cannot send a
-// workgroup out of bounds.
-__device__ __forceinline__ void sequence_tokens(const DiagParams& p, int32_t s, int64_t& t0,
-                                                int64_t& t1) {
-    int64_t a = p.cu_seqlens[s], b = p.cu_seqlens[s + 1];
-    a = a < 0 ? 0 : (a > p.T ? p.T : a);
-    b = b < a ? a : (b > p.T ? p.T : b);
-    t0 = a;
-    t1 = b;
-}
-
-// The sequence holding packed token t: the last s with cu[s] <= t.
-__device__ __forceinline__ int32_t find_sequence(const DiagParams& p, int64_t t) {
-    int32_t lo = 0, hi = p.nseq;
-    while (hi - lo > 1) {
-        const int32_t mid = (lo + hi) / 2;
-        if (p.cu_seqlens[mid] <= t) lo = mid;
-        else hi = mid;
-    }
-    return lo;
-}
-
-// Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S).
-__device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
-                                               int64_t& t0, int64_t& t1) {
-    const int64_t c0 = static_cast<int64_t>(seg) * p.nchunks / p.S;
-    const int64_t c1 = static_cast<int64_t>(seg + 1) * p.nchunks / p.S;
-    t0 = c0 * C;
-    t1 = c1 * C < p.T ? c1 * C : p.T;
-}
-
 // Scaled frame.  Between renormalisations the kernel keeps I~ = s_t I_t and
 // eta~ = s_t eta_t, where s_t = prod(1/alpha) since the frame's start token.
 // Per token and entry that turns both updates into accumulations:
@@ -133,11 +101,12 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     const int i = tile * CI + col;
     // bh: head of the token inputs; sb: slot of this run's starting/final state
     int seg;
+    int32_t sq = -1;
     int64_t bh, sb, t_begin, t_end;
     if (p.cu_seqlens) {
         // one whole sequence of one head
         bh = wg % p.H;
-        const int32_t sq = p.seq_order[wg / p.H];
+        sq = p.seq_order[wg / p.H];
         sb = static_cast<int64_t>(sq) * p.H + bh;
         seg = 0;
         sequence_tokens(p, sq, t_begin, t_end);
@@ -147,6 +116,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         sb = bh;
         segment_tokens(p, C, seg, t_begin, t_end);
     }
+    if (tid == 0) echo_bounds(p, blockIdx.x, 1, sb, seg, tile, t_begin, t_end, sq);
 
     const float I_prior = p.I_prior;
     const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
@@ -369,20 +339,37 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     }
 }
 
-// The same scan for 64-column tiles with a block of RB key rows x 2 value
-// columns per lane and every multiplicand in a VGPR.  A wave holds 2*RB key
-// rows: lanes 0-31 the first RB, lanes 32-63 the next RB, lane l % 32 the
-// column pair (2c, 2c+1).  At d_k = 128, RB = 4 gives 16-wave workgroups,
-// four waves per SIMD: a wave issues a VALU instruction at most every few
-// clocks, so the SIMD needs several waves to keep its VALU busy, and a
-// 64-column tile of a head is all the work one workgroup has.
-//   * Staging folds the frame scale into the key side (s_t k_t[j] and
-//     s_t k_t[j]^2) and pairs beta with beta*v, so a token's operands are
-//     four LDS vector reads per lane (three shared by half a wave), loaded
-//     while the previous token computes.
-//   * Per entry: two fmacs for the updates, the prior increment (held in a
-//     VGPR: an SGPR operand halves the issue rate), the reciprocal, the
-//     quotient and the read-out fmac; no DPP or SGPR multiplicands.
+// The scan for 64-column tiles, with a block of RB key rows x 2 value columns
+// per lane and every multiplicand in a VGPR.  A wave holds 2*RB key rows:
+// lanes 0-31 the first RB, lanes 32-63 the next RB, lane l % 32 the column
+// pair (2c, 2c+1).  At d_k = 128, RB = 4 gives 16-wave workgroups, four waves
+// per SIMD: a 64-column tile of a head is all the work one workgroup has.
+//
+// Frames.  The precision is kept in true units: with the decay alpha_t and
+// the prior increment P_t = (1 - alpha_t) I_prior from the frame-scalar pass,
+//   I = fma(I, alpha_t, P_t),   I = fma(k_j^2, beta_i, I)
+// costs the same two instructions as an update in a scaled frame, and needs
+// no rescale when a frame restarts.  The information mean is kept scaled,
+// eta~ = s_t eta (s_t as in k_diag), so its update is one fmac with s_t k_j
+// staged; the read-out divides by s_t through the staged query q_j / s_t.
+//
+// Read-out.  sum_j q_j mu_j over a lane's key rows is taken four rows at a
+// time with one reciprocal: for rows a, b, c, d of a column,
+//   q_a e_a / I_a + q_b e_b / I_b = (q_a e_a I_b + q_b e_b I_a) / (I_a I_b) = n_ab / d_ab,
+//   n_ab / d_ab + n_cd / d_cd = (n_ab d_cd + n_cd d_ab) / (d_ab d_cd),
+// 14 full-rate instructions and one v_rcp_f32 per four entries in place of
+// four reciprocals, four multiplies and four fmacs (measured on gfx950, the
+// reciprocal issues at about a quarter of the full rate).  The products of
+// four precisions must stay in range, so the grouped form runs only where
+//   * every precision of the wave is at least 2^-24 (checked once: I never
+//     falls below min(I_0, I_prior)), and
+//   * every precision stays below 2^24 through the chunk: checked per chunk
+//     from the wave's largest precision at the chunk start plus the chunk's
+//     largest possible growth, I_prior + 16 max(beta) max(k^2) (maxima taken
+//     while staging);
+// and a token whose grouped read-out is not finite (a numerator past the
+// fp32 range) is read out again one reciprocal per entry.  Elsewhere the
+// read-out takes one reciprocal per entry.
 //   * The two row blocks of a column are summed by one v_permlane32_swap;
 //     the waves' partial read-outs go through LDS once per chunk, single-
 //     buffered (with a second barrier) when 16 waves' worth would not fit
@@ -401,15 +388,24 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     constexpr int VB = C * CI / VW;
     constexpr int NVK = (VK + NTH - 1) / NTH;
     constexpr int NVB = (VB + NTH - 1) / NTH;
-    static_assert(RB == 4 || RB == 8, "key rows per lane");
+    constexpr int NKW = (VK < NTH ? VK : NTH) / kWave > 0 ? (VK < NTH ? VK : NTH) / kWave : 1;
+    constexpr int NBW = (VB < NTH ? VB : NTH) / kWave > 0 ? (VB < NTH ? VB : NTH) / kWave : 1;
+    static_assert(RB == 4 || RB == 8, "key rows per lane: whole groups of four");
     static_assert(DK % (2 * RB) == 0 && NTH <= 1024, "tile shape");
     static_assert(C == 16, "per-token scalars come in 16-token chunks");
+    static_assert(NKW <= W && NBW <= W, "staging waves");
+    constexpr float kQuadHi = 16777216.0f;          // 2^24
+    constexpr float kQuadLo = 1.0f / 16777216.0f;   // 2^-24
 
     struct Stage {
         float ks[C][DK];    // s_t k_t[j]
-        float k2s[C][DK];   // s_t k_t[j]^2
-        float q[C][DK];
+        float k2[C][DK];    // k_t[j]^2
+        float q[C][DK];     // q_t[j] / s_t
         float2 bv[C][CI];   // (beta_i, beta_i v_i)
+        float4 ap[C];       // (alpha_t, (1 - alpha_t) I_prior, rho_t of the eta frame, -)
+        float kmax[NKW];    // largest k^2 staged by each k-staging wave
+        float bmax[NBW];    // largest beta staged by each beta-staging wave
+        uint32_t restarts;  // bit t: token t restarts the eta frame (rho_t != 1)
     };
     __shared__ Stage stg[2];
     __shared__ float opart[NOB][C][P][CI];
@@ -441,10 +437,11 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     const int i0 = tile * CI + 2 * cp;
     // bh: head of the token inputs; sb: slot of this run's starting/final state
     int seg;
+    int32_t sq = -1;
     int64_t bh, sb, t_begin, t_end;
     if (p.cu_seqlens) {
         bh = wg % p.H;
-        const int32_t sq = p.seq_order[wg / p.H];
+        sq = p.seq_order[wg / p.H];
         sb = static_cast<int64_t>(sq) * p.H + bh;
         seg = 0;
         sequence_tokens(p, sq, t_begin, t_end);
@@ -454,6 +451,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         sb = bh;
         segment_tokens(p, C, seg, t_begin, t_end);
     }
+    if (tid == 0) echo_bounds(p, blockIdx.x, 1, sb, seg, tile, t_begin, t_end, sq);
 
     const float I_prior = p.I_prior;
     const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
@@ -462,6 +460,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     const E* bth = p.beta ? static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI : nullptr;
     const E* dh = static_cast<const E*>(p.d) + bh * p.T;
 
+    // I in true units, eta~ = s eta with s = 1 at the segment start
     float I[RB][2], eta[RB][2];
     if (p.S == 1) {
 #pragma unroll
@@ -487,13 +486,25 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
             }
         }
     }
+    // I never falls below min(I_0, I_prior): the grouped read-out's lower
+    // bound holds for the whole run if it holds now
+    bool quad_ok;
+    {
+        float lo = I_prior;
+#pragma unroll
+        for (int r = 0; r < RB; ++r)
+#pragma unroll
+            for (int c = 0; c < 2; ++c) lo = fminf(lo, I[r][c]);
+        quad_ok = __builtin_amdgcn_ballot_w64(!(lo >= kQuadLo)) == 0;
+    }
 
     uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
     float rs[NVK];
-    float s_prev = 1.0f;
+    // frame scalars (rho, P, s, A d) of token tid of the chunk (tid < C), and
+    // for tid 0 the scale of the token before the chunk (1 at the run start)
+    float4 rsc = make_float4(1.0f, 0.0f, 1.0f, 0.0f);
+    float rsp = 1.0f;
     const float4* sch = p.scal + bh * p.T;
-    typedef __attribute__((address_space(4))) const float scalar_f32;
-    auto frame_scalars = [&](int64_t t0) { return (scalar_f32*)(uintptr_t)(sch + t0); };
 
     auto fetch = [&](int64_t t0, int L) {
 #pragma unroll
@@ -516,10 +527,13 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
                 rv[n] = ld16(vh + off);
             }
         }
+        if (tid < L) rsc = sch[t0 + tid];
+        if (tid == 0) rsp = t0 > t_begin ? sch[t0 - 1].z : 1.0f;
     };
 
     auto commit = [&](int nb, int L) {
         Stage& S = stg[nb];
+        float mk = 0.0f, mb = 0.0f;
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
             const int vi = tid + n * NTH;
@@ -530,13 +544,15 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
                 widen<BF16>(rk[n], f);
 #pragma unroll
                 for (int e = 0; e < VW; ++e) {
-                    const float ks = f[e] * rs[n];
-                    S.ks[row][c0 + e] = ks;
-                    S.k2s[row][c0 + e] = ks * f[e];
+                    const float k2 = f[e] * f[e];
+                    S.ks[row][c0 + e] = f[e] * rs[n];
+                    S.k2[row][c0 + e] = k2;
+                    mk = fmaxf(mk, k2);
                 }
+                const float inv_s = 1.0f / rs[n];
                 widen<BF16>(rq[n], f);
 #pragma unroll
-                for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
+                for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e] * inv_s;
             }
         }
 #pragma unroll
@@ -549,8 +565,27 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
                 widen<BF16>(rv[n], fv);
                 widen<BF16>(rb[n], fb);
 #pragma unroll
-                for (int e = 0; e < VW; ++e) S.bv[row][c0 + e] = make_float2(fb[e], fb[e] * fv[e]);
+                for (int e = 0; e < VW; ++e) {
+                    S.bv[row][c0 + e] = make_float2(fb[e], fb[e] * fv[e]);
+                    mb = fmaxf(mb, fb[e]);
+                }
             }
+        }
+        // per-token (alpha, P, rho): a chunk's first token restarts the eta
+        // frame from the previous token's scale
+        if (wv == 0) {
+            const float rho = tid == 0 ? rsc.x / rsp : rsc.x;
+            if (tid < L) S.ap[tid] = make_float4(fast_exp(-rsc.w), rsc.y, rho, 0.0f);
+            const uint64_t m = __builtin_amdgcn_ballot_w64(tid < L && rho != 1.0f);
+            if (tid == 0) S.restarts = static_cast<uint32_t>(m);
+        }
+        if (wv < NKW) {
+            mk = wave_max(mk);
+            if (lane == 0) S.kmax[wv] = mk;
+        }
+        if (wv < NBW) {
+            mb = wave_max(mb);
+            if (lane == 0) S.bmax[wv] = mb;
         }
     };
 
@@ -572,19 +607,39 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         const int L = chunk_len(c);
         const int64_t t0 = t_begin + c * C;
         const Stage& S = stg[b];
-        const float inv_sp = 1.0f / s_prev;
-        scalar_f32* const cs = frame_scalars(t0);
+        const uint32_t restarts = __builtin_amdgcn_readfirstlane(S.restarts);
 
-        // A token's operands: RB key rows of s k, s k^2 and q (shared by
-        // half a wave) and the lane's (beta, beta v) column pair.
+        // Grouped read-out for this chunk: every precision of the wave stays
+        // below 2^24 if the largest now, or I_prior, plus the chunk's largest
+        // growth does.
+        bool quad;
+        {
+            float km = S.kmax[0], bm = S.bmax[0];
+#pragma unroll
+            for (int w = 1; w < NKW; ++w) km = fmaxf(km, S.kmax[w]);
+#pragma unroll
+            for (int w = 1; w < NBW; ++w) bm = fmaxf(bm, S.bmax[w]);
+            const float lim = kQuadHi - static_cast<float>(C) * km * bm;
+            float hi = I_prior;
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) hi = fmaxf(hi, I[r][cc]);
+            quad = quad_ok && __builtin_amdgcn_ballot_w64(!(hi + I_prior <= lim)) == 0;
+        }
+
+        // A token's operands: RB key rows of s k, k^2 and q / s (shared by
+        // half a wave), the lane's (beta, beta v) column pair and the token's
+        // (alpha, P).
         struct Ops {
             float4 k[RB / 4], k2[RB / 4], q[RB / 4];
             float4 bv;
+            float4 ap;
         };
         auto load_ops = [&](int tt) __attribute__((always_inline)) {
             Ops o;
             const float4* kp = reinterpret_cast<const float4*>(&S.ks[tt][j0]);
-            const float4* k2p = reinterpret_cast<const float4*>(&S.k2s[tt][j0]);
+            const float4* k2p = reinterpret_cast<const float4*>(&S.k2[tt][j0]);
             const float4* qp = reinterpret_cast<const float4*>(&S.q[tt][j0]);
 #pragma unroll
             for (int h = 0; h < RB / 4; ++h) {
@@ -593,77 +648,85 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
                 o.q[h] = qp[h];
             }
             o.bv = *reinterpret_cast<const float4*>(&S.bv[tt][2 * cp]);
+            o.ap = S.ap[tt];
             return o;
         };
         auto lane_of = [](const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; };
-        // One token from its operands and its frame scalars (rho as bits, the
-        // prior increment dP): frame change, state update, read-out partial.
-        auto token = [&](int tt, const Ops& o, uint32_t rho_bits, float dP) __attribute__((always_inline)) {
-            if (rho_bits != 0x3f800000u) {
-                const float rho = __uint_as_float(rho_bits);
+        // read-out of column cc over the lane's RB rows, four rows per reciprocal
+        auto readout_quad = [&](const Ops& o, int cc) __attribute__((always_inline)) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int g = 0; g < RB; g += 4) {
+                const float4 qv = o.q[g / 4];
+                const float Ia = I[g][cc], Ib = I[g + 1][cc], Ic = I[g + 2][cc], Id = I[g + 3][cc];
+                float nab = qv.x * (eta[g][cc] * Ib);
+                nab = __builtin_fmaf(qv.y, eta[g + 1][cc] * Ia, nab);
+                float ncd = qv.z * (eta[g + 2][cc] * Id);
+                ncd = __builtin_fmaf(qv.w, eta[g + 3][cc] * Ic, ncd);
+                const float dab = Ia * Ib;
+                const float dcd = Ic * Id;
+                const float num = __builtin_fmaf(ncd, dab, nab * dcd);
+                const float rq = fast_rcp(dab * dcd);
+                acc = g == 0 ? num * rq : __builtin_fmaf(num, rq, acc);
+            }
+            return acc;
+        };
+        // the same with one reciprocal per entry
+        auto readout_direct = [&](const Ops& o, int cc) __attribute__((always_inline)) {
+            float acc = 0.0f;
+#pragma unroll
+            for (int r = 0; r < RB; ++r) {
+                const float qq = lane_of(o.q[r / 4], r % 4);
+                const float m = eta[r][cc] * fast_rcp(I[r][cc]);
+                acc = r == 0 ? qq * m : __builtin_fmaf(qq, m, acc);
+            }
+            return acc;
+        };
+        // One token from its operands: eta frame restart, state update,
+        // read-out partial.
+        auto token = [&](int tt, const Ops& o) __attribute__((always_inline)) {
+            if ((restarts >> tt) & 1u) {
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
 #pragma unroll
-                    for (int cc = 0; cc < 2; ++cc) {
-                        I[r][cc] *= rho;
-                        eta[r][cc] *= rho;
-                    }
+                    for (int cc = 0; cc < 2; ++cc) eta[r][cc] *= o.ap.z;
             }
             const float bet[2] = {o.bv.x, o.bv.z};
             const float bvv[2] = {o.bv.y, o.bv.w};
-            float acc[2];
 #pragma unroll
             for (int r = 0; r < RB; ++r) {
                 const float kk = lane_of(o.k[r / 4], r % 4);
                 const float k2 = lane_of(o.k2[r / 4], r % 4);
-                const float qq = lane_of(o.q[r / 4], r % 4);
 #pragma unroll
                 for (int cc = 0; cc < 2; ++cc) {
-                    I[r][cc] = __builtin_fmaf(k2, bet[cc], I[r][cc]) + dP;
+                    I[r][cc] = __builtin_fmaf(k2, bet[cc], __builtin_fmaf(I[r][cc], o.ap.x, o.ap.y));
                     eta[r][cc] = __builtin_fmaf(kk, bvv[cc], eta[r][cc]);
-                    const float m = eta[r][cc] * fast_rcp(I[r][cc]);
-                    acc[cc] = r == 0 ? qq * m : __builtin_fmaf(qq, m, acc[cc]);
                 }
             }
-            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0]), __float_as_uint(acc[1]), false, false);
-            opart[b % NOB][tt][wv][ocol] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            float x = 0.0f;
+            bool done = false;
+            if (quad) {
+                x = swap32_add(readout_quad(o, 0), readout_quad(o, 1));
+                done = __builtin_amdgcn_ballot_w64(!__builtin_isfinite(x)) == 0;
+            }
+            if (!done) x = swap32_add(readout_direct(o, 0), readout_direct(o, 1));
+            opart[b % NOB][tt][wv][ocol] = x;
         };
-        auto rho_at = [&](int tt) -> uint32_t {
-            return tt == 0 ? __builtin_amdgcn_readfirstlane(__float_as_uint(cs[0] * inv_sp))
-                           : __float_as_uint(cs[4 * tt]);
-        };
-        // the prior increment in a VGPR: an SGPR operand halves the issue
-        // rate of the adds that read it
-        auto dP_at = [&](int tt) { return vgpr_copy(cs[4 * tt + 1]); };
-
         if (L == C) {
-            // a whole chunk, unrolled; each token's LDS operands and frame
-            // scalars are loaded while the previous token computes
+            // a whole chunk, unrolled; each token's LDS operands are loaded
+            // while the previous token computes
             Ops cur = load_ops(0);
-            uint32_t rho_c = rho_at(0);
-            float dP_c = dP_at(0);
             Unroll<0, C>::run([&](auto u) {
                 constexpr int tt = decltype(u)::value;
                 Ops nxt;
-                uint32_t rho_n = 0;
-                float dP_n = 0.0f;
-                if constexpr (tt + 1 < C) {
-                    nxt = load_ops(tt + 1);
-                    rho_n = rho_at(tt + 1);
-                    dP_n = dP_at(tt + 1);
-                }
-                token(tt, cur, rho_c, dP_c);
-                if constexpr (tt + 1 < C) {
-                    cur = nxt;
-                    rho_c = rho_n;
-                    dP_c = dP_n;
-                }
+                if constexpr (tt + 1 < C) nxt = load_ops(tt + 1);
+                token(tt, cur);
+                if constexpr (tt + 1 < C) cur = nxt;
             });
         } else {
-            for (int tt = 0; tt < L; ++tt) token(tt, load_ops(tt), rho_at(tt), dP_at(tt));
+            for (int tt = 0; tt < L; ++tt) token(tt, load_ops(tt));
         }
 
-        s_prev = cs[4 * (L - 1) + 2];
         if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
         __syncthreads();
         for (int e = tid; e < L * CI; e += NTH) {
@@ -679,15 +742,15 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         if (c + 2 < nch) fetch(t0 + 2 * C, chunk_len(c + 2));
     }
 
-    const float s_last = s_prev;
     if (seg == p.S - 1) {
+        const float inv_s_last = t_end > t_begin ? 1.0f / sch[t_end - 1].z : 1.0f;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int64_t off = (sb * DK + j0 + r) * p.dv + i0;
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-                if (p.I_T) p.I_T[off + cc] = I[r][cc] / s_last;
-                if (p.mu_T) p.mu_T[off + cc] = eta[r][cc] / I[r][cc];
+                if (p.I_T) p.I_T[off + cc] = I[r][cc];
+                if (p.mu_T) p.mu_T[off + cc] = eta[r][cc] * inv_s_last / I[r][cc];
             }
         }
     }
@@ -698,10 +761,13 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
 // frame starts at the chunk's first token and wherever the log-growth since
 // that token crosses a multiple of kFrameLog), s = product of 1/alpha since
 // the frame start, rho = alpha / s_{t-1} at a start (for the chunk's first
-// token only alpha: the main pass divides by the previous chunk's last s),
-// dP = (1 - alpha) I_prior s.  Output (rho, dP, s, A d) per token.
+// token only alpha: the main pass divides by the previous chunk's last s).
+// Output (rho, dP, s, A d) per token, where the prior increment dP is
+// (1 - alpha) I_prior s for a pass that keeps the precision in the scaled
+// frame (TRUE_I false) and (1 - alpha) I_prior for one that keeps it in true
+// units (TRUE_I true; 1 - alpha from expm1, exact to rounding at small A d).
 // One chunk's walk: tokens [t0, t0 + L) of head bh, a chunk start.
-template <bool BF16>
+template <bool BF16, bool TRUE_I>
 __device__ __forceinline__ void prep_chunk(const DiagParams& p, int64_t bh, int64_t t0, int L) {
     const float A = p.A[bh % p.H];
     float cum = 0.0f, s = 1.0f;
@@ -728,23 +794,24 @@ __device__ __forceinline__ void prep_chunk(const DiagParams& p, int64_t bh, int6
             }
             fr_prev = fr;
         }
-        out[k] = make_float4(rho, (1.0f - alpha) * p.I_prior * s, s, ell);
+        const float dP = TRUE_I ? -expm1f(-ell) * p.I_prior : (1.0f - alpha) * p.I_prior * s;
+        out[k] = make_float4(rho, dP, s, ell);
     }
 }
 
-template <bool BF16>
+template <bool BF16, bool TRUE_I>
 __global__ __launch_bounds__(256) void k_diag_prep(DiagParams p, int64_t n_units, int32_t nch) {
     constexpr int C = kDiagChunkTokens;
     for (int64_t u = elem_first(); u < n_units; u += elem_stride()) {
         const int64_t bh = u / nch;
         const int64_t t0 = (u % nch) * C;
-        prep_chunk<BF16>(p, bh, t0, p.T - t0 < C ? static_cast<int>(p.T - t0) : C);
+        prep_chunk<BF16, TRUE_I>(p, bh, t0, p.T - t0 < C ? static_cast<int>(p.T - t0) : C);
     }
 }
 
 // Packed variable-length batch: chunks start at every sequence's first token.
 // One thread per (head, packed token); the threads at a chunk start walk it.
-template <bool BF16>
+template <bool BF16, bool TRUE_I>
 __global__ __launch_bounds__(256) void k_diag_prep_varlen(DiagParams p) {
     constexpr int C = kDiagChunkTokens;
     for (int64_t u = elem_first(); u < p.H * p.T; u += elem_stride()) {
@@ -754,7 +821,7 @@ __global__ __launch_bounds__(256) void k_diag_prep_varlen(DiagParams p) {
         const int32_t s = find_sequence(p, t);
         sequence_tokens(p, s, t_begin, t_end);
         if ((t - t_begin) % C != 0) continue;
-        prep_chunk<BF16>(p, h, t, t_end - t < C ? static_cast<int>(t_end - t) : C);
+        prep_chunk<BF16, TRUE_I>(p, h, t, t_end - t < C ? static_cast<int>(t_end - t) : C);
     }
 }
 
@@ -903,8 +970,11 @@ int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t s
     const int64_t n = p.H * p.T;
     if (n > 0) {
         const dim3 grid(elem_groups(n));
-        if (bf16) hipLaunchKernelGGL(k_diag_prep_varlen<true>, grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL(k_diag_prep_varlen<false>, grid, dim3(256), 0, st, p);
+        const bool true_i = varlen_cols(p.dv) == 64;   // the block kernel keeps I in true units
+        if (bf16 && true_i) hipLaunchKernelGGL((k_diag_prep_varlen<true, true>), grid, dim3(256), 0, st, p);
+        else if (bf16) hipLaunchKernelGGL((k_diag_prep_varlen<true, false>), grid, dim3(256), 0, st, p);
+        else if (true_i) hipLaunchKernelGGL((k_diag_prep_varlen<false, true>), grid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL((k_diag_prep_varlen<false, false>), grid, dim3(256), 0, st, p);
     }
     const int CI = varlen_cols(p.dv);
     const int64_t runs = static_cast<int64_t>(p.nseq) * p.H;
@@ -915,13 +985,15 @@ int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t s
     return launch_status();
 }
 
-int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st) {
+int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, bool true_i, hipStream_t st) {
     const int32_t nch = static_cast<int32_t>((p.T + kDiagChunk - 1) / kDiagChunk);
     const int64_t n = B * p.H * nch;
     if (n == 0) return KDN_OK;
     const dim3 grid(elem_groups(n));
-    if (bf16) hipLaunchKernelGGL(k_diag_prep<true>, grid, dim3(256), 0, st, p, n, nch);
-    else hipLaunchKernelGGL(k_diag_prep<false>, grid, dim3(256), 0, st, p, n, nch);
+    if (bf16 && true_i) hipLaunchKernelGGL((k_diag_prep<true, true>), grid, dim3(256), 0, st, p, n, nch);
+    else if (bf16) hipLaunchKernelGGL((k_diag_prep<true, false>), grid, dim3(256), 0, st, p, n, nch);
+    else if (true_i) hipLaunchKernelGGL((k_diag_prep<false, true>), grid, dim3(256), 0, st, p, n, nch);
+    else hipLaunchKernelGGL((k_diag_prep<false, false>), grid, dim3(256), 0, st, p, n, nch);
     return launch_status();
 }
 
@@ -951,10 +1023,15 @@ int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int3
     if (p.T == 0) return copy_state_launch(p, B, dk, false, st);
     const int CI = p.dv < 64 ? static_cast<int>(p.dv) : 64;
     const int64_t ntile = p.dv / CI;
-    int rc = diag_prep_launch(p, B, bf16, st);
+    // the block kernel (64-column tiles) keeps the precision in true units
+    int rc = diag_prep_launch(p, B, bf16, CI == 64, st);
     if (rc != KDN_OK) return rc;
-    if (p.S > 1 && (rc = diag_comp_launch(p, B, dk, bf16, R, st)) != KDN_OK) return rc;
     const int64_t g2 = BH * p.S * ntile;
+    if (p.S > 1) {
+        DiagParams pc = p;
+        pc.echo_base = g2;   // composite records after the main pass's
+        if ((rc = diag_comp_launch(pc, B, dk, bf16, R, st)) != KDN_OK) return rc;
+    }
     rc = bf16 ? launch_main<true>(p, dk, CI, g2, st) : launch_main<false>(p, dk, CI, g2, st);
     if (rc != KDN_OK) return rc;
     return launch_status();

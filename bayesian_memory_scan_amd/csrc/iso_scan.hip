@@ -98,10 +98,9 @@ void k_iso(DiagParams p) {
     const int nseg_run = COMPOSITE ? p.S - 1 : p.S;
     if (seg >= nseg_run) return;
 
-    const int64_t c0 = static_cast<int64_t>(seg) * p.nchunks / p.S;
-    const int64_t c1 = static_cast<int64_t>(seg + 1) * p.nchunks / p.S;
-    const int64_t t_begin = c0 * C;
-    const int64_t t_end = c1 * C < p.T ? c1 * C : p.T;
+    int64_t t_begin, t_end;
+    segment_tokens(p, C, seg, t_begin, t_end);
+    if (lane == 0) echo_bounds(p, blockIdx.x, COMPOSITE ? 4 : 3, bh, seg, tile, t_begin, t_end, -1);
     const int64_t DV = p.dv;
     const int64_t cb = static_cast<int64_t>(tile) * NC;   // first column of the tile
 
@@ -350,7 +349,9 @@ int iso_mean_launch(const DiagParams& p, int64_t B, int64_t dk, hipStream_t st) 
     const int64_t grid = BH * p.S * iso_tiles(p.dv);
     int rc;
     if (p.S > 1) {
-        if ((rc = iso_launch<true>(p, dk, p.dv, grid, st)) != KDN_OK) return rc;
+        DiagParams pc = p;
+        pc.echo_base = grid;   // composite records after the main pass's
+        if ((rc = iso_launch<true>(pc, dk, p.dv, grid, st)) != KDN_OK) return rc;
         if ((rc = diag_carry_launch(p, B, dk, true, st)) != KDN_OK) return rc;
     }
     return iso_launch<false>(p, dk, p.dv, grid, st);

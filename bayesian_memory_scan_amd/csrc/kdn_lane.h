@@ -158,6 +158,18 @@ __device__ __forceinline__ float wave_sum2(float a, float b) {
     return x + dpp<kDppQuadSwap1>(x);
 }
 
+// Maximum over the 64 lanes of the wave, returned in every lane.
+__device__ __forceinline__ float wave_max(float x) {
+    x = fmaxf(x, dpp<kDppQuadSwap1>(x));
+    x = fmaxf(x, dpp<kDppQuadReverse>(x));
+    x = fmaxf(x, dpp<kDppHalfMirror>(x));
+    x = fmaxf(x, dpp<kDppMirror>(x));
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 // Buffer resource over `bytes` bytes from `base` (raw, untyped, gfx9 format
 // word).  Loads past the end return 0 and stores past the end are dropped, so
 // a ragged chunk needs no branches: the wait counters stay exact and the next

@@ -36,7 +36,81 @@ struct DiagParams {
     const int64_t* cu_seqlens;   // packed variable-length batch: [nseq + 1] offsets, or NULL
     int32_t* seq_order;          // its sequences, longest first (written by the plan pass)
     int32_t nseq;
+    int64_t* echo;               // bounds echo (kdn_scan_opts), or NULL
+    int64_t echo_cap;            // its capacity in int64 words
+    int64_t echo_base;           // first record slot of the launch being made
 };
+
+// ---------------------------------------------------------------------------
+// Token bounds of the work units: every kernel takes them from these, and the
+// bounds echo reports what they returned.
+// ---------------------------------------------------------------------------
+
+// Packed variable-length batch: tokens of sequence s, [cu[s], cu[s+1]),
+// clamped into [0, T] so that a malformed offset table cannot send a
+// workgroup out of bounds.
+__device__ __forceinline__ void sequence_tokens(const DiagParams& p, int32_t s, int64_t& t0,
+                                                int64_t& t1) {
+    int64_t a = p.cu_seqlens[s], b = p.cu_seqlens[s + 1];
+    a = a < 0 ? 0 : (a > p.T ? p.T : a);
+    b = b < a ? a : (b > p.T ? p.T : b);
+    t0 = a;
+    t1 = b;
+}
+
+// The sequence holding packed token t: the last s with cu[s] <= t.
+__device__ __forceinline__ int32_t find_sequence(const DiagParams& p, int64_t t) {
+    int32_t lo = 0, hi = p.nseq;
+    while (hi - lo > 1) {
+        const int32_t mid = (lo + hi) / 2;
+        if (p.cu_seqlens[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+// Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S) of the
+// n = p.nchunks chunks of C tokens.
+__device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
+                                               int64_t& t0, int64_t& t1) {
+    const int64_t c0 = static_cast<int64_t>(seg) * p.nchunks / p.S;
+    const int64_t c1 = static_cast<int64_t>(seg + 1) * p.nchunks / p.S;
+    t0 = c0 * C;
+    t1 = c1 * C < p.T ? c1 * C : p.T;
+}
+
+// Token range of sub-segment r of segment s: the segment's chunks split in R.
+__device__ __forceinline__ void sub_tokens(const DiagParams& p, int C, int R, int s, int r,
+                                           int64_t& t0, int64_t& t1) {
+    const int64_t c0 = static_cast<int64_t>(s) * p.nchunks / p.S;
+    const int64_t c1 = static_cast<int64_t>(s + 1) * p.nchunks / p.S;
+    const int64_t n = c1 - c0;
+    const int64_t a = c0 + static_cast<int64_t>(r) * n / R;
+    const int64_t b = c0 + static_cast<int64_t>(r + 1) * n / R;
+    t0 = a * C;
+    t1 = b * C < p.T ? b * C : p.T;
+}
+
+// One bounds-echo record {kind, run, segment, part, t_begin, t_end,
+// sequence, 0} at slot p.echo_base + unit, if an echo buffer was given and
+// the record fits.  Called by one lane per work unit.
+constexpr int kEchoWords = KDN_ECHO_WORDS;
+__device__ __forceinline__ void echo_bounds(const DiagParams& p, int64_t unit, int64_t kind, int64_t run,
+                                            int64_t seg, int64_t part, int64_t t0, int64_t t1,
+                                            int64_t sequence) {
+    if (p.echo == nullptr) return;
+    const int64_t slot = p.echo_base + unit;
+    if ((slot + 1) * kEchoWords > p.echo_cap) return;
+    int64_t* r = p.echo + slot * kEchoWords;
+    r[0] = kind;
+    r[1] = run;
+    r[2] = seg;
+    r[3] = part;
+    r[4] = t0;
+    r[5] = t1;
+    r[6] = sequence;
+    r[7] = 0;
+}
 
 struct DecodeParams {
     const void* q;
@@ -129,11 +203,12 @@ int diag_chunk();
 int varlen_cols(int64_t dv);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
                     bool bf16, hipStream_t st);
-int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, hipStream_t st);
+int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, bool true_i, hipStream_t st);
 int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
+int comp_tiles(int64_t dv);
 int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int mob_block();

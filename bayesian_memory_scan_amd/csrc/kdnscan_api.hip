@@ -2,7 +2,6 @@
 // layout and kernel dispatch.  Validation completes before any HIP call.
 #include "kdn_params.h"
 
-#include <atomic>
 #include <cmath>
 
 namespace kdn {
@@ -15,8 +14,6 @@ void note_hip_error(hipError_t e) { g_last_error = e; }
 namespace {
 
 using namespace kdn;
-
-std::atomic<int32_t> g_segments_override{0};
 
 // One dispatch covers at most 2^32 - 1 work-items (the dispatch packet's grid
 // size is 32 bits).  Per-head and per-block launches use at most 512 threads
@@ -35,17 +32,17 @@ struct Plan {
     int32_t R;   // sub-segments per segment for the composite pass (diagonal scan)
 };
 
-// Chunking and segment count of a (possibly isotropic) segmented scan.
-Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
+// Chunking and segment count of the diagonal scan; `request` is the
+// caller's segment count (0: automatic).
+Plan plan_scan(int64_t BH, int64_t T, int64_t dv, int32_t request) {
     Plan pl;
     pl.chunk = diag_chunk();
     pl.nchunks = static_cast<int32_t>((T + pl.chunk - 1) / pl.chunk);
     const int64_t ci = dv < 64 ? dv : 64;
     const int64_t units = BH * (dv / ci);
     int64_t S = 1;
-    const int32_t ov = g_segments_override.load();
-    if (ov > 0) {
-        S = ov;
+    if (request > 0) {
+        S = request;
     } else if (units > 0 && units < kNumCU && pl.nchunks >= 16) {
         S = (kNumCU + units - 1) / units;
         if (S > pl.nchunks / 8) S = pl.nchunks / 8;
@@ -70,15 +67,14 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv) {
 }
 
 // Segments of the isotropic mean scan: about two one-wave workgroups per
-// SIMD, at least four 16-token chunks per segment.
-Plan plan_iso(int64_t BH, int64_t T, int64_t dv) {
+// SIMD, at least four 16-token chunks per segment (or the caller's request).
+Plan plan_iso(int64_t BH, int64_t T, int64_t dv, int32_t request) {
     Plan pl;
     pl.chunk = iso_chunk();
     pl.nchunks = static_cast<int32_t>((T + pl.chunk - 1) / pl.chunk);
     int64_t S = 1;
-    const int32_t ov = g_segments_override.load();
-    if (ov > 0) {
-        S = ov;
+    if (request > 0) {
+        S = request;
     } else if (BH > 0) {
         const int64_t units = BH * iso_tiles(dv);
         S = (8 * kNumCU + units - 1) / units;
@@ -135,6 +131,25 @@ int workspace_check(void* workspace, size_t* workspace_bytes, size_t need) {
     return KDN_OK;
 }
 
+// Options of an extended call: a NULL pointer is the zero struct.  Checks
+// what the call can check (segment request, echo buffer) before any HIP call.
+bool opts_ok(const kdn_scan_opts* o) {
+    if (o == nullptr) return true;
+    if (o->segments < 0 || o->echo_capacity < 0) return false;
+    if (o->bounds_echo != nullptr && (reinterpret_cast<uintptr_t>(o->bounds_echo) & 7u) != 0) return false;
+    return true;
+}
+int32_t opt_segments(const kdn_scan_opts* o) { return o ? o->segments : 0; }
+void set_echo(DiagParams& p, const kdn_scan_opts* o) {
+    if (o && o->bounds_echo) {
+        p.echo = o->bounds_echo;
+        p.echo_cap = o->echo_capacity;
+    }
+}
+void report_echo(kdn_scan_opts* o, int64_t records) {
+    if (o) o->echo_words = records * KDN_ECHO_WORDS;
+}
+
 // Guard against overflow: B*H*T*D must stay < 2^62 (int64 element counts)
 // and T below 2^31 (chunk and block counts are int32).
 bool sizes_fit(int64_t B, int64_t H, int64_t T, int64_t D) {
@@ -163,18 +178,16 @@ const char* kdn_last_hip_error(void) {
     return hipGetErrorString(g_last_error);
 }
 
-int32_t kdn_set_diag_segments(int32_t segments) {
-    return g_segments_override.exchange(segments > 0 ? segments : 0);
-}
-
-int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
-                  int32_t* chunk, int32_t* segments, int64_t* seg_bounds, int32_t max_segments) {
-    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, int32_t segments,
+                  int32_t* chunk, int32_t* segments_out, int32_t* subsegments,
+                  int64_t* seg_bounds, int32_t max_segments) {
+    if (B < 0 || H < 0 || T < 0 || segments < 0) return KDN_EINVAL;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
     if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
-    const Plan pl = plan_scan(B * H, T, d_v);
+    const Plan pl = plan_scan(B * H, T, d_v, segments);
     if (chunk) *chunk = pl.chunk;
-    if (segments) *segments = pl.S;
+    if (segments_out) *segments_out = pl.S;
+    if (subsegments) *subsegments = pl.R;
     if (seg_bounds) {
         if (max_segments < pl.S) return KDN_EINVAL;
         for (int32_t s = 0; s <= pl.S; ++s) {
@@ -194,7 +207,19 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       const float* I0, const float* mu0,
                       float* o, float* I_T, float* mu_T,
                       void* workspace, size_t* workspace_bytes, void* stream) {
-    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    return kdn_diag_scan_fwd_ex(B, H, T, d_k, d_v, in_dtype, q, k, v, beta, d, A, I_prior, I0, mu0,
+                                o, I_T, mu_T, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                         kdn_dtype in_dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* beta, const void* d,
+                         const float* A, float I_prior,
+                         const float* I0, const float* mu0,
+                         float* o, float* I_T, float* mu_T, kdn_scan_opts* opts,
+                         void* workspace, size_t* workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0 || !opts_ok(opts)) return KDN_EINVAL;
     if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
     if (!finite_positive(I_prior)) return KDN_EINVAL;
@@ -207,11 +232,12 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     }
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
 
-    const Plan pl = plan_scan(BH, T, d_v);
+    const Plan pl = plan_scan(BH, T, d_v, opt_segments(opts));
     const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
     if (!grid_fits(BH * pl.S * ntile)) return KDN_EINVAL;
     // composite pass: one wave per (head, sub-segment, column tile of 16 or 32)
     if (pl.S > 1 && !grid_fits(BH * (pl.S - 1) * pl.R * (d_v / 16), kWave)) return KDN_EINVAL;
+    report_echo(opts, T > 0 ? BH * pl.S * ntile + (pl.S > 1 ? BH * (pl.S - 1) * pl.R * comp_tiles(d_v) : 0) : 0);
     const DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
     const size_t need = dw.total;
     const int wc = workspace_check(workspace, workspace_bytes, need);
@@ -232,6 +258,7 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     }
     p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.S = pl.S; p.nchunks = pl.nchunks;
+    set_echo(p, opts);
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
 }
@@ -244,7 +271,21 @@ int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
                              const float* I0, const float* mu0,
                              float* o, float* I_T, float* mu_T,
                              void* workspace, size_t* workspace_bytes, void* stream) {
-    if (N < 0 || H < 0 || total_T < 0 || N >= 2147483647) return KDN_EINVAL;
+    return kdn_diag_scan_varlen_fwd_ex(N, H, total_T, d_k, d_v, in_dtype, cu_seqlens, q, k, v, beta, d, A,
+                                       I_prior, I0, mu0, o, I_T, mu_T, nullptr, workspace,
+                                       workspace_bytes, stream);
+}
+
+int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                                kdn_dtype in_dtype, const int64_t* cu_seqlens,
+                                const void* q, const void* k, const void* v,
+                                const void* beta, const void* d,
+                                const float* A, float I_prior,
+                                const float* I0, const float* mu0,
+                                float* o, float* I_T, float* mu_T, kdn_scan_opts* opts,
+                                void* workspace, size_t* workspace_bytes, void* stream) {
+    if (N < 0 || H < 0 || total_T < 0 || N >= 2147483647 || !opts_ok(opts)) return KDN_EINVAL;
+    if (opt_segments(opts) > 1) return KDN_EINVAL;
     if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
     if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
     if (!finite_positive(I_prior)) return KDN_EINVAL;
@@ -260,6 +301,7 @@ int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
     const int64_t ntile = d_v / varlen_cols(d_v);
     if (!grid_fits((N * H + 7) * ntile)) return KDN_EINVAL;
+    report_echo(opts, N > 0 && H > 0 ? (N * H + 7) / 8 * 8 * ntile : 0);
     const size_t b_scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
     const size_t need = work ? b_scal + align_up(4 * static_cast<size_t>(N), 256) : 0;
     const int wc = workspace_check(workspace, workspace_bytes, need);
@@ -276,6 +318,7 @@ int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     p.H = H; p.T = total_T; p.dv = d_v; p.I_prior = I_prior;
     p.S = 1; p.nchunks = 0;
     p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
+    set_echo(p, opts);
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_varlen_launch(p, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
 }
@@ -404,7 +447,18 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
                               const float* q, const float* k, const float* v,
                               const float* mu0, float* o, float* mu_T,
                               void* workspace, size_t* workspace_bytes, void* stream) {
-    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    return kdn_mobius_precision_scan_ex(B, H, T, a, p, Lambda, lambda0, lambda_out, d_k, d_v, q, k, v, mu0,
+                                        o, mu_T, nullptr, workspace, workspace_bytes, stream);
+}
+
+int kdn_mobius_precision_scan_ex(int64_t B, int64_t H, int64_t T,
+                                 const float* a, const float* p, const float* Lambda,
+                                 const float* lambda0, float* lambda_out,
+                                 int64_t d_k, int64_t d_v,
+                                 const float* q, const float* k, const float* v,
+                                 const float* mu0, float* o, float* mu_T, kdn_scan_opts* opts,
+                                 void* workspace, size_t* workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0 || !opts_ok(opts)) return KDN_EINVAL;
     const bool mean = !(d_k == 0 && d_v == 0);
     if (mean && (!head_size_ok(d_k) || !head_size_ok(d_v))) return KDN_EUNSUPPORTED;
     if (!sizes_fit(B, H, T, mean ? (d_k > d_v ? d_k : d_v) : 1)) return KDN_EINVAL;
@@ -422,9 +476,11 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
     size_t need = (BH > 0 && T > 0) ? b_blk : 0;
     Plan pl{};
     size_t b_gate = 0;
+    report_echo(opts, 0);
     if (mean) {
-        pl = plan_iso(BH, T, d_v);
+        pl = plan_iso(BH, T, d_v, opt_segments(opts));
         if (!grid_fits(BH * pl.S * iso_tiles(d_v), kWave)) return KDN_EINVAL;
+        if (T > 0) report_echo(opts, BH * pl.S * iso_tiles(d_v) * (pl.S > 1 ? 2 : 1));
         b_gate = align_up(sizeof(float) * static_cast<size_t>(BH) * T, 256);
         need += 2 * b_gate + scan_workspace_bytes(BH, d_k, d_v, pl);
     }
@@ -461,6 +517,7 @@ int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,
     }
     dp.H = H; dp.T = T; dp.dv = d_v; dp.I_prior = 1.0f;
     dp.S = pl.S; dp.nchunks = pl.nchunks;
+    set_echo(dp, opts);
     return iso_mean_launch(dp, B, d_k, st);
 }
 

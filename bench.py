@@ -205,7 +205,7 @@ def main():
         x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "d", "A")}
         o = torch.empty((spec.B, spec.H, spec.T, spec.d_v), dtype=torch.float32, device=dev)
         st = torch.empty((2, spec.B, spec.H, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
-        _, S, _ = kdn.kdn_diag_plan(spec.B, spec.H, spec.T, spec.d_k, spec.d_v)
+        _, S, _, _ = kdn.kdn_diag_plan(spec.B, spec.H, spec.T, spec.d_k, spec.d_v)
 
         def step():
             kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], x["A"],

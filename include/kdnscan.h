@@ -84,8 +84,10 @@ enum {
  * Outputs (float): o [B,H,T,d_v]; I_T, mu_T [B,H,d_k,d_v] final state, or
  *   NULL to skip.  I_T may alias I0 and mu_T may alias mu0 (continuation);
  *   no other aliasing between inputs and outputs is allowed.
- * Long sequences are split into segments whose composites are carried in
- * order; the workspace holds them (the query returns 0 when not needed).
+ * Workspace: always needed when B*H*T > 0: 16 bytes of per-token frame
+ * scalars per (head, token), plus, when the plan splits long sequences into
+ * segments (whose composites are carried in order), the segment composites
+ * and carry-in states.  Query its size first.
  */
 int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       kdn_dtype in_dtype,
@@ -229,22 +231,79 @@ int kdn_decode_step(int64_t B, int64_t H, int64_t d_k, int64_t d_v, kdn_dtype in
 
 /*
  * Plan of a diagonal scan (host only, no HIP call): the token chunk length
- * staged per step, the number of sequence segments and their token bounds
- * seg_bounds[0..S] (seg_bounds may be NULL; it must hold S+1 entries when
- * given, S <= max_segments).  Segment s owns whole chunks
- * [floor(s n / S), floor((s+1) n / S)) of the n = ceil(T / chunk) chunks.
+ * staged per step, the number of sequence segments S, the number of
+ * sub-segments R each composite segment is cut into, and the segment token
+ * bounds seg_bounds[0..S] (seg_bounds may be NULL; it must hold S+1 entries
+ * when given, S <= max_segments).  `segments` is the request of the call
+ * being planned: 0 for the automatic choice, n >= 1 for n segments (clamped
+ * to [1, min(64, number of chunks)]), as in kdn_scan_opts.  Segment s owns
+ * whole chunks [floor(s n / S), floor((s+1) n / S)) of the n = ceil(T / chunk)
+ * chunks; sub-segment r of segment s owns the segment's chunks
+ * [c0 + floor(r m / R), c0 + floor((r+1) m / R)), m the segment's chunk count.
  */
-int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
-                  int32_t* chunk, int32_t* segments,
+int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, int32_t segments,
+                  int32_t* chunk, int32_t* segments_out, int32_t* subsegments,
                   int64_t* seg_bounds, int32_t max_segments);
 
 /*
- * Process-wide override of the number of sequence segments used by
- * kdn_diag_scan_fwd (0 restores the automatic choice).  For tests and
- * tuning; not thread-safe against concurrent calls.  Returns the previous
- * value.
+ * Options of the extended entry points below.  A zero-initialised struct (or
+ * a NULL pointer) gives exactly the behaviour of the plain entry point.
+ *   segments: 0 = automatic plan; n >= 1 = cut each sequence into n segments
+ *     (clamped as in kdn_diag_plan; the isotropic mean scan clamps to its own
+ *     chunk count).  Results agree with any segmenting up to rounding.
+ *   bounds_echo / echo_capacity: a device buffer of echo_capacity int64
+ *     words, or NULL.  When given, every workgroup (or one-wave work unit)
+ *     of the scan writes one record of KDN_ECHO_WORDS words holding the token
+ *     bounds it actually used: {kind, run, segment, part, t_begin, t_end,
+ *     sequence, 0}, kind 1 = main pass (run = b*H + h, part = column tile),
+ *     2 = diagonal segment composite (part = sub-segment), 3 = isotropic mean
+ *     scan (part = column tile), 4 = isotropic segment composite; for a
+ *     packed batch run = s*H + h of sequence s = `sequence`.  Record r of
+ *     kind k sits at a fixed slot; records that would pass echo_capacity are
+ *     dropped; slots of work units with nothing to do stay untouched (clear
+ *     the buffer first).  For testing the integer bookkeeping.
+ *   echo_words (out): the words the call's records span (written on every
+ *     call, queries included).
  */
-int32_t kdn_set_diag_segments(int32_t segments);
+#define KDN_ECHO_WORDS 8
+typedef struct kdn_scan_opts {
+    int32_t segments;
+    int32_t reserved;
+    int64_t* bounds_echo;
+    int64_t echo_capacity;
+    int64_t echo_words;
+} kdn_scan_opts;
+
+/* kdn_diag_scan_fwd with options (opts may be NULL). */
+int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                         kdn_dtype in_dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* beta, const void* d,
+                         const float* A, float I_prior,
+                         const float* I0, const float* mu0,
+                         float* o, float* I_T, float* mu_T, kdn_scan_opts* opts,
+                         void* workspace, size_t* workspace_bytes, void* stream);
+
+/* kdn_diag_scan_varlen_fwd with options (opts may be NULL; segments must be
+ * 0 or 1: a packed batch runs each sequence in one segment). */
+int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                                kdn_dtype in_dtype, const int64_t* cu_seqlens,
+                                const void* q, const void* k, const void* v,
+                                const void* beta, const void* d,
+                                const float* A, float I_prior,
+                                const float* I0, const float* mu0,
+                                float* o, float* I_T, float* mu_T, kdn_scan_opts* opts,
+                                void* workspace, size_t* workspace_bytes, void* stream);
+
+/* kdn_mobius_precision_scan with options (opts may be NULL; segments applies
+ * to the gated mean scan). */
+int kdn_mobius_precision_scan_ex(int64_t B, int64_t H, int64_t T,
+                                 const float* a, const float* p, const float* Lambda,
+                                 const float* lambda0, float* lambda_out,
+                                 int64_t d_k, int64_t d_v,
+                                 const float* q, const float* k, const float* v,
+                                 const float* mu0, float* o, float* mu_T, kdn_scan_opts* opts,
+                                 void* workspace, size_t* workspace_bytes, void* stream);
 
 /* Human-readable text of a status code; never NULL. */
 const char* kdn_status_string(int status);

@@ -359,6 +359,24 @@ def plan(T: int, chunk: int, segments: int):
     return starts, lens, bounds
 
 
+def plan_sub(T: int, chunk: int, segments: int, subsegments: int):
+    """Token bounds of every sub-segment of the composite segments 0..S-2:
+    sub-segment r of segment s owns the segment's chunks
+    [c0 + floor(r m / R), c0 + floor((r+1) m / R)), with [c0, c1) the
+    segment's chunks (as in plan) and m = c1 - c0.  Returns
+    {(s, r): (t_begin, t_end)} as Python ints."""
+    n = -(-T // chunk)
+    out = {}
+    for s in range(segments - 1):
+        c0, c1 = s * n // segments, (s + 1) * n // segments
+        m = c1 - c0
+        for r in range(subsegments):
+            a = c0 + r * m // subsegments
+            b = c0 + (r + 1) * m // subsegments
+            out[(s, r)] = (min(a * chunk, T), min(b * chunk, T))
+    return out
+
+
 def element_offset(b: int, h: int, t: int, x: int, H: int, T: int, D: int) -> int:
     """Element index of [b, h, t, x] in a contiguous [B, H, T, D] tensor (Python int)."""
     return ((b * H + h) * T + t) * D + x

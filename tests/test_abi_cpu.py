@@ -91,7 +91,7 @@ def test_diag_workspace_protocol():
     assert n.value == 16 * 8 * 16 * 2048  # one segment: per-token scalars only
     n = ctypes.c_size_t(0)
     assert _diag(B=2, H=16, T=16384, dk=128, dv=128, nbytes=n) == kdn.KDN_OK
-    chunk, S, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
+    chunk, S, _, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
     expect = 16 * 2 * 16 * 16384 + 4 * 2 * 16 * S * 2 * 128 * 128
     assert n.value >= expect and n.value % 256 == 0
     need = n.value
@@ -138,11 +138,7 @@ def test_decode_validation():
 def test_plan_matches_oracle_enumeration(T, S):
     """P-11: the library's chunk and segment bounds equal the oracle's
     enumeration from the definition, bit for bit."""
-    prev = kdn.kdn_set_diag_segments(S)
-    try:
-        chunk, segs, bounds = kdn.kdn_diag_plan(2, 16, T, 128, 128)
-    finally:
-        kdn.kdn_set_diag_segments(prev)
+    chunk, segs, _, bounds = kdn.kdn_diag_plan(2, 16, T, 128, 128, segments=S)
     _, _, ref = oracle.plan(T, chunk, segs)
     assert bounds == ref
     if S:
@@ -150,9 +146,9 @@ def test_plan_matches_oracle_enumeration(T, S):
 
 
 def test_plan_auto_segments_fill_the_chip():
-    _, S1, _ = kdn.kdn_diag_plan(8, 16, 2048, 128, 128)
-    _, S2, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
-    _, S3, _ = kdn.kdn_diag_plan(1, 2, 64, 16, 16)
+    _, S1, _, _ = kdn.kdn_diag_plan(8, 16, 2048, 128, 128)
+    _, S2, _, _ = kdn.kdn_diag_plan(2, 16, 16384, 128, 128)
+    _, S3, _, _ = kdn.kdn_diag_plan(1, 2, 64, 16, 16)
     assert S1 == 1 and S2 == 4 and S3 == 1
 
 

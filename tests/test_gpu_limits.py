@@ -20,7 +20,6 @@ def kdn():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from bayesian_memory_scan_amd import kdnscan
-    kdnscan.kdn_set_diag_segments(0)
     return kdnscan
 
 

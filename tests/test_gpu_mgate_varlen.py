@@ -25,12 +25,6 @@ def kdn():
     return kdnscan
 
 
-@pytest.fixture(autouse=True)
-def _auto_segments(kdn):
-    yield
-    kdn.kdn_set_diag_segments(0)
-
-
 def _heads(B, H):
     return [(b, h) for b in range(B) for h in range(H)]
 
@@ -41,9 +35,10 @@ def _m_inputs(spec):
     return inp
 
 
-def _fwd(kdn, inp):
+def _fwd(kdn, inp, S=0):
     x = gu.upload_diag({**inp, "beta": inp["d"]})   # beta slot unused below
-    res = kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], None, x["d"], x["A"], inp["I_prior"])
+    res = kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], None, x["d"], x["A"], inp["I_prior"],
+                                segments=S)
     torch.cuda.synchronize()
     return res
 
@@ -54,9 +49,8 @@ def _fwd(kdn, inp):
                          ids=lambda s: "x".join(map(str, s)))
 def test_m_gating_forward(kdn, shape, S):
     B, H, T, dk, dv, dt = shape
-    kdn.kdn_set_diag_segments(S)
     inp = _m_inputs(gu.diag_spec(B, H, T, dk, dv, dt, seed=81 + T))
-    gu.compare_diag(inp, _fwd(kdn, inp), _heads(B, H), what=f"M S={S}")
+    gu.compare_diag(inp, _fwd(kdn, inp, S), _heads(B, H), what=f"M S={S}")
 
 
 def test_m_gating_forward_full_size_sampled(kdn):

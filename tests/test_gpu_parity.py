@@ -24,19 +24,13 @@ def kdn():
     return kdnscan
 
 
-@pytest.fixture(autouse=True)
-def _auto_segments(kdn):
-    yield
-    kdn.kdn_set_diag_segments(0)
-
-
 def _all_heads(B, H):
     return [(b, h) for b in range(B) for h in range(H)]
 
 
-def _run_diag(kdn, x, I0=None, mu0=None):
+def _run_diag(kdn, x, I0=None, mu0=None, S=0):
     res = kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], x["A"], 1.0,
-                                I0=I0, mu0=mu0)
+                                I0=I0, mu0=mu0, segments=S)
     torch.cuda.synchronize()
     return res
 
@@ -57,10 +51,9 @@ SMALL = [
 @pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_diag_small(kdn, shape, S):
     B, H, T, dk, dv, dt = shape
-    kdn.kdn_set_diag_segments(S)
     inp = synth.diag_inputs(gu.diag_spec(B, H, T, dk, dv, dt, seed=11))
     print(f"diag small {shape} S={S}", flush=True)
-    res = _run_diag(kdn, gu.upload_diag(inp))
+    res = _run_diag(kdn, gu.upload_diag(inp), S=S)
     gu.compare_diag(inp, res, _all_heads(B, H), what=f"{shape} S={S}")
 
 
@@ -86,11 +79,10 @@ def test_diag_composite_head_sizes(kdn, dk, dv):
     """Two segments, so the first is a composite cut into several sub-segments:
     every (d_k, d_v) pairing of the composite pass's one-wave tiles, with a
     ragged final chunk (T = 601)."""
-    kdn.kdn_set_diag_segments(2)
     dt = "bf16" if (dk + dv) % 64 == 0 else "f32"
     inp = synth.diag_inputs(gu.diag_spec(1, 2, 601, dk, dv, dt, seed=7000 + dk + dv))
     print(f"diag composite dk={dk} dv={dv} {dt}", flush=True)
-    res = _run_diag(kdn, gu.upload_diag(inp))
+    res = _run_diag(kdn, gu.upload_diag(inp), S=2)
     gu.compare_diag(inp, res, _all_heads(1, 2), what=f"composite dk={dk} dv={dv}")
 
 
@@ -101,24 +93,22 @@ def test_diag_frame_restarts_inside_chunks(kdn, dv, S):
     frame restarts two or three times inside every 16-token chunk (not only at
     chunk starts), in the 64-column block kernel (d_v = 128) and the narrow-tile
     kernel (d_v = 32), with a ragged last chunk and with composites (S = 2)."""
-    kdn.kdn_set_diag_segments(S)
     inp = synth.diag_inputs(gu.diag_spec(1, 2, 203, 128, dv, "bf16", seed=8100 + dv))
     inp["A"] = np.full_like(inp["A"], 6.0)
     print(f"diag frame restarts dv={dv} S={S}", flush=True)
-    res = _run_diag(kdn, gu.upload_diag(inp))
+    res = _run_diag(kdn, gu.upload_diag(inp), S=S)
     gu.compare_diag(inp, res, _all_heads(1, 2), what=f"frame restarts dv={dv} S={S}")
 
 
 @pytest.mark.parametrize("S", [1, 4])
 def test_diag_initial_state(kdn, S):
     """Nonzero starting state (I0 != I_prior, mu0 != 0), both segmentings."""
-    kdn.kdn_set_diag_segments(S)
     B, H, T, dk, dv = 2, 2, 90, 64, 128
     inp = synth.diag_inputs(gu.diag_spec(B, H, T, dk, dv, "bf16", seed=5))
     g = np.random.default_rng(3)
     I0 = (0.2 + 3.0 * g.random((B, H, dk, dv))).astype(np.float32)
     mu0 = g.standard_normal((B, H, dk, dv)).astype(np.float32)
-    res = _run_diag(kdn, gu.upload_diag(inp), I0=gu.dev_tensor(I0), mu0=gu.dev_tensor(mu0))
+    res = _run_diag(kdn, gu.upload_diag(inp), I0=gu.dev_tensor(I0), mu0=gu.dev_tensor(mu0), S=S)
     gu.compare_diag(inp, res, _all_heads(B, H), I0=I0.astype(np.float64),
                     mu0=mu0.astype(np.float64), what=f"initial state S={S}")
 
@@ -143,10 +133,9 @@ def test_diag_empty_and_zero_length(kdn):
 
 
 def test_diag_deterministic(kdn):
-    kdn.kdn_set_diag_segments(3)
     x = gu.upload_diag(synth.diag_inputs(gu.diag_spec(2, 2, 200, 128, 128, "bf16", seed=9)))
-    r1 = [t.clone() for t in _run_diag(kdn, x)]
-    r2 = _run_diag(kdn, x)
+    r1 = [t.clone() for t in _run_diag(kdn, x, S=3)]
+    r2 = _run_diag(kdn, x, S=3)
     for a, b in zip(r1, r2):
         assert torch.equal(a, b), "two runs differ bitwise"
 
@@ -157,8 +146,7 @@ def test_diag_segmentings_agree(kdn):
     x = gu.upload_diag(inp)
     ref = oracle.diag_scan(inp)
     for S in (1, 2, 5, 16):
-        kdn.kdn_set_diag_segments(S)
-        gu.compare_diag(inp, _run_diag(kdn, x), _all_heads(1, 2), ref=ref, what=f"S={S}")
+        gu.compare_diag(inp, _run_diag(kdn, x, S=S), _all_heads(1, 2), ref=ref, what=f"S={S}")
 
 
 def test_diag_chaining_in_place(kdn):
@@ -232,13 +220,12 @@ ISO_SMALL = [(1, 2, 100, 16, 16), (2, 3, 5000, 64, 64), (1, 1, 4097, 32, 128), (
 @pytest.mark.parametrize("shape", ISO_SMALL, ids=lambda s: "x".join(map(str, s)))
 def test_iso_small(kdn, shape, S):
     B, H, T, dk, dv = shape
-    kdn.kdn_set_diag_segments(S)
     spec = synth.IsoSpec("iso_test", B, H, T, dk, dv, 31)
     inp = synth.iso_inputs(spec)
     x = gu.upload_iso(inp)
     print(f"iso small {shape} S={S}", flush=True)
     lam, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
-                                                 x["q"], x["k"], x["v"])
+                                                 x["q"], x["k"], x["v"], segments=S)
     torch.cuda.synchronize()
     ref = oracle.iso_scan(inp)
     lam, o, mu_T = lam.cpu().numpy(), o.cpu().numpy(), mu_T.cpu().numpy()
@@ -255,13 +242,12 @@ def test_iso_small(kdn, shape, S):
 def test_iso_head_sizes(kdn, dk, dv, S):
     """Every (d_k, d_v) pairing of the one-wave kernel: row and column tile
     interleaves, 1-4 column tiles per head, ragged last chunk (T = 45)."""
-    kdn.kdn_set_diag_segments(S)
     spec = synth.IsoSpec("iso_sizes", 1, 2, 45, dk, dv, dk * 1000 + dv)
     inp = synth.iso_inputs(spec)
     x = gu.upload_iso(inp)
     print(f"iso head sizes dk={dk} dv={dv} S={S}", flush=True)
     _, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
-                                               x["q"], x["k"], x["v"])
+                                               x["q"], x["k"], x["v"], segments=S)
     torch.cuda.synchronize()
     ref = oracle.iso_scan(inp)
     o, mu_T = o.cpu().numpy(), mu_T.cpu().numpy()
@@ -276,13 +262,12 @@ def test_iso_head_sizes(kdn, dk, dv, S):
 def test_iso_short_sequences(kdn, T, S):
     """Chunks of one token, a single ragged chunk, exact chunk multiples, and
     more segments requested than there are chunks (the plan clamps)."""
-    kdn.kdn_set_diag_segments(S)
     spec = synth.IsoSpec("iso_short", 2, 2, T, 64, 64, 4000 + T)
     inp = synth.iso_inputs(spec)
     x = gu.upload_iso(inp)
     print(f"iso short T={T} S={S}", flush=True)
     _, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
-                                               x["q"], x["k"], x["v"])
+                                               x["q"], x["k"], x["v"], segments=S)
     torch.cuda.synchronize()
     ref = oracle.iso_scan(inp)
     o, mu_T = o.cpu().numpy(), mu_T.cpu().numpy()
@@ -296,7 +281,6 @@ def test_iso_short_sequences(kdn, T, S):
 def test_iso_initial_state(kdn, S):
     """A nonzero starting mean (mu0) and precision (lambda0), both segmentings:
     the starting mean reaches the first segment through the carry pass."""
-    kdn.kdn_set_diag_segments(S)
     B, H, T, dk, dv = 2, 2, 300, 64, 128
     spec = synth.IsoSpec("iso_state", B, H, T, dk, dv, 51)
     inp = synth.iso_inputs(spec)
@@ -306,7 +290,8 @@ def test_iso_initial_state(kdn, S):
     x = gu.upload_iso(inp)
     print(f"iso initial state S={S}", flush=True)
     _, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
-                                               x["q"], x["k"], x["v"], mu0=gu.dev_tensor(mu0))
+                                               x["q"], x["k"], x["v"], mu0=gu.dev_tensor(mu0),
+                                               segments=S)
     torch.cuda.synchronize()
     ref = oracle.iso_scan(inp, mu0=mu0)
     o, mu_T = o.cpu().numpy(), mu_T.cpu().numpy()
@@ -380,10 +365,9 @@ def test_full_diag_b8h16t2048d128(kdn):
 
 @pytest.mark.parametrize("S", [0, 1])
 def test_full_diag_b2h16t16384d128(kdn, S):
-    kdn.kdn_set_diag_segments(S)  # 0 = the automatic plan the bench uses
     spec = synth.workload("diag_b2h16t16384d128_bf16")
     inp = synth.diag_inputs(spec)
-    res = _run_diag(kdn, gu.upload_diag(inp))
+    res = _run_diag(kdn, gu.upload_diag(inp), S=S)   # S = 0: the automatic plan the bench uses
     gu.compare_diag(inp, res, _sample(2, 16, 4, 2), what=f"{spec.name} S={S}")
 
 
