@@ -2,6 +2,7 @@
 // layout and kernel dispatch.  Validation completes before any HIP call.
 #include "kdn_params.h"
 
+#include <atomic>
 #include <cmath>
 
 namespace kdn {
@@ -159,6 +160,105 @@ bool sizes_fit(int64_t B, int64_t H, int64_t T, int64_t D) {
     return n < 4.0e18;
 }
 
+// The no-allocation entry's scratch: one array per GPU, reserved when the
+// code object is loaded.  Host code must not use the array's name as a
+// device address (it is a host-side stand-in): scratch_on_current_device
+// returns the device address, looked up once per device with that device
+// current and kept.
+constexpr size_t kScratchBytes = KDN_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        note_hip_error(e);
+        return KDN_EHIP;
+    }
+    if (dev < 0 || dev >= kMaxDevices) return KDN_EUNSUPPORTED;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        // threads racing here look up the same address; any of them may store it
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || ptr == nullptr) {
+            note_hip_error(e);
+            return KDN_EHIP;
+        }
+        g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+    *out = ptr;
+    return KDN_OK;
+}
+
+// The diagonal forward call.  fixed_scratch: the no-allocation entry, whose
+// workspace is this GPU's scratch array (sub-segments reduced to fit it).
+int diag_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, kdn_dtype in_dtype,
+             const void* q, const void* k, const void* v, const void* beta, const void* d,
+             const float* A, float I_prior, const float* I0, const float* mu0,
+             float* o, float* I_T, float* mu_T, kdn_scan_opts* opts,
+             void* workspace, size_t* workspace_bytes, void* stream, bool fixed_scratch) {
+    if (B < 0 || H < 0 || T < 0 || !opts_ok(opts)) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    if (!finite_positive(I_prior)) return KDN_EINVAL;
+    if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
+    const int64_t BH = B * H;
+    if (BH > 0 && !ok_ptr(A)) return KDN_EINVAL;
+    if (BH > 0 && T > 0) {
+        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(o))
+            return KDN_EINVAL;
+    }
+    if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
+
+    Plan pl = plan_scan(BH, T, d_v, opt_segments(opts));
+    const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
+    if (!grid_fits(BH * pl.S * ntile)) return KDN_EINVAL;
+    // composite pass: one wave per (head, sub-segment, column tile of 16 or 32)
+    if (pl.S > 1 && !grid_fits(BH * (pl.S - 1) * pl.R * (d_v / 16), kWave)) return KDN_EINVAL;
+    DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
+    size_t scratch_cap = 0;
+    if (fixed_scratch) {
+        while (dw.total > kScratchBytes && pl.S > 1 && pl.R > 1) {
+            --pl.R;
+            dw = diag_workspace(BH, T, d_k, d_v, pl);
+        }
+        if (dw.total > kScratchBytes) return KDN_ESCRATCH;
+        if (BH > 0 && dw.total > 0) {
+            const int rc = scratch_on_current_device(&workspace);
+            if (rc != KDN_OK) return rc;
+            scratch_cap = kScratchBytes;
+            workspace_bytes = &scratch_cap;
+        }
+    }
+    report_echo(opts, T > 0 ? BH * pl.S * ntile + (pl.S > 1 ? BH * (pl.S - 1) * pl.R * comp_tiles(d_v) : 0) : 0);
+    const size_t need = dw.total;
+    const int wc = workspace_check(workspace, workspace_bytes, need);
+    if (wc == 1) return KDN_OK;
+    if (wc != KDN_OK) return wc;
+    if (BH == 0) return KDN_OK;
+
+    DiagParams p{};
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
+    p.A = A; p.I0 = I0; p.mu0 = mu0;
+    p.o = o; p.I_T = I_T; p.mu_T = mu_T;
+    char* ws = static_cast<char*>(workspace);
+    p.scal = reinterpret_cast<float4*>(ws);
+    if (pl.S > 1) {
+        p.comp = reinterpret_cast<float*>(ws + dw.scal);
+        p.sub = reinterpret_cast<float*>(ws + dw.scal + dw.comp);
+        p.gsub = reinterpret_cast<float*>(ws + dw.scal + dw.comp + dw.sub);
+    }
+    p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
+    p.S = pl.S; p.nchunks = pl.nchunks;
+    set_echo(p, opts);
+    (void)hipGetLastError();  // launch status below must reflect this call only
+    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
+}
+
+
 }  // namespace
 
 extern "C" {
@@ -207,8 +307,8 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       const float* I0, const float* mu0,
                       float* o, float* I_T, float* mu_T,
                       void* workspace, size_t* workspace_bytes, void* stream) {
-    return kdn_diag_scan_fwd_ex(B, H, T, d_k, d_v, in_dtype, q, k, v, beta, d, A, I_prior, I0, mu0,
-                                o, I_T, mu_T, nullptr, workspace, workspace_bytes, stream);
+    return diag_fwd(B, H, T, d_k, d_v, in_dtype, q, k, v, beta, d, A, I_prior, I0, mu0, o, I_T, mu_T,
+                    nullptr, workspace, workspace_bytes, stream, false);
 }
 
 int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
@@ -219,48 +319,19 @@ int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d
                          const float* I0, const float* mu0,
                          float* o, float* I_T, float* mu_T, kdn_scan_opts* opts,
                          void* workspace, size_t* workspace_bytes, void* stream) {
-    if (B < 0 || H < 0 || T < 0 || !opts_ok(opts)) return KDN_EINVAL;
-    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
-    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
-    if (!finite_positive(I_prior)) return KDN_EINVAL;
-    if (!sizes_fit(B, H, T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
-    const int64_t BH = B * H;
-    if (BH > 0 && !ok_ptr(A)) return KDN_EINVAL;
-    if (BH > 0 && T > 0) {
-        if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(o))
-            return KDN_EINVAL;
-    }
-    if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
+    return diag_fwd(B, H, T, d_k, d_v, in_dtype, q, k, v, beta, d, A, I_prior, I0, mu0, o, I_T, mu_T,
+                    opts, workspace, workspace_bytes, stream, false);
+}
 
-    const Plan pl = plan_scan(BH, T, d_v, opt_segments(opts));
-    const int64_t ntile = d_v / (d_v < 64 ? d_v : 64);
-    if (!grid_fits(BH * pl.S * ntile)) return KDN_EINVAL;
-    // composite pass: one wave per (head, sub-segment, column tile of 16 or 32)
-    if (pl.S > 1 && !grid_fits(BH * (pl.S - 1) * pl.R * (d_v / 16), kWave)) return KDN_EINVAL;
-    report_echo(opts, T > 0 ? BH * pl.S * ntile + (pl.S > 1 ? BH * (pl.S - 1) * pl.R * comp_tiles(d_v) : 0) : 0);
-    const DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
-    const size_t need = dw.total;
-    const int wc = workspace_check(workspace, workspace_bytes, need);
-    if (wc == 1) return KDN_OK;
-    if (wc != KDN_OK) return wc;
-    if (BH == 0) return KDN_OK;
-
-    DiagParams p{};
-    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
-    p.A = A; p.I0 = I0; p.mu0 = mu0;
-    p.o = o; p.I_T = I_T; p.mu_T = mu_T;
-    char* ws = static_cast<char*>(workspace);
-    p.scal = reinterpret_cast<float4*>(ws);
-    if (pl.S > 1) {
-        p.comp = reinterpret_cast<float*>(ws + dw.scal);
-        p.sub = reinterpret_cast<float*>(ws + dw.scal + dw.comp);
-        p.gsub = reinterpret_cast<float*>(ws + dw.scal + dw.comp + dw.sub);
-    }
-    p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
-    p.S = pl.S; p.nchunks = pl.nchunks;
-    set_echo(p, opts);
-    (void)hipGetLastError();  // launch status below must reflect this call only
-    return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
+int kdn_diag_scan_fwd_noalloc(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                              kdn_dtype in_dtype,
+                              const void* q, const void* k, const void* v,
+                              const void* beta, const void* d,
+                              const float* A, float I_prior,
+                              const float* I0, const float* mu0,
+                              float* o, float* I_T, float* mu_T, void* stream) {
+    return diag_fwd(B, H, T, d_k, d_v, in_dtype, q, k, v, beta, d, A, I_prior, I0, mu0, o, I_T, mu_T,
+                    nullptr, nullptr, nullptr, stream, true);
 }
 
 int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,

@@ -22,8 +22,8 @@ import re
 
 __all__ = [
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
-    "KDN_F32", "KDN_BF16", "KDN_ECHO_WORDS", "KdnError", "ScanOpts",
-    "kdn_diag_scan_fwd", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd", "kdn_diag_scan_varlen_fwd",
+    "KDN_ESCRATCH", "KDN_F32", "KDN_BF16", "KDN_ECHO_WORDS", "KdnError", "ScanOpts",
+    "kdn_diag_scan_fwd", "kdn_diag_scan_fwd_noalloc", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd", "kdn_diag_scan_varlen_fwd",
     "kdn_mobius_precision_scan", "kdn_decode_step",
     "kdn_diag_plan", "kdn_status_string", "kdn_last_hip_error",
     "header_functions",
@@ -33,7 +33,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkdnscan.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "kdnscan.h")
 
-KDN_OK, KDN_EINVAL, KDN_EUNSUPPORTED, KDN_EWORKSPACE, KDN_EHIP = 0, -1, -2, -3, -4
+KDN_OK, KDN_EINVAL, KDN_EUNSUPPORTED, KDN_EWORKSPACE, KDN_EHIP, KDN_ESCRATCH = 0, -1, -2, -3, -4, -5
 KDN_F32, KDN_BF16 = 0, 1
 KDN_ECHO_WORDS = 8
 
@@ -76,6 +76,7 @@ _WS = [_vp, _szp, _vp]
 
 lib.kdn_diag_scan_fwd.argtypes = _DIAG_ARGS + _WS
 lib.kdn_diag_scan_fwd_ex.argtypes = _DIAG_ARGS + [_optp] + _WS
+lib.kdn_diag_scan_fwd_noalloc.argtypes = _DIAG_ARGS + [_vp]
 lib.kdn_diag_scan_varlen_fwd.argtypes = _VARLEN_ARGS + _WS
 lib.kdn_diag_scan_varlen_fwd_ex.argtypes = _VARLEN_ARGS + [_optp] + _WS
 lib.kdn_mobius_precision_scan.argtypes = _MOB_ARGS + _WS
@@ -90,7 +91,7 @@ lib.kdn_decode_step.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, 
                                 _vp, _f, _vp, _vp, _vp, _vp]
 lib.kdn_diag_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, ctypes.POINTER(_i32),
                               ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i64), _i32]
-for _fn in (lib.kdn_diag_scan_fwd, lib.kdn_diag_scan_fwd_ex, lib.kdn_diag_scan_varlen_fwd,
+for _fn in (lib.kdn_diag_scan_fwd, lib.kdn_diag_scan_fwd_ex, lib.kdn_diag_scan_fwd_noalloc, lib.kdn_diag_scan_varlen_fwd,
             lib.kdn_diag_scan_varlen_fwd_ex, lib.kdn_mobius_precision_scan,
             lib.kdn_mobius_precision_scan_ex, lib.kdn_diag_noise_scan_fwd, lib.kdn_diag_scan_bwd,
             lib.kdn_decode_step, lib.kdn_diag_plan):
@@ -300,6 +301,45 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
         raise KdnError("kdn_diag_scan_fwd", rc)
     if info is not None:
         info["echo_words"] = opts.echo_words
+    return o, I_T, mu_T
+
+
+def kdn_diag_scan_fwd_noalloc(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
+                              o=None, I_T=None, mu_T=None, want_state=True, stream=None):
+    """kdn_diag_scan_fwd through the no-allocation entry point: the library
+    uses its fixed per-GPU scratch instead of a workspace.  Arguments and
+    results as for kdn_diag_scan_fwd.  Pass o (and I_T, mu_T, or
+    want_state=False) to keep the call itself free of allocations."""
+    torch = _torch()
+    _rank(q, "q", 4)
+    _rank(v, "v", 4)
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    dts, f32 = _in_dtypes(), (torch.float32,)
+    for n, t, shp in (("q", q, (B, H, T, dk)), ("k", k, (B, H, T, dk)), ("v", v, (B, H, T, dv)),
+                      ("beta", beta, (B, H, T, dv)), ("d", d, (B, H, T))):
+        if t is None and n != "beta":
+            raise ValueError(f"{n} is required")
+        _check(t, n, dts, shp)
+    _same_dtype((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d)))
+    state = (B, H, dk, dv)
+    for n, t, shp in (("A", A, (H,)), ("I0", I0, state), ("mu0", mu0, state),
+                      ("o", o, (B, H, T, dv)), ("I_T", I_T, state), ("mu_T", mu_T, state)):
+        _check(t, n, f32, shp)
+    dev = _on_gpu((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d), ("A", A), ("I0", I0),
+                   ("mu0", mu0), ("o", o), ("I_T", I_T), ("mu_T", mu_T)))
+    s = _stream(stream)
+    with torch.cuda.device(dev), torch.cuda.stream(s):
+        if o is None:
+            o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
+        if want_state:
+            I_T = torch.empty(state, dtype=torch.float32, device=dev) if I_T is None else I_T
+            mu_T = torch.empty(state, dtype=torch.float32, device=dev) if mu_T is None else mu_T
+        rc = lib.kdn_diag_scan_fwd_noalloc(B, H, T, dk, dv, _in_dtype(q), _ptr(q), _ptr(k), _ptr(v),
+                                           _ptr(beta), _ptr(d), _ptr(A), float(I_prior), _ptr(I0),
+                                           _ptr(mu0), _ptr(o), _ptr(I_T), _ptr(mu_T), s.cuda_stream)
+    if rc != KDN_OK:
+        raise KdnError("kdn_diag_scan_fwd_noalloc", rc)
     return o, I_T, mu_T
 
 

@@ -65,7 +65,8 @@ enum {
     KDN_EINVAL = -1,        /* bad size, NULL required pointer, misalignment, I_prior <= 0 */
     KDN_EUNSUPPORTED = -2,  /* valid but not implemented (head size outside the list) */
     KDN_EWORKSPACE = -3,    /* workspace missing or too small */
-    KDN_EHIP = -4           /* a HIP launch failed */
+    KDN_EHIP = -4,          /* a HIP launch failed */
+    KDN_ESCRATCH = -5       /* the call needs more than the fixed scratch of the no-allocation entry holds */
 };
 
 /*
@@ -304,6 +305,33 @@ int kdn_mobius_precision_scan_ex(int64_t B, int64_t H, int64_t T,
                                  const float* q, const float* k, const float* v,
                                  const float* mu0, float* o, float* mu_T, kdn_scan_opts* opts,
                                  void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
+ * kdn_diag_scan_fwd for callers that cannot allocate device memory: code
+ * under stream capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and rules as kdn_diag_scan_fwd minus the
+ * workspace: the call uses a fixed scratch array of
+ * KDN_NOALLOC_SCRATCH_BYTES in device memory, one per GPU, reserved when the
+ * library is loaded and held until the process ends.  The call allocates
+ * nothing (no hipMalloc, no hipFree) and its result is the same as the plain
+ * call's; where the plain call's plan would need more scratch than the array
+ * holds, the composite segments are cut into fewer sub-segments (same
+ * results up to rounding), and if even that does not fit it returns
+ * KDN_ESCRATCH.  (Roughly: 16 bytes per head-token of frame scalars, plus,
+ * for segmented long sequences, 8 d_k d_v bytes per head and segment.)
+ * The current device must be the device of `stream`.  Every call on one GPU
+ * shares that GPU's array, which keeps the last call's contents: calls that
+ * overlap on one GPU (other streams, other threads) race and must be ordered
+ * by the caller.
+ */
+#define KDN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int kdn_diag_scan_fwd_noalloc(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                              kdn_dtype in_dtype,
+                              const void* q, const void* k, const void* v,
+                              const void* beta, const void* d,
+                              const float* A, float I_prior,
+                              const float* I0, const float* mu0,
+                              float* o, float* I_T, float* mu_T, void* stream);
 
 /* Human-readable text of a status code; never NULL. */
 const char* kdn_status_string(int status);
