@@ -364,9 +364,9 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 //   * every precision of the wave is at least 2^-24 (checked once: I never
 //     falls below min(I_0, I_prior)), and
 //   * every precision stays below 2^24 through the chunk: checked per chunk
-//     from the wave's largest precision at the chunk start plus the chunk's
-//     largest possible growth, I_prior + 16 max(beta) max(k^2) (maxima taken
-//     while staging);
+//     from the wave's largest precision at the chunk start plus the largest
+//     growth 16 tokens can bring, I_prior + 16 max(beta) max(k^2), with the
+//     maxima running over every token staged so far;
 // and a token whose grouped read-out is not finite (a numerator past the
 // fp32 range) is read out again one reciprocal per entry.  Elsewhere the
 // read-out takes one reciprocal per entry.
@@ -386,14 +386,13 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     constexpr int VW = BF16 ? 8 : 4;
     constexpr int VK = C * DK / VW;
     constexpr int VB = C * CI / VW;
-    constexpr int NVK = (VK + NTH - 1) / NTH;
-    constexpr int NVB = (VB + NTH - 1) / NTH;
-    constexpr int NKW = (VK < NTH ? VK : NTH) / kWave > 0 ? (VK < NTH ? VK : NTH) / kWave : 1;
-    constexpr int NBW = (VB < NTH ? VB : NTH) / kWave > 0 ? (VB < NTH ? VB : NTH) / kWave : 1;
+    // staging jobs of a chunk: VK vectors of k, VK of q, VB of (beta, v), dealt
+    // to threads in that order, NJS per thread
+    constexpr int NJ = 2 * VK + VB;
+    constexpr int NJS = (NJ + NTH - 1) / NTH;
     static_assert(RB == 4 || RB == 8, "key rows per lane: whole groups of four");
     static_assert(DK % (2 * RB) == 0 && NTH <= 1024, "tile shape");
     static_assert(C == 16, "per-token scalars come in 16-token chunks");
-    static_assert(NKW <= W && NBW <= W, "staging waves");
     constexpr float kQuadHi = 16777216.0f;          // 2^24
     constexpr float kQuadLo = 1.0f / 16777216.0f;   // 2^-24
 
@@ -403,12 +402,13 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         float q[C][DK];     // q_t[j] / s_t
         float2 bv[C][CI];   // (beta_i, beta_i v_i)
         float4 ap[C];       // (alpha_t, (1 - alpha_t) I_prior, rho_t of the eta frame, -)
-        float kmax[NKW];    // largest k^2 staged by each k-staging wave
-        float bmax[NBW];    // largest beta staged by each beta-staging wave
         uint32_t restarts;  // bit t: token t restarts the eta frame (rho_t != 1)
     };
     __shared__ Stage stg[2];
     __shared__ float opart[NOB][C][P][CI];
+    // running maxima of k^2 and beta over every token staged so far, as the
+    // bits of non-negative floats (which order like the floats)
+    __shared__ uint32_t run_max[2];
 
     const int tid = threadIdx.x;
     const int lane = tid % kWave;
@@ -498,33 +498,44 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         quad_ok = __builtin_amdgcn_ballot_w64(!(lo >= kQuadLo)) == 0;
     }
 
-    uint4 rk[NVK], rq[NVK], rb[NVB], rv[NVB];
-    float rs[NVK];
+    // A thread's staging jobs: job j < VK is vector j of the chunk's k (its
+    // s k and k^2), VK <= j < 2 VK vector j - VK of q (q / s), then (beta, v)
+    // vectors; the jobs spread over 10 of the 16 waves at d_k = 128, so no
+    // wave carries much staging into the chunk's barrier.
+    uint4 ra[NJS], rb2[NJS];      // raw vectors (k, q or beta; v)
+    float rs[NJS];                // s of the job's token (k and q jobs)
     // frame scalars (rho, P, s, A d) of token tid of the chunk (tid < C), and
     // for tid 0 the scale of the token before the chunk (1 at the run start)
     float4 rsc = make_float4(1.0f, 0.0f, 1.0f, 0.0f);
     float rsp = 1.0f;
     const float4* sch = p.scal + bh * p.T;
+    // the running maxima as this wave last read them
+    float seen_k = 0.0f, seen_b = 0.0f;
 
     auto fetch = [&](int64_t t0, int L) {
 #pragma unroll
-        for (int n = 0; n < NVK; ++n) {
-            const int vi = tid + n * NTH;
-            if (vi < VK && vi * VW < L * DK) {
-                rk[n] = ld16(kh + t0 * DK + static_cast<int64_t>(vi) * VW);
-                rq[n] = ld16(qh + t0 * DK + static_cast<int64_t>(vi) * VW);
-                rs[n] = sch[t0 + vi * VW / DK].z;
-            }
-        }
-#pragma unroll
-        for (int n = 0; n < NVB; ++n) {
-            const int vi = tid + n * NTH;
-            const int row = vi / (CI / VW);
-            const int cv = vi % (CI / VW);
-            if (vi < VB && row < L) {
-                const int64_t off = (t0 + row) * p.dv + cv * VW;
-                rb[n] = bth ? ld16(bth + off) : splat16<BF16>(dh, t0 + row);
-                rv[n] = ld16(vh + off);
+        for (int n = 0; n < NJS; ++n) {
+            const int j = tid + n * NTH;
+            if (j < VK) {
+                if (j * VW < L * DK) {
+                    ra[n] = ld16(kh + t0 * DK + static_cast<int64_t>(j) * VW);
+                    rs[n] = sch[t0 + j * VW / DK].z;
+                }
+            } else if (j < 2 * VK) {
+                const int vi = j - VK;
+                if (vi * VW < L * DK) {
+                    ra[n] = ld16(qh + t0 * DK + static_cast<int64_t>(vi) * VW);
+                    rs[n] = sch[t0 + vi * VW / DK].z;
+                }
+            } else if (j < NJ) {
+                const int vi = j - 2 * VK;
+                const int row = vi / (CI / VW);
+                const int cv = vi % (CI / VW);
+                if (row < L) {
+                    const int64_t off = (t0 + row) * p.dv + cv * VW;
+                    ra[n] = bth ? ld16(bth + off) : splat16<BF16>(dh, t0 + row);
+                    rb2[n] = ld16(vh + off);
+                }
             }
         }
         if (tid < L) rsc = sch[t0 + tid];
@@ -535,42 +546,57 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         Stage& S = stg[nb];
         float mk = 0.0f, mb = 0.0f;
 #pragma unroll
-        for (int n = 0; n < NVK; ++n) {
-            const int vi = tid + n * NTH;
-            if (vi < VK && vi * VW < L * DK) {
-                const int row = vi * VW / DK;
-                const int c0 = vi * VW % DK;
-                float f[VW];
-                widen<BF16>(rk[n], f);
+        for (int n = 0; n < NJS; ++n) {
+            const int j = tid + n * NTH;
+            float f[VW];
+            if (j < VK) {
+                if (j * VW < L * DK) {
+                    const int row = j * VW / DK;
+                    const int c0 = j * VW % DK;
+                    widen<BF16>(ra[n], f);
+                    float ks[VW], k2[VW];
 #pragma unroll
-                for (int e = 0; e < VW; ++e) {
-                    const float k2 = f[e] * f[e];
-                    S.ks[row][c0 + e] = f[e] * rs[n];
-                    S.k2[row][c0 + e] = k2;
-                    mk = fmaxf(mk, k2);
+                    for (int e = 0; e < VW; ++e) {
+                        ks[e] = f[e] * rs[n];
+                        k2[e] = f[e] * f[e];
+                        mk = fmaxf(mk, k2[e]);
+                    }
+                    store_run<VW>(&S.ks[row][c0], ks);
+                    store_run<VW>(&S.k2[row][c0], k2);
                 }
-                const float inv_s = 1.0f / rs[n];
-                widen<BF16>(rq[n], f);
+            } else if (j < 2 * VK) {
+                const int vi = j - VK;
+                if (vi * VW < L * DK) {
+                    const int row = vi * VW / DK;
+                    const int c0 = vi * VW % DK;
+                    const float inv_s = fast_rcp(rs[n]);
+                    widen<BF16>(ra[n], f);
 #pragma unroll
-                for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e] * inv_s;
+                    for (int e = 0; e < VW; ++e) f[e] *= inv_s;
+                    store_run<VW>(&S.q[row][c0], f);
+                }
+            } else if (j < NJ) {
+                const int vi = j - 2 * VK;
+                const int row = vi / (CI / VW);
+                const int c0 = (vi % (CI / VW)) * VW;
+                if (row < L) {
+                    float fv[VW], bv[2 * VW];
+                    widen<BF16>(ra[n], f);
+                    widen<BF16>(rb2[n], fv);
+#pragma unroll
+                    for (int e = 0; e < VW; ++e) {
+                        bv[2 * e] = f[e];
+                        bv[2 * e + 1] = f[e] * fv[e];
+                        mb = fmaxf(mb, f[e]);
+                    }
+                    store_run<2 * VW>(reinterpret_cast<float*>(&S.bv[row][c0]), bv);
+                }
             }
         }
-#pragma unroll
-        for (int n = 0; n < NVB; ++n) {
-            const int vi = tid + n * NTH;
-            const int row = vi / (CI / VW);
-            const int c0 = (vi % (CI / VW)) * VW;
-            if (vi < VB && row < L) {
-                float fv[VW], fb[VW];
-                widen<BF16>(rv[n], fv);
-                widen<BF16>(rb[n], fb);
-#pragma unroll
-                for (int e = 0; e < VW; ++e) {
-                    S.bv[row][c0 + e] = make_float2(fb[e], fb[e] * fv[e]);
-                    mb = fmaxf(mb, fb[e]);
-                }
-            }
-        }
+        // raise the running maxima only where this lane saw more (rarely,
+        // once the first chunks are in)
+        if (mk > seen_k) atomicMax(&run_max[0], __float_as_uint(mk));
+        if (mb > seen_b) atomicMax(&run_max[1], __float_as_uint(mb));
         // per-token (alpha, P, rho): a chunk's first token restarts the eta
         // frame from the previous token's scale
         if (wv == 0) {
@@ -578,14 +604,6 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
             if (tid < L) S.ap[tid] = make_float4(fast_exp(-rsc.w), rsc.y, rho, 0.0f);
             const uint64_t m = __builtin_amdgcn_ballot_w64(tid < L && rho != 1.0f);
             if (tid == 0) S.restarts = static_cast<uint32_t>(m);
-        }
-        if (wv < NKW) {
-            mk = wave_max(mk);
-            if (lane == 0) S.kmax[wv] = mk;
-        }
-        if (wv < NBW) {
-            mb = wave_max(mb);
-            if (lane == 0) S.bmax[wv] = mb;
         }
     };
 
@@ -595,6 +613,8 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         return static_cast<int>(rem < C ? rem : C);
     };
 
+    if (tid < 2) run_max[tid] = 0u;
+    __syncthreads();
     if (nch > 0) {
         fetch(t_begin, chunk_len(0));
         commit(0, chunk_len(0));
@@ -614,12 +634,9 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         // growth does.
         bool quad;
         {
-            float km = S.kmax[0], bm = S.bmax[0];
-#pragma unroll
-            for (int w = 1; w < NKW; ++w) km = fmaxf(km, S.kmax[w]);
-#pragma unroll
-            for (int w = 1; w < NBW; ++w) bm = fmaxf(bm, S.bmax[w]);
-            const float lim = kQuadHi - static_cast<float>(C) * km * bm;
+            seen_k = __uint_as_float(run_max[0]);
+            seen_b = __uint_as_float(run_max[1]);
+            const float lim = kQuadHi - static_cast<float>(C) * seen_k * seen_b;
             float hi = I_prior;
 #pragma unroll
             for (int r = 0; r < RB; ++r)

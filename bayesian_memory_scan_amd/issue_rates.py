@@ -69,12 +69,15 @@ def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--iters", type=int, default=2048)
     ap.add_argument("--wps", default="2,4,8")
+    ap.add_argument("--only", default=None, help="run only the probes whose name contains this")
     a = ap.parse_args(argv)
     lib = load()
     print("| probe | waves/SIMD | VGPRs | ms | clock MHz | per clk per CU @2.4 GHz | "
           "per clk per CU @clock | TFLOP/s (11 flop/entry-step) |")
     print("|---|---|---|---|---|---|---|---|")
     for i in range(lib.kdn_probe_count()):
+        if a.only and a.only not in lib.kdn_probe_name(i).decode():
+            continue
         for wps in (int(x) for x in a.wps.split(",")):
             r = run(lib, i, wps, a.iters)
             tf = f"{r['tflops']:.1f}" if r["mix"] else ""
