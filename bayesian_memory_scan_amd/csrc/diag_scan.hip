@@ -352,6 +352,10 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 // no rescale when a frame restarts.  The information mean is kept scaled,
 // eta~ = s_t eta (s_t as in k_diag), so its update is one fmac with s_t k_j
 // staged; the read-out divides by s_t through the staged query q_j / s_t.
+// The eta frame restarts at every chunk's first token; a chunk with no other
+// restart (the usual case: s stays below e^kFrameLog for 16 tokens) applies
+// that rescale before its tokens and runs them unrolled with no per-token
+// branch, any other chunk checks every token.
 //
 // Read-out.  sum_j q_j mu_j over a lane's key rows is taken four rows at a
 // time with one reciprocal: for rows a, b, c, d of a column,
@@ -701,8 +705,8 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         };
         // One token from its operands: eta frame restart, state update,
         // read-out partial.
-        auto token = [&](int tt, const Ops& o) __attribute__((always_inline)) {
-            if ((restarts >> tt) & 1u) {
+        auto token = [&](int tt, const Ops& o, bool mid_restarts) __attribute__((always_inline)) {
+            if (mid_restarts && ((restarts >> tt) & 1u)) {
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
 #pragma unroll
@@ -729,19 +733,27 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
             if (!done) x = swap32_add(readout_direct(o, 0), readout_direct(o, 1));
             opart[b % NOB][tt][wv][ocol] = x;
         };
-        if (L == C) {
-            // a whole chunk, unrolled; each token's LDS operands are loaded
-            // while the previous token computes
+        if (L == C && (restarts >> 1) == 0u) {
+            // a whole chunk whose frame restarts at most at its first token
+            // (the usual case): that rescale goes first, then the tokens run
+            // unrolled and branch-free, each token's LDS operands loaded while
+            // the previous token computes
             Ops cur = load_ops(0);
+            if (restarts & 1u) {
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+#pragma unroll
+                    for (int cc = 0; cc < 2; ++cc) eta[r][cc] *= cur.ap.z;
+            }
             Unroll<0, C>::run([&](auto u) {
                 constexpr int tt = decltype(u)::value;
                 Ops nxt;
                 if constexpr (tt + 1 < C) nxt = load_ops(tt + 1);
-                token(tt, cur);
+                token(tt, cur, false);
                 if constexpr (tt + 1 < C) cur = nxt;
             });
         } else {
-            for (int tt = 0; tt < L; ++tt) token(tt, load_ops(tt));
+            for (int tt = 0; tt < L; ++tt) token(tt, load_ops(tt), true);
         }
 
         if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
@@ -997,8 +1009,11 @@ int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t s
     const int64_t runs = static_cast<int64_t>(p.nseq) * p.H;
     const int64_t grid = (runs + 7) / 8 * 8 * (p.dv / CI);   // whole groups of 8 runs
     if (grid == 0) return launch_status();
-    const int rc = bf16 ? launch_main<true>(p, dk, CI, grid, st) : launch_main<false>(p, dk, CI, grid, st);
+    int rc = record_event(p.main_begin, st);
     if (rc != KDN_OK) return rc;
+    rc = bf16 ? launch_main<true>(p, dk, CI, grid, st) : launch_main<false>(p, dk, CI, grid, st);
+    if (rc != KDN_OK) return rc;
+    if ((rc = record_event(p.main_end, st)) != KDN_OK) return rc;
     return launch_status();
 }
 
@@ -1049,8 +1064,10 @@ int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int3
         pc.echo_base = g2;   // composite records after the main pass's
         if ((rc = diag_comp_launch(pc, B, dk, bf16, R, st)) != KDN_OK) return rc;
     }
+    if ((rc = record_event(p.main_begin, st)) != KDN_OK) return rc;
     rc = bf16 ? launch_main<true>(p, dk, CI, g2, st) : launch_main<false>(p, dk, CI, g2, st);
     if (rc != KDN_OK) return rc;
+    if ((rc = record_event(p.main_end, st)) != KDN_OK) return rc;
     return launch_status();
 }
 

@@ -354,7 +354,9 @@ int iso_mean_launch(const DiagParams& p, int64_t B, int64_t dk, hipStream_t st) 
         if ((rc = iso_launch<true>(pc, dk, p.dv, grid, st)) != KDN_OK) return rc;
         if ((rc = diag_carry_launch(p, B, dk, true, st)) != KDN_OK) return rc;
     }
-    return iso_launch<false>(p, dk, p.dv, grid, st);
+    if ((rc = record_event(p.main_begin, st)) != KDN_OK) return rc;
+    if ((rc = iso_launch<false>(p, dk, p.dv, grid, st)) != KDN_OK) return rc;
+    return record_event(p.main_end, st);
 }
 
 }  // namespace kdn

@@ -94,6 +94,16 @@ inline int launch_status() {
     return KDN_EHIP;
 }
 
+// A caller's timing event (a hipEvent_t, or NULL for none), recorded on the
+// call's stream.
+inline int record_event(void* ev, hipStream_t st) {
+    if (ev == nullptr) return KDN_OK;
+    const hipError_t e = hipEventRecord(static_cast<hipEvent_t>(ev), st);
+    if (e == hipSuccess) return KDN_OK;
+    note_hip_error(e);
+    return KDN_EHIP;
+}
+
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace kdn

@@ -39,6 +39,8 @@ struct DiagParams {
     int64_t* echo;               // bounds echo (kdn_scan_opts), or NULL
     int64_t echo_cap;            // its capacity in int64 words
     int64_t echo_base;           // first record slot of the launch being made
+    void* main_begin;            // caller's events around the main pass (kdn_scan_opts), or NULL
+    void* main_end;
 };
 
 // ---------------------------------------------------------------------------

@@ -141,11 +141,14 @@ bool opts_ok(const kdn_scan_opts* o) {
     return true;
 }
 int32_t opt_segments(const kdn_scan_opts* o) { return o ? o->segments : 0; }
-void set_echo(DiagParams& p, const kdn_scan_opts* o) {
-    if (o && o->bounds_echo) {
+void apply_opts(DiagParams& p, const kdn_scan_opts* o) {
+    if (o == nullptr) return;
+    if (o->bounds_echo) {
         p.echo = o->bounds_echo;
         p.echo_cap = o->echo_capacity;
     }
+    p.main_begin = o->main_begin;
+    p.main_end = o->main_end;
 }
 void report_echo(kdn_scan_opts* o, int64_t records) {
     if (o) o->echo_words = records * KDN_ECHO_WORDS;
@@ -253,7 +256,7 @@ int diag_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, kdn_dtyp
     }
     p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.S = pl.S; p.nchunks = pl.nchunks;
-    set_echo(p, opts);
+    apply_opts(p, opts);
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_scan_launch(p, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
 }
@@ -389,7 +392,7 @@ int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d
     p.H = H; p.T = total_T; p.dv = d_v; p.I_prior = I_prior;
     p.S = 1; p.nchunks = 0;
     p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
-    set_echo(p, opts);
+    apply_opts(p, opts);
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_varlen_launch(p, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
 }
@@ -588,7 +591,7 @@ int kdn_mobius_precision_scan_ex(int64_t B, int64_t H, int64_t T,
     }
     dp.H = H; dp.T = T; dp.dv = d_v; dp.I_prior = 1.0f;
     dp.S = pl.S; dp.nchunks = pl.nchunks;
-    set_echo(dp, opts);
+    apply_opts(dp, opts);
     return iso_mean_launch(dp, B, d_k, st);
 }
 

@@ -60,9 +60,10 @@ _szp = ctypes.POINTER(ctypes.c_size_t)
 
 
 class ScanOpts(ctypes.Structure):
-    """kdn_scan_opts: per-call segment request and bounds echo."""
+    """kdn_scan_opts: per-call segment request, bounds echo and main-pass events."""
     _fields_ = [("segments", _i32), ("reserved", _i32), ("bounds_echo", _vp),
-                ("echo_capacity", _i64), ("echo_words", _i64)]
+                ("echo_capacity", _i64), ("echo_words", _i64), ("main_begin", _vp),
+                ("main_end", _vp)]
 
 
 _optp = ctypes.POINTER(ScanOpts)
@@ -208,7 +209,11 @@ def _stream(stream):
     return stream
 
 
-def _opts(segments, echo):
+def _opts(segments, echo, timing=None, stream=None):
+    """The options struct of one call.  timing: None or a pair of
+    torch.cuda.Event(enable_timing=True) that the library records right before
+    and right after the call's main pass (events not yet recorded are recorded
+    once on `stream` first, which creates them)."""
     torch = _torch()
     if int(segments) < 0:
         raise ValueError("segments must be >= 0")
@@ -218,6 +223,14 @@ def _opts(segments, echo):
         _check(echo, "echo", (torch.int64,))
         o.bounds_echo = echo.data_ptr()
         o.echo_capacity = echo.numel()
+    if timing is not None:
+        ev = tuple(timing)
+        if len(ev) != 2 or not all(isinstance(e, torch.cuda.Event) for e in ev):
+            raise TypeError("timing must be a pair of torch.cuda.Event")
+        for e in ev:
+            if not e.cuda_event:
+                e.record(stream)
+        o.main_begin, o.main_end = ev[0].cuda_event, ev[1].cuda_event
     return o
 
 
@@ -252,7 +265,7 @@ def _in_dtype(t):
 
 def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
                       o=None, I_T=None, mu_T=None, want_state=True, segments=0, echo=None,
-                      info=None, stream=None):
+                      info=None, timing=None, stream=None):
     """Diagonal-precision scan forward on [B,H,T,.] GPU tensors.
 
     q, k [B,H,T,d_k]; v, beta [B,H,T,d_v]; d [B,H,T] (all float32, or all
@@ -260,8 +273,9 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
     [B,H,d_k,d_v] float32.  beta None selects Palimpsa-M gating (beta_t = d_t).
     segments: 0 = automatic plan, n = n segments.  echo: optional int64 GPU
     tensor that receives the bounds echo (kdn_scan_opts); info: optional dict
-    that receives "echo_words".  Returns (o, I_T, mu_T) (states None when
-    want_state is False).
+    that receives "echo_words"; timing: optional pair of timing-enabled
+    torch.cuda.Event recorded around the main pass.  Returns (o, I_T, mu_T)
+    (states None when want_state is False).
     """
     torch = _torch()
     _rank(q, "q", 4)
@@ -282,7 +296,7 @@ def kdn_diag_scan_fwd(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
     dev = _on_gpu((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d), ("A", A), ("I0", I0),
                    ("mu0", mu0), ("o", o), ("I_T", I_T), ("mu_T", mu_T), ("echo", echo)))
     s = _stream(stream)
-    opts = _opts(segments, echo)
+    opts = _opts(segments, echo, timing, s)
     with torch.cuda.stream(s):
         if o is None:
             o = torch.empty((B, H, T, dv), dtype=torch.float32, device=dev)
@@ -344,7 +358,7 @@ def kdn_diag_scan_fwd_noalloc(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
 
 
 def kdn_diag_scan_varlen_fwd(q, k, v, beta, d, A, I_prior, cu_seqlens, I0=None, mu0=None,
-                             want_state=True, echo=None, info=None, stream=None):
+                             want_state=True, echo=None, info=None, timing=None, stream=None):
     """Diagonal scan over a packed variable-length batch.
 
     q, k [H,total_T,d_k]; v, beta [H,total_T,d_v]; d [H,total_T] (float32 or
@@ -375,7 +389,7 @@ def kdn_diag_scan_varlen_fwd(q, k, v, beta, d, A, I_prior, cu_seqlens, I0=None, 
     dev = _on_gpu((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d), ("A", A),
                    ("cu_seqlens", cu_seqlens), ("I0", I0), ("mu0", mu0), ("echo", echo)))
     s = _stream(stream)
-    opts = _opts(0, echo)
+    opts = _opts(0, echo, timing, s)
     with torch.cuda.stream(s):
         o = torch.empty((H, T, dv), dtype=torch.float32, device=dev)
         I_T = mu_T = None
@@ -500,7 +514,7 @@ def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_
 
 def kdn_mobius_precision_scan(a, p, Lam, lambda0=None, q=None, k=None, v=None, mu0=None,
                               want_lambda=True, want_state=True, segments=0, echo=None,
-                              info=None, stream=None):
+                              info=None, timing=None, stream=None):
     """Isotropic filter: Mobius precision scan, then (if q, k, v given) the gated mean scan.
 
     a, p, Lam [B,H,T] float32; lambda0 [B,H] or None (-> 1); q, k [B,H,T,d_k],
@@ -532,7 +546,7 @@ def kdn_mobius_precision_scan(a, p, Lam, lambda0=None, q=None, k=None, v=None, m
     dev = _on_gpu((("a", a), ("p", p), ("Lambda", Lam), ("lambda0", lambda0), ("q", q), ("k", k),
                    ("v", v), ("mu0", mu0), ("echo", echo)))
     s = _stream(stream)
-    opts = _opts(segments, echo)
+    opts = _opts(segments, echo, timing, s)
     with torch.cuda.stream(s):
         lam = torch.empty((B, H, T), dtype=torch.float32, device=dev) if want_lambda else None
         o = mu_T = None

@@ -1,15 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of the diagonal-precision scan forward on one MI355X.
 
-Default workload: B=8, H=16, T=2048, d_k=d_v=128, bf16 inputs, fp32 state
-and output (a 760M-class layer shape).  A step is one kdn_diag_scan_fwd call
-over that batch, inputs already resident in HBM.  Prints one JSON line with
-tokens/s (tokens = B*T positions, all heads), the roofline of the dominant
-kernel (timed live with HIP events on the launch stream) and the fp64 CPU
-oracle timed on a bounded sample of the same workload.
+Default workload: B=2, H=16, T=16384, d_k=d_v=128, bf16 inputs, fp32 state
+and output: the largest single-GPU diagonal configuration, a long sequence
+that the plan cuts into segments (segment composites + ordered carry + the
+main pass).  A step is one kdn_diag_scan_fwd call over that batch, inputs
+already resident in HBM.  Prints one JSON line with tokens/s (tokens = B*T
+positions, all heads) from the wall clock, the roofline of the dominant
+kernel (the main pass, timed live by HIP events that the library records
+around that launch on the launch stream), the whole call's event times, the
+fp64 CPU oracle timed on a bounded sample of the same workload, and the
+error of the GPU output on that sample against the oracle.
 
-Other workloads (--workload) print the same fields for the decode step and
-the isotropic scan; they are not the headline line.
+Other workloads (--workload) print the same fields for the short-sequence
+batch (B=8, H=16, T=2048), Palimpsa-M gating, the packed variable-length
+batch, the backward pass, the process-noise variant, the decode step and the
+isotropic scan; they are not the headline line.
 """
 from __future__ import annotations
 
@@ -43,9 +49,11 @@ NOISE_FLOPS_PER_ENTRY_STEP = 17
 def _args():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="diag_b8h16t2048d128_bf16")
+    # about 0.6 s of timed and warm-up work on the default workload: enough for
+    # the clocks to settle, far inside a minute
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--workload", default="diag_b2h16t16384d128_bf16")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
@@ -71,23 +79,72 @@ def _up(x, torch, dev):
     return torch.from_numpy(x.view(np.int16) if x.dtype == np.uint16 else x).to(dev)
 
 
-def _time_steps(torch, step, steps, warmup):
-    """Warmup, then `steps` timed steps; wall clock plus per-step HIP events on
-    the current stream (the stream every launch goes to)."""
+def _stats(ms):
+    v = sorted(ms)
+    n = len(v)
+    med = v[n // 2] if n % 2 else 0.5 * (v[n // 2 - 1] + v[n // 2])
+    return {"avg": sum(v) / n, "median": med, "min": v[0], "max": v[-1]}
+
+
+class Timing:
+    """Wall clock of the timed steps, per-step HIP events around the whole
+    call, and (for calls that take them) per-step events that the library
+    records right before and after its main pass, all on the current stream
+    (the stream every launch goes to)."""
+
+    def __init__(self, wall, call, main):
+        self.wall, self.call, self.main = wall, call, main
+
+    def kernel(self):
+        """Event statistics of the dominant kernel: the main pass where the
+        call records it, else the whole call."""
+        return self.main or self.call
+
+    def fields(self):
+        k = self.kernel()
+        out = {"launch_ms_avg": k["avg"], "launch_ms_median": k["median"], "launch_ms_min": k["min"],
+               "call_ms_avg": self.call["avg"], "call_ms_median": self.call["median"],
+               "call_ms_min": self.call["min"],
+               "timed_kernel": "main pass" if self.main else "whole call"}
+        return out
+
+
+def _time_steps(torch, step, steps, warmup, main_events=False):
+    """Warmup, then `steps` timed steps.  step(timing) runs one call; with
+    main_events it passes the call a pair of events to record around its main
+    pass, else None."""
     for _ in range(warmup):
-        step()
+        step(None)
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    mk = lambda: torch.cuda.Event(enable_timing=True)
+    ev = [(mk(), mk()) for _ in range(steps)]
+    mev = [(mk(), mk()) for _ in range(steps)] if main_events else [None] * steps
+    if main_events:   # create the library's events before the clock starts
+        for a, b in mev:
+            a.record()
+            b.record()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for e0, e1 in ev:
+    for (e0, e1), m in zip(ev, mev):
         e0.record()
-        step()
+        step(m)
         e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = [e0.elapsed_time(e1) for e0, e1 in ev]
-    return wall, sum(per) / len(per), min(per)
+    call = _stats([e0.elapsed_time(e1) for e0, e1 in ev])
+    main = _stats([a.elapsed_time(b) for a, b in mev]) if main_events else None
+    return Timing(wall, call, main)
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def _cpu_threads():
@@ -108,13 +165,41 @@ def cpu_baseline_diag(inp, spec, target_s):
     n = max(1, min(len(heads_all), int(target_s / max(t1.seconds, 1e-3) * threads)))
     heads = heads_all[:n]
     with oracle.Timer() as t:
-        oracle.diag_scan(inp, heads=heads, threads=threads)
+        ref = oracle.diag_scan(inp, heads=heads, threads=threads)
     T = spec.prefix + spec.T
     tokens = n * T / spec.H
     return {"value": tokens / t.seconds, "unit": "tokens/s", "cores": min(threads, n),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{n} of {len(heads_all)} heads x {T} tokens, fp64 sequential oracle, "
-                      f"{t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
+                      f"{t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}, ref
+
+
+def parity_report(o_gpu, ref, what="o"):
+    """The GPU output of the sampled heads against the oracle's: the acceptance
+    measure max |o - o_ref| / s_ref (s_ref = sum_j |q_j mu_ref[j,i]|, which
+    bounds |o_ref|), and the plain relative error over the elements with
+    |o_ref| >= 1e-2 rms(o_ref), where it is well posed."""
+    import numpy as np
+    worst_s, worst_rel, n_large, n_all, rels = 0.0, 0.0, 0, 0, []
+    for (b, h), r in ref.items():
+        og = o_gpu[b, h].astype(np.float64)
+        oref = np.asarray(r["o"], dtype=np.float64)
+        err = np.abs(og - oref)
+        worst_s = max(worst_s, float(np.max(err / (np.asarray(r["s"]) + 1e-30))))
+        rms = float(np.sqrt(np.mean(oref * oref)))
+        big = np.abs(oref) >= 1e-2 * rms
+        if big.any():
+            rel = err[big] / np.abs(oref[big])
+            worst_rel = max(worst_rel, float(np.max(rel)))
+            rels.append(rel)
+        n_large += int(big.sum())
+        n_all += oref.size
+    allrel = np.concatenate(rels) if rels else np.zeros(1)
+    return {"of": what, "heads": len(ref), "max_err_over_s_ref": worst_s,
+            "acceptance": "max_err_over_s_ref <= 1e-4",
+            "max_rel_err_large": worst_rel, "median_rel_err_large": float(np.median(allrel)),
+            "p999_rel_err_large": float(np.quantile(allrel, 0.999)),
+            "large_elements": n_large, "elements": n_all}
 
 
 def cpu_baseline_bwd(inp, grads, spec, target_s):
@@ -128,7 +213,7 @@ def cpu_baseline_bwd(inp, grads, spec, target_s):
     with oracle.Timer() as t:
         oracle.diag_scan_bwd(inp, grads["d_o"], heads=heads_all[:n], threads=threads)
     return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
-            "cores": min(threads, n), "kind": "oracle",
+            "cores": min(threads, n), "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle "
                       f"gradient, {t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
 
@@ -148,6 +233,7 @@ def cpu_baseline_varlen(inp, spec, target_s):
     with oracle.Timer() as t:
         oracle.diag_scan_varlen(inp, cu[:n + 1], threads=threads)
     return {"value": cu[n] / t.seconds, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"first {n} of {spec.N} sequences ({cu[n]} of {spec.total_T} packed tokens) x "
                       f"{spec.H} heads, fp64 sequential oracle, {t.seconds:.1f} s wall"}
 
@@ -162,7 +248,7 @@ def cpu_baseline_noise(inp, spec, target_s):
     with oracle.Timer() as t:
         oracle.diag_noise_scan(inp, heads=heads_all[:n], threads=threads)
     return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
-            "cores": min(threads, n), "kind": "oracle",
+            "cores": min(threads, n), "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle, "
                       f"{t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
 
@@ -177,7 +263,7 @@ def cpu_baseline_iso(inp, spec, target_s):
     with oracle.Timer() as t:
         oracle.iso_scan(inp, heads=heads_all[:n], threads=threads)
     return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
-            "cores": min(threads, n), "kind": "oracle",
+            "cores": min(threads, n), "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle, "
                       f"{t.seconds:.1f} s wall"}
 
@@ -207,11 +293,12 @@ def main():
         st = torch.empty((2, spec.B, spec.H, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
         _, S, _, _ = kdn.kdn_diag_plan(spec.B, spec.H, spec.T, spec.d_k, spec.d_v)
 
-        def step():
+        def step(m):
             kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], x["A"],
-                                  spec.I_prior, o=o, I_T=st[0], mu_T=st[1])
+                                  spec.I_prior, o=o, I_T=st[0], mu_T=st[1], timing=m)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup, main_events=True)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         tokens = spec.B * spec.T
         flops = DIAG_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
         achieved = flops / (ev_ms * 1e-3) / 1e12
@@ -224,13 +311,16 @@ def main():
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min,
+                         **tm.fields(),
                          "kernels_per_step": 2 if S == 1 else 4,
-                         "note": "events bracket the whole call: prep (<1 %) + main pass "
-                                 "(+ composite and carry passes when segments > 1)"},
+                         "note": "achieved: algorithmic flops of every entry-step over the main "
+                                 "pass's own event time; call_ms_*: the whole call (frame "
+                                 "scalars + main pass, + composite and carry passes when "
+                                 "segments > 1)"},
         })
         if not a.no_cpu:
-            out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+            out["cpu_baseline"], ref = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+            out["parity"] = parity_report(o.cpu().numpy(), ref)
     elif a.workload.startswith("diagm_"):
         # Palimpsa-M gating: the step gate d_t is also the input gate (no beta input)
         inp = synth.diag_inputs(spec)
@@ -239,11 +329,12 @@ def main():
         o = torch.empty((spec.B, spec.H, spec.T, spec.d_v), dtype=torch.float32, device=dev)
         st = torch.empty((2, spec.B, spec.H, spec.d_k, spec.d_v), dtype=torch.float32, device=dev)
 
-        def step():
+        def step(m):
             kdn.kdn_diag_scan_fwd(x["q"], x["k"], x["v"], None, x["d"], x["A"], spec.I_prior,
-                                  o=o, I_T=st[0], mu_T=st[1])
+                                  o=o, I_T=st[0], mu_T=st[1], timing=m)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup, main_events=True)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         flops = DIAG_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
         achieved = flops / (ev_ms * 1e-3) / 1e12
         out.update({
@@ -256,21 +347,23 @@ def main():
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+                         **tm.fields()},
         })
         if not a.no_cpu:
-            out["cpu_baseline"] = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+            out["cpu_baseline"], ref = cpu_baseline_diag(inp, spec, a.cpu_seconds)
+            out["parity"] = parity_report(o.cpu().numpy(), ref)
     elif a.workload.startswith("varlen_"):
         inp = synth.varlen_inputs(spec)
         x = {n: _up(inp[n][0], torch, dev) for n in ("q", "k", "v", "beta", "d")}
         A = _up(inp["A"], torch, dev)
         cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
 
-        def step():
+        def step(m):
             kdn.kdn_diag_scan_varlen_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], A,
-                                         spec.I_prior, cu)
+                                         spec.I_prior, cu, timing=m)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup, main_events=True)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         flops = DIAG_FLOPS_PER_ENTRY_STEP * spec.H * spec.total_T * spec.d_k * spec.d_v
         achieved = flops / (ev_ms * 1e-3) / 1e12
         lens = [int(b - a_) for a_, b in zip(inp["cu_seqlens"][:-1], inp["cu_seqlens"][1:])]
@@ -285,7 +378,7 @@ def main():
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+                         **tm.fields()},
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_varlen(inp, spec, a.cpu_seconds)
@@ -293,10 +386,11 @@ def main():
         inp = synth.noise_inputs(spec)
         x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "a", "p")}
 
-        def step():
+        def step(_m):
             kdn.kdn_diag_noise_scan_fwd(x["q"], x["k"], x["v"], x["beta"], x["a"], x["p"])
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         flops = NOISE_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
         achieved = flops / (ev_ms * 1e-3) / 1e12
         out.update({
@@ -309,7 +403,7 @@ def main():
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_noise.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+                         **tm.fields()},
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_noise(inp, spec, a.cpu_seconds)
@@ -319,11 +413,12 @@ def main():
         x = {n: _up(inp[n], torch, dev) for n in ("q", "k", "v", "beta", "d", "A")}
         d_o = _up(grads["d_o"], torch, dev)
 
-        def step():
+        def step(_m):
             kdn.kdn_diag_scan_bwd(x["q"], x["k"], x["v"], x["beta"], x["d"], x["A"],
                                   spec.I_prior, d_o)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         flops = BWD_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
         achieved = flops / (ev_ms * 1e-3) / 1e12
         out.update({
@@ -336,7 +431,7 @@ def main():
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_bwd.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min,
+                         **tm.fields(),
                          "note": "events bracket the whole call: frame scalars, checkpoints, "
                                  "reverse pass and finishing sums; traffic is the reverse pass"},
         })
@@ -353,11 +448,12 @@ def main():
         y = {n: _up(inp[n][:, :, P], torch, dev) for n in ("q", "k", "v", "beta", "d")}
         o = torch.empty((spec.B, spec.H, spec.d_v), dtype=torch.float32, device=dev)
 
-        def step():
+        def step(_m):
             kdn.kdn_decode_step(y["q"], y["k"], y["v"], y["beta"], y["d"], A, spec.I_prior,
                                 I, mu, o=o)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         BH = spec.B * spec.H
         nbytes = BH * (4 * 4 * spec.d_k * spec.d_v + 2 * (2 * spec.d_k + 2 * spec.d_v + 1)
                        + 4 * spec.d_v)
@@ -371,19 +467,20 @@ def main():
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                          "traffic": _traffic("decode.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min},
+                         **tm.fields()},
         })
         if not a.no_cpu:
-            out["cpu_baseline"] = cpu_baseline_diag(inp, spec.with_(B=8), a.cpu_seconds)
+            out["cpu_baseline"], _ = cpu_baseline_diag(inp, spec.with_(B=8), a.cpu_seconds)
     elif a.workload.startswith("iso_"):
         inp = synth.iso_inputs(spec)
         x = {n: _up(inp[n], torch, dev) for n in ("a", "p", "Lambda", "q", "k", "v", "lambda0")}
 
-        def step():
+        def step(m):
             kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"], x["q"],
-                                          x["k"], x["v"])
+                                          x["k"], x["v"], timing=m)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup, main_events=True)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         flops = ISO_FLOPS_PER_ENTRY_STEP * spec.B * spec.H * spec.T * spec.d_k * spec.d_v
         achieved = flops / (ev_ms * 1e-3) / 1e12
         out.update({
@@ -397,7 +494,7 @@ def main():
             "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("iso_scan.hip", f"traffic_{spec.name}.json"),
-                         "launch_ms_avg": ev_ms, "launch_ms_min": ev_min,
+                         **tm.fields(),
                          "note": "whole step (all kernels) timed by events; traffic is the "
                                  "main mean-scan pass"},
         })
@@ -410,17 +507,18 @@ def main():
         src = torch.ones(n, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
 
-        def step():
+        def step(_m):
             dst.copy_(src)
 
-        wall, ev_ms, ev_min = _time_steps(torch, step, a.steps, a.warmup)
+        tm = _time_steps(torch, step, a.steps, a.warmup)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
         gbs = 2 * 4 * n / (ev_ms * 1e-3) / 1e9
         out.update({"metric": "copy GB/s (read + write)", "value": gbs, "unit": "GB/s",
                     "ms_per_step": wall / a.steps * 1e3,
                     "config": {"workload": "copy_1gib", "bytes_read": 4 * n, "bytes_written": 4 * n},
                     "roofline": {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": gbs / PEAK_HBM_GBS, "traffic": None,
-                                 "launch_ms_avg": ev_ms, "launch_ms_min": ev_min}})
+                                 **tm.fields()}})
     else:
         raise SystemExit(f"unknown workload {a.workload}")
 

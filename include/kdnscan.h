@@ -263,6 +263,12 @@ int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, int
  *     kind k sits at a fixed slot; records that would pass echo_capacity are
  *     dropped; slots of work units with nothing to do stay untouched (clear
  *     the buffer first).  For testing the integer bookkeeping.
+ *   main_begin / main_end: hipEvent_t handles, or NULL.  Each given event is
+ *     recorded on the call's stream right before (main_begin) and right after
+ *     (main_end) the call's main pass, the kernel that reads every token and
+ *     writes o, so a caller can time that kernel apart from the frame-scalar
+ *     and segment-composite passes around it.  Not recorded when the call has
+ *     no main pass (B*H == 0 or T == 0); a failed record returns KDN_EHIP.
  *   echo_words (out): the words the call's records span (written on every
  *     call, queries included).
  */
@@ -273,6 +279,8 @@ typedef struct kdn_scan_opts {
     int64_t* bounds_echo;
     int64_t echo_capacity;
     int64_t echo_words;
+    void* main_begin;
+    void* main_end;
 } kdn_scan_opts;
 
 /* kdn_diag_scan_fwd with options (opts may be NULL). */

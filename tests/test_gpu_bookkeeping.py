@@ -243,3 +243,29 @@ def test_side_stream(kdn):
     for (b, h), r in iref.items():
         gu.check_rel(lam[b, h].cpu().numpy(), r["lambda"], "side stream lambda")
         gu.check_o(io[b, h].cpu().numpy(), r, "side stream iso o")
+
+
+def test_main_pass_events(kdn):
+    """The events of the options struct bracket the main pass alone: the
+    composite passes come before main_begin, and the main pass sits inside
+    the whole call's events (the benchmark times the main pass with them)."""
+    B, H, T, dk, dv = 1, 4, 4000, 128, 128
+    q, k, v, beta, d, A = _zeros_diag(B, H, T, dk, dv)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    print("main-pass events, diagonal S=3", flush=True)
+    ev[0].record()
+    kdn.kdn_diag_scan_fwd(q, k, v, beta, d, A, 1.0, segments=3, timing=(ev[1], ev[2]))
+    ev[3].record()
+    torch.cuda.synchronize()
+    before, main, call = ev[0].elapsed_time(ev[1]), ev[1].elapsed_time(ev[2]), ev[0].elapsed_time(ev[3])
+    assert 0 < main <= call and before > 0, (before, main, call)
+    # the isotropic call and the packed batch record them too
+    f = lambda *s: torch.rand(s, device="cuda") + 0.5
+    kdn.kdn_mobius_precision_scan(f(1, 2, 300), f(1, 2, 300), f(1, 2, 300), q=f(1, 2, 300, 64),
+                                  k=f(1, 2, 300, 64), v=f(1, 2, 300, 64), timing=(ev[1], ev[2]))
+    cu = torch.tensor([0, 100, 300], dtype=torch.int64, device="cuda")
+    c = lambda x: x[0, :2, :300].contiguous()
+    kdn.kdn_diag_scan_varlen_fwd(c(q), c(k), c(v), c(beta), c(d), A[:2].contiguous(), 1.0, cu,
+                                 timing=(ev[0], ev[3]))
+    torch.cuda.synchronize()
+    assert ev[1].elapsed_time(ev[2]) > 0 and ev[0].elapsed_time(ev[3]) > 0
