@@ -43,8 +43,15 @@ __device__ __forceinline__ f32x4c mfma4c(float a, float b, f32x4c c) {
 
 constexpr int kCompCols = 32;   // value columns per wave: 2 x MT x 2 x 4 accumulator registers
 
-// Column tiles of one head in the composite pass.
-int comp_tiles(int64_t dv) { return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1; }
+// Wave tiles of one head in the composite pass: fp32 inputs take 32-column
+// tiles with every key row, bf16 inputs tiles of at most 64 x 64 entries.
+constexpr int kCompBfEdge = 64;
+int comp_tiles(int64_t dk, int64_t dv, bool bf16) {
+    if (!bf16) return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1;
+    const int64_t tr = dk > kCompBfEdge ? dk / kCompBfEdge : 1;
+    const int64_t tc = dv > kCompBfEdge ? dv / kCompBfEdge : 1;
+    return static_cast<int>(tr * tc);
+}
 
 template <int DK, int NC, bool BF16>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(BF16 || DK < 128 ? 2 : 1)))
@@ -200,6 +207,269 @@ void k_diag_comp(DiagParams p, int32_t R) {
     if (lane == 0 && tile == 0) p.gsub[slot] = fast_exp(-Rsum);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: the same two contractions on v_mfma_f32_16x16x32_bf16, with
+// every product exact.
+//
+// bf16 keys are exact in one bf16 limb, so X takes A = k (one limb) against
+// B = w beta v.  J takes A = w k^2 against B = beta (exact in one limb).  The
+// fp32 factors w beta v and w k^2 are cut into three bf16 limbs by truncation:
+// hi = x with the low 16 bits of its pattern cleared, then the same on
+// x - hi, and the rest, which has at most 8 significant bits, is exact in
+// bf16.  So hi + mid + lo == x exactly, every limb product is exact in the
+// MFMA's fp32 accumulation, and
+//   J = sum_limbs (w k^2)_limb^T beta,   X = k^T sum_limbs (w beta v)_limb
+// accumulate the same products as fp32 arithmetic on the rounded fp32
+// factors: six MFMAs of 16x16x32 (bf16 rate, about 14x that of
+// 16x16x4 fp32 measured on gfx950) per 16 x 16 tile and 32 tokens.
+//
+// One wave per (head, sub-segment, tile of MT x NT 16 x 16 tiles, at most
+// 64 x 64 entries).  Operand layout of 16x16x32: lane (c, g) holds
+// A[row c][k = 8g .. 8g+7] and B[k = 8g .. 8g+7][column c], D[rows 4g .. 4g+3]
+// [column c].  Rows and columns interleave as in the fp32 kernel: tile (m, n)
+// row c is key row rb + MT c + m and column c is value column cb + NT c + n,
+// so one lane's keys of a token are one contiguous run (MT elements), and
+// likewise its beta and v.  Token k of a 32-token block is 8g + e; pairs of
+// consecutive tokens share one 32-bit operand word (low half the earlier).
+// Blocks are visited last to first, with the decay weights built by additions
+// as in the fp32 kernel.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8c __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4c __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4c mfma_bf(u32x4c a, u32x4c b, f32x4c c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8c, a), __builtin_bit_cast(bf16x8c, b),
+                                                   c, 0, 0, 0);
+}
+
+// The top halves of two fp32 patterns as one bf16 pair: a in the low half.
+__device__ __forceinline__ uint32_t pack_top(uint32_t a, uint32_t b) {
+    return (a >> 16) | (b & 0xffff0000u);
+}
+
+// Three-limb split of the pair (xa, xb): limb words l[0..2], with
+// l[0] + l[1] + l[2] == x exactly in each half.
+// (No contraction here: fusing x - hi with the product that made x would
+// split the unrounded product instead of x.)
+__device__ __forceinline__ void split3(float xa, float xb, uint32_t& l0, uint32_t& l1, uint32_t& l2) {
+#pragma clang fp contract(off)
+    const uint32_t ua = __float_as_uint(xa), ub = __float_as_uint(xb);
+    l0 = pack_top(ua, ub);
+    const float ra = xa - __uint_as_float(ua & 0xffff0000u);
+    const float rb = xb - __uint_as_float(ub & 0xffff0000u);
+    const uint32_t va = __float_as_uint(ra), vb = __float_as_uint(rb);
+    l1 = pack_top(va, vb);
+    const float sa = ra - __uint_as_float(va & 0xffff0000u);
+    const float sb = rb - __uint_as_float(vb & 0xffff0000u);
+    l2 = pack_top(__float_as_uint(sa), __float_as_uint(sb));
+}
+
+// bf16 element e (0-based) of a run held as 32-bit words, widened to fp32.
+template <int N>
+__device__ __forceinline__ float bf_elem(const uint32_t (&w)[N], int e) {
+    return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
+}
+template <int N>
+__device__ __forceinline__ uint32_t bf_bits(const uint32_t (&w)[N], int e) {
+    return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+}
+
+// n 16-bit elements (n = 1, 2, 4) at byte offset off, as 32-bit words.
+template <int NW>
+__device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off, int n, uint32_t (&w)[NW]) {
+    if (n == 4) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+        w[0] = u[0];
+        if constexpr (NW > 1) w[1] = u[1];
+    } else if (n == 2) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+    } else {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+}
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R) {
+    constexpr int KB = 32;                                     // tokens per k-step
+    constexpr int MT = (DK > kCompBfEdge ? kCompBfEdge : DK) / 16;
+    constexpr int NT = (DV > kCompBfEdge ? kCompBfEdge : DV) / 16;
+    constexpr int TC = DV / (16 * NT);                         // wave tiles across the columns
+    constexpr int TILES = (DK / (16 * MT)) * TC;
+    constexpr int KW = (MT + 1) / 2;                           // 32-bit words of a lane's key run
+    constexpr int BW = (NT + 1) / 2;                           // ... of its beta / v run
+    static_assert(MT == 1 || MT == 2 || MT == 4, "key rows per lane run");
+    static_assert(NT == 1 || NT == 2 || NT == 4, "value columns per lane run");
+
+    const int lane = threadIdx.x;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int nsub = (p.S - 1) * R;
+    const int64_t id = xcd_local_id();       // a sub-segment's tiles share an XCD
+    const int tile = static_cast<int>(id % TILES);
+    const int64_t rest = id / TILES;
+    const int sr = static_cast<int>(rest % nsub);
+    const int64_t bh = rest / nsub;
+    const int seg = sr / R;
+    const int sub = sr % R;
+    int64_t t_begin, t_end;
+    sub_tokens(p, 16, R, seg, sub, t_begin, t_end);
+    if (lane == 0) echo_bounds(p, blockIdx.x, 2, bh, seg, sub, t_begin, t_end, tile);
+    const int rb = (tile / TC) * 16 * MT;    // first key row of the wave tile
+    const int cb = (tile % TC) * 16 * NT;    // first value column
+    const int64_t DV_ = p.dv;
+
+    const uint16_t* kh = static_cast<const uint16_t*>(p.k) + bh * p.T * DK;
+    const uint16_t* vh = static_cast<const uint16_t*>(p.v) + bh * p.T * DV_;
+    // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
+    const uint16_t* bth = p.beta ? static_cast<const uint16_t*>(p.beta) + bh * p.T * DV_ : nullptr;
+    const uint16_t* dh = static_cast<const uint16_t*>(p.d) + bh * p.T;
+    const float4* sch = p.scal + bh * p.T;
+
+    f32x4c J[MT][NT], X[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            J[m][n] = f32x4c{0.0f, 0.0f, 0.0f, 0.0f};
+            X[m][n] = J[m][n];
+        }
+
+    // one block's raw operands in lane (c, g): tokens 8g + e
+    struct Raw {
+        uint32_t k[8][KW];   // k_t[rb + MT c .. + MT)
+        uint32_t b[8][BW];   // beta_t[cb + NT c .. + NT)  (or d_t under Palimpsa-M gating)
+        uint32_t v[8][BW];   // v_t[cb + NT c .. + NT)
+        float ad;            // A d of token tb + (lane % 32) (0 past the end)
+    };
+    // tokens of the block at tb that exist (0 for a block before the sub-segment)
+    auto block_len = [&](int64_t tb) -> int64_t {
+        const int64_t L0 = t_end - tb;
+        return (tb < t_begin || L0 < 0) ? 0 : (L0 < KB ? L0 : KB);
+    };
+    auto load_k = [&](int64_t tb, Raw& x) __attribute__((always_inline)) {
+        const int64_t L = block_len(tb);
+        const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kh + tb * DK, L * DK * 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            buf_words<KW>(rk, static_cast<uint32_t>(((8 * g + e) * DK + rb + MT * c) * 2), MT, x.k[e]);
+    };
+    auto load_bv = [&](int64_t tb, Raw& x) __attribute__((always_inline)) {
+        const int64_t L = block_len(tb);
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vh + tb * DV_, L * DV_ * 2);
+        const __amdgpu_buffer_rsrc_t rb_ = bth ? buf_rsrc(bth + tb * DV_, L * DV_ * 2) : buf_rsrc(dh + tb, L * 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s_ = 8 * g + e;
+            buf_words<BW>(rv, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.v[e]);
+            if (bth) {
+                buf_words<BW>(rb_, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.b[e]);
+            } else {
+                const uint32_t d1 = __builtin_amdgcn_raw_buffer_load_b16(rb_, static_cast<uint32_t>(s_ * 2), 0, 0);
+#pragma unroll
+                for (int h = 0; h < BW; ++h) x.b[e][h] = d1 | (d1 << 16);
+            }
+        }
+        float ad[1];
+        buf_load<1>(buf_rsrc(sch + tb, L * 16), static_cast<uint32_t>((lane & 31) * 16 + 12), ad);
+        x.ad = ad[0];
+    };
+
+    float Rsum = 0.0f;
+    // One block: weights, B operands, then (with the next block's beta and v
+    // loading into the registers just freed) the A operands and MFMAs row
+    // tile by row tile, then the next block's keys.
+    auto compute = [&](Raw& x, int64_t tn) __attribute__((always_inline)) {
+        // decay of token tb + t to the sub-segment's end: exp(-(Rsum + sum of
+        // A d over the block's tokens after t)), by additions only
+        float P = row_prefix16(x.ad);                        // inclusive, within each 16
+        const int lo_bits = __builtin_amdgcn_readlane(__float_as_int(P), 15);
+        P += (lane & 16) ? __int_as_float(lo_bits) : 0.0f;   // inclusive over lanes 0..31
+        const float total = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(P), 31));
+        const float wt = fast_exp(-(Rsum + (total - P)));    // weight of token tb + lane % 32
+        float w[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) w[e] = __shfl(wt, 8 * g + e);
+
+        // B operands: beta (exact) and the limbs of w beta v, per column tile
+        u32x4c Bb[NT], B0[NT], B1[NT], B2[NT];
+#pragma unroll
+        for (int n = 0; n < NT; ++n)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e0 = 2 * q, e1 = 2 * q + 1;
+                Bb[n][q] = bf_bits(x.b[e0], n) | (bf_bits(x.b[e1], n) << 16);
+                const float ya = w[e0] * (bf_elem(x.b[e0], n) * bf_elem(x.v[e0], n));
+                const float yb = w[e1] * (bf_elem(x.b[e1], n) * bf_elem(x.v[e1], n));
+                uint32_t l0, l1, l2;
+                split3(ya, yb, l0, l1, l2);
+                B0[n][q] = l0;
+                B1[n][q] = l1;
+                B2[n][q] = l2;
+            }
+        load_bv(tn, x);
+        // A operands row tile by row tile: k (exact) and the limbs of w k^2
+#pragma unroll
+        for (int m = 0; m < MT; ++m) {
+            u32x4c Ak, A0, A1, A2;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int e0 = 2 * q, e1 = 2 * q + 1;
+                Ak[q] = bf_bits(x.k[e0], m) | (bf_bits(x.k[e1], m) << 16);
+                const float ka = bf_elem(x.k[e0], m), kb = bf_elem(x.k[e1], m);
+                uint32_t l0, l1, l2;
+                split3(w[e0] * (ka * ka), w[e1] * (kb * kb), l0, l1, l2);
+                A0[q] = l0;
+                A1[q] = l1;
+                A2[q] = l2;
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                J[m][n] = mfma_bf(A0, Bb[n], J[m][n]);
+                X[m][n] = mfma_bf(Ak, B0[n], X[m][n]);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                J[m][n] = mfma_bf(A1, Bb[n], J[m][n]);
+                X[m][n] = mfma_bf(Ak, B1[n], X[m][n]);
+            }
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                J[m][n] = mfma_bf(A2, Bb[n], J[m][n]);
+                X[m][n] = mfma_bf(Ak, B2[n], X[m][n]);
+            }
+        }
+        load_k(tn, x);
+        Rsum += total;
+    };
+
+    // one operand set: each block's loads are issued as the previous block's
+    // operands die (a block before the sub-segment reads nothing)
+    const int64_t nblk = (t_end - t_begin + KB - 1) / KB;
+    Raw x;
+    int64_t tb = t_begin + (nblk - 1) * KB;
+    load_bv(tb, x);
+    load_k(tb, x);
+    for (int64_t i = 0; i < nblk; ++i, tb -= KB) compute(x, tb - KB);
+
+    const int64_t slot = (bh * (p.S - 1) + seg) * R + sub;
+    float* out = p.sub + slot * 2 * DK * DV_;
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            float rowJ[NT], rowX[NT];
+#pragma unroll
+            for (int n = 0; n < NT; ++n) {
+                rowJ[n] = J[m][n][r];
+                rowX[n] = X[m][n][r];
+            }
+            const int64_t off = static_cast<int64_t>(rb + MT * (4 * g + r) + m) * DV_ + cb + NT * c;
+            store_run<NT>(out + off, rowJ);
+            store_run<NT>(out + static_cast<int64_t>(DK) * DV_ + off, rowX);
+        }
+    if (lane == 0 && tile == 0) p.gsub[slot] = fast_exp(-Rsum);
+}
+
 // Ordered carry: sub-segment composites -> the starting (J, eta) of every
 // main segment.  One thread per memory entry of every head.
 __device__ __forceinline__ void carry_sub_entry(const DiagParams& p, int64_t dk, int64_t e, int32_t R) {
@@ -258,13 +528,35 @@ static int comp_launch(const DiagParams& p, int64_t dk, int64_t grid, int32_t R,
     }
 }
 
+template <int DK>
+static int comp_bf_launch_dv(const DiagParams& p, int64_t grid, int32_t R, hipStream_t st) {
+    switch (p.dv) {
+        case 16: hipLaunchKernelGGL((k_diag_comp_bf<DK, 16>), dim3(grid), dim3(kWave), 0, st, p, R); break;
+        case 32: hipLaunchKernelGGL((k_diag_comp_bf<DK, 32>), dim3(grid), dim3(kWave), 0, st, p, R); break;
+        case 64: hipLaunchKernelGGL((k_diag_comp_bf<DK, 64>), dim3(grid), dim3(kWave), 0, st, p, R); break;
+        case 128: hipLaunchKernelGGL((k_diag_comp_bf<DK, 128>), dim3(grid), dim3(kWave), 0, st, p, R); break;
+        default: return KDN_EUNSUPPORTED;
+    }
+    return launch_status();
+}
+
+static int comp_bf_launch(const DiagParams& p, int64_t dk, int64_t grid, int32_t R, hipStream_t st) {
+    switch (dk) {
+        case 16: return comp_bf_launch_dv<16>(p, grid, R, st);
+        case 32: return comp_bf_launch_dv<32>(p, grid, R, st);
+        case 64: return comp_bf_launch_dv<64>(p, grid, R, st);
+        case 128: return comp_bf_launch_dv<128>(p, grid, R, st);
+        default: return KDN_EUNSUPPORTED;
+    }
+}
+
 // Composites of segments 0..S-2 in R sub-segments each (one wave per
 // sub-segment and column tile), then the carry into every segment's starting
 // state (p.comp).  Needs the per-token scalars.
 int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
     const int64_t BH = B * p.H;
-    const int64_t grid = BH * (p.S - 1) * R * comp_tiles(p.dv);
-    int rc = bf16 ? comp_launch<true>(p, dk, grid, R, st) : comp_launch<false>(p, dk, grid, R, st);
+    const int64_t grid = BH * (p.S - 1) * R * comp_tiles(dk, p.dv, bf16);
+    int rc = bf16 ? comp_bf_launch(p, dk, grid, R, st) : comp_launch<false>(p, dk, grid, R, st);
     if (rc != KDN_OK) return rc;
     const int64_t n = BH * dk * p.dv;
     hipLaunchKernelGGL(k_diag_carry_sub, dim3(elem_groups(n)), dim3(256), 0, st,

@@ -210,7 +210,7 @@ int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int3
 int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
-int comp_tiles(int64_t dv);
+int comp_tiles(int64_t dk, int64_t dv, bool bf16);
 int diag_comp_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int diag_carry_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int mob_block();

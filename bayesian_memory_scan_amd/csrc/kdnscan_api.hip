@@ -52,9 +52,9 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv, int32_t request) {
     if (S > pl.nchunks) S = pl.nchunks;
     if (S < 1) S = 1;
     pl.S = static_cast<int32_t>(S);
-    // composites: at most eight one-wave workgroups (32 columns each) per CU,
-    // the number resident at once (two per SIMD), so that none waits for a
-    // second round; at least 4 chunks per sub-segment
+    // composites: about eight one-wave work units (32-column tiles) per CU,
+    // at least 4 chunks per sub-segment (the bf16 kernel's 64 x 64 tiles come
+    // to the same unit count at d_k = d_v = 128)
     int64_t R = 1;
     if (pl.S > 1 && BH > 0) {
         const int64_t units = BH * (pl.S - 1) * (dv > 32 ? dv / 32 : 1);
@@ -236,7 +236,7 @@ int diag_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, kdn_dtyp
             workspace_bytes = &scratch_cap;
         }
     }
-    report_echo(opts, T > 0 ? BH * pl.S * ntile + (pl.S > 1 ? BH * (pl.S - 1) * pl.R * comp_tiles(d_v) : 0) : 0);
+    report_echo(opts, T > 0 ? BH * pl.S * ntile + (pl.S > 1 ? BH * (pl.S - 1) * pl.R * comp_tiles(d_k, d_v, in_dtype == KDN_BF16) : 0) : 0);
     const size_t need = dw.total;
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
