@@ -14,13 +14,16 @@
 // exact power-of-two rescaling (a fractional-linear map is unchanged by a
 // common factor).
 //
-// Two launches:
+// Three launches, O(T) work in all:
 //   k_mob_reduce: per (head, block of 4096 tokens) the block's composite;
-//   k_mob_apply:  per (head, block) the carry-in (ordered product of earlier
-//                 block composites, itself a wave scan), the in-block
-//                 exclusive scan of per-thread composites (__shfl_up within the
-//                 wave, LDS across the 4 waves), then each thread walks its 16
-//                 tokens sequentially from its starting precision and writes
+//   k_mob_carry:  per head, one wave turns the block composites, in place,
+//                 into each block's carry-in (the ordered product of all
+//                 earlier blocks), 64 blocks per step, the running product
+//                 carried from step to step;
+//   k_mob_apply:  per (head, block) the in-block exclusive scan of per-thread
+//                 composites (a DPP wave scan, LDS across the 4 waves) after
+//                 the block's carry-in, then each thread walks its 16 tokens
+//                 sequentially from its starting precision and writes
 //                 lambda_t and the gates of KLA Metodologia 3:
 //                   lambda^-_t = lambda_{t-1} / (a_t^2 + p_t lambda_{t-1})
 //                   F_t = a_t lambda^-_t / lambda_t,   G_t = Lambda_t / lambda_t.
@@ -61,8 +64,41 @@ __device__ __forceinline__ float mob_apply(const Mob& M, float l) {
     return __builtin_fmaf(M.m11, l, M.m12) / __builtin_fmaf(M.m21, l, M.m22);
 }
 
-__device__ __forceinline__ Mob mob_shfl_up(const Mob& M, int s) {
-    return {__shfl_up(M.m11, s), __shfl_up(M.m12, s), __shfl_up(M.m21, s), __shfl_up(M.m22, s)};
+// The map of the lane that DPP control CTRL names, in the rows ROWS enables;
+// other lanes (no source lane, or a row left out) get the identity.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_or(float x, float id) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), CTRL, ROWS, 0xf, false));
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ Mob mob_dpp(const Mob& M) {
+    return {dpp_or<CTRL, ROWS>(M.m11, 1.0f), dpp_or<CTRL, ROWS>(M.m12, 0.0f), dpp_or<CTRL, ROWS>(M.m21, 0.0f),
+            dpp_or<CTRL, ROWS>(M.m22, 1.0f)};
+}
+
+// Inclusive scan of the wave's 64 maps in lane order: lane l ends with
+// M_l o ... o M_0.  Four row_shr steps within each row of 16, then the
+// last lane of a row is broadcast into the next row (row_bcast:15, rows 1
+// and 3) and lane 31 into the upper half (row_bcast:31, rows 2 and 3).
+__device__ __forceinline__ Mob mob_wave_scan(Mob P) {
+    P = mob_norm(mob_after(P, mob_dpp<0x111, 0xf>(P)));
+    P = mob_norm(mob_after(P, mob_dpp<0x112, 0xf>(P)));
+    P = mob_norm(mob_after(P, mob_dpp<0x114, 0xf>(P)));
+    P = mob_norm(mob_after(P, mob_dpp<0x118, 0xf>(P)));
+    P = mob_norm(mob_after(P, mob_dpp<0x142, 0xa>(P)));
+    P = mob_norm(mob_after(P, mob_dpp<0x143, 0xc>(P)));
+    return P;
+}
+
+// The previous lane's map (wave_shr:1); the identity in lane 0.
+__device__ __forceinline__ Mob mob_prev_lane(const Mob& M) { return mob_dpp<0x138, 0xf>(M); }
+
+// Lane 63's map in every lane.
+__device__ __forceinline__ Mob mob_last_lane(const Mob& M) {
+    return {__int_as_float(__builtin_amdgcn_readlane(__float_as_int(M.m11), kWave - 1)),
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M.m12), kWave - 1)),
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M.m21), kWave - 1)),
+            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(M.m22), kWave - 1))};
 }
 
 
@@ -114,13 +150,8 @@ __device__ __forceinline__ Mob run_composite(const Run16& r) {
 __device__ Mob block_scan(Mob P, Mob* excl, Mob (&s_w)[kMobThreads / kWave]) {
     const int lane = threadIdx.x % kWave;
     const int wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int s = 1; s < kWave; s <<= 1) {
-        const Mob Q = mob_shfl_up(P, s);
-        if (lane >= s) P = mob_norm(mob_after(P, Q));
-    }
-    Mob ex = mob_shfl_up(P, 1);
-    if (lane == 0) ex = mob_identity();
+    P = mob_wave_scan(P);
+    const Mob ex = mob_prev_lane(P);
     if (lane == kWave - 1) s_w[wave] = P;
     __syncthreads();
     Mob before = mob_identity();
@@ -144,40 +175,42 @@ __global__ __launch_bounds__(kMobThreads) void k_mob_reduce(MobParams p) {
     }
 }
 
+// Block composites -> carry-ins, in place: one wave per head walks its
+// blocks 64 at a time (a wave scan per step, the running product of all
+// earlier steps carried in a register).
+__global__ __launch_bounds__(kWave) void k_mob_carry(MobParams p) {
+    const int64_t bh = blockIdx.x;
+    const int lane = threadIdx.x;
+    float* base = p.blk + bh * p.nblk * 4;
+    Mob C = mob_identity();
+    for (int64_t b0 = 0; b0 < p.nblk; b0 += kWave) {
+        const bool in = b0 + lane < p.nblk;
+        Mob x = mob_identity();
+        if (in) {
+            const float4 m = *reinterpret_cast<const float4*>(base + (b0 + lane) * 4);
+            x = Mob{m.x, m.y, m.z, m.w};
+        }
+        const Mob inc = mob_wave_scan(x);
+        const Mob cin = mob_norm(mob_after(mob_prev_lane(inc), C));
+        if (in) *reinterpret_cast<float4*>(base + (b0 + lane) * 4) = make_float4(cin.m11, cin.m12, cin.m21, cin.m22);
+        C = mob_norm(mob_after(mob_last_lane(inc), C));
+    }
+}
+
 __global__ __launch_bounds__(kMobThreads) void k_mob_apply(MobParams p) {
     __shared__ Mob s_w[kMobThreads / kWave];
-    __shared__ Mob s_carry;
     const int64_t bh = blockIdx.x / p.nblk;
     const int blk = static_cast<int>(blockIdx.x % p.nblk);
     const int64_t t0 = static_cast<int64_t>(blk) * kMobBlock + static_cast<int64_t>(threadIdx.x) * kMobPer;
 
-    // carry-in: ordered product of the earlier blocks' composites, a wave scan
-    // over groups of 64 blocks
-    if (threadIdx.x < kWave) {
-        const int lane = threadIdx.x;
-        Mob C = mob_identity();
-        for (int b0 = 0; b0 < blk; b0 += kWave) {
-            Mob x = mob_identity();
-            if (b0 + lane < blk) {
-                const float* m = p.blk + (bh * p.nblk + b0 + lane) * 4;
-                x = Mob{m[0], m[1], m[2], m[3]};
-            }
-#pragma unroll
-            for (int s = 1; s < kWave; s <<= 1) {
-                const Mob y = mob_shfl_up(x, s);
-                if (lane >= s) x = mob_norm(mob_after(x, y));
-            }
-            const Mob grp = Mob{__shfl(x.m11, kWave - 1), __shfl(x.m12, kWave - 1),
-                                __shfl(x.m21, kWave - 1), __shfl(x.m22, kWave - 1)};
-            C = mob_norm(mob_after(grp, C));
-        }
-        if (lane == 0) s_carry = C;
-    }
+    // carry-in of the block (written by k_mob_carry)
+    const float4 cm = *reinterpret_cast<const float4*>(p.blk + (bh * p.nblk + blk) * 4);
+    const Mob carry{cm.x, cm.y, cm.z, cm.w};
     Run16 run;
     load_run(p, bh, t0, run);
     Mob excl;
-    block_scan(run_composite(run), &excl, s_w);  // its barrier also publishes s_carry
-    const Mob start = mob_after(excl, s_carry);
+    block_scan(run_composite(run), &excl, s_w);
+    const Mob start = mob_after(excl, carry);
 
     const float l0 = p.lambda0 ? p.lambda0[bh] : 1.0f;
     float lam = mob_apply(start, l0);
@@ -227,6 +260,8 @@ int mobius_launch(const MobParams& p, int64_t BH, hipStream_t st) {
     hipLaunchKernelGGL(k_mob_reduce, dim3(static_cast<uint32_t>(grid)), dim3(kMobThreads), 0, st, p);
     int rc = launch_status();
     if (rc != KDN_OK) return rc;
+    hipLaunchKernelGGL(k_mob_carry, dim3(static_cast<uint32_t>(BH)), dim3(kWave), 0, st, p);
+    if ((rc = launch_status()) != KDN_OK) return rc;
     hipLaunchKernelGGL(k_mob_apply, dim3(static_cast<uint32_t>(grid)), dim3(kMobThreads), 0, st, p);
     return launch_status();
 }

@@ -495,8 +495,9 @@ def main():
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("iso_scan.hip", f"traffic_{spec.name}.json"),
                          **tm.fields(),
-                         "note": "whole step (all kernels) timed by events; traffic is the "
-                                 "main mean-scan pass"},
+                         "note": "achieved: algorithmic flops over the main mean-scan pass's "
+                                 "own event time; call_ms_*: the whole call (Mobius scan, "
+                                 "segment composites, carry and main pass)"},
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_iso(inp, spec, a.cpu_seconds)

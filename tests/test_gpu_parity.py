@@ -301,6 +301,34 @@ def test_iso_initial_state(kdn, S):
         gu.check_state(mu_T[b, h], r["mu_T"], f"iso mu_T[{b},{h}] S={S}")
 
 
+@pytest.mark.parametrize("with_mean", [False, True])
+def test_mobius_long_sequence(kdn, with_mean):
+    """T = 2^20 + 37: 257 Mobius blocks per head, so the carry pass walks
+    five steps of 64 block composites (the last one ragged) and the last
+    block is ragged too.  lambda elementwise against the oracle's sequential
+    fp64 filter; with the mean path also o and mu_T (automatic segments)."""
+    B, H, T = 1, 2, 2 ** 20 + 37
+    dk = dv = 16
+    spec = synth.IsoSpec("iso_long", B, H, T, dk, dv, 2020)
+    inp = synth.iso_inputs(spec, with_mean=with_mean)
+    x = gu.upload_iso(inp)
+    print(f"mobius long T={T} mean={with_mean}", flush=True)
+    if with_mean:
+        lam, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"],
+                                                     x["q"], x["k"], x["v"])
+    else:
+        lam, o, mu_T = kdn.kdn_mobius_precision_scan(x["a"], x["p"], x["Lambda"], x["lambda0"])
+    torch.cuda.synchronize()
+    ref = oracle.iso_scan(inp, with_mean=with_mean)
+    lam = lam.cpu().numpy()
+    for b, h in _all_heads(B, H):
+        r = ref[(b, h)]
+        gu.check_rel(lam[b, h], r["lambda"], f"lambda[{b},{h}] T={T}")
+        if with_mean:
+            gu.check_o(o[b, h].cpu().numpy(), r, f"iso o[{b},{h}] T={T}")
+            gu.check_state(mu_T[b, h].cpu().numpy(), r["mu_T"], f"iso mu_T[{b},{h}] T={T}")
+
+
 def test_iso_chaining(kdn):
     """scan(T1) then scan(T2) started from its last precision and final mean
     equals one scan over T1 + T2."""
