@@ -13,7 +13,7 @@ _BINDING = {
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
     "KDN_ESCRATCH", "KDN_F32", "KDN_BF16", "KDN_ECHO_WORDS", "KdnError", "ScanOpts", "kdn_diag_scan_fwd",
     "kdn_diag_scan_fwd_noalloc", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd",
-    "kdn_diag_scan_varlen_fwd",
+    "kdn_diag_scan_varlen_fwd", "kdn_diag_scan_varlen_bwd",
     "kdn_mobius_precision_scan",
     "kdn_decode_step", "kdn_diag_plan", "kdn_status_string",
     "kdn_last_hip_error",

@@ -234,14 +234,15 @@ struct BwdLoader {
     float4 rg[REV ? NVG : 1];
     float4 rsc;
 
-    __device__ __forceinline__ void fetch(const BwdParams& p, int64_t bh, int tile, int64_t t0,
-                                          int L, int tid) {
-        const E* kh = static_cast<const E*>(p.k) + bh * p.T * DK;
-        const E* qh = static_cast<const E*>(p.q) + bh * p.T * DK;
+    // tokens tbase + t of the token axis; t_end: the run's end (scalars past it are the identity)
+    __device__ __forceinline__ void fetch(const BwdParams& p, int64_t tbase, int tile, int64_t t0,
+                                          int L, int64_t t_end, int tid) {
+        const E* kh = static_cast<const E*>(p.k) + tbase * DK;
+        const E* qh = static_cast<const E*>(p.q) + tbase * DK;
         // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
-        const E* bth = p.beta ? static_cast<const E*>(p.beta) + bh * p.T * p.dv + tile * CI : nullptr;
-        const E* dh = static_cast<const E*>(p.d) + bh * p.T;
-        const E* vh = static_cast<const E*>(p.v) + bh * p.T * p.dv + tile * CI;
+        const E* bth = p.beta ? static_cast<const E*>(p.beta) + tbase * p.dv + tile * CI : nullptr;
+        const E* dh = static_cast<const E*>(p.d) + tbase;
+        const E* vh = static_cast<const E*>(p.v) + tbase * p.dv + tile * CI;
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
             const int vi = tid + n * NTH;
@@ -262,7 +263,7 @@ struct BwdLoader {
             }
         }
         if constexpr (REV) {
-            const float* gh = p.dout + bh * p.T * p.dv + tile * CI;
+            const float* gh = p.dout + tbase * p.dv + tile * CI;
 #pragma unroll
             for (int n = 0; n < NVG; ++n) {
                 const int vi = tid + n * NTH;
@@ -277,7 +278,7 @@ struct BwdLoader {
         }
         if (tid <= L) {
             const int64_t t = t0 + tid;
-            rsc = t < p.T ? p.scal[bh * p.T + t] : make_float4(1.0f, 0.0f, 1.0f, 0.0f);
+            rsc = t < t_end ? p.scal[tbase + t] : make_float4(1.0f, 0.0f, 1.0f, 0.0f);
         }
     }
 
@@ -399,6 +400,70 @@ __device__ __forceinline__ float* ckpt_slot(float* base, int64_t r, int64_t c, i
     return c < nch ? base + (r * nch + c) * 2 * BLK : base + (nruns * nch + r) * 2 * BLK;
 }
 
+// One run of the gradient: a (batch, head) row of a fixed-length batch, or a
+// (sequence, head) of a packed variable-length batch, and one column tile.
+struct BwdRun {
+    int64_t state;      // slot of the run's starting and final states ([nruns][dk][dv])
+    int64_t tbase;      // token-axis index of its row's token 0 (a token t is tbase + t)
+    int64_t t_begin;    // the run's tokens on its row: [t_begin, t_end)
+    int64_t t_end;
+    int64_t nch;        // 16-token chunks from t_begin (the last one ragged)
+    float* ck0;         // checkpoint before chunk 0; chunk c < nch at ck0 + c * 2 BLK
+    float* ckfin;       // the final state
+    int tile;
+    bool valid;         // false: a padding workgroup of a packed batch
+};
+
+// Fixed-length rows: XCD-local ids, the checkpoint layout of ckpt_slot.  A
+// packed batch: runs follow the plan's longest-first order in groups of 8
+// runs x NTILE tiles (a run's tiles 8 blocks apart, so on one XCD), as in the
+// forward pass; each sequence's chunks and final state sit at its plan
+// offset inside its (head, tile) block of ck_stride slots.
+template <int BLK, int NTILE>
+__device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
+    BwdRun r;
+    if (p.cu_seqlens == nullptr) {
+        const int64_t wg = xcd_local_id();
+        r.tile = static_cast<int>(wg % NTILE);
+        const int64_t bh = wg / NTILE;
+        r.state = bh;
+        r.tbase = bh * p.T;
+        r.t_begin = 0;
+        r.t_end = p.T;
+        r.nch = p.nchunks;
+        const int64_t rt = bh * NTILE + r.tile;
+        r.ck0 = ckpt_slot<BLK>(p.ckpt, rt, 0, r.nch, p.nruns * NTILE);
+        r.ckfin = ckpt_slot<BLK>(p.ckpt, rt, r.nch, r.nch, p.nruns * NTILE);
+        r.valid = true;
+        return r;
+    }
+    const int64_t blk = blockIdx.x;
+    const int64_t within = blk % (8 * NTILE);
+    r.tile = static_cast<int>(within / 8);
+    const int64_t wg = blk / (8 * NTILE) * 8 + within % 8;
+    r.valid = wg < static_cast<int64_t>(p.nseq) * p.H;
+    if (!r.valid) return r;
+    const int64_t h = wg % p.H;
+    const int32_t sq = p.seq_order[wg / p.H];
+    r.state = static_cast<int64_t>(sq) * p.H + h;
+    r.tbase = h * p.T;
+    int64_t a = p.cu_seqlens[sq], b = p.cu_seqlens[sq + 1];
+    a = a < 0 ? 0 : (a > p.T ? p.T : a);
+    b = b < a ? a : (b > p.T ? p.T : b);
+    r.t_begin = a;
+    r.t_end = b;
+    r.nch = (b - a + kBwdChunk - 1) / kBwdChunk;
+    r.ck0 = p.ckpt + ((h * NTILE + r.tile) * p.ck_stride + p.seq_ckoff[sq]) * 2 * BLK;
+    r.ckfin = r.ck0 + r.nch * 2 * BLK;
+    return r;
+}
+
+// The state before chunk c of a run (c == nch: its final state).
+template <int BLK>
+__device__ __forceinline__ float* ck_at(const BwdRun& r, int64_t c) {
+    return c < r.nch ? r.ck0 + c * 2 * BLK : r.ckfin;
+}
+
 __device__ __forceinline__ void store16(float* dst, const float (&x)[16]) {
 #pragma unroll
     for (int n = 0; n < 4; ++n)
@@ -476,31 +541,30 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
     const int cg = w % Sh::CG;
     const int j = rh * 64 + lane;
     const int lc = cg * 16 + (lane & 15);      // this lane's value column in the tile (for operands)
-    const int64_t wg = xcd_local_id();
-    const int tile = static_cast<int>(wg % Sh::NTILE);
-    const int64_t bh = wg / Sh::NTILE;
-    const int64_t nch = p.nchunks;
+    const BwdRun run = bwd_run<Sh::BLK, Sh::NTILE>(p);
+    if (!run.valid) return;
+    const int tile = run.tile;
+    const int64_t nch = run.nch;
 
     float I[16], m0[16], J[16], E[16];
-    start_state(p, (bh * DK + j) * p.dv + tile * CI + cg * 16, I, J, E, m0);
-    const int64_t run = bh * Sh::NTILE + tile;
-    const int64_t nruns = p.BH * Sh::NTILE;
+    start_state(p, (run.state * DK + j) * p.dv + tile * CI + cg * 16, I, J, E, m0);
     const int64_t lid = cg * DK + j;            // this lane's index in a checkpoint half
-    float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, 0, nch, nruns);
+    float* ck = ck_at<Sh::BLK>(run, 0);
     store16_ckpt<Sh::BLK>(ck, lid, J);
     store16_ckpt<Sh::BLK>(ck + Sh::BLK, lid, E);
 
     auto chunk_len = [&](int64_t c) -> int {
-        const int64_t rem = p.T - c * C;
+        const int64_t rem = run.t_end - (run.t_begin + c * C);
         return static_cast<int>(rem < C ? rem : C);
     };
+    auto fetch = [&](int64_t c) { ld.fetch(p, run.tbase, tile, run.t_begin + c * C, chunk_len(c), run.t_end, tid); };
     const int64_t nrun = nch;                   // slot nch: the final state (for the last token's adjoint)
     if (nrun > 0) {
-        ld.fetch(p, bh, tile, 0, chunk_len(0), tid);
+        fetch(0);
         ld.commit(stg[0], chunk_len(0), tid);
     }
     __syncthreads();
-    if (nrun > 1) ld.fetch(p, bh, tile, C, chunk_len(1), tid);
+    if (nrun > 1) fetch(1);
 
     for (int64_t c = 0; c < nrun; ++c) {
         const int b = static_cast<int>(c & 1);
@@ -527,12 +591,12 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
             J[e] *= inv_s;
             E[e] *= inv_s;
         }
-        float* dst = ckpt_slot<Sh::BLK>(p.ckpt, run, c + 1, nch, nruns);
+        float* dst = ck_at<Sh::BLK>(run, c + 1);
         store16_ckpt<Sh::BLK>(dst, lid, J);
         store16_ckpt<Sh::BLK>(dst + Sh::BLK, lid, E);
         if (c + 1 < nrun) ld.commit(stg[b ^ 1], chunk_len(c + 1), tid);
         __syncthreads();
-        if (c + 2 < nrun) ld.fetch(p, bh, tile, (c + 2) * C, chunk_len(c + 2), tid);
+        if (c + 2 < nrun) fetch(c + 2);
     }
 }
 
@@ -563,13 +627,13 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
     const int cg = w % CG;
     const int j = rh * 64 + lane;
     const int lc = cg * 16 + (lane & 15);
-    const int64_t wg = xcd_local_id();
-    const int tile = static_cast<int>(wg % Sh::NTILE);
-    const int64_t bh = wg / Sh::NTILE;
+    const BwdRun run = bwd_run<Sh::BLK, Sh::NTILE>(p);
+    if (!run.valid) return;
+    const int tile = run.tile;
     const int64_t T = p.T;
-    const int64_t nch = p.nchunks;
+    const int64_t nch = run.nch;
     const float I_prior = p.I_prior;
-    const int64_t ent = (bh * DK + j) * p.dv + tile * CI + cg * 16;   // this lane's 16 entries
+    const int64_t ent = (run.state * DK + j) * p.dv + tile * CI + cg * 16;   // this lane's 16 entries
     // this column tile's slices of the partial-sum buffers
     float* const part_dq = p.part_dq + tile * p.BH * T * DK;
     float* const part_dk = p.part_dk + tile * p.BH * T * DK;
@@ -583,26 +647,24 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         M[c] = 0.0f;
     }
 
-    const int64_t run = bh * Sh::NTILE + tile;
-    const int64_t nruns = p.BH * Sh::NTILE;
     const int64_t lid = cg * DK + j;            // this lane's index in a checkpoint half
 
     auto chunk_len = [&](int64_t c) -> int {
-        const int64_t rem = T - c * C;
+        const int64_t rem = run.t_end - (run.t_begin + c * C);
         return static_cast<int>(rem < C ? rem : C);
     };
+    auto fetch = [&](int64_t c) { ld.fetch(p, run.tbase, tile, run.t_begin + c * C, chunk_len(c), run.t_end, tid); };
 
     if (nch > 0) {
-        ld.fetch(p, bh, tile, (nch - 1) * C, chunk_len(nch - 1), tid);
+        fetch(nch - 1);
         ld.commit(stg[0], chunk_len(nch - 1), tid);
         // Gradients arriving through the final state, in the last token's
         // frame (s = s_{T-1}): lam_eta = dmu_T / I_T and lam_I = dI_T -
         // dmu_T mu_T / I_T, scaled by 1 / s.  The checkpoint pass stored the
         // final state (J_T, eta_T) unscaled after the last chunk.
         float JT[16], ET[16];
-        const float* ckT = ckpt_slot<Sh::BLK>(p.ckpt, run, nch, nch, nruns);
-        load_ckpt<Sh::BLK>(ckT, lid, JT, ET);
-        const float inv_s = 1.0f / uniform(p.scal[bh * T + T - 1].z);
+        load_ckpt<Sh::BLK>(run.ckfin, lid, JT, ET);
+        const float inv_s = 1.0f / uniform(p.scal[run.tbase + run.t_end - 1].z);
         Unroll<0, 16>::run([&](auto cc) {
             constexpr int c = decltype(cc)::value;
             const float gm = p.dmu_T ? p.dmu_T[ent + c] : 0.0f;
@@ -620,7 +682,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const int64_t t = t0 + tt;
         const float4 sct = S.sc[tt];
         const float sIp = uniform(sct.z) * I_prior;     // s_t I_prior: I~ = J~ + s I_prior
-        const bool has_next = t + 1 < T;
+        const bool has_next = t + 1 < run.t_end;
         {
             // dalpha of token t+1: (L, M) still belong to it (its frame), (J, E)
             // is the state before it (computed for every token, written when
@@ -697,8 +759,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         const int b = static_cast<int>((nch - 1 - c) & 1);
         const BwdStage<DK, CI, true>& S = stg[b];
         const int Lc = chunk_len(c);
-        const int64_t t0 = c * C;
-        const float* ck = ckpt_slot<Sh::BLK>(p.ckpt, run, c, nch, nruns);
+        const int64_t t0 = run.t_begin + c * C;
+        const float* ck = ck_at<Sh::BLK>(run, c);
         const int nheld = (Lc + HELD - 1) / HELD;
         auto operands = [&](int tt, float& rho, float& bs, float& bvs,
                             float& kj) __attribute__((always_inline)) {
@@ -781,10 +843,10 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
 
         __syncthreads();
         // the previous chunk's loads fly while this chunk's outputs are written
-        if (c > 0) ld.fetch(p, bh, tile, (c - 1) * C, chunk_len(c - 1), tid);
+        if (c > 0) fetch(c - 1);
 
         // ---- chunk outputs ----
-        const int64_t tokbase = bh * T + t0;                      // token index into [BH,T]
+        const int64_t tokbase = run.tbase + t0;                   // token index into the token axis
         for (int e = tid; e < Lc * CI; e += NTH) {
             const int tt = e / CI;
             const int ci = e % CI;
@@ -835,7 +897,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             part_dk[o] = sk * S.sc[tt].z;
         }
         for (int tt = tid; tt < Lc; tt += NTH) {
-            if (t0 + tt + 1 < T) {
+            if (t0 + tt + 1 < run.t_end) {
                 float X1 = 0.0f, X2 = 0.0f;
 #pragma unroll
                 for (int ww = 0; ww < W; ++ww) {
@@ -856,7 +918,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
     start_state(p, ent, I0, J0, E0, m0);
     __shared__ float2 xfin[W];
     float di[16], dm[16];   // gradients of the starting state's I0 and mu0
-    if (T > 0) {
+    if (run.t_end > run.t_begin) {
         float x1a = 0.0f, x1b = 0.0f, x2 = 0.0f;
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
@@ -868,7 +930,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         if (lane == 0) xfin[w].x = tot;
         if (lane == 32) xfin[w].y = tot;
         // token 0 starts a frame with s = 1 and rho = alpha_0
-        const float alpha0 = fast_exp(-uniform(p.scal[bh * T].w));
+        const float alpha0 = fast_exp(-uniform(p.scal[run.tbase + run.t_begin].w));
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
             L[c] *= alpha0;
@@ -881,8 +943,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 X1 += xfin[ww].x;
                 X2 += xfin[ww].y;
             }
-            part_da[bh * T] = X1;
-            part_dip[bh * T] = (1.0f - alpha0) * X2;
+            part_da[run.tbase + run.t_begin] = X1;
+            part_dip[run.tbase + run.t_begin] = (1.0f - alpha0) * X2;
         }
 #pragma unroll
         for (int c = 0; c < 16; ++c) {
@@ -917,7 +979,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         if (tid == 0) {
             float X = 0.0f;
             for (int ww = 0; ww < W; ++ww) X += xfin[ww].x;
-            p.part_dip0[tile * p.BH + bh] = X;
+            p.part_dip0[tile * p.nruns + run.state] = X;
         }
     }
 }
@@ -942,16 +1004,30 @@ __global__ __launch_bounds__(256) void k_diag_bwd_rows(BwdParams p, int64_t n4) 
     }
 }
 
-// One workgroup per head (b, h): dd_t = -A alpha_t dalpha_t, and the head's
-// sums of the dA terms (-d_t alpha_t dalpha_t) and the dI_prior terms.
+// Token ranges of the finishing sums: about two workgroups per CU, each range
+// at least 1024 tokens.
+int32_t bwd_token_split(int64_t rows, int64_t T) {
+    const int64_t want = rows > 0 ? (2 * kNumCU + rows - 1) / rows : 1;
+    const int64_t most = (T + 1023) / 1024;
+    const int64_t s = want < most ? want : most;
+    return s < 1 ? 1 : static_cast<int32_t>(s);
+}
+
+// One workgroup per token range r of row bh: dd_t = -A alpha_t dalpha_t, and
+// the range's sums of the dA terms (-d_t alpha_t dalpha_t) and the dI_prior
+// terms; range 0 also takes the row's starting-state terms.
 template <bool BF16>
 __global__ __launch_bounds__(256) void k_diag_bwd_tokens(BwdParams p) {
-    const int64_t bh = blockIdx.x;
+    const int64_t bh = blockIdx.x / p.tok_split;
+    const int32_t r = static_cast<int32_t>(blockIdx.x % p.tok_split);
+    const int64_t per = (p.T + p.tok_split - 1) / p.tok_split;
+    const int64_t t0 = r * per;
+    const int64_t t1 = t0 + per < p.T ? t0 + per : p.T;
     const int tid = threadIdx.x;
     const float A = p.A[bh % p.H];
     const int64_t n = p.BH * p.T;
     float sa = 0.0f, si = 0.0f;
-    for (int64_t t = tid; t < p.T; t += 256) {
+    for (int64_t t = t0 + tid; t < t1; t += 256) {
         const int64_t x = bh * p.T + t;
         float da = 0.0f, di = 0.0f;
         for (int tl = 0; tl < p.ntile; ++tl) {
@@ -968,6 +1044,12 @@ __global__ __launch_bounds__(256) void k_diag_bwd_tokens(BwdParams p) {
         sa = fmaf(-d * alpha, da, sa);
         si += di;
     }
+    // packed batch: row bh is head bh, whose runs (sequence s, head bh) each
+    // have a starting state
+    if (p.cu_seqlens && r == 0) {
+        for (int64_t sq = tid; sq < p.nseq; sq += 256)
+            for (int tl = 0; tl < p.ntile; ++tl) si += p.part_dip0[tl * p.nruns + sq * p.H + bh];
+    }
     __shared__ float red[2][256];
     red[0][tid] = sa;
     red[1][tid] = si;
@@ -981,25 +1063,29 @@ __global__ __launch_bounds__(256) void k_diag_bwd_tokens(BwdParams p) {
     }
     if (tid == 0) {
         float i0 = 0.0f;
-        for (int tl = 0; tl < p.ntile; ++tl) i0 += p.part_dip0[tl * p.BH + bh];
-        p.part_head[2 * bh] = red[0][0];
-        p.part_head[2 * bh + 1] = red[1][0] + i0;
+        if (!p.cu_seqlens && r == 0)
+            for (int tl = 0; tl < p.ntile; ++tl) i0 += p.part_dip0[tl * p.nruns + bh];
+        p.part_head[2 * blockIdx.x] = red[0][0];
+        p.part_head[2 * blockIdx.x + 1] = red[1][0] + i0;
     }
 }
 
-// dA[h] = sum over the batch of the heads' sums; dI_prior = sum over all.
+// dA[h] = sum over the batch and token ranges of the range sums; dI_prior =
+// sum over all.
 __global__ __launch_bounds__(256) void k_diag_bwd_heads(BwdParams p) {
     const int tid = threadIdx.x;
     const int64_t B = p.H > 0 ? p.BH / p.H : 0;
+    const int64_t R = p.tok_split;
     for (int64_t h = tid; h < p.H; h += 256) {
         float s = 0.0f;
-        for (int64_t b = 0; b < B; ++b) s += p.part_head[2 * (b * p.H + h)];
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t r = 0; r < R; ++r) s += p.part_head[2 * ((b * p.H + h) * R + r)];
         p.dA[h] = s;
     }
     if (!p.dI_prior) return;
     __shared__ float red[256];
     float s = 0.0f;
-    for (int64_t x = tid; x < p.BH; x += 256) s += p.part_head[2 * x + 1];
+    for (int64_t x = tid; x < p.BH * R; x += 256) s += p.part_head[2 * x + 1];
     red[tid] = s;
     __syncthreads();
     for (int h = 128; h > 0; h >>= 1) {
@@ -1012,7 +1098,11 @@ __global__ __launch_bounds__(256) void k_diag_bwd_heads(BwdParams p) {
 template <int DK, int DV, bool BF16>
 static int launch_bwd_shape(const BwdParams& p, hipStream_t st) {
     using Sh = BwdShape<DK, DV>;
-    const dim3 grid(static_cast<uint32_t>(p.BH * Sh::NTILE));
+    // a packed batch: whole groups of 8 runs (see bwd_run)
+    const int64_t g = p.cu_seqlens ? (static_cast<int64_t>(p.nseq) * p.H + 7) / 8 * 8 * Sh::NTILE
+                                   : p.BH * Sh::NTILE;
+    if (g == 0) return KDN_OK;
+    const dim3 grid(static_cast<uint32_t>(g));
     if (p.T > 0) hipLaunchKernelGGL((k_diag_bwd_ckpt<DK, DV, BF16>), grid, dim3(Sh::NTH), 0, st, p);
     hipLaunchKernelGGL((k_diag_bwd<DK, DV, BF16>), grid, dim3(Sh::NTH), 0, st, p);
     return launch_status();
@@ -1026,6 +1116,42 @@ static int launch_bwd_dv(const BwdParams& p, int64_t dv, hipStream_t st) {
         case 64: return launch_bwd_shape<DK, 64, BF16>(p, st);
         case 128: return launch_bwd_shape<DK, 128, BF16>(p, st);
         default: return KDN_EUNSUPPORTED;
+    }
+}
+
+// Packed batch: the sequences' longest-first order (rank counting, as the
+// forward's plan; past 16384 sequences, index order) and the first checkpoint
+// slot of each sequence, an exclusive prefix sum of ceil(len / 16) + 1 slots
+// (the states before its chunks and its final state).  One workgroup.
+__global__ __launch_bounds__(kPlanThreads) void k_varlen_bwd_plan(BwdParams p) {
+    __shared__ int64_t lens[kPlanLds];
+    __shared__ int64_t part[kPlanThreads];
+    const int32_t n = p.nseq;
+    const int tid = threadIdx.x;
+    plan_longest_first(p.cu_seqlens, n, p.T, p.seq_order, lens);
+    // thread tid owns sequences [s0, s1); lens stays as staged above
+    const int32_t per = (n + kPlanThreads - 1) / kPlanThreads;
+    const int32_t s0 = tid * per < n ? tid * per : n;
+    const int32_t s1 = s0 + per < n ? s0 + per : n;
+    auto slots = [&](int32_t s) {
+        const int64_t len = n <= kPlanLds ? lens[s] : clamped_length(p.cu_seqlens, p.T, s);
+        return (len + kBwdChunk - 1) / kBwdChunk + 1;
+    };
+    int64_t sum = 0;
+    for (int32_t s = s0; s < s1; ++s) sum += slots(s);
+    // inclusive prefix over the threads' sums (Hillis-Steele in LDS)
+    part[tid] = sum;
+    __syncthreads();
+    for (int o = 1; o < kPlanThreads; o <<= 1) {
+        const int64_t v = tid >= o ? part[tid - o] : 0;
+        __syncthreads();
+        part[tid] += v;
+        __syncthreads();
+    }
+    int64_t off = part[tid] - sum;
+    for (int32_t s = s0; s < s1; ++s) {
+        p.seq_ckoff[s] = off;
+        off += slots(s);
     }
 }
 
@@ -1047,10 +1173,38 @@ int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64
             hipLaunchKernelGGL(k_diag_bwd_rows, dim3(elem_groups(n4)), dim3(256), 0,
                                st, p, n4);
         }
-        if (bf16) hipLaunchKernelGGL(k_diag_bwd_tokens<true>, dim3(static_cast<uint32_t>(p.BH)), dim3(256), 0, st, p);
-        else hipLaunchKernelGGL(k_diag_bwd_tokens<false>, dim3(static_cast<uint32_t>(p.BH)), dim3(256), 0, st, p);
+        const dim3 tgrid(static_cast<uint32_t>(p.BH * p.tok_split));
+        if (bf16) hipLaunchKernelGGL(k_diag_bwd_tokens<true>, tgrid, dim3(256), 0, st, p);
+        else hipLaunchKernelGGL(k_diag_bwd_tokens<false>, tgrid, dim3(256), 0, st, p);
     }
     if (p.H > 0) hipLaunchKernelGGL(k_diag_bwd_heads, dim3(1), dim3(256), 0, st, p);
+    return launch_status();
+}
+
+// The gradient over a packed variable-length batch: the plan, the frame
+// scalars per sequence-aligned chunk, then the same kernels with (sequence,
+// head) runs; the finishing sums run over the H rows of the token axis.
+int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t dk, bool bf16,
+                           hipStream_t st) {
+    if (p.H == 0) return KDN_OK;
+    if (p.nseq > 0) {
+        hipLaunchKernelGGL(k_varlen_bwd_plan, dim3(1), dim3(kPlanThreads), 0, st, p);
+        int rc = diag_prep_varlen_launch(prep, bf16, false, st);
+        if (rc != KDN_OK) return rc;
+        if (dk == 64) rc = bf16 ? launch_bwd_dv<64, true>(p, p.dv, st) : launch_bwd_dv<64, false>(p, p.dv, st);
+        else rc = bf16 ? launch_bwd_dv<128, true>(p, p.dv, st) : launch_bwd_dv<128, false>(p, p.dv, st);
+        if (rc != KDN_OK) return rc;
+    }
+    if (p.T > 0) {
+        if (p.ntile > 1) {
+            const int64_t n4 = p.BH * p.T * dk / 4;
+            hipLaunchKernelGGL(k_diag_bwd_rows, dim3(elem_groups(n4)), dim3(256), 0, st, p, n4);
+        }
+    }
+    const dim3 tgrid(static_cast<uint32_t>(p.BH * p.tok_split));
+    if (bf16) hipLaunchKernelGGL(k_diag_bwd_tokens<true>, tgrid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL(k_diag_bwd_tokens<false>, tgrid, dim3(256), 0, st, p);
+    hipLaunchKernelGGL(k_diag_bwd_heads, dim3(1), dim3(256), 0, st, p);
     return launch_status();
 }
 

@@ -967,44 +967,32 @@ int diag_chunk() { return kDiagChunk; }
 int varlen_cols(int64_t dv) { return dv >= 64 ? 64 : (dv < 32 ? static_cast<int>(dv) : 32); }
 
 // The plan of a packed batch: sequences ordered longest first (ties by
-// index), by rank counting in one workgroup.  Past kMaxPlanSort sequences
-// the quadratic count is skipped and the order is the identity.
-constexpr int32_t kMaxPlanSort = 16384;
-
-__global__ __launch_bounds__(1024) void k_varlen_plan(DiagParams p) {
-    const int32_t n = p.nseq;
-    for (int32_t s = threadIdx.x; s < n; s += 1024) {
-        int32_t rank = s;
-        if (n <= kMaxPlanSort) {
-            int64_t a0, a1;
-            sequence_tokens(p, s, a0, a1);
-            const int64_t len = a1 - a0;
-            rank = 0;
-            for (int32_t u = 0; u < n; ++u) {
-                int64_t b0, b1;
-                sequence_tokens(p, u, b0, b1);
-                const int64_t lu = b1 - b0;
-                rank += (lu > len || (lu == len && u < s)) ? 1 : 0;
-            }
-        }
-        p.seq_order[rank] = s;
-    }
+// index), by rank counting in one workgroup.
+__global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(DiagParams p) {
+    __shared__ int64_t lens[kPlanLds];
+    plan_longest_first(p.cu_seqlens, p.nseq, p.T, p.seq_order, lens);
 }
 
 // Packed variable-length batch (p.cu_seqlens set, p.S == 1): the plan, frame
 // scalars per sequence-aligned chunk, then one workgroup per (sequence, head,
 // tile).
-int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st) {
-    hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(1024), 0, st, p);
+// Frame scalars of a packed batch (chunks aligned to sequence starts).
+int diag_prep_varlen_launch(const DiagParams& p, bool bf16, bool true_i, hipStream_t st) {
     const int64_t n = p.H * p.T;
-    if (n > 0) {
-        const dim3 grid(elem_groups(n));
-        const bool true_i = varlen_cols(p.dv) == 64;   // the block kernel keeps I in true units
-        if (bf16 && true_i) hipLaunchKernelGGL((k_diag_prep_varlen<true, true>), grid, dim3(256), 0, st, p);
-        else if (bf16) hipLaunchKernelGGL((k_diag_prep_varlen<true, false>), grid, dim3(256), 0, st, p);
-        else if (true_i) hipLaunchKernelGGL((k_diag_prep_varlen<false, true>), grid, dim3(256), 0, st, p);
-        else hipLaunchKernelGGL((k_diag_prep_varlen<false, false>), grid, dim3(256), 0, st, p);
-    }
+    if (n == 0) return KDN_OK;
+    const dim3 grid(elem_groups(n));
+    if (bf16 && true_i) hipLaunchKernelGGL((k_diag_prep_varlen<true, true>), grid, dim3(256), 0, st, p);
+    else if (bf16) hipLaunchKernelGGL((k_diag_prep_varlen<true, false>), grid, dim3(256), 0, st, p);
+    else if (true_i) hipLaunchKernelGGL((k_diag_prep_varlen<false, true>), grid, dim3(256), 0, st, p);
+    else hipLaunchKernelGGL((k_diag_prep_varlen<false, false>), grid, dim3(256), 0, st, p);
+    return launch_status();
+}
+
+int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st) {
+    hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(kPlanThreads), 0, st, p);
+    // the block kernel keeps I in true units
+    const int prc = diag_prep_varlen_launch(p, bf16, varlen_cols(p.dv) == 64, st);
+    if (prc != KDN_OK) return prc;
     const int CI = varlen_cols(p.dv);
     const int64_t runs = static_cast<int64_t>(p.nseq) * p.H;
     const int64_t grid = (runs + 7) / 8 * 8 * (p.dv / CI);   // whole groups of 8 runs

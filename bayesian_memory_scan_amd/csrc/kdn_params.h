@@ -71,6 +71,43 @@ __device__ __forceinline__ int32_t find_sequence(const DiagParams& p, int64_t t)
     return lo;
 }
 
+// Plan of a packed batch, run by one workgroup of kPlanThreads: order[rank] =
+// s with the sequences ranked longest first (ties by index), by counting.
+// Lengths are staged in LDS (lens, kPlanLds entries) when they fit; past
+// kMaxPlanSort sequences the quadratic count is skipped and the order is the
+// identity.  Every thread of the workgroup must call it.
+constexpr int32_t kPlanThreads = 1024;
+constexpr int32_t kPlanLds = 4096;
+constexpr int32_t kMaxPlanSort = 16384;
+
+__device__ __forceinline__ int64_t clamped_length(const int64_t* cu, int64_t T, int32_t s) {
+    int64_t a = cu[s], b = cu[s + 1];
+    a = a < 0 ? 0 : (a > T ? T : a);
+    b = b < a ? a : (b > T ? T : b);
+    return b - a;
+}
+
+__device__ inline void plan_longest_first(const int64_t* cu, int32_t n, int64_t T, int32_t* order,
+                                          int64_t* lens) {
+    const bool staged = n <= kPlanLds;
+    if (staged) {
+        for (int32_t s = threadIdx.x; s < n; s += kPlanThreads) lens[s] = clamped_length(cu, T, s);
+        __syncthreads();
+    }
+    for (int32_t s = threadIdx.x; s < n; s += kPlanThreads) {
+        int32_t rank = s;
+        if (n <= kMaxPlanSort) {
+            const int64_t ls = staged ? lens[s] : clamped_length(cu, T, s);
+            rank = 0;
+            for (int32_t u = 0; u < n; ++u) {
+                const int64_t lu = staged ? lens[u] : clamped_length(cu, T, u);
+                rank += (lu > ls || (lu == ls && u < s)) ? 1 : 0;
+            }
+        }
+        order[rank] = s;
+    }
+}
+
 // Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S) of the
 // n = p.nchunks chunks of C tokens.
 __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
@@ -191,21 +228,33 @@ struct BwdParams {
     float* part_dip;      // [ntile][BH,T]: d loss / d I_prior through token t, per tile
     float* part_dip0;     // [ntile][BH]: through the starting state (I0 == NULL)
     float* part_db;       // [ntile][BH,T]: sum_i dbeta_t[i] per tile (Palimpsa-M gating only)
-    float* part_head;     // [BH][2]: per-head sums of the dA and dI_prior terms
-    int64_t BH;
+    float* part_head;     // [BH][tok_split][2]: sums of the dA and dI_prior terms per token range
+    int64_t BH;           // token rows: B*H, or H for a packed batch (its token axis is [H, total_T])
     int64_t H;
-    int64_t T;
+    int64_t T;            // tokens per row (total_T for a packed batch)
     int64_t dv;
     float I_prior;
-    int32_t nchunks;
+    int32_t nchunks;      // chunks per row (fixed-length rows only)
     int32_t ntile;
+    int32_t tok_split;    // token ranges per row in the finishing sums (bwd_token_split)
+    // packed variable-length batch (cu_seqlens != NULL): runs are (sequence, head)
+    const int64_t* cu_seqlens;   // [nseq + 1] token offsets into total_T
+    int32_t* seq_order;          // sequences, longest first (written by the plan pass)
+    int64_t* seq_ckoff;          // [nseq] first checkpoint slot of each sequence (plan pass)
+    int32_t nseq;
+    int64_t nruns;               // state slots: B*H, or nseq*H
+    int64_t ck_stride;           // checkpoint slots per (head, column tile) of a packed batch
 };
 
 int diag_chunk();
 int varlen_cols(int64_t dv);
+int32_t bwd_token_split(int64_t rows, int64_t T);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
                     bool bf16, hipStream_t st);
+int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t dk, bool bf16,
+                           hipStream_t st);
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, bool true_i, hipStream_t st);
+int diag_prep_varlen_launch(const DiagParams& p, bool bf16, bool true_i, hipStream_t st);
 int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);

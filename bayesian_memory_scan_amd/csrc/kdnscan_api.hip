@@ -464,7 +464,8 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const size_t b_rows = ntile > 1 ? align_up(f * static_cast<size_t>(ntile) * BH * T * d_k, 256) : 0;
     const size_t b_tok = align_up(f * static_cast<size_t>(ntile) * BH * T, 256);
     const size_t b_dip0 = align_up(f * static_cast<size_t>(ntile) * BH, 256);
-    const size_t b_head = align_up(f * 2 * static_cast<size_t>(BH), 256);
+    const int32_t split = bwd_token_split(BH, T);
+    const size_t b_head = align_up(f * 2 * static_cast<size_t>(BH) * split, 256);
     const size_t b_db = beta ? 0 : b_tok;
     const size_t need = b_scal + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db;
     const int wc = workspace_check(workspace, workspace_bytes, need);
@@ -505,6 +506,7 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     }
     p.BH = BH; p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.nchunks = static_cast<int32_t>(nch); p.ntile = static_cast<int32_t>(ntile);
+    p.nruns = BH; p.tok_split = split;
 
     DiagParams prep{};
     prep.d = d; prep.A = A; prep.scal = scal;
@@ -512,6 +514,112 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     prep.S = 1; prep.nchunks = static_cast<int32_t>(nch);
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_bwd_launch(p, prep, B, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+}
+
+int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                             kdn_dtype in_dtype, const int64_t* cu_seqlens,
+                             const void* q, const void* k, const void* v,
+                             const void* beta, const void* d,
+                             const float* A, float I_prior,
+                             const float* I0, const float* mu0,
+                             const float* d_o, const float* d_I_T, const float* d_mu_T,
+                             float* dq, float* dk, float* dv, float* dbeta, float* dd,
+                             float* dA, float* dI_prior, float* dI0, float* dmu0,
+                             void* workspace, size_t* workspace_bytes, void* stream) {
+    if (N < 0 || H < 0 || total_T < 0 || N >= 2147483647) return KDN_EINVAL;
+    if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v) || d_k < 64) return KDN_EUNSUPPORTED;
+    if (!finite_positive(I_prior)) return KDN_EINVAL;
+    if (!sizes_fit(1, H, total_T, d_k > d_v ? d_k : d_v)) return KDN_EINVAL;
+    if (!sizes_fit(N, H, 1, d_k * d_v)) return KDN_EINVAL;
+    if (H > 0 && !ok_ptr(dA)) return KDN_EINVAL;
+    const bool work = N > 0 && H > 0;
+    if (work) {
+        if (!ok_ptr(A) || !ok_ptr(cu_seqlens)) return KDN_EINVAL;
+        if (total_T > 0) {
+            if (!ok_ptr(q) || !ok_ptr(k) || !ok_ptr(v) || !ok_opt(beta) || !ok_ptr(d) || !ok_ptr(d_o))
+                return KDN_EINVAL;
+            if (!ok_ptr(dq) || !ok_ptr(dk) || !ok_ptr(dv) || !ok_ptr(dd)) return KDN_EINVAL;
+            if (beta ? !ok_ptr(dbeta) : dbeta != nullptr) return KDN_EINVAL;
+        }
+    }
+    if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(d_I_T) || !ok_opt(d_mu_T)) return KDN_EINVAL;
+    if (!ok_opt(dI_prior) || !ok_opt(dI0) || !ok_opt(dmu0)) return KDN_EINVAL;
+    if ((dI0 && !I0) || (dmu0 && !mu0)) return KDN_EINVAL;
+
+    const int64_t ci = d_v < 64 ? d_v : 64;
+    const int64_t ntile = d_v / ci;
+    const int64_t C = diag_chunk();
+    // checkpoint slots per (head, column tile): every sequence holds
+    // ceil(len / C) + 1, at most total_T / C + 2 N in all
+    const int64_t ck_stride = (total_T + C - 1) / C + 2 * N;
+    if (!grid_fits(((N * H + 7) / 8 * 8) * ntile)) return KDN_EINVAL;
+    const size_t f = sizeof(float);
+    const size_t rows = static_cast<size_t>(H) * total_T;
+    const size_t b_scal = align_up(16 * rows, 256);
+    const size_t b_order = align_up(4 * static_cast<size_t>(N), 256);
+    const size_t b_ckoff = align_up(8 * static_cast<size_t>(N), 256);
+    const size_t b_ckpt = align_up(f * static_cast<size_t>(H) * ck_stride * 2 * d_k * d_v, 256);
+    const size_t b_rows = ntile > 1 ? align_up(f * static_cast<size_t>(ntile) * rows * d_k, 256) : 0;
+    const size_t b_tok = align_up(f * static_cast<size_t>(ntile) * rows, 256);
+    const size_t b_dip0 = align_up(f * static_cast<size_t>(ntile) * N * H, 256);
+    const int32_t split = bwd_token_split(H, work ? total_T : 0);
+    const size_t b_head = align_up(f * 2 * static_cast<size_t>(H) * split, 256);
+    const size_t b_db = beta ? 0 : b_tok;
+    const size_t need = work ? b_scal + b_order + b_ckoff + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db
+                             : b_head;
+    const int wc = workspace_check(workspace, workspace_bytes, need);
+    if (wc == 1) return KDN_OK;
+    if (wc != KDN_OK) return wc;
+    if (H == 0) return KDN_OK;
+
+    char* ws = static_cast<char*>(workspace);
+    BwdParams p{};
+    p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
+    p.A = A; p.I0 = I0; p.mu0 = mu0;
+    p.dout = d_o; p.dI_T = d_I_T; p.dmu_T = d_mu_T;
+    p.dv_out = dv; p.dbeta = dbeta; p.dd = dd; p.dA = dA; p.dI_prior = dI_prior;
+    p.dI0 = dI0; p.dmu0 = dmu0; p.dq = dq; p.dk = dk;
+    p.BH = H; p.H = H; p.T = work ? total_T : 0; p.dv = d_v; p.I_prior = I_prior;
+    p.nchunks = 0; p.ntile = static_cast<int32_t>(ntile);
+    p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
+    p.nruns = N * H; p.ck_stride = ck_stride; p.tok_split = split;
+    DiagParams prep{};
+    if (work) {
+        float4* scal = reinterpret_cast<float4*>(ws);
+        p.scal = scal;
+        ws += b_scal;
+        p.seq_order = reinterpret_cast<int32_t*>(ws);
+        ws += b_order;
+        p.seq_ckoff = reinterpret_cast<int64_t*>(ws);
+        ws += b_ckoff;
+        p.ckpt = reinterpret_cast<float*>(ws);
+        ws += b_ckpt;
+        if (ntile > 1) {
+            p.part_dq = reinterpret_cast<float*>(ws);
+            p.part_dk = reinterpret_cast<float*>(ws + b_rows);
+            ws += 2 * b_rows;
+        } else {
+            p.part_dq = dq;
+            p.part_dk = dk;
+        }
+        p.part_da = reinterpret_cast<float*>(ws);
+        p.part_dip = reinterpret_cast<float*>(ws + b_tok);
+        ws += 2 * b_tok;
+        p.part_dip0 = reinterpret_cast<float*>(ws);
+        ws += b_dip0;
+        if (!beta) p.part_db = reinterpret_cast<float*>(ws + b_head);
+        prep.d = d; prep.A = A; prep.scal = scal;
+        prep.H = H; prep.T = total_T; prep.dv = d_v; prep.I_prior = I_prior;
+        prep.S = 1; prep.cu_seqlens = cu_seqlens; prep.nseq = static_cast<int32_t>(N);
+    } else {
+        // nothing to run but the finishing sums: dA = 0, dI_prior = 0
+        p.nseq = 0;
+        p.ntile = 0;
+    }
+    p.part_head = reinterpret_cast<float*>(ws);
+    (void)hipGetLastError();  // launch status below must reflect this call only
+    return diag_varlen_bwd_launch(p, prep, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
 }
 
 int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,

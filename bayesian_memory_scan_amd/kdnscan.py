@@ -88,6 +88,10 @@ lib.kdn_diag_scan_bwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                   _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp] + _WS
+lib.kdn_diag_scan_varlen_bwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
+                                         _vp, _vp, _vp,
+                                         _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp] + _WS
 lib.kdn_decode_step.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                 _vp, _f, _vp, _vp, _vp, _vp]
 lib.kdn_diag_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, ctypes.POINTER(_i32),
@@ -509,6 +513,71 @@ def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_
         rc = lib.kdn_diag_scan_bwd(*args(_ptr(ws), _nbytes(ws, need)))
     if rc != KDN_OK:
         raise KdnError("kdn_diag_scan_bwd", rc)
+    return g
+
+
+def kdn_diag_scan_varlen_bwd(q, k, v, beta, d, A, I_prior, cu_seqlens, d_o, I0=None, mu0=None,
+                             d_I_T=None, d_mu_T=None, want_prior=True, stream=None):
+    """Gradient of kdn_diag_scan_varlen_fwd over a packed batch.
+
+    q, k [H,total_T,d_k]; v, beta [H,total_T,d_v]; d [H,total_T] (float32 or
+    bf16; beta None = Palimpsa-M gating); cu_seqlens int64 [N+1] on the device;
+    d_o [H,total_T,d_v]; I0, mu0, d_I_T, d_mu_T [N,H,d_k,d_v] float32 or None.
+    Returns a dict: dq, dk [H,total_T,d_k]; dv, dbeta [H,total_T,d_v];
+    dd [H,total_T]; dA [H]; dI_prior [1] (when want_prior); dI0 / dmu0
+    [N,H,d_k,d_v] when I0 / mu0 are given.
+    """
+    torch = _torch()
+    _rank(q, "q", 3)
+    _rank(v, "v", 3)
+    H, T, dk = q.shape
+    dv = v.shape[-1]
+    dts, f32 = _in_dtypes(), (torch.float32,)
+    for n, t, shp in (("q", q, (H, T, dk)), ("k", k, (H, T, dk)), ("v", v, (H, T, dv)),
+                      ("beta", beta, (H, T, dv)), ("d", d, (H, T))):
+        if t is None and n != "beta":
+            raise ValueError(f"{n} is required")
+        _check(t, n, dts, shp)
+    _same_dtype((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d)))
+    _rank(cu_seqlens, "cu_seqlens", 1)
+    _check(cu_seqlens, "cu_seqlens", (torch.int64,))
+    N = cu_seqlens.numel() - 1
+    if N < 0:
+        raise ValueError("cu_seqlens needs at least one entry")
+    state = (N, H, dk, dv)
+    for n, t, shp in (("A", A, (H,)), ("d_o", d_o, (H, T, dv)), ("I0", I0, state),
+                      ("mu0", mu0, state), ("d_I_T", d_I_T, state), ("d_mu_T", d_mu_T, state)):
+        if t is None and n == "d_o":
+            raise ValueError("d_o is required")
+        _check(t, n, f32, shp)
+    dev = _on_gpu((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d), ("A", A),
+                   ("cu_seqlens", cu_seqlens), ("d_o", d_o), ("I0", I0), ("mu0", mu0),
+                   ("d_I_T", d_I_T), ("d_mu_T", d_mu_T)))
+    s = _stream(stream)
+    with torch.cuda.stream(s):
+        new = lambda *shape: torch.empty(shape, dtype=torch.float32, device=dev)
+        g = {"dq": new(H, T, dk), "dk": new(H, T, dk), "dv": new(H, T, dv), "dd": new(H, T),
+             "dA": new(H)}
+        if beta is not None:
+            g["dbeta"] = new(H, T, dv)
+        if want_prior:
+            g["dI_prior"] = new(1)
+        if I0 is not None:
+            g["dI0"] = new(*state)
+        if mu0 is not None:
+            g["dmu0"] = new(*state)
+        o = lambda n: _ptr(g.get(n))
+
+        def args(ws, nbytes):
+            return (N, H, T, dk, dv, _in_dtype(q), _ptr(cu_seqlens), _ptr(q), _ptr(k), _ptr(v),
+                    _ptr(beta), _ptr(d), _ptr(A), float(I_prior), _ptr(I0), _ptr(mu0), _ptr(d_o),
+                    _ptr(d_I_T), _ptr(d_mu_T), o("dq"), o("dk"), o("dv"), o("dbeta"), o("dd"),
+                    o("dA"), o("dI_prior"), o("dI0"), o("dmu0"), ws, nbytes, s.cuda_stream)
+
+        ws, need = _workspace(lib.kdn_diag_scan_varlen_bwd, "kdn_diag_scan_varlen_bwd", args, dev)
+        rc = lib.kdn_diag_scan_varlen_bwd(*args(_ptr(ws), _nbytes(ws, need)))
+    if rc != KDN_OK:
+        raise KdnError("kdn_diag_scan_varlen_bwd", rc)
     return g
 
 

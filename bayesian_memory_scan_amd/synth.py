@@ -43,7 +43,7 @@ import numpy as np
 __all__ = [
     "DiagSpec", "IsoSpec", "WORKLOADS", "workload",
     "diag_head", "diag_inputs", "iso_head", "iso_inputs", "grad_inputs", "state_inputs",
-    "noise_inputs", "VarlenSpec", "varlen_inputs",
+    "noise_inputs", "VarlenSpec", "varlen_inputs", "varlen_grad_inputs",
     "f32_to_bf16_bits",
 ]
 
@@ -131,6 +131,8 @@ WORKLOADS = {
         DiagSpec("diagm_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1006),
         # packed variable-length batch: 64 sequences, 16384 packed tokens per head
         VarlenSpec("varlen_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1007),
+        # gradient over the same packed batch
+        VarlenSpec("varlenbwd_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1007),
         # gradient of the headline forward workload (same inputs)
         DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
@@ -210,6 +212,13 @@ def grad_inputs(spec: DiagSpec, final_state: bool = True) -> dict:
         out["d_I_T"] = g.standard_normal((spec.B, spec.H, spec.d_k, spec.d_v), dtype=np.float32)
         out["d_mu_T"] = g.standard_normal((spec.B, spec.H, spec.d_k, spec.d_v), dtype=np.float32)
     return out
+
+
+def varlen_grad_inputs(spec: VarlenSpec) -> dict:
+    """Seeded upstream gradient of a packed batch: d_o [1,H,total_T,d_v]
+    float32 standard normal."""
+    g = _rng(spec.seed, 0xD1)
+    return {"d_o": g.standard_normal((1, spec.H, spec.total_T, spec.d_v), dtype=np.float32)}
 
 
 def noise_inputs(spec: DiagSpec) -> dict:

@@ -14,7 +14,7 @@ error of the GPU output on that sample against the oracle.
 
 Other workloads (--workload) print the same fields for the short-sequence
 batch (B=8, H=16, T=2048), Palimpsa-M gating, the packed variable-length
-batch, the backward pass, the process-noise variant, the decode step and the
+batch and its gradient, the backward pass, the process-noise variant, the decode step and the
 isotropic scan; they are not the headline line.
 """
 from __future__ import annotations
@@ -216,6 +216,45 @@ def cpu_baseline_bwd(inp, grads, spec, target_s):
             "cores": min(threads, n), "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{n} of {len(heads_all)} heads x {spec.T} tokens, fp64 sequential oracle "
                       f"gradient, {t.seconds:.1f} s wall, heads in parallel on {min(threads, n)} threads"}
+
+
+def _varlen_seq(inp, cu, s):
+    """Sequence s of a packed batch as a one-row batch (the oracle's input form)."""
+    import numpy as np
+    sub = dict(inp)
+    for n in ("q", "k", "v", "beta", "d"):
+        if inp.get(n) is not None:
+            sub[n] = np.ascontiguousarray(inp[n][:, :, cu[s]:cu[s + 1]])
+    return sub
+
+
+def cpu_baseline_varlen_bwd(inp, d_o, spec, target_s):
+    """fp64 oracle gradient of the packed batch, sequence by sequence (every
+    head of a sequence in parallel), over a prefix of the sequences sized to
+    about target_s; tokens/s over the prefix's packed tokens."""
+    import oracle
+    threads = _cpu_threads()
+    cu = [int(x) for x in inp["cu_seqlens"]]
+    heads = [(0, h) for h in range(spec.H)]
+
+    def run(n):
+        for s in range(n):
+            oracle.diag_scan_bwd(_varlen_seq(inp, cu, s), d_o[:, :, cu[s]:cu[s + 1]], heads=heads,
+                                 threads=threads)
+
+    with oracle.Timer() as t1:
+        run(1)
+    per_token = t1.seconds / max(1, cu[1])
+    n = 1
+    while n < spec.N and cu[n + 1] * per_token < target_s:
+        n += 1
+    with oracle.Timer() as t:
+        run(n)
+    return {"value": cu[n] / t.seconds, "unit": "tokens/s", "cores": min(threads, spec.H),
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"first {n} of {spec.N} sequences ({cu[n]} of {spec.total_T} packed tokens) x "
+                      f"{spec.H} heads, fp64 sequential oracle gradient, {t.seconds:.1f} s wall, "
+                      f"heads of a sequence in parallel"}
 
 
 def cpu_baseline_varlen(inp, spec, target_s):
@@ -437,6 +476,41 @@ def main():
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_bwd(inp, grads, spec, a.cpu_seconds)
+    elif a.workload.startswith("varlenbwd_"):
+        inp = synth.varlen_inputs(spec)
+        d_o_h = synth.varlen_grad_inputs(spec)["d_o"]
+        x = {n: _up(inp[n][0], torch, dev) for n in ("q", "k", "v", "beta", "d")}
+        A = _up(inp["A"], torch, dev)
+        cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+        d_o = _up(d_o_h[0], torch, dev)
+
+        def step(_m):
+            kdn.kdn_diag_scan_varlen_bwd(x["q"], x["k"], x["v"], x["beta"], x["d"], A,
+                                         spec.I_prior, cu, d_o)
+
+        tm = _time_steps(torch, step, a.steps, a.warmup)
+        wall, ev_ms = tm.wall, tm.kernel()["avg"]
+        flops = BWD_FLOPS_PER_ENTRY_STEP * spec.H * spec.total_T * spec.d_k * spec.d_v
+        achieved = flops / (ev_ms * 1e-3) / 1e12
+        lens = [int(b - a_) for a_, b in zip(inp["cu_seqlens"][:-1], inp["cu_seqlens"][1:])]
+        out.update({
+            "metric": "tokens/s per MI355X, diag-precision scan backward over a packed "
+                      "variable-length batch",
+            "value": spec.total_T / (wall / a.steps), "unit": "tokens/s",
+            "ms_per_step": wall / a.steps * 1e3,
+            "config": {"workload": spec.name, "sequences": spec.N, "H": spec.H,
+                       "packed_T": spec.total_T, "d_k": spec.d_k, "d_v": spec.d_v,
+                       "inputs": spec.dtype, "length_min": min(lens), "length_max": max(lens),
+                       "gradients": "fp32, loss on o only", "parallelism": "single GPU"},
+            "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
+                         "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
+                         "traffic": _traffic("diag_bwd.hip", f"traffic_{spec.name}.json"),
+                         **tm.fields(),
+                         "note": "events bracket the whole call: sequence plan, frame scalars, "
+                                 "checkpoints, reverse pass and finishing sums"},
+        })
+        if not a.no_cpu:
+            out["cpu_baseline"] = cpu_baseline_varlen_bwd(inp, d_o_h, spec, a.cpu_seconds)
     elif a.workload.startswith("decode_"):
         inp = synth.diag_inputs(spec)
         P = spec.prefix

@@ -187,6 +187,39 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       void* workspace, size_t* workspace_bytes, void* stream);
 
 /*
+ * Gradient of kdn_diag_scan_varlen_fwd (reverse mode) over a packed batch of
+ * N variable-length sequences [Palimpsa Metodologia 3, Palimpsa-M training
+ * on packed sequences], the exact adjoint of the same recurrence per
+ * (sequence, head), in fp32.  For the scalar loss
+ *   L = sum d_o * o + sum d_I_T * I_T + sum d_mu_T * mu_T
+ * it writes (float, overwritten):
+ *   dq, dk [H,total_T,d_k];  dv, dbeta [H,total_T,d_v];  dd [H,total_T];
+ *   dA [H] (summed over every sequence);  dI_prior [1] or NULL;
+ *   dI0, dmu0 [N,H,d_k,d_v] or NULL (allowed only when I0 / mu0 are given).
+ * Inputs: those of kdn_diag_scan_varlen_fwd (cu_seqlens int64 [N+1] on the
+ *   device, q, k [H,total_T,d_k], v, beta [H,total_T,d_v], d [H,total_T],
+ *   I0, mu0 [N,H,d_k,d_v] or NULL), plus d_o [H,total_T,d_v] float
+ *   (required when N*H*total_T > 0), d_I_T, d_mu_T [N,H,d_k,d_v] float or NULL.
+ *   beta == NULL is Palimpsa-M gating (dbeta must then be NULL).
+ * Supported: d_k in {64, 128}, d_v in {16, 32, 64, 128}.  Each sequence runs
+ *   from its own starting state, its chunks aligned to its first token; runs
+ *   are dispatched longest sequence first.  Workspace as for the other calls
+ *   (query with workspace == NULL): frame scalars, the plan, checkpoints
+ *   (8 bytes per state entry per 16 tokens of each sequence, plus one final
+ *   state per sequence) and per-token partial sums.  Deterministic.
+ */
+int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                             kdn_dtype in_dtype, const int64_t* cu_seqlens,
+                             const void* q, const void* k, const void* v,
+                             const void* beta, const void* d,
+                             const float* A, float I_prior,
+                             const float* I0, const float* mu0,
+                             const float* d_o, const float* d_I_T, const float* d_mu_T,
+                             float* dq, float* dk, float* dv, float* dbeta, float* dd,
+                             float* dA, float* dI_prior, float* dI0, float* dmu0,
+                             void* workspace, size_t* workspace_bytes, void* stream);
+
+/*
  * Isotropic scalar-precision filter [KDN abstract, Isotropic KDN;
  * KLA Metodologia 1-3].  Per head, per token:
  *   lambda_t = M_t(lambda_{t-1}),  M_t = [[1 + Lambda_t p_t, Lambda_t a_t^2],

@@ -246,3 +246,44 @@ def test_varlen_validation_and_workspace():
     assert call(I0=MIS) == kdn.KDN_EINVAL
     assert call(N=0, cu=None) == kdn.KDN_OK and n.value == 0
     assert call(nb=None, ws=None) == kdn.KDN_EWORKSPACE
+
+
+def test_varlen_bwd_validation_and_workspace():
+    n = ctypes.c_size_t(0)
+
+    def call(N=3, H=2, T=40, dk=64, dv=64, dt=kdn.KDN_BF16, cu=FAKE, q=FAKE, beta=FAKE, dbeta=FAKE,
+             d_o=FAKE, dA=FAKE, I0=None, mu0=None, dI0=None, dmu0=None, dq=FAKE, nb=n, ws=None):
+        return lib.kdn_diag_scan_varlen_bwd(N, H, T, dk, dv, dt, cu, q, FAKE, FAKE, beta, FAKE, FAKE,
+                                            1.0, I0, mu0, d_o, None, None, dq, FAKE, FAKE, dbeta, FAKE,
+                                            dA, FAKE, dI0, dmu0, ws,
+                                            None if nb is None else ctypes.byref(nb), None)
+
+    assert call() == kdn.KDN_OK
+    # frame scalars (16 B a token row) and checkpoints: every sequence of a
+    # head holds ceil(len / 16) + 1 slots of 2 d_k d_v floats, at most
+    # ceil(T / 16) + 2 N in all
+    ckpt = 4 * 2 * (3 + 2 * 3) * 2 * 64 * 64
+    assert n.value >= 16 * 2 * 40 + ckpt and n.value % 256 == 0
+    full = n.value
+    assert call(beta=None, dbeta=None) == kdn.KDN_OK and n.value > full  # Palimpsa-M: dbeta partials
+    assert call(beta=None, dbeta=FAKE) == kdn.KDN_EINVAL
+    assert call(dbeta=None) == kdn.KDN_EINVAL
+    assert call(N=-1) == kdn.KDN_EINVAL
+    assert call(dt=7) == kdn.KDN_EINVAL
+    assert call(dk=32) == kdn.KDN_EUNSUPPORTED
+    assert call(dv=24) == kdn.KDN_EUNSUPPORTED
+    assert call(cu=None) == kdn.KDN_EINVAL
+    assert call(cu=FAKE + 4) == kdn.KDN_EINVAL
+    assert call(q=None) == kdn.KDN_EINVAL
+    assert call(d_o=None) == kdn.KDN_EINVAL
+    assert call(dA=None) == kdn.KDN_EINVAL
+    assert call(dq=MIS) == kdn.KDN_EINVAL
+    assert call(dI0=FAKE) == kdn.KDN_EINVAL                  # dI0 needs I0
+    assert call(dmu0=FAKE) == kdn.KDN_EINVAL
+    assert call(I0=FAKE, mu0=FAKE, dI0=FAKE, dmu0=FAKE) == kdn.KDN_OK
+    assert call(I0=MIS) == kdn.KDN_EINVAL
+    # no sequences: only the finishing sums (dA = 0, dI_prior = 0) are written
+    assert call(N=0, cu=None, q=None, d_o=None, dq=None) == kdn.KDN_OK and 0 < n.value <= 256
+    assert call(nb=None, ws=None) == kdn.KDN_EWORKSPACE
+    small = ctypes.c_size_t(full - 1)
+    assert call(nb=small, ws=FAKE) == kdn.KDN_EWORKSPACE

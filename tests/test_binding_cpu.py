@@ -124,6 +124,25 @@ def test_backward_and_noise_shapes():
                                     torch.zeros((2, 3, 5)))
 
 
+def test_varlen_backward_shapes():
+    H, T, dk, dv = 2, 9, 64, 16
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    f = lambda *s: torch.zeros(s)
+    cu = torch.tensor([0, 4, 9], dtype=torch.int64)
+    args = lambda d_o: (z(H, T, dk), z(H, T, dk), z(H, T, dv), z(H, T, dv), z(H, T), torch.ones(H),
+                        1.0, cu, d_o)
+    with pytest.raises(ValueError, match="d_o"):
+        kdn.kdn_diag_scan_varlen_bwd(*args(f(H, T + 1, dv)))
+    with pytest.raises(ValueError, match="d_o"):
+        kdn.kdn_diag_scan_varlen_bwd(*args(None))
+    with pytest.raises(ValueError, match="d_mu_T"):
+        kdn.kdn_diag_scan_varlen_bwd(*args(f(H, T, dv)), d_mu_T=f(3, H, dk, dv))
+    with pytest.raises(TypeError, match="cu_seqlens"):
+        kdn.kdn_diag_scan_varlen_bwd(*args(f(H, T, dv))[:7], cu.int(), f(H, T, dv))
+    with pytest.raises(ValueError, match="GPU"):
+        kdn.kdn_diag_scan_varlen_bwd(*args(f(H, T, dv)))
+
+
 # --- the extended C entry points -----------------------------------------
 
 def _fwd_ex(opts, B=1, H=2, T=100, dk=64, dv=64, nbytes=None):
