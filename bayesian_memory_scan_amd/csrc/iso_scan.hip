@@ -34,7 +34,8 @@
 //     the chunk's k transposed; the main pass writes its q-side k to a
 //     per-wave LDS tile and reads it back transposed (the only LDS use).
 // The segment composite pass (COMPOSITE) runs only the state update from a
-// zero state; segments are then combined in order by the shared carry pass.
+// zero state, adding the chunks last to first, each weighted by the decay
+// after it; segments are then combined in order by the shared carry pass.
 #include "kdn_lane.h"
 #include "kdn_params.h"
 
@@ -131,8 +132,10 @@ void k_iso(DiagParams p) {
             }
 
     // Operand loads of the chunk at token t0 through buffer resources that
-    // end at the chunk's last token (rows past it read as 0; F as 1).
+    // end at the chunk's last token (rows past it read as 0; F as 1), and
+    // hold no rows at all for a chunk outside the segment.
     auto chunk_rows = [&](int64_t t0) -> int64_t {
+        if (t0 < t_begin) return 0;   // the composite pass's prefetch before the segment
         const int64_t L = t_end - t0;
         return L < 0 ? 0 : (L < C ? L : C);
     };
@@ -167,6 +170,9 @@ void k_iso(DiagParams p) {
     };
 
     float logsum = 0.0f;   // sum of log2 F over the segment
+    // composite pass: the decay from the end of the chunk being added to the
+    // end of the segment (chunks are added last to first)
+    float dscale = 1.0f;
     // One chunk: qk is the query-side set (unused by the composite pass), kv
     // the update-side set; F and G come from kv in the composite pass.
     auto compute = [&](int64_t t0, QK& qk, const KV& kv) __attribute__((always_inline)) {
@@ -230,7 +236,8 @@ void k_iso(DiagParams p) {
                 buf_store<NT>(ro, static_cast<uint32_t>(((4 * g + r) * DV + cb + NT * c) * 4), row);
             }
         }
-        // mu = e^{b_last} mu + (w (.) K)^T V
+        // main pass: mu = e^{b_last} mu + (w (.) K)^T V; composite pass, chunks
+        // last to first: mu += dscale (w (.) K)^T V, then dscale *= e^{b_last}
         const float decay = exp2f(blast);
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -238,17 +245,18 @@ void k_iso(DiagParams p) {
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) {
                 float ktm;
-                if constexpr (COMPOSITE) ktm = kv.kt[kk][m];
+                if constexpr (COMPOSITE) ktm = kv.kt[kk][m] * dscale;
                 else ktm = kbuf[(4 * g + kk) * KR + MT * c + m];
                 aw[kk] = ws[kk] * ktm;
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                macc[m][n] *= decay;
+                if constexpr (!COMPOSITE) macc[m][n] *= decay;
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) macc[m][n] = mfma4(aw[kk], kv.v[kk][n], macc[m][n]);
             }
         }
+        if constexpr (COMPOSITE) dscale *= decay;
         logsum += blast;
     };
 
@@ -257,17 +265,21 @@ void k_iso(DiagParams p) {
     // exact and never wait on the chunk being prefetched.
     const int64_t nch = (t_end - t_begin + C - 1) / C;
     if constexpr (COMPOSITE) {
-        // two update-side sets: the next chunk's loads are in flight while one computes
+        // Chunks last to first, so that the segment's first chunks are the
+        // ones read most recently when the main pass starts on them.  Two
+        // update-side sets: the previous chunk's loads are in flight while
+        // one computes (a chunk before the segment reads nothing).
         QK none;
         KV xa, xb;
-        load_kv(t_begin, xa);
+        const int64_t tl = t_begin + (nch - 1) * C;
+        load_kv(tl, xa);
         for (int64_t ch = 0; ch < nch; ch += 2) {
-            const int64_t t0 = t_begin + ch * C;
-            load_kv(t0 + C, xb);
+            const int64_t t0 = tl - ch * C;
+            load_kv(t0 - C, xb);
             compute(t0, none, xa);
             if (ch + 1 >= nch) break;
-            load_kv(t0 + 2 * C, xa);
-            compute(t0 + C, none, xb);
+            load_kv(t0 - 2 * C, xa);
+            compute(t0 - C, none, xb);
         }
     } else {
         // two sets of everything: each chunk's operands load a whole chunk ahead
