@@ -15,7 +15,7 @@ _BINDING = {
     "kdn_diag_scan_fwd_noalloc", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd",
     "kdn_diag_scan_varlen_fwd", "kdn_diag_scan_varlen_bwd",
     "kdn_mobius_precision_scan",
-    "kdn_decode_step", "kdn_diag_plan", "kdn_status_string",
+    "kdn_decode_step", "kdn_diag_plan", "kdn_diag_varlen_plan", "kdn_status_string",
     "kdn_last_hip_error",
     "header_functions",
 }

@@ -53,6 +53,37 @@ int comp_tiles(int64_t dk, int64_t dv, bool bf16) {
     return static_cast<int>(tr * tc);
 }
 
+// Composite unit `rest` (the column tile taken out): its token row bh,
+// output slot and token bounds.  A fixed-length batch: sub-segment `sub` of
+// segment `seg` of row bh (sub_tokens).  A packed batch: varlen_comp_unit,
+// run = sequence * H + head.  False when a packed batch's plan has no such
+// unit.
+struct CompUnit {
+    int64_t bh, slot, run, t_begin, t_end;
+    int32_t seg, sub, sq;
+};
+
+__device__ __forceinline__ bool comp_unit(const DiagParams& p, int64_t rest, int32_t R, CompUnit& u) {
+    if (p.cu_seqlens) {
+        int64_t h;
+        if (!varlen_comp_unit(p, rest, h, u.sq, u.seg, u.sub, u.t_begin, u.t_end)) return false;
+        u.bh = h;
+        u.slot = rest;
+        u.run = static_cast<int64_t>(u.sq) * p.H + h;
+        return true;
+    }
+    const int64_t nsub = static_cast<int64_t>(p.S - 1) * R;
+    const int32_t sr = static_cast<int32_t>(rest % nsub);
+    u.bh = rest / nsub;
+    u.seg = sr / R;
+    u.sub = sr % R;
+    u.sq = 0;
+    sub_tokens(p, kDiagChunkTokens, R, u.seg, u.sub, u.t_begin, u.t_end);
+    u.slot = (u.bh * (p.S - 1) + u.seg) * R + u.sub;
+    u.run = u.bh;
+    return true;
+}
+
 template <int DK, int NC, bool BF16>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(BF16 || DK < 128 ? 2 : 1)))
 void k_diag_comp(DiagParams p, int32_t R) {
@@ -66,17 +97,13 @@ void k_diag_comp(DiagParams p, int32_t R) {
     const int g = lane >> 4;
     const int c = lane & 15;
     const int ntile = static_cast<int>(p.dv / NC);
-    const int nsub = (p.S - 1) * R;
     const int64_t id = xcd_local_id();       // a sub-segment's column tiles share an XCD
     const int tile = static_cast<int>(id % ntile);
-    const int64_t rest = id / ntile;
-    const int sr = static_cast<int>(rest % nsub);
-    const int64_t bh = rest / nsub;
-    const int seg = sr / R;
-    const int sub = sr % R;
-    int64_t t_begin, t_end;
-    sub_tokens(p, C, R, seg, sub, t_begin, t_end);
-    if (lane == 0) echo_bounds(p, blockIdx.x, 2, bh, seg, sub, t_begin, t_end, tile);
+    CompUnit u;
+    if (!comp_unit(p, id / ntile, R, u)) return;
+    const int64_t bh = u.bh;
+    const int64_t t_begin = u.t_begin, t_end = u.t_end;
+    if (lane == 0) echo_bounds(p, blockIdx.x, 2, u.run, u.seg, u.sub, t_begin, t_end, tile, u.sq);
     const int64_t DV = p.dv;
     const int64_t cb = static_cast<int64_t>(tile) * NC;
 
@@ -188,7 +215,7 @@ void k_diag_comp(DiagParams p, int32_t R) {
         compute(xb);
     }
 
-    const int64_t slot = (bh * (p.S - 1) + seg) * R + sub;
+    const int64_t slot = u.slot;
     float* out = p.sub + slot * 2 * DK * DV;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -303,17 +330,13 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
     const int lane = threadIdx.x;
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int nsub = (p.S - 1) * R;
     const int64_t id = xcd_local_id();       // a sub-segment's tiles share an XCD
     const int tile = static_cast<int>(id % TILES);
-    const int64_t rest = id / TILES;
-    const int sr = static_cast<int>(rest % nsub);
-    const int64_t bh = rest / nsub;
-    const int seg = sr / R;
-    const int sub = sr % R;
-    int64_t t_begin, t_end;
-    sub_tokens(p, 16, R, seg, sub, t_begin, t_end);
-    if (lane == 0) echo_bounds(p, blockIdx.x, 2, bh, seg, sub, t_begin, t_end, tile);
+    CompUnit u;
+    if (!comp_unit(p, id / TILES, R, u)) return;
+    const int64_t bh = u.bh;
+    const int64_t t_begin = u.t_begin, t_end = u.t_end;
+    if (lane == 0) echo_bounds(p, blockIdx.x, 2, u.run, u.seg, u.sub, t_begin, t_end, tile, u.sq);
     const int rb = (tile / TC) * 16 * MT;    // first key row of the wave tile
     const int cb = (tile % TC) * 16 * NT;    // first value column
     const int64_t DV_ = p.dv;
@@ -451,7 +474,7 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
     load_k(tb, x);
     for (int64_t i = 0; i < nblk; ++i, tb -= KB) compute(x, tb - KB);
 
-    const int64_t slot = (bh * (p.S - 1) + seg) * R + sub;
+    const int64_t slot = u.slot;
     float* out = p.sub + slot * 2 * DK * DV_;
 #pragma unroll
     for (int m = 0; m < MT; ++m)
@@ -505,6 +528,56 @@ __global__ __launch_bounds__(256) void k_diag_carry_sub(DiagParams p, int64_t dk
     for (int64_t e = elem_first(); e < n_total; e += elem_stride()) carry_sub_entry(p, dk, e, R);
 }
 
+// Packed batch: the ordered carry of every split sequence.  One thread per
+// (split sequence, head, memory entry) runs from the sequence's own starting
+// state through its segments' sub-segment composites; composite slot c of
+// head h then holds the state that segment c - c0 + 1 starts from, c0 the
+// sequence's first composite segment.  A grid of at most kCarryGroups
+// workgroups walks the entries of the split sequences there are.
+constexpr int64_t kCarryGroups = 1024;
+__global__ __launch_bounds__(256) void k_varlen_carry(DiagParams p, int64_t dk, int64_t n_total) {
+    const int64_t n_per_head = dk * p.dv;
+    const int64_t n_seq = p.H * n_per_head;
+    const int64_t nsplit = p.nwork[2];
+    const int32_t R = p.nwork[3];
+    for (int64_t e = elem_first(); e < n_total; e += elem_stride()) {
+        const int64_t k = e / n_seq;
+        if (k >= nsplit) break;   // e only grows
+        const int64_t h = e % n_seq / n_per_head;
+        const int64_t r = e % n_per_head;
+        const int32_t sq = p.split_seq[k];
+        const int32_t c0 = p.seq_comp[sq];
+        if (c0 < 0) continue;
+        int64_t a, b;
+        sequence_tokens(p, sq, a, b);
+        const int64_t nseg = varlen_segments(p, b - a);
+        const int64_t off = (static_cast<int64_t>(sq) * p.H + h) * n_per_head + r;
+        const float m0 = p.mu0 ? p.mu0[off] : 0.0f;
+        float J = 0.0f, eta;
+        if (p.I0) {
+            const float I0 = p.I0[off];
+            J = I0 - p.I_prior;
+            eta = I0 * m0;
+        } else {
+            eta = p.I_prior * m0;
+        }
+        for (int64_t g = 0; g + 1 < nseg; ++g) {
+            const int64_t c = c0 + g;
+            if (c >= p.vl_comps) break;
+            for (int u = 0; u < R; ++u) {
+                const int64_t slot = (c * p.H + h) * R + u;
+                const float* sub = p.sub + slot * 2 * n_per_head;
+                const float G = p.gsub[slot];
+                J = __builtin_fmaf(G, J, sub[r]);
+                eta = __builtin_fmaf(G, eta, sub[n_per_head + r]);
+            }
+            float* cin = p.comp + (c * p.H + h) * 2 * n_per_head;
+            cin[r] = J;
+            cin[n_per_head + r] = eta;
+        }
+    }
+}
+
 template <int DK, bool BF16>
 static int comp_launch_dv(const DiagParams& p, int64_t dv, int64_t grid, int32_t R, hipStream_t st) {
     switch (dv) {
@@ -548,6 +621,21 @@ static int comp_bf_launch(const DiagParams& p, int64_t dk, int64_t grid, int32_t
         case 128: return comp_bf_launch_dv<128>(p, grid, R, st);
         default: return KDN_EUNSUPPORTED;
     }
+}
+
+// Packed batch: composites of every split sequence's segments but its last,
+// in the plan's sub-segments (the grid covers the composite storage of
+// vl_comps x H x R units; waves past the plan's composites return at once),
+// then the carries.
+int diag_varlen_comp_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
+    const int64_t grid = p.vl_comps * p.H * R * comp_tiles(dk, p.dv, bf16);
+    if (grid == 0) return KDN_OK;
+    int rc = bf16 ? comp_bf_launch(p, dk, grid, R, st) : comp_launch<false>(p, dk, grid, R, st);
+    if (rc != KDN_OK) return rc;
+    const int64_t n = p.vl_comps * p.H * dk * p.dv;
+    const int64_t groups = elem_groups(n) < kCarryGroups ? elem_groups(n) : kCarryGroups;
+    hipLaunchKernelGGL(k_varlen_carry, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, st, p, dk, n);
+    return launch_status();
 }
 
 // Composites of segments 0..S-2 in R sub-segments each (one wave per

@@ -40,7 +40,6 @@ namespace kdn {
 // first token and wherever s would pass e^kFrameLog; at a start the state is
 // multiplied by rho_t = alpha_t / s_{t-1} and s restarts at 1.
 constexpr float kFrameLog = 30.0f;
-constexpr int kDiagChunkTokens = 16;
 
 template <int DK, int CI, int W, int C, bool BF16>
 __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
@@ -92,29 +91,39 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
         const int64_t within = b % (8 * ntile);
         tile = static_cast<int>(within / 8);
         wg = b / (8 * ntile) * 8 + within % 8;
-        if (wg >= static_cast<int64_t>(p.nseq) * p.H) return;   // padding of the last group
     } else {
         wg = xcd_local_id();
         tile = static_cast<int>(wg % ntile);
         wg /= ntile;
     }
     const int i = tile * CI + col;
-    // bh: head of the token inputs; sb: slot of this run's starting/final state
+    // bh: head of the token inputs; sb: slot of this run's starting/final
+    // state; cin: its carried-in starting state, or NULL for the run's own;
+    // last: the run ends its sequence and writes the final state
     int seg;
     int32_t sq = -1;
     int64_t bh, sb, t_begin, t_end;
+    const float* cin = nullptr;
+    bool last;
     if (p.cu_seqlens) {
-        // one whole sequence of one head
-        bh = wg % p.H;
-        sq = p.seq_order[wg / p.H];
-        sb = static_cast<int64_t>(sq) * p.H + bh;
-        seg = 0;
-        sequence_tokens(p, sq, t_begin, t_end);
+        // one segment (the whole sequence unless it is split) of one head
+        VarlenItem it;
+        if (!varlen_item(p, wg, it)) return;   // past the plan's items
+        bh = it.bh;
+        sb = it.sb;
+        sq = it.sq;
+        seg = it.seg;
+        t_begin = it.t_begin;
+        t_end = it.t_end;
+        last = it.last;
+        if (it.carry >= 0) cin = p.comp + ((it.carry * p.H + bh) * 2) * DK * p.dv;
     } else {
         seg = static_cast<int>(wg % p.S);
         bh = wg / p.S;
         sb = bh;
         segment_tokens(p, C, seg, t_begin, t_end);
+        last = seg == p.S - 1;
+        if (p.S > 1) cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
     }
     if (tid == 0) echo_bounds(p, blockIdx.x, 1, sb, seg, tile, t_begin, t_end, sq);
 
@@ -129,7 +138,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
     // ---- state, JP key rows per lane, in the scaled frame with s = 1 at the
     //      segment start: I~ and the information mean eta~ ----
     float I[JP], eta[JP];
-    if (p.S == 1) {
+    if (!cin) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = (sb * DK + j0 + r) * p.dv + i;
@@ -139,7 +148,6 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
             eta[r] = I0 * m0;
         }
     } else {
-        const float* cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i;
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(W * kWave) void k_diag(DiagParams p) {
 
     // back from the scaled frame: true state = scaled state / s_last
     const float s_last = s_prev;
-    if (seg == p.S - 1) {
+    if (last) {
 #pragma unroll
         for (int r = 0; r < JP; ++r) {
             const int64_t off = (sb * DK + j0 + r) * p.dv + i;
@@ -432,28 +440,38 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         const int64_t within = blk % (8 * ntile);
         tile = static_cast<int>(within / 8);
         wg = blk / (8 * ntile) * 8 + within % 8;
-        if (wg >= static_cast<int64_t>(p.nseq) * p.H) return;   // padding of the last group
     } else {
         wg = xcd_local_id();
         tile = static_cast<int>(wg % ntile);
         wg /= ntile;
     }
     const int i0 = tile * CI + 2 * cp;
-    // bh: head of the token inputs; sb: slot of this run's starting/final state
+    // bh: head of the token inputs; sb: slot of this run's starting/final
+    // state; cin: its carried-in starting state, or NULL for the run's own;
+    // last: the run ends its sequence and writes the final state
     int seg;
     int32_t sq = -1;
     int64_t bh, sb, t_begin, t_end;
+    const float* cin = nullptr;
+    bool last;
     if (p.cu_seqlens) {
-        bh = wg % p.H;
-        sq = p.seq_order[wg / p.H];
-        sb = static_cast<int64_t>(sq) * p.H + bh;
-        seg = 0;
-        sequence_tokens(p, sq, t_begin, t_end);
+        VarlenItem it;
+        if (!varlen_item(p, wg, it)) return;   // past the plan's items
+        bh = it.bh;
+        sb = it.sb;
+        sq = it.sq;
+        seg = it.seg;
+        t_begin = it.t_begin;
+        t_end = it.t_end;
+        last = it.last;
+        if (it.carry >= 0) cin = p.comp + ((it.carry * p.H + bh) * 2) * DK * p.dv;
     } else {
         seg = static_cast<int>(wg % p.S);
         bh = wg / p.S;
         sb = bh;
         segment_tokens(p, C, seg, t_begin, t_end);
+        last = seg == p.S - 1;
+        if (p.S > 1) cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
     }
     if (tid == 0) echo_bounds(p, blockIdx.x, 1, sb, seg, tile, t_begin, t_end, sq);
 
@@ -466,7 +484,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
 
     // I in true units, eta~ = s eta with s = 1 at the segment start
     float I[RB][2], eta[RB][2];
-    if (p.S == 1) {
+    if (!cin) {
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int64_t off = (sb * DK + j0 + r) * p.dv + i0;
@@ -479,7 +497,6 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
             }
         }
     } else {
-        const float* cin = p.comp + ((bh * p.S + seg) * 2) * DK * p.dv;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
             const int64_t off = static_cast<int64_t>(j0 + r) * p.dv + i0;
@@ -771,7 +788,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         if (c + 2 < nch) fetch(t0 + 2 * C, chunk_len(c + 2));
     }
 
-    if (seg == p.S - 1) {
+    if (last) {
         const float inv_s_last = t_end > t_begin ? 1.0f / sch[t_end - 1].z : 1.0f;
 #pragma unroll
         for (int r = 0; r < RB; ++r) {
@@ -966,11 +983,139 @@ int diag_chunk() { return kDiagChunk; }
 // that wide, else 32- or d_v-column tiles.
 int varlen_cols(int64_t dv) { return dv >= 64 ? 64 : (dv < 32 ? static_cast<int>(dv) : 32); }
 
-// The plan of a packed batch: sequences ordered longest first (ties by
-// index), by rank counting in one workgroup.
-__global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(DiagParams p) {
+// Main-pass grid of a packed batch: whole groups of 8 runs (item x head) x
+// column tiles.
+int64_t varlen_main_grid(int64_t items, int64_t H, int64_t dv) {
+    return (items * H + 7) / 8 * 8 * (dv / varlen_cols(dv));
+}
+
+// The plan of a packed batch, one workgroup.  Sequences are ordered longest
+// first (ties by index) by rank counting; a sequence longer than vl_seg
+// tokens is cut into ceil(len / vl_seg) segments.  The main-pass items are
+// every sequence's segments in that order, each sequence's in token order;
+// the composite segments are every split sequence's segments but its last.
+// A sequence's offsets into the item, composite and split-sequence tables
+// are sums over the sequences ranked before it, taken in the same counting
+// loop as its rank.  Past kMaxPlanSort sequences the order is the index
+// order and the offsets are prefix sums.  Table writes stay within their
+// capacities, and the counts in nwork are clamped to them, so a malformed
+// offset table cannot send a later pass out of bounds.  `units` is the
+// composite storage in (segment, head, sub-segment) units; each composite
+// segment takes units / (segments x H) sub-segments (nwork[3]), at most one
+// per 4 chunks, so fewer split sequences get finer sub-segments.
+__global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(DiagParams p, int64_t units) {
     __shared__ int64_t lens[kPlanLds];
-    plan_longest_first(p.cu_seqlens, p.nseq, p.T, p.seq_order, lens);
+    __shared__ int32_t nsg[kPlanLds];
+    __shared__ int64_t part[3][kPlanThreads];
+    const int32_t n = p.nseq;
+    const int tid = threadIdx.x;
+    const bool staged = n <= kPlanLds;
+    if (staged) {
+        for (int32_t s = tid; s < n; s += kPlanThreads) {
+            const int64_t l = clamped_length(p.cu_seqlens, p.T, s);
+            lens[s] = l;
+            nsg[s] = static_cast<int32_t>(varlen_segments(p, l));
+        }
+        __syncthreads();
+    }
+    auto len = [&](int32_t s) { return staged ? lens[s] : clamped_length(p.cu_seqlens, p.T, s); };
+    auto segs = [&](int32_t s) -> int64_t { return staged ? nsg[s] : varlen_segments(p, len(s)); };
+    auto place = [&](int32_t s, int64_t nseg, int64_t rank, int64_t io, int64_t co, int64_t so) {
+        p.seq_order[rank] = s;
+        for (int64_t g = 0; g < nseg && io + g < p.vl_items; ++g) {
+            p.item_seq[io + g] = s;
+            p.item_seg[io + g] = static_cast<int32_t>(g);
+        }
+        p.seq_comp[s] = nseg > 1 && co < p.vl_comps ? static_cast<int32_t>(co) : -1;
+        for (int64_t g = 0; g + 1 < nseg && co + g < p.vl_comps; ++g) {
+            p.comp_seq[co + g] = s;
+            p.comp_seg[co + g] = static_cast<int32_t>(g);
+        }
+        if (nseg > 1 && so < p.vl_comps) p.split_seq[so] = s;
+    };
+    // this thread's sums of items, composite segments and split sequences
+    int64_t ni = 0, nc = 0, ns = 0;
+    const bool sorted = n <= kMaxPlanSort;
+    const int32_t per = (n + kPlanThreads - 1) / kPlanThreads;
+    const int32_t s0 = tid * per < n ? tid * per : n;
+    const int32_t s1 = s0 + per < n ? s0 + per : n;
+    if (sorted) {
+        for (int32_t s = tid; s < n; s += kPlanThreads) {
+            const int64_t ls = len(s);
+            int64_t rank = 0, io = 0, co = 0, so = 0;
+            for (int32_t u = 0; u < n; ++u) {
+                const int64_t lu = len(u);
+                if (lu > ls || (lu == ls && u < s)) {
+                    const int64_t g = segs(u);
+                    ++rank;
+                    io += g;
+                    co += g - 1;
+                    so += g > 1 ? 1 : 0;
+                }
+            }
+            const int64_t g = segs(s);
+            place(s, g, rank, io, co, so);
+            ni += g;
+            nc += g - 1;
+            ns += g > 1 ? 1 : 0;
+        }
+    } else {
+        for (int32_t s = s0; s < s1; ++s) {
+            const int64_t g = segs(s);
+            ni += g;
+            nc += g - 1;
+            ns += g > 1 ? 1 : 0;
+        }
+    }
+    part[0][tid] = ni;
+    part[1][tid] = nc;
+    part[2][tid] = ns;
+    __syncthreads();
+    if (!sorted) {
+        // index order: inclusive prefix sums over the threads (Hillis-Steele
+        // in LDS), then each thread places its run of sequences
+        for (int o = 1; o < kPlanThreads; o <<= 1) {
+            int64_t v[3];
+#pragma unroll
+            for (int x = 0; x < 3; ++x) v[x] = tid >= o ? part[x][tid - o] : 0;
+            __syncthreads();
+#pragma unroll
+            for (int x = 0; x < 3; ++x) part[x][tid] += v[x];
+            __syncthreads();
+        }
+        int64_t io = part[0][tid] - ni, co = part[1][tid] - nc, so = part[2][tid] - ns;
+        for (int32_t s = s0; s < s1; ++s) {
+            const int64_t g = segs(s);
+            place(s, g, s, io, co, so);
+            io += g;
+            co += g - 1;
+            so += g > 1 ? 1 : 0;
+        }
+    } else {
+        // totals only: a tree sum in LDS
+        for (int h = kPlanThreads / 2; h > 0; h >>= 1) {
+            if (tid < h) {
+#pragma unroll
+                for (int x = 0; x < 3; ++x) part[x][tid] += part[x][tid + h];
+            }
+            __syncthreads();
+        }
+    }
+    if (tid == 0) {
+        const int64_t last = sorted ? 0 : kPlanThreads - 1;
+        const int64_t ti = part[0][last], tc = part[1][last], ts = part[2][last];
+        const int64_t c = tc < p.vl_comps ? tc : p.vl_comps;
+        p.nwork[0] = static_cast<int32_t>(ti < p.vl_items ? ti : p.vl_items);
+        p.nwork[1] = static_cast<int32_t>(c);
+        p.nwork[2] = static_cast<int32_t>(ts < p.vl_comps ? ts : p.vl_comps);
+        // sub-segments per composite segment: the unit budget spread over the
+        // composite segments there are, at least 4 chunks each
+        int64_t R = c > 0 ? units / (c * p.H) : 1;
+        const int64_t rmax = p.vl_seg / (4 * kDiagChunkTokens);
+        if (R > rmax) R = rmax;
+        if (R < 1) R = 1;
+        p.nwork[3] = static_cast<int32_t>(R);
+    }
 }
 
 // Packed variable-length batch (p.cu_seqlens set, p.S == 1): the plan, frame
@@ -988,14 +1133,22 @@ int diag_prep_varlen_launch(const DiagParams& p, bool bf16, bool true_i, hipStre
     return launch_status();
 }
 
-int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st) {
-    hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(kPlanThreads), 0, st, p);
+// Packed batch: the plan, the frame scalars, the composites and carries of
+// split sequences, then the main pass over the plan's items (the grid covers
+// the item capacity; workgroups past the plan's items return at once).
+int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
+    hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(kPlanThreads), 0, st, p, p.vl_comps * p.H * R);
     // the block kernel keeps I in true units
     const int prc = diag_prep_varlen_launch(p, bf16, varlen_cols(p.dv) == 64, st);
     if (prc != KDN_OK) return prc;
     const int CI = varlen_cols(p.dv);
-    const int64_t runs = static_cast<int64_t>(p.nseq) * p.H;
-    const int64_t grid = (runs + 7) / 8 * 8 * (p.dv / CI);   // whole groups of 8 runs
+    const int64_t grid = varlen_main_grid(p.vl_items, p.H, p.dv);
+    if (p.vl_comps > 0) {
+        DiagParams pc = p;
+        pc.echo_base = grid;   // composite records after the main pass's
+        const int crc = diag_varlen_comp_launch(pc, dk, bf16, R, st);
+        if (crc != KDN_OK) return crc;
+    }
     if (grid == 0) return launch_status();
     int rc = record_event(p.main_begin, st);
     if (rc != KDN_OK) return rc;

@@ -36,6 +36,23 @@ struct DiagParams {
     const int64_t* cu_seqlens;   // packed variable-length batch: [nseq + 1] offsets, or NULL
     int32_t* seq_order;          // its sequences, longest first (written by the plan pass)
     int32_t nseq;
+    // Packed batch: sequences longer than vl_seg tokens are cut into segments
+    // of vl_seg tokens (the last one shorter); the plan pass writes the tables.
+    // A packed batch's comp / sub / gsub are indexed by composite segment c
+    // (a segment that is not its sequence's last): comp [vl_comps][H][2][dk][dv]
+    // holds the carry into segment c + 1 of its sequence, sub
+    // [vl_comps][H][R][2][dk][dv] and gsub [vl_comps][H][R] its sub-segments.
+    int32_t* item_seq;           // [vl_items] sequence of each main-pass item, dispatch order
+    int32_t* item_seg;           // [vl_items] the item's segment within its sequence
+    int32_t* seq_comp;           // [nseq] first composite segment of a split sequence, else -1
+    int32_t* comp_seq;           // [vl_comps] sequence of each composite segment
+    int32_t* comp_seg;           // [vl_comps] its segment within the sequence
+    int32_t* split_seq;          // [vl_comps] the split sequences, in plan order
+    int32_t* nwork;              // [4]: items, composite segments, split sequences (each <= capacity),
+                                 // sub-segments per composite segment
+    int64_t vl_seg;              // segment length of a split sequence (multiple of 256), 0 = no split
+    int64_t vl_items;            // capacity of the item tables
+    int64_t vl_comps;            // capacity of the composite tables
     int64_t* echo;               // bounds echo (kdn_scan_opts), or NULL
     int64_t echo_cap;            // its capacity in int64 words
     int64_t echo_base;           // first record slot of the launch being made
@@ -47,6 +64,8 @@ struct DiagParams {
 // Token bounds of the work units: every kernel takes them from these, and the
 // bounds echo reports what they returned.
 // ---------------------------------------------------------------------------
+
+constexpr int kDiagChunkTokens = 16;   // tokens per chunk of the diagonal scan
 
 // Packed variable-length batch: tokens of sequence s, [cu[s], cu[s+1]),
 // clamped into [0, T] so that a malformed offset table cannot send a
@@ -108,6 +127,77 @@ __device__ inline void plan_longest_first(const int64_t* cu, int32_t n, int64_t 
     }
 }
 
+// Packed batch: segments of a sequence of len tokens (1 when it is not split).
+__device__ __forceinline__ int64_t varlen_segments(const DiagParams& p, int64_t len) {
+    return p.vl_seg > 0 && len > p.vl_seg ? (len + p.vl_seg - 1) / p.vl_seg : 1;
+}
+
+// One main-pass work item of a packed batch, run wg = item * H + head: the
+// item's sequence and segment from the plan's tables, its tokens (segment g
+// of sequence s holds [cu[s] + g vl_seg, min(cu[s] + (g + 1) vl_seg,
+// cu[s+1]))), whether it is the sequence's last segment (it then writes the
+// final state), and the composite slot holding its starting state (-1: the
+// sequence's own starting state).  False past the plan's items.
+struct VarlenItem {
+    int64_t bh, sb, t_begin, t_end, carry;
+    int32_t sq, seg;
+    bool last;
+};
+
+__device__ __forceinline__ bool varlen_item(const DiagParams& p, int64_t wg, VarlenItem& it) {
+    const int64_t item = wg / p.H;
+    if (item >= p.nwork[0]) return false;
+    it.bh = wg % p.H;
+    it.sq = p.item_seq[item];
+    it.seg = p.item_seg[item];
+    it.sb = static_cast<int64_t>(it.sq) * p.H + it.bh;
+    int64_t a, b;
+    sequence_tokens(p, it.sq, a, b);
+    if (p.vl_seg > 0) {
+        const int64_t t0 = a + static_cast<int64_t>(it.seg) * p.vl_seg;
+        it.t_begin = t0 < b ? t0 : b;
+        it.t_end = t0 + p.vl_seg < b ? t0 + p.vl_seg : b;
+    } else {
+        it.t_begin = a;
+        it.t_end = b;
+    }
+    it.last = it.t_end == b;
+    it.carry = -1;
+    const int32_t c0 = p.seq_comp[it.sq];
+    if (it.seg > 0 && c0 >= 0) {
+        const int64_t c = static_cast<int64_t>(c0) + it.seg - 1;
+        if (c < p.vl_comps) it.carry = c;
+    }
+    return true;
+}
+
+// One composite unit of a packed batch, rest = (c * H + h) * R + u with R
+// the plan's sub-segments per composite segment (nwork[3]): sub-segment u of
+// composite segment c (segment `seg` of sequence `sq`) on head h, the
+// segment's vl_seg / 16 chunks split evenly over R.  Its output slot is
+// rest.  False past the plan's composite segments.
+__device__ __forceinline__ bool varlen_comp_unit(const DiagParams& p, int64_t rest,
+                                                 int64_t& h, int32_t& sq, int32_t& seg, int32_t& sub,
+                                                 int64_t& t0, int64_t& t1) {
+    const int32_t R = p.nwork[3];
+    sub = static_cast<int32_t>(rest % R);
+    const int64_t ch = rest / R;
+    h = ch % p.H;
+    const int64_t c = ch / p.H;
+    if (c >= p.nwork[1]) return false;
+    sq = p.comp_seq[c];
+    seg = p.comp_seg[c];
+    int64_t a, b;
+    sequence_tokens(p, sq, a, b);
+    const int64_t m = p.vl_seg / kDiagChunkTokens;
+    const int64_t s0 = a + static_cast<int64_t>(seg) * p.vl_seg;
+    const int64_t x0 = s0 + (sub * m / R) * kDiagChunkTokens;
+    const int64_t x1 = s0 + ((sub + 1) * m / R) * kDiagChunkTokens;
+    t0 = x0 < b ? x0 : b;
+    t1 = x1 < b ? x1 : b;
+    return true;
+}
+
 // Token bounds of segment `seg`: whole chunks [seg*n/S, (seg+1)*n/S) of the
 // n = p.nchunks chunks of C tokens.
 __device__ __forceinline__ void segment_tokens(const DiagParams& p, int C, int seg,
@@ -136,7 +226,7 @@ __device__ __forceinline__ void sub_tokens(const DiagParams& p, int C, int R, in
 constexpr int kEchoWords = KDN_ECHO_WORDS;
 __device__ __forceinline__ void echo_bounds(const DiagParams& p, int64_t unit, int64_t kind, int64_t run,
                                             int64_t seg, int64_t part, int64_t t0, int64_t t1,
-                                            int64_t sequence) {
+                                            int64_t sequence, int64_t extra = 0) {
     if (p.echo == nullptr) return;
     const int64_t slot = p.echo_base + unit;
     if ((slot + 1) * kEchoWords > p.echo_cap) return;
@@ -148,7 +238,7 @@ __device__ __forceinline__ void echo_bounds(const DiagParams& p, int64_t unit, i
     r[4] = t0;
     r[5] = t1;
     r[6] = sequence;
-    r[7] = 0;
+    r[7] = extra;
 }
 
 struct DecodeParams {
@@ -248,6 +338,7 @@ struct BwdParams {
 
 int diag_chunk();
 int varlen_cols(int64_t dv);
+int diag_varlen_comp_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int32_t bwd_token_split(int64_t rows, int64_t T);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
                     bool bf16, hipStream_t st);
@@ -256,7 +347,8 @@ int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t d
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, bool true_i, hipStream_t st);
 int diag_prep_varlen_launch(const DiagParams& p, bool bf16, bool true_i, hipStream_t st);
 int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);
-int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, hipStream_t st);
+int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st);
+int64_t varlen_main_grid(int64_t items, int64_t H, int64_t dv);
 int copy_state_launch(const DiagParams& p, int64_t B, int64_t dk, bool iso, hipStream_t st);
 int decode_launch(const DecodeParams& p, int64_t B, int64_t dk, int64_t dv, bool bf16, hipStream_t st);
 int comp_tiles(int64_t dk, int64_t dv, bool bf16);

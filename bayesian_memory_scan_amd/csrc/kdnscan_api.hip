@@ -88,6 +88,63 @@ Plan plan_iso(int64_t BH, int64_t T, int64_t dv, int32_t request) {
     return pl;
 }
 
+// Packed batch: the segment length of a split sequence and the sub-segments
+// of each composite.  A sequence is split when it is longer than its fair
+// share of the chip, ceil(H total_T tiles / CUs) tokens rounded up to a
+// multiple of 256, and than kVarlenMinSeg; the request is 0 (automatic) or
+// 1 (never split).  comps bounds the composite segments: a split sequence
+// of len tokens has ceil(len / seg) - 1 <= len / seg of them, so all
+// sequences together at most total_T / seg.  Sub-segments: about eight
+// one-wave units (32 value columns) per CU over that bound, at least four
+// chunks each.
+constexpr int64_t kVarlenMinSeg = 512;
+struct VarlenPlan {
+    int64_t seg;     // 0: no sequence is split
+    int32_t R;
+    int64_t comps;   // capacity of the composite tables
+    int64_t items;   // capacity of the item tables
+};
+VarlenPlan plan_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dv, int32_t request) {
+    VarlenPlan v{0, 1, 0, N};
+    if (request == 1 || N == 0 || H == 0) return v;
+    const int64_t ntile = dv / varlen_cols(dv);
+    const int64_t fair = (H * total_T * ntile + kNumCU - 1) / kNumCU;
+    int64_t L = (fair + 255) / 256 * 256;
+    if (L < kVarlenMinSeg) L = kVarlenMinSeg;
+    if (total_T <= L) return v;
+    v.seg = L;
+    v.comps = total_T / L;
+    v.items = N + v.comps;
+    const int64_t units = v.comps * H * (dv > 32 ? dv / 32 : 1);
+    int64_t R = 8 * kNumCU / units;
+    if (R > L / (4 * diag_chunk())) R = L / (4 * diag_chunk());
+    if (R < 1) R = 1;
+    v.R = static_cast<int32_t>(R);
+    return v;
+}
+
+// Workspace of a packed batch's forward scan, in this order.
+struct VarlenWs {
+    size_t scal, order, items, seqcomp, comptab, nwork, comp, sub, gsub, total;
+};
+VarlenWs varlen_workspace(int64_t N, int64_t H, int64_t total_T, int64_t dk, int64_t dv,
+                          const VarlenPlan& v) {
+    VarlenWs w{};
+    const size_t f = sizeof(float);
+    w.scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
+    w.order = align_up(4 * static_cast<size_t>(N), 256);
+    w.items = align_up(4 * static_cast<size_t>(v.items), 256);          // each of item_seq, item_seg
+    w.seqcomp = align_up(4 * static_cast<size_t>(N), 256);
+    w.comptab = v.comps > 0 ? align_up(4 * static_cast<size_t>(v.comps), 256) : 0;   // each of 3
+    w.nwork = 256;
+    const size_t units = static_cast<size_t>(v.comps) * H;
+    w.comp = v.comps > 0 ? align_up(f * units * 2 * dk * dv, 256) : 0;
+    w.sub = v.comps > 0 ? align_up(f * units * v.R * 2 * dk * dv, 256) : 0;
+    w.gsub = v.comps > 0 ? align_up(f * units * v.R, 256) : 0;
+    w.total = w.scal + w.order + 2 * w.items + w.seqcomp + 3 * w.comptab + w.nwork + w.comp + w.sub + w.gsub;
+    return w;
+}
+
 size_t scan_workspace_bytes(int64_t BH, int64_t dk, int64_t dv, const Plan& pl) {
     if (pl.S <= 1) return 0;
     const size_t comp = align_up(sizeof(float) * static_cast<size_t>(BH) * pl.S * 2 * dk * dv, 256);
@@ -365,6 +422,8 @@ int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d
     if (!finite_positive(I_prior)) return KDN_EINVAL;
     if (!sizes_fit(1, H, total_T, d_k > d_v ? d_k : d_v) || !sizes_fit(N, H, 1, d_k * d_v)) return KDN_EINVAL;
     const bool work = N > 0 && H > 0;
+    const VarlenPlan vp = plan_varlen(N, H, total_T, d_v, opt_segments(opts));
+    if (vp.items >= 2147483647) return KDN_EINVAL;
     if (work && (cu_seqlens == nullptr || (reinterpret_cast<uintptr_t>(cu_seqlens) & 7u) != 0))
         return KDN_EINVAL;
     if (work && !ok_ptr(A)) return KDN_EINVAL;
@@ -373,11 +432,12 @@ int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d
             return KDN_EINVAL;
     }
     if (!ok_opt(I0) || !ok_opt(mu0) || !ok_opt(I_T) || !ok_opt(mu_T)) return KDN_EINVAL;
-    const int64_t ntile = d_v / varlen_cols(d_v);
-    if (!grid_fits((N * H + 7) * ntile)) return KDN_EINVAL;
-    report_echo(opts, N > 0 && H > 0 ? (N * H + 7) / 8 * 8 * ntile : 0);
-    const size_t b_scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
-    const size_t need = work ? b_scal + align_up(4 * static_cast<size_t>(N), 256) : 0;
+    const int64_t main_grid = varlen_main_grid(vp.items, H, d_v);
+    const int64_t comp_grid = vp.comps * H * vp.R * comp_tiles(d_k, d_v, in_dtype == KDN_BF16);
+    if (!grid_fits(main_grid) || !grid_fits(comp_grid)) return KDN_EINVAL;
+    report_echo(opts, work ? main_grid + comp_grid : 0);
+    const VarlenWs w = varlen_workspace(N, H, total_T, d_k, d_v, vp);
+    const size_t need = work ? w.total : 0;
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
     if (wc != KDN_OK) return wc;
@@ -387,14 +447,51 @@ int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d
     p.q = q; p.k = k; p.v = v; p.beta = beta; p.d = d;
     p.A = A; p.I0 = I0; p.mu0 = mu0;
     p.o = o; p.I_T = I_T; p.mu_T = mu_T;
-    p.scal = reinterpret_cast<float4*>(workspace);
-    p.seq_order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + b_scal);
+    char* ws = static_cast<char*>(workspace);
+    p.scal = reinterpret_cast<float4*>(ws);
+    ws += w.scal;
+    p.seq_order = reinterpret_cast<int32_t*>(ws);
+    ws += w.order;
+    p.item_seq = reinterpret_cast<int32_t*>(ws);
+    ws += w.items;
+    p.item_seg = reinterpret_cast<int32_t*>(ws);
+    ws += w.items;
+    p.seq_comp = reinterpret_cast<int32_t*>(ws);
+    ws += w.seqcomp;
+    if (vp.comps > 0) {
+        p.comp_seq = reinterpret_cast<int32_t*>(ws);
+        p.comp_seg = reinterpret_cast<int32_t*>(ws + w.comptab);
+        p.split_seq = reinterpret_cast<int32_t*>(ws + 2 * w.comptab);
+        ws += 3 * w.comptab;
+    }
+    p.nwork = reinterpret_cast<int32_t*>(ws);
+    ws += w.nwork;
+    if (vp.comps > 0) {
+        p.comp = reinterpret_cast<float*>(ws);
+        p.sub = reinterpret_cast<float*>(ws + w.comp);
+        p.gsub = reinterpret_cast<float*>(ws + w.comp + w.sub);
+    }
     p.H = H; p.T = total_T; p.dv = d_v; p.I_prior = I_prior;
     p.S = 1; p.nchunks = 0;
     p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
+    p.vl_seg = vp.seg; p.vl_items = vp.items; p.vl_comps = vp.comps;
     apply_opts(p, opts);
     (void)hipGetLastError();  // launch status below must reflect this call only
-    return diag_varlen_launch(p, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+    return diag_varlen_launch(p, d_k, in_dtype == KDN_BF16, vp.R, static_cast<hipStream_t>(stream));
+}
+
+int kdn_diag_varlen_plan(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                         int32_t segments, int64_t* seg_tokens, int32_t* subsegments,
+                         int64_t* max_items, int64_t* max_composites) {
+    if (N < 0 || H < 0 || total_T < 0 || N >= 2147483647) return KDN_EINVAL;
+    if (segments < 0 || segments > 1) return KDN_EINVAL;
+    if (!head_size_ok(d_k) || !head_size_ok(d_v)) return KDN_EUNSUPPORTED;
+    const VarlenPlan vp = plan_varlen(N, H, total_T, d_v, segments);
+    if (seg_tokens) *seg_tokens = vp.seg;
+    if (subsegments) *subsegments = vp.R;
+    if (max_items) *max_items = vp.items;
+    if (max_composites) *max_composites = vp.comps;
+    return KDN_OK;
 }
 
 int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,

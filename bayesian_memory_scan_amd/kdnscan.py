@@ -23,9 +23,10 @@ import re
 __all__ = [
     "lib", "LIB_PATH", "KDN_OK", "KDN_EINVAL", "KDN_EUNSUPPORTED", "KDN_EWORKSPACE", "KDN_EHIP",
     "KDN_ESCRATCH", "KDN_F32", "KDN_BF16", "KDN_ECHO_WORDS", "KdnError", "ScanOpts",
-    "kdn_diag_scan_fwd", "kdn_diag_scan_fwd_noalloc", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd", "kdn_diag_scan_varlen_fwd",
+    "kdn_diag_scan_fwd", "kdn_diag_scan_fwd_noalloc", "kdn_diag_scan_bwd", "kdn_diag_noise_scan_fwd",
+    "kdn_diag_scan_varlen_fwd", "kdn_diag_scan_varlen_bwd",
     "kdn_mobius_precision_scan", "kdn_decode_step",
-    "kdn_diag_plan", "kdn_status_string", "kdn_last_hip_error",
+    "kdn_diag_plan", "kdn_diag_varlen_plan", "kdn_status_string", "kdn_last_hip_error",
     "header_functions",
 ]
 
@@ -96,10 +97,13 @@ lib.kdn_decode_step.argtypes = [_i64, _i64, _i64, _i64, ctypes.c_int, _vp, _vp, 
                                 _vp, _f, _vp, _vp, _vp, _vp]
 lib.kdn_diag_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, ctypes.POINTER(_i32),
                               ctypes.POINTER(_i32), ctypes.POINTER(_i32), ctypes.POINTER(_i64), _i32]
+lib.kdn_diag_varlen_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, ctypes.POINTER(_i64),
+                                     ctypes.POINTER(_i32), ctypes.POINTER(_i64), ctypes.POINTER(_i64)]
 for _fn in (lib.kdn_diag_scan_fwd, lib.kdn_diag_scan_fwd_ex, lib.kdn_diag_scan_fwd_noalloc, lib.kdn_diag_scan_varlen_fwd,
             lib.kdn_diag_scan_varlen_fwd_ex, lib.kdn_mobius_precision_scan,
             lib.kdn_mobius_precision_scan_ex, lib.kdn_diag_noise_scan_fwd, lib.kdn_diag_scan_bwd,
-            lib.kdn_decode_step, lib.kdn_diag_plan):
+            lib.kdn_diag_scan_varlen_bwd, lib.kdn_decode_step, lib.kdn_diag_plan,
+            lib.kdn_diag_varlen_plan):
     _fn.restype = ctypes.c_int
 lib.kdn_status_string.argtypes = [ctypes.c_int]
 lib.kdn_status_string.restype = ctypes.c_char_p
@@ -141,6 +145,17 @@ def kdn_diag_plan(B: int, H: int, T: int, d_k: int, d_v: int, segments: int = 0)
     if rc != KDN_OK:
         raise KdnError("kdn_diag_plan", rc)
     return chunk.value, segs.value, subs.value, list(bounds)
+
+
+def kdn_diag_varlen_plan(N: int, H: int, total_T: int, d_k: int, d_v: int, segments: int = 0):
+    """(seg_tokens, sub-segments, item capacity, composite capacity) of a
+    packed batch's forward scan; `segments` 0 (automatic) or 1 (no split)."""
+    seg, subs, items, comps = _i64(), _i32(), _i64(), _i64()
+    rc = lib.kdn_diag_varlen_plan(N, H, total_T, d_k, d_v, segments, ctypes.byref(seg),
+                                  ctypes.byref(subs), ctypes.byref(items), ctypes.byref(comps))
+    if rc != KDN_OK:
+        raise KdnError("kdn_diag_varlen_plan", rc)
+    return seg.value, subs.value, items.value, comps.value
 
 
 # ---------------------------------------------------------------------------
@@ -362,13 +377,15 @@ def kdn_diag_scan_fwd_noalloc(q, k, v, beta, d, A, I_prior, I0=None, mu0=None,
 
 
 def kdn_diag_scan_varlen_fwd(q, k, v, beta, d, A, I_prior, cu_seqlens, I0=None, mu0=None,
-                             want_state=True, echo=None, info=None, timing=None, stream=None):
+                             want_state=True, segments=0, echo=None, info=None, timing=None,
+                             stream=None):
     """Diagonal scan over a packed variable-length batch.
 
     q, k [H,total_T,d_k]; v, beta [H,total_T,d_v]; d [H,total_T] (float32 or
     bf16; beta None = Palimpsa-M gating); cu_seqlens int64 [N+1] on the device;
-    I0, mu0 [N,H,d_k,d_v] float32 or None.  Returns (o [H,total_T,d_v], I_T,
-    mu_T [N,H,d_k,d_v]).
+    I0, mu0 [N,H,d_k,d_v] float32 or None.  segments: 0 splits sequences
+    longer than their fair share (kdn_diag_varlen_plan), 1 never splits.
+    Returns (o [H,total_T,d_v], I_T, mu_T [N,H,d_k,d_v]).
     """
     torch = _torch()
     _rank(q, "q", 3)
@@ -393,7 +410,7 @@ def kdn_diag_scan_varlen_fwd(q, k, v, beta, d, A, I_prior, cu_seqlens, I0=None, 
     dev = _on_gpu((("q", q), ("k", k), ("v", v), ("beta", beta), ("d", d), ("A", A),
                    ("cu_seqlens", cu_seqlens), ("I0", I0), ("mu0", mu0), ("echo", echo)))
     s = _stream(stream)
-    opts = _opts(0, echo, timing, s)
+    opts = _opts(segments, echo, timing, s)
     with torch.cuda.stream(s):
         o = torch.empty((H, T, dv), dtype=torch.float32, device=dev)
         I_T = mu_T = None

@@ -115,6 +115,7 @@ class VarlenSpec:
     seed: int
     m_gating: bool = False
     I_prior: float = 1.0
+    long_tokens: int = 0  # > 0: sequence 0 holds this many tokens, the rest cut at random
 
     def with_(self, **kw) -> "VarlenSpec":
         return replace(self, **kw)
@@ -133,6 +134,9 @@ WORKLOADS = {
         VarlenSpec("varlen_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1007),
         # gradient over the same packed batch
         VarlenSpec("varlenbwd_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1007),
+        # a skewed packed batch: one 8192-token sequence, 63 short ones in the other half
+        VarlenSpec("varlenskew_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1008,
+                   long_tokens=8192),
         # gradient of the headline forward workload (same inputs)
         DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
@@ -241,8 +245,14 @@ def varlen_inputs(spec: VarlenSpec) -> dict:
     if spec.m_gating:
         out["beta"] = None
     g = _rng(spec.seed, 0x1E)
-    cuts = np.sort(g.choice(np.arange(1, spec.total_T), size=spec.N - 1, replace=False)) \
-        if spec.N > 1 else np.zeros(0, np.int64)
+    if spec.long_tokens > 0:
+        L = spec.long_tokens
+        cuts = np.sort(g.choice(np.arange(L + 1, spec.total_T), size=spec.N - 2, replace=False))
+        cuts = np.concatenate([[L], cuts])
+    elif spec.N > 1:
+        cuts = np.sort(g.choice(np.arange(1, spec.total_T), size=spec.N - 1, replace=False))
+    else:
+        cuts = np.zeros(0, np.int64)
     out["cu_seqlens"] = np.concatenate([[0], cuts, [spec.total_T]]).astype(np.int64)
     return out
 

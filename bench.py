@@ -14,7 +14,8 @@ error of the GPU output on that sample against the oracle.
 
 Other workloads (--workload) print the same fields for the short-sequence
 batch (B=8, H=16, T=2048), Palimpsa-M gating, the packed variable-length
-batch and its gradient, the backward pass, the process-noise variant, the decode step and the
+batch (also a skewed one whose long sequence runs in segments) and its gradient, the backward
+pass, the process-noise variant, the decode step and the
 isotropic scan; they are not the headline line.
 """
 from __future__ import annotations
@@ -57,6 +58,8 @@ def _args():
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle leg")
+    ap.add_argument("--segments", type=int, default=0,
+                    help="packed batches: 0 splits sequences longer than a fair share, 1 never")
     return ap.parse_args()
 
 
@@ -391,15 +394,17 @@ def main():
         if not a.no_cpu:
             out["cpu_baseline"], ref = cpu_baseline_diag(inp, spec, a.cpu_seconds)
             out["parity"] = parity_report(o.cpu().numpy(), ref)
-    elif a.workload.startswith("varlen_"):
+    elif a.workload.startswith(("varlen_", "varlenskew_")):
         inp = synth.varlen_inputs(spec)
         x = {n: _up(inp[n][0], torch, dev) for n in ("q", "k", "v", "beta", "d")}
         A = _up(inp["A"], torch, dev)
         cu = torch.from_numpy(inp["cu_seqlens"]).to(dev)
+        seg_tokens = kdn.kdn_diag_varlen_plan(spec.N, spec.H, spec.total_T, spec.d_k, spec.d_v,
+                                              a.segments)[0]
 
         def step(m):
             kdn.kdn_diag_scan_varlen_fwd(x["q"], x["k"], x["v"], x["beta"], x["d"], A,
-                                         spec.I_prior, cu, timing=m)
+                                         spec.I_prior, cu, segments=a.segments, timing=m)
 
         tm = _time_steps(torch, step, a.steps, a.warmup, main_events=True)
         wall, ev_ms = tm.wall, tm.kernel()["avg"]
@@ -413,7 +418,7 @@ def main():
             "config": {"workload": spec.name, "sequences": spec.N, "H": spec.H,
                        "packed_T": spec.total_T, "d_k": spec.d_k, "d_v": spec.d_v,
                        "inputs": spec.dtype, "length_min": min(lens), "length_max": max(lens),
-                       "parallelism": "single GPU"},
+                       "segment_tokens": seg_tokens, "parallelism": "single GPU"},
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_scan.hip", f"traffic_{spec.name}.json"),

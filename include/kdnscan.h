@@ -111,13 +111,19 @@ int kdn_diag_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
  *     beta may be NULL); A [H] float; I_prior > 0.
  *   I0, mu0 [N,H,d_k,d_v] float or NULL: each sequence's starting state.
  *   Outputs: o [H,total_T,d_v]; I_T, mu_T [N,H,d_k,d_v] or NULL.
- *   Workspace: 16 bytes per (head, packed token) of frame scalars, plus the
- *   plan (4 bytes per sequence).
- * Work plan: one workgroup per (sequence, head, column tile: 64 columns, or
- * 32 / d_v columns when d_v < 64), chunks of 16
- * tokens aligned to each sequence start, dispatched longest sequence first
- * (the order is computed on the device from cu_seqlens; up to 16384
- * sequences, beyond that in index order).
+ *   Workspace: 16 bytes per (head, packed token) of frame scalars, the plan
+ *   (a few int32 per sequence and per segment), and for split sequences the
+ *   carried states and sub-segment composites (kdn_diag_varlen_plan).
+ * Work plan: chunks of 16 tokens aligned to each sequence start.  A
+ * sequence longer than its fair share of the chip (kdn_diag_varlen_plan) is
+ * cut into segments of seg_tokens tokens [KLA Metodologia 2: associative
+ * composition]: the segments' composites are built on the matrix cores and
+ * carried in order, so every segment runs from its true starting state.
+ * The main pass runs one workgroup per (segment, head, column tile: 64
+ * columns, or 32 / d_v columns when d_v < 64), sequences longest first (the
+ * order and the tables are computed on the device from cu_seqlens; up to
+ * 16384 sequences, beyond that in index order), a sequence's segments in
+ * token order.  Results agree with the unsplit scan up to rounding.
  */
 int kdn_diag_scan_varlen_fwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
                              kdn_dtype in_dtype, const int64_t* cu_seqlens,
@@ -292,7 +298,9 @@ int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, int
  *     sequence, 0}, kind 1 = main pass (run = b*H + h, part = column tile),
  *     2 = diagonal segment composite (part = sub-segment), 3 = isotropic mean
  *     scan (part = column tile), 4 = isotropic segment composite; for a
- *     packed batch run = s*H + h of sequence s = `sequence`.  Record r of
+ *     packed batch run = s*H + h of sequence s = `sequence`.  Kind 2 records
+ *     hold the wave's tile in the `sequence` word and, for a packed batch,
+ *     the sequence in the last word (0 otherwise).  Record r of
  *     kind k sits at a fixed slot; records that would pass echo_capacity are
  *     dropped; slots of work units with nothing to do stay untouched (clear
  *     the buffer first).  For testing the integer bookkeeping.
@@ -316,6 +324,29 @@ typedef struct kdn_scan_opts {
     void* main_end;
 } kdn_scan_opts;
 
+/*
+ * Plan of a packed batch's forward scan (kdn_diag_scan_varlen_fwd[_ex]),
+ * computed on the host from the sizes alone.  segments: 0 (automatic) or 1
+ * (no split).  seg_tokens: the segment length (a multiple of 256) of a
+ * split sequence, or 0 when no sequence can be split; a sequence of len >
+ * seg_tokens tokens runs as ceil(len / seg_tokens) segments, segment g
+ * holding its tokens [g seg_tokens, min((g + 1) seg_tokens, len)).  It is
+ * the fair share ceil(H total_T tiles / 256) tokens (tiles = d_v / 64, or 1
+ * when d_v < 64) rounded up to a multiple of 256, at least 512.
+ * max_items, max_composites: capacities of the plan's tables (N plus
+ * total_T / seg_tokens, and total_T / seg_tokens).  subsegments: R, the
+ * composite storage holds max_composites x H x R sub-segment composites.
+ * The composite of each segment but a sequence's last is built in
+ * R' = min(seg_tokens / 64, floor(max_composites R / C)) sub-segments, C the
+ * number of such segments in the batch (known on the device only),
+ * sub-segment r holding the segment's 16-token chunks
+ * [floor(r m / R'), floor((r + 1) m / R')), m = seg_tokens / 16.  Any output
+ * may be NULL.
+ */
+int kdn_diag_varlen_plan(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
+                         int32_t segments, int64_t* seg_tokens, int32_t* subsegments,
+                         int64_t* max_items, int64_t* max_composites);
+
 /* kdn_diag_scan_fwd with options (opts may be NULL). */
 int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                          kdn_dtype in_dtype,
@@ -327,7 +358,8 @@ int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d
                          void* workspace, size_t* workspace_bytes, void* stream);
 
 /* kdn_diag_scan_varlen_fwd with options (opts may be NULL; segments must be
- * 0 or 1: a packed batch runs each sequence in one segment). */
+ * 0, the automatic plan of kdn_diag_varlen_plan, or 1: every sequence in one
+ * segment, however long). */
 int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
                                 kdn_dtype in_dtype, const int64_t* cu_seqlens,
                                 const void* q, const void* k, const void* v,

@@ -377,6 +377,42 @@ def plan_sub(T: int, chunk: int, segments: int, subsegments: int):
     return out
 
 
+def varlen_plan(cu_seqlens, seg_tokens: int, subsegments: int, chunk: int = 16):
+    """Plan of a packed batch's forward scan, enumerated from its definition.
+
+    Sequences are ranked longest first, ties by index.  A sequence of len >
+    seg_tokens tokens (seg_tokens > 0) runs as ceil(len / seg_tokens)
+    segments, segment g owning its tokens [g*seg, min((g+1)*seg, len)); any
+    other sequence is one segment.  The main-pass items are the sequences'
+    segments in rank order, each sequence's in token order.  The composite
+    segments are the split sequences' segments but their last, in the same
+    order; sub-segment r of one owns the segment's chunks
+    [floor(r m / R), floor((r+1) m / R)), m = seg_tokens / chunk.
+    Returns (items, composites) with packed token offsets: items
+    [(s, g, t_begin, t_end)], composites [(s, g, [(t_begin, t_end) per r])].
+    """
+    cu = [int(x) for x in cu_seqlens]
+    N = len(cu) - 1
+    lens = [cu[s + 1] - cu[s] for s in range(N)]
+    order = sorted(range(N), key=lambda s: (-lens[s], s))
+    items, comps = [], []
+    for s in order:
+        L = lens[s]
+        nseg = -(-L // seg_tokens) if seg_tokens > 0 and L > seg_tokens else 1
+        for g in range(nseg):
+            if nseg == 1:
+                items.append((s, 0, cu[s], cu[s + 1]))
+            else:
+                items.append((s, g, cu[s] + g * seg_tokens, cu[s] + min((g + 1) * seg_tokens, L)))
+        m = seg_tokens // chunk if seg_tokens > 0 else 0
+        for g in range(nseg - 1):
+            base = cu[s] + g * seg_tokens
+            subs = [(base + (r * m // subsegments) * chunk, base + ((r + 1) * m // subsegments) * chunk)
+                    for r in range(subsegments)]
+            comps.append((s, g, subs))
+    return items, comps
+
+
 def element_offset(b: int, h: int, t: int, x: int, H: int, T: int, D: int) -> int:
     """Element index of [b, h, t, x] in a contiguous [B, H, T, D] tensor (Python int)."""
     return ((b * H + h) * T + t) * D + x

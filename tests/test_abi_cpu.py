@@ -236,7 +236,11 @@ def test_varlen_validation_and_workspace():
                                      FAKE, 1.0, I0, None, FAKE, None, None, ws,
                                      None if nb is None else ctypes.byref(nb), None)
     assert call() == kdn.KDN_OK
-    assert n.value == 16 * 2 * 40 + 256        # frame scalars + the longest-first plan
+    # frame scalars, then the plan's tables (order, item sequence and segment,
+    # first composite of each sequence, counts), 256 bytes each at this size;
+    # 40 tokens cannot be split, so no composite tables or states
+    assert kdn.kdn_diag_varlen_plan(3, 2, 40, 64, 64) == (0, 1, 3, 0)
+    assert n.value == 16 * 2 * 40 + 5 * 256
     assert call(N=-1) == kdn.KDN_EINVAL
     assert call(cu=None) == kdn.KDN_EINVAL
     assert call(cu=FAKE + 4) == kdn.KDN_EINVAL  # int64 offsets must be 8-byte aligned
@@ -246,6 +250,39 @@ def test_varlen_validation_and_workspace():
     assert call(I0=MIS) == kdn.KDN_EINVAL
     assert call(N=0, cu=None) == kdn.KDN_OK and n.value == 0
     assert call(nb=None, ws=None) == kdn.KDN_EWORKSPACE
+
+
+def test_varlen_split_plan():
+    """The packed batch's split plan from the sizes: the fair share of the
+    chip, H total_T tiles / 256 tokens, rounded up to 256, at least 512."""
+    # 16 heads x 16384 tokens x 2 tiles: 2048 tokens a share, 8 composites at most
+    seg, R, items, comps = kdn.kdn_diag_varlen_plan(64, 16, 16384, 128, 128)
+    assert (seg, items, comps) == (2048, 72, 8)
+    assert 1 <= R <= 2048 // 64 and R == min(8 * 256 // (8 * 16 * 4), 2048 // 64)
+    # small batches: the 512-token floor
+    assert kdn.kdn_diag_varlen_plan(4, 2, 3000, 64, 64)[:1] == (512,)
+    assert kdn.kdn_diag_varlen_plan(4, 2, 3000, 64, 64)[2:] == (4 + 5, 5)
+    # d_v < 64: one tile per head
+    assert kdn.kdn_diag_varlen_plan(4, 64, 4096, 64, 32)[0] == 1024
+    # no split requested, or nothing long enough to split
+    assert kdn.kdn_diag_varlen_plan(64, 16, 16384, 128, 128, segments=1) == (0, 1, 64, 0)
+    assert kdn.kdn_diag_varlen_plan(4, 2, 512, 64, 64) == (0, 1, 4, 0)
+    seg = ctypes.c_int64(0)
+    assert lib.kdn_diag_varlen_plan(4, 2, 512, 64, 64, 2, ctypes.byref(seg), None, None, None) \
+        == kdn.KDN_EINVAL
+    assert lib.kdn_diag_varlen_plan(4, 2, 512, 24, 64, 0, None, None, None, None) \
+        == kdn.KDN_EUNSUPPORTED
+    # the workspace grows by the composite tables and states when a split is possible
+    n1, n2 = ctypes.c_size_t(0), ctypes.c_size_t(0)
+    opts = kdn.ScanOpts()
+    for segs, n in ((0, n1), (1, n2)):
+        opts.segments = segs
+        assert lib.kdn_diag_scan_varlen_fwd_ex(4, 2, 3000, 64, 64, kdn.KDN_F32, FAKE, FAKE, FAKE, FAKE,
+                                               FAKE, FAKE, FAKE, 1.0, None, None, FAKE, None, None,
+                                               ctypes.byref(opts), None, ctypes.byref(n), None) \
+            == kdn.KDN_OK
+    R = kdn.kdn_diag_varlen_plan(4, 2, 3000, 64, 64)[1]
+    assert n1.value - n2.value >= 4 * 5 * 2 * (2 + 2 * R) * 64 * 64
 
 
 def test_varlen_bwd_validation_and_workspace():
