@@ -22,7 +22,7 @@ BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["kdnscan_api.hip", "diag_scan.hip", "decode.hip", "mobius_scan.hip", "iso_scan.hip", "diag_comp.hip",
-           "diag_bwd.hip", "diag_noise.hip"]
+           "diag_bwd.hip", "diag_bwd_seg.hip", "diag_noise.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

@@ -334,6 +334,14 @@ struct BwdParams {
     int32_t nseq;
     int64_t nruns;               // state slots: B*H, or nseq*H
     int64_t ck_stride;           // checkpoint slots per (head, column tile) of a packed batch
+    // Fixed-length rows cut into S segments of whole chunks (S == 1: none;
+    // always 1 for a packed batch).  Slots of 2 dk*CI floats in the
+    // checkpoint layout, per (row, column tile, segment):
+    int32_t S;
+    const float* comp;           // [BH][S][2][dk][dv]: each segment's starting (I - I_prior, eta)
+    float* adj;                  // [BH*ntile][S][slot]: segment s's adjoint composite (s >= 1)
+    float* lam;                  // [BH*ntile][S][slot]: the adjoint flowing into segment s's end
+    float* adjg;                 // [BH][S]: product of alpha over segment s
 };
 
 int diag_chunk();
@@ -341,7 +349,8 @@ int varlen_cols(int64_t dv);
 int diag_varlen_comp_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st);
 int32_t bwd_token_split(int64_t rows, int64_t T);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
-                    bool bf16, hipStream_t st);
+                    bool bf16, int32_t R, hipStream_t st);
+int diag_bwd_seg_launch(const BwdParams& p, int64_t dk, bool bf16, hipStream_t st);
 int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t dk, bool bf16,
                            hipStream_t st);
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, bool true_i, hipStream_t st);

@@ -532,7 +532,24 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       float* dq, float* dk, float* dv, float* dbeta, float* dd,
                       float* dA, float* dI_prior, float* dI0, float* dmu0,
                       void* workspace, size_t* workspace_bytes, void* stream) {
-    if (B < 0 || H < 0 || T < 0) return KDN_EINVAL;
+    return kdn_diag_scan_bwd_ex(B, H, T, d_k, d_v, in_dtype, q, k, v, beta, d, A, I_prior, I0, mu0, d_o,
+                                d_I_T, d_mu_T, dq, dk, dv, dbeta, dd, dA, dI_prior, dI0, dmu0, nullptr,
+                                workspace, workspace_bytes, stream);
+}
+
+int kdn_diag_scan_bwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                         kdn_dtype in_dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* beta, const void* d,
+                         const float* A, float I_prior,
+                         const float* I0, const float* mu0,
+                         const float* d_o, const float* d_I_T, const float* d_mu_T,
+                         float* dq, float* dk, float* dv, float* dbeta, float* dd,
+                         float* dA, float* dI_prior, float* dI0, float* dmu0, kdn_scan_opts* opts,
+                         void* workspace, size_t* workspace_bytes, void* stream) {
+    if (B < 0 || H < 0 || T < 0 || !opts_ok(opts)) return KDN_EINVAL;
+    // the gradient takes the segment request only
+    if (opts && (opts->bounds_echo || opts->main_begin || opts->main_end)) return KDN_EINVAL;
     if (in_dtype != KDN_F32 && in_dtype != KDN_BF16) return KDN_EINVAL;
     if (!head_size_ok(d_k) || !head_size_ok(d_v) || d_k < 64) return KDN_EUNSUPPORTED;
     if (!finite_positive(I_prior)) return KDN_EINVAL;
@@ -554,7 +571,13 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const int64_t ci = d_v < 64 ? d_v : 64;
     const int64_t ntile = d_v / ci;
     const int64_t nch = (T + diag_chunk() - 1) / diag_chunk();
-    if (!grid_fits(BH * ntile)) return KDN_EINVAL;
+    // Rows too few to fill the chip are cut into segments, planned as the
+    // forward scan plans them (same segment bounds, so the forward composites
+    // give each segment's starting state).
+    const Plan pl = plan_scan(BH, T, d_v, opt_segments(opts));
+    const int64_t S = pl.S;
+    if (!grid_fits(BH * S * ntile)) return KDN_EINVAL;
+    report_echo(opts, 0);
     const size_t f = sizeof(float);
     const size_t b_scal = align_up(16 * static_cast<size_t>(BH) * T, 256);
     const size_t b_ckpt = align_up(f * static_cast<size_t>(BH) * (nch + 1) * 2 * d_k * d_v, 256);
@@ -564,7 +587,14 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
     const int32_t split = bwd_token_split(BH, T);
     const size_t b_head = align_up(f * 2 * static_cast<size_t>(BH) * split, 256);
     const size_t b_db = beta ? 0 : b_tok;
-    const size_t need = b_scal + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db;
+    // segments: forward composites (carry-ins, sub-segment composites), the
+    // adjoint composites and carried adjoints, and the segments' decays
+    const DiagWs dw = diag_workspace(BH, T, d_k, d_v, pl);
+    const size_t b_seg = S > 1 ? align_up(f * static_cast<size_t>(BH) * S * 2 * d_k * d_v, 256) : 0;
+    const size_t b_adjg = S > 1 ? align_up(f * static_cast<size_t>(BH) * S, 256) : 0;
+    const size_t b_fwd = S > 1 ? dw.comp + dw.sub + dw.gsub : 0;
+    const size_t need = b_scal + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db + b_fwd +
+                        2 * b_seg + b_adjg;
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
     if (wc != KDN_OK) return wc;
@@ -600,17 +630,31 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
         p.part_head = reinterpret_cast<float*>(ws);
         ws += b_head;
         if (!beta) p.part_db = reinterpret_cast<float*>(ws);
+        ws += b_db;
     }
     p.BH = BH; p.H = H; p.T = T; p.dv = d_v; p.I_prior = I_prior;
     p.nchunks = static_cast<int32_t>(nch); p.ntile = static_cast<int32_t>(ntile);
     p.nruns = BH; p.tok_split = split;
+    p.S = static_cast<int32_t>(S);
 
     DiagParams prep{};
-    prep.d = d; prep.A = A; prep.scal = scal;
+    prep.k = k; prep.v = v; prep.beta = beta; prep.d = d; prep.A = A; prep.scal = scal;
+    prep.I0 = I0; prep.mu0 = mu0;
     prep.H = H; prep.T = T; prep.dv = d_v; prep.I_prior = I_prior;
     prep.S = 1; prep.nchunks = static_cast<int32_t>(nch);
+    if (BH > 0 && S > 1) {
+        prep.S = static_cast<int32_t>(S);
+        prep.comp = reinterpret_cast<float*>(ws);
+        prep.sub = reinterpret_cast<float*>(ws + dw.comp);
+        prep.gsub = reinterpret_cast<float*>(ws + dw.comp + dw.sub);
+        ws += b_fwd;
+        p.comp = prep.comp;
+        p.adj = reinterpret_cast<float*>(ws);
+        p.lam = reinterpret_cast<float*>(ws + b_seg);
+        p.adjg = reinterpret_cast<float*>(ws + 2 * b_seg);
+    }
     (void)hipGetLastError();  // launch status below must reflect this call only
-    return diag_bwd_launch(p, prep, B, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+    return diag_bwd_launch(p, prep, B, d_k, in_dtype == KDN_BF16, pl.R, static_cast<hipStream_t>(stream));
 }
 
 int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
@@ -680,7 +724,7 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     p.BH = H; p.H = H; p.T = work ? total_T : 0; p.dv = d_v; p.I_prior = I_prior;
     p.nchunks = 0; p.ntile = static_cast<int32_t>(ntile);
     p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
-    p.nruns = N * H; p.ck_stride = ck_stride; p.tok_split = split;
+    p.nruns = N * H; p.ck_stride = ck_stride; p.tok_split = split; p.S = 1;
     DiagParams prep{};
     if (work) {
         float4* scal = reinterpret_cast<float4*>(ws);

@@ -89,6 +89,7 @@ lib.kdn_diag_scan_bwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                   _vp, _vp, _vp,
                                   _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp] + _WS
+lib.kdn_diag_scan_bwd_ex.argtypes = lib.kdn_diag_scan_bwd.argtypes[:-3] + [_optp] + _WS
 lib.kdn_diag_scan_varlen_bwd.argtypes = [_i64, _i64, _i64, _i64, _i64, ctypes.c_int, _vp,
                                          _vp, _vp, _vp, _vp, _vp, _vp, _f, _vp, _vp,
                                          _vp, _vp, _vp,
@@ -102,7 +103,7 @@ lib.kdn_diag_varlen_plan.argtypes = [_i64, _i64, _i64, _i64, _i64, _i32, ctypes.
 for _fn in (lib.kdn_diag_scan_fwd, lib.kdn_diag_scan_fwd_ex, lib.kdn_diag_scan_fwd_noalloc, lib.kdn_diag_scan_varlen_fwd,
             lib.kdn_diag_scan_varlen_fwd_ex, lib.kdn_mobius_precision_scan,
             lib.kdn_mobius_precision_scan_ex, lib.kdn_diag_noise_scan_fwd, lib.kdn_diag_scan_bwd,
-            lib.kdn_diag_scan_varlen_bwd, lib.kdn_decode_step, lib.kdn_diag_plan,
+            lib.kdn_diag_scan_bwd_ex, lib.kdn_diag_scan_varlen_bwd, lib.kdn_decode_step, lib.kdn_diag_plan,
             lib.kdn_diag_varlen_plan):
     _fn.restype = ctypes.c_int
 lib.kdn_status_string.argtypes = [ctypes.c_int]
@@ -476,14 +477,14 @@ def kdn_diag_noise_scan_fwd(q, k, v, beta, a, p, lambda0=None, mu0=None, want_st
 
 
 def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_T=None,
-                      d_mu_T=None, want_prior=True, stream=None):
+                      d_mu_T=None, want_prior=True, segments=0, stream=None):
     """Gradient of kdn_diag_scan_fwd for L = sum(d_o o) + sum(d_I_T I_T) + sum(d_mu_T mu_T).
 
     Inputs as for the forward call plus d_o [B,H,T,d_v] and optional d_I_T,
-    d_mu_T [B,H,d_k,d_v] (all float32).  Returns a dict of float32 tensors:
-    dq, dk [B,H,T,d_k]; dv, dbeta [B,H,T,d_v]; dd [B,H,T]; dA [H];
-    dI_prior [1] (when want_prior); dI0 / dmu0 [B,H,d_k,d_v] when I0 / mu0
-    are given.
+    d_mu_T [B,H,d_k,d_v] (all float32).  segments: 0 = automatic plan, n =
+    n segments per row.  Returns a dict of float32 tensors: dq, dk
+    [B,H,T,d_k]; dv, dbeta [B,H,T,d_v]; dd [B,H,T]; dA [H]; dI_prior [1]
+    (when want_prior); dI0 / dmu0 [B,H,d_k,d_v] when I0 / mu0 are given.
     """
     torch = _torch()
     _rank(q, "q", 4)
@@ -520,14 +521,18 @@ def kdn_diag_scan_bwd(q, k, v, beta, d, A, I_prior, d_o, I0=None, mu0=None, d_I_
             g["dmu0"] = new(B, H, dk, dv)
         o = lambda n: _ptr(g.get(n))
 
+        opts = ScanOpts()
+        opts.segments = segments
+
         def args(ws, nbytes):
             return (B, H, T, dk, dv, _in_dtype(q), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(d),
                     _ptr(A), float(I_prior), _ptr(I0), _ptr(mu0), _ptr(d_o), _ptr(d_I_T),
                     _ptr(d_mu_T), o("dq"), o("dk"), o("dv"), o("dbeta"), o("dd"), o("dA"),
-                    o("dI_prior"), o("dI0"), o("dmu0"), ws, nbytes, s.cuda_stream)
+                    o("dI_prior"), o("dI0"), o("dmu0"), ctypes.byref(opts), ws, nbytes,
+                    s.cuda_stream)
 
-        ws, need = _workspace(lib.kdn_diag_scan_bwd, "kdn_diag_scan_bwd", args, dev)
-        rc = lib.kdn_diag_scan_bwd(*args(_ptr(ws), _nbytes(ws, need)))
+        ws, need = _workspace(lib.kdn_diag_scan_bwd_ex, "kdn_diag_scan_bwd", args, dev)
+        rc = lib.kdn_diag_scan_bwd_ex(*args(_ptr(ws), _nbytes(ws, need)))
     if rc != KDN_OK:
         raise KdnError("kdn_diag_scan_bwd", rc)
     return g

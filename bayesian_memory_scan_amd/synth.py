@@ -139,6 +139,8 @@ WORKLOADS = {
                    long_tokens=8192),
         # gradient of the headline forward workload (same inputs)
         DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
+        # gradient of the long-sequence workload (same inputs)
+        DiagSpec("bwd_b2h16t16384d128_bf16", 2, 16, 16384, 128, 128, "bf16", 1002),
         IsoSpec("iso_b1h32t65536d64_f32", 1, 32, 65536, 64, 64, 1003),
         # one decode token after a 512-token prefix that builds the state
         DiagSpec("decode_b256h16d128_bf16", 256, 16, 1, 128, 128, "bf16", 1004, prefix=512),

@@ -471,7 +471,9 @@ def main():
             "ms_per_step": wall / a.steps * 1e3,
             "config": {"workload": spec.name, "B": spec.B, "H": spec.H, "T": spec.T,
                        "d_k": spec.d_k, "d_v": spec.d_v, "inputs": spec.dtype,
-                       "gradients": "fp32, loss on o only", "parallelism": "single GPU"},
+                       "gradients": "fp32, loss on o only",
+                       "segments": kdn.kdn_diag_plan(spec.B, spec.H, spec.T, spec.d_k, spec.d_v)[1],
+                       "parallelism": "single GPU"},
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
                          "traffic": _traffic("diag_bwd.hip", f"traffic_{spec.name}.json"),

@@ -180,6 +180,11 @@ int kdn_diag_noise_scan_fwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_
  *   call writes into its workspace (8 bytes per state entry per 16 tokens,
  *   plus per-token partial sums); query its size as for the forward call.
  *   Outputs must not alias inputs.  Deterministic: no atomics.
+ * Rows too few to fill the chip are cut into the forward plan's segments
+ * (kdn_diag_plan) [KLA Metodologia 2]: the forward composites give every
+ * segment its starting state; the adjoint recurrence, linear as well, is
+ * composed per segment while the checkpoints are written and carried from
+ * the row's end, so every segment's reverse pass runs at once.
  */
 int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
                       kdn_dtype in_dtype,
@@ -346,6 +351,20 @@ typedef struct kdn_scan_opts {
 int kdn_diag_varlen_plan(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
                          int32_t segments, int64_t* seg_tokens, int32_t* subsegments,
                          int64_t* max_items, int64_t* max_composites);
+
+/* kdn_diag_scan_bwd with options (opts may be NULL): only `segments` applies
+ * (0: the automatic plan, n >= 1: n segments per row, clamped as in
+ * kdn_diag_plan); bounds_echo, main_begin and main_end must be NULL. */
+int kdn_diag_scan_bwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
+                         kdn_dtype in_dtype,
+                         const void* q, const void* k, const void* v,
+                         const void* beta, const void* d,
+                         const float* A, float I_prior,
+                         const float* I0, const float* mu0,
+                         const float* d_o, const float* d_I_T, const float* d_mu_T,
+                         float* dq, float* dk, float* dv, float* dbeta, float* dd,
+                         float* dA, float* dI_prior, float* dI0, float* dmu0, kdn_scan_opts* opts,
+                         void* workspace, size_t* workspace_bytes, void* stream);
 
 /* kdn_diag_scan_fwd with options (opts may be NULL). */
 int kdn_diag_scan_fwd_ex(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
