@@ -1,4 +1,4 @@
-"""Recompute schedules of the reverse pass (diag_bwd.hip), printed as C++ tables.
+"""Recompute schedules of the reverse pass (diag_bwd_kernels.h), printed as C++ tables.
 
 The reverse pass walks a chunk's tokens last to first and needs, for token t,
 the state after t.  Only the state before the chunk is stored (a

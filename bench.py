@@ -476,7 +476,7 @@ def main():
                        "parallelism": "single GPU"},
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
-                         "traffic": _traffic("diag_bwd.hip", f"traffic_{spec.name}.json"),
+                         "traffic": _traffic("diag_bwd_kernels.h", f"traffic_{spec.name}.json"),
                          **tm.fields(),
                          "note": "events bracket the whole call: frame scalars, checkpoints, "
                                  "reverse pass and finishing sums; traffic is the reverse pass"},
@@ -511,7 +511,7 @@ def main():
                        "gradients": "fp32, loss on o only", "parallelism": "single GPU"},
             "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_VALU_TFLOPS,
                          "unit": "TFLOP/s", "frac": achieved / PEAK_FP32_VALU_TFLOPS,
-                         "traffic": _traffic("diag_bwd.hip", f"traffic_{spec.name}.json"),
+                         "traffic": _traffic("diag_bwd_kernels.h", f"traffic_{spec.name}.json"),
                          **tm.fields(),
                          "note": "events bracket the whole call: sequence plan, frame scalars, "
                                  "checkpoints, reverse pass and finishing sums"},

@@ -1,4 +1,4 @@
-"""The reverse pass's recompute schedules (diag_bwd.hip): the tables compiled
+"""The reverse pass's recompute schedules (diag_bwd_kernels.h): the tables compiled
 into the kernel are the ones the generator prints, and simulating them on
 symbolic states shows every reverse step gets the state after its token, in
 order, with no more register slots than the kernel holds."""
@@ -21,7 +21,7 @@ def _generator():
 
 
 def _tables():
-    src = open(os.path.join(CSRC, "diag_bwd.hip")).read()
+    src = open(os.path.join(CSRC, "diag_bwd_kernels.h")).read()
     out = {}
     for m in re.finditer(r"struct RecSchedule<(\d+)> \{\s*static constexpr int N = (\d+);\s*"
                          r"static constexpr RecOp ops\[N\] = \{(.*?)\};\s*\};", src, re.S):
