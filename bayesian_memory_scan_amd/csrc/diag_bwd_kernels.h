@@ -451,15 +451,17 @@ __device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
         return r;
     }
     if (SEG) {
+        // the divisions leave their results in VGPRs; the run's fields are
+        // wave-uniform and go back to SGPRs for the kernel's lifetime
         const int64_t wg = xcd_local_id();
         r.tile = static_cast<int>(wg % NTILE);
         const int64_t rs = wg / NTILE;
-        r.seg = static_cast<int>(rs % p.S);
-        const int64_t bh = rs / p.S;
+        r.seg = static_cast<int>(uniform64(rs % p.S));
+        const int64_t bh = uniform64(rs / p.S);
         r.state = bh;
         r.tbase = bh * p.T;
         const int64_t n = p.nchunks;
-        const int64_t c0 = r.seg * n / p.S, c1 = (r.seg + 1) * n / p.S;
+        const int64_t c0 = uniform64(r.seg * n / p.S), c1 = uniform64((r.seg + 1) * n / p.S);
         r.t_begin = c0 * kBwdChunk;
         r.t_end = c1 * kBwdChunk < p.T ? c1 * kBwdChunk : p.T;
         r.nch = c1 - c0;
@@ -478,8 +480,8 @@ __device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
     const int64_t wg = blk / (8 * NTILE) * 8 + within % 8;
     r.valid = wg < static_cast<int64_t>(p.nseq) * p.H;
     if (!r.valid) return r;
-    const int64_t h = wg % p.H;
-    const int32_t sq = p.seq_order[wg / p.H];
+    const int64_t h = uniform64(wg % p.H);
+    const int32_t sq = p.seq_order[uniform64(wg / p.H)];
     r.state = static_cast<int64_t>(sq) * p.H + h;
     r.rt = r.state * NTILE + r.tile;
     r.tbase = h * p.T;
@@ -488,7 +490,7 @@ __device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
     b = b < a ? a : (b > p.T ? p.T : b);
     r.t_begin = a;
     r.t_end = b;
-    r.nch = (b - a + kBwdChunk - 1) / kBwdChunk;
+    r.nch = uniform64((b - a + kBwdChunk - 1) / kBwdChunk);
     r.ck0 = p.ckpt + ((h * NTILE + r.tile) * p.ck_stride + p.seq_ckoff[sq]) * 2 * BLK;
     r.ckfin = r.ck0 + r.nch * 2 * BLK;
     return r;

@@ -84,6 +84,15 @@ __device__ __forceinline__ float uniform(float x) {
     return __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(x)));
 }
 
+// A wave-uniform 64-bit integer moved to scalar registers (integer division
+// leaves its results in VGPRs).
+__device__ __forceinline__ int64_t uniform64(int64_t x) {
+    const uint64_t u = static_cast<uint64_t>(x);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // DPP lane permutations inside a row of 16 lanes, each an involution:
 // row_mirror pairs l with 15-l, row_half_mirror l with 7-l (within 8),
 // quad_perm [3,2,1,0] l with 3-l (within 4), quad_perm [1,0,3,2] l with l^1.
