@@ -116,8 +116,10 @@ __global__ __launch_bounds__(256) void k_diag_bwd_heads(BwdParams p) {
     if (tid == 0) p.dI_prior[0] = red[0];
 }
 
+// reverse == false: the checkpoint pass only (a packed batch whose split
+// sequences run through diag_bwd_seg_launch)
 template <int DK, int DV, bool BF16>
-static int launch_bwd_shape(const BwdParams& p, hipStream_t st) {
+static int launch_bwd_shape(const BwdParams& p, hipStream_t st, bool reverse = true) {
     using Sh = BwdShape<DK, DV>;
     // a packed batch: whole groups of 8 runs (see bwd_run)
     const int64_t g = p.cu_seqlens ? (static_cast<int64_t>(p.nseq) * p.H + 7) / 8 * 8 * Sh::NTILE
@@ -125,17 +127,17 @@ static int launch_bwd_shape(const BwdParams& p, hipStream_t st) {
     if (g == 0) return KDN_OK;
     const dim3 grid(static_cast<uint32_t>(g));
     if (p.T > 0) hipLaunchKernelGGL((k_diag_bwd_ckpt<DK, DV, BF16, false>), grid, dim3(Sh::NTH), 0, st, p);
-    hipLaunchKernelGGL((k_diag_bwd<DK, DV, BF16, false>), grid, dim3(Sh::NTH), 0, st, p);
+    if (reverse) hipLaunchKernelGGL((k_diag_bwd<DK, DV, BF16, false>), grid, dim3(Sh::NTH), 0, st, p);
     return launch_status();
 }
 
 template <int DK, bool BF16>
-static int launch_bwd_dv(const BwdParams& p, int64_t dv, hipStream_t st) {
+static int launch_bwd_dv(const BwdParams& p, int64_t dv, hipStream_t st, bool reverse = true) {
     switch (dv) {
-        case 16: return launch_bwd_shape<DK, 16, BF16>(p, st);
-        case 32: return launch_bwd_shape<DK, 32, BF16>(p, st);
-        case 64: return launch_bwd_shape<DK, 64, BF16>(p, st);
-        case 128: return launch_bwd_shape<DK, 128, BF16>(p, st);
+        case 16: return launch_bwd_shape<DK, 16, BF16>(p, st, reverse);
+        case 32: return launch_bwd_shape<DK, 32, BF16>(p, st, reverse);
+        case 64: return launch_bwd_shape<DK, 64, BF16>(p, st, reverse);
+        case 128: return launch_bwd_shape<DK, 128, BF16>(p, st, reverse);
         default: return KDN_EUNSUPPORTED;
     }
 }
@@ -211,16 +213,34 @@ int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64
 
 // The gradient over a packed variable-length batch: the plan, the frame
 // scalars per sequence-aligned chunk, then the same kernels with (sequence,
-// head) runs; the finishing sums run over the H rows of the token axis.
+// head) runs, or (item, head) runs of the segmented kernels where sequences
+// can be longer than a fair share; the finishing sums run over the H rows of
+// the token axis.
 int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t dk, bool bf16,
-                           hipStream_t st) {
+                           int32_t R, hipStream_t st) {
     if (p.H == 0) return KDN_OK;
     if (p.nseq > 0) {
+        // sequences longer than a fair share run in segments: the forward
+        // plan (items, composite segments), then after the frame scalars the
+        // forward composites and carries give the segments' starting states
+        if (p.vl_seg > 0) varlen_plan_launch(prep, R, st);
         hipLaunchKernelGGL(k_varlen_bwd_plan, dim3(1), dim3(kPlanThreads), 0, st, p);
         int rc = diag_prep_varlen_launch(prep, bf16, false, st);
         if (rc != KDN_OK) return rc;
-        if (dk == 64) rc = bf16 ? launch_bwd_dv<64, true>(p, p.dv, st) : launch_bwd_dv<64, false>(p, p.dv, st);
-        else rc = bf16 ? launch_bwd_dv<128, true>(p, p.dv, st) : launch_bwd_dv<128, false>(p, p.dv, st);
+        if (p.vl_seg > 0) {
+            if (prep.vl_comps > 0 && (rc = diag_varlen_comp_launch(prep, dk, bf16, R, st)) != KDN_OK) return rc;
+            // whole sequences' checkpoints (the plain pass), then the split
+            // sequences' with their adjoint composites, the carry, and the
+            // reverse pass over every item
+            rc = dk == 64 ? (bf16 ? launch_bwd_dv<64, true>(p, p.dv, st, false) : launch_bwd_dv<64, false>(p, p.dv, st, false))
+                          : (bf16 ? launch_bwd_dv<128, true>(p, p.dv, st, false) : launch_bwd_dv<128, false>(p, p.dv, st, false));
+            if (rc != KDN_OK) return rc;
+            rc = diag_bwd_seg_launch(p, dk, bf16, st);
+        } else if (dk == 64) {
+            rc = bf16 ? launch_bwd_dv<64, true>(p, p.dv, st) : launch_bwd_dv<64, false>(p, p.dv, st);
+        } else {
+            rc = bf16 ? launch_bwd_dv<128, true>(p, p.dv, st) : launch_bwd_dv<128, false>(p, p.dv, st);
+        }
         if (rc != KDN_OK) return rc;
     }
     if (p.T > 0) {

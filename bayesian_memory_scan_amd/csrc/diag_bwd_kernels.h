@@ -414,9 +414,12 @@ struct BwdRun {
     int64_t nch;        // 16-token chunks from t_begin (the last one ragged)
     float* ck0;         // checkpoint before chunk 0; chunk c < nch at ck0 + c * 2 BLK
     float* ckfin;       // the final state
-    int64_t rt;         // (row, column tile) index of the segment slots: row * NTILE + tile
-    int seg;            // segment of a fixed-length row cut into p.S segments (else 0)
+    int64_t rt;         // (row, column tile) index: row * NTILE + tile
+    int seg;            // the run's segment of its row or sequence (0 when not cut)
     bool last;          // the run ends its row or sequence
+    // runs in segments: its adjoint slots (adj, lam), its decay (adjg) and
+    // the forward carry it starts from (comp, for seg > 0)
+    int64_t slot, gidx, cslot;
     int tile;
     bool valid;         // false: a padding workgroup of a packed batch
 };
@@ -450,7 +453,7 @@ __device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
         r.valid = true;
         return r;
     }
-    if (SEG) {
+    if (SEG && p.cu_seqlens == nullptr) {
         // the divisions leave their results in VGPRs; the run's fields are
         // wave-uniform and go back to SGPRs for the kernel's lifetime
         const int64_t wg = xcd_local_id();
@@ -469,7 +472,44 @@ __device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
         r.rt = bh * NTILE + r.tile;
         r.ck0 = ckpt_slot<BLK>(p.ckpt, r.rt, c0, n, p.nruns * NTILE);
         r.ckfin = ckpt_slot<BLK>(p.ckpt, r.rt, n, n, p.nruns * NTILE);
+        r.slot = r.rt * p.S + r.seg;
+        r.gidx = bh * p.S + r.seg;
+        r.cslot = bh * p.S + r.seg;
         r.valid = true;
+        return r;
+    }
+    if (SEG) {
+        // a packed batch whose long sequences run in segments: item `item` of
+        // the forward plan (sequence sq, segment g) on head h, in groups of 8
+        // runs x NTILE tiles as below
+        const int64_t blk = blockIdx.x;
+        const int64_t within = blk % (8 * NTILE);
+        r.tile = static_cast<int>(within / 8);
+        const int64_t wg = blk / (8 * NTILE) * 8 + within % 8;
+        const int64_t item = uniform64(wg / p.H);
+        const int64_t h = uniform64(wg % p.H);
+        r.valid = item < p.nwork[0];
+        if (!r.valid) return r;
+        const int32_t sq = p.item_seq[item];
+        r.seg = p.item_seg[item];
+        int64_t a = p.cu_seqlens[sq], b = p.cu_seqlens[sq + 1];
+        a = a < 0 ? 0 : (a > p.T ? p.T : a);
+        b = b < a ? a : (b > p.T ? p.T : b);
+        const int64_t t0 = a + static_cast<int64_t>(r.seg) * p.vl_seg;
+        r.t_begin = t0 < b ? t0 : b;
+        r.t_end = r.t_begin + p.vl_seg < b ? r.t_begin + p.vl_seg : b;
+        r.nch = uniform64((r.t_end - r.t_begin + kBwdChunk - 1) / kBwdChunk);
+        r.last = r.t_end == b;
+        r.state = static_cast<int64_t>(sq) * p.H + h;
+        r.rt = r.state * NTILE + r.tile;
+        r.tbase = h * p.T;
+        float* const base = p.ckpt + ((h * NTILE + r.tile) * p.ck_stride + p.seq_ckoff[sq]) * 2 * BLK;
+        r.ck0 = base + (r.t_begin - a) / kBwdChunk * 2 * BLK;
+        r.ckfin = base + (b - a + kBwdChunk - 1) / kBwdChunk * 2 * BLK;
+        r.slot = (item * p.H + h) * NTILE + r.tile;
+        r.gidx = item * p.H + h;
+        const int32_t c0 = p.seq_comp[sq];
+        r.cslot = r.seg > 0 && c0 >= 0 && c0 + r.seg - 1 < p.vl_comps ? (c0 + r.seg - 1) * p.H + h : -1;
         return r;
     }
     r.seg = 0;
@@ -564,10 +604,10 @@ __device__ __forceinline__ void start_state(const BwdParams& p, int64_t off, flo
 // Checkpoint pass: the state before every chunk, unscaled, in the slab layout
 // [bh][tile][chunk][I | eta][column wave][row][16] the reverse pass reads.
 // ---------------------------------------------------------------------------
-// A (row, tile, segment) slot of 2 BLK floats in the checkpoint layout.
+// The run's adjoint slot (2 BLK floats in the checkpoint layout).
 template <int BLK>
-__device__ __forceinline__ float* seg_slot(float* base, const BwdRun& r, int S, int seg) {
-    return base + (r.rt * S + seg) * 2 * BLK;
+__device__ __forceinline__ float* adj_slot(float* base, const BwdRun& r) {
+    return base + r.slot * 2 * BLK;
 }
 
 // With ADJ (rows cut into S > 1 segments) every segment starts from its own
@@ -579,9 +619,10 @@ __device__ __forceinline__ float* seg_slot(float* base, const BwdRun& r, int S, 
 //   alpha_a lam_a = sum_{t in [a, e)} P_t b_t + P_{e-1} (alpha_e lam_e),
 //   P_t = prod_{u = a..t} alpha_u,
 // where the sum is known from the forward states alone: it is accumulated
-// here (adj slot) with P_{e-1} (adjg), and a carry pass chains the segments
-// from the row's end.  The last segment stores the adjoint that the final
-// state's gradients start, alpha_e lam_e of the chain (lam slot S - 1).
+// here (the run's adj slot) with P_{e-1} (adjg), and a carry pass chains the
+// segments from the row's or sequence's end.  The last segment stores the
+// adjoint that the final state's gradients start (its lam slot).  Runs are
+// a fixed-length row's segments or a packed batch's items (bwd_run).
 template <int DK, int DV, bool BF16, bool ADJ>
 __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdParams p) {
     using Sh = BwdShape<DK, DV>;
@@ -599,14 +640,20 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
     const int lc = cg * 16 + (lane & 15);      // this lane's value column in the tile (for operands)
     const BwdRun run = bwd_run<Sh::BLK, Sh::NTILE, ADJ>(p);
     if (!run.valid) return;
+    if (p.cu_seqlens && p.vl_seg > 0) {
+        // a packed batch that can hold split sequences: their runs take the
+        // ADJ instantiation, the whole sequences' the plain one
+        const bool split = p.seq_comp[uniform64(run.state / p.H)] >= 0;
+        if (split != ADJ) return;
+    }
     const int tile = run.tile;
     const int64_t nch = run.nch;
     const float I_prior = p.I_prior;
     const int64_t ent = (run.state * DK + j) * p.dv + tile * CI + cg * 16;   // this lane's 16 entries
 
     float I[16], m0[16], J[16], E[16];
-    if (ADJ && run.seg > 0) {
-        const float* cin = p.comp + (run.state * p.S + run.seg) * 2 * DK * p.dv + (ent - run.state * DK * p.dv);
+    if (ADJ && run.seg > 0 && run.cslot >= 0) {
+        const float* cin = p.comp + run.cslot * 2 * DK * p.dv + (ent - run.state * DK * p.dv);
         load16(cin, J);
         load16(cin + DK * p.dv, E);
     } else {
@@ -699,10 +746,10 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
 
     if constexpr (ADJ) {
         if (acc) {
-            float* dst = seg_slot<Sh::BLK>(p.adj, run, p.S, run.seg);
+            float* dst = adj_slot<Sh::BLK>(p.adj, run);
             store16_ckpt<Sh::BLK>(dst, lid, Ba);
             store16_ckpt<Sh::BLK>(dst + Sh::BLK, lid, Bb);
-            if (tid == 0 && tile == 0) p.adjg[run.state * p.S + run.seg] = P;
+            if (tid == 0 && tile == 0) p.adjg[run.gidx] = P;
         }
         if (run.last) {
             // the gradients of the final state (J, E now unscaled):
@@ -716,7 +763,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
                 La[e] = gm * rI;
                 Lb[e] = gi - gm * E[e] * rI * rI;
             });
-            float* dst = seg_slot<Sh::BLK>(p.lam, run, p.S, p.S - 1);
+            float* dst = adj_slot<Sh::BLK>(p.lam, run);
             store16_ckpt<Sh::BLK>(dst, lid, La);
             store16_ckpt<Sh::BLK>(dst + Sh::BLK, lid, Lb);
         }
@@ -781,11 +828,12 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         fetch(nch - 1);
         ld.commit(stg[0], chunk_len(nch - 1), tid);
         const float inv_s = 1.0f / uniform(p.scal[run.tbase + run.t_end - 1].z);
-        if constexpr (SEG) {
-            // a segment of a row: the adjoint flowing into its end, unscaled,
-            // from the carry pass; to the last token's frame (s = s_{e-1})
+        if (SEG && !run.last) {
+            // a segment before the last: the adjoint flowing into its end,
+            // unscaled, from the carry pass; to the last token's frame
+            // (s = s_{e-1})
             float La[16], Lb[16];
-            load_ckpt<Sh::BLK>(seg_slot<Sh::BLK>(p.lam, run, p.S, run.seg), lid, La, Lb);
+            load_ckpt<Sh::BLK>(adj_slot<Sh::BLK>(p.lam, run), lid, La, Lb);
 #pragma unroll
             for (int c = 0; c < 16; ++c) {
                 L[c] = La[c] * inv_s;

@@ -1022,6 +1022,7 @@ __global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(DiagParams p, int6
     auto segs = [&](int32_t s) -> int64_t { return staged ? nsg[s] : varlen_segments(p, len(s)); };
     auto place = [&](int32_t s, int64_t nseg, int64_t rank, int64_t io, int64_t co, int64_t so) {
         p.seq_order[rank] = s;
+        if (p.seq_item) p.seq_item[s] = io < p.vl_items ? static_cast<int32_t>(io) : -1;
         for (int64_t g = 0; g < nseg && io + g < p.vl_items; ++g) {
             p.item_seq[io + g] = s;
             p.item_seg[io + g] = static_cast<int32_t>(g);
@@ -1136,8 +1137,12 @@ int diag_prep_varlen_launch(const DiagParams& p, bool bf16, bool true_i, hipStre
 // Packed batch: the plan, the frame scalars, the composites and carries of
 // split sequences, then the main pass over the plan's items (the grid covers
 // the item capacity; workgroups past the plan's items return at once).
-int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
+void varlen_plan_launch(const DiagParams& p, int32_t R, hipStream_t st) {
     hipLaunchKernelGGL(k_varlen_plan, dim3(1), dim3(kPlanThreads), 0, st, p, p.vl_comps * p.H * R);
+}
+
+int diag_varlen_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t R, hipStream_t st) {
+    varlen_plan_launch(p, R, st);
     // the block kernel keeps I in true units
     const int prc = diag_prep_varlen_launch(p, bf16, varlen_cols(p.dv) == 64, st);
     if (prc != KDN_OK) return prc;

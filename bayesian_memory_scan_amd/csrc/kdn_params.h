@@ -48,6 +48,7 @@ struct DiagParams {
     int32_t* comp_seq;           // [vl_comps] sequence of each composite segment
     int32_t* comp_seg;           // [vl_comps] its segment within the sequence
     int32_t* split_seq;          // [vl_comps] the split sequences, in plan order
+    int32_t* seq_item;           // [nseq] first item of each sequence, or NULL (not written)
     int32_t* nwork;              // [4]: items, composite segments, split sequences (each <= capacity),
                                  // sub-segments per composite segment
     int64_t vl_seg;              // segment length of a split sequence (multiple of 256), 0 = no split
@@ -342,6 +343,19 @@ struct BwdParams {
     float* adj;                  // [BH*ntile][S][slot]: segment s's adjoint composite (s >= 1)
     float* lam;                  // [BH*ntile][S][slot]: the adjoint flowing into segment s's end
     float* adjg;                 // [BH][S]: product of alpha over segment s
+    // A packed batch whose long sequences run in segments (vl_seg > 0): the
+    // forward plan's tables; runs are (item, head, tile); comp holds the
+    // forward composites' carries [vl_comps][H][2][dk][dv]; adj and lam are
+    // [vl_items][H][ntile][slot], adjg [vl_items][H].
+    const int32_t* item_seq;
+    const int32_t* item_seg;
+    const int32_t* seq_item;
+    const int32_t* seq_comp;
+    const int32_t* split_seq;
+    const int32_t* nwork;
+    int64_t vl_seg;
+    int64_t vl_items;
+    int64_t vl_comps;
 };
 
 int diag_chunk();
@@ -351,8 +365,9 @@ int32_t bwd_token_split(int64_t rows, int64_t T);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
                     bool bf16, int32_t R, hipStream_t st);
 int diag_bwd_seg_launch(const BwdParams& p, int64_t dk, bool bf16, hipStream_t st);
+void varlen_plan_launch(const DiagParams& p, int32_t R, hipStream_t st);
 int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t dk, bool bf16,
-                           hipStream_t st);
+                           int32_t R, hipStream_t st);
 int diag_prep_launch(const DiagParams& p, int64_t B, bool bf16, bool true_i, hipStream_t st);
 int diag_prep_varlen_launch(const DiagParams& p, bool bf16, bool true_i, hipStream_t st);
 int diag_scan_launch(const DiagParams& p, int64_t B, int64_t dk, bool bf16, int32_t R, hipStream_t st);

@@ -707,7 +707,19 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     const int32_t split = bwd_token_split(H, work ? total_T : 0);
     const size_t b_head = align_up(f * 2 * static_cast<size_t>(H) * split, 256);
     const size_t b_db = beta ? 0 : b_tok;
-    const size_t need = work ? b_scal + b_order + b_ckoff + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db
+    // sequences longer than a fair share run in segments (the forward plan of
+    // kdn_diag_varlen_plan): its tables and composites, plus per item the
+    // adjoint composite and carried adjoint (adj, lam) and the decay (adjg)
+    const VarlenPlan vp = work ? plan_varlen(N, H, total_T, d_v, 0) : VarlenPlan{0, 1, 0, N};
+    if (vp.items >= 2147483647 || !grid_fits((vp.items * H + 7) / 8 * 8 * ntile)) return KDN_EINVAL;
+    const VarlenWs vw = varlen_workspace(N, H, total_T, d_k, d_v, vp);
+    const size_t b_item = align_up(f * static_cast<size_t>(vp.items) * H * 2 * d_k * d_v, 256);
+    const size_t b_itemg = align_up(f * static_cast<size_t>(vp.items) * H, 256);
+    const size_t b_split = vp.seg > 0 ? 2 * vw.items + 2 * vw.seqcomp + 3 * vw.comptab + vw.nwork + vw.comp +
+                                            vw.sub + vw.gsub + 2 * b_item + b_itemg
+                                      : 0;
+    const size_t need = work ? b_scal + b_order + b_ckoff + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db +
+                                   b_split
                              : b_head;
     const int wc = workspace_check(workspace, workspace_bytes, need);
     if (wc == 1) return KDN_OK;
@@ -753,6 +765,35 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
         prep.d = d; prep.A = A; prep.scal = scal;
         prep.H = H; prep.T = total_T; prep.dv = d_v; prep.I_prior = I_prior;
         prep.S = 1; prep.cu_seqlens = cu_seqlens; prep.nseq = static_cast<int32_t>(N);
+        if (vp.seg > 0) {
+            char* w = ws + b_head + b_db;
+            auto take = [&](size_t n) { char* x = w; w += n; return x; };
+            prep.k = k; prep.v = v; prep.beta = beta; prep.I0 = I0; prep.mu0 = mu0;
+            prep.seq_order = p.seq_order;
+            prep.item_seq = reinterpret_cast<int32_t*>(take(vw.items));
+            prep.item_seg = reinterpret_cast<int32_t*>(take(vw.items));
+            prep.seq_comp = reinterpret_cast<int32_t*>(take(vw.seqcomp));
+            prep.seq_item = reinterpret_cast<int32_t*>(take(vw.seqcomp));
+            if (vp.comps > 0) {
+                prep.comp_seq = reinterpret_cast<int32_t*>(take(vw.comptab));
+                prep.comp_seg = reinterpret_cast<int32_t*>(take(vw.comptab));
+                prep.split_seq = reinterpret_cast<int32_t*>(take(vw.comptab));
+            }
+            prep.nwork = reinterpret_cast<int32_t*>(take(vw.nwork));
+            if (vp.comps > 0) {
+                prep.comp = reinterpret_cast<float*>(take(vw.comp));
+                prep.sub = reinterpret_cast<float*>(take(vw.sub));
+                prep.gsub = reinterpret_cast<float*>(take(vw.gsub));
+            }
+            prep.vl_seg = vp.seg; prep.vl_items = vp.items; prep.vl_comps = vp.comps;
+            p.item_seq = prep.item_seq; p.item_seg = prep.item_seg; p.seq_item = prep.seq_item;
+            p.seq_comp = prep.seq_comp; p.split_seq = prep.split_seq; p.nwork = prep.nwork;
+            p.comp = prep.comp;
+            p.vl_seg = vp.seg; p.vl_items = vp.items; p.vl_comps = vp.comps;
+            p.adj = reinterpret_cast<float*>(take(b_item));
+            p.lam = reinterpret_cast<float*>(take(b_item));
+            p.adjg = reinterpret_cast<float*>(take(b_itemg));
+        }
     } else {
         // nothing to run but the finishing sums: dA = 0, dI_prior = 0
         p.nseq = 0;
@@ -760,7 +801,7 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     }
     p.part_head = reinterpret_cast<float*>(ws);
     (void)hipGetLastError();  // launch status below must reflect this call only
-    return diag_varlen_bwd_launch(p, prep, d_k, in_dtype == KDN_BF16, static_cast<hipStream_t>(stream));
+    return diag_varlen_bwd_launch(p, prep, d_k, in_dtype == KDN_BF16, vp.R, static_cast<hipStream_t>(stream));
 }
 
 int kdn_mobius_precision_scan(int64_t B, int64_t H, int64_t T,

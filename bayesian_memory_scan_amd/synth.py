@@ -137,6 +137,9 @@ WORKLOADS = {
         # a skewed packed batch: one 8192-token sequence, 63 short ones in the other half
         VarlenSpec("varlenskew_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1008,
                    long_tokens=8192),
+        # gradient over the skewed batch
+        VarlenSpec("varlenskewbwd_n64h16t16384d128_bf16", 16, 64, 16384, 128, 128, "bf16", 1008,
+                   long_tokens=8192),
         # gradient of the headline forward workload (same inputs)
         DiagSpec("bwd_b8h16t2048d128_bf16", 8, 16, 2048, 128, 128, "bf16", 1001),
         # gradient of the long-sequence workload (same inputs)

@@ -483,7 +483,7 @@ def main():
         })
         if not a.no_cpu:
             out["cpu_baseline"] = cpu_baseline_bwd(inp, grads, spec, a.cpu_seconds)
-    elif a.workload.startswith("varlenbwd_"):
+    elif a.workload.startswith(("varlenbwd_", "varlenskewbwd_")):
         inp = synth.varlen_inputs(spec)
         d_o_h = synth.varlen_grad_inputs(spec)["d_o"]
         x = {n: _up(inp[n][0], torch, dev) for n in ("q", "k", "v", "beta", "d")}

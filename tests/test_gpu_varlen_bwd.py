@@ -161,3 +161,43 @@ def test_varlen_bwd_deterministic(kdn):
     b = _run(kdn, inp, inp["cu_seqlens"], d_o)
     for n in a:
         assert np.array_equal(a[n], b[n]), n
+
+
+# long sequences run in 512-token segments at these sizes (kdn_diag_varlen_plan)
+SPLIT_LENGTHS = [1500, 30, 700, 0, 2100, 5, 1200, 513, 512]
+
+
+@pytest.mark.parametrize("case", [(64, 64, "f32", False, True), (128, 128, "bf16", False, False),
+                                  (128, 64, "bf16", True, True), (64, 32, "bf16", False, True)],
+                         ids=lambda c: "d{}x{}{}{}{}".format(c[0], c[1], c[2], "_m" if c[3] else "",
+                                                             "_state" if c[4] else ""))
+def test_varlen_bwd_split_sequences(kdn, case):
+    """Sequences longer than a fair share run in segments (forward composites
+    for their starting states, adjoint composites carried from each sequence's
+    end); every sequence against the oracle run on its own."""
+    dk, dv, dt, mg, with_state = case
+    H = 2
+    cu = np.concatenate([[0], np.cumsum(SPLIT_LENGTHS)]).astype(np.int64)
+    T, N = int(cu[-1]), len(SPLIT_LENGTHS)
+    assert kdn.kdn_diag_varlen_plan(N, H, T, dk, dv)[0] == 512
+    spec = synth.VarlenSpec("varlen_bwd_split", H, N, T, dk, dv, dt, 7990, m_gating=mg, I_prior=1.3)
+    inp = synth.varlen_inputs(spec)
+    inp["cu_seqlens"] = cu
+    d_o = np.random.default_rng(7991).standard_normal((1, H, T, dv)).astype(np.float32)
+    st = _states(N, H, dk, dv, 7992) if with_state else None
+    print(f"varlen bwd split {case}", flush=True)
+    g = _run(kdn, inp, cu, d_o[0], st)
+    _compare(g, inp, cu, d_o, st, range(N), range(H), True, f"split {case}")
+
+
+def test_varlen_bwd_skewed_workload_sampled(kdn):
+    """The skewed packed batch (one 8192-token sequence among 63 short ones,
+    16 heads, d 128 bf16): the long sequence on two heads and a short one
+    against the oracle."""
+    spec = synth.workload("varlenskew_n64h16t16384d128_bf16")
+    inp = synth.varlen_inputs(spec)
+    cu = inp["cu_seqlens"]
+    d_o = synth.varlen_grad_inputs(spec)["d_o"]
+    print("varlen bwd skewed workload", flush=True)
+    g = _run(kdn, inp, cu, d_o[0])
+    _compare(g, inp, cu, d_o, None, [0, 40], (0, spec.H - 1), False, "skew")
