@@ -67,13 +67,25 @@ static int launch_seg_shape(const BwdParams& p, hipStream_t st) {
                                    : p.BH * p.S * Sh::NTILE;
     if (g == 0) return KDN_OK;
     const dim3 grid(static_cast<uint32_t>(g));
-    hipLaunchKernelGGL((k_diag_bwd_ckpt<DK, DV, BF16, true>), grid, dim3(Sh::NTH), 0, st, p);
+    // A packed batch: the split sequences rank before every whole one (they
+    // are the longer ones), so their items are the plan's first, at most two
+    // per composite segment; the checkpoint pass with adjoint composites
+    // needs no more (past kMaxPlanSort sequences the order is the index
+    // order and the grid covers every item).
+    int64_t gc = g;
+    if (p.cu_seqlens && p.nseq <= kMaxPlanSort) {
+        const int64_t split_items = 2 * p.vl_comps < p.vl_items ? 2 * p.vl_comps : p.vl_items;
+        gc = (split_items * p.H + 7) / 8 * 8 * Sh::NTILE;
+    }
+    if (gc > 0) hipLaunchKernelGGL((k_diag_bwd_ckpt<DK, DV, BF16, true>), dim3(static_cast<uint32_t>(gc)),
+                                   dim3(Sh::NTH), 0, st, p);
     const int64_t slot = 2 * Sh::BLK;
     if (p.cu_seqlens) {
         if (p.vl_comps > 0) {
             const int64_t n = p.vl_comps * p.H * Sh::NTILE * slot;
-            hipLaunchKernelGGL(k_bwd_adj_carry_varlen, dim3(elem_groups(n)), dim3(256), 0, st, p, slot, n,
-                               static_cast<int32_t>(Sh::NTILE));
+            const int64_t groups = elem_groups(n) < 1024 ? elem_groups(n) : 1024;
+            hipLaunchKernelGGL(k_bwd_adj_carry_varlen, dim3(static_cast<uint32_t>(groups)), dim3(256), 0, st, p,
+                               slot, n, static_cast<int32_t>(Sh::NTILE));
         }
     } else {
         const int64_t n = p.BH * Sh::NTILE * slot;
