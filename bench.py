@@ -212,7 +212,9 @@ def cpu_baseline_bwd(inp, grads, spec, target_s):
     heads_all = [(b, h) for b in range(spec.B) for h in range(spec.H)]
     with oracle.Timer() as t1:
         oracle.diag_scan_bwd(inp, grads["d_o"], heads=heads_all[:1], threads=1)
-    n = max(1, min(len(heads_all), int(target_s / max(t1.seconds, 1e-3) * threads)))
+    # whole rounds of `threads` heads, each round taking about t1
+    rounds = max(1, int(target_s / max(t1.seconds, 1e-3)))
+    n = max(1, min(len(heads_all), rounds * threads))
     with oracle.Timer() as t:
         oracle.diag_scan_bwd(inp, grads["d_o"], heads=heads_all[:n], threads=threads)
     return {"value": n * spec.T / spec.H / t.seconds, "unit": "tokens/s",
