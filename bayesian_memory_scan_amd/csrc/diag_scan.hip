@@ -1023,9 +1023,20 @@ __global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(DiagParams p, int6
     auto place = [&](int32_t s, int64_t nseg, int64_t rank, int64_t io, int64_t co, int64_t so) {
         p.seq_order[rank] = s;
         if (p.seq_item) p.seq_item[s] = io < p.vl_items ? static_cast<int32_t>(io) : -1;
+        int64_t a, b;
+        sequence_tokens(p, s, a, b);
         for (int64_t g = 0; g < nseg && io + g < p.vl_items; ++g) {
             p.item_seq[io + g] = s;
             p.item_seg[io + g] = static_cast<int32_t>(g);
+            VarlenItemRec r;
+            const int64_t t0 = nseg > 1 ? a + g * p.vl_seg : a;
+            r.t_begin = t0 < b ? t0 : b;
+            r.t_end = nseg > 1 && t0 + p.vl_seg < b ? t0 + p.vl_seg : b;
+            r.sq = s;
+            r.seg = static_cast<int32_t>(g);
+            r.carry = g > 0 && co + g - 1 < p.vl_comps ? static_cast<int32_t>(co + g - 1) : -1;
+            r.last = g + 1 == nseg ? 1 : 0;
+            p.items[io + g] = r;
         }
         p.seq_comp[s] = nseg > 1 && co < p.vl_comps ? static_cast<int32_t>(co) : -1;
         for (int64_t g = 0; g + 1 < nseg && co + g < p.vl_comps; ++g) {
@@ -1100,6 +1111,15 @@ __global__ __launch_bounds__(kPlanThreads) void k_varlen_plan(DiagParams p, int6
                 for (int x = 0; x < 3; ++x) part[x][tid] += part[x][tid + h];
             }
             __syncthreads();
+        }
+    }
+    // the item slots past the plan's items: a sentinel record
+    {
+        const int64_t last = sorted ? 0 : kPlanThreads - 1;
+        for (int64_t i = part[0][last] + tid; i < p.vl_items; i += kPlanThreads) {
+            VarlenItemRec r{};
+            r.sq = -1;
+            p.items[i] = r;
         }
     }
     if (tid == 0) {

@@ -8,6 +8,16 @@ namespace kdn {
 
 // Segmented scan over a d_k x d_v state per head: the diagonal-precision scan,
 // or the gated mean of the isotropic filter (F, G set, beta/d unused).
+// One main-pass item of a packed batch as the plan writes it: everything a
+// workgroup needs in one 32-byte record.
+struct VarlenItemRec {
+    int64_t t_begin, t_end;     // packed tokens of the segment
+    int32_t sq;                 // its sequence, or -1 past the plan's items
+    int32_t seg;                // its segment within the sequence
+    int32_t carry;              // composite slot of its starting state, or -1 (the sequence's own)
+    int32_t last;               // 1: the sequence's last segment (writes the final state)
+};
+
 struct DiagParams {
     const void* q;
     const void* k;
@@ -44,6 +54,7 @@ struct DiagParams {
     // [vl_comps][H][R][2][dk][dv] and gsub [vl_comps][H][R] its sub-segments.
     int32_t* item_seq;           // [vl_items] sequence of each main-pass item, dispatch order
     int32_t* item_seg;           // [vl_items] the item's segment within its sequence
+    struct VarlenItemRec* items; // [vl_items] each item's bounds and carry (sq < 0: past the plan's items)
     int32_t* seq_comp;           // [nseq] first composite segment of a split sequence, else -1
     int32_t* comp_seq;           // [vl_comps] sequence of each composite segment
     int32_t* comp_seg;           // [vl_comps] its segment within the sequence
@@ -147,28 +158,19 @@ struct VarlenItem {
 
 __device__ __forceinline__ bool varlen_item(const DiagParams& p, int64_t wg, VarlenItem& it) {
     const int64_t item = wg / p.H;
-    if (item >= p.nwork[0]) return false;
+    if (item >= p.vl_items) return false;
+    // one record, written by the plan for every slot up to the capacity
+    const int4* rec = reinterpret_cast<const int4*>(p.items + item);
+    const int4 lo = rec[0], hi = rec[1];
+    it.sq = hi.x;
+    if (it.sq < 0) return false;
     it.bh = wg % p.H;
-    it.sq = p.item_seq[item];
-    it.seg = p.item_seg[item];
+    it.t_begin = (static_cast<int64_t>(static_cast<uint32_t>(lo.y)) << 32) | static_cast<uint32_t>(lo.x);
+    it.t_end = (static_cast<int64_t>(static_cast<uint32_t>(lo.w)) << 32) | static_cast<uint32_t>(lo.z);
+    it.seg = hi.y;
+    it.carry = hi.z;
+    it.last = hi.w != 0;
     it.sb = static_cast<int64_t>(it.sq) * p.H + it.bh;
-    int64_t a, b;
-    sequence_tokens(p, it.sq, a, b);
-    if (p.vl_seg > 0) {
-        const int64_t t0 = a + static_cast<int64_t>(it.seg) * p.vl_seg;
-        it.t_begin = t0 < b ? t0 : b;
-        it.t_end = t0 + p.vl_seg < b ? t0 + p.vl_seg : b;
-    } else {
-        it.t_begin = a;
-        it.t_end = b;
-    }
-    it.last = it.t_end == b;
-    it.carry = -1;
-    const int32_t c0 = p.seq_comp[it.sq];
-    if (it.seg > 0 && c0 >= 0) {
-        const int64_t c = static_cast<int64_t>(c0) + it.seg - 1;
-        if (c < p.vl_comps) it.carry = c;
-    }
     return true;
 }
 

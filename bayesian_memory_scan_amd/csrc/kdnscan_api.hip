@@ -125,7 +125,7 @@ VarlenPlan plan_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dv, int32_
 
 // Workspace of a packed batch's forward scan, in this order.
 struct VarlenWs {
-    size_t scal, order, items, seqcomp, comptab, nwork, comp, sub, gsub, total;
+    size_t scal, order, items, recs, seqcomp, comptab, nwork, comp, sub, gsub, total;
 };
 VarlenWs varlen_workspace(int64_t N, int64_t H, int64_t total_T, int64_t dk, int64_t dv,
                           const VarlenPlan& v) {
@@ -134,6 +134,7 @@ VarlenWs varlen_workspace(int64_t N, int64_t H, int64_t total_T, int64_t dk, int
     w.scal = align_up(16 * static_cast<size_t>(H) * total_T, 256);
     w.order = align_up(4 * static_cast<size_t>(N), 256);
     w.items = align_up(4 * static_cast<size_t>(v.items), 256);          // each of item_seq, item_seg
+    w.recs = align_up(sizeof(VarlenItemRec) * static_cast<size_t>(v.items), 256);
     w.seqcomp = align_up(4 * static_cast<size_t>(N), 256);
     w.comptab = v.comps > 0 ? align_up(4 * static_cast<size_t>(v.comps), 256) : 0;   // each of 3
     w.nwork = 256;
@@ -141,7 +142,7 @@ VarlenWs varlen_workspace(int64_t N, int64_t H, int64_t total_T, int64_t dk, int
     w.comp = v.comps > 0 ? align_up(f * units * 2 * dk * dv, 256) : 0;
     w.sub = v.comps > 0 ? align_up(f * units * v.R * 2 * dk * dv, 256) : 0;
     w.gsub = v.comps > 0 ? align_up(f * units * v.R, 256) : 0;
-    w.total = w.scal + w.order + 2 * w.items + w.seqcomp + 3 * w.comptab + w.nwork + w.comp + w.sub + w.gsub;
+    w.total = w.scal + w.order + 2 * w.items + w.recs + w.seqcomp + 3 * w.comptab + w.nwork + w.comp + w.sub + w.gsub;
     return w;
 }
 
@@ -456,6 +457,8 @@ int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d
     ws += w.items;
     p.item_seg = reinterpret_cast<int32_t*>(ws);
     ws += w.items;
+    p.items = reinterpret_cast<VarlenItemRec*>(ws);
+    ws += w.recs;
     p.seq_comp = reinterpret_cast<int32_t*>(ws);
     ws += w.seqcomp;
     if (vp.comps > 0) {
@@ -715,8 +718,8 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     const VarlenWs vw = varlen_workspace(N, H, total_T, d_k, d_v, vp);
     const size_t b_item = align_up(f * static_cast<size_t>(vp.items) * H * 2 * d_k * d_v, 256);
     const size_t b_itemg = align_up(f * static_cast<size_t>(vp.items) * H, 256);
-    const size_t b_split = vp.seg > 0 ? 2 * vw.items + 2 * vw.seqcomp + 3 * vw.comptab + vw.nwork + vw.comp +
-                                            vw.sub + vw.gsub + 2 * b_item + b_itemg
+    const size_t b_split = vp.seg > 0 ? 2 * vw.items + vw.recs + 2 * vw.seqcomp + 3 * vw.comptab + vw.nwork +
+                                            vw.comp + vw.sub + vw.gsub + 2 * b_item + b_itemg
                                       : 0;
     const size_t need = work ? b_scal + b_order + b_ckoff + b_ckpt + 2 * b_rows + 2 * b_tok + b_dip0 + b_head + b_db +
                                    b_split
@@ -772,6 +775,7 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
             prep.seq_order = p.seq_order;
             prep.item_seq = reinterpret_cast<int32_t*>(take(vw.items));
             prep.item_seg = reinterpret_cast<int32_t*>(take(vw.items));
+            prep.items = reinterpret_cast<VarlenItemRec*>(take(vw.recs));
             prep.seq_comp = reinterpret_cast<int32_t*>(take(vw.seqcomp));
             prep.seq_item = reinterpret_cast<int32_t*>(take(vw.seqcomp));
             if (vp.comps > 0) {

@@ -236,11 +236,12 @@ def test_varlen_validation_and_workspace():
                                      FAKE, 1.0, I0, None, FAKE, None, None, ws,
                                      None if nb is None else ctypes.byref(nb), None)
     assert call() == kdn.KDN_OK
-    # frame scalars, then the plan's tables (order, item sequence and segment,
-    # first composite of each sequence, counts), 256 bytes each at this size;
-    # 40 tokens cannot be split, so no composite tables or states
+    # frame scalars, then the plan's tables (order, item sequence, segment and
+    # 32-byte record, first composite of each sequence, counts), 256 bytes
+    # each at this size; 40 tokens cannot be split, so no composite tables or
+    # states
     assert kdn.kdn_diag_varlen_plan(3, 2, 40, 64, 64) == (0, 1, 3, 0)
-    assert n.value == 16 * 2 * 40 + 5 * 256
+    assert n.value == 16 * 2 * 40 + 6 * 256
     assert call(N=-1) == kdn.KDN_EINVAL
     assert call(cu=None) == kdn.KDN_EINVAL
     assert call(cu=FAKE + 4) == kdn.KDN_EINVAL  # int64 offsets must be 8-byte aligned
