@@ -147,6 +147,44 @@ void other_queries() {
     expect("bwd d_o null", kdn_diag_scan_bwd(1, 2, 64, 64, 64, KDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, fk, 1.0f,
                                              nullptr, nullptr, nullptr, nullptr, nullptr, fk, fk, fk, fk, fk, fk,
                                              nullptr, nullptr, nullptr, nullptr, &need, nullptr), KDN_EINVAL);
+    // the gradient with a segment request (long rows) and over packed batches,
+    // split and whole, and the packed plan query
+    for (int32_t S : {0, 1, 4, 64}) {
+        kdn_scan_opts m{};
+        m.segments = S;
+        expect("bwd_ex query", kdn_diag_scan_bwd_ex(2, 16, 16384, 128, 128, KDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                                    fk, 1.0f, nullptr, nullptr, fk, nullptr, nullptr, fk, fk, fk, fk,
+                                                    fk, fk, nullptr, nullptr, nullptr, &m, nullptr, &need, nullptr),
+               KDN_OK);
+    }
+    {
+        kdn_scan_opts m{};
+        int64_t echo[8];
+        m.bounds_echo = echo;
+        m.echo_capacity = 8;
+        expect("bwd_ex echo", kdn_diag_scan_bwd_ex(1, 2, 64, 64, 64, KDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, fk, 1.0f,
+                                                   nullptr, nullptr, fk, nullptr, nullptr, fk, fk, fk, fk, fk, fk,
+                                                   nullptr, nullptr, nullptr, &m, nullptr, &need, nullptr),
+               KDN_EINVAL);
+    }
+    for (int64_t T : {int64_t(40), int64_t(16384)}) {
+        expect("varlen bwd query", kdn_diag_scan_varlen_bwd(64, 16, T, 128, 128, KDN_BF16,
+                                                            static_cast<const int64_t*>(FAKE), FAKE, FAKE, FAKE,
+                                                            FAKE, FAKE, fk, 1.0f, nullptr, nullptr, fk, nullptr,
+                                                            nullptr, fk, fk, fk, fk, fk, fk, fk, nullptr, nullptr,
+                                                            nullptr, &need, nullptr), KDN_OK);
+    }
+    {
+        int64_t seg = -1, items = -1, comps = -1;
+        int32_t R = -1;
+        expect("varlen plan", kdn_diag_varlen_plan(64, 16, 16384, 128, 128, 0, &seg, &R, &items, &comps), KDN_OK);
+        if (seg != 2048 || items != 72 || comps != 8 || R < 1) {
+            std::fprintf(stderr, "varlen plan values\n");
+            g_fail = 1;
+        }
+        expect("varlen plan request", kdn_diag_varlen_plan(64, 16, 16384, 128, 128, 2, nullptr, nullptr, nullptr,
+                                                           nullptr), KDN_EINVAL);
+    }
     expect("decode dk", kdn_decode_step(1, 2, 8, 64, KDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, fk, 1.0f, fk, fk, fk,
                                         nullptr), KDN_EUNSUPPORTED);
     expect("decode prior", kdn_decode_step(1, 2, 64, 64, KDN_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, fk, -1.0f, fk, fk,
