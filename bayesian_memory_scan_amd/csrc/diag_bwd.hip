@@ -3,6 +3,8 @@
 // and packed batches (rows cut into segments: diag_bwd_seg.hip).
 #include "diag_bwd_kernels.h"
 
+#include <mutex>
+
 namespace kdn {
 
 // ---------------------------------------------------------------------------
@@ -211,6 +213,58 @@ int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64
     return launch_status();
 }
 
+// A second stream per device, with the events of one fork and one join.  A
+// packed batch's two checkpoint passes write disjoint runs' checkpoints: the
+// split sequences' pass (with adjoint composites) holds one workgroup per CU
+// on their items alone, so the whole sequences' pass runs beside it on this
+// stream, and the reverse pass waits for both.  Created on first use (default
+// priority, no implicit ordering with the null stream) and kept until the
+// process ends; g_side_mu makes a call's fork-and-join one unit between host
+// threads, so that no other call re-records the events in between.
+namespace {
+constexpr int kSideDevices = 64;
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+    bool made = false, failed = false;
+};
+std::mutex g_side_mu;
+SideStream g_side[kSideDevices];
+
+// The current device's side stream (g_side_mu held), or nullptr where none
+// could be made; a failed creation is not retried and leaves no pending error.
+SideStream* side_stream() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kSideDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    SideStream& sd = g_side[dev];
+    if (!sd.made && !sd.failed) {
+        if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) == hipSuccess) {
+            sd.made = true;
+        } else {
+            sd.failed = true;
+            (void)hipGetLastError();
+        }
+    }
+    return sd.made ? &sd : nullptr;
+}
+
+// The stream may fork: not under graph capture, where the caller's graph
+// would have to take in the side stream's work.
+bool may_fork(hipStream_t st) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return cs == hipStreamCaptureStatusNone;
+}
+}  // namespace
+
 // The gradient over a packed variable-length batch: the plan, the frame
 // scalars per sequence-aligned chunk, then the same kernels with (sequence,
 // head) runs, or (item, head) runs of the segmented kernels where sequences
@@ -229,13 +283,33 @@ int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t d
         if (rc != KDN_OK) return rc;
         if (p.vl_seg > 0) {
             if (prep.vl_comps > 0 && (rc = diag_varlen_comp_launch(prep, dk, bf16, R, st)) != KDN_OK) return rc;
-            // whole sequences' checkpoints (the plain pass), then the split
-            // sequences' with their adjoint composites, the carry, and the
-            // reverse pass over every item
-            rc = dk == 64 ? (bf16 ? launch_bwd_dv<64, true>(p, p.dv, st, false) : launch_bwd_dv<64, false>(p, p.dv, st, false))
-                          : (bf16 ? launch_bwd_dv<128, true>(p, p.dv, st, false) : launch_bwd_dv<128, false>(p, p.dv, st, false));
+            // whole sequences' checkpoints (the plain pass, on the side
+            // stream where there is one), then the split sequences' with
+            // their adjoint composites, the carry, and the reverse pass over
+            // every item once both checkpoint passes are done
+            std::lock_guard<std::mutex> lk(g_side_mu);
+            SideStream* sd = may_fork(st) ? side_stream() : nullptr;
+            hipStream_t ck = st;
+            if (sd != nullptr) {
+                hipError_t e = hipEventRecord(sd->fork, st);
+                if (e == hipSuccess) e = hipStreamWaitEvent(sd->s, sd->fork, 0);
+                if (e != hipSuccess) {
+                    note_hip_error(e);
+                    return KDN_EHIP;
+                }
+                ck = sd->s;
+            }
+            rc = dk == 64 ? (bf16 ? launch_bwd_dv<64, true>(p, p.dv, ck, false) : launch_bwd_dv<64, false>(p, p.dv, ck, false))
+                          : (bf16 ? launch_bwd_dv<128, true>(p, p.dv, ck, false) : launch_bwd_dv<128, false>(p, p.dv, ck, false));
             if (rc != KDN_OK) return rc;
-            rc = diag_bwd_seg_launch(p, dk, bf16, st);
+            if (sd != nullptr) {
+                const hipError_t e = hipEventRecord(sd->join, sd->s);
+                if (e != hipSuccess) {
+                    note_hip_error(e);
+                    return KDN_EHIP;
+                }
+            }
+            rc = diag_bwd_seg_launch(p, dk, bf16, st, sd != nullptr ? sd->join : nullptr);
         } else if (dk == 64) {
             rc = bf16 ? launch_bwd_dv<64, true>(p, p.dv, st) : launch_bwd_dv<64, false>(p, p.dv, st);
         } else {

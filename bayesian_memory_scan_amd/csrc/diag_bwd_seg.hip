@@ -61,7 +61,7 @@ __global__ __launch_bounds__(256) void k_bwd_adj_carry_varlen(BwdParams p, int64
 // checkpoints and adjoint composites, the adjoint carry, then the reverse
 // pass.
 template <int DK, int DV, bool BF16>
-static int launch_seg_shape(const BwdParams& p, hipStream_t st) {
+static int launch_seg_shape(const BwdParams& p, hipStream_t st, hipEvent_t join) {
     using Sh = BwdShape<DK, DV>;
     const int64_t g = p.cu_seqlens ? (p.vl_items * p.H + 7) / 8 * 8 * Sh::NTILE
                                    : p.BH * p.S * Sh::NTILE;
@@ -92,24 +92,31 @@ static int launch_seg_shape(const BwdParams& p, hipStream_t st) {
         hipLaunchKernelGGL(k_bwd_adj_carry, dim3(elem_groups(n)), dim3(256), 0, st, p, slot, n,
                            static_cast<int32_t>(Sh::NTILE));
     }
+    if (join != nullptr) {
+        const hipError_t e = hipStreamWaitEvent(st, join, 0);
+        if (e != hipSuccess) {
+            note_hip_error(e);
+            return KDN_EHIP;
+        }
+    }
     hipLaunchKernelGGL((k_diag_bwd<DK, DV, BF16, true>), grid, dim3(Sh::NTH), 0, st, p);
     return launch_status();
 }
 
 template <int DK, bool BF16>
-static int launch_seg_dv(const BwdParams& p, hipStream_t st) {
+static int launch_seg_dv(const BwdParams& p, hipStream_t st, hipEvent_t join) {
     switch (p.dv) {
-        case 16: return launch_seg_shape<DK, 16, BF16>(p, st);
-        case 32: return launch_seg_shape<DK, 32, BF16>(p, st);
-        case 64: return launch_seg_shape<DK, 64, BF16>(p, st);
-        case 128: return launch_seg_shape<DK, 128, BF16>(p, st);
+        case 16: return launch_seg_shape<DK, 16, BF16>(p, st, join);
+        case 32: return launch_seg_shape<DK, 32, BF16>(p, st, join);
+        case 64: return launch_seg_shape<DK, 64, BF16>(p, st, join);
+        case 128: return launch_seg_shape<DK, 128, BF16>(p, st, join);
         default: return KDN_EUNSUPPORTED;
     }
 }
 
-int diag_bwd_seg_launch(const BwdParams& p, int64_t dk, bool bf16, hipStream_t st) {
-    if (dk == 64) return bf16 ? launch_seg_dv<64, true>(p, st) : launch_seg_dv<64, false>(p, st);
-    return bf16 ? launch_seg_dv<128, true>(p, st) : launch_seg_dv<128, false>(p, st);
+int diag_bwd_seg_launch(const BwdParams& p, int64_t dk, bool bf16, hipStream_t st, hipEvent_t join) {
+    if (dk == 64) return bf16 ? launch_seg_dv<64, true>(p, st, join) : launch_seg_dv<64, false>(p, st, join);
+    return bf16 ? launch_seg_dv<128, true>(p, st, join) : launch_seg_dv<128, false>(p, st, join);
 }
 
 }  // namespace kdn

@@ -366,7 +366,9 @@ int diag_varlen_comp_launch(const DiagParams& p, int64_t dk, bool bf16, int32_t 
 int32_t bwd_token_split(int64_t rows, int64_t T);
 int diag_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t B, int64_t dk,
                     bool bf16, int32_t R, hipStream_t st);
-int diag_bwd_seg_launch(const BwdParams& p, int64_t dk, bool bf16, hipStream_t st);
+// join: where non-null, an event the reverse pass waits for on st (the
+// whole sequences' checkpoint pass of a packed batch, run on another stream)
+int diag_bwd_seg_launch(const BwdParams& p, int64_t dk, bool bf16, hipStream_t st, hipEvent_t join = nullptr);
 void varlen_plan_launch(const DiagParams& p, int32_t R, hipStream_t st);
 int diag_varlen_bwd_launch(const BwdParams& p, const DiagParams& prep, int64_t dk, bool bf16,
                            int32_t R, hipStream_t st);

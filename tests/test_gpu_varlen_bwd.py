@@ -201,3 +201,29 @@ def test_varlen_bwd_skewed_workload_sampled(kdn):
     print("varlen bwd skewed workload", flush=True)
     g = _run(kdn, inp, cu, d_o[0])
     _compare(g, inp, cu, d_o, None, [0, 40], (0, spec.H - 1), False, "skew")
+
+
+def test_varlen_bwd_split_streams(kdn):
+    """With split sequences the whole sequences' checkpoint pass runs on a
+    second stream and the reverse pass waits for it: repeated calls, on the
+    default stream and on a caller's stream, give bitwise equal gradients."""
+    H, dk, dv = 2, 128, 128
+    cu = np.concatenate([[0], np.cumsum(SPLIT_LENGTHS)]).astype(np.int64)
+    T, N = int(cu[-1]), len(SPLIT_LENGTHS)
+    spec = synth.VarlenSpec("varlen_bwd_streams", H, N, T, dk, dv, "bf16", 7993)
+    inp = synth.varlen_inputs(spec)
+    inp["cu_seqlens"] = cu
+    d_o = np.random.default_rng(7994).standard_normal((H, T, dv)).astype(np.float32)
+    x = {n: gu.dev_tensor(inp[n][0]) for n in ("q", "k", "v", "beta", "d")}
+    args = (x["q"], x["k"], x["v"], x["beta"], x["d"], gu.dev_tensor(inp["A"]), inp["I_prior"],
+            torch.from_numpy(cu).cuda(), gu.dev_tensor(d_o))
+    print("varlen bwd split streams", flush=True)
+    ref = {n: t.cpu() for n, t in kdn.kdn_diag_scan_varlen_bwd(*args).items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    for rep in range(3):
+        for s in (None, side):
+            g = kdn.kdn_diag_scan_varlen_bwd(*args, stream=s)
+            torch.cuda.synchronize()
+            for n in ref:
+                assert torch.equal(g[n].cpu(), ref[n]), (rep, s is not None, n)
