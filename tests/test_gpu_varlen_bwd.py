@@ -227,3 +227,51 @@ def test_varlen_bwd_split_streams(kdn):
             torch.cuda.synchronize()
             for n in ref:
                 assert torch.equal(g[n].cpu(), ref[n]), (rep, s is not None, n)
+
+
+def test_varlen_bwd_split_host_threads(kdn):
+    """Two host threads, each on its own stream, differentiate two different
+    split batches at once (the second stream's fork and join are one unit per
+    call): each result equals the same call made alone."""
+    import threading
+    H, dk, dv = 2, 128, 64
+    cu = np.concatenate([[0], np.cumsum(SPLIT_LENGTHS)]).astype(np.int64)
+    T, N = int(cu[-1]), len(SPLIT_LENGTHS)
+    jobs = []
+    for seed in (7995, 7997):
+        spec = synth.VarlenSpec("varlen_bwd_threads", H, N, T, dk, dv, "bf16", seed)
+        inp = synth.varlen_inputs(spec)
+        d_o = np.random.default_rng(seed + 1).standard_normal((H, T, dv)).astype(np.float32)
+        x = {n: gu.dev_tensor(inp[n][0]) for n in ("q", "k", "v", "beta", "d")}
+        jobs.append((x["q"], x["k"], x["v"], x["beta"], x["d"], gu.dev_tensor(inp["A"]), inp["I_prior"],
+                     torch.from_numpy(cu).cuda(), gu.dev_tensor(d_o)))
+    print("varlen bwd split host threads", flush=True)
+    alone = [{n: t.cpu() for n, t in kdn.kdn_diag_scan_varlen_bwd(*a).items()} for a in jobs]
+    streams = [torch.cuda.Stream() for _ in jobs]
+    for s in streams:
+        s.wait_stream(torch.cuda.current_stream())
+    out = [None, None]
+    errs = []
+
+    def work(i):
+        try:
+            res = []
+            for _ in range(4):
+                g = kdn.kdn_diag_scan_varlen_bwd(*jobs[i], stream=streams[i])
+                streams[i].synchronize()
+                res.append({n: t.cpu() for n, t in g.items()})
+            out[i] = res
+        except Exception as e:  # reported below, in the test's own thread
+            errs.append(repr(e))
+
+    th = [threading.Thread(target=work, args=(i,)) for i in range(2)]
+    for t in th:
+        t.start()
+    for t in th:
+        t.join(timeout=120)
+    assert not errs, errs
+    for i in range(2):
+        assert out[i] is not None, f"thread {i} did not finish"
+        for rep, g in enumerate(out[i]):
+            for n in alone[i]:
+                assert torch.equal(g[n], alone[i][n]), (i, rep, n)
