@@ -858,11 +858,26 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
     }
     __syncthreads();
 
-    // one reverse step: token tt of the staged chunk, (J, E) its state after the token
-    auto reverse_step = [&](const BwdStage<DK, CI, true>& S, int tt, int64_t t0, int Lc,
+    // A reverse step's LDS operands (token tt of the staged chunk: its frame
+    // scalars and the next token's, k_j, q_j, beta_c, v_c, dout_c), loaded
+    // apart from the step so that a recompute step can load them ahead.
+    struct RevRaw { float4 sct, scn; float k, q, b, v, g; };
+    auto rev_raw = [&](const BwdStage<DK, CI, true>& S, int tt) __attribute__((always_inline)) {
+        RevRaw r;
+        r.sct = S.sc[tt];
+        r.scn = S.sc[tt + 1];
+        r.k = S.k[tt][j];
+        r.q = S.q[tt][j];
+        r.b = S.b[tt][lc];
+        r.v = S.v[tt][lc];
+        r.g = S.g[tt][lc];
+        return r;
+    };
+    // one reverse step: token tt, (J, E) its state after the token
+    auto reverse_step = [&](const RevRaw& rr, int tt, int64_t t0, int Lc,
                             const float (&J)[16], const float (&E)[16]) __attribute__((always_inline)) {
         const int64_t t = t0 + tt;
-        const float4 sct = S.sc[tt];
+        const float4 sct = rr.sct;
         const float sIp = uniform(sct.z) * I_prior;     // s_t I_prior: I~ = J~ + s I_prior
         const bool has_next = t + 1 < run.t_end;
         {
@@ -879,7 +894,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             const float tot = wave_sum2(x1a + x1b, x2);
             if (lane == 0) xs[tt][w].x = tot;
             if (lane == 32) xs[tt][w].y = tot;
-            const float4 scn = S.sc[tt + 1];
+            const float4 scn = rr.scn;
             const float rho_n = has_next ? uniform(tt + 1 < Lc ? scn.x : scn.x / sct.z) : 1.0f;
             if (tid == 0 && has_next) {
                 // rho_{t+1} / alpha_{t+1}: 1 / s_t where token t+1 starts a frame
@@ -897,13 +912,13 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             }
         }
 
-        const float kj = S.k[tt][j];
-        const float qj = S.q[tt][j];
+        const float kj = rr.k;
+        const float qj = rr.q;
         const float k2j = kj * kj;
-        const float bc = dpp_src(S.b[tt][lc]);
-        const float bvc = dpp_src(S.b[tt][lc] * S.v[tt][lc]);
-        const float gc = dpp_src(S.g[tt][lc]);
-        const float ngc = dpp_src(-S.g[tt][lc]);
+        const float bc = dpp_src(rr.b);
+        const float bvc = dpp_src(rr.b * rr.v);
+        const float gc = dpp_src(rr.g);
+        const float ngc = dpp_src(-rr.g);
         float dq4[4], dka[2], dkb[2];
         // The row sums P_c = sum_j M k_j^2 and Q_c = sum_j L k_j are folded into
         // the 64-lane butterfly as soon as column c is done (the first two
@@ -959,23 +974,60 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             // indices and stage offsets are constants)
             using RS = RecSchedule<HELD>;
             float sJ[HELD][16], sE[HELD][16];
+            // a step's LDS operands: frame scalars (rho, s), k_j, beta_c, v_c
+            struct Raw { float scx, scz, k, b, v; };
+            auto raw = [&](int tt) __attribute__((always_inline)) {
+                Raw r;
+                const float4 sc = S.sc[tt];
+                r.scx = sc.x;
+                r.scz = sc.z;
+                r.k = S.k[tt][j];
+                r.b = S.b[tt][lc];
+                r.v = S.v[tt][lc];
+                return r;
+            };
+            Raw pre{};
+            RevRaw rpre{};
             Unroll<0, RS::N>::run([&](auto ii) {
-                constexpr RecOp op = RS::ops[decltype(ii)::value];
+                constexpr int i = decltype(ii)::value;
+                constexpr RecOp op = RS::ops[i];
                 if constexpr (op.kind == kRecLoad) {
                     load_ckpt<Sh::BLK>(ck, lid, sJ[op.dst], sE[op.dst]);
                 } else if constexpr (op.kind == kRecStep) {
-                    float rho, bs, bvs, kj;
-                    operands(op.tok, rho, bs, bvs, kj);
+                    // A step right after a step finds its operands loaded; a
+                    // step right before a step or a reverse step loads that
+                    // one's before its own arithmetic, so their LDS latency
+                    // overlaps it.
+                    constexpr int ip = i > 0 ? i - 1 : 0;
+                    constexpr int in = i + 1 < RS::N ? i + 1 : i;
+                    constexpr bool pre_in = i > 0 && RS::ops[ip].kind == kRecStep;
+                    constexpr bool pre_out = i + 1 < RS::N && RS::ops[in].kind == kRecStep;
+                    constexpr bool pre_rev = i + 1 < RS::N && RS::ops[in].kind == kRecRev;
+                    Raw o;
+                    if constexpr (pre_in) o = pre;
+                    else o = raw(op.tok);
+                    if constexpr (pre_out) pre = raw(RS::ops[in].tok);
+                    if constexpr (pre_rev) rpre = rev_raw(S, RS::ops[in].tok);
+                    const float rho = o.scx;
+                    const float kj = o.k;
+                    const float bb = o.b * o.scz;
+                    const float bvs = dpp_src(bb * o.v);
+                    const float bs = dpp_src(bb);
                     if constexpr (op.src == op.dst)
                         bwd_step_inplace(sJ[op.dst], sE[op.dst], rho, bs, bvs, kj, kj * kj);
                     else
                         bwd_step_copy(sJ[op.src], sE[op.src], sJ[op.dst], sE[op.dst], rho, bs, bvs, kj,
                                       kj * kj);
                 } else {
-                    reverse_step(S, op.tok, t0, Lc, sJ[op.src], sE[op.src]);
+                    constexpr int ip = i > 0 ? i - 1 : 0;
+                    if constexpr (i > 0 && RS::ops[ip].kind == kRecStep)
+                        reverse_step(rpre, op.tok, t0, Lc, sJ[op.src], sE[op.src]);
+                    else
+                        reverse_step(rev_raw(S, op.tok), op.tok, t0, Lc, sJ[op.src], sE[op.src]);
                 }
-                // keep each op's loads and temporaries within the op: hoisting
-                // across ops raises register pressure past the budget
+                // keep each op's loads and temporaries within the op (beyond
+                // the prefetch above): hoisting across ops raises register
+                // pressure past the budget
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
@@ -1019,7 +1071,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             Unroll<0, HELD>::run([&](auto uu) {
                 constexpr int u = HELD - 1 - decltype(uu)::value;
                 const int tt = HELD * m + u;
-                if (tt < Lc) reverse_step(S, tt, t0, Lc, sJ[u], sE[u]);
+                if (tt < Lc) reverse_step(rev_raw(S, tt), tt, t0, Lc, sJ[u], sE[u]);
             });
         }
 
