@@ -952,6 +952,9 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                                      2.0f * kj * (dka[0] + dka[1]) + (dkb[0] + dkb[1]));
     };
 
+    // the state slots of the whole-chunk schedule; slot 0 of chunk c - 1 is
+    // loaded from its checkpoint at the end of chunk c
+    float sJ[HELD][16], sE[HELD][16];
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int b = static_cast<int>((nch - 1 - c) & 1);
         const BwdStage<DK, CI, true>& S = stg[b];
@@ -973,7 +976,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             // a whole chunk: the fixed recompute schedule, unrolled (slot
             // indices and stage offsets are constants)
             using RS = RecSchedule<HELD>;
-            float sJ[HELD][16], sE[HELD][16];
+            static_assert(RS::ops[0].kind == kRecLoad && RS::ops[0].dst == 0,
+                          "a whole chunk starts by loading its checkpoint into slot 0");
             // a step's LDS operands: frame scalars (rho, s), k_j, beta_c, v_c
             struct Raw { float scx, scz, k, b, v; };
             auto raw = [&](int tt) __attribute__((always_inline)) {
@@ -992,7 +996,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 constexpr int i = decltype(ii)::value;
                 constexpr RecOp op = RS::ops[i];
                 if constexpr (op.kind == kRecLoad) {
-                    load_ckpt<Sh::BLK>(ck, lid, sJ[op.dst], sE[op.dst]);
+                    // the first load was made at the end of chunk c + 1
+                    if (i > 0 || c == nch - 1) load_ckpt<Sh::BLK>(ck, lid, sJ[op.dst], sE[op.dst]);
                 } else if constexpr (op.kind == kRecStep) {
                     // A step right after a step finds its operands loaded; a
                     // step right before a step or a reverse step loads that
@@ -1035,8 +1040,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
         // the ragged last chunk: groups of HELD consecutive states, each
         // rebuilt from the checkpoint
         for (int m = Lc == C ? -1 : nheld - 1; m >= 0; --m) {
-            float sJ[HELD][16], sE[HELD][16];
-            load_ckpt<Sh::BLK>(ck, lid, sJ[0], sE[0]);
+            float gJ[HELD][16], gE[HELD][16];
+            load_ckpt<Sh::BLK>(ck, lid, gJ[0], gE[0]);
             {
                 // software-pipelined like the checkpoint pass
                 const int n = HELD * m;
@@ -1048,7 +1053,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                     const float kj_n = S.k[tn][j], bj_n = S.b[tn][lc], vj_n = S.v[tn][lc];
                     const float b = bj * scx.y;
                     const float bvs = dpp_src(b * vj);
-                    bwd_step_inplace(sJ[0], sE[0], scx.x, dpp_src(b), bvs, kj, kj * kj);
+                    bwd_step_inplace(gJ[0], gE[0], scx.x, dpp_src(b), bvs, kj, kj * kj);
                     scx = scx_n;
                     kj = kj_n;
                     bj = bj_n;
@@ -1062,19 +1067,22 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                     float rho, bs, bvs, kj;
                     operands(tt, rho, bs, bvs, kj);
                     if constexpr (u == 0)
-                        bwd_step_inplace(sJ[0], sE[0], rho, bs, bvs, kj, kj * kj);
+                        bwd_step_inplace(gJ[0], gE[0], rho, bs, bvs, kj, kj * kj);
                     else
-                        bwd_step_copy(sJ[u - 1], sE[u - 1], sJ[u], sE[u], rho, bs, bvs, kj, kj * kj);
+                        bwd_step_copy(gJ[u - 1], gE[u - 1], gJ[u], gE[u], rho, bs, bvs, kj, kj * kj);
                 }
                 __builtin_amdgcn_sched_barrier(0);
             });
             Unroll<0, HELD>::run([&](auto uu) {
                 constexpr int u = HELD - 1 - decltype(uu)::value;
                 const int tt = HELD * m + u;
-                if (tt < Lc) reverse_step(rev_raw(S, tt), tt, t0, Lc, sJ[u], sE[u]);
+                if (tt < Lc) reverse_step(rev_raw(S, tt), tt, t0, Lc, gJ[u], gE[u]);
             });
         }
 
+        // the next chunk (c - 1, a whole one) starts from its checkpoint in
+        // slot 0: its load flies through the barrier and the outputs below
+        if (c > 0) load_ckpt<Sh::BLK>(ck_at<Sh::BLK>(run, c - 1), lid, sJ[0], sE[0]);
         __syncthreads();
         // the previous chunk's loads fly while this chunk's outputs are written
         if (c > 0) fetch(c - 1);
