@@ -648,24 +648,6 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         const int L = chunk_len(c);
         const int64_t t0 = t_begin + c * C;
         const Stage& S = stg[b];
-        const uint32_t restarts = __builtin_amdgcn_readfirstlane(S.restarts);
-
-        // Grouped read-out for this chunk: every precision of the wave stays
-        // below 2^24 if the largest now, or I_prior, plus the chunk's largest
-        // growth does.
-        bool quad;
-        {
-            seen_k = __uint_as_float(run_max[0]);
-            seen_b = __uint_as_float(run_max[1]);
-            const float lim = kQuadHi - static_cast<float>(C) * seen_k * seen_b;
-            float hi = I_prior;
-#pragma unroll
-            for (int r = 0; r < RB; ++r)
-#pragma unroll
-                for (int cc = 0; cc < 2; ++cc) hi = fmaxf(hi, I[r][cc]);
-            quad = quad_ok && __builtin_amdgcn_ballot_w64(!(hi + I_prior <= lim)) == 0;
-        }
-
         // A token's operands: RB key rows of s k, k^2 and q / s (shared by
         // half a wave), the lane's (beta, beta v) column pair and the token's
         // (alpha, P).
@@ -689,6 +671,31 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
             o.ap = S.ap[tt];
             return o;
         };
+        // The chunk's first operands are read with its flags, so that their
+        // latency overlaps the flag reads and the range check below (not at
+        // d_k = 64 in fp32, whose registers would then exceed 128 and halve
+        // the workgroups per CU).
+        constexpr bool kFirstEarly = BF16 || DK == 128;
+        Ops op0{};
+        if constexpr (kFirstEarly) op0 = load_ops(0);
+        const uint32_t restarts = __builtin_amdgcn_readfirstlane(S.restarts);
+
+        // Grouped read-out for this chunk: every precision of the wave stays
+        // below 2^24 if the largest now, or I_prior, plus the chunk's largest
+        // growth does.
+        bool quad;
+        {
+            seen_k = __uint_as_float(run_max[0]);
+            seen_b = __uint_as_float(run_max[1]);
+            const float lim = kQuadHi - static_cast<float>(C) * seen_k * seen_b;
+            float hi = I_prior;
+#pragma unroll
+            for (int r = 0; r < RB; ++r)
+#pragma unroll
+                for (int cc = 0; cc < 2; ++cc) hi = fmaxf(hi, I[r][cc]);
+            quad = quad_ok && __builtin_amdgcn_ballot_w64(!(hi + I_prior <= lim)) == 0;
+        }
+
         auto lane_of = [](const float4& v, int e) { return e == 0 ? v.x : e == 1 ? v.y : e == 2 ? v.z : v.w; };
         // read-out of column cc over the lane's RB rows, four rows per reciprocal
         auto readout_quad = [&](const Ops& o, int cc) __attribute__((always_inline)) {
@@ -755,7 +762,9 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
             // (the usual case): that rescale goes first, then the tokens run
             // unrolled and branch-free, each token's LDS operands loaded while
             // the previous token computes
-            Ops cur = load_ops(0);
+            Ops cur;
+            if constexpr (kFirstEarly) cur = op0;
+            else cur = load_ops(0);
             if (restarts & 1u) {
 #pragma unroll
                 for (int r = 0; r < RB; ++r)
@@ -770,7 +779,8 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
                 if constexpr (tt + 1 < C) cur = nxt;
             });
         } else {
-            for (int tt = 0; tt < L; ++tt) token(tt, load_ops(tt), true);
+            if constexpr (kFirstEarly) token(0, op0, true);
+            for (int tt = kFirstEarly ? 1 : 0; tt < L; ++tt) token(tt, load_ops(tt), true);
         }
 
         if (c + 1 < nch) commit(b ^ 1, chunk_len(c + 1));
