@@ -952,9 +952,6 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                                      2.0f * kj * (dka[0] + dka[1]) + (dkb[0] + dkb[1]));
     };
 
-    // the state slots of the whole-chunk schedule; slot 0 of chunk c - 1 is
-    // loaded from its checkpoint at the end of chunk c
-    float sJ[HELD][16], sE[HELD][16];
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int b = static_cast<int>((nch - 1 - c) & 1);
         const BwdStage<DK, CI, true>& S = stg[b];
@@ -976,8 +973,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             // a whole chunk: the fixed recompute schedule, unrolled (slot
             // indices and stage offsets are constants)
             using RS = RecSchedule<HELD>;
-            static_assert(RS::ops[0].kind == kRecLoad && RS::ops[0].dst == 0,
-                          "a whole chunk starts by loading its checkpoint into slot 0");
+            float sJ[HELD][16], sE[HELD][16];
             // a step's LDS operands: frame scalars (rho, s), k_j, beta_c, v_c
             struct Raw { float scx, scz, k, b, v; };
             auto raw = [&](int tt) __attribute__((always_inline)) {
@@ -996,8 +992,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 constexpr int i = decltype(ii)::value;
                 constexpr RecOp op = RS::ops[i];
                 if constexpr (op.kind == kRecLoad) {
-                    // the first load was made at the end of chunk c + 1
-                    if (i > 0 || c == nch - 1) load_ckpt<Sh::BLK>(ck, lid, sJ[op.dst], sE[op.dst]);
+                    load_ckpt<Sh::BLK>(ck, lid, sJ[op.dst], sE[op.dst]);
                 } else if constexpr (op.kind == kRecStep) {
                     // A step right after a step finds its operands loaded; a
                     // step right before a step or a reverse step loads that
@@ -1080,14 +1075,13 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             });
         }
 
-        // the next chunk (c - 1, a whole one) starts from its checkpoint in
-        // slot 0: its load flies through the barrier and the outputs below
-        if (c > 0) load_ckpt<Sh::BLK>(ck_at<Sh::BLK>(run, c - 1), lid, sJ[0], sE[0]);
         __syncthreads();
         // the previous chunk's loads fly while this chunk's outputs are written
         if (c > 0) fetch(c - 1);
 
-        // ---- chunk outputs ----
+        // ---- chunk outputs ---- (written once and read only by later
+        // passes: non-temporal, so that they do not push this pass's chunk
+        // checkpoints, read up to three times, out of L2)
         const int64_t tokbase = run.tbase + t0;                   // token index into the token axis
         for (int e = tid; e < Lc * CI; e += NTH) {
             const int tt = e / CI;
@@ -1104,8 +1098,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
             const float bi = S.b[tt][ci];
             const float vi = S.v[tt][ci];
             const int64_t o = (tokbase + tt) * p.dv + tile * CI + ci;
-            if (p.dbeta) p.dbeta[o] = s * fmaf(vi, Q, P);
-            p.dv_out[o] = s * bi * Q;
+            if (p.dbeta) __builtin_nontemporal_store(s * fmaf(vi, Q, P), &p.dbeta[o]);
+            __builtin_nontemporal_store(s * bi * Q, &p.dv_out[o]);
         }
         if (!p.beta) {
             // Palimpsa-M gating: beta_t[i] = d_t, so d_t collects sum_i dbeta_t[i]
@@ -1135,8 +1129,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 sk += x.y;
             }
             const int64_t o = (tokbase + tt) * DK + jj;
-            part_dq[o] = sq;
-            part_dk[o] = sk * S.sc[tt].z;
+            __builtin_nontemporal_store(sq, &part_dq[o]);
+            __builtin_nontemporal_store(sk * S.sc[tt].z, &part_dk[o]);
         }
         for (int tt = tid; tt < Lc; tt += NTH) {
             if (t0 + tt + 1 < run.t_end) {
