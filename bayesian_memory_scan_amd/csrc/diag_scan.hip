@@ -393,8 +393,12 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
     constexpr int W = DK / (2 * RB);     // waves: 2*RB key rows each
     constexpr int NTH = W * kWave;
     constexpr int P = W;                 // row groups of the read-out: one per wave
-    // partial read-outs double-buffered while they fit next to the stage
-    constexpr int NOB = W > 8 ? 1 : 2;
+    // Partial read-outs double-buffered (no second barrier per chunk) only
+    // where two workgroups still fit in a CU's 160 KB of LDS: at d_k = 64 a
+    // second buffer would leave one 8-wave workgroup per CU, half the waves.
+    constexpr int kStageBytes = (3 * C * DK + 2 * C * CI + 4 * C + 4) * 4;
+    constexpr int kPartBytes = C * P * CI * 4;
+    constexpr int NOB = W <= 8 && 2 * (2 * kStageBytes + 2 * kPartBytes) <= 160 * 1024 ? 2 : 1;
     constexpr int VW = BF16 ? 8 : 4;
     constexpr int VK = C * DK / VW;
     constexpr int VB = C * CI / VW;
@@ -416,6 +420,7 @@ __global__ __launch_bounds__(DK / (2 * RB) * kWave) void k_diag_blk(DiagParams p
         float4 ap[C];       // (alpha_t, (1 - alpha_t) I_prior, rho_t of the eta frame, -)
         uint32_t restarts;  // bit t: token t restarts the eta frame (rho_t != 1)
     };
+    static_assert(sizeof(Stage) == kStageBytes, "stage size used to choose the partial buffers");
     __shared__ Stage stg[2];
     __shared__ float opart[NOB][C][P][CI];
     // running maxima of k^2 and beta over every token staged so far, as the
