@@ -196,9 +196,9 @@ struct BwdShape {
     static constexpr int NTH = W * kWave;
     static constexpr int NTILE = DV / CI;
     static constexpr int BLK = DK * CI;                // floats of one checkpoint half
-    // token states held in registers at once: 4, or 3 where two waves share a
-    // SIMD (256 registers per lane)
-    static constexpr int HELD = W > 4 ? 3 : 4;
+    // token states held in registers at once: 3, so that two waves share a
+    // SIMD (256 registers per lane) at every tile shape
+    static constexpr int HELD = 3;
     static_assert(DK == 64 || DK == 128, "key rows: one or two waves of 64");
 };
 
@@ -210,6 +210,15 @@ struct BwdStage {
     float v[kBwdChunk][CI];
     float g[REV ? kBwdChunk : 1][CI];      // dout
     float4 sc[kBwdChunk + 1];              // frame scalars; [L] = next chunk's first token
+};
+
+// The reverse pass's q and dout of a chunk, single-buffered: the output sums
+// between its two barriers do not read them, so the next chunk's can be
+// written there (8 KB at d_k = 64, enough for two workgroups per CU).
+template <int DK, int CI>
+struct BwdQG {
+    float q[kBwdChunk][DK];
+    float g[kBwdChunk][CI];                // dout
 };
 
 // One 16-byte vector of a column tile's own operands (beta, v, dout), read
@@ -286,7 +295,8 @@ struct BwdLoader {
         }
     }
 
-    __device__ __forceinline__ void commit(BwdStage<DK, CI, REV>& S, int L, int tid) {
+    template <class St>
+    __device__ __forceinline__ void commit_parts(St& S, float (*qd)[DK], float (*gd)[CI], int L, int tid) {
 #pragma unroll
         for (int n = 0; n < NVK; ++n) {
             const int vi = tid + n * NTH;
@@ -300,7 +310,7 @@ struct BwdLoader {
                 if constexpr (REV) {
                     widen<BF16>(rq[n], f);
 #pragma unroll
-                    for (int e = 0; e < VW; ++e) S.q[row][c0 + e] = f[e];
+                    for (int e = 0; e < VW; ++e) qd[row][c0 + e] = f[e];
                 }
             }
         }
@@ -326,10 +336,17 @@ struct BwdLoader {
                 const int vi = tid + n * NTH;
                 const int row = vi / (CI / 4);
                 const int c0 = (vi % (CI / 4)) * 4;
-                if (vi < VG && row < L) *reinterpret_cast<float4*>(&S.g[row][c0]) = rg[n];
+                if (vi < VG && row < L) *reinterpret_cast<float4*>(&gd[row][c0]) = rg[n];
             }
         }
         if (tid <= L) S.sc[tid] = rsc;
+    }
+    __device__ __forceinline__ void commit(BwdStage<DK, CI, REV>& S, int L, int tid) {
+        commit_parts(S, S.q, S.g, L, tid);
+    }
+    // the reverse pass: q and dout into their own single buffer
+    __device__ __forceinline__ void commit(BwdStage<DK, CI, false>& S, BwdQG<DK, CI>& X, int L, int tid) {
+        commit_parts(S, X.q, X.g, L, tid);
     }
 };
 
@@ -773,7 +790,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd_ckpt(BwdPa
 // SEG: rows cut into segments (p.S > 1), a separate instantiation so that
 // the unsegmented kernel carries none of its prologue and epilogue code.
 template <int DK, int DV, bool BF16, bool SEG>
-__global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams p) {
+__global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) __attribute__((amdgpu_waves_per_eu(2)))
+void k_diag_bwd(BwdParams p) {
     using Sh = BwdShape<DK, DV>;
     constexpr int C = kBwdChunk;
     constexpr int CI = Sh::CI;
@@ -782,7 +800,8 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
     constexpr int W = Sh::W;
     constexpr int NTH = Sh::NTH;
     constexpr int HELD = Sh::HELD;
-    __shared__ BwdStage<DK, CI, true> stg[2];
+    __shared__ BwdStage<DK, CI, false> stg[2];
+    __shared__ BwdQG<DK, CI> qg;
     __shared__ float2 dqk[C][CG][DK];          // per-wave dq and (dk / s) partial sums
     __shared__ float pq[C][RH][CG][32];        // per-wave sums over rows: P (0..15), Q (16..31)
     __shared__ float2 xs[C][W];                // per-wave dalpha sums (X1, X2) of token t + 1
@@ -826,7 +845,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
 
     if (nch > 0) {
         fetch(nch - 1);
-        ld.commit(stg[0], chunk_len(nch - 1), tid);
+        ld.commit(stg[0], qg, chunk_len(nch - 1), tid);
         const float inv_s = 1.0f / uniform(p.scal[run.tbase + run.t_end - 1].z);
         if (SEG && !run.last) {
             // a segment before the last: the adjoint flowing into its end,
@@ -862,15 +881,15 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
     // scalars and the next token's, k_j, q_j, beta_c, v_c, dout_c), loaded
     // apart from the step so that a recompute step can load them ahead.
     struct RevRaw { float4 sct, scn; float k, q, b, v, g; };
-    auto rev_raw = [&](const BwdStage<DK, CI, true>& S, int tt) __attribute__((always_inline)) {
+    auto rev_raw = [&](const BwdStage<DK, CI, false>& S, int tt) __attribute__((always_inline)) {
         RevRaw r;
         r.sct = S.sc[tt];
         r.scn = S.sc[tt + 1];
         r.k = S.k[tt][j];
-        r.q = S.q[tt][j];
+        r.q = qg.q[tt][j];
         r.b = S.b[tt][lc];
         r.v = S.v[tt][lc];
-        r.g = S.g[tt][lc];
+        r.g = qg.g[tt][lc];
         return r;
     };
     // one reverse step: token tt, (J, E) its state after the token
@@ -954,7 +973,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int b = static_cast<int>((nch - 1 - c) & 1);
-        const BwdStage<DK, CI, true>& S = stg[b];
+        const BwdStage<DK, CI, false>& S = stg[b];
         const int Lc = chunk_len(c);
         const int64_t t0 = run.t_begin + c * C;
         const float* ck = ck_at<Sh::BLK>(run, c);
@@ -1145,7 +1164,7 @@ __global__ __launch_bounds__((BwdShape<DK, DV>::NTH)) void k_diag_bwd(BwdParams 
                 part_dip[tokbase + tt + 1] = f.y * X2;
             }
         }
-        if (c > 0) ld.commit(stg[b ^ 1], chunk_len(c - 1), tid);
+        if (c > 0) ld.commit(stg[b ^ 1], qg, chunk_len(c - 1), tid);
         __syncthreads();
     }
 
