@@ -212,9 +212,10 @@ struct BwdStage {
     float4 sc[kBwdChunk + 1];              // frame scalars; [L] = next chunk's first token
 };
 
-// The reverse pass's q and dout of a chunk, single-buffered: the output sums
-// between its two barriers do not read them, so the next chunk's can be
-// written there (8 KB at d_k = 64, enough for two workgroups per CU).
+// The reverse pass's q and dout of a chunk, single-buffered where the space
+// counts: the output sums between the chunk's two barriers do not read them,
+// so the next chunk's can be written there (8 KB less at d_k = 64, enough
+// for two workgroups per CU).
 template <int DK, int CI>
 struct BwdQG {
     float q[kBwdChunk][DK];
@@ -800,8 +801,13 @@ void k_diag_bwd(BwdParams p) {
     constexpr int W = Sh::W;
     constexpr int NTH = Sh::NTH;
     constexpr int HELD = Sh::HELD;
-    __shared__ BwdStage<DK, CI, false> stg[2];
-    __shared__ BwdQG<DK, CI> qg;
+    // q and dout single-buffered where that makes room for a second
+    // workgroup per CU (4 or fewer waves); with 8 waves, one workgroup fills
+    // the CU anyway and they stay in the double-buffered stage
+    constexpr bool QG1 = W <= 4;
+    using Stage = BwdStage<DK, CI, !QG1>;
+    __shared__ Stage stg[2];
+    __shared__ BwdQG<QG1 ? DK : 1, QG1 ? CI : 1> qg;
     __shared__ float2 dqk[C][CG][DK];          // per-wave dq and (dk / s) partial sums
     __shared__ float pq[C][RH][CG][32];        // per-wave sums over rows: P (0..15), Q (16..31)
     __shared__ float2 xs[C][W];                // per-wave dalpha sums (X1, X2) of token t + 1
@@ -815,6 +821,10 @@ void k_diag_bwd(BwdParams p) {
     const int cg = w % CG;
     const int j = rh * 64 + lane;
     const int lc = cg * 16 + (lane & 15);
+    auto commit_stage = [&](int bb, int L) __attribute__((always_inline)) {
+        if constexpr (QG1) ld.commit(stg[bb], qg, L, tid);
+        else ld.commit(stg[bb], L, tid);
+    };
     const BwdRun run = bwd_run<Sh::BLK, Sh::NTILE, SEG>(p);
     if (!run.valid) return;
     const int tile = run.tile;
@@ -845,7 +855,7 @@ void k_diag_bwd(BwdParams p) {
 
     if (nch > 0) {
         fetch(nch - 1);
-        ld.commit(stg[0], qg, chunk_len(nch - 1), tid);
+        commit_stage(0, chunk_len(nch - 1));
         const float inv_s = 1.0f / uniform(p.scal[run.tbase + run.t_end - 1].z);
         if (SEG && !run.last) {
             // a segment before the last: the adjoint flowing into its end,
@@ -881,15 +891,17 @@ void k_diag_bwd(BwdParams p) {
     // scalars and the next token's, k_j, q_j, beta_c, v_c, dout_c), loaded
     // apart from the step so that a recompute step can load them ahead.
     struct RevRaw { float4 sct, scn; float k, q, b, v, g; };
-    auto rev_raw = [&](const BwdStage<DK, CI, false>& S, int tt) __attribute__((always_inline)) {
+    auto rev_raw = [&](const Stage& S, int tt) __attribute__((always_inline)) {
         RevRaw r;
         r.sct = S.sc[tt];
         r.scn = S.sc[tt + 1];
         r.k = S.k[tt][j];
-        r.q = qg.q[tt][j];
+        if constexpr (QG1) r.q = qg.q[tt][j];
+        else r.q = S.q[tt][j];
         r.b = S.b[tt][lc];
         r.v = S.v[tt][lc];
-        r.g = qg.g[tt][lc];
+        if constexpr (QG1) r.g = qg.g[tt][lc];
+        else r.g = S.g[tt][lc];
         return r;
     };
     // one reverse step: token tt, (J, E) its state after the token
@@ -973,7 +985,7 @@ void k_diag_bwd(BwdParams p) {
 
     for (int64_t c = nch - 1; c >= 0; --c) {
         const int b = static_cast<int>((nch - 1 - c) & 1);
-        const BwdStage<DK, CI, false>& S = stg[b];
+        const Stage& S = stg[b];
         const int Lc = chunk_len(c);
         const int64_t t0 = run.t_begin + c * C;
         const float* ck = ck_at<Sh::BLK>(run, c);
@@ -1164,7 +1176,7 @@ void k_diag_bwd(BwdParams p) {
                 part_dip[tokbase + tt + 1] = f.y * X2;
             }
         }
-        if (c > 0) ld.commit(stg[b ^ 1], qg, chunk_len(c - 1), tid);
+        if (c > 0) commit_stage(b ^ 1, chunk_len(c - 1));
         __syncthreads();
     }
 
