@@ -27,7 +27,8 @@
  *     o_t[i] = sum_j q_t[j] mu_t[j][i], taken after token t's update.
  *   - Calls enqueue kernels on `stream` (a hipStream_t passed as void*;
  *     NULL = the default stream) and return without synchronising.  The
- *     library never allocates device memory.
+ *     library never allocates device memory (the packed-batch gradient keeps
+ *     one extra stream and two events per device, see there).
  *   - Arguments are validated before any HIP call; a rejected call touches
  *     no memory.  Return values: KDN_OK or a negative KDN_E* code (see
  *     kdn_status_string).  Values inside tensors are not checked: they are
@@ -218,6 +219,14 @@ int kdn_diag_scan_bwd(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v,
  *   (query with workspace == NULL): frame scalars, the plan, checkpoints
  *   (8 bytes per state entry per 16 tokens of each sequence, plus one final
  *   state per sequence) and per-token partial sums.  Deterministic.
+ * Streams: where the batch can hold sequences longer than a fair share of
+ *   the chip, the whole sequences' checkpoint pass runs on a second stream
+ *   of the current device, forked from `stream` and joined back before the
+ *   reverse pass; all later work is ordered on `stream` as usual.  That
+ *   stream and its two events are created on the first such call on a device
+ *   (default priority) and kept until the process ends.  A `stream` under
+ *   graph capture does not fork.  The current device must be the device of
+ *   `stream`.
  */
 int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k, int64_t d_v,
                              kdn_dtype in_dtype, const int64_t* cu_seqlens,
