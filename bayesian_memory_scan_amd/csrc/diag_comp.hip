@@ -50,7 +50,7 @@ int comp_tiles(int64_t dk, int64_t dv, bool bf16) {
     if (!bf16) return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1;
     const int64_t tr = dk > kCompBfEdge ? dk / kCompBfEdge : 1;
     const int64_t tc = dv > kCompBfEdge ? dv / kCompBfEdge : 1;
-    return static_cast<int>(tr * tc);
+    return static_cast<int>(2 * tr * tc);   // a J wave and an X wave per tile
 }
 
 // Composite unit `rest` (the column tile taken out): its token row bh,
@@ -315,8 +315,8 @@ __device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off
     }
 }
 
-template <int DK, int DV>
-__global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R) {
+template <int DK, int DV, int PART>
+__device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int64_t unit, int tile) {
     constexpr int KB = 32;                                     // tokens per k-step
     constexpr int MT = (DK > kCompBfEdge ? kCompBfEdge : DK) / 16;
     constexpr int NT = (DV > kCompBfEdge ? kCompBfEdge : DV) / 16;
@@ -330,13 +330,11 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
     const int lane = threadIdx.x;
     const int g = lane >> 4;
     const int c = lane & 15;
-    const int64_t id = xcd_local_id();       // a sub-segment's tiles share an XCD
-    const int tile = static_cast<int>(id % TILES);
     CompUnit u;
-    if (!comp_unit(p, id / TILES, R, u)) return;
+    if (!comp_unit(p, unit, R, u)) return;
     const int64_t bh = u.bh;
     const int64_t t_begin = u.t_begin, t_end = u.t_end;
-    if (lane == 0) echo_bounds(p, blockIdx.x, 2, u.run, u.seg, u.sub, t_begin, t_end, tile, u.sq);
+    if (lane == 0) echo_bounds(p, blockIdx.x, 2, u.run, u.seg, u.sub, t_begin, t_end, 2 * tile + PART, u.sq);
     const int rb = (tile / TC) * 16 * MT;    // first key row of the wave tile
     const int cb = (tile % TC) * 16 * NT;    // first value column
     const int64_t DV_ = p.dv;
@@ -383,7 +381,7 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int s_ = 8 * g + e;
-            buf_words<BW>(rv, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.v[e]);
+            if constexpr (PART == 1) buf_words<BW>(rv, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.v[e]);
             if (bth) {
                 buf_words<BW>(rb_, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.b[e]);
             } else {
@@ -420,14 +418,17 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int e0 = 2 * q, e1 = 2 * q + 1;
-                Bb[n][q] = bf_bits(x.b[e0], n) | (bf_bits(x.b[e1], n) << 16);
-                const float ya = w[e0] * (bf_elem(x.b[e0], n) * bf_elem(x.v[e0], n));
-                const float yb = w[e1] * (bf_elem(x.b[e1], n) * bf_elem(x.v[e1], n));
-                uint32_t l0, l1, l2;
-                split3(ya, yb, l0, l1, l2);
-                B0[n][q] = l0;
-                B1[n][q] = l1;
-                B2[n][q] = l2;
+                if constexpr (PART == 0) {
+                    Bb[n][q] = bf_bits(x.b[e0], n) | (bf_bits(x.b[e1], n) << 16);
+                } else {
+                    const float ya = w[e0] * (bf_elem(x.b[e0], n) * bf_elem(x.v[e0], n));
+                    const float yb = w[e1] * (bf_elem(x.b[e1], n) * bf_elem(x.v[e1], n));
+                    uint32_t l0, l1, l2;
+                    split3(ya, yb, l0, l1, l2);
+                    B0[n][q] = l0;
+                    B1[n][q] = l1;
+                    B2[n][q] = l2;
+                }
             }
         load_bv(tn, x);
         // A operands row tile by row tile: k (exact) and the limbs of w k^2
@@ -437,28 +438,31 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int e0 = 2 * q, e1 = 2 * q + 1;
-                Ak[q] = bf_bits(x.k[e0], m) | (bf_bits(x.k[e1], m) << 16);
-                const float ka = bf_elem(x.k[e0], m), kb = bf_elem(x.k[e1], m);
-                uint32_t l0, l1, l2;
-                split3(w[e0] * (ka * ka), w[e1] * (kb * kb), l0, l1, l2);
-                A0[q] = l0;
-                A1[q] = l1;
-                A2[q] = l2;
+                if constexpr (PART == 1) {
+                    Ak[q] = bf_bits(x.k[e0], m) | (bf_bits(x.k[e1], m) << 16);
+                } else {
+                    const float ka = bf_elem(x.k[e0], m), kb = bf_elem(x.k[e1], m);
+                    uint32_t l0, l1, l2;
+                    split3(w[e0] * (ka * ka), w[e1] * (kb * kb), l0, l1, l2);
+                    A0[q] = l0;
+                    A1[q] = l1;
+                    A2[q] = l2;
+                }
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                J[m][n] = mfma_bf(A0, Bb[n], J[m][n]);
-                X[m][n] = mfma_bf(Ak, B0[n], X[m][n]);
+                if constexpr (PART == 0) J[m][n] = mfma_bf(A0, Bb[n], J[m][n]);
+                else X[m][n] = mfma_bf(Ak, B0[n], X[m][n]);
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                J[m][n] = mfma_bf(A1, Bb[n], J[m][n]);
-                X[m][n] = mfma_bf(Ak, B1[n], X[m][n]);
+                if constexpr (PART == 0) J[m][n] = mfma_bf(A1, Bb[n], J[m][n]);
+                else X[m][n] = mfma_bf(Ak, B1[n], X[m][n]);
             }
 #pragma unroll
             for (int n = 0; n < NT; ++n) {
-                J[m][n] = mfma_bf(A2, Bb[n], J[m][n]);
-                X[m][n] = mfma_bf(Ak, B2[n], X[m][n]);
+                if constexpr (PART == 0) J[m][n] = mfma_bf(A2, Bb[n], J[m][n]);
+                else X[m][n] = mfma_bf(Ak, B2[n], X[m][n]);
             }
         }
         load_k(tn, x);
@@ -487,10 +491,23 @@ __global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R)
                 rowX[n] = X[m][n][r];
             }
             const int64_t off = static_cast<int64_t>(rb + MT * (4 * g + r) + m) * DV_ + cb + NT * c;
-            store_run<NT>(out + off, rowJ);
-            store_run<NT>(out + static_cast<int64_t>(DK) * DV_ + off, rowX);
+            if constexpr (PART == 0) store_run<NT>(out + off, rowJ);
+            else store_run<NT>(out + static_cast<int64_t>(DK) * DV_ + off, rowX);
         }
-    if (lane == 0 && tile == 0) p.gsub[slot] = fast_exp(-Rsum);
+    if (PART == 0 && lane == 0 && tile == 0) p.gsub[slot] = fast_exp(-Rsum);
+}
+
+// One wave per (sub-segment, tile, part): part 0 accumulates J, part 1 X, so
+// that each wave holds one accumulator set (two waves per SIMD).
+template <int DK, int DV>
+__global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R) {
+    constexpr int MT = (DK > kCompBfEdge ? kCompBfEdge : DK) / 16;
+    constexpr int NT = (DV > kCompBfEdge ? kCompBfEdge : DV) / 16;
+    constexpr int TILES = (DK / (16 * MT)) * (DV / (16 * NT));
+    const int64_t id = xcd_local_id();       // a sub-segment's tiles share an XCD
+    const int tp = static_cast<int>(id % (2 * TILES));
+    if (tp & 1) comp_bf_part<DK, DV, 1>(p, R, id / (2 * TILES), tp >> 1);
+    else comp_bf_part<DK, DV, 0>(p, R, id / (2 * TILES), tp >> 1);
 }
 
 // Ordered carry: sub-segment composites -> the starting (J, eta) of every

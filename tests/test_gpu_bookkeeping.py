@@ -48,8 +48,9 @@ def _check_diag_records(kdn, recs, B, H, T, dk, dv, S_req):
     _, _, bounds = oracle.plan(T, chunk, S)
     sub = oracle.plan_sub(T, chunk, S, R)
     ntile = dv // min(dv, 64)
-    # composite wave tiles of bf16 inputs: at most 64 key rows x 64 value columns
-    ctile = max(dk // 64, 1) * max(dv // 64, 1)
+    # composite waves of bf16 inputs: tiles of at most 64 key rows x 64 value
+    # columns, each summed by two waves (J, X), echoed as 2 tile + part
+    ctile = 2 * max(dk // 64, 1) * max(dv // 64, 1)
     main = [r for r in recs if r[0] == 1]
     comp = [r for r in recs if r[0] == 2]
     assert all(r[0] in (1, 2) for r in recs), "records of an unknown kind"
