@@ -515,7 +515,9 @@ __device__ __forceinline__ BwdRun bwd_run(const BwdParams& p) {
         b = b < a ? a : (b > p.T ? p.T : b);
         const int64_t t0 = a + static_cast<int64_t>(r.seg) * p.vl_seg;
         r.t_begin = t0 < b ? t0 : b;
-        r.t_end = r.t_begin + p.vl_seg < b ? r.t_begin + p.vl_seg : b;
+        // a sequence up to vl_thr tokens long is one whole item
+        const bool whole = b - a <= p.vl_thr;
+        r.t_end = !whole && r.t_begin + p.vl_seg < b ? r.t_begin + p.vl_seg : b;
         r.nch = uniform64((r.t_end - r.t_begin + kBwdChunk - 1) / kBwdChunk);
         r.last = r.t_end == b;
         r.state = static_cast<int64_t>(sq) * p.H + h;

@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void k_bwd_adj_carry_varlen(BwdParams p, int64
         int64_t a = p.cu_seqlens[sq], b = p.cu_seqlens[sq + 1];
         a = a < 0 ? 0 : (a > p.T ? p.T : a);
         b = b < a ? a : (b > p.T ? p.T : b);
-        int64_t nseg = b - a > p.vl_seg ? (b - a + p.vl_seg - 1) / p.vl_seg : 1;
+        int64_t nseg = b - a > p.vl_thr ? (b - a + p.vl_seg - 1) / p.vl_seg : 1;
         if (fi + nseg > p.vl_items) nseg = p.vl_items - fi;
         const int64_t h = ht / ntile;
         auto at = [&](int64_t item) { return (item * p.H) * ntile + ht; };

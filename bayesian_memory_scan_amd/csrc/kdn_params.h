@@ -46,7 +46,7 @@ struct DiagParams {
     const int64_t* cu_seqlens;   // packed variable-length batch: [nseq + 1] offsets, or NULL
     int32_t* seq_order;          // its sequences, longest first (written by the plan pass)
     int32_t nseq;
-    // Packed batch: sequences longer than vl_seg tokens are cut into segments
+    // Packed batch: sequences longer than vl_thr tokens are cut into segments
     // of vl_seg tokens (the last one shorter); the plan pass writes the tables.
     // A packed batch's comp / sub / gsub are indexed by composite segment c
     // (a segment that is not its sequence's last): comp [vl_comps][H][2][dk][dv]
@@ -63,6 +63,7 @@ struct DiagParams {
     int32_t* nwork;              // [4]: items, composite segments, split sequences (each <= capacity),
                                  // sub-segments per composite segment
     int64_t vl_seg;              // segment length of a split sequence (multiple of 256), 0 = no split
+    int64_t vl_thr;              // a sequence is split when longer than this (>= vl_seg)
     int64_t vl_items;            // capacity of the item tables
     int64_t vl_comps;            // capacity of the composite tables
     int64_t* echo;               // bounds echo (kdn_scan_opts), or NULL
@@ -141,7 +142,7 @@ __device__ inline void plan_longest_first(const int64_t* cu, int32_t n, int64_t 
 
 // Packed batch: segments of a sequence of len tokens (1 when it is not split).
 __device__ __forceinline__ int64_t varlen_segments(const DiagParams& p, int64_t len) {
-    return p.vl_seg > 0 && len > p.vl_seg ? (len + p.vl_seg - 1) / p.vl_seg : 1;
+    return p.vl_seg > 0 && len > p.vl_thr ? (len + p.vl_seg - 1) / p.vl_seg : 1;
 }
 
 // One main-pass work item of a packed batch, run wg = item * H + head: the
@@ -356,6 +357,7 @@ struct BwdParams {
     const int32_t* split_seq;
     const int32_t* nwork;
     int64_t vl_seg;
+    int64_t vl_thr;
     int64_t vl_items;
     int64_t vl_comps;
 };

@@ -103,7 +103,19 @@ struct VarlenPlan {
     int32_t R;
     int64_t comps;   // capacity of the composite tables
     int64_t items;   // capacity of the item tables
+    int64_t thr = 0; // sequences longer than thr are split (thr >= seg)
 };
+// Composite tables and sub-segments of a plan whose segment length is set.
+static void plan_tables(VarlenPlan& v, int64_t N, int64_t H, int64_t total_T, int64_t dv) {
+    v.comps = total_T / v.seg;
+    v.items = N + v.comps;
+    const int64_t units = v.comps * H * (dv > 32 ? dv / 32 : 1);
+    int64_t R = 8 * kNumCU / units;
+    if (R > v.seg / (4 * diag_chunk())) R = v.seg / (4 * diag_chunk());
+    if (R < 1) R = 1;
+    v.R = static_cast<int32_t>(R);
+}
+
 VarlenPlan plan_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dv, int32_t request) {
     VarlenPlan v{0, 1, 0, N};
     if (request == 1 || N == 0 || H == 0) return v;
@@ -113,13 +125,24 @@ VarlenPlan plan_varlen(int64_t N, int64_t H, int64_t total_T, int64_t dv, int32_
     if (L < kVarlenMinSeg) L = kVarlenMinSeg;
     if (total_T <= L) return v;
     v.seg = L;
-    v.comps = total_T / L;
-    v.items = N + v.comps;
-    const int64_t units = v.comps * H * (dv > 32 ? dv / 32 : 1);
-    int64_t R = 8 * kNumCU / units;
-    if (R > L / (4 * diag_chunk())) R = L / (4 * diag_chunk());
-    if (R < 1) R = 1;
-    v.R = static_cast<int32_t>(R);
+    v.thr = L;
+    plan_tables(v, N, H, total_T, dv);
+    return v;
+}
+
+// The gradient's plan: the same split rule (sequences longer than a fair
+// share), but the split sequences are cut into half-share segments.  Their
+// checkpoint pass carries the adjoint composites at about three times the
+// plain pass's cost per token, one workgroup per CU, so with fair-share
+// segments a single long sequence fills only part of the chip for the
+// whole pass; half-share segments give it twice the workgroups for half as
+// long.  The reverse pass stays bound by the total work per CU.
+VarlenPlan plan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t dv) {
+    VarlenPlan v = plan_varlen(N, H, total_T, dv, 0);
+    if (v.seg >= 2 * kVarlenMinSeg) {
+        v.seg = (v.seg / 2 + 255) / 256 * 256;
+        plan_tables(v, N, H, total_T, dv);
+    }
     return v;
 }
 
@@ -477,7 +500,7 @@ int kdn_diag_scan_varlen_fwd_ex(int64_t N, int64_t H, int64_t total_T, int64_t d
     p.H = H; p.T = total_T; p.dv = d_v; p.I_prior = I_prior;
     p.S = 1; p.nchunks = 0;
     p.cu_seqlens = cu_seqlens; p.nseq = static_cast<int32_t>(N);
-    p.vl_seg = vp.seg; p.vl_items = vp.items; p.vl_comps = vp.comps;
+    p.vl_seg = vp.seg; p.vl_thr = vp.thr; p.vl_items = vp.items; p.vl_comps = vp.comps;
     apply_opts(p, opts);
     (void)hipGetLastError();  // launch status below must reflect this call only
     return diag_varlen_launch(p, d_k, in_dtype == KDN_BF16, vp.R, static_cast<hipStream_t>(stream));
@@ -713,7 +736,7 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
     // sequences longer than a fair share run in segments (the forward plan of
     // kdn_diag_varlen_plan): its tables and composites, plus per item the
     // adjoint composite and carried adjoint (adj, lam) and the decay (adjg)
-    const VarlenPlan vp = work ? plan_varlen(N, H, total_T, d_v, 0) : VarlenPlan{0, 1, 0, N};
+    const VarlenPlan vp = work ? plan_varlen_bwd(N, H, total_T, d_v) : VarlenPlan{0, 1, 0, N};
     if (vp.items >= 2147483647 || !grid_fits((vp.items * H + 7) / 8 * 8 * ntile)) return KDN_EINVAL;
     const VarlenWs vw = varlen_workspace(N, H, total_T, d_k, d_v, vp);
     const size_t b_item = align_up(f * static_cast<size_t>(vp.items) * H * 2 * d_k * d_v, 256);
@@ -789,11 +812,11 @@ int kdn_diag_scan_varlen_bwd(int64_t N, int64_t H, int64_t total_T, int64_t d_k,
                 prep.sub = reinterpret_cast<float*>(take(vw.sub));
                 prep.gsub = reinterpret_cast<float*>(take(vw.gsub));
             }
-            prep.vl_seg = vp.seg; prep.vl_items = vp.items; prep.vl_comps = vp.comps;
+            prep.vl_seg = vp.seg; prep.vl_thr = vp.thr; prep.vl_items = vp.items; prep.vl_comps = vp.comps;
             p.item_seq = prep.item_seq; p.item_seg = prep.item_seg; p.seq_item = prep.seq_item;
             p.seq_comp = prep.seq_comp; p.split_seq = prep.split_seq; p.nwork = prep.nwork;
             p.comp = prep.comp;
-            p.vl_seg = vp.seg; p.vl_items = vp.items; p.vl_comps = vp.comps;
+            p.vl_seg = vp.seg; p.vl_thr = vp.thr; p.vl_items = vp.items; p.vl_comps = vp.comps;
             p.adj = reinterpret_cast<float*>(take(b_item));
             p.lam = reinterpret_cast<float*>(take(b_item));
             p.adjg = reinterpret_cast<float*>(take(b_itemg));
