@@ -43,14 +43,21 @@ __device__ __forceinline__ f32x4c mfma4c(float a, float b, f32x4c c) {
 
 constexpr int kCompCols = 32;   // value columns per wave: 2 x MT x 2 x 4 accumulator registers
 
-// Wave tiles of one head in the composite pass: fp32 inputs take 32-column
-// tiles with every key row, bf16 inputs tiles of at most 64 x 64 entries.
-constexpr int kCompBfEdge = 64;
+// Wave tiles of one head in the composite pass.  fp32 inputs: 32-column
+// tiles with every key row.  bf16 inputs: waves summing J take at most 2 x 8
+// MFMA tiles of 16 x 16 (32 key rows x 128 value columns), waves summing X
+// at most 8 x 2 (128 x 32).  Each wave cuts only its own fp32 factor into
+// limbs, w k^2 over its key rows or w beta v over its value columns, so the
+// narrow side of its tile is the one it splits.
+constexpr int comp_bf_mt(int dk, int part) { return part == 0 ? (dk / 16 < 2 ? dk / 16 : 2) : (dk / 16 < 8 ? dk / 16 : 8); }
+constexpr int comp_bf_nt(int dv, int part) { return part == 0 ? (dv / 16 < 8 ? dv / 16 : 8) : (dv / 16 < 2 ? dv / 16 : 2); }
+constexpr int comp_bf_tiles(int dk, int dv, int part) {
+    return (dk / (16 * comp_bf_mt(dk, part))) * (dv / (16 * comp_bf_nt(dv, part)));
+}
 int comp_tiles(int64_t dk, int64_t dv, bool bf16) {
     if (!bf16) return dv > kCompCols ? static_cast<int>(dv / kCompCols) : 1;
-    const int64_t tr = dk > kCompBfEdge ? dk / kCompBfEdge : 1;
-    const int64_t tc = dv > kCompBfEdge ? dv / kCompBfEdge : 1;
-    return static_cast<int>(2 * tr * tc);   // a J wave and an X wave per tile
+    const int k = static_cast<int>(dk), v = static_cast<int>(dv);
+    return comp_bf_tiles(k, v, 0) + comp_bf_tiles(k, v, 1);   // J waves, then X waves
 }
 
 // Composite unit `rest` (the column tile taken out): its token row bh,
@@ -250,8 +257,11 @@ void k_diag_comp(DiagParams p, int32_t R) {
 // factors: six MFMAs of 16x16x32 (bf16 rate, about 14x that of
 // 16x16x4 fp32 measured on gfx950) per 16 x 16 tile and 32 tokens.
 //
-// One wave per (head, sub-segment, tile of MT x NT 16 x 16 tiles, at most
-// 64 x 64 entries).  Operand layout of 16x16x32: lane (c, g) holds
+// One wave per (head, sub-segment, part, tile of MT x NT 16 x 16 tiles):
+// J waves at most 2 x 8 such tiles, X waves at most 8 x 2, so each splits
+// the factor on its tile's narrow side (comp_bf_mt, comp_bf_nt) and no
+// wave cuts more than 16 elements per lane and block into limbs.
+// Operand layout of 16x16x32: lane (c, g) holds
 // A[row c][k = 8g .. 8g+7] and B[k = 8g .. 8g+7][column c], D[rows 4g .. 4g+3]
 // [column c].  Rows and columns interleave as in the fp32 kernel: tile (m, n)
 // row c is key row rb + MT c + m and column c is value column cb + NT c + n,
@@ -270,8 +280,9 @@ __device__ __forceinline__ f32x4c mfma_bf(u32x4c a, u32x4c b, f32x4c c) {
 }
 
 // The top halves of two fp32 patterns as one bf16 pair: a in the low half.
+// One v_perm_b32 (bytes 2, 3 of a, then bytes 2, 3 of b).
 __device__ __forceinline__ uint32_t pack_top(uint32_t a, uint32_t b) {
-    return (a >> 16) | (b & 0xffff0000u);
+    return __builtin_amdgcn_perm(b, a, 0x07060302u);
 }
 
 // Three-limb split of the pair (xa, xb): limb words l[0..2], with
@@ -296,15 +307,20 @@ template <int N>
 __device__ __forceinline__ float bf_elem(const uint32_t (&w)[N], int e) {
     return (e & 1) ? __uint_as_float(w[e >> 1] & 0xffff0000u) : __uint_as_float(w[e >> 1] << 16);
 }
+// bf16 element e of run a (low half) and of run b (high half) as one word.
 template <int N>
-__device__ __forceinline__ uint32_t bf_bits(const uint32_t (&w)[N], int e) {
-    return (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
+__device__ __forceinline__ uint32_t bf_pair(const uint32_t (&a)[N], const uint32_t (&b)[N], int e) {
+    return __builtin_amdgcn_perm(b[e >> 1], a[e >> 1], (e & 1) ? 0x07060302u : 0x05040100u);
 }
 
-// n 16-bit elements (n = 1, 2, 4) at byte offset off, as 32-bit words.
+// n 16-bit elements (n = 1, 2, 4, 8) at byte offset off, as 32-bit words.
 template <int NW>
 __device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off, int n, uint32_t (&w)[NW]) {
-    if (n == 4) {
+    if (n == 8) {
+        const auto u = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4 && i < NW; ++i) w[i] = u[i];
+    } else if (n == 4) {
         const auto u = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
         w[0] = u[0];
         if constexpr (NW > 1) w[1] = u[1];
@@ -315,17 +331,16 @@ __device__ __forceinline__ void buf_words(__amdgpu_buffer_rsrc_t r, uint32_t off
     }
 }
 
-template <int DK, int DV, int PART>
+template <int DK, int DV, int PART, bool MG>
 __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int64_t unit, int tile) {
     constexpr int KB = 32;                                     // tokens per k-step
-    constexpr int MT = (DK > kCompBfEdge ? kCompBfEdge : DK) / 16;
-    constexpr int NT = (DV > kCompBfEdge ? kCompBfEdge : DV) / 16;
+    constexpr int MT = comp_bf_mt(DK, PART);
+    constexpr int NT = comp_bf_nt(DV, PART);
     constexpr int TC = DV / (16 * NT);                         // wave tiles across the columns
-    constexpr int TILES = (DK / (16 * MT)) * TC;
     constexpr int KW = (MT + 1) / 2;                           // 32-bit words of a lane's key run
     constexpr int BW = (NT + 1) / 2;                           // ... of its beta / v run
-    static_assert(MT == 1 || MT == 2 || MT == 4, "key rows per lane run");
-    static_assert(NT == 1 || NT == 2 || NT == 4, "value columns per lane run");
+    static_assert(MT == 1 || MT == 2 || MT == 4 || MT == 8, "key rows per lane run");
+    static_assert(NT == 1 || NT == 2 || NT == 4 || NT == 8, "value columns per lane run");
 
     const int lane = threadIdx.x;
     const int g = lane >> 4;
@@ -334,15 +349,17 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
     if (!comp_unit(p, unit, R, u)) return;
     const int64_t bh = u.bh;
     const int64_t t_begin = u.t_begin, t_end = u.t_end;
-    if (lane == 0) echo_bounds(p, blockIdx.x, 2, u.run, u.seg, u.sub, t_begin, t_end, 2 * tile + PART, u.sq);
+    if (lane == 0)
+        echo_bounds(p, blockIdx.x, 2, u.run, u.seg, u.sub, t_begin, t_end,
+                    PART ? comp_bf_tiles(DK, DV, 0) + tile : tile, u.sq);
     const int rb = (tile / TC) * 16 * MT;    // first key row of the wave tile
     const int cb = (tile % TC) * 16 * NT;    // first value column
     const int64_t DV_ = p.dv;
 
     const uint16_t* kh = static_cast<const uint16_t*>(p.k) + bh * p.T * DK;
     const uint16_t* vh = static_cast<const uint16_t*>(p.v) + bh * p.T * DV_;
-    // beta == NULL: Palimpsa-M gating, beta_t[i] = d_t
-    const uint16_t* bth = p.beta ? static_cast<const uint16_t*>(p.beta) + bh * p.T * DV_ : nullptr;
+    // MG (beta == NULL): Palimpsa-M gating, beta_t[i] = d_t
+    const uint16_t* bth = MG ? nullptr : static_cast<const uint16_t*>(p.beta) + bh * p.T * DV_;
     const uint16_t* dh = static_cast<const uint16_t*>(p.d) + bh * p.T;
     const float4* sch = p.scal + bh * p.T;
 
@@ -367,39 +384,36 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
         const int64_t L0 = t_end - tb;
         return (tb < t_begin || L0 < 0) ? 0 : (L0 < KB ? L0 : KB);
     };
-    auto load_k = [&](int64_t tb, Raw& x) __attribute__((always_inline)) {
+    // A block's loads in the order of their first use: A d, beta, v, then k.
+    auto load = [&](int64_t tb, Raw& x) __attribute__((always_inline)) {
         const int64_t L = block_len(tb);
+        float ad[1];
+        buf_load<1>(buf_rsrc(sch + tb, L * 16), static_cast<uint32_t>((lane & 31) * 16 + 12), ad);
+        x.ad = ad[0];
+        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vh + tb * DV_, L * DV_ * 2);
+        const __amdgpu_buffer_rsrc_t rb_ = MG ? buf_rsrc(dh + tb, L * 2) : buf_rsrc(bth + tb * DV_, L * DV_ * 2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int s_ = 8 * g + e;
+            if constexpr (MG) {
+                const uint32_t d1 = __builtin_amdgcn_raw_buffer_load_b16(rb_, static_cast<uint32_t>(s_ * 2), 0, 0);
+#pragma unroll
+                for (int h = 0; h < BW; ++h) x.b[e][h] = d1 | (d1 << 16);
+            } else {
+                buf_words<BW>(rb_, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.b[e]);
+            }
+            if constexpr (PART == 1) buf_words<BW>(rv, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.v[e]);
+        }
         const __amdgpu_buffer_rsrc_t rk = buf_rsrc(kh + tb * DK, L * DK * 2);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
             buf_words<KW>(rk, static_cast<uint32_t>(((8 * g + e) * DK + rb + MT * c) * 2), MT, x.k[e]);
     };
-    auto load_bv = [&](int64_t tb, Raw& x) __attribute__((always_inline)) {
-        const int64_t L = block_len(tb);
-        const __amdgpu_buffer_rsrc_t rv = buf_rsrc(vh + tb * DV_, L * DV_ * 2);
-        const __amdgpu_buffer_rsrc_t rb_ = bth ? buf_rsrc(bth + tb * DV_, L * DV_ * 2) : buf_rsrc(dh + tb, L * 2);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int s_ = 8 * g + e;
-            if constexpr (PART == 1) buf_words<BW>(rv, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.v[e]);
-            if (bth) {
-                buf_words<BW>(rb_, static_cast<uint32_t>((s_ * DV_ + cb + NT * c) * 2), NT, x.b[e]);
-            } else {
-                const uint32_t d1 = __builtin_amdgcn_raw_buffer_load_b16(rb_, static_cast<uint32_t>(s_ * 2), 0, 0);
-#pragma unroll
-                for (int h = 0; h < BW; ++h) x.b[e][h] = d1 | (d1 << 16);
-            }
-        }
-        float ad[1];
-        buf_load<1>(buf_rsrc(sch + tb, L * 16), static_cast<uint32_t>((lane & 31) * 16 + 12), ad);
-        x.ad = ad[0];
-    };
 
     float Rsum = 0.0f;
-    // One block: weights, B operands, then (with the next block's beta and v
-    // loading into the registers just freed) the A operands and MFMAs row
-    // tile by row tile, then the next block's keys.
-    auto compute = [&](Raw& x, int64_t tn) __attribute__((always_inline)) {
+    // One block: weights, B operands, then the A operands and MFMAs row tile
+    // by row tile.
+    auto compute = [&](const Raw& x) __attribute__((always_inline)) {
         // decay of token tb + t to the sub-segment's end: exp(-(Rsum + sum of
         // A d over the block's tokens after t)), by additions only
         float P = row_prefix16(x.ad);                        // inclusive, within each 16
@@ -419,7 +433,7 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
             for (int q = 0; q < 4; ++q) {
                 const int e0 = 2 * q, e1 = 2 * q + 1;
                 if constexpr (PART == 0) {
-                    Bb[n][q] = bf_bits(x.b[e0], n) | (bf_bits(x.b[e1], n) << 16);
+                    Bb[n][q] = bf_pair(x.b[e0], x.b[e1], n);
                 } else {
                     const float ya = w[e0] * (bf_elem(x.b[e0], n) * bf_elem(x.v[e0], n));
                     const float yb = w[e1] * (bf_elem(x.b[e1], n) * bf_elem(x.v[e1], n));
@@ -430,7 +444,6 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
                     B2[n][q] = l2;
                 }
             }
-        load_bv(tn, x);
         // A operands row tile by row tile: k (exact) and the limbs of w k^2
 #pragma unroll
         for (int m = 0; m < MT; ++m) {
@@ -439,7 +452,7 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
             for (int q = 0; q < 4; ++q) {
                 const int e0 = 2 * q, e1 = 2 * q + 1;
                 if constexpr (PART == 1) {
-                    Ak[q] = bf_bits(x.k[e0], m) | (bf_bits(x.k[e1], m) << 16);
+                    Ak[q] = bf_pair(x.k[e0], x.k[e1], m);
                 } else {
                     const float ka = bf_elem(x.k[e0], m), kb = bf_elem(x.k[e1], m);
                     uint32_t l0, l1, l2;
@@ -465,18 +478,24 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
                 else X[m][n] = mfma_bf(Ak, B2[n], X[m][n]);
             }
         }
-        load_k(tn, x);
         Rsum += total;
     };
 
-    // one operand set: each block's loads are issued as the previous block's
-    // operands die (a block before the sub-segment reads nothing)
+    // Two operand sets, two blocks per trip: a block's loads are issued
+    // before the other set's block is computed, so each has a whole block's
+    // work to land in (a block before the sub-segment reads nothing).
     const int64_t nblk = (t_end - t_begin + KB - 1) / KB;
-    Raw x;
+    Raw xa, xb;
     int64_t tb = t_begin + (nblk - 1) * KB;
-    load_bv(tb, x);
-    load_k(tb, x);
-    for (int64_t i = 0; i < nblk; ++i, tb -= KB) compute(x, tb - KB);
+    load(tb, xa);
+    int64_t i = 0;
+    for (; i + 2 <= nblk; i += 2, tb -= 2 * KB) {
+        load(tb - KB, xb);
+        compute(xa);
+        load(tb - 2 * KB, xa);
+        compute(xb);
+    }
+    if (i < nblk) compute(xa);
 
     const int64_t slot = u.slot;
     float* out = p.sub + slot * 2 * DK * DV_;
@@ -497,17 +516,22 @@ __device__ __forceinline__ void comp_bf_part(const DiagParams& p, int32_t R, int
     if (PART == 0 && lane == 0 && tile == 0) p.gsub[slot] = fast_exp(-Rsum);
 }
 
-// One wave per (sub-segment, tile, part): part 0 accumulates J, part 1 X, so
-// that each wave holds one accumulator set (two waves per SIMD).
+// One wave per (sub-segment, part, tile): the unit's J waves first, then its
+// X waves, so that each wave holds one accumulator set (two waves per SIMD).
 template <int DK, int DV>
-__global__ __launch_bounds__(kWave) void k_diag_comp_bf(DiagParams p, int32_t R) {
-    constexpr int MT = (DK > kCompBfEdge ? kCompBfEdge : DK) / 16;
-    constexpr int NT = (DV > kCompBfEdge ? kCompBfEdge : DV) / 16;
-    constexpr int TILES = (DK / (16 * MT)) * (DV / (16 * NT));
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void k_diag_comp_bf(DiagParams p, int32_t R) {
+    constexpr int TJ = comp_bf_tiles(DK, DV, 0);
+    constexpr int TX = comp_bf_tiles(DK, DV, 1);
     const int64_t id = xcd_local_id();       // a sub-segment's tiles share an XCD
-    const int tp = static_cast<int>(id % (2 * TILES));
-    if (tp & 1) comp_bf_part<DK, DV, 1>(p, R, id / (2 * TILES), tp >> 1);
-    else comp_bf_part<DK, DV, 0>(p, R, id / (2 * TILES), tp >> 1);
+    const int tp = static_cast<int>(id % (TJ + TX));
+    const int64_t unit = id / (TJ + TX);
+    if (p.beta) {
+        if (tp >= TJ) comp_bf_part<DK, DV, 1, false>(p, R, unit, tp - TJ);
+        else comp_bf_part<DK, DV, 0, false>(p, R, unit, tp);
+    } else {
+        if (tp >= TJ) comp_bf_part<DK, DV, 1, true>(p, R, unit, tp - TJ);
+        else comp_bf_part<DK, DV, 0, true>(p, R, unit, tp);
+    }
 }
 
 // Ordered carry: sub-segment composites -> the starting (J, eta) of every

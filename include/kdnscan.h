@@ -313,8 +313,9 @@ int kdn_diag_plan(int64_t B, int64_t H, int64_t T, int64_t d_k, int64_t d_v, int
  *     2 = diagonal segment composite (part = sub-segment), 3 = isotropic mean
  *     scan (part = column tile), 4 = isotropic segment composite; for a
  *     packed batch run = s*H + h of sequence s = `sequence`.  Kind 2 records
- *     hold the wave's tile in the `sequence` word (bf16 inputs: 2 * tile +
- *     p, p = 0 for the wave summing J, 1 for eta) and, for a packed batch,
+ *     hold the wave's tile in the `sequence` word (bf16 inputs: its index
+ *     among the unit's waves, those summing J first, then those summing
+ *     eta) and, for a packed batch,
  *     the sequence in the last word (0 otherwise).  Record r of
  *     kind k sits at a fixed slot; records that would pass echo_capacity are
  *     dropped; slots of work units with nothing to do stay untouched (clear

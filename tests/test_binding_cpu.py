@@ -186,8 +186,9 @@ def test_ex_segments_change_the_workspace_and_echo_size():
         sizes.append(n.value)
         words.append(o.echo_words)
         _, S_plan, R, _ = kdn.kdn_diag_plan(1, 2, 1000, 128, 128, segments=S)
-        # bf16 composites: 64 x 64 tiles, each summed by a J wave and an X wave
-        comp_units = 2 * (S_plan - 1) * R * 4 * 2
+        # bf16 composites at d_k = d_v = 128: four J waves (32 x 128 tiles)
+        # and four X waves (128 x 32) per sub-segment
+        comp_units = 2 * (S_plan - 1) * R * (4 + 4)
         assert o.echo_words == kdn.KDN_ECHO_WORDS * (2 * S_plan * 2 + comp_units)
     assert sizes[0] < sizes[1] < sizes[2] and words[0] < words[1] < words[2]
 

@@ -48,9 +48,10 @@ def _check_diag_records(kdn, recs, B, H, T, dk, dv, S_req):
     _, _, bounds = oracle.plan(T, chunk, S)
     sub = oracle.plan_sub(T, chunk, S, R)
     ntile = dv // min(dv, 64)
-    # composite waves of bf16 inputs: tiles of at most 64 key rows x 64 value
-    # columns, each summed by two waves (J, X), echoed as 2 tile + part
-    ctile = 2 * max(dk // 64, 1) * max(dv // 64, 1)
+    # composite waves of bf16 inputs, echoed by their index in the unit: J
+    # waves over tiles of at most 32 key rows x 128 value columns, then X
+    # waves over tiles of at most 128 x 32
+    ctile = (dk // min(dk, 32)) * (dv // min(dv, 128)) + (dk // min(dk, 128)) * (dv // min(dv, 32))
     main = [r for r in recs if r[0] == 1]
     comp = [r for r in recs if r[0] == 2]
     assert all(r[0] in (1, 2) for r in recs), "records of an unknown kind"

@@ -116,8 +116,9 @@ def test_split_echo_matches_plan(kdn):
     recs = [tuple(int(x) for x in r) for r in echo[:words].view(-1, W).cpu().numpy()]
     ntile = dv // 64
     main_grid = (items_cap * H + 7) // 8 * 8 * ntile
-    # 64 x 64 bf16 composite tiles: 4, each summed by a J wave and an X wave
-    assert words == W * (main_grid + comps_cap * H * R * 4 * 2)
+    # bf16 composite waves per unit at d_k = d_v = 128: four J waves (32 x 128
+    # tiles) and four X waves (128 x 32)
+    assert words == W * (main_grid + comps_cap * H * R * (4 + 4))
     seen = set()
     for slot, r in enumerate(recs[:main_grid]):
         within = slot % (8 * ntile)
@@ -135,7 +136,7 @@ def test_split_echo_matches_plan(kdn):
     for s, g, subs in comps:
         for r_, (t0, t1) in enumerate(subs):
             for h in range(H):
-                for tile in range(4 * 2):
+                for tile in range(4 + 4):
                     want[(s * H + h, g, r_, tile)] = (t0, t1, s)
     got = {}
     for r in recs[main_grid:]:
