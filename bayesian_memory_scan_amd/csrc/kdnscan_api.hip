@@ -52,9 +52,9 @@ Plan plan_scan(int64_t BH, int64_t T, int64_t dv, int32_t request) {
     if (S > pl.nchunks) S = pl.nchunks;
     if (S < 1) S = 1;
     pl.S = static_cast<int32_t>(S);
-    // composites: about eight one-wave work units (32-column tiles) per CU,
-    // at least 4 chunks per sub-segment (the bf16 kernel's 64 x 64 tiles come
-    // to the same unit count at d_k = d_v = 128)
+    // composites: about eight work units of 32 value columns per CU (one
+    // wave each for fp32 inputs, two for bf16: a J wave's and an X wave's
+    // share), at least 4 chunks per sub-segment
     int64_t R = 1;
     if (pl.S > 1 && BH > 0) {
         const int64_t units = BH * (pl.S - 1) * (dv > 32 ? dv / 32 : 1);
