@@ -53,6 +53,15 @@ def test_m_gating_forward(kdn, shape, S):
     gu.compare_diag(inp, _fwd(kdn, inp, S), _heads(B, H), what=f"M S={S}")
 
 
+@pytest.mark.parametrize("dk,dv", [(16, 128), (128, 16), (32, 32), (64, 128)], ids=lambda d: str(d))
+def test_m_gating_composite_shapes(kdn, dk, dv):
+    """Palimpsa-M gating through the bf16 composite pass at tile shapes
+    where its J and X waves differ in count (two segments, T = 601)."""
+    inp = _m_inputs(gu.diag_spec(1, 2, 601, dk, dv, "bf16", seed=8100 + dk + dv))
+    print(f"M composite dk={dk} dv={dv}", flush=True)
+    gu.compare_diag(inp, _fwd(kdn, inp, 2), _heads(1, 2), what=f"M composite dk={dk} dv={dv}")
+
+
 def test_m_gating_forward_full_size_sampled(kdn):
     spec = synth.workload("diagm_b8h16t2048d128_bf16")
     inp = _m_inputs(spec)

@@ -86,6 +86,19 @@ def test_diag_composite_head_sizes(kdn, dk, dv):
     gu.compare_diag(inp, res, _all_heads(1, 2), what=f"composite dk={dk} dv={dv}")
 
 
+@pytest.mark.parametrize("dk", [16, 32, 64, 128])
+@pytest.mark.parametrize("dv", [16, 32, 64, 128])
+def test_diag_composite_head_sizes_bf16(kdn, dk, dv):
+    """bf16 inputs at every (d_k, d_v): the composite pass's J waves (tiles
+    of at most 32 key rows x 128 value columns) and X waves (128 x 32) take
+    different shapes and counts at each pairing; two segments, ragged final
+    chunk (T = 601)."""
+    inp = synth.diag_inputs(gu.diag_spec(1, 2, 601, dk, dv, "bf16", seed=7100 + dk + dv))
+    print(f"diag composite bf16 dk={dk} dv={dv}", flush=True)
+    res = _run_diag(kdn, gu.upload_diag(inp), S=2)
+    gu.compare_diag(inp, res, _all_heads(1, 2), what=f"composite bf16 dk={dk} dv={dv}")
+
+
 @pytest.mark.parametrize("S", [1, 2])
 @pytest.mark.parametrize("dv", [32, 128])
 def test_diag_frame_restarts_inside_chunks(kdn, dv, S):
